@@ -1,0 +1,239 @@
+/*
+ * mesa_oracle.c -- plain, slow fp64 CPU reference of the Mesa layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link or call
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark load it.  It shares no code with the HIP library.
+ *
+ * What it computes (MesaNet summary, gist.science paper 2506.05233):
+ *  - Section "A Camada Mesa", displayed objective: Phi_t minimises
+ *      1/2 sum_{t'<=t} zeta_{tt'} |v_t' - Phi k_t'|^2 + 1/2 Tr(Phi Lambda Phi^T).
+ *    Setting its gradient to zero gives Phi_t (H_t + Lambda) = G_t with
+ *      H_t = sum zeta_{tt'} k_t' k_t'^T   (d_k x d_k)
+ *      G_t = sum zeta_{tt'} v_t' k_t'^T   (d_v x d_k).
+ *    With zeta_{tt'} = prod_{s=t'+1..t} gamma_s ("cumulative forget
+ *    factors") these obey H_t = gamma_t H_{t-1} + k_t k_t^T and
+ *    G_t = gamma_t G_{t-1} + v_t k_t^T, H_0 = G_0 = 0.
+ *  - Same section, sentence after the objective: the output is
+ *    Delta_t = Phi_t q_t = G_t q*_t with q*_t = (H_t + Lambda)^{-1} q_t,
+ *    the solve done by Conjugate Gradient.
+ *  - Same section, bullet "Computacao Dinamica": the number of CG
+ *    iterations needed to meet a stopping criterion varies per token.
+ *
+ * Readings where the page is silent (each one listed in the design notes):
+ *  - Lambda = diag(lambda), one lambda vector per head, constant in t.
+ *  - CG is the textbook unpreconditioned method started from x0 = 0.
+ *  - Stopping: before each update, stop when |r|_2 / |q_t|_2 < tol, where r
+ *    is the recursively updated residual; tol == 0 runs exactly max_iters
+ *    updates.  rr == 0 or p^T A p <= 0 also stop (breakdown guards); q_t = 0
+ *    gives x = 0 and zero iterations.
+ *  - The output is G_t x_k, with x_k the CG iterate that was reached.
+ *
+ * The H_t and G_t are formed explicitly per token, in fp64, exactly as the
+ * recurrence above says.  No chunking, no blocking.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum {
+    ORACLE_STOP_CAP = 0,       /* max_iters updates were made            */
+    ORACLE_STOP_TOL = 1,       /* residual ratio fell below tol          */
+    ORACLE_STOP_RR_ZERO = 2,   /* r^T r == 0 (exact convergence)         */
+    ORACLE_STOP_BREAKDOWN = 3, /* p^T A p <= 0 (cannot occur for SPD A)  */
+    ORACLE_STOP_Q_ZERO = 4     /* q_t == 0: x = 0                        */
+};
+
+static double dot(int n, const double *a, const double *b)
+{
+    double s = 0.0;
+    for (int i = 0; i < n; ++i) s += a[i] * b[i];
+    return s;
+}
+
+/* y = (Hm + diag(lam)) p, Hm is n x n row-major. */
+static void apply_a(int n, const double *Hm, const double *lam, const double *p, double *y)
+{
+    for (int i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < n; ++j) s += Hm[(size_t)i * n + j] * p[j];
+        y[i] = s + lam[i] * p[i];
+    }
+}
+
+/*
+ * Conjugate Gradient on (Hm + diag(lam)) x = b from x = 0.
+ * Outputs: x, number of updates (return value), the stop reason, the residual
+ * ratio rho at the stop (rho_n = sqrt(r^T r)/|b| after the last update) and
+ * the smallest ratio that was checked and passed before it (+inf if none).
+ * scratch: 3n doubles.
+ */
+int oracle_cg_solve(int n, const double *Hm, const double *lam, const double *b,
+                    int max_iters, double tol, double *x, double *scratch,
+                    int *reason, double *rho_stop, double *rho_min_prev)
+{
+    double *r = scratch, *p = scratch + n, *y = scratch + 2 * n;
+    for (int i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; p[i] = b[i]; }
+    double rr = dot(n, r, r);
+    double nq = sqrt(dot(n, b, b));
+    double minprev = INFINITY;
+    int it = 0, why = ORACLE_STOP_CAP;
+    if (nq == 0.0) {
+        if (reason) *reason = ORACLE_STOP_Q_ZERO;
+        if (rho_stop) *rho_stop = 0.0;
+        if (rho_min_prev) *rho_min_prev = INFINITY;
+        return 0;
+    }
+    while (it < max_iters) {
+        double rho = sqrt(rr) / nq;
+        if (tol > 0.0 && rho < tol) { why = ORACLE_STOP_TOL; break; }
+        if (rr == 0.0) { why = ORACLE_STOP_RR_ZERO; break; }
+        apply_a(n, Hm, lam, p, y);
+        double pap = dot(n, p, y);
+        if (!(pap > 0.0)) { why = ORACLE_STOP_BREAKDOWN; break; }
+        double alpha = rr / pap;
+        for (int i = 0; i < n; ++i) { x[i] += alpha * p[i]; r[i] -= alpha * y[i]; }
+        double rr_new = dot(n, r, r);
+        double beta = rr_new / rr;
+        for (int i = 0; i < n; ++i) p[i] = r[i] + beta * p[i];
+        rr = rr_new;
+        if (rho < minprev) minprev = rho;
+        ++it;
+    }
+    if (reason) *reason = why;
+    if (rho_stop) *rho_stop = sqrt(rr) / nq;
+    if (rho_min_prev) *rho_min_prev = minprev;
+    return it;
+}
+
+/* H = g*H + a b^T  (rows x cols, row-major) */
+static void decay_rank1(int rows, int cols, double *M, double g, const double *a, const double *b)
+{
+    for (int i = 0; i < rows; ++i)
+        for (int j = 0; j < cols; ++j)
+            M[(size_t)i * cols + j] = g * M[(size_t)i * cols + j] + a[i] * b[j];
+}
+
+/* out = M x  (rows x cols) */
+static void matvec(int rows, int cols, const double *M, const double *x, double *out)
+{
+    for (int i = 0; i < rows; ++i) out[i] = dot(cols, M + (size_t)i * cols, x);
+}
+
+/*
+ * One token of the recurrence plus its solve: update Hs, Gs in place with
+ * (gamma, k, v), then CG on (Hs + diag lam) x = q and out = Gs x.
+ */
+static void token_step(int dk, int dv, double *Hs, double *Gs, double g,
+                       const double *q, const double *k, const double *v,
+                       const double *lam, int max_iters, double tol, int solve,
+                       double *out, int *iters, double *rho_stop, double *rho_min_prev,
+                       int *reason, double *x, double *scratch)
+{
+    decay_rank1(dk, dk, Hs, g, k, k);
+    decay_rank1(dv, dk, Gs, g, v, k);
+    if (!solve) return;
+    int why = 0;
+    double rs = 0.0, rm = 0.0;
+    int n = oracle_cg_solve(dk, Hs, lam, q, max_iters, tol, x, scratch, &why, &rs, &rm);
+    matvec(dv, dk, Gs, x, out);
+    if (iters) *iters = n;
+    if (rho_stop) *rho_stop = rs;
+    if (rho_min_prev) *rho_min_prev = rm;
+    if (reason) *reason = why;
+}
+
+/*
+ * Forward pass over [B, H, T] tokens.
+ *   q, k : [B,H,T,dk]   v : [B,H,T,dv]   gamma : [B,H,T]   lam : [H,dk]
+ *   want : [B,H,T] bytes or NULL; a token with want == 0 still updates the
+ *          state but is not solved (its outputs are left untouched).
+ *   out  : [B,H,T,dv]; iters, reason : [B,H,T] int32; rho_stop,
+ *          rho_min_prev : [B,H,T] (each may be NULL)
+ *   final_H : [B,H,dk,dk], final_G : [B,H,dv,dk] or NULL.
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+int oracle_forward(const double *q, const double *k, const double *v,
+                   const double *gamma, const double *lam,
+                   int B, int H, int T, int dk, int dv, int max_iters, double tol,
+                   const uint8_t *want, double *out, int32_t *iters,
+                   double *rho_stop, double *rho_min_prev, int32_t *reason,
+                   double *final_H, double *final_G)
+{
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || max_iters < 0 || !(tol >= 0.0))
+        return -1;
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long bh = 0; bh < (long)B * H; ++bh) {
+        int h = (int)(bh % H);
+        double *Hs = calloc((size_t)dk * dk, sizeof(double));
+        double *Gs = calloc((size_t)dv * dk, sizeof(double));
+        double *x = malloc(sizeof(double) * dk);
+        double *scratch = malloc(sizeof(double) * 3 * dk);
+        if (!Hs || !Gs || !x || !scratch) {
+            bad = 1;
+        } else {
+            for (int t = 0; t < T; ++t) {
+                size_t tok = (size_t)bh * T + t;
+                int solve = want ? want[tok] != 0 : 1;
+                int it = 0, why = 0;
+                double rs = 0.0, rm = 0.0;
+                token_step(dk, dv, Hs, Gs, gamma[tok], q + tok * dk, k + tok * dk,
+                           v + tok * dv, lam + (size_t)h * dk, max_iters, tol, solve,
+                           out + tok * dv, &it, &rs, &rm, &why, x, scratch);
+                if (solve) {
+                    if (iters) iters[tok] = it;
+                    if (rho_stop) rho_stop[tok] = rs;
+                    if (rho_min_prev) rho_min_prev[tok] = rm;
+                    if (reason) reason[tok] = why;
+                }
+            }
+            if (final_H) memcpy(final_H + (size_t)bh * dk * dk, Hs, sizeof(double) * dk * dk);
+            if (final_G) memcpy(final_G + (size_t)bh * dv * dk, Gs, sizeof(double) * dv * dk);
+        }
+        free(Hs); free(Gs); free(x); free(scratch);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * One recurrent decode step for N x H heads (same section, bullet
+ * "Paralelizacao": O(1) inference with the states G_t, H_t).
+ *   q, k : [N,H,dk]  v : [N,H,dv]  gamma : [N,H]  lam : [H,dk]
+ *   state_H : [N,H,dk,dk], state_G : [N,H,dv,dk] (updated in place)
+ *   out : [N,H,dv]; iters, reason : [N,H]; rho_stop, rho_min_prev : [N,H]
+ */
+int oracle_decode_step(const double *q, const double *k, const double *v,
+                       const double *gamma, const double *lam,
+                       double *state_H, double *state_G,
+                       int N, int H, int dk, int dv, int max_iters, double tol,
+                       double *out, int32_t *iters, double *rho_stop,
+                       double *rho_min_prev, int32_t *reason)
+{
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0 || max_iters < 0 || !(tol >= 0.0))
+        return -1;
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long nh = 0; nh < (long)N * H; ++nh) {
+        int h = (int)(nh % H);
+        double *x = malloc(sizeof(double) * dk);
+        double *scratch = malloc(sizeof(double) * 3 * dk);
+        if (!x || !scratch) {
+            bad = 1;
+        } else {
+            int it = 0, why = 0;
+            double rs = 0.0, rm = 0.0;
+            token_step(dk, dv, state_H + (size_t)nh * dk * dk, state_G + (size_t)nh * dv * dk,
+                       gamma[nh], q + (size_t)nh * dk, k + (size_t)nh * dk, v + (size_t)nh * dv,
+                       lam + (size_t)h * dk, max_iters, tol, 1, out + (size_t)nh * dv,
+                       &it, &rs, &rm, &why, x, scratch);
+            if (iters) iters[nh] = it;
+            if (rho_stop) rho_stop[nh] = rs;
+            if (rho_min_prev) rho_min_prev[nh] = rm;
+            if (reason) reason[nh] = why;
+        }
+        free(x); free(scratch);
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the Mesa layer (forward and decode).
+
+This module only draws random numbers and lays them out.  It holds none of
+the layer's arithmetic, so both the GPU path's tests/bench and the fp64
+oracle can take their inputs from here.
+
+Workload laws follow the MesaNet summary page (gist.science, paper
+2506.05233), section "A Camada Mesa": queries/keys arrive already
+normalised (section "Arquitetura (MesaNet)", bullet on pre-processing), values
+are unconstrained, the forget gate gamma in (0, 1] and the regulariser Lambda
+is symmetric positive definite (taken diagonal here).
+
+Layout (row-major, contiguous):
+  q, k : [B, H, T, d]     v : [B, H, T, d]
+  gamma: [B, H, T] float32
+  lam  : [H, d]    float32
+bf16 tensors are carried as uint16 bit patterns (round-to-nearest-even from
+float32), so that the exact stored value is known on the host.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "forward_inputs", "decode_head_inputs",
+    "bf16_bits", "bf16_bits_to_f32", "as_f64",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shapes, dtypes and the laws of every input."""
+    name: str
+    B: int                 # batch (decode: sequences N)
+    H: int                 # heads
+    T: int                 # tokens (decode: prefix length)
+    d: int                 # d_k = d_v
+    chunk: int
+    dtype: str             # storage dtype of q, k, v: "f32" or "bf16"
+    gamma_lo: float        # gamma ~ U[gamma_lo, 1)
+    lam_law: str           # "const", "uniform" or "loguniform"
+    lam_a: float
+    lam_b: float
+    max_iters: int
+    tol: float
+    seed: int
+    steps: int = 0         # decode steps (decode workloads only)
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_f32_d16_T256", 1, 1, 256, 16, 64, "f32", 0.9,
+                 "const", 1.0, 1.0, 10, 0.0, 1000),
+        Workload("mid_bf16_d64_T2048", 2, 4, 2048, 64, 64, "bf16", 0.95,
+                 "uniform", 0.5, 2.0, 15, 0.0, 1001),
+        Workload("layer_bf16_d128_T4096_k30", 8, 16, 4096, 128, 64, "bf16", 0.97,
+                 "uniform", 0.5, 2.0, 30, 0.0, 1002),
+        Workload("dynamic_f32_d128_T8192_tol1e-4", 4, 16, 8192, 128, 64, "f32", 0.99,
+                 "loguniform", 0.25, 4.0, 30, 1e-4, 1003),
+        Workload("decode_f32_d128_N256_prefix4096", 256, 16, 4096, 128, 64, "f32", 0.97,
+                 "uniform", 0.5, 2.0, 30, 1e-4, 1004, steps=1024),
+    ]
+}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> the exact float32 values they encode."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact stored value of a q/k/v array as float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    """Gaussian rows scaled to unit L2 norm over the last axis (float64)."""
+    x = rng.standard_normal(shape)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    n[n == 0] = 1.0
+    return x / n
+
+
+def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x64.astype(np.float32)
+    return bf16_bits(x32) if dtype == "bf16" else x32
+
+
+def _lam(rng: np.random.Generator, H: int, d: int, law: str, a: float, b: float) -> np.ndarray:
+    if law == "const":
+        return np.full((H, d), a, dtype=np.float32)
+    if law == "uniform":
+        return rng.uniform(a, b, size=(H, d)).astype(np.float32)
+    if law == "loguniform":
+        return np.exp(rng.uniform(np.log(a), np.log(b), size=(H, d))).astype(np.float32)
+    raise ValueError(f"unknown lambda law {law!r}")
+
+
+def forward_inputs(w: Workload, B=None, H=None, T=None, seed=None):
+    """Inputs of a forward workload (optionally with overridden sizes).
+
+    Draw order from one PCG64 stream: q, k, v, gamma, lambda.
+    Returns dict(q, k, v, gamma, lam) with q/k/v in the storage dtype.
+    """
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    shape = (B, H, T, w.d)
+    q = _store(_unit_rows(rng, shape), w.dtype)
+    k = _store(_unit_rows(rng, shape), w.dtype)
+    v = _store(rng.standard_normal(shape), w.dtype)
+    gamma = rng.uniform(w.gamma_lo, 1.0, size=(B, H, T)).astype(np.float32)
+    lam = _lam(rng, H, w.d, w.lam_law, w.lam_a, w.lam_b)
+    return dict(q=q, k=k, v=v, gamma=gamma, lam=lam)
+
+
+def decode_lambda(w: Workload, H=None) -> np.ndarray:
+    """Per-head regulariser of a decode workload ([H, d] float32)."""
+    H = w.H if H is None else H
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0x1A])))
+    return _lam(rng, H, w.d, w.lam_law, w.lam_a, w.lam_b)
+
+
+def decode_head_inputs(w: Workload, n: int, h: int, prefix: int = None, steps: int = None):
+    """Prefix and per-step inputs of one decode head (n, h), float32.
+
+    Each head has its own stream (SeedSequence([seed, n, h])), so any subset of
+    heads can be drawn alone.  Draw order: prefix k, v, gamma; then step q, k,
+    v, gamma.  Returns dict(pk [P,d], pv [P,d], pgamma [P], q [S,d], k [S,d],
+    v [S,d], gamma [S]).
+    """
+    P = w.T if prefix is None else prefix
+    S = w.steps if steps is None else steps
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, n, h])))
+    pk = _unit_rows(rng, (P, w.d)).astype(np.float32)
+    pv = rng.standard_normal((P, w.d)).astype(np.float32)
+    pg = rng.uniform(w.gamma_lo, 1.0, size=P).astype(np.float32)
+    q = _unit_rows(rng, (S, w.d)).astype(np.float32)
+    k = _unit_rows(rng, (S, w.d)).astype(np.float32)
+    v = rng.standard_normal((S, w.d)).astype(np.float32)
+    g = rng.uniform(w.gamma_lo, 1.0, size=S).astype(np.float32)
+    return dict(pk=pk, pv=pv, pgamma=pg, q=q, k=k, v=v, gamma=g)

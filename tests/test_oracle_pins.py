@@ -1,0 +1,351 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Every check here uses an independent route to the answer: exact rational
+arithmetic, a direct factorisation, a least-squares solve of the objective
+itself, a closed form, or the characterisation of the CG iterate as a Krylov
+projection.  The passages are from the MesaNet summary page (gist.science,
+paper 2506.05233), section "A Camada Mesa": the displayed objective, the
+output Delta_t = Phi_t q_t with q*_t = (H_t + Lambda)^-1 q_t solved by CG, and
+the bullet on dynamic computation (per-token iteration counts).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from test_regression_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def zeta(gamma, t):
+    """zeta_{t t'} for t' = 0..t (0-based) as explicit products of gammas."""
+    return np.array([np.prod(gamma[tp + 1:t + 1]) for tp in range(t + 1)])
+
+
+def brute_states(k, v, gamma, t):
+    """H_t, G_t straight from their definition as zeta-weighted sums."""
+    z = zeta(gamma, t)
+    Hm = sum(z[i] * np.outer(k[i], k[i]) for i in range(t + 1))
+    Gm = sum(z[i] * np.outer(v[i], k[i]) for i in range(t + 1))
+    return Hm, Gm
+
+
+def rand_problem(rng, T, dk, dv, glo=0.6, lam=None):
+    q = rng.standard_normal((1, 1, T, dk))
+    k = rng.standard_normal((1, 1, T, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((1, 1, T, dv))
+    g = rng.uniform(glo, 1.0, (1, 1, T))
+    lam = rng.uniform(0.3, 2.0, (1, dk)) if lam is None else lam
+    return q, k, v, g, lam
+
+
+def rel(a, b):
+    return np.linalg.norm(np.asarray(a) - np.asarray(b)) / max(np.linalg.norm(b), 1e-300)
+
+
+# --------------------------------------------------------------------------
+# golden hand-worked examples
+# --------------------------------------------------------------------------
+def test_hand_worked_examples():
+    with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    assert cases
+    for c in cases:
+        q = np.array(c["q"])[None, None]
+        k = np.array(c["k"])[None, None]
+        v = np.array(c["v"])[None, None]
+        g = np.array(c["gamma"])[None, None]
+        lam = np.array(c["lam"])[None]
+        res = oracle.forward(q, k, v, g, lam, c["max_iters"], 0.0)
+        exact = np.array([[float(Fraction(n, d)) for n, d in row] for row in c["out_num_den"]])
+        np.testing.assert_allclose(res["out"][0, 0], exact, rtol=1e-12, atol=1e-14, err_msg=c["name"])
+        np.testing.assert_allclose(exact, np.array(c["out"]), rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# P1: converged CG equals a Cholesky solve of (H_t + Lambda)
+# --------------------------------------------------------------------------
+def test_converged_matches_cholesky():
+    rng = np.random.default_rng(1)
+    T, dk, dv = 24, 6, 4
+    q, k, v, g, lam = rand_problem(rng, T, dk, dv)
+    res = oracle.forward(q, k, v, g, lam, max_iters=4 * dk, tol=1e-13)
+    for t in range(T):
+        Hm, Gm = brute_states(k[0, 0], v[0, 0], g[0, 0], t)
+        c = scipy.linalg.cho_factor(Hm + np.diag(lam[0]))
+        x = scipy.linalg.cho_solve(c, q[0, 0, t])
+        assert rel(res["out"][0, 0, t], Gm @ x) < 1e-10, t
+
+
+# --------------------------------------------------------------------------
+# P2: the objective itself, solved as weighted least squares
+# --------------------------------------------------------------------------
+def test_objective_least_squares_and_normal_equations():
+    rng = np.random.default_rng(2)
+    T, dk, dv = 15, 5, 3   # dk != dv: a transposed G cannot pass
+    q, k, v, g, lam = rand_problem(rng, T, dk, dv)
+    res = oracle.forward(q, k, v, g, lam, max_iters=6 * dk, tol=1e-14, final_state=True)
+    K, V, gam = k[0, 0], v[0, 0], g[0, 0]
+    for t in [0, 3, 7, T - 1]:
+        sz = np.sqrt(zeta(gam, t))
+        # minimise sum zeta |v - Phi k|^2 + Tr(Phi Lambda Phi^T) = |A Phi^T - Y|_F^2
+        A = np.vstack([sz[:, None] * K[:t + 1], np.diag(np.sqrt(lam[0]))])
+        Y = np.vstack([sz[:, None] * V[:t + 1], np.zeros((dk, dv))])
+        PhiT, *_ = np.linalg.lstsq(A, Y, rcond=None)
+        assert rel(res["out"][0, 0, t], PhiT.T @ q[0, 0, t]) < 1e-9, t
+    # zero gradient of the objective at the final token: Phi (H_T + Lambda) = G_T
+    sz = np.sqrt(zeta(gam, T - 1))
+    A = np.vstack([sz[:, None] * K, np.diag(np.sqrt(lam[0]))])
+    Y = np.vstack([sz[:, None] * V, np.zeros((dk, dv))])
+    PhiT, *_ = np.linalg.lstsq(A, Y, rcond=None)
+    Phi = PhiT.T
+    assert rel(Phi @ (res["final_H"][0, 0] + np.diag(lam[0])), res["final_G"][0, 0]) < 1e-10
+
+
+# --------------------------------------------------------------------------
+# P3: gamma == 1, Lambda = lam I  ->  kernel-ridge form (a t x t solve)
+# --------------------------------------------------------------------------
+def test_ridge_kernel_form_without_forgetting():
+    rng = np.random.default_rng(3)
+    T, dk, dv, lamv = 12, 7, 4, 0.7
+    q, k, v, _, _ = rand_problem(rng, T, dk, dv)
+    g = np.ones((1, 1, T))
+    lam = np.full((1, dk), lamv)
+    res = oracle.forward(q, k, v, g, lam, max_iters=4 * dk, tol=1e-14)
+    K, V = k[0, 0], v[0, 0]
+    for t in range(T):
+        Kt, Vt = K[:t + 1], V[:t + 1]
+        o = Vt.T @ np.linalg.solve(Kt @ Kt.T + lamv * np.eye(t + 1), Kt @ q[0, 0, t])
+        assert rel(res["out"][0, 0, t], o) < 1e-10, t
+
+
+# --------------------------------------------------------------------------
+# P4: first token, Sherman-Morrison; Lambda = lam I reached in two CG steps
+# --------------------------------------------------------------------------
+def test_first_token_sherman_morrison():
+    rng = np.random.default_rng(4)
+    dk, dv = 9, 5
+    for lam_iso in (True, False):
+        q, k, v, g, lam = rand_problem(rng, 3, dk, dv)
+        if lam_iso:
+            lam = np.full((1, dk), 1.3)
+        iters = 2 if lam_iso else 3 * dk
+        res = oracle.forward(q, k, v, g, lam, max_iters=iters, tol=0.0 if lam_iso else 1e-14)
+        k1, v1, q1, li = k[0, 0, 0], v[0, 0, 0], q[0, 0, 0], 1.0 / lam[0]
+        o1 = v1 * (k1 @ (li * q1)) / (1.0 + k1 @ (li * k1))
+        assert rel(res["out"][0, 0, 0], o1) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# P5: the k-step CG iterate is the A-orthogonal projection onto the Krylov
+#     space span{b, Ab, ..., A^{k-1} b} (exact rational arithmetic)
+# --------------------------------------------------------------------------
+def _frac_solve(M, y):
+    n = len(M)
+    M = [row[:] + [y[i]] for i, row in enumerate(M)]
+    for c in range(n):
+        p = next(r for r in range(c, n) if M[r][c] != 0)
+        M[c], M[p] = M[p], M[c]
+        for r in range(n):
+            if r != c and M[r][c] != 0:
+                f = M[r][c] / M[c][c]
+                M[r] = [a - f * b for a, b in zip(M[r], M[c])]
+    return [M[i][n] / M[i][i] for i in range(n)]
+
+
+def _krylov_iterate(A, b, kk):
+    n = len(b)
+    cols = [b]
+    for _ in range(kk - 1):
+        prev = cols[-1]
+        cols.append([sum(A[i][j] * prev[j] for j in range(n)) for i in range(n)])
+    AK = [[sum(A[i][j] * cols[c][j] for j in range(n)) for i in range(n)] for c in range(kk)]
+    KtAK = [[sum(cols[a][i] * AK[c][i] for i in range(n)) for c in range(kk)] for a in range(kk)]
+    Ktb = [sum(cols[a][i] * b[i] for i in range(n)) for a in range(kk)]
+    y = _frac_solve(KtAK, Ktb)
+    return [sum(cols[c][i] * y[c] for c in range(kk)) for i in range(n)]
+
+
+def test_k_step_iterate_is_krylov_projection():
+    rng = np.random.default_rng(5)
+    n = 5
+    for trial in range(3):
+        ints = rng.integers(-3, 4, size=(n + 2, n))
+        Hq = [[Fraction(int(sum(ints[r, i] * ints[r, j] for r in range(n + 2))), 4)
+               for j in range(n)] for i in range(n)]
+        lam = [Fraction(int(x), 2) for x in rng.integers(1, 6, size=n)]
+        b = [Fraction(int(x)) for x in rng.integers(-4, 5, size=n)]
+        if all(x == 0 for x in b):
+            b[0] = Fraction(1)
+        A = [[Hq[i][j] + (lam[i] if i == j else 0) for j in range(n)] for i in range(n)]
+        Hf = np.array([[float(x) for x in row] for row in Hq])
+        lf = np.array([float(x) for x in lam])
+        bf = np.array([float(x) for x in b])
+        for kk in range(1, n + 1):
+            exact = np.array([float(x) for x in _krylov_iterate(A, b, kk)])
+            x, it, *_ = oracle.cg_solve(Hf, lf, bf, kk, 0.0)
+            if it < kk:      # exact convergence before kk steps: iterate is A^-1 b
+                exact = np.array([float(x) for x in _frac_solve(A, b)])
+            assert rel(x, exact) < 1e-11, (trial, kk)
+
+
+# --------------------------------------------------------------------------
+# P6: finite termination on the tiny workload (Lambda = I, k = 10):
+#     H_t has rank <= t (1-based), so A_t has <= t+1 distinct eigenvalues and
+#     10 CG steps are exact for t <= 9.
+# --------------------------------------------------------------------------
+def test_finite_termination_tiny_workload():
+    w = inputs.WORKLOADS["tiny_f32_d16_T256"]
+    x = inputs.forward_inputs(w, T=12)
+    q, k, v = (inputs.as_f64(x[n], w.dtype) for n in ("q", "k", "v"))
+    g, lam = x["gamma"].astype(np.float64), x["lam"].astype(np.float64)
+    assert np.all(lam == 1.0)
+    res = oracle.forward(q, k, v, g, lam, w.max_iters, 0.0)
+    for t in range(9):
+        Hm, Gm = brute_states(k[0, 0], v[0, 0], g[0, 0], t)
+        xs = scipy.linalg.solve(Hm + np.eye(w.d), q[0, 0, t], assume_a="pos")
+        assert rel(res["out"][0, 0, t], Gm @ xs) < 1e-12, t
+    # a later token is NOT exact after 10 steps (the pin has teeth)
+    t = 11
+    Hm, Gm = brute_states(k[0, 0], v[0, 0], g[0, 0], t)
+    xs = scipy.linalg.solve(Hm + np.eye(w.d), q[0, 0, t], assume_a="pos")
+    assert rel(res["out"][0, 0, t], Gm @ xs) > 1e-12
+
+
+# --------------------------------------------------------------------------
+# P7: d = 1 closed form
+# --------------------------------------------------------------------------
+def test_scalar_closed_form():
+    rng = np.random.default_rng(7)
+    T = 30
+    q, k, v, g, lam = rand_problem(rng, T, 1, 1)
+    res = oracle.forward(q, k, v, g, lam, max_iters=1, tol=0.0)
+    K, V, gam = k[0, 0, :, 0], v[0, 0, :, 0], g[0, 0]
+    for t in range(T):
+        z = zeta(gam, t)
+        o = q[0, 0, t, 0] * np.sum(z * V[:t + 1] * K[:t + 1]) / (np.sum(z * K[:t + 1] ** 2) + lam[0, 0])
+        assert abs(res["out"][0, 0, t, 0] - o) <= 1e-13 * max(1.0, abs(o)), t
+
+
+# --------------------------------------------------------------------------
+# P8: dynamic stopping bookkeeping, with residuals recomputed from the
+#     definition (q - A x_j, A built from explicit zeta sums)
+# --------------------------------------------------------------------------
+def test_dynamic_stop_matches_true_residuals():
+    rng = np.random.default_rng(8)
+    T, dk, dv, tol, cap = 40, 12, 6, 1e-3, 9
+    q, k, v, g, lam = rand_problem(rng, T, dk, dv, glo=0.9)
+    res = oracle.forward(q, k, v, g, lam, max_iters=cap, tol=tol)
+    checked = 0
+    for t in range(T):
+        n = int(res["iters"][0, 0, t])
+        Hm, _ = brute_states(k[0, 0], v[0, 0], g[0, 0], t)
+        A = Hm + np.diag(lam[0])
+        qt = q[0, 0, t]
+
+        def rho(j):
+            x, *_ = oracle.cg_solve(Hm, lam[0], qt, j, 0.0)
+            return np.linalg.norm(qt - A @ x) / np.linalg.norm(qt)
+        rhos = [rho(j) for j in range(n + 1)]
+        if any(abs(r / tol - 1.0) < 1e-9 for r in rhos):
+            continue
+        assert all(r >= tol for r in rhos[:n]), t
+        if n < cap:
+            assert res["reason"][0, 0, t] == oracle.STOP_TOL
+            assert rhos[n] < tol, t
+        else:
+            assert res["reason"][0, 0, t] == oracle.STOP_CAP
+        assert abs(res["rho_stop"][0, 0, t] - rhos[n]) <= 1e-9 * max(rhos[n], 1e-12) + 1e-13
+        checked += 1
+    assert checked >= T - 2
+    assert len(set(res["iters"][0, 0].tolist())) > 1   # counts do vary per token
+
+
+# --------------------------------------------------------------------------
+# P9: count bound for Lambda = lam I:  iters_t <= t + 1 (1-based t)
+# --------------------------------------------------------------------------
+def test_iteration_count_bound_isotropic():
+    rng = np.random.default_rng(9)
+    T, dk, dv = 20, 16, 4
+    q, k, v, g, _ = rand_problem(rng, T, dk, dv, glo=0.9)
+    lam = np.full((1, dk), 0.8)
+    res = oracle.forward(q, k, v, g, lam, max_iters=40, tol=1e-10)
+    it = res["iters"][0, 0]
+    for t in range(T):
+        assert it[t] <= t + 2, (t, it[t])     # 0-based t: rank <= t+1
+    assert it[0] <= 2 and it[T - 1] > 2
+
+
+# --------------------------------------------------------------------------
+# P10: CG internals -- residuals mutually orthogonal, A-norm error decreasing
+# --------------------------------------------------------------------------
+def test_cg_residual_orthogonality_and_energy_decrease():
+    rng = np.random.default_rng(10)
+    n = 24
+    M = rng.standard_normal((2 * n, n)) / np.sqrt(n)
+    Hm = M.T @ M
+    lam = rng.uniform(0.2, 1.0, n)
+    A = Hm + np.diag(lam)
+    b = rng.standard_normal(n)
+    xs = np.linalg.solve(A, b)
+    res, errs = [], []
+    for j in range(8):
+        x, *_ = oracle.cg_solve(Hm, lam, b, j, 0.0)
+        res.append(b - A @ x)
+        e = xs - x
+        errs.append(np.sqrt(e @ A @ e))
+    for i in range(8):
+        for j in range(i):
+            c = res[i] @ res[j] / (np.linalg.norm(res[i]) * np.linalg.norm(res[j]))
+            assert abs(c) < 1e-8, (i, j, c)
+    assert all(errs[j + 1] < errs[j] for j in range(7))
+
+
+# --------------------------------------------------------------------------
+# internal consistency: decode continues the forward recurrence; selecting
+# tokens does not change them; zero query -> zero output and count
+# --------------------------------------------------------------------------
+def test_decode_continues_forward():
+    rng = np.random.default_rng(11)
+    T, S, dk, dv, cap, tol = 30, 5, 8, 8, 12, 1e-6
+    q, k, v, g, lam = rand_problem(rng, T, dk, dv, glo=0.8)
+    full = oracle.forward(q, k, v, g, lam, cap, tol)
+    pre = oracle.forward(q[:, :, :T - S], k[:, :, :T - S], v[:, :, :T - S], g[:, :, :T - S],
+                         lam, cap, tol, final_state=True)
+    Hs, Gs = pre["final_H"][:, :].copy(), pre["final_G"][:, :].copy()
+    for s in range(T - S, T):
+        r = oracle.decode_step(q[:, :, s], k[:, :, s], v[:, :, s], g[:, :, s], lam, Hs, Gs, cap, tol)
+        np.testing.assert_allclose(r["out"][0, 0], full["out"][0, 0, s], rtol=1e-12, atol=1e-13)
+        assert r["iters"][0, 0] == full["iters"][0, 0, s]
+
+
+def test_want_mask_and_zero_query():
+    rng = np.random.default_rng(12)
+    T, dk, dv = 25, 6, 6
+    q, k, v, g, lam = rand_problem(rng, T, dk, dv)
+    q[0, 0, 4] = 0.0
+    full = oracle.forward(q, k, v, g, lam, 7, 1e-5)
+    want = np.zeros((1, 1, T), bool)
+    want[0, 0, [2, 4, 20]] = True
+    part = oracle.forward(q, k, v, g, lam, 7, 1e-5, want=want)
+    for t in [2, 4, 20]:
+        np.testing.assert_array_equal(part["out"][0, 0, t], full["out"][0, 0, t])
+    assert np.isnan(part["out"][0, 0, 3]).all()
+    assert full["iters"][0, 0, 4] == 0 and np.all(full["out"][0, 0, 4] == 0)
+    assert full["reason"][0, 0, 4] == oracle.STOP_Q_ZERO
+
+
+def test_generator_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(13).standard_normal(100000).astype(np.float32)
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, 3.0e38]   # ties to even, sign, large
+    ours = inputs.bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(inputs.bf16_bits_to_f32(ours),
+                                  torch.from_numpy(x).to(torch.bfloat16).float().numpy())
