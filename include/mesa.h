@@ -1,0 +1,161 @@
+/*
+ * mesa.h -- C ABI of the MI355X (gfx950) Mesa-layer library (libmesa.so).
+ *
+ * The operation is the Mesa layer of the MesaNet summary page
+ * (gist.science, paper 2506.05233), section "A Camada Mesa":
+ *   - displayed objective: Phi_t = argmin 1/2 sum_{t'<=t} zeta_{tt'}
+ *     |v_t' - Phi k_t'|^2 + 1/2 Tr(Phi Lambda Phi^T), zeta_{tt'} the cumulative
+ *     forget factors, Lambda symmetric positive definite;
+ *   - output Delta_t = Phi_t q_t = G_t q*_t, q*_t = (H_t + Lambda)^{-1} q_t,
+ *     solved by Conjugate Gradient;
+ *   - bullet "Paralelizacao": CG over all time steps is a gated-linear-attention
+ *     pass, run chunk-parallel with the states H_t, G_t (O(T) forward, O(1)
+ *     per decoded token);
+ *   - bullet "Computacao Dinamica": the CG iteration count needed to meet a
+ *     stopping criterion varies per token.
+ *
+ * Concretely, per batch row b, head h and token t (readings of the page):
+ *   H_t = gamma_t H_{t-1} + k_t k_t^T,  G_t = gamma_t G_{t-1} + v_t k_t^T,
+ *   H_0 = G_0 = 0  (i.e. zeta_{tt'} = prod_{s=t'+1..t} gamma_s);
+ *   Lambda = diag(lambda[h, :]);
+ *   x = CG on (H_t + Lambda) x = q_t from x0 = 0, at most max_iters updates;
+ *       when tol > 0 a token stops before an update once
+ *       |r|_2 / |q_t|_2 < tol (r the recursively updated residual);
+ *       tol == 0 makes exactly max_iters updates; r^T r == 0 or p^T A p <= 0
+ *       also stop; q_t == 0 gives x = 0 and 0 iterations;
+ *   out_t = G_t x,  iters_t = number of CG updates made.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory),
+ *     contiguous row-major, 16-byte aligned.  The caller owns every buffer;
+ *     the library allocates nothing and keeps no state between calls, except
+ *     the optional profiling records below.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Results are valid once the caller synchronises.
+ *   - All arguments are validated on the host before anything is enqueued;
+ *     on error nothing is enqueued.  Device data preconditions (0 < gamma <= 1,
+ *     lambda > 0, finite inputs) are documented, not checked.
+ *   - Outputs must not alias inputs.  Nothing aborts; no C++ exception
+ *     crosses the ABI.  Errors return a mesa_status; the thread-local text
+ *     from mesa_last_error_message() says which argument was wrong.
+ *   - Supported sizes: d_k == d_v in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ *     any T >= 0 (a ragged last chunk is handled); 0 <= max_iters <= 4096.
+ */
+#ifndef MESA_H
+#define MESA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MESA_ABI_VERSION 1
+
+typedef enum {
+    MESA_OK = 0,
+    MESA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, tol < 0 or NaN, misaligned */
+    MESA_ERR_UNSUPPORTED = 2,        /* valid but not built: d, chunk or d_k != d_v      */
+    MESA_ERR_WORKSPACE_TOO_SMALL = 3,
+    MESA_ERR_HIP = 4                 /* a HIP runtime call failed (text in the message)  */
+} mesa_status;
+
+typedef enum {
+    MESA_DTYPE_F32 = 0,              /* q, k, v stored as float32                        */
+    MESA_DTYPE_BF16 = 1              /* q, k, v stored as bfloat16; all math in fp32     */
+} mesa_dtype;
+
+/* Kernel ids for the optional profiling records. */
+typedef enum {
+    MESA_KERNEL_CHUNK_STATES = 0,    /* chunk-boundary states S^H_c, S^G_c (+ final)     */
+    MESA_KERNEL_CG_OUTPUT = 1,       /* all CG iterations of a chunk + output contraction */
+    MESA_KERNEL_DECODE = 2,          /* one recurrent decode step                        */
+    MESA_KERNEL_COUNT = 3
+} mesa_kernel_id;
+
+/* Library ABI version (MESA_ABI_VERSION of the build). */
+int mesa_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *mesa_status_string(int status);
+
+/* Thread-local detail about the last error returned on this thread ("" if none). */
+const char *mesa_last_error_message(void);
+
+/*
+ * Bytes of device workspace mesa_forward needs for these sizes: the
+ * chunk-boundary states S^H_c = H_{c*chunk-1} and S^G_c (fp32, d*d each per
+ * chunk and head).  Returns 0 if the sizes are invalid.
+ */
+size_t mesa_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/*
+ * Mesa-layer forward over a whole sequence (the "Paralelizacao" bullet:
+ * chunkwise-parallel CG; every CG matvec over all t is one gated-linear-
+ * attention pass with query p and key = value = k).
+ *
+ *   q, k      [B, H, T, dk]   qkv_dtype
+ *   v         [B, H, T, dv]   qkv_dtype
+ *   gamma     [B, H, T]       float32, 0 < gamma <= 1 (gamma at the first
+ *                             token has no effect: H_0 = 0)
+ *   lambda    [H, dk]         float32, lambda > 0 (shared over the batch)
+ *   chunk                     GPU chunk length; results do not depend on it
+ *                             beyond rounding
+ *   max_iters, tol            CG cap and residual tolerance (see top)
+ *   out       [B, H, T, dv]   float32, written
+ *   iters     [B, H, T]       int32 CG update counts, or NULL
+ *   final_H   [B, H, dk, dk]  float32 H_T, or NULL   (prefill -> decode
+ *   final_G   [B, H, dv, dk]  float32 G_T, or NULL    hand-off)
+ *   workspace, workspace_bytes  at least mesa_forward_workspace_bytes(...);
+ *                             may be NULL/0 when max_iters == 0
+ *   stream                    hipStream_t or NULL
+ */
+mesa_status mesa_forward(const void *q, const void *k, const void *v, int qkv_dtype,
+                         const float *gamma, const float *lambda,
+                         int B, int H, int T, int dk, int dv, int chunk,
+                         int max_iters, float tol,
+                         float *out, int32_t *iters, float *final_H, float *final_G,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for N x H independent heads (the "Paralelizacao"
+ * bullet: O(1) per-token inference on the states H_t, G_t; "Computacao
+ * Dinamica": per-head dynamic stopping).  For each (n, h):
+ *   H <- gamma H + k k^T;  G <- gamma G + v k^T   (in place)
+ *   x  = CG on (H + diag lambda[h]) x = q  (max_iters, tol as above)
+ *   out = G x
+ *
+ *   q, k      [N, H, dk]      qkv_dtype
+ *   v         [N, H, dv]      qkv_dtype
+ *   gamma     [N, H]          float32
+ *   lambda    [H, dk]         float32
+ *   state_H   [N, H, dk, dk]  float32, read and overwritten
+ *   state_G   [N, H, dv, dk]  float32, read and overwritten
+ *   out       [N, H, dv]      float32, written
+ *   iters     [N, H]          int32, or NULL
+ */
+mesa_status mesa_decode_step(const void *q, const void *k, const void *v, int qkv_dtype,
+                             const float *gamma, const float *lambda,
+                             float *state_H, float *state_G,
+                             int N, int H, int dk, int dv, int max_iters, float tol,
+                             float *out, int32_t *iters, void *stream);
+
+/*
+ * Optional per-kernel timing (not part of the method).  While enabled, each
+ * kernel launch made by the library is bracketed by two hipEvents recorded on
+ * its stream.  mesa_profile_read synchronises on the recorded events, returns
+ * the summed milliseconds and launch count for one kernel id since the last
+ * reset, and mesa_profile_reset drops all records.  Records are process-wide
+ * and guarded by a mutex.
+ */
+mesa_status mesa_profile_enable(int on);
+mesa_status mesa_profile_read(int kernel_id, double *total_ms, int64_t *launches);
+mesa_status mesa_profile_reset(void);
+const char *mesa_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MESA_H */

@@ -1,0 +1,170 @@
+// chunk_states.hip -- chunk-boundary states of the Mesa layer (gfx950).
+//
+// MesaNet summary page (gist.science, paper 2506.05233), section "A Camada
+// Mesa", bullet "Paralelizacao": the layer keeps the state variables H_t and
+// G_t and solves chunks of the sequence in parallel.  With the forget factors
+// zeta_{tt'} = prod_{s=t'+1..t} gamma_s the states obey
+//   H_t = gamma_t H_{t-1} + k_t k_t^T,   G_t = gamma_t G_{t-1} + v_t k_t^T.
+// Over a chunk c of C tokens with within-chunk log decays l_i (prefix sums of
+// ln gamma) this is
+//   S_{c+1} = e^{l_end} S_c + sum_{i in c} e^{l_end - l_i} a_i k_i^T,
+// a = k for H and a = v for G, S_0 = 0.  This kernel produces S_c for every
+// chunk (the state before the chunk's first token) and, optionally, the final
+// state after the last token.
+//
+// The G states are produced transposed (G^T, [d_k][d_v]) in the workspace,
+// which is the layout the output contraction reads; the exported final G is
+// written in the [d_v][d_k] layout of the ABI.
+//
+// Work split: one workgroup per (head, {H, G^T}, 16*NW-row block of the
+// state); each wave holds a 16 x D slab of the running state in MFMA
+// accumulator layout and walks the chunks in order.  Per chunk the update is
+// one (16 x C) x (C x D) product on v_mfma_f32_16x16x4_f32 with the weighted
+// keys as the A operand: rows of the state are key features, the contraction
+// runs over the chunk's tokens.
+#include "mesa_device.h"
+#include "mesa_kernels.h"
+
+namespace mesa {
+
+template <int D, int C, typename In>
+__global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
+    int T, int n_chunks, float* __restrict__ SH, float* __restrict__ SGt,
+    float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks) {
+    constexpr int NW = D >= 64 ? 4 : D / 16;   // waves per workgroup
+    constexpr int RB = D / (16 * NW);          // row blocks per state
+    constexpr int NT = D / 16;                 // 16-column tiles of the state
+    constexpr int PD = lds_pitch(D);
+    constexpr int NTHR = 64 * NW;
+
+    __shared__ float sK[C * PD];   // keys of the chunk (A rows and, for H, B)
+    __shared__ float sB[C * PD];   // values of the chunk (B for G^T)
+    __shared__ float sW[C];        // e^{l_end - l_i}
+    __shared__ float sGam;         // e^{l_end}
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int n = lane & 15;
+    const int kk = lane >> 4;
+
+    const int bid = blockIdx.x;
+    const int rb = bid % RB;
+    const int which = (bid / RB) & 1;          // 0: H, 1: G^T
+    const long bh = bid / (2 * RB);
+    const int m0 = rb * 16 * NW + 16 * w;      // first state row of this wave
+
+    const In* kh = k + (size_t)bh * T * D;
+    const In* vh = v + (size_t)bh * T * D;
+    const float* gh = gamma + (size_t)bh * T;
+    float* Sout = (which == 0 ? SH : SGt) + (size_t)bh * n_chunks * D * D;
+    float* sBuse = which == 0 ? sK : sB;
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = 0; c < n_chunks; ++c) {
+        const int t0 = c * C;
+        const int valid = min(C, T - t0);
+        // ---- stage the chunk's keys (and values) in LDS as fp32 ----
+        for (int e = tid * 4; e < C * D; e += NTHR * 4) {
+            const int i = e / D, f = e % D;
+            f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = x;
+            if (i < valid) {
+                x = load4(kh + (size_t)(t0 + i) * D + f);
+                if (which) y = load4(vh + (size_t)(t0 + i) * D + f);
+            }
+            *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = x;
+            if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = y;
+        }
+        if (w == 0) {
+            const float l = chunk_log_decay(gh + t0, valid, lane);
+            const float lend = __shfl(l, C - 1, 64);
+            if (lane < C) sW[lane] = __expf(lend - l);
+            if (lane == 0) sGam = __expf(lend);
+        }
+        __syncthreads();
+
+        // ---- the state before this chunk ----
+        if (write_chunks) {
+            float* dst = Sout + (size_t)c * D * D;
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+        }
+
+        // ---- S <- Gamma_c S + sum_i w_i k_i b_i^T ----
+        const float G = sGam;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] *= G;
+#pragma unroll
+        for (int g = 0; g < C / 16; ++g) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int i = 16 * g + 4 * kk + s;
+                const float a = sK[i * PD + m0 + n] * sW[i];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[j] = mfma4(a, sBuse[i * PD + 16 * j + n], acc[j]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- final state (after the last token) ----
+    if (which == 0 && final_H) {
+        float* dst = final_H + (size_t)bh * D * D;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+    }
+    if (which == 1 && final_G) {   // acc holds G^T[key feature][value feature]
+        float* dst = final_G + (size_t)bh * D * D;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(size_t)(16 * j + n) * D + m0 + 4 * kk + r] = acc[j][r];
+    }
+}
+
+template <int D, int C, typename In>
+hipError_t launch_chunk_states_t(const ChunkStatesArgs& a, hipStream_t s) {
+    constexpr int NW = D >= 64 ? 4 : D / 16;
+    constexpr int RB = D / (16 * NW);
+    const long grid = (long)a.BH * 2 * RB;
+    hipLaunchKernelGGL((chunk_states_kernel<D, C, In>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+                       (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SGt,
+                       a.final_H, a.final_G, a.write_chunks);
+    return hipGetLastError();
+}
+
+template <int D, typename In>
+static hipError_t dispatch_c(const ChunkStatesArgs& a, hipStream_t s) {
+    switch (a.chunk) {
+        case 16: return launch_chunk_states_t<D, 16, In>(a, s);
+        case 32: return launch_chunk_states_t<D, 32, In>(a, s);
+        case 64: return launch_chunk_states_t<D, 64, In>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename In>
+static hipError_t dispatch_d(const ChunkStatesArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 16: return dispatch_c<16, In>(a, s);
+        case 32: return dispatch_c<32, In>(a, s);
+        case 64: return dispatch_c<64, In>(a, s);
+        case 128: return dispatch_c<128, In>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_states(const ChunkStatesArgs& a, hipStream_t s) {
+    return a.bf16 ? dispatch_d<bf16_t>(a, s) : dispatch_d<float>(a, s);
+}
+
+}  // namespace mesa

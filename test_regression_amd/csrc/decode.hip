@@ -1,0 +1,167 @@
+// decode.hip -- one recurrent decode step of the Mesa layer (gfx950).
+//
+// MesaNet summary page (gist.science, paper 2506.05233), section "A Camada
+// Mesa", bullet "Paralelizacao": inference costs O(1) per token on the state
+// variables H_t, G_t; bullet "Computacao Dinamica": the number of CG
+// iterations needed to meet the stopping criterion varies per token.  One
+// step, per head:
+//   H <- gamma H + k k^T,  G <- gamma G + v k^T   (in place)
+//   x  = CG on (H + diag lambda) x = q from x0 = 0
+//   out = G x
+//
+// Work split: one 256-thread workgroup per head.  Thread (row, part) keeps
+// D/TPR consecutive entries of one row of H in registers for the whole solve,
+// so H is read once and written once; the matvec reads p from LDS.  The CG
+// scalars are block reductions with a fixed order (deterministic), and the
+// stop test is block-uniform.  The step is bound by HBM traffic on the two
+// d x d states (read + write of H and G).
+#include "mesa_device.h"
+#include "mesa_kernels.h"
+
+namespace mesa {
+
+template <int D, typename In>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+    const float* __restrict__ gamma, const float* __restrict__ lambda, float* __restrict__ SH,
+    float* __restrict__ SG, int H, int max_iters, float tol, float* __restrict__ out,
+    int32_t* __restrict__ iters) {
+    constexpr int TPR = 256 / D;   // threads per state row
+    constexpr int EPT = D / TPR;   // state entries per thread
+    __shared__ float sq[D], sk[D], sv[D], sp[D], sx[D];
+    __shared__ float red[2][4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const long nh = blockIdx.x;
+    const int h = (int)(nh % H);
+    const int row = tid / TPR;
+    const int part = tid % TPR;
+    const int c0 = part * EPT;
+
+    if (tid < D) {
+        sq[tid] = to_f32(q[nh * D + tid]);
+        sk[tid] = to_f32(k[nh * D + tid]);
+        sv[tid] = to_f32(v[nh * D + tid]);
+    }
+    const float g = gamma[nh];
+    const float lam_r = lambda[(size_t)h * D + row];
+    __syncthreads();
+
+    // Block-wide sum with a fixed reduction order; slot alternates so that a
+    // fast thread's next write cannot race a slow thread's read.
+    auto block_sum = [&](float val, int slot) {
+        val = wavesum(val);
+        if (lane == 0) red[slot][wv] = val;
+        __syncthreads();
+        return (red[slot][0] + red[slot][1]) + (red[slot][2] + red[slot][3]);
+    };
+    auto row_sum = [&](float val) {
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) val += __shfl_xor(val, o, 64);
+        return val;
+    };
+
+    // ---- H <- gamma H + k k^T, kept in registers ----
+    float hr[EPT];
+    float* Hrow = SH + (size_t)nh * D * D + (size_t)row * D + c0;
+    const float kr = sk[row];
+    if constexpr (EPT % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+            f32x4 x = *reinterpret_cast<const f32x4*>(Hrow + e);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) hr[e + u] = g * x[u] + kr * sk[c0 + e + u];
+            *reinterpret_cast<f32x4*>(Hrow + e) = f32x4{hr[e], hr[e + 1], hr[e + 2], hr[e + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            hr[e] = g * Hrow[e] + kr * sk[c0 + e];
+            Hrow[e] = hr[e];
+        }
+    }
+
+    // ---- CG on (H + diag lambda) x = q from x = 0 ----
+    float x_r = 0.f, r_r = sq[row], p_r = r_r;
+    float rr = block_sum(part == 0 ? r_r * r_r : 0.f, 0);
+    const float nq = sqrtf(rr);
+    if (tid < D) sp[tid] = sq[tid];
+    __syncthreads();
+    int it = 0;
+    while (it < max_iters) {
+        if ((tol > 0.f && sqrtf(rr) / nq < tol) || rr == 0.f) break;
+        float y = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) y += hr[e] * sp[c0 + e];
+        y = row_sum(y) + lam_r * p_r;
+        const float pap = block_sum(part == 0 ? p_r * y : 0.f, 1);
+        if (!(pap > 0.f)) break;
+        const float alpha = rr / pap;
+        x_r += alpha * p_r;
+        r_r -= alpha * y;
+        const float rrn = block_sum(part == 0 ? r_r * r_r : 0.f, 0);
+        const float beta = rrn / rr;
+        p_r = r_r + beta * p_r;
+        rr = rrn;
+        ++it;
+        if (part == 0) sp[row] = p_r;
+        __syncthreads();
+    }
+    if (part == 0) sx[row] = x_r;
+    __syncthreads();
+
+    // ---- G <- gamma G + v k^T (in place), out = G x ----
+    float* Grow = SG + (size_t)nh * D * D + (size_t)row * D + c0;
+    const float vr = sv[row];
+    float o = 0.f;
+    if constexpr (EPT % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+            f32x4 x = *reinterpret_cast<const f32x4*>(Grow + e);
+            f32x4 y;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                y[u] = g * x[u] + vr * sk[c0 + e + u];
+                o += y[u] * sx[c0 + e + u];
+            }
+            *reinterpret_cast<f32x4*>(Grow + e) = y;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const float y = g * Grow[e] + vr * sk[c0 + e];
+            Grow[e] = y;
+            o += y * sx[c0 + e];
+        }
+    }
+    o = row_sum(o);
+    if (part == 0) out[nh * D + row] = o;
+    if (tid == 0 && iters) iters[nh] = it;
+}
+
+template <int D, typename In>
+static hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((decode_kernel<D, In>), dim3((unsigned)a.NH), dim3(256), 0, s, (const In*)a.q,
+                       (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.SH, a.SG, a.H, a.max_iters,
+                       a.tol, a.out, a.iters);
+    return hipGetLastError();
+}
+
+template <typename In>
+static hipError_t dispatch_d(const DecodeArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 16: return launch_t<16, In>(a, s);
+        case 32: return launch_t<32, In>(a, s);
+        case 64: return launch_t<64, In>(a, s);
+        case 128: return launch_t<128, In>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+    return a.bf16 ? dispatch_d<bf16_t>(a, s) : dispatch_d<float>(a, s);
+}
+
+}  // namespace mesa

@@ -1,0 +1,92 @@
+// mesa_device.h -- device helpers shared by the gfx950 Mesa-layer kernels.
+//
+// Wave64 only.  MFMA layout used throughout (v_mfma_f32_16x16x4_f32, one
+// block of 16x16 outputs per instruction): lane l = 16*kk + n holds
+//   A operand : A[m = n][k-slot kk]        (one fp32)
+//   B operand : B[k-slot kk][col = n]      (one fp32)
+//   C/D       : C[row = 4*kk + r][col = n] for r = 0..3 (four fp32)
+// The mapping of the 4 k-slots to actual contraction indices is free as long
+// as A and B agree; the kernels use k = 16*g + 4*kk + s for sub-step s of
+// group g, so that a lane's four A values are contiguous (one 128-bit LDS
+// read feeds four MFMAs).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mesa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// LDS row pitch (floats): the row length rounded up to 64 plus 4, so that the
+// access patterns of the MFMA operand loads are free of bank conflicts.
+__host__ __device__ constexpr int lds_pitch(int n) { return ((n + 63) / 64) * 64 + 4; }
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 stored as raw 16-bit patterns.
+struct bf16_t { uint16_t bits; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+
+// Load 4 consecutive elements (16-byte aligned for float, 8-byte for bf16).
+__device__ __forceinline__ f32x4 load4(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ f32x4 load4(const bf16_t* p) {
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    f32x4 r;
+    r[0] = __uint_as_float(u.x << 16);
+    r[1] = __uint_as_float(u.x & 0xffff0000u);
+    r[2] = __uint_as_float(u.y << 16);
+    r[3] = __uint_as_float(u.y & 0xffff0000u);
+    return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a DPP row (lanes 16*kk .. 16*kk+15), i.e. over the
+// MFMA column index n.  Every lane of the row gets the same, bit-identical
+// value (each step adds two commuted operands).
+__device__ __forceinline__ float rowsum16(float v) {
+    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);   // row_half_mirror
+    v += dpp<0x140>(v);   // row_mirror
+    return v;
+}
+
+// Sum over all 64 lanes (butterfly; every lane gets the same value).
+__device__ __forceinline__ float wavesum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Orders this wave's earlier LDS accesses before its later ones (the kernels
+// pass data between lanes of one wave through LDS without a block barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Within-chunk log decays.  Lane i < len gets l_i = sum_{s<=i} ln(gamma_s) of
+// the chunk's tokens (tokens past the sequence end count as gamma = 1).
+// Must be called by a whole wave.
+__device__ __forceinline__ float chunk_log_decay(const float* gamma_chunk, int valid, int lane) {
+    float x = (lane < valid) ? __logf(gamma_chunk[lane]) : 0.0f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        float t = __shfl_up(x, o, 64);
+        if (lane >= o) x += t;
+    }
+    return x;
+}
+
+}  // namespace mesa

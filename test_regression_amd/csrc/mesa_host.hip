@@ -1,0 +1,269 @@
+// mesa_host.hip -- the C ABI of libmesa (declared in include/mesa.h).
+//
+// Host-side only: validates every argument before anything is enqueued,
+// carves the caller's workspace, and enqueues the kernels on the caller's
+// stream.  Allocates no device memory and never synchronises (except in
+// mesa_profile_read, which waits for its own events).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mesa.h"
+#include "mesa_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+mesa_status fail(mesa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+mesa_status hip_fail(hipError_t e, const char* what) {
+    return fail(MESA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+
+constexpr int kMaxIters = 4096;
+
+// ---------------- optional per-kernel timing ----------------
+struct ProfRec { hipEvent_t a, b; int kid; };
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pending;
+double g_prof_ms[MESA_KERNEL_COUNT] = {0, 0, 0};
+int64_t g_prof_n[MESA_KERNEL_COUNT] = {0, 0, 0};
+
+// Launches `fn` on `s`; when profiling is on, brackets it with two events.
+template <typename Fn>
+hipError_t timed_launch(int kid, hipStream_t s, Fn fn) {
+    bool on;
+    {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        on = g_prof_on;
+    }
+    if (!on) return fn();
+    ProfRec r{nullptr, nullptr, kid};
+    hipError_t e = hipEventCreate(&r.a);
+    if (e != hipSuccess) return e;
+    e = hipEventCreate(&r.b);
+    if (e == hipSuccess) e = hipEventRecord(r.a, s);
+    if (e == hipSuccess) e = fn();
+    if (e == hipSuccess) e = hipEventRecord(r.b, s);
+    if (e != hipSuccess) {
+        (void)hipEventDestroy(r.a);
+        if (r.b) (void)hipEventDestroy(r.b);
+        return e;
+    }
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_pending.push_back(r);
+    return hipSuccess;
+}
+
+// Zero-fill with a kernel rather than hipMemsetAsync, so that a caller may
+// capture the call in a HIP graph.
+__global__ void zero_fill_kernel(uint32_t* p, size_t n_words) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+hipError_t zero_fill(void* p, size_t bytes, hipStream_t s) {
+    if (!p || bytes == 0) return hipSuccess;
+    const size_t words = bytes / 4;   // every buffer filled here is 4-byte elements
+    const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t*>(p), words);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mesa_abi_version(void) { return MESA_ABI_VERSION; }
+
+const char* mesa_status_string(int s) {
+    switch (s) {
+        case MESA_OK: return "MESA_OK";
+        case MESA_ERR_INVALID_ARGUMENT: return "MESA_ERR_INVALID_ARGUMENT";
+        case MESA_ERR_UNSUPPORTED: return "MESA_ERR_UNSUPPORTED";
+        case MESA_ERR_WORKSPACE_TOO_SMALL: return "MESA_ERR_WORKSPACE_TOO_SMALL";
+        case MESA_ERR_HIP: return "MESA_ERR_HIP";
+    }
+    return "MESA_ERR_UNKNOWN";
+}
+
+const char* mesa_last_error_message(void) { return g_err.c_str(); }
+
+size_t mesa_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+    const size_t nc = ((size_t)T + chunk - 1) / chunk;
+    return (size_t)B * H * nc * ((size_t)dk * dk + (size_t)dv * dk) * sizeof(float);
+}
+
+mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dtype,
+                         const float* gamma, const float* lambda, int B, int H, int T, int dk,
+                         int dv, int chunk, int max_iters, float tol, float* out, int32_t* iters,
+                         float* final_H, float* final_G, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    g_err.clear();
+    if (qkv_dtype != MESA_DTYPE_F32 && qkv_dtype != MESA_DTYPE_BF16)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "qkv_dtype %d is not MESA_DTYPE_F32 or MESA_DTYPE_BF16", qkv_dtype);
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d H=%d T=%d dk=%d dv=%d chunk=%d)",
+                    B, H, T, dk, dv, chunk);
+    if (max_iters < 0 || max_iters > kMaxIters)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "max_iters=%d outside [0, %d]", max_iters, kMaxIters);
+    if (!(tol >= 0.0f) || std::isinf(tol))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "tol must be finite and >= 0");
+    const bool need_ws = max_iters > 0 && T > 0;
+    if (T > 0 && (!q || !k || !v || !gamma || !out))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "q, k, v, gamma and out must be non-null");
+    if (!lambda) return fail(MESA_ERR_INVALID_ARGUMENT, "lambda must be non-null");
+    if (need_ws && !workspace) return fail(MESA_ERR_INVALID_ARGUMENT, "workspace must be non-null when max_iters > 0");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(final_H, 16) || !aligned(final_G, 16) || !aligned(workspace, 16) ||
+        !aligned(gamma, 4) || !aligned(lambda, 4) || !aligned(iters, 4))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "misaligned pointer (16 B for tensors/workspace, 4 B for gamma/lambda/iters)");
+    if (dk != dv) return fail(MESA_ERR_UNSUPPORTED, "dk (%d) != dv (%d) is not built", dk, dv);
+    if (!supported_d(dk)) return fail(MESA_ERR_UNSUPPORTED, "d=%d not built (16, 32, 64, 128)", dk);
+    if (!supported_chunk(chunk)) return fail(MESA_ERR_UNSUPPORTED, "chunk=%d not built (16, 32, 64)", chunk);
+    const long n_chunks = ((long)T + chunk - 1) / chunk;
+    const long BH = (long)B * H;
+    if (BH * 4 > 0x7fffffffL || BH * n_chunks > 0x7fffffffL)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "grid too large (B*H=%ld, chunks=%ld)", BH, n_chunks);
+    if (need_ws) {
+        const size_t need = mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk);
+        if (workspace_bytes < need)
+            return fail(MESA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int bf16 = qkv_dtype == MESA_DTYPE_BF16;
+    float* SH = static_cast<float*>(workspace);
+    float* SGt = need_ws ? SH + (size_t)BH * n_chunks * dk * dk : nullptr;
+
+    if (T == 0) {
+        // Nothing to solve; the final states are the zero initial states.
+        hipError_t e = zero_fill(final_H, (size_t)BH * dk * dk * sizeof(float), s);
+        if (e == hipSuccess) e = zero_fill(final_G, (size_t)BH * dv * dk * sizeof(float), s);
+        if (e != hipSuccess) return hip_fail(e, "zero fill of the final states");
+        return MESA_OK;
+    }
+
+    if (need_ws || final_H || final_G) {
+        mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
+                                SH, SGt, final_H, final_G, need_ws ? 1 : 0};
+        hipError_t e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
+        if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
+    }
+    if (!need_ws) {
+        // max_iters == 0: x = 0, so out = 0 and no update is made.
+        hipError_t e = zero_fill(out, (size_t)BH * T * dv * sizeof(float), s);
+        if (e == hipSuccess) e = zero_fill(iters, (size_t)BH * T * sizeof(int32_t), s);
+        if (e != hipSuccess) return hip_fail(e, "zero fill of out/iters");
+        return MESA_OK;
+    }
+    mesa::CgOutputArgs a{q, k, v, gamma, lambda, SH, SGt, BH, H, T, dk, chunk, (int)n_chunks,
+                         bf16, max_iters, tol, out, iters};
+    hipError_t e = timed_launch(MESA_KERNEL_CG_OUTPUT, s, [&] { return mesa::launch_cg_output(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "CG/output kernel launch");
+    return MESA_OK;
+}
+
+mesa_status mesa_decode_step(const void* q, const void* k, const void* v, int qkv_dtype,
+                             const float* gamma, const float* lambda, float* state_H,
+                             float* state_G, int N, int H, int dk, int dv, int max_iters,
+                             float tol, float* out, int32_t* iters, void* stream) {
+    g_err.clear();
+    if (qkv_dtype != MESA_DTYPE_F32 && qkv_dtype != MESA_DTYPE_BF16)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "qkv_dtype %d is not MESA_DTYPE_F32 or MESA_DTYPE_BF16", qkv_dtype);
+    if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "sizes must be positive (N=%d H=%d dk=%d dv=%d)", N, H, dk, dv);
+    if (max_iters < 0 || max_iters > kMaxIters)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "max_iters=%d outside [0, %d]", max_iters, kMaxIters);
+    if (!(tol >= 0.0f) || std::isinf(tol))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "tol must be finite and >= 0");
+    if (!q || !k || !v || !gamma || !lambda || !state_H || !state_G || !out)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "q, k, v, gamma, lambda, state_H, state_G and out must be non-null");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(state_H, 16) || !aligned(state_G, 16) || !aligned(gamma, 4) ||
+        !aligned(lambda, 4) || !aligned(iters, 4))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "misaligned pointer (16 B for tensors, 4 B for gamma/lambda/iters)");
+    if (dk != dv) return fail(MESA_ERR_UNSUPPORTED, "dk (%d) != dv (%d) is not built", dk, dv);
+    if (!supported_d(dk)) return fail(MESA_ERR_UNSUPPORTED, "d=%d not built (16, 32, 64, 128)", dk);
+    const long NH = (long)N * H;
+    if (NH > 0x7fffffffL) return fail(MESA_ERR_INVALID_ARGUMENT, "grid too large (N*H=%ld)", NH);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mesa::DecodeArgs a{q, k, v, gamma, lambda, state_H, state_G, NH, H, dk,
+                       qkv_dtype == MESA_DTYPE_BF16, max_iters, tol, out, iters};
+    hipError_t e = timed_launch(MESA_KERNEL_DECODE, s, [&] { return mesa::launch_decode(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    return MESA_OK;
+}
+
+mesa_status mesa_profile_enable(int on) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_on = on != 0;
+    return MESA_OK;
+}
+
+mesa_status mesa_profile_reset(void) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    for (auto& r : g_prof_pending) {
+        (void)hipEventSynchronize(r.b);
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    g_prof_pending.clear();
+    for (int i = 0; i < MESA_KERNEL_COUNT; ++i) { g_prof_ms[i] = 0; g_prof_n[i] = 0; }
+    return MESA_OK;
+}
+
+mesa_status mesa_profile_read(int kernel_id, double* total_ms, int64_t* launches) {
+    g_err.clear();
+    if (kernel_id < 0 || kernel_id >= MESA_KERNEL_COUNT || !total_ms || !launches)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "bad kernel id %d or null output", kernel_id);
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    mesa_status st = MESA_OK;
+    for (auto& r : g_prof_pending) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == MESA_OK) st = hip_fail(e, "profiling event");
+        g_prof_ms[r.kid] += ms;
+        g_prof_n[r.kid] += 1;
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    g_prof_pending.clear();
+    *total_ms = g_prof_ms[kernel_id];
+    *launches = g_prof_n[kernel_id];
+    return st;
+}
+
+const char* mesa_kernel_name(int kernel_id) {
+    switch (kernel_id) {
+        case MESA_KERNEL_CHUNK_STATES: return "chunk_states_kernel";
+        case MESA_KERNEL_CG_OUTPUT: return "cg_output_kernel";
+        case MESA_KERNEL_DECODE: return "decode_kernel";
+    }
+    return "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// mesa_kernels.h -- host-side launch interface of the gfx950 Mesa-layer kernels.
+// Internal to libmesa; the public ABI is include/mesa.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mesa {
+
+struct ChunkStatesArgs {
+    const void* k; const void* v; const float* gamma;
+    long BH; int T; int d; int chunk; int n_chunks; int bf16;
+    float* SH; float* SGt; float* final_H; float* final_G; int write_chunks;
+};
+
+struct CgOutputArgs {
+    const void* q; const void* k; const void* v; const float* gamma; const float* lambda;
+    const float* SH; const float* SGt;
+    long BH; int H; int T; int d; int chunk; int n_chunks; int bf16;
+    int max_iters; float tol;
+    float* out; int32_t* iters;
+};
+
+struct DecodeArgs {
+    const void* q; const void* k; const void* v; const float* gamma; const float* lambda;
+    float* SH; float* SG;
+    long NH; int H; int d; int bf16; int max_iters; float tol;
+    float* out; int32_t* iters;
+};
+
+hipError_t launch_chunk_states(const ChunkStatesArgs& a, hipStream_t s);
+hipError_t launch_cg_output(const CgOutputArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace mesa

@@ -23,7 +23,7 @@ import dataclasses
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "forward_inputs", "decode_head_inputs",
+    "Workload", "WORKLOADS", "forward_inputs", "decode_lambda", "decode_prefix", "decode_steps",
     "bf16_bits", "bf16_bits_to_f32", "as_f64",
 ]
 
@@ -132,22 +132,34 @@ def decode_lambda(w: Workload, H=None) -> np.ndarray:
     return _lam(rng, H, w.d, w.lam_law, w.lam_a, w.lam_b)
 
 
-def decode_head_inputs(w: Workload, n: int, h: int, prefix: int = None, steps: int = None):
-    """Prefix and per-step inputs of one decode head (n, h), float32.
+def decode_prefix(w: Workload, n: int, h: int, prefix: int = None):
+    """Prefix tokens of one decode head (n, h): dict(k [P,d], v [P,d], gamma [P]).
 
-    Each head has its own stream (SeedSequence([seed, n, h])), so any subset of
-    heads can be drawn alone.  Draw order: prefix k, v, gamma; then step q, k,
-    v, gamma.  Returns dict(pk [P,d], pv [P,d], pgamma [P], q [S,d], k [S,d],
-    v [S,d], gamma [S]).
+    Each head has its own stream (SeedSequence([seed, n, h])), so any subset
+    of heads can be drawn alone.  Draw order: k, v, gamma.  Keys are unit
+    Gaussian rows, values N(0, 1), gamma ~ U[gamma_lo, 1); all float32.
     """
     P = w.T if prefix is None else prefix
-    S = w.steps if steps is None else steps
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, n, h])))
-    pk = _unit_rows(rng, (P, w.d)).astype(np.float32)
-    pv = rng.standard_normal((P, w.d)).astype(np.float32)
-    pg = rng.uniform(w.gamma_lo, 1.0, size=P).astype(np.float32)
-    q = _unit_rows(rng, (S, w.d)).astype(np.float32)
-    k = _unit_rows(rng, (S, w.d)).astype(np.float32)
-    v = rng.standard_normal((S, w.d)).astype(np.float32)
-    g = rng.uniform(w.gamma_lo, 1.0, size=S).astype(np.float32)
-    return dict(pk=pk, pv=pv, pgamma=pg, q=q, k=k, v=v, gamma=g)
+    k = _unit_rows(rng, (P, w.d)).astype(np.float32)
+    v = rng.standard_normal((P, w.d)).astype(np.float32)
+    g = rng.uniform(w.gamma_lo, 1.0, size=P).astype(np.float32)
+    return dict(k=k, v=v, gamma=g)
+
+
+def decode_steps(w: Workload, steps: int, N: int = None, H: int = None, stream: int = 0):
+    """Per-step decode inputs for N x H heads from one stream.
+
+    Returns dict(q, k [steps,N,H,d] unit Gaussian rows, v [steps,N,H,d]
+    N(0, 1), gamma [steps,N,H] U[gamma_lo, 1)); all float32.  Draw order:
+    q, k, v, gamma.
+    """
+    N = w.B if N is None else N
+    H = w.H if H is None else H
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0x57E9, stream])))
+    shape = (steps, N, H, w.d)
+    q = _unit_rows(rng, shape).astype(np.float32)
+    k = _unit_rows(rng, shape).astype(np.float32)
+    v = rng.standard_normal(shape).astype(np.float32)
+    g = rng.uniform(w.gamma_lo, 1.0, size=(steps, N, H)).astype(np.float32)
+    return dict(q=q, k=k, v=v, gamma=g)

@@ -1,0 +1,197 @@
+"""Thin Python binding of libmesa (include/mesa.h): argument marshalling only.
+
+Every step of the Mesa layer runs in the library's HIP kernels; this module
+allocates outputs with torch, passes raw device pointers and the current HIP
+stream, and maps status codes to Python exceptions.  There is no fallback:
+if libmesa.so is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmesa.so")
+
+MESA_OK, MESA_ERR_INVALID_ARGUMENT, MESA_ERR_UNSUPPORTED, MESA_ERR_WORKSPACE_TOO_SMALL, MESA_ERR_HIP = range(5)
+MESA_DTYPE_F32, MESA_DTYPE_BF16 = 0, 1
+KERNEL_CHUNK_STATES, KERNEL_CG_OUTPUT, KERNEL_DECODE = 0, 1, 2
+
+# Every symbol include/mesa.h declares, with its ctypes signature.
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "mesa_abi_version": ([], _I),
+    "mesa_status_string": ([_I], ctypes.c_char_p),
+    "mesa_last_error_message": ([], ctypes.c_char_p),
+    "mesa_forward_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
+    "mesa_forward": ([_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                      _P, _P, _P, _P, _P, _Z, _P], _I),
+    "mesa_decode_step": ([_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
+                          _P, _P, _P], _I),
+    "mesa_profile_enable": ([_I], _I),
+    "mesa_profile_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
+    "mesa_profile_reset": ([], _I),
+    "mesa_kernel_name": ([_I], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+class MesaError(RuntimeError):
+    """A HIP runtime failure reported by libmesa."""
+
+
+def lib():
+    """The loaded libmesa (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status == MESA_OK:
+        return
+    L = lib()
+    msg = f"{what}: {L.mesa_status_string(status).decode()}: {L.mesa_last_error_message().decode()}"
+    if status in (MESA_ERR_INVALID_ARGUMENT, MESA_ERR_WORKSPACE_TOO_SMALL):
+        raise ValueError(msg)
+    if status == MESA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise MesaError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _qkv_dtype(t):
+    import torch
+    if t.dtype == torch.float32:
+        return MESA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MESA_DTYPE_BF16
+    raise ValueError(f"q/k/v dtype {t.dtype} is not float32 or bfloat16")
+
+
+def _need(t, name, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk) -> int:
+    return int(lib().mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def mesa_forward(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out=None, iters=None,
+                 return_iters=True, return_final=False, final_H=None, final_G=None,
+                 workspace=None, stream=None):
+    """Mesa-layer forward (see include/mesa.h, mesa_forward).
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (float32 or bfloat16, same dtype);
+    gamma: [B,H,T] float32; lam: [H,dk] float32.  Returns (out, iters,
+    final_H, final_G); iters/final_* are None unless requested.
+    """
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = _qkv_dtype(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(gamma, "gamma", torch.float32, dev)
+    _need(lam, "lambda", torch.float32, dev)
+    if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("q, k, v shapes disagree")
+    if tuple(gamma.shape) != (B, H, T) or tuple(lam.shape) != (H, dk):
+        raise ValueError("gamma must be [B,H,T] and lambda [H,dk]")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    if iters is None and return_iters:
+        iters = torch.empty((B, H, T), dtype=torch.int32, device=dev)
+    if return_final:
+        if final_H is None:
+            final_H = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+        if final_G is None:
+            final_G = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    ws_bytes = mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk) if max_iters > 0 else 0
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib().mesa_forward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(gamma), _ptr(lam),
+                            B, H, T, dk, dv, int(chunk), int(max_iters), float(tol),
+                            _ptr(out), _ptr(iters), _ptr(final_H), _ptr(final_G),
+                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            _stream(stream))
+    _check(st, "mesa_forward")
+    return out, iters, final_H, final_G
+
+
+def mesa_decode_step(q, k, v, gamma, lam, state_H, state_G, max_iters, tol=0.0, *,
+                     out=None, iters=None, return_iters=True, stream=None):
+    """One decode step (see include/mesa.h, mesa_decode_step); state_H/G updated in place.
+
+    q, k: [N,H,dk]; v: [N,H,dv]; gamma: [N,H]; lam: [H,dk];
+    state_H: [N,H,dk,dk], state_G: [N,H,dv,dk] float32.  Returns (out, iters).
+    """
+    import torch
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = _qkv_dtype(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(gamma, "gamma", torch.float32, dev)
+    _need(lam, "lambda", torch.float32, dev)
+    _need(state_H, "state_H", torch.float32, dev)
+    _need(state_G, "state_G", torch.float32, dev)
+    if tuple(state_H.shape) != (N, H, dk, dk) or tuple(state_G.shape) != (N, H, dv, dk):
+        raise ValueError("state shapes disagree with q/v")
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    if iters is None and return_iters:
+        iters = torch.empty((N, H), dtype=torch.int32, device=dev)
+    st = lib().mesa_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(gamma), _ptr(lam),
+                                _ptr(state_H), _ptr(state_G), N, H, dk, dv, int(max_iters),
+                                float(tol), _ptr(out), _ptr(iters), _stream(stream))
+    _check(st, "mesa_decode_step")
+    return out, iters
+
+
+def profile_enable(on: bool = True):
+    _check(lib().mesa_profile_enable(1 if on else 0), "mesa_profile_enable")
+
+
+def profile_reset():
+    _check(lib().mesa_profile_reset(), "mesa_profile_reset")
+
+
+def profile_read(kernel_id: int):
+    """(total milliseconds, launches) recorded for one kernel id since the last reset."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    _check(lib().mesa_profile_read(kernel_id, ctypes.byref(ms), ctypes.byref(n)), "mesa_profile_read")
+    return ms.value, n.value
+
+
+def kernel_name(kernel_id: int) -> str:
+    return lib().mesa_kernel_name(kernel_id).decode()

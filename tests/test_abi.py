@@ -1,0 +1,180 @@
+"""The C ABI of libmesa on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before touching the device.
+
+The pointers passed here are fake (never dereferenced): every call below
+fails validation, so no HIP call is made and no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from test_regression_amd import mesa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mesa.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = range(5)
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mesa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mesa.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in mesa.SIGNATURES, f"binding lacks {n}"
+    assert set(mesa.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings():
+    L = mesa.lib()
+    assert L.mesa_abi_version() == 1
+    for s, name in [(OK, b"MESA_OK"), (INVALID, b"MESA_ERR_INVALID_ARGUMENT"),
+                    (UNSUPPORTED, b"MESA_ERR_UNSUPPORTED"), (WS_SMALL, b"MESA_ERR_WORKSPACE_TOO_SMALL"),
+                    (HIPERR, b"MESA_ERR_HIP")]:
+        assert L.mesa_status_string(s) == name
+    assert L.mesa_status_string(99) == b"MESA_ERR_UNKNOWN"
+    assert [mesa.kernel_name(i) for i in range(3)] == ["chunk_states_kernel", "cg_output_kernel", "decode_kernel"]
+
+
+def test_workspace_bytes():
+    f = mesa.mesa_forward_workspace_bytes
+    assert f(8, 16, 4096, 128, 128, 64) == 8 * 16 * 64 * 2 * 128 * 128 * 4
+    assert f(1, 1, 65, 16, 16, 64) == 2 * 2 * 16 * 16 * 4        # ragged: 2 chunks
+    assert f(1, 1, 0, 16, 16, 64) == 0
+    assert f(0, 1, 10, 16, 16, 64) == 0 and f(1, 1, 10, 16, 16, 0) == 0
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=0, gamma=FAKE, lam=FAKE, B=1, H=2, T=128, dk=64, dv=64,
+             chunk=64, max_iters=5, tol=0.0, out=FAKE, iters=FAKE, fH=None, fG=None, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    L = mesa.lib()
+    st = L.mesa_forward(a["q"], a["k"], a["v"], a["dtype"], a["gamma"], a["lam"], a["B"], a["H"],
+                        a["T"], a["dk"], a["dv"], a["chunk"], a["max_iters"], ctypes.c_float(a["tol"]),
+                        a["out"], a["iters"], a["fH"], a["fG"], a["ws"], a["ws_bytes"], a["stream"])
+    return st, L.mesa_last_error_message().decode()
+
+
+def dec(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=0, gamma=FAKE, lam=FAKE, SH=FAKE, SG=FAKE, N=4, H=2,
+             dk=64, dv=64, max_iters=5, tol=1e-4, out=FAKE, iters=FAKE, stream=None)
+    a.update(kw)
+    L = mesa.lib()
+    st = L.mesa_decode_step(a["q"], a["k"], a["v"], a["dtype"], a["gamma"], a["lam"], a["SH"], a["SG"],
+                            a["N"], a["H"], a["dk"], a["dv"], a["max_iters"], ctypes.c_float(a["tol"]),
+                            a["out"], a["iters"], a["stream"])
+    return st, L.mesa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), INVALID, "non-null"),
+    (dict(v=None), INVALID, "non-null"),
+    (dict(gamma=None), INVALID, "non-null"),
+    (dict(lam=None), INVALID, "lambda"),
+    (dict(out=None), INVALID, "non-null"),
+    (dict(ws=None), INVALID, "workspace"),
+    (dict(dtype=7), INVALID, "qkv_dtype"),
+    (dict(B=0), INVALID, "positive"),
+    (dict(H=-1), INVALID, "positive"),
+    (dict(T=-5), INVALID, "positive"),
+    (dict(chunk=0), INVALID, "positive"),
+    (dict(max_iters=-1), INVALID, "max_iters"),
+    (dict(max_iters=5000), INVALID, "max_iters"),
+    (dict(tol=-1e-3), INVALID, "tol"),
+    (dict(tol=float("nan")), INVALID, "tol"),
+    (dict(tol=float("inf")), INVALID, "tol"),
+    (dict(q=FAKE + 4), INVALID, "misaligned"),
+    (dict(ws=FAKE + 8), INVALID, "misaligned"),
+    (dict(gamma=FAKE + 2), INVALID, "misaligned"),
+    (dict(dk=64, dv=32), UNSUPPORTED, "dv"),
+    (dict(dk=48, dv=48), UNSUPPORTED, "d=48"),
+    (dict(dk=256, dv=256), UNSUPPORTED, "d=256"),
+    (dict(chunk=128), UNSUPPORTED, "chunk"),
+    (dict(chunk=8), UNSUPPORTED, "chunk"),
+    (dict(ws_bytes=1000), WS_SMALL, "workspace"),
+])
+def test_forward_rejects_bad_arguments(kw, status, needle):
+    st, msg = fwd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_forward_workspace_optional_without_iterations():
+    # max_iters == 0 needs no workspace; with a bad dtype it still fails in validation
+    st, msg = fwd(ws=None, ws_bytes=0, max_iters=0, dtype=9)
+    assert st == INVALID and "qkv_dtype" in msg
+    st, msg = fwd(ws=None, ws_bytes=0, max_iters=0, dk=48, dv=48)
+    assert st == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), INVALID, "non-null"),
+    (dict(SH=None), INVALID, "non-null"),
+    (dict(SG=None), INVALID, "non-null"),
+    (dict(lam=None), INVALID, "non-null"),
+    (dict(dtype=3), INVALID, "qkv_dtype"),
+    (dict(N=0), INVALID, "positive"),
+    (dict(max_iters=-2), INVALID, "max_iters"),
+    (dict(tol=float("nan")), INVALID, "tol"),
+    (dict(SH=FAKE + 4), INVALID, "misaligned"),
+    (dict(iters=FAKE + 1), INVALID, "misaligned"),
+    (dict(dk=128, dv=64), UNSUPPORTED, "dv"),
+    (dict(dk=8, dv=8), UNSUPPORTED, "d=8"),
+])
+def test_decode_rejects_bad_arguments(kw, status, needle):
+    st, msg = dec(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_profile_api_host_paths():
+    L = mesa.lib()
+    ms = ctypes.c_double(-1)
+    n = ctypes.c_int64(-1)
+    assert L.mesa_profile_read(7, ctypes.byref(ms), ctypes.byref(n)) == INVALID
+    assert L.mesa_profile_read(0, None, ctypes.byref(n)) == INVALID
+    assert L.mesa_profile_reset() == OK
+    assert L.mesa_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == OK
+    assert ms.value == 0.0 and n.value == 0
+
+
+def test_error_message_is_thread_local_and_cleared():
+    import threading
+    st, msg = fwd(q=None)
+    assert st == INVALID and msg
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(mesa.lib().mesa_last_error_message()))
+    t.start()
+    t.join()
+    assert seen == [b""]
+    st, msg = dec(dtype=5)
+    assert st == INVALID and "qkv_dtype" in msg
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mesa, "_lib", None)
+    monkeypatch.setattr(mesa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        mesa.lib()
+
+
+def test_status_mapping():
+    with pytest.raises(ValueError):
+        mesa._check(INVALID, "x")
+    with pytest.raises(NotImplementedError):
+        mesa._check(UNSUPPORTED, "x")
+    with pytest.raises(ValueError):
+        mesa._check(WS_SMALL, "x")
+    with pytest.raises(mesa.MesaError):
+        mesa._check(HIPERR, "x")
