@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mesa-layer forward (and decode) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+
+One step is one ``mesa_forward`` call (chunk states, every CG iteration and
+the output contraction) over the layer-sized workload: B=8, H=16, T=4096,
+d=128, chunk 64, bf16 q/k/v, fp32 arithmetic, fixed 30 CG iterations, seeded
+synthetic inputs already resident in device memory.  Prints ONE JSON line.
+
+Besides the headline it measures, in the same run and reported in the same
+line: the dynamic-stopping forward (4x16x8192, fp32, tol 1e-4, cap 30) and
+1024 recurrent decode steps over 256 x 16 heads (d=128, states from
+4096-token prefixes).  Per-kernel average durations come from HIP events
+recorded by the library around each launch on the stream it runs on.
+The CPU baseline is the fp64 oracle timed on a bounded sample of the same
+headline workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cg_output_layer_bf16_d128_T4096_traffic.json")
+KERNEL_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/mesa_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_per_token_head(d, C, k):
+    """Algorithmic flops of one forward token-head: chunk states, k CG matvecs
+    (state term 2d^2, causal intra-chunk term 2(C+1)d, vector work 11d) and the
+    output contraction."""
+    states = 4 * d * d
+    cg = k * (2 * d * d + 2 * (C + 1) * d + 11 * d)
+    output = 2 * d * d + 2 * (C + 1) * d
+    return states, cg, output
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the CG/output kernel from committed rocprofv3
+    counters, only if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def to_dev(torch, x, dtype, dev):
+    import numpy as np
+    if dtype == "bf16" and x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(x).to(dev)
+
+
+def timed_forward(torch, mesa, t, w, steps, warmup):
+    """Warmup, then `steps` timed calls bracketed by device synchronisation."""
+    B, H, T, d = t["q"].shape
+    out = torch.empty((B, H, T, d), dtype=torch.float32, device=t["q"].device)
+    iters = torch.empty((B, H, T), dtype=torch.int32, device=t["q"].device)
+    ws = torch.empty(mesa.mesa_forward_workspace_bytes(B, H, T, d, d, w.chunk), dtype=torch.uint8,
+                     device=t["q"].device)
+
+    def step():
+        mesa.mesa_forward(t["q"], t["k"], t["v"], t["gamma"], t["lam"], w.max_iters, w.tol, w.chunk,
+                          out=out, iters=iters, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mesa.profile_reset()
+    mesa.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mesa.profile_enable(False)
+    k1 = mesa.profile_read(mesa.KERNEL_CHUNK_STATES)
+    k2 = mesa.profile_read(mesa.KERNEL_CG_OUTPUT)
+    mesa.profile_reset()
+    return (t1 - t0), k1, k2, out, iters
+
+
+def headline(torch, mesa, inputs, args, dev):
+    w = inputs.WORKLOADS["layer_bf16_d128_T4096_k30"]
+    log(f"[bench] generating {w.name}")
+    x = inputs.forward_inputs(w)
+    t = {n: to_dev(torch, x[n], w.dtype if n in ("q", "k", "v") else "f32", dev) for n in x}
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    el, k1, k2, _, _ = timed_forward(torch, mesa, t, w, args.steps, args.warmup)
+    n_tok = w.B * w.H * w.T
+    fs, fcg, fo = flops_per_token_head(w.d, w.chunk, w.max_iters)
+    ms_step = 1e3 * el / args.steps
+    k2_ms = k2[0] / max(k2[1], 1)
+    k1_ms = k1[0] / max(k1[1], 1)
+    k2_flops = (fcg + fo) * n_tok
+    # chunk-state kernel: reads k, v (bf16) and gamma, writes S^H and S^G once
+    k1_bytes = n_tok * (2 * w.d * 2 + 4) + 2 * (w.B * w.H * (w.T // w.chunk) * w.d * w.d * 4)
+    achieved = k2_flops / (k2_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    res = dict(
+        w=w, x=x, n_tok=n_tok, ms_step=ms_step, value=n_tok * args.steps / el,
+        tflops=(fs + fcg + fo) * n_tok / (ms_step * 1e-3) / 1e12,
+        roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP32_MFMA_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+                      traffic=traffic, kernel="cg_output_kernel<128,64,bf16>",
+                      flops_per_launch=k2_flops, avg_launch_ms=round(k2_ms, 4)),
+        kernels={
+            "cg_output_kernel": dict(avg_ms=round(k2_ms, 4), launches=k2[1],
+                                     tflops=round(achieved, 2)),
+            "chunk_states_kernel": dict(avg_ms=round(k1_ms, 4), launches=k1[1],
+                                        gbs=round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
+                                        hbm_frac=round(k1_bytes / (k1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)),
+        })
+    del t
+    return res
+
+
+def dynamic(torch, mesa, inputs, dev):
+    w = inputs.WORKLOADS["dynamic_f32_d128_T8192_tol1e-4"]
+    log(f"[bench] generating {w.name}")
+    x = inputs.forward_inputs(w)
+    t = {n: to_dev(torch, x[n], "f32", dev) for n in x}
+    del x
+    el, k1, k2, _, iters = timed_forward(torch, mesa, t, w, 3, 1)
+    n_tok = w.B * w.H * w.T
+    it = iters.to(torch.float64)
+    mean_it = float(it.mean())
+    fs, _, fo = flops_per_token_head(w.d, w.chunk, 0)
+    per_it = 2 * w.d * w.d + 2 * (w.chunk + 1) * w.d + 11 * w.d
+    useful = n_tok * (fs + fo) + float(it.sum()) * per_it
+    ms = 1e3 * el / 3
+    k2_ms = k2[0] / max(k2[1], 1)
+    del t
+    return {"workload": w.name, "tokens_per_s": round(n_tok / (ms * 1e-3), 1), "ms_per_call": round(ms, 3),
+            "iters_mean": round(mean_it, 3), "iters_min": int(iters.min()), "iters_max": int(iters.max()),
+            "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+            "cg_output_kernel_ms": round(k2_ms, 4)}
+
+
+def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
+    """1024 decode steps over 256 x 16 heads; states built on the device from
+    seeded 4096-token prefixes by the forward path with zero CG iterations."""
+    w = inputs.WORKLOADS["decode_f32_d128_N256_prefix4096"]
+    N, H, d, P = w.B, w.H, w.d, w.T
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    log(f"[bench] decode: building {N}x{H} prefix states of {P} tokens")
+    SH = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    SG = torch.empty_like(SH)
+    lam = torch.from_numpy(inputs.decode_lambda(w)).to(dev)
+    for n0 in range(0, N, 64):      # 64 sequences at a time keeps the prefix buffers at 2 GiB each
+        nb = min(64, N - n0)
+        pk = torch.randn((nb, H, P, d), generator=g, device=dev)
+        pk /= pk.norm(dim=-1, keepdim=True)
+        pv = torch.randn((nb, H, P, d), generator=g, device=dev)
+        pg = w.gamma_lo + (1 - w.gamma_lo) * torch.rand((nb, H, P), generator=g, device=dev)
+        mesa.mesa_forward(pk, pk, pv, pg, lam, 0, 0.0, w.chunk, return_iters=False,
+                          final_H=SH[n0:n0 + nb], final_G=SG[n0:n0 + nb], return_final=True)
+        del pk, pv, pg
+    S = steps + warmup
+    q = torch.randn((S, N, H, d), generator=g, device=dev)
+    q /= q.norm(dim=-1, keepdim=True)
+    k = torch.randn((S, N, H, d), generator=g, device=dev)
+    k /= k.norm(dim=-1, keepdim=True)
+    v = torch.randn((S, N, H, d), generator=g, device=dev)
+    ga = w.gamma_lo + (1 - w.gamma_lo) * torch.rand((S, N, H), generator=g, device=dev)
+    out = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    its = torch.empty((S, N, H), dtype=torch.int32, device=dev)
+    for s in range(warmup):
+        mesa.mesa_decode_step(q[s], k[s], v[s], ga[s], lam, SH, SG, w.max_iters, w.tol, out=out, iters=its[s])
+    torch.cuda.synchronize()
+    mesa.profile_reset()
+    mesa.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(warmup, S):
+        mesa.mesa_decode_step(q[s], k[s], v[s], ga[s], lam, SH, SG, w.max_iters, w.tol, out=out, iters=its[s])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    mesa.profile_enable(False)
+    kd = mesa.profile_read(mesa.KERNEL_DECODE)
+    mesa.profile_reset()
+    kd_ms = kd[0] / max(kd[1], 1)
+    nh = N * H
+    # per head-step: read + write H and G (fp32 d x d each), q, k, v, gamma, out, iters
+    bytes_hs = 4 * 4 * d * d + 3 * 4 * d + 4 + 4 * d + 4
+    gbs = bytes_hs * nh / (kd_ms * 1e-3) / 1e9
+    itf = its[warmup:].to(torch.float64)
+    del q, k, v, ga
+    return {"workload": w.name, "head_steps_per_s": round(steps * nh / el, 1), "ms_per_step": round(1e3 * el / steps, 4),
+            "iters_mean": round(float(itf.mean()), 3), "iters_max": int(itf.max()),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "decode_kernel<128,float>",
+                         "bytes_per_launch": bytes_hs * nh, "avg_launch_ms": round(kd_ms, 4)}}
+
+
+def cpu_baseline(x, w, heads=16):
+    """The fp64 oracle, as it stands, on `heads` heads x all T tokens of the
+    headline workload (one OpenMP thread per head)."""
+    import numpy as np
+    import oracle
+    from test_regression_amd import inputs
+    heads = min(heads, w.B * w.H)
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:heads] if heads == w.B * w.H else \
+        [(i % w.B, (5 * i) % w.H) for i in range(heads)]
+    q = np.stack([inputs.as_f64(x["q"][b, h], w.dtype) for b, h in sel])[None]
+    k = np.stack([inputs.as_f64(x["k"][b, h], w.dtype) for b, h in sel])[None]
+    v = np.stack([inputs.as_f64(x["v"][b, h], w.dtype) for b, h in sel])[None]
+    g = np.stack([x["gamma"][b, h] for b, h in sel])[None].astype(np.float64)
+    lam = np.stack([x["lam"][h] for _, h in sel]).astype(np.float64)
+    threads = min(oracle.max_threads(), heads)
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, g, lam, w.max_iters, w.tol)
+    el = time.perf_counter() - t0
+    n = heads * w.T
+    return {"value": round(n / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"all {w.B * w.H} heads" if heads == w.B * w.H else
+                       f"{heads} of {w.B * w.H} heads (b, h) = {sel[:3]}...") +
+                      f", all {w.T} tokens, k={w.max_iters}; {n} token-heads in {el:.1f} s",
+            "seconds": round(el, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the dynamic-stopping and decode measurements")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=128)
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="also run one device-to-device copy of this many GiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the Mesa layer's heads are independent; sharding is described in the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from test_regression_amd import inputs, mesa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    mesa.lib()
+    h = headline(torch, mesa, inputs, args, dev)
+    torch.cuda.empty_cache()
+    if args.copy_probe_gib > 0:
+        n = int(args.copy_probe_gib * (1 << 30)) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {4 * n} bytes read, {4 * n} bytes written")
+        del a, b
+    extra = {}
+    if not args.no_extra:
+        extra["dynamic"] = dynamic(torch, mesa, inputs, dev)
+        torch.cuda.empty_cache()
+        extra["decode"] = decode(torch, mesa, inputs, dev)
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the oracle on {args.cpu_heads} heads")
+        cpu = cpu_baseline(h["x"], h["w"], args.cpu_heads)
+    w = h["w"]
+    line = {
+        "metric": "Mesa-layer fwd tokens/sec (B·H·T) at d=128, k=30 CG; % of MFMA/HBM roofline",
+        "value": round(h["value"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(h["ms_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d, "d_v": w.d,
+                   "chunk": w.chunk, "qkv_storage": w.dtype, "cg_iters": w.max_iters, "tol": w.tol,
+                   "seed": w.seed},
+        "tflops": round(h["tflops"], 2),
+        "roofline": h["roofline"],
+        "cpu_baseline": cpu,
+        "kernels": h["kernels"],
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

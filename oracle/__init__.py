@@ -57,6 +57,8 @@ def _load():
         lib.oracle_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, D,
                                            P, P, P, P, P]
         lib.oracle_decode_step.restype = I
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = I
         _lib = lib
     return _lib
 
@@ -67,6 +69,11 @@ def _f64(a):
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use (one head per thread)."""
+    return int(_load().oracle_max_threads())
 
 
 def cg_solve(Hm, lam, b, max_iters, tol=0.0):

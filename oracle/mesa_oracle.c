@@ -33,6 +33,7 @@
  * recurrence above says.  No chunking, no blocking.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -237,3 +238,6 @@ int oracle_decode_step(const double *q, const double *k, const double *v,
     }
     return bad ? -1 : 0;
 }
+
+/* Threads an OpenMP parallel region of this library would use. */
+int oracle_max_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,122 @@
+"""Summarise rocprofv3 output for libmesa's kernels.
+
+    python -m test_regression_amd.profile_summary stats <kernel_stats.csv | results.db> [--command CMD]
+    python -m test_regression_amd.profile_summary traffic <fetch_counter_collection.csv>
+        <write_counter_collection.csv> --copy-bytes N --kernel NAME_SUBSTRING [--command CMD]
+
+``stats`` prints per-kernel call counts and average durations (from a
+``--kernel-trace --stats`` run, CSV or rocpd database).  ``traffic`` turns two
+``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs (KiB per dispatch) into HBM
+bytes per launch of one kernel, each counter scaled by what it read for a
+plain device copy of ``--copy-bytes`` bytes in the same run, and prints JSON
+(with a hash of the CG kernel's source so stale numbers can be detected).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sqlite3
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CG_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/mesa_device.h"]
+
+
+def cg_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in CG_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short(name: str) -> str:
+    """Kernel name without its argument list."""
+    return name.split("(")[0].replace("void ", "") if "(" in name else name
+
+
+def read_stats(path: str):
+    rows = []
+    if path.endswith(".db"):
+        c = sqlite3.connect(path)
+        for name, calls, total, avg, pct in c.execute(
+                "select name, total_calls, total_duration, average, percentage from top_kernels"):
+            # the rocpd summary view is in microseconds already
+            rows.append((short(name), int(calls), float(total), float(avg), float(pct)))
+    else:
+        for r in csv.DictReader(open(path)):
+            rows.append((short(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
+                         float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
+    return rows
+
+
+def cmd_stats(a):
+    rows = read_stats(a.path)
+    out = []
+    if a.command:
+        out.append(f"command: {a.command}")
+    out.append(f"{'kernel':70s} {'calls':>6s} {'total_us':>12s} {'avg_us':>11s} {'pct':>6s}")
+    for name, calls, tot, avg, pct in rows:
+        if a.all or name.startswith("mesa::") or "zero_fill" in name:
+            out.append(f"{name:70s} {calls:6d} {tot:12.1f} {avg:11.1f} {pct:6.2f}")
+    print("\n".join(out))
+
+
+def counter_rows(path: str, counter: str):
+    res = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            res.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return res
+
+
+def cmd_traffic(a):
+    fetch = counter_rows(a.fetch, "FETCH_SIZE")
+    write = counter_rows(a.write, "WRITE_SIZE")
+
+    def copy_kib(rows):
+        cands = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        return max(cands) if cands else None
+
+    copy_gib = a.copy_bytes / 2 ** 30
+    f_copy, w_copy = copy_kib(fetch), copy_kib(write)
+    f_scale = a.copy_bytes / 1024 / f_copy
+    w_scale = a.copy_bytes / 1024 / w_copy
+    f_k = [v for n, v in fetch if a.kernel in n]
+    w_k = [v for n, v in write if a.kernel in n]
+    fb = statistics.median(f_k) * 1024 * f_scale
+    wb = statistics.median(w_k) * 1024 * w_scale
+    print(json.dumps({
+        "kernel": a.kernel, "command": a.command, "kernel_source_hash": cg_source_hash(),
+        "fetch_kib_per_dispatch": statistics.median(f_k), "write_kib_per_dispatch": statistics.median(w_k),
+        "copy_probe_bytes": a.copy_bytes, "copy_probe_gib": copy_gib,
+        "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+        "bytes_per_launch": round(fb + wb), "dispatches": [len(f_k), len(w_k)],
+    }, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("path")
+    s.add_argument("--command", default="")
+    s.add_argument("--all", action="store_true")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch")
+    t.add_argument("write")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
