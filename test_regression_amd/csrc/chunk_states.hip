@@ -12,16 +12,17 @@
 // chunk (the state before the chunk's first token) and, optionally, the final
 // state after the last token.
 //
-// The G states are produced transposed (G^T, [d_k][d_v]) in the workspace,
-// which is the layout the output contraction reads; the exported final G is
-// written in the [d_v][d_k] layout of the ABI.
+// Both states are stored row-major ([d][d_k], rows are key features for H
+// and value features for G), the layout of the exported final states.
 //
-// Work split: one workgroup per (head, {H, G^T}, 16*NW-row block of the
+// Work split: one workgroup per (head, {H, G}, 16*NW-row block of the
 // state); each wave holds a 16 x D slab of the running state in MFMA
 // accumulator layout and walks the chunks in order.  Per chunk the update is
 // one (16 x C) x (C x D) product on v_mfma_f32_16x16x4_f32 with the weighted
-// keys as the A operand: rows of the state are key features, the contraction
-// runs over the chunk's tokens.
+// rows (keys for H, values for G) as the A operand and the keys as the B
+// operand; the contraction runs over the chunk's tokens.  Workgroup ids are
+// mapped so that the 2*RB workgroups of one head land on the same XCD (ids
+// congruent mod 8) and share its L2 for the key and value tiles.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -30,16 +31,16 @@ namespace mesa {
 template <int D, int C, typename In>
 __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kernel(
     const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
-    int T, int n_chunks, float* __restrict__ SH, float* __restrict__ SGt,
-    float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks) {
+    int T, int n_chunks, float* __restrict__ SH, float* __restrict__ SG,
+    float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks, long BH) {
     constexpr int NW = D >= 64 ? 4 : D / 16;   // waves per workgroup
     constexpr int RB = D / (16 * NW);          // row blocks per state
     constexpr int NT = D / 16;                 // 16-column tiles of the state
     constexpr int PD = lds_pitch(D);
     constexpr int NTHR = 64 * NW;
 
-    __shared__ float sK[C * PD];   // keys of the chunk (A rows and, for H, B)
-    __shared__ float sB[C * PD];   // values of the chunk (B for G^T)
+    __shared__ float sK[C * PD];   // keys of the chunk (B operand; A rows for H)
+    __shared__ float sB[C * PD];   // values of the chunk (A rows for G)
     __shared__ float sW[C];        // e^{l_end - l_i}
     __shared__ float sGam;         // e^{l_end}
 
@@ -49,17 +50,22 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
     const int n = lane & 15;
     const int kk = lane >> 4;
 
-    const int bid = blockIdx.x;
-    const int rb = bid % RB;
-    const int which = (bid / RB) & 1;          // 0: H, 1: G^T
-    const long bh = bid / (2 * RB);
+    // XCD-aware id: consecutive ids go round-robin over the 8 XCDs, so the
+    // 2*RB parts of head bh get ids xcd + 8*(slot) with equal xcd.
+    constexpr int PARTS = 2 * RB;
+    const long xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const long bh = (slot / PARTS) * 8 + xcd;
+    const int part = (int)(slot % PARTS);
+    if (bh >= BH) return;                      // whole workgroup: no barrier is skipped
+    const int rb = part % RB;
+    const int which = part / RB;               // 0: H, 1: G
     const int m0 = rb * 16 * NW + 16 * w;      // first state row of this wave
 
     const In* kh = k + (size_t)bh * T * D;
     const In* vh = v + (size_t)bh * T * D;
     const float* gh = gamma + (size_t)bh * T;
-    float* Sout = (which == 0 ? SH : SGt) + (size_t)bh * n_chunks * D * D;
-    float* sBuse = which == 0 ? sK : sB;
+    float* Sout = (which == 0 ? SH : SG) + (size_t)bh * n_chunks * D * D;
+    const float* sArows = which == 0 ? sK : sB;
 
     f32x4 acc[NT];
 #pragma unroll
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
                     dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
         }
 
-        // ---- S <- Gamma_c S + sum_i w_i k_i b_i^T ----
+        // ---- S <- Gamma_c S + sum_i w_i a_i k_i^T ----
         const float G = sGam;
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j] *= G;
@@ -106,28 +112,22 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int i = 16 * g + 4 * kk + s;
-                const float a = sK[i * PD + m0 + n] * sW[i];
+                const float a = sArows[i * PD + m0 + n] * sW[i];
 #pragma unroll
-                for (int j = 0; j < NT; ++j) acc[j] = mfma4(a, sBuse[i * PD + 16 * j + n], acc[j]);
+                for (int j = 0; j < NT; ++j) acc[j] = mfma4(a, sK[i * PD + 16 * j + n], acc[j]);
             }
         }
         __syncthreads();
     }
 
     // ---- final state (after the last token) ----
-    if (which == 0 && final_H) {
-        float* dst = final_H + (size_t)bh * D * D;
+    float* fin = which == 0 ? final_H : final_G;
+    if (fin) {
+        float* dst = fin + (size_t)bh * D * D;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
-    }
-    if (which == 1 && final_G) {   // acc holds G^T[key feature][value feature]
-        float* dst = final_G + (size_t)bh * D * D;
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(size_t)(16 * j + n) * D + m0 + 4 * kk + r] = acc[j][r];
     }
 }
 
@@ -135,10 +135,11 @@ template <int D, int C, typename In>
 hipError_t launch_chunk_states_t(const ChunkStatesArgs& a, hipStream_t s) {
     constexpr int NW = D >= 64 ? 4 : D / 16;
     constexpr int RB = D / (16 * NW);
-    const long grid = (long)a.BH * 2 * RB;
+    // ids: 8 XCD lanes x (heads rounded up to a multiple of 8) / 8 x parts
+    const long grid = ((a.BH + 7) / 8) * 8 * 2 * RB;
     hipLaunchKernelGGL((chunk_states_kernel<D, C, In>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
-                       (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SGt,
-                       a.final_H, a.final_G, a.write_chunks);
+                       (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG,
+                       a.final_H, a.final_G, a.write_chunks, a.BH);
     return hipGetLastError();
 }
 

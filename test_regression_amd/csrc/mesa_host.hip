@@ -156,7 +156,7 @@ mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dt
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int bf16 = qkv_dtype == MESA_DTYPE_BF16;
     float* SH = static_cast<float*>(workspace);
-    float* SGt = need_ws ? SH + (size_t)BH * n_chunks * dk * dk : nullptr;
+    float* SG = need_ws ? SH + (size_t)BH * n_chunks * dk * dk : nullptr;
 
     if (T == 0) {
         // Nothing to solve; the final states are the zero initial states.
@@ -168,7 +168,7 @@ mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dt
 
     if (need_ws || final_H || final_G) {
         mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
-                                SH, SGt, final_H, final_G, need_ws ? 1 : 0};
+                                SH, SG, final_H, final_G, need_ws ? 1 : 0};
         hipError_t e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
         if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
     }
@@ -179,7 +179,7 @@ mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dt
         if (e != hipSuccess) return hip_fail(e, "zero fill of out/iters");
         return MESA_OK;
     }
-    mesa::CgOutputArgs a{q, k, v, gamma, lambda, SH, SGt, BH, H, T, dk, chunk, (int)n_chunks,
+    mesa::CgOutputArgs a{q, k, v, gamma, lambda, SH, SG, BH, H, T, dk, chunk, (int)n_chunks,
                          bf16, max_iters, tol, out, iters};
     hipError_t e = timed_launch(MESA_KERNEL_CG_OUTPUT, s, [&] { return mesa::launch_cg_output(a, s); });
     if (e != hipSuccess) return hip_fail(e, "CG/output kernel launch");

@@ -9,12 +9,12 @@ namespace mesa {
 struct ChunkStatesArgs {
     const void* k; const void* v; const float* gamma;
     long BH; int T; int d; int chunk; int n_chunks; int bf16;
-    float* SH; float* SGt; float* final_H; float* final_G; int write_chunks;
+    float* SH; float* SG; float* final_H; float* final_G; int write_chunks;
 };
 
 struct CgOutputArgs {
     const void* q; const void* k; const void* v; const float* gamma; const float* lambda;
-    const float* SH; const float* SGt;
+    const float* SH; const float* SG;
     long BH; int H; int T; int d; int chunk; int n_chunks; int bf16;
     int max_iters; float tol;
     float* out; int32_t* iters;
