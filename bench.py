@@ -220,6 +220,42 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
                          "bytes_per_launch": bytes_hs * nh, "avg_launch_ms": round(kd_ms, 4)}}
 
 
+def measured_peaks(torch, mesa, dev):
+    """Attainable rates on this GPU from known-work probe kernels: fp32 and
+    bf16 MFMA register-resident loops (1024 workgroups x 4 waves) and a 1 GiB
+    streaming copy; each timed with events on the stream it runs on."""
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device=dev)
+    res = {}
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    for dt, it in (("f32", 2000), ("bf16", 2000)):
+        flops = [0]
+
+        def run(dt=dt, it=it):
+            flops[0] = mesa.probe_mfma(dt, 1024, it, sink)
+        ms = timed(run)
+        res[f"mfma_{dt}_tflops"] = round(flops[0] / (ms * 1e-3) / 1e12, 1)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: mesa.probe_copy(src, dst))
+    res["copy_gbs"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
+    del src, dst, sink
+    return res
+
+
 def cpu_baseline(x, w, heads=16):
     """The fp64 oracle, as it stands, on `heads` heads x all T tokens of the
     headline workload (one OpenMP thread per head)."""
@@ -269,7 +305,12 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     mesa.lib()
+    log("[bench] measuring attainable peaks")
+    peaks = measured_peaks(torch, mesa, dev)
     h = headline(torch, mesa, inputs, args, dev)
+    rf = h["roofline"]
+    rf["peak_measured"] = peaks["mfma_f32_tflops"]
+    rf["frac_measured"] = round(rf["achieved"] / peaks["mfma_f32_tflops"], 4)
     torch.cuda.empty_cache()
     if args.copy_probe_gib > 0:
         n = int(args.copy_probe_gib * (1 << 30)) // 4
@@ -303,6 +344,11 @@ def main():
         "cpu_baseline": cpu,
         "kernels": h["kernels"],
     }
+    line["measured_peaks"] = peaks
+    if "decode" in extra:
+        d = extra["decode"]["roofline"]
+        d["peak_measured"] = peaks["copy_gbs"]
+        d["frac_measured"] = round(d["achieved"] / peaks["copy_gbs"], 4)
     line.update(extra)
     print(json.dumps(line), flush=True)
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmesa.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
-SOURCES = ["mesa_host.hip", "chunk_states.hip", "cg_output.hip", "decode.hip"]
+SOURCES = ["mesa_host.hip", "chunk_states.hip", "cg_output.hip", "decode.hip", "probes.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -25,9 +25,20 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The probes' plain accumulator loops are allocated
+# with tied accumulator chains only in the VGPR form of MFMA (the AGPR form
+# shuffles them through copies); the other kernels are cleanest in the
+# default form.  Both are checked by codegen_check.
+SOURCE_FLAGS = {"probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def flags_for(src: str):
+    return [*FLAGS, *SOURCE_FLAGS.get(src, [])]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *flags_for(src), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -73,7 +73,7 @@ def check_all(sources=None):
     with tempfile.TemporaryDirectory() as td:
         for src in sources:
             asm = os.path.join(td, src + ".s")
-            cmd = [B.HIPCC, *B.FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", asm]
+            cmd = [B.HIPCC, *B.flags_for(src), "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", asm]
             subprocess.run(cmd, check=True, capture_output=True)
             res[src] = scan_asm(open(asm).read())
     return res

@@ -45,8 +45,9 @@ template <int D, int C>
 struct CgLds {
     static constexpr int NW = C / 16;
     static constexpr int PD = lds_pitch(D);
+    static constexpr int PS = lds_pitch_rows(D);
     static constexpr int PC = lds_pitch(C);
-    float S[D * PD];          // S^H_c, later G_c           [row][feature]
+    float S[D * PS];          // S^H_c, later G_c           [row][feature]
     float KV[C * PD];         // K_c, later V_c             [token][feature]
     float P[NW][16 * PD];     // per wave: P (later X) rows, MFMA A staging
     float A[NW][16 * PC];     // per wave: decayed scores M o (Z K^T)
@@ -58,7 +59,7 @@ __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast
 
 // Y[j]  += sum_f Z[m][f] * Bs[16j + n][f]      (if STATE; Bs symmetric or row-major G)
 // Sc[ib] += sum_f Z[m][f] * Bk[16ib + n][f]    (ib < NB; the score blocks)
-// Z, Bs, Bk: LDS rows of pitch lds_pitch(D).  Software-pipelined over the
+// Z, Bk: LDS rows of pitch lds_pitch(D); Bs: pitch lds_pitch_rows(D).  Software-pipelined over the
 // 16-wide k-groups: group g+1's operands are in flight while group g's MFMAs
 // issue.
 template <int D, int NB, bool STATE>
@@ -66,16 +67,17 @@ __device__ __forceinline__ void contract_rows(const float* Z, const float* Bs, c
                                               f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB > 0 ? NB : 1]) {
     constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
+    constexpr int PS = lds_pitch_rows(D);
     constexpr int NBB = NB > 0 ? NB : 1;
     const float* za = Z + n * PD + 4 * kk;
-    const float* bsa = STATE ? Bs + n * PD + 4 * kk : nullptr;
+    const float* bsa = STATE ? Bs + n * PS + 4 * kk : nullptr;
     const float* bka = NB > 0 ? Bk + n * PD + 4 * kk : nullptr;
     f32x4 a[2], bs[2][STATE ? NT : 1], bk[2][NBB];
     auto load = [&](int g, int buf) {
         a[buf] = lds4(za + 16 * g);
         if constexpr (STATE) {
 #pragma unroll
-            for (int j = 0; j < NT; ++j) bs[buf][j] = lds4(bsa + 16 * j * PD + 16 * g);
+            for (int j = 0; j < NT; ++j) bs[buf][j] = lds4(bsa + 16 * j * PS + 16 * g);
         }
 #pragma unroll
         for (int ib = 0; ib < NB; ++ib) bk[buf][ib] = lds4(bka + 16 * ib * PD + 16 * g);
@@ -155,6 +157,7 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
     constexpr int NT = D / 16;
     constexpr int NB = W + 1;          // causal key blocks of this wave
     constexpr int PD = lds_pitch(D);
+    constexpr int PS = lds_pitch_rows(D);
     constexpr int NTHR = 64 * (C / 16);
     const int lane = tid & 63;
     const int n = lane & 15;
@@ -191,7 +194,8 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
         P[j] = R[j];
         X[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    float rr[4], nq[4];
+    // stop before an update when |r| / |q| < tol, tested as r.r < (tol |q|)^2
+    float rr[4], stop_rr[4];
     bool done[4];
     int it[4];
 #pragma unroll
@@ -200,7 +204,8 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
 #pragma unroll
         for (int j = 0; j < NT; ++j) s += R[j][r] * R[j][r];
         rr[r] = rowsum16(s);
-        nq[r] = sqrtf(rr[r]);
+        const float tq = tol * sqrtf(rr[r]);
+        stop_rr[r] = tq * tq;
         done[r] = !(rr[r] > 0.f);   // q_t == 0 (or a padded row): x = 0, 0 iterations
         it[r] = 0;
     }
@@ -212,8 +217,7 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             if (!done[r]) {
-                const float rho = sqrtf(rr[r]) / nq[r];
-                if ((tol > 0.f && rho < tol) || rr[r] == 0.f) done[r] = true;
+                if (rr[r] < stop_rr[r] || rr[r] == 0.f) done[r] = true;
                 else alive = true;
             }
         }
@@ -295,7 +299,7 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
     }
     __syncthreads();   // every wave is done with S^H_c and K_c
     for (int e = tid * 4; e < D * D; e += NTHR * 4)
-        *reinterpret_cast<f32x4*>(&L.S[(e / D) * PD + e % D]) = *reinterpret_cast<const f32x4*>(Gc + e);
+        *reinterpret_cast<f32x4*>(&L.S[(e / D) * PS + e % D]) = *reinterpret_cast<const f32x4*>(Gc + e);
     for (int e = tid * 4; e < C * D; e += NTHR * 4) {
         const int i = e / D;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -325,6 +329,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     int max_iters, float tol, float* __restrict__ out, int32_t* __restrict__ iters) {
     constexpr int NW = C / 16;
     constexpr int PD = lds_pitch(D);
+    constexpr int PS = lds_pitch_rows(D);
     constexpr int NTHR = 64 * NW;
     __shared__ CgLds<D, C> L;
 
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
 
     // ---- stage S^H_c, K_c, lambda, l ----
     for (int e = tid * 4; e < D * D; e += NTHR * 4)
-        *reinterpret_cast<f32x4*>(&L.S[(e / D) * PD + e % D]) = *reinterpret_cast<const f32x4*>(SH + soff + e);
+        *reinterpret_cast<f32x4*>(&L.S[(e / D) * PS + e % D]) = *reinterpret_cast<const f32x4*>(SH + soff + e);
     for (int e = tid * 4; e < C * D; e += NTHR * 4) {
         const int i = e / D;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -71,27 +71,52 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int c = 0; c < n_chunks; ++c) {
+    // The next chunk's keys, values and gates are loaded into registers while
+    // the current chunk's MFMAs run (global latency hidden behind compute).
+    constexpr int EL4 = C * D / (4 * NTHR);   // 4-element groups per thread per tile
+    static_assert(C * D % (4 * NTHR) == 0, "tile must split evenly over the workgroup");
+    f32x4 kreg[EL4], vreg[EL4];
+    float greg = 1.0f;
+    auto prefetch = [&](int c) {
         const int t0 = c * C;
         const int valid = min(C, T - t0);
-        // ---- stage the chunk's keys (and values) in LDS as fp32 ----
-        for (int e = tid * 4; e < C * D; e += NTHR * 4) {
+#pragma unroll
+        for (int u = 0; u < EL4; ++u) {
+            const int e = (tid + u * NTHR) * 4;
             const int i = e / D, f = e % D;
-            f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = x;
+            kreg[u] = vreg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (i < valid) {
-                x = load4(kh + (size_t)(t0 + i) * D + f);
-                if (which) y = load4(vh + (size_t)(t0 + i) * D + f);
+                kreg[u] = load4(kh + (size_t)(t0 + i) * D + f);
+                if (which) vreg[u] = load4(vh + (size_t)(t0 + i) * D + f);
             }
-            *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = x;
-            if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = y;
+        }
+        if (w == 0) greg = lane < valid ? gh[t0 + lane] : 1.0f;
+    };
+    if (n_chunks > 0) prefetch(0);
+
+    for (int c = 0; c < n_chunks; ++c) {
+        // ---- stage the chunk's keys (and values) in LDS as fp32 ----
+#pragma unroll
+        for (int u = 0; u < EL4; ++u) {
+            const int e = (tid + u * NTHR) * 4;
+            const int i = e / D, f = e % D;
+            *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = kreg[u];
+            if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = vreg[u];
         }
         if (w == 0) {
-            const float l = chunk_log_decay(gh + t0, valid, lane);
+            // within-chunk log decays (tokens past the end count as gamma = 1)
+            float l = __logf(greg);
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float t = __shfl_up(l, o, 64);
+                if (lane >= o) l += t;
+            }
             const float lend = __shfl(l, C - 1, 64);
             if (lane < C) sW[lane] = __expf(lend - l);
             if (lane == 0) sGam = __expf(lend);
         }
         __syncthreads();
+        if (c + 1 < n_chunks) prefetch(c + 1);
 
         // ---- the state before this chunk ----
         if (write_chunks) {

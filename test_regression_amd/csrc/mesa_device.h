@@ -17,9 +17,16 @@ namespace mesa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// LDS row pitch (floats): the row length rounded up to 64 plus 4, so that the
-// access patterns of the MFMA operand loads are free of bank conflicts.
+// LDS row pitches (floats), measured on gfx950 for the kernels' patterns:
+//  - lds_pitch (row length rounded up to 64, plus 4): conflict-free for
+//    32-bit accesses where 16 lanes walk a row and the 4 lane groups take 4
+//    consecutive rows (the MFMA operand staging and column reads), and a
+//    2-way conflict for 128-bit row reads;
+//  - lds_pitch_rows (plus 8): conflict-free for 128-bit reads where 16 lanes
+//    take 16 consecutive rows and the 4 lane groups 4 consecutive 16-byte
+//    pieces of a row; used for tiles that are only ever read that way.
 __host__ __device__ constexpr int lds_pitch(int n) { return ((n + 63) / 64) * 64 + 4; }
+__host__ __device__ constexpr int lds_pitch_rows(int n) { return ((n + 63) / 64) * 64 + 8; }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

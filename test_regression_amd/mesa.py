@@ -32,6 +32,10 @@ SIGNATURES = {
     "mesa_profile_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "mesa_profile_reset": ([], _I),
     "mesa_kernel_name": ([_I], ctypes.c_char_p),
+    # include/mesa_probe.h
+    "mesa_probe_mfma_f32": ([_I, _I, _P, _P], _I),
+    "mesa_probe_mfma_bf16": ([_I, _I, _P, _P], _I),
+    "mesa_probe_copy": ([_P, _P, _Z, _P], _I),
 }
 
 _lib = None
@@ -191,6 +195,19 @@ def profile_read(kernel_id: int):
     n = ctypes.c_int64(0)
     _check(lib().mesa_profile_read(kernel_id, ctypes.byref(ms), ctypes.byref(n)), "mesa_profile_read")
     return ms.value, n.value
+
+
+def probe_mfma(dtype: str, n_workgroups: int, iters: int, sink, stream=None):
+    """Launch the register-resident MFMA probe ("f32" or "bf16"); returns its flops."""
+    fn = lib().mesa_probe_mfma_f32 if dtype == "f32" else lib().mesa_probe_mfma_bf16
+    _check(fn(n_workgroups, iters, _ptr(sink), _stream(stream)), "mesa_probe_mfma")
+    return n_workgroups * 4 * iters * 8 * (2048 if dtype == "f32" else 16384)
+
+
+def probe_copy(src, dst, stream=None):
+    """Launch the streaming-copy probe over src.numel() bytes of src (uint8) into dst."""
+    _check(lib().mesa_probe_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(), _stream(stream)),
+           "mesa_probe_copy")
 
 
 def kernel_name(kernel_id: int) -> str:

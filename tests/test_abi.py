@@ -13,16 +13,18 @@ import pytest
 from test_regression_amd import mesa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mesa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("mesa.h", "mesa_probe.h")]
 
 OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = range(5)
 FAKE = 0x10000          # 16-byte aligned, never dereferenced
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mesa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mesa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -136,6 +138,16 @@ def test_decode_rejects_bad_arguments(kw, status, needle):
     st, msg = dec(**kw)
     assert st == status, (st, msg)
     assert needle in msg
+
+
+def test_probe_argument_validation():
+    L = mesa.lib()
+    assert L.mesa_probe_mfma_f32(0, 10, FAKE, None) == INVALID
+    assert L.mesa_probe_mfma_bf16(4, 0, FAKE, None) == INVALID
+    assert L.mesa_probe_mfma_f32(4, 10, None, None) == INVALID
+    assert L.mesa_probe_copy(FAKE, FAKE, 100, None) == INVALID          # not a multiple of 16
+    assert L.mesa_probe_copy(FAKE + 4, FAKE, 160, None) == INVALID      # misaligned
+    assert L.mesa_probe_copy(None, FAKE, 160, None) == INVALID
 
 
 def test_profile_api_host_paths():
