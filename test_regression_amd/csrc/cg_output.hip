@@ -9,59 +9,111 @@
 //    attention pass and runs chunk-parallel on the states H_t, G_t;
 //  - bullet "Computacao Dinamica": the iteration count varies per token.
 //
-// Chunkwise form used here (chunk c covers tokens t0..t0+C-1, l_t the
-// within-chunk prefix sum of ln gamma, S^H_c = H_{t0-1}, S^G_c = G_{t0-1}):
+// Chunkwise form (chunk c covers tokens t0..t0+C-1, l_t the within-chunk
+// prefix sum of ln gamma, S^H_c = H_{t0-1}, S^G_c = G_{t0-1}):
 //   H_t p = e^{l_t} S^H_c p + sum_{i=t0..t} e^{l_t - l_i} (k_i . p) k_i
 //   G_t x = e^{l_t} S^G_c x + sum_{i=t0..t} e^{l_t - l_i} (k_i . x) v_i
-// For the C tokens of a chunk at once (P, K, V in R^{C x d},
-// M_ti = e^{l_t - l_i} [i <= t]):
-//   Y = diag(e^l) P S^H_c + (M o (P K^T)) K + P diag(lambda)
-//   O = diag(e^l) X (S^G_c)^T + (M o (X K^T)) V
-// The keys are both the "keys" and the "values" of the CG matvec and do not
-// change between iterations, so S^H_c and K_c stay in LDS for every
-// iteration.
+// The keys are both the "keys" and the "values" of the CG matvec and never
+// change between iterations, so everything the matvec needs stays in LDS.
+//
+// Sub-chunk states.  H is symmetric, so only the upper triangle of 16x16
+// blocks of a state is kept in LDS; that leaves room for a second state,
+//   S_mid = H_{t0+h-1} = e^{l_{h-1}} S^H_c + sum_{i<h} e^{l_{h-1}-l_i} k_i k_i^T,
+// the state at the middle of the chunk (h = C/2), formed once per chunk.
+// Tokens in the second half then use S_mid and need intra-chunk terms only
+// against the keys of the second half, which halves the causal work of the
+// waves that had the most of it.
 //
 // Work split: one workgroup per (head, chunk); wave w owns tokens
-// 16w..16w+15 of the chunk and runs their CG entirely on its own: the state
-// and key tiles in LDS are read-only during the iterations, so the CG loop
-// has no workgroup barrier and waves stop independently.  Each wave runs a
-// body specialised on w, so its causal block count (w + 1 key blocks) is a
-// compile-time constant.  All contractions use v_mfma_f32_16x16x4_f32; the
-// CG vectors x, r, p, y live in registers in MFMA accumulator layout, so the
-// alpha/beta dot products are 16-lane DPP row reductions.
+// 16w..16w+15 and runs their CG entirely on its own: the tiles in LDS are
+// read-only during the iterations, so the CG loop has no workgroup barrier
+// and waves stop independently.  Each wave runs a body specialised on w
+// (static sub-chunk, causal block range).  All contractions use
+// v_mfma_f32_16x16x4_f32; x, r, p, y live in registers in MFMA accumulator
+// layout and the alpha/beta dot products are 16-lane DPP row reductions.
+// Every MFMA chain starts from zero and is only read afterwards.
 //
-// Operand loads: the contraction index of every MFMA is mapped so that a
-// lane's four k-values are contiguous, and every B operand that is a matrix
-// row in LDS (S^H, which is symmetric; G, stored row-major; the key rows of
-// the scores) is read 128 bits at a time.  The next k-group's operands are
-// loaded before the current group's MFMAs are issued: with one wave per
-// SIMD (the tiles take ~150 KiB of LDS) the wave hides its own LDS latency.
+// Operand loads: a lane's four k-values of an MFMA are contiguous, so row
+// operands are 128-bit LDS reads; a state block read along its columns is
+// four 32-bit reads.  The next k-group's operands are loaded before the
+// current group's MFMAs issue: one wave per SIMD fits (the tiles take
+// ~157 KiB of LDS), so the wave hides its own LDS latency.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
 namespace mesa {
 
+constexpr int kBlockPitch = 20;   // floats per row of a stored 16x16 state block
+
 template <int D, int C>
-struct CgLds {
+struct alignas(16) CgLds {
     static constexpr int NW = C / 16;
+    static constexpr int NT = D / 16;
+    static constexpr int NBLK = NT * (NT + 1) / 2;       // upper-triangle blocks
+    static constexpr int HALF = NBLK * 16 * kBlockPitch;  // floats per stored state
+    static constexpr int NSTATE = NW >= 2 ? 2 : 1;
     static constexpr int PD = lds_pitch(D);
     static constexpr int PS = lds_pitch_rows(D);
-    static constexpr int PC = lds_pitch(C);
-    float S[D * PS];          // S^H_c, later G_c           [row][feature]
-    float KV[C * PD];         // K_c, later V_c             [token][feature]
-    float P[NW][16 * PD];     // per wave: P (later X) rows, MFMA A staging
-    float A[NW][16 * PC];     // per wave: decayed scores M o (Z K^T)
+    static constexpr int REGION = NSTATE * HALF > D * PS ? NSTATE * HALF : D * PS;
+    float R[REGION];          // CG: stored S^H_c [, S_mid];  output: G_c full [D][PS]
+    float KV[C * PD];         // K_c, later V_c   [token][feature]
+    float P[NW][16 * PD];     // per wave: P / decayed scores / X rows
     float L[C];               // l_i
     float Lam[D];
 };
 
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-// Y[j]  += sum_f Z[m][f] * Bs[16j + n][f]      (if STATE; Bs symmetric or row-major G)
-// Sc[ib] += sum_f Z[m][f] * Bk[16ib + n][f]    (ib < NB; the score blocks)
-// Z, Bk: LDS rows of pitch lds_pitch(D); Bs: pitch lds_pitch_rows(D).  Software-pipelined over the
-// 16-wide k-groups: group g+1's operands are in flight while group g's MFMAs
-// issue.
+// Offset (floats) of stored block (a, b), a <= b, of an NT x NT block triangle.
+template <int NT>
+__host__ __device__ constexpr int blk(int a, int b) {
+    return (a * NT - a * (a - 1) / 2 + (b - a)) * 16 * kBlockPitch;
+}
+
+// Y[j]   += sum_f Z[m][f] * S[f][16j + n]   (S symmetric, upper block triangle stored)
+// Sc[ib] += sum_f Z[m][f] * K[KB0+ib][n][f] (NB score blocks against key rows)
+// Z: wave's staged rows (pitch lds_pitch(D)); K rows: pitch lds_pitch(D).
+// For k-group g and output block j, S[16g + k][16j + n] is stored block (g, j)
+// read down its columns when g <= j, else block (j, g) read along row n.
+template <int D, int NB, int KB0>
+__device__ __forceinline__ void contract_state_scores(const float* Z, const float* Sst, const float* Kr, int n,
+                                                      int kk, f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB]) {
+    constexpr int NT = D / 16;
+    constexpr int PD = lds_pitch(D);
+    const float* za = Z + n * PD + 4 * kk;
+    f32x4 a[2], bs[2][NT], bk[2][NB];
+    auto load = [&](int g, int buf) {
+        a[buf] = lds4(za + 16 * g);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            if (g > j) {
+                bs[buf][j] = lds4(Sst + blk<NT>(j, g) + n * kBlockPitch + 4 * kk);
+            } else {
+                const float* col = Sst + blk<NT>(g, j) + (4 * kk) * kBlockPitch + n;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) bs[buf][j][s] = col[s * kBlockPitch];
+            }
+        }
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) bk[buf][ib] = lds4(Kr + (16 * (KB0 + ib) + n) * PD + 16 * g + 4 * kk);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        const int cur = g & 1;
+        if (g + 1 < NT) load(g + 1, cur ^ 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) Y[j] = mfma4(a[cur][s], bs[cur][j][s], Y[j]);
+#pragma unroll
+            for (int ib = 0; ib < NB; ++ib) Sc[ib] = mfma4(a[cur][s], bk[cur][ib][s], Sc[ib]);
+        }
+    }
+}
+
+// Y[j] += sum_f Z[m][f] * Bs[16j + n][f] (Bs full, row-major, pitch lds_pitch_rows(D));
+// Sc[ib] += sum_f Z[m][f] * K[16ib + n][f] for ib < NB.
 template <int D, int NB, bool STATE>
 __device__ __forceinline__ void contract_rows(const float* Z, const float* Bs, const float* Bk, int n, int kk,
                                               f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB > 0 ? NB : 1]) {
@@ -99,23 +151,23 @@ __device__ __forceinline__ void contract_rows(const float* Z, const float* Bs, c
     }
 }
 
-// Y[j] += sum_{i < 16 NB} A[m][i] * B[i][16j + n]   (A: per-wave scores,
-// pitch lds_pitch(C); B: K or V tile rows, pitch lds_pitch(D)).
-template <int D, int C, int NB>
+// Y[j] += sum_{ib < NB} sum_i A[m][16ib + i] * B[16(KB0 + ib) + i][16j + n]
+// A: decayed scores (columns relative to key block KB0, pitch lds_pitch(D));
+// B: K or V tile rows (pitch lds_pitch(D)).
+template <int D, int NB, int KB0>
 __device__ __forceinline__ void contract_intra(const float* A, const float* B, int n, int kk, f32x4 (&Y)[D / 16]) {
     constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
-    constexpr int PC = lds_pitch(C);
     float b[2][NT];
     auto load = [&](int ib, int s, int buf) {
-        const float* brow = B + (16 * ib + 4 * kk + s) * PD + n;
+        const float* brow = B + (16 * (KB0 + ib) + 4 * kk + s) * PD + n;
 #pragma unroll
         for (int j = 0; j < NT; ++j) b[buf][j] = brow[16 * j];
     };
     load(0, 0, 0);
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib) {
-        const f32x4 a4 = lds4(A + n * PC + 16 * ib + 4 * kk);
+        const f32x4 a4 = lds4(A + n * PD + 16 * ib + 4 * kk);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int step = 4 * ib + s, cur = step & 1;
@@ -126,7 +178,7 @@ __device__ __forceinline__ void contract_intra(const float* A, const float* B, i
     }
 }
 
-// Stage a wave's 16 rows (MFMA accumulator layout) as A-operand rows in LDS.
+// Stage a wave's 16 rows (MFMA accumulator layout) as rows of its LDS region.
 template <int D>
 __device__ __forceinline__ void stage_rows(float* dst, const f32x4 (&V)[D / 16], int n, int kk) {
     constexpr int PD = lds_pitch(D);
@@ -137,15 +189,49 @@ __device__ __forceinline__ void stage_rows(float* dst, const f32x4 (&V)[D / 16],
     wave_lds_sync();
 }
 
-template <int C, int NB>
+// Write decayed score blocks (columns relative to the first block) as rows.
+template <int D, int NB>
 __device__ __forceinline__ void stage_scores(float* dst, const f32x4 (&Sc)[NB], const float (&dec)[NB][4], int n,
                                              int kk) {
-    constexpr int PC = lds_pitch(C);
+    constexpr int PD = lds_pitch(D);
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * kk + r) * PC + 16 * ib + n] = Sc[ib][r] * dec[ib][r];
+        for (int r = 0; r < 4; ++r) dst[(4 * kk + r) * PD + 16 * ib + n] = Sc[ib][r] * dec[ib][r];
     wave_lds_sync();
+}
+
+// S_mid (upper block triangle) = e^{l_{h-1}} S0 + sum_{i<h} e^{l_{h-1}-l_i} k_i k_i^T,
+// blocks distributed over the NW waves.  Written to S1.
+template <int D, int C>
+__device__ __forceinline__ void form_mid_state(CgLds<D, C>& L, int w, int n, int kk) {
+    constexpr int NT = D / 16;
+    constexpr int NW = C / 16;
+    constexpr int H = C / 2;
+    constexpr int PD = lds_pitch(D);
+    const float* S0 = L.R;
+    float* S1 = L.R + CgLds<D, C>::HALF;
+    const float lh = L.L[H - 1];
+    const float Gh = __expf(lh);
+    int q = 0;
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+#pragma unroll
+        for (int b = a; b < NT; ++b, ++q) {
+            if (q % NW != w) continue;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < H / 4; ++st) {
+                const int i = 4 * st + kk;
+                const float wi = __expf(lh - L.L[i]);
+                acc = mfma4(wi * L.KV[i * PD + 16 * a + n], L.KV[i * PD + 16 * b + n], acc);
+            }
+            const float* s0 = S0 + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n;
+            float* s1 = S1 + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s1[r * kBlockPitch] = Gh * s0[r * kBlockPitch] + acc[r];
+        }
+    }
 }
 
 // The CG of wave W (tokens 16W..16W+15 of the chunk) and its output rows.
@@ -155,29 +241,40 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
                                         int valid, int max_iters, float tol, float* __restrict__ out,
                                         int32_t* __restrict__ iters) {
     constexpr int NT = D / 16;
-    constexpr int NB = W + 1;          // causal key blocks of this wave
+    constexpr int NW = C / 16;
+    constexpr int SUB = (NW >= 2 && W >= NW / 2) ? 1 : 0;   // which stored state
+    constexpr int KB0 = SUB ? NW / 2 : 0;                    // first key block of the sub-chunk
+    constexpr int NB = W - KB0 + 1;                          // causal key blocks in the CG
+    constexpr int NBO = W + 1;                               // causal key blocks of the output
     constexpr int PD = lds_pitch(D);
     constexpr int PS = lds_pitch_rows(D);
-    constexpr int NTHR = 64 * (C / 16);
+    constexpr int NTHR = 64 * NW;
     const int lane = tid & 63;
     const int n = lane & 15;
     const int kk = lane >> 4;
     float* myP = L.P[W];
-    float* myA = L.A[W];
+    const float* Sst = L.R + SUB * CgLds<D, C>::HALF;
 
     // ---- per-lane constants; lane rows are chunk tokens 16W + 4kk + r ----
-    float eL[4];
-    float dec[NB][4];
+    const float lbase = SUB ? L.L[16 * KB0 - 1] : 0.f;   // l at the end of the first half
+    float eL[4], eLo[4];
+    float dec[NBO][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int tr = 16 * W + 4 * kk + r;
-        eL[r] = __expf(L.L[tr]);
+        eL[r] = __expf(L.L[tr] - lbase);
+        eLo[r] = __expf(L.L[tr]);
 #pragma unroll
-        for (int ib = 0; ib < NB; ++ib) {
+        for (int ib = 0; ib < NBO; ++ib) {
             const int i = 16 * ib + n;
             dec[ib][r] = (i <= tr) ? __expf(L.L[tr] - L.L[i]) : 0.f;
         }
     }
+    float decs[NB][4];   // the sub-chunk's blocks
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) decs[ib][r] = dec[KB0 + ib][r];
     float lamc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) lamc[j] = L.Lam[16 * j + n];
@@ -223,10 +320,8 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
         }
         if (__builtin_amdgcn_ballot_w64(alive) == 0) break;
 
-        // Y = diag(e^l) P S^H + (M o (P K^T)) K + diag(lambda) P.  Each MFMA
-        // chain starts from zero and is only read afterwards (never written
-        // back into), so the state and intra-chunk sums use separate
-        // accumulators and are combined on the VALU.
+        // Y = diag(e^{l - lbase}) P S + (M o (P K^T)) K + diag(lambda) P over
+        // the sub-chunk; state and intra-chunk sums in separate accumulators.
         f32x4 Y[NT];
         {
             f32x4 YS[NT], YI[NT], Sc[NB];
@@ -234,9 +329,9 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
             for (int j = 0; j < NT; ++j) YS[j] = YI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ib = 0; ib < NB; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-            contract_rows<D, NB, true>(myP, L.S, L.KV, n, kk, YS, Sc);
-            stage_scores<C, NB>(myA, Sc, dec, n, kk);
-            contract_intra<D, C, NB>(myA, L.KV, n, kk, YI);
+            contract_state_scores<D, NB, KB0>(myP, Sst, L.KV, n, kk, YS, Sc);
+            stage_scores<D, NB>(myP, Sc, decs, n, kk);     // P rows are consumed: reuse the region
+            contract_intra<D, NB, KB0>(myP, L.KV, n, kk, YI);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -288,18 +383,18 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
         }
     }
 
-    // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V ----
+    // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk ----
     stage_rows<D>(myP, X, n, kk);
+    f32x4 Sc[NBO];
     {
-        f32x4 unused[NT], Sc[NB];
+        f32x4 unused[NT];
 #pragma unroll
-        for (int ib = 0; ib < NB; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-        contract_rows<D, NB, false>(myP, nullptr, L.KV, n, kk, unused, Sc);
-        stage_scores<C, NB>(myA, Sc, dec, n, kk);
+        for (int ib = 0; ib < NBO; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        contract_rows<D, NBO, false>(myP, nullptr, L.KV, n, kk, unused, Sc);
     }
-    __syncthreads();   // every wave is done with S^H_c and K_c
+    __syncthreads();   // every wave is done with the states and K_c
     for (int e = tid * 4; e < D * D; e += NTHR * 4)
-        *reinterpret_cast<f32x4*>(&L.S[(e / D) * PS + e % D]) = *reinterpret_cast<const f32x4*>(Gc + e);
+        *reinterpret_cast<f32x4*>(&L.R[(e / D) * PS + e % D]) = *reinterpret_cast<const f32x4*>(Gc + e);
     for (int e = tid * 4; e < C * D; e += NTHR * 4) {
         const int i = e / D;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -310,14 +405,15 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
     f32x4 OS[NT], OI[NT], none[1];
 #pragma unroll
     for (int j = 0; j < NT; ++j) OS[j] = OI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    contract_rows<D, 0, true>(myP, L.S, nullptr, n, kk, OS, none);
-    contract_intra<D, C, NB>(myA, L.KV, n, kk, OI);
+    contract_rows<D, 0, true>(myP, L.R, nullptr, n, kk, OS, none);
+    stage_scores<D, NBO>(myP, Sc, dec, n, kk);   // X rows are consumed: reuse the region
+    contract_intra<D, NBO, 0>(myP, L.KV, n, kk, OI);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * W + 4 * kk + r;
-            if (row < valid) out[(tok0 + row) * D + 16 * j + n] = eL[r] * OS[j][r] + OI[j][r];
+            if (row < valid) out[(tok0 + row) * D + 16 * j + n] = eLo[r] * OS[j][r] + OI[j][r];
         }
 }
 
@@ -328,8 +424,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     const float* __restrict__ SH, const float* __restrict__ SG, int H, int T, int n_chunks,
     int max_iters, float tol, float* __restrict__ out, int32_t* __restrict__ iters) {
     constexpr int NW = C / 16;
+    constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
-    constexpr int PS = lds_pitch_rows(D);
     constexpr int NTHR = 64 * NW;
     __shared__ CgLds<D, C> L;
 
@@ -344,9 +440,13 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     const size_t tok0 = (size_t)bh * T + t0;   // first token of the chunk
     const size_t soff = ((size_t)bh * n_chunks + c) * D * D;
 
-    // ---- stage S^H_c, K_c, lambda, l ----
-    for (int e = tid * 4; e < D * D; e += NTHR * 4)
-        *reinterpret_cast<f32x4*>(&L.S[(e / D) * PS + e % D]) = *reinterpret_cast<const f32x4*>(SH + soff + e);
+    // ---- stage the upper block triangle of S^H_c, K_c, lambda, l ----
+    for (int e = tid * 4; e < D * D; e += NTHR * 4) {
+        const int i = e / D, j = e % D;
+        if (i / 16 <= j / 16)
+            *reinterpret_cast<f32x4*>(&L.R[blk<NT>(i / 16, j / 16) + (i % 16) * kBlockPitch + j % 16]) =
+                *reinterpret_cast<const f32x4*>(SH + soff + e);
+    }
     for (int e = tid * 4; e < C * D; e += NTHR * 4) {
         const int i = e / D;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -359,6 +459,10 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
         if (lane < C) L.L[lane] = l;
     }
     __syncthreads();
+    if constexpr (NW >= 2) {
+        form_mid_state<D, C>(L, w, lane & 15, lane >> 4);
+        __syncthreads();
+    }
 
     const float* Gc = SG + soff;
     if (w == 0) {
