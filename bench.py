@@ -119,8 +119,9 @@ def headline(torch, mesa, inputs, args, dev):
     k2_ms = k2[0] / max(k2[1], 1)
     k1_ms = k1[0] / max(k1[1], 1)
     k2_flops = (fcg + fo) * n_tok
-    # chunk-state kernel: reads k, v (bf16) and gamma, writes S^H and S^G once
-    k1_bytes = n_tok * (2 * w.d * 2 + 4) + 2 * (w.B * w.H * (w.T // w.chunk) * w.d * w.d * 4)
+    # chunk-state kernel: reads k, v (bf16) and gamma once; writes each chunk's
+    # S^H (packed upper 16x16-block triangle, d(d+16)/2 floats) and S^G (d*d)
+    k1_bytes = n_tok * (2 * w.d * 2 + 4) + w.B * w.H * (w.T // w.chunk) * (w.d * (w.d + 16) // 2 + w.d * w.d) * 4
     achieved = k2_flops / (k2_ms * 1e-3) / 1e12
     traffic = measured_traffic()
     res = dict(

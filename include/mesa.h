@@ -85,8 +85,9 @@ const char *mesa_last_error_message(void);
 
 /*
  * Bytes of device workspace mesa_forward needs for these sizes: the
- * chunk-boundary states S^H_c = H_{c*chunk-1} and S^G_c (fp32, d*d each per
- * chunk and head).  Returns 0 if the sizes are invalid.
+ * chunk-boundary states S^H_c = H_{c*chunk-1} (symmetric; its upper triangle
+ * of 16x16 blocks, dk (dk + 16) / 2 floats) and S^G_c (dv * dk floats), fp32,
+ * per chunk and head.  Returns 0 if the sizes are invalid.
  */
 size_t mesa_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 

@@ -438,15 +438,14 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     const int t0 = c * C;
     const int valid = min(C, T - t0);
     const size_t tok0 = (size_t)bh * T + t0;   // first token of the chunk
+    constexpr int HPACK = D * (D + 16) / 2;    // packed upper block triangle of S^H
+    const size_t hoff = ((size_t)bh * n_chunks + c) * HPACK;
     const size_t soff = ((size_t)bh * n_chunks + c) * D * D;
 
-    // ---- stage the upper block triangle of S^H_c, K_c, lambda, l ----
-    for (int e = tid * 4; e < D * D; e += NTHR * 4) {
-        const int i = e / D, j = e % D;
-        if (i / 16 <= j / 16)
-            *reinterpret_cast<f32x4*>(&L.R[blk<NT>(i / 16, j / 16) + (i % 16) * kBlockPitch + j % 16]) =
-                *reinterpret_cast<const f32x4*>(SH + soff + e);
-    }
+    // ---- stage S^H_c (packed 16x16 upper blocks, in blk order), K_c, lambda, l ----
+    for (int e = tid * 4; e < HPACK; e += NTHR * 4)
+        *reinterpret_cast<f32x4*>(&L.R[(e / 256) * 16 * kBlockPitch + ((e % 256) / 16) * kBlockPitch + e % 16]) =
+            *reinterpret_cast<const f32x4*>(SH + hoff + e);
     for (int e = tid * 4; e < C * D; e += NTHR * 4) {
         const int i = e / D;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -464,6 +463,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
         __syncthreads();
     }
 
+    (void)NT;
     const float* Gc = SG + soff;
     if (w == 0) {
         cg_wave<D, C, 0, In>(L, tid, q, v, Gc, tok0, valid, max_iters, tol, out, iters);

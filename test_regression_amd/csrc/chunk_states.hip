@@ -12,8 +12,10 @@
 // chunk (the state before the chunk's first token) and, optionally, the final
 // state after the last token.
 //
-// Both states are stored row-major ([d][d_k], rows are key features for H
-// and value features for G), the layout of the exported final states.
+// Chunk states in the workspace: G row-major ([d_v][d_k], the layout of the
+// exported final G); H, which is symmetric, as its packed upper triangle of
+// 16 x 16 blocks (block (a, b), a <= b, in row-major block order, each block
+// row-major) -- the part the CG kernel reads.  The exported final H is full.
 //
 // Work split: one workgroup per (head, {H, G}, 16*NW-row block of the
 // state); each wave holds a 16 x D slab of the running state in MFMA
@@ -28,16 +30,46 @@
 
 namespace mesa {
 
-template <int D, int C, typename In>
-__global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kernel(
+// Registers holding 4 prefetched input elements (bf16 stays packed until staged).
+template <typename In> struct Raw4;
+template <> struct Raw4<float> {
+    f32x4 v;
+    __device__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+    __device__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ f32x4 get() const { return v; }
+};
+template <> struct Raw4<bf16_t> {
+    uint2 v;
+    __device__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ void zero() { v = make_uint2(0u, 0u); }
+    __device__ f32x4 get() const {
+        return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xffff0000u)};
+    }
+};
+
+// Offset (floats) of block (a, b), a <= b, in the packed upper block triangle
+// of a d x d state (16 x 16 blocks stored row-major one after another).
+template <int NT>
+__device__ __forceinline__ int packed_blk(int a, int b) {
+    return (a * NT - a * (a - 1) / 2 + (b - a)) * 256;
+}
+
+// NWK: waves per workgroup (each owns 16 rows of the state).  With
+// NWK = D / 16 a workgroup holds a whole state (one per head for H, one for
+// G); fewer waves split a state into RB row blocks, giving more workgroups
+// for problems with few heads.
+template <int D, int C, int NWK, typename In>
+__global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
     int T, int n_chunks, float* __restrict__ SH, float* __restrict__ SG,
     float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks, long BH) {
-    constexpr int NW = D >= 64 ? 4 : D / 16;   // waves per workgroup
+    constexpr int NW = NWK;                    // waves per workgroup
     constexpr int RB = D / (16 * NW);          // row blocks per state
     constexpr int NT = D / 16;                 // 16-column tiles of the state
     constexpr int PD = lds_pitch(D);
     constexpr int NTHR = 64 * NW;
+    constexpr int HPACK = D * (D + 16) / 2;    // floats of a packed upper block triangle
 
     __shared__ float sK[C * PD];   // keys of the chunk (B operand; A rows for H)
     __shared__ float sB[C * PD];   // values of the chunk (A rows for G)
@@ -60,52 +92,55 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
     const int rb = part % RB;
     const int which = part / RB;               // 0: H, 1: G
     const int m0 = rb * 16 * NW + 16 * w;      // first state row of this wave
+    const int a0 = m0 / 16;                    // its row block
 
     const In* kh = k + (size_t)bh * T * D;
     const In* vh = v + (size_t)bh * T * D;
     const float* gh = gamma + (size_t)bh * T;
-    float* Sout = (which == 0 ? SH : SG) + (size_t)bh * n_chunks * D * D;
+    // H: packed upper block triangle per chunk; G: full d x d per chunk
+    float* Sout = which == 0 ? SH + (size_t)bh * n_chunks * HPACK : SG + (size_t)bh * n_chunks * D * D;
     const float* sArows = which == 0 ? sK : sB;
 
     f32x4 acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // The next chunk's keys, values and gates are loaded into registers while
-    // the current chunk's MFMAs run (global latency hidden behind compute).
+    // Keys, values and gates of the next two chunks are held in registers
+    // (a two-slot ring), so a chunk's global loads have two chunk steps of
+    // MFMAs and stores to complete behind.
     constexpr int EL4 = C * D / (4 * NTHR);   // 4-element groups per thread per tile
     static_assert(C * D % (4 * NTHR) == 0, "tile must split evenly over the workgroup");
-    f32x4 kreg[EL4], vreg[EL4];
-    float greg = 1.0f;
-    auto prefetch = [&](int c) {
+    Raw4<In> kreg[2][EL4], vreg[2][EL4];
+    float greg[2] = {1.0f, 1.0f};
+    auto prefetch = [&](int c, int sl) {
         const int t0 = c * C;
         const int valid = min(C, T - t0);
 #pragma unroll
         for (int u = 0; u < EL4; ++u) {
             const int e = (tid + u * NTHR) * 4;
             const int i = e / D, f = e % D;
-            kreg[u] = vreg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            kreg[sl][u].zero();
+            vreg[sl][u].zero();
             if (i < valid) {
-                kreg[u] = load4(kh + (size_t)(t0 + i) * D + f);
-                if (which) vreg[u] = load4(vh + (size_t)(t0 + i) * D + f);
+                kreg[sl][u].load(kh + (size_t)(t0 + i) * D + f);
+                if (which) vreg[sl][u].load(vh + (size_t)(t0 + i) * D + f);
             }
         }
-        if (w == 0) greg = lane < valid ? gh[t0 + lane] : 1.0f;
+        if (w == 0) greg[sl] = lane < valid ? gh[t0 + lane] : 1.0f;
     };
-    if (n_chunks > 0) prefetch(0);
 
-    for (int c = 0; c < n_chunks; ++c) {
+    auto step = [&](int c, int sl) {
         // ---- stage the chunk's keys (and values) in LDS as fp32 ----
 #pragma unroll
         for (int u = 0; u < EL4; ++u) {
             const int e = (tid + u * NTHR) * 4;
             const int i = e / D, f = e % D;
-            *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = kreg[u];
-            if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = vreg[u];
+            *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = kreg[sl][u].get();
+            if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = vreg[sl][u].get();
         }
         if (w == 0) {
             // within-chunk log decays (tokens past the end count as gamma = 1)
-            float l = __logf(greg);
+            float l = __logf(greg[sl]);
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const float t = __shfl_up(l, o, 64);
@@ -116,22 +151,32 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
             if (lane == 0) sGam = __expf(lend);
         }
         __syncthreads();
-        if (c + 1 < n_chunks) prefetch(c + 1);
+        if (c + 2 < n_chunks) prefetch(c + 2, sl);
 
         // ---- the state before this chunk ----
         if (write_chunks) {
-            float* dst = Sout + (size_t)c * D * D;
+            float* dst = Sout + (size_t)c * (which == 0 ? HPACK : D * D);
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
+            for (int j = 0; j < NT; ++j) {
+                if (which == 0) {
+                    if (j >= a0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+                        for (int r = 0; r < 4; ++r)
+                            dst[packed_blk<NT>(a0, j) + (4 * kk + r) * 16 + n] = acc[j][r];
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+                }
+            }
         }
 
-        // ---- S <- Gamma_c S + sum_i w_i a_i k_i^T ----
-        const float G = sGam;
+        // ---- S <- Gamma_c S + U,  U = sum_i w_i a_i k_i^T ----
+        // U is a fresh MFMA chain (started from zero, only read afterwards);
+        // the decayed running state is combined with it on the VALU.
+        f32x4 U[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j] *= G;
+        for (int j = 0; j < NT; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < C / 16; ++g) {
 #pragma unroll
@@ -139,10 +184,20 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
                 const int i = 16 * g + 4 * kk + s;
                 const float a = sArows[i * PD + m0 + n] * sW[i];
 #pragma unroll
-                for (int j = 0; j < NT; ++j) acc[j] = mfma4(a, sK[i * PD + 16 * j + n], acc[j]);
+                for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sK[i * PD + 16 * j + n], U[j]);
             }
         }
+        const float G = sGam;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = G * acc[j] + U[j];
         __syncthreads();
+    };
+
+    if (n_chunks > 0) prefetch(0, 0);
+    if (n_chunks > 1) prefetch(1, 1);
+    for (int c = 0; c < n_chunks; c += 2) {
+        step(c, 0);
+        if (c + 1 < n_chunks) step(c + 1, 1);
     }
 
     // ---- final state (after the last token) ----
@@ -156,16 +211,24 @@ __global__ __launch_bounds__(64 * (D >= 64 ? 4 : D / 16)) void chunk_states_kern
     }
 }
 
-template <int D, int C, typename In>
-hipError_t launch_chunk_states_t(const ChunkStatesArgs& a, hipStream_t s) {
-    constexpr int NW = D >= 64 ? 4 : D / 16;
+template <int D, int C, int NW, typename In>
+hipError_t launch_chunk_states_nw(const ChunkStatesArgs& a, hipStream_t s) {
     constexpr int RB = D / (16 * NW);
     // ids: 8 XCD lanes x (heads rounded up to a multiple of 8) / 8 x parts
     const long grid = ((a.BH + 7) / 8) * 8 * 2 * RB;
-    hipLaunchKernelGGL((chunk_states_kernel<D, C, In>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+    hipLaunchKernelGGL((chunk_states_kernel<D, C, NW, In>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
                        (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG,
                        a.final_H, a.final_G, a.write_chunks, a.BH);
     return hipGetLastError();
+}
+
+template <int D, int C, typename In>
+hipError_t launch_chunk_states_t(const ChunkStatesArgs& a, hipStream_t s) {
+    // Four waves (64 state rows) per workgroup.  Eight waves (a whole d = 128
+    // state per workgroup) would share the key tile better, but must fit two
+    // waves per SIMD in 256 registers, where the compiler's allocation
+    // rewrites MFMA accumulator inputs early (see codegen_check).
+    return launch_chunk_states_nw<D, C, (D >= 64 ? 4 : D / 16), In>(a, s);
 }
 
 template <int D, typename In>

@@ -113,8 +113,10 @@ const char* mesa_last_error_message(void) { return g_err.c_str(); }
 
 size_t mesa_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+    // per chunk and head: the packed upper 16x16-block triangle of H
+    // (dk (dk + 16) / 2 floats) and the full G (dv x dk); both fp32
     const size_t nc = ((size_t)T + chunk - 1) / chunk;
-    return (size_t)B * H * nc * ((size_t)dk * dk + (size_t)dv * dk) * sizeof(float);
+    return (size_t)B * H * nc * ((size_t)dk * (dk + 16) / 2 + (size_t)dv * dk) * sizeof(float);
 }
 
 mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dtype,
@@ -156,7 +158,7 @@ mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dt
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int bf16 = qkv_dtype == MESA_DTYPE_BF16;
     float* SH = static_cast<float*>(workspace);
-    float* SG = need_ws ? SH + (size_t)BH * n_chunks * dk * dk : nullptr;
+    float* SG = need_ws ? SH + (size_t)BH * n_chunks * ((size_t)dk * (dk + 16) / 2) : nullptr;
 
     if (T == 0) {
         // Nothing to solve; the final states are the zero initial states.
