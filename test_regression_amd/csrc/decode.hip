@@ -11,10 +11,11 @@
 //
 // Work split: one 256-thread workgroup per head.  Thread (row, part) keeps
 // D/TPR consecutive entries of one row of H in registers for the whole solve,
-// so H is read once and written once; the matvec reads p from LDS.  The CG
-// scalars are block reductions with a fixed order (deterministic), and the
-// stop test is block-uniform.  The step is bound by HBM traffic on the two
-// d x d states (read + write of H and G).
+// so H is read once and written once; the matvec reads p from LDS.  The
+// matching entries of G are requested together with H's, so they arrive
+// while the CG runs.  The CG scalars are block reductions with a fixed order
+// (deterministic), and the stop test is block-uniform.  The step is bound by
+// HBM traffic on the two d x d states (read + write of H and G).
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -38,7 +39,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const int h = (int)(nh % H);
     const int row = tid / TPR;
     const int part = tid % TPR;
-    const int c0 = part * EPT;
+    // Column of this thread's e-th entry: the TPR threads of a row interleave
+    // their 4-float pieces, so one 16-byte load instruction of a wave covers
+    // TPR * 16 contiguous bytes of each row it touches.
+    auto col = [&](int e) {
+        if constexpr (EPT % 4 == 0) return (((e >> 2) * TPR + part) << 2) + (e & 3);
+        else return part * EPT + e;
+    };
 
     if (tid < D) {
         sq[tid] = to_f32(q[nh * D + tid]);
@@ -63,24 +70,40 @@ __global__ __launch_bounds__(256) void decode_kernel(
         return val;
     };
 
-    // ---- H <- gamma H + k k^T, kept in registers ----
-    float hr[EPT];
-    float* Hrow = SH + (size_t)nh * D * D + (size_t)row * D + c0;
-    const float kr = sk[row];
+    // ---- load this thread's pieces of H and G; H <- gamma H + k k^T ----
+    float hr[EPT], gr[EPT];
+    float* Hrow = SH + (size_t)nh * D * D + (size_t)row * D;
+    float* Grow = SG + (size_t)nh * D * D + (size_t)row * D;
     if constexpr (EPT % 4 == 0) {
 #pragma unroll
         for (int e = 0; e < EPT; e += 4) {
-            f32x4 x = *reinterpret_cast<const f32x4*>(Hrow + e);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(Hrow + col(e));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) hr[e + u] = g * x[u] + kr * sk[c0 + e + u];
-            *reinterpret_cast<f32x4*>(Hrow + e) = f32x4{hr[e], hr[e + 1], hr[e + 2], hr[e + 3]};
+            for (int u = 0; u < 4; ++u) hr[e + u] = x[u];
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+            const f32x4 y = *reinterpret_cast<const f32x4*>(Grow + col(e));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) gr[e + u] = y[u];
         }
     } else {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            hr[e] = g * Hrow[e] + kr * sk[c0 + e];
-            Hrow[e] = hr[e];
+            hr[e] = Hrow[col(e)];
+            gr[e] = Grow[col(e)];
         }
+    }
+    const float kr = sk[row];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) hr[e] = g * hr[e] + kr * sk[col(e)];
+    if constexpr (EPT % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4)
+            *reinterpret_cast<f32x4*>(Hrow + col(e)) = f32x4{hr[e], hr[e + 1], hr[e + 2], hr[e + 3]};
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) Hrow[col(e)] = hr[e];
     }
 
     // ---- CG on (H + diag lambda) x = q from x = 0 ----
@@ -94,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
         if ((tol > 0.f && sqrtf(rr) / nq < tol) || rr == 0.f) break;
         float y = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) y += hr[e] * sp[c0 + e];
+        for (int e = 0; e < EPT; ++e) y += hr[e] * sp[col(e)];
         y = row_sum(y) + lam_r * p_r;
         const float pap = block_sum(part == 0 ? p_r * y : 0.f, 1);
         if (!(pap > 0.f)) break;
@@ -113,28 +136,20 @@ __global__ __launch_bounds__(256) void decode_kernel(
     __syncthreads();
 
     // ---- G <- gamma G + v k^T (in place), out = G x ----
-    float* Grow = SG + (size_t)nh * D * D + (size_t)row * D + c0;
     const float vr = sv[row];
     float o = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        gr[e] = g * gr[e] + vr * sk[col(e)];
+        o += gr[e] * sx[col(e)];
+    }
     if constexpr (EPT % 4 == 0) {
 #pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-            f32x4 x = *reinterpret_cast<const f32x4*>(Grow + e);
-            f32x4 y;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                y[u] = g * x[u] + vr * sk[c0 + e + u];
-                o += y[u] * sx[c0 + e + u];
-            }
-            *reinterpret_cast<f32x4*>(Grow + e) = y;
-        }
+        for (int e = 0; e < EPT; e += 4)
+            *reinterpret_cast<f32x4*>(Grow + col(e)) = f32x4{gr[e], gr[e + 1], gr[e + 2], gr[e + 3]};
     } else {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const float y = g * Grow[e] + vr * sk[c0 + e];
-            Grow[e] = y;
-            o += y * sx[c0 + e];
-        }
+        for (int e = 0; e < EPT; ++e) Grow[col(e)] = gr[e];
     }
     o = row_sum(o);
     if (part == 0) out[nh * D + row] = o;
