@@ -21,23 +21,25 @@
 //   S_mid = H_{t0+h-1} = e^{l_{h-1}} S^H_c + sum_{i<h} e^{l_{h-1}-l_i} k_i k_i^T,
 // the state at the middle of the chunk (h = C/2), formed once per chunk.
 // Tokens in the second half then use S_mid and need intra-chunk terms only
-// against the keys of the second half, which halves the causal work of the
-// waves that had the most of it.
+// against the keys of the second half.
 //
 // Work split: one workgroup per (head, chunk); wave w owns tokens
 // 16w..16w+15 and runs their CG entirely on its own: the tiles in LDS are
 // read-only during the iterations, so the CG loop has no workgroup barrier
 // and waves stop independently.  Each wave runs a body specialised on w
-// (static sub-chunk, causal block range).  All contractions use
-// v_mfma_f32_16x16x4_f32; x, r, p, y live in registers in MFMA accumulator
-// layout and the alpha/beta dot products are 16-lane DPP row reductions.
-// Every MFMA chain starts from zero and is only read afterwards.
+// (static sub-chunk, causal block range).
 //
-// Operand loads: a lane's four k-values of an MFMA are contiguous, so row
-// operands are 128-bit LDS reads; a state block read along its columns is
-// four 32-bit reads.  The next k-group's operands are loaded before the
-// current group's MFMAs issue: one wave per SIMD fits (the tiles take
-// ~157 KiB of LDS), so the wave hides its own LDS latency.
+// Transposed products.  Every contraction is computed as its transpose,
+// e.g. Y^T = S P^T with the state as the MFMA A operand and the wave's CG
+// vectors as the B operand (v_mfma_f32_16x16x4_f32).  In that form the B
+// operand a lane supplies (token n, four consecutive features) is exactly
+// what it holds of the result: lane (n, kk) keeps features 16j + 4kk + r of
+// token n in block j.  So the CG vectors and the decayed scores feed the next
+// MFMA straight from registers, the loop writes nothing to LDS, and each
+// token's alpha/beta dot products finish with two lane swaps over its four
+// k-slot lanes.  The A operands (state rows, key rows, K^T rows) are 128-bit
+// LDS reads, issued one k-group ahead of the MFMAs that use them.  Every MFMA
+// chain starts from zero and is only read afterwards.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -54,10 +56,11 @@ struct alignas(16) CgLds {
     static constexpr int NSTATE = NW >= 2 ? 2 : 1;
     static constexpr int PD = lds_pitch(D);
     static constexpr int PS = lds_pitch_rows(D);
+    static constexpr int PT = lds_pitch_rows(C);
     static constexpr int REGION = NSTATE * HALF > D * PS ? NSTATE * HALF : D * PS;
     float R[REGION];          // CG: stored S^H_c [, S_mid];  output: G_c full [D][PS]
-    float KV[C * PD];         // K_c, later V_c   [token][feature]
-    float P[NW][16 * PD];     // per wave: P / decayed scores / X rows
+    float KV[C * PD];         // K_c rows [token][feature]
+    float KT[D * PT];         // K_c^T, later V_c^T   [feature][token]
     float L[C];               // l_i
     float Lam[D];
 };
@@ -70,32 +73,30 @@ __host__ __device__ constexpr int blk(int a, int b) {
     return (a * NT - a * (a - 1) / 2 + (b - a)) * 16 * kBlockPitch;
 }
 
-// Y[j]   += sum_f Z[m][f] * S[f][16j + n]   (S symmetric, upper block triangle stored)
-// Sc[ib] += sum_f Z[m][f] * K[KB0+ib][n][f] (NB score blocks against key rows)
-// Z: wave's staged rows (pitch lds_pitch(D)); K rows: pitch lds_pitch(D).
-// For k-group g and output block j, S[16g + k][16j + n] is stored block (g, j)
-// read down its columns when g <= j, else block (j, g) read along row n.
+// Y[j]   += S[16j + m][:] . Z^T[:][n]                 (S symmetric, upper block triangle stored)
+// Sc[ib] += K[16(KB0 + ib) + m][:] . Z^T[:][n]        (NB score blocks)
+// Z: the wave's vectors in registers (lane (n, kk), block g: features 16g + 4kk + s of token n).
+// S[16j + m][16g + 4kk + s] is stored block (j, g) read along row m when j < g,
+// else block (g, j) read down column m (S symmetric).
 template <int D, int NB, int KB0>
-__device__ __forceinline__ void contract_state_scores(const float* Z, const float* Sst, const float* Kr, int n,
-                                                      int kk, f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB]) {
+__device__ __forceinline__ void contract_state_scores(const f32x4 (&Z)[D / 16], const float* Sst, const float* Kr,
+                                                      int m, int kk, f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB]) {
     constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
-    const float* za = Z + n * PD + 4 * kk;
-    f32x4 a[2], bs[2][NT], bk[2][NB];
+    f32x4 bs[2][NT], bk[2][NB];
     auto load = [&](int g, int buf) {
-        a[buf] = lds4(za + 16 * g);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (g > j) {
-                bs[buf][j] = lds4(Sst + blk<NT>(j, g) + n * kBlockPitch + 4 * kk);
+                bs[buf][j] = lds4(Sst + blk<NT>(j, g) + m * kBlockPitch + 4 * kk);
             } else {
-                const float* col = Sst + blk<NT>(g, j) + (4 * kk) * kBlockPitch + n;
+                const float* col = Sst + blk<NT>(g, j) + (4 * kk) * kBlockPitch + m;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) bs[buf][j][s] = col[s * kBlockPitch];
             }
         }
 #pragma unroll
-        for (int ib = 0; ib < NB; ++ib) bk[buf][ib] = lds4(Kr + (16 * (KB0 + ib) + n) * PD + 16 * g + 4 * kk);
+        for (int ib = 0; ib < NB; ++ib) bk[buf][ib] = lds4(Kr + (16 * (KB0 + ib) + m) * PD + 16 * g + 4 * kk);
     };
     load(0, 0);
 #pragma unroll
@@ -105,28 +106,26 @@ __device__ __forceinline__ void contract_state_scores(const float* Z, const floa
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int j = 0; j < NT; ++j) Y[j] = mfma4(a[cur][s], bs[cur][j][s], Y[j]);
+            for (int j = 0; j < NT; ++j) Y[j] = mfma4(bs[cur][j][s], Z[g][s], Y[j]);
 #pragma unroll
-            for (int ib = 0; ib < NB; ++ib) Sc[ib] = mfma4(a[cur][s], bk[cur][ib][s], Sc[ib]);
+            for (int ib = 0; ib < NB; ++ib) Sc[ib] = mfma4(bk[cur][ib][s], Z[g][s], Sc[ib]);
         }
     }
 }
 
-// Y[j] += sum_f Z[m][f] * Bs[16j + n][f] (Bs full, row-major, pitch lds_pitch_rows(D));
-// Sc[ib] += sum_f Z[m][f] * K[16ib + n][f] for ib < NB.
+// Y[j] += Bs[16j + m][:] . Z^T[:][n]  (Bs full, row-major, pitch lds_pitch_rows(D)), when STATE;
+// Sc[ib] += K[16ib + m][:] . Z^T[:][n] for ib < NB (K rows, pitch lds_pitch(D)).
 template <int D, int NB, bool STATE>
-__device__ __forceinline__ void contract_rows(const float* Z, const float* Bs, const float* Bk, int n, int kk,
-                                              f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB > 0 ? NB : 1]) {
+__device__ __forceinline__ void contract_rows(const f32x4 (&Z)[D / 16], const float* Bs, const float* Bk, int m,
+                                              int kk, f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB > 0 ? NB : 1]) {
     constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
     constexpr int PS = lds_pitch_rows(D);
     constexpr int NBB = NB > 0 ? NB : 1;
-    const float* za = Z + n * PD + 4 * kk;
-    const float* bsa = STATE ? Bs + n * PS + 4 * kk : nullptr;
-    const float* bka = NB > 0 ? Bk + n * PD + 4 * kk : nullptr;
-    f32x4 a[2], bs[2][STATE ? NT : 1], bk[2][NBB];
+    const float* bsa = STATE ? Bs + m * PS + 4 * kk : nullptr;
+    const float* bka = NB > 0 ? Bk + m * PD + 4 * kk : nullptr;
+    f32x4 bs[2][STATE ? NT : 1], bk[2][NBB];
     auto load = [&](int g, int buf) {
-        a[buf] = lds4(za + 16 * g);
         if constexpr (STATE) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) bs[buf][j] = lds4(bsa + 16 * j * PS + 16 * g);
@@ -143,62 +142,38 @@ __device__ __forceinline__ void contract_rows(const float* Z, const float* Bs, c
         for (int s = 0; s < 4; ++s) {
             if constexpr (STATE) {
 #pragma unroll
-                for (int j = 0; j < NT; ++j) Y[j] = mfma4(a[cur][s], bs[cur][j][s], Y[j]);
+                for (int j = 0; j < NT; ++j) Y[j] = mfma4(bs[cur][j][s], Z[g][s], Y[j]);
             }
 #pragma unroll
-            for (int ib = 0; ib < NB; ++ib) Sc[ib] = mfma4(a[cur][s], bk[cur][ib][s], Sc[ib]);
+            for (int ib = 0; ib < NB; ++ib) Sc[ib] = mfma4(bk[cur][ib][s], Z[g][s], Sc[ib]);
         }
     }
 }
 
-// Y[j] += sum_{ib < NB} sum_i A[m][16ib + i] * B[16(KB0 + ib) + i][16j + n]
-// A: decayed scores (columns relative to key block KB0, pitch lds_pitch(D));
-// B: K or V tile rows (pitch lds_pitch(D)).
-template <int D, int NB, int KB0>
-__device__ __forceinline__ void contract_intra(const float* A, const float* B, int n, int kk, f32x4 (&Y)[D / 16]) {
+// Y[j] += sum_{ib < NB} sum_i BT[16j + m][16(KB0 + ib) + i] * W[ib][i]
+// BT: K^T or V^T tile [feature][token] (pitch lds_pitch_rows(C));
+// W: decayed score blocks in registers (lane (n, kk): keys 16(KB0 + ib) + 4kk + s of token n).
+template <int D, int C, int NB, int KB0>
+__device__ __forceinline__ void contract_intra(const f32x4 (&W)[NB], const float* BT, int m, int kk,
+                                               f32x4 (&Y)[D / 16]) {
     constexpr int NT = D / 16;
-    constexpr int PD = lds_pitch(D);
-    float b[2][NT];
-    auto load = [&](int ib, int s, int buf) {
-        const float* brow = B + (16 * (KB0 + ib) + 4 * kk + s) * PD + n;
+    constexpr int PT = lds_pitch_rows(C);
+    const float* base = BT + m * PT + 16 * KB0 + 4 * kk;
+    f32x4 a[2][NT];
+    auto load = [&](int ib, int buf) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) b[buf][j] = brow[16 * j];
+        for (int j = 0; j < NT; ++j) a[buf][j] = lds4(base + 16 * j * PT + 16 * ib);
     };
-    load(0, 0, 0);
+    load(0, 0);
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib) {
-        const f32x4 a4 = lds4(A + n * PD + 16 * ib + 4 * kk);
+        const int cur = ib & 1;
+        if (ib + 1 < NB) load(ib + 1, cur ^ 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int step = 4 * ib + s, cur = step & 1;
-            if (step + 1 < 4 * NB) load((step + 1) / 4, (step + 1) % 4, cur ^ 1);
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) Y[j] = mfma4(a4[s], b[cur][j], Y[j]);
-        }
+            for (int j = 0; j < NT; ++j) Y[j] = mfma4(a[cur][j][s], W[ib][s], Y[j]);
     }
-}
-
-// Stage a wave's 16 rows (MFMA accumulator layout) as rows of its LDS region.
-template <int D>
-__device__ __forceinline__ void stage_rows(float* dst, const f32x4 (&V)[D / 16], int n, int kk) {
-    constexpr int PD = lds_pitch(D);
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * kk + r) * PD + 16 * j + n] = V[j][r];
-    wave_lds_sync();
-}
-
-// Write decayed score blocks (columns relative to the first block) as rows.
-template <int D, int NB>
-__device__ __forceinline__ void stage_scores(float* dst, const f32x4 (&Sc)[NB], const float (&dec)[NB][4], int n,
-                                             int kk) {
-    constexpr int PD = lds_pitch(D);
-#pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * kk + r) * PD + 16 * ib + n] = Sc[ib][r] * dec[ib][r];
-    wave_lds_sync();
 }
 
 // S_mid (upper block triangle) = e^{l_{h-1}} S0 + sum_{i<h} e^{l_{h-1}-l_i} k_i k_i^T,
@@ -213,6 +188,9 @@ __device__ __forceinline__ void form_mid_state(CgLds<D, C>& L, int w, int n, int
     float* S1 = L.R + CgLds<D, C>::HALF;
     const float lh = L.L[H - 1];
     const float Gh = __expf(lh);
+    float wk[H / 4];
+#pragma unroll
+    for (int st = 0; st < H / 4; ++st) wk[st] = __expf(lh - L.L[4 * st + kk]);
     int q = 0;
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
@@ -223,8 +201,7 @@ __device__ __forceinline__ void form_mid_state(CgLds<D, C>& L, int w, int n, int
 #pragma unroll
             for (int st = 0; st < H / 4; ++st) {
                 const int i = 4 * st + kk;
-                const float wi = __expf(lh - L.L[i]);
-                acc = mfma4(wi * L.KV[i * PD + 16 * a + n], L.KV[i * PD + 16 * b + n], acc);
+                acc = mfma4(wk[st] * L.KV[i * PD + 16 * a + n], L.KV[i * PD + 16 * b + n], acc);
             }
             const float* s0 = S0 + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n;
             float* s1 = S1 + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n;
@@ -246,82 +223,59 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
     constexpr int KB0 = SUB ? NW / 2 : 0;                    // first key block of the sub-chunk
     constexpr int NB = W - KB0 + 1;                          // causal key blocks in the CG
     constexpr int NBO = W + 1;                               // causal key blocks of the output
-    constexpr int PD = lds_pitch(D);
     constexpr int PS = lds_pitch_rows(D);
+    constexpr int PT = lds_pitch_rows(C);
     constexpr int NTHR = 64 * NW;
     const int lane = tid & 63;
-    const int n = lane & 15;
-    const int kk = lane >> 4;
-    float* myP = L.P[W];
+    const int n = lane & 15;    // token of the lane (B operand / result column)
+    const int kk = lane >> 4;   // k-slot group (features 4kk..4kk+3 of each block)
     const float* Sst = L.R + SUB * CgLds<D, C>::HALF;
+    const int tr = 16 * W + n;  // chunk token of this lane
+    const bool tok_ok = tr < valid;
 
-    // ---- per-lane constants; lane rows are chunk tokens 16W + 4kk + r ----
+    // ---- per-lane constants ----
     const float lbase = SUB ? L.L[16 * KB0 - 1] : 0.f;   // l at the end of the first half
-    float eL[4], eLo[4];
-    float dec[NBO][4];
+    const float eL = __expf(L.L[tr] - lbase);
+    const float eLo = __expf(L.L[tr]);
+    float dec[NBO][4];   // e^{l_t - l_i} for key i = 16ib + 4kk + r <= t, else 0
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int tr = 16 * W + 4 * kk + r;
-        eL[r] = __expf(L.L[tr] - lbase);
-        eLo[r] = __expf(L.L[tr]);
+    for (int ib = 0; ib < NBO; ++ib)
 #pragma unroll
-        for (int ib = 0; ib < NBO; ++ib) {
-            const int i = 16 * ib + n;
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ib + 4 * kk + r;
             dec[ib][r] = (i <= tr) ? __expf(L.L[tr] - L.L[i]) : 0.f;
         }
-    }
-    float decs[NB][4];   // the sub-chunk's blocks
-#pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) decs[ib][r] = dec[KB0 + ib][r];
-    float lamc[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) lamc[j] = L.Lam[16 * j + n];
 
     // ---- CG state: x = 0, r = p = q ----
     f32x4 X[NT], R[NT], P[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * W + 4 * kk + r;
-            R[j][r] = row < valid ? to_f32(q[(tok0 + row) * D + 16 * j + n]) : 0.f;
-        }
+        R[j] = tok_ok ? load4(q + (tok0 + tr) * D + 16 * j + 4 * kk) : f32x4{0.f, 0.f, 0.f, 0.f};
         P[j] = R[j];
         X[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // stop before an update when |r| / |q| < tol, tested as r.r < (tol |q|)^2
-    float rr[4], stop_rr[4];
-    bool done[4];
-    int it[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    auto dot = [&](const f32x4 (&A)[NT], const f32x4 (&B)[NT]) {
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) s += R[j][r] * R[j][r];
-        rr[r] = rowsum16(s);
-        const float tq = tol * sqrtf(rr[r]);
-        stop_rr[r] = tq * tq;
-        done[r] = !(rr[r] > 0.f);   // q_t == 0 (or a padded row): x = 0, 0 iterations
-        it[r] = 0;
-    }
-    stage_rows<D>(myP, P, n, kk);
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s += A[j][r] * B[j][r];
+        return kslot_sum(s);
+    };
+    // stop before an update when |r| / |q| < tol, tested as r.r < (tol |q|)^2
+    float rr = dot(R, R);
+    const float tq = tol * sqrtf(rr);
+    const float stop_rr = tq * tq;
+    bool done = !(rr > 0.f);   // q_t == 0 (or a padded token): x = 0, 0 iterations
+    int it = 0;
 
     // ---- CG iterations ----
     for (int itn = 0; itn < max_iters; ++itn) {
-        bool alive = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (!done[r]) {
-                if (rr[r] < stop_rr[r] || rr[r] == 0.f) done[r] = true;
-                else alive = true;
-            }
-        }
-        if (__builtin_amdgcn_ballot_w64(alive) == 0) break;
+        if (!done && (rr < stop_rr || rr == 0.f)) done = true;
+        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
 
-        // Y = diag(e^{l - lbase}) P S + (M o (P K^T)) K + diag(lambda) P over
-        // the sub-chunk; state and intra-chunk sums in separate accumulators.
+        // Y = diag(e^{l - lbase}) P S + (M o (P K^T)) K + P diag(lambda) over
+        // the sub-chunk, transposed; state and intra-chunk sums in separate chains.
         f32x4 Y[NT];
         {
             f32x4 YS[NT], YI[NT], Sc[NB];
@@ -329,92 +283,84 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
             for (int j = 0; j < NT; ++j) YS[j] = YI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ib = 0; ib < NB; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-            contract_state_scores<D, NB, KB0>(myP, Sst, L.KV, n, kk, YS, Sc);
-            stage_scores<D, NB>(myP, Sc, decs, n, kk);     // P rows are consumed: reuse the region
-            contract_intra<D, NB, KB0>(myP, L.KV, n, kk, YI);
+            contract_state_scores<D, NB, KB0>(P, Sst, L.KV, n, kk, YS, Sc);
+            f32x4 Wt[NB];
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
+            for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Y[j][r] = eL[r] * YS[j][r] + YI[j][r] + lamc[j] * P[j][r];
+                for (int r = 0; r < 4; ++r) Wt[ib][r] = Sc[ib][r] * dec[KB0 + ib][r];
+            contract_intra<D, C, NB, KB0>(Wt, L.KT, n, kk, YI);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const f32x4 lam = lds4(&L.Lam[16 * j + 4 * kk]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Y[j][r] = eL * YS[j][r] + YI[j][r] + lam[r] * P[j][r];
+            }
         }
 
-        float alpha[4];
-        bool act[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float s = 0.f;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) s += P[j][r] * Y[j][r];
-            const float pap = rowsum16(s);
-            act[r] = !done[r] && (pap > 0.f);
-            if (!done[r] && !act[r]) done[r] = true;   // breakdown guard
-            alpha[r] = act[r] ? rr[r] / pap : 0.f;
-        }
+        const float pap = dot(P, Y);
+        const bool act = !done && (pap > 0.f);
+        if (!done && !act) done = true;   // breakdown guard
+        const float alpha = act ? rr / pap : 0.f;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                X[j][r] += alpha[r] * P[j][r];
-                R[j][r] -= alpha[r] * Y[j][r];
+                X[j][r] += alpha * P[j][r];
+                R[j][r] -= alpha * Y[j][r];
             }
+        const float rrn = dot(R, R);
+        if (act) {
+            const float beta = rrn / rr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float s = 0.f;
+            for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) s += R[j][r] * R[j][r];
-            const float rrn = rowsum16(s);
-            if (act[r]) {
-                const float beta = rrn / rr[r];
-#pragma unroll
-                for (int j = 0; j < NT; ++j) P[j][r] = R[j][r] + beta * P[j][r];
-                rr[r] = rrn;
-                it[r] += 1;
-            }
+                for (int r = 0; r < 4; ++r) P[j][r] = R[j][r] + beta * P[j][r];
+            rr = rrn;
+            it += 1;
         }
-        stage_rows<D>(myP, P, n, kk);
     }
 
     // ---- iteration counts ----
-    if (iters && n == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * W + 4 * kk + r;
-            if (row < valid) iters[tok0 + row] = it[r];
-        }
-    }
+    if (iters && kk == 0 && tok_ok) iters[tok0 + tr] = it;
 
-    // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk ----
-    stage_rows<D>(myP, X, n, kk);
-    f32x4 Sc[NBO];
+    // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
+    f32x4 Wo[NBO];
     {
-        f32x4 unused[NT];
+        f32x4 Sc[NBO], unused[NT];
 #pragma unroll
         for (int ib = 0; ib < NBO; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-        contract_rows<D, NBO, false>(myP, nullptr, L.KV, n, kk, unused, Sc);
+        contract_rows<D, NBO, false>(X, nullptr, L.KV, n, kk, unused, Sc);
+#pragma unroll
+        for (int ib = 0; ib < NBO; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wo[ib][r] = Sc[ib][r] * dec[ib][r];
     }
-    __syncthreads();   // every wave is done with the states and K_c
+    __syncthreads();   // every wave is done with the states, K_c and K_c^T
     for (int e = tid * 4; e < D * D; e += NTHR * 4)
         *reinterpret_cast<f32x4*>(&L.R[(e / D) * PS + e % D]) = *reinterpret_cast<const f32x4*>(Gc + e);
     for (int e = tid * 4; e < C * D; e += NTHR * 4) {
-        const int i = e / D;
+        const int i = e / D, f = e % D;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (i < valid) x = load4(v + (tok0 + i) * D + e % D);
-        *reinterpret_cast<f32x4*>(&L.KV[i * PD + e % D]) = x;
+        if (i < valid) x = load4(v + (tok0 + i) * D + f);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) L.KT[(f + u) * PT + i] = x[u];
     }
     __syncthreads();
     f32x4 OS[NT], OI[NT], none[1];
 #pragma unroll
     for (int j = 0; j < NT; ++j) OS[j] = OI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    contract_rows<D, 0, true>(myP, L.R, nullptr, n, kk, OS, none);
-    stage_scores<D, NBO>(myP, Sc, dec, n, kk);   // X rows are consumed: reuse the region
-    contract_intra<D, NBO, 0>(myP, L.KV, n, kk, OI);
+    contract_rows<D, 0, true>(X, L.R, nullptr, n, kk, OS, none);
+    contract_intra<D, C, NBO, 0>(Wo, L.KT, n, kk, OI);
+    if (tok_ok) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+        for (int j = 0; j < NT; ++j) {
+            f32x4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * W + 4 * kk + r;
-            if (row < valid) out[(tok0 + row) * D + 16 * j + n] = eLo[r] * OS[j][r] + OI[j][r];
+            for (int r = 0; r < 4; ++r) o[r] = eLo * OS[j][r] + OI[j][r];
+            *reinterpret_cast<f32x4*>(out + (tok0 + tr) * D + 16 * j + 4 * kk) = o;
         }
+    }
 }
 
 template <int D, int C, typename In>
@@ -424,8 +370,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     const float* __restrict__ SH, const float* __restrict__ SG, int H, int T, int n_chunks,
     int max_iters, float tol, float* __restrict__ out, int32_t* __restrict__ iters) {
     constexpr int NW = C / 16;
-    constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
+    constexpr int PT = lds_pitch_rows(C);
     constexpr int NTHR = 64 * NW;
     __shared__ CgLds<D, C> L;
 
@@ -442,15 +388,17 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     const size_t hoff = ((size_t)bh * n_chunks + c) * HPACK;
     const size_t soff = ((size_t)bh * n_chunks + c) * D * D;
 
-    // ---- stage S^H_c (packed 16x16 upper blocks, in blk order), K_c, lambda, l ----
+    // ---- stage S^H_c (packed 16x16 upper blocks, in blk order), K_c, K_c^T, lambda, l ----
     for (int e = tid * 4; e < HPACK; e += NTHR * 4)
         *reinterpret_cast<f32x4*>(&L.R[(e / 256) * 16 * kBlockPitch + ((e % 256) / 16) * kBlockPitch + e % 16]) =
             *reinterpret_cast<const f32x4*>(SH + hoff + e);
     for (int e = tid * 4; e < C * D; e += NTHR * 4) {
-        const int i = e / D;
+        const int i = e / D, f = e % D;
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (i < valid) x = load4(k + (tok0 + i) * D + e % D);
-        *reinterpret_cast<f32x4*>(&L.KV[i * PD + e % D]) = x;
+        if (i < valid) x = load4(k + (tok0 + i) * D + f);
+        *reinterpret_cast<f32x4*>(&L.KV[i * PD + f]) = x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) L.KT[(f + u) * PT + i] = x[u];
     }
     for (int e = tid; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)h * D + e];
     if (w == 0) {
@@ -463,7 +411,6 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
         __syncthreads();
     }
 
-    (void)NT;
     const float* Gc = SG + soff;
     if (w == 0) {
         cg_wave<D, C, 0, In>(L, tid, q, v, Gc, tok0, valid, max_iters, tol, out, iters);

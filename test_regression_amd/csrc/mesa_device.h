@@ -68,6 +68,17 @@ __device__ __forceinline__ float rowsum16(float v) {
     return v;
 }
 
+// Sum over the 4 lanes n, n+16, n+32, n+48 (the four DPP rows), i.e. over
+// the MFMA k-slot group kk.  The two gfx950 lane swaps pair row 0 with 1 and
+// 2 with 3, then the lower half with the upper; every lane adds the same two
+// operands, so all four get bit-identical sums.
+__device__ __forceinline__ float kslot_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Sum over all 64 lanes (butterfly; every lane gets the same value).
 __device__ __forceinline__ float wavesum(float v) {
 #pragma unroll
