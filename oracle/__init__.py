@@ -51,12 +51,17 @@ def _load():
         D = ctypes.c_double
         lib.oracle_cg_solve.argtypes = [I, P, P, P, I, D, P, P, P, P, P]
         lib.oracle_cg_solve.restype = I
+        lib.oracle_cg_solve_from.argtypes = [I, P, P, P, P, I, D, P, P, P, P, P]
+        lib.oracle_cg_solve_from.restype = I
         lib.oracle_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D,
                                        P, P, P, P, P, P, P, P]
         lib.oracle_forward.restype = I
         lib.oracle_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, D,
                                            P, P, P, P, P]
         lib.oracle_decode_step.restype = I
+        lib.oracle_decode_step_warm.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, D, I,
+                                                P, P, P, P, P]
+        lib.oracle_decode_step_warm.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -76,8 +81,8 @@ def max_threads() -> int:
     return int(_load().oracle_max_threads())
 
 
-def cg_solve(Hm, lam, b, max_iters, tol=0.0):
-    """CG on (Hm + diag(lam)) x = b from x = 0.
+def cg_solve(Hm, lam, b, max_iters, tol=0.0, x0=None):
+    """CG on (Hm + diag(lam)) x = b from x = 0, or from x = x0 when given.
 
     Returns (x, iters, reason, rho_stop, rho_min_prev).
     """
@@ -90,9 +95,16 @@ def cg_solve(Hm, lam, b, max_iters, tol=0.0):
     reason = ctypes.c_int(0)
     rs = ctypes.c_double(0)
     rm = ctypes.c_double(0)
-    it = lib.oracle_cg_solve(n, _ptr(Hm), _ptr(lam), _ptr(b), int(max_iters), float(tol),
-                             _ptr(x), _ptr(scratch), ctypes.byref(reason),
-                             ctypes.byref(rs), ctypes.byref(rm))
+    if x0 is None:
+        it = lib.oracle_cg_solve(n, _ptr(Hm), _ptr(lam), _ptr(b), int(max_iters), float(tol),
+                                 _ptr(x), _ptr(scratch), ctypes.byref(reason),
+                                 ctypes.byref(rs), ctypes.byref(rm))
+    else:
+        x0 = _f64(x0)
+        assert x0.shape == (n,)
+        it = lib.oracle_cg_solve_from(n, _ptr(Hm), _ptr(lam), _ptr(b), _ptr(x0), int(max_iters),
+                                      float(tol), _ptr(x), _ptr(scratch), ctypes.byref(reason),
+                                      ctypes.byref(rs), ctypes.byref(rm))
     return x, it, reason.value, rs.value, rm.value
 
 
@@ -150,4 +162,37 @@ def decode_step(q, k, v, gamma, lam, state_H, state_G, max_iters, tol=0.0):
                                 _ptr(rho_stop), _ptr(rho_min_prev), _ptr(reason))
     if rc != 0:
         raise ValueError("oracle_decode_step rejected its arguments")
+    return dict(out=out, iters=iters, reason=reason, rho_stop=rho_stop, rho_min_prev=rho_min_prev)
+
+
+WARM_COLD, WARM_PREVIOUS, WARM_PROJECTED = 0, 1, 2
+
+
+def decode_step_warm(q, k, v, gamma, lam, state_H, state_G, state_x, max_iters, tol=0.0,
+                     mode=WARM_PROJECTED):
+    """One decode step with a warm-started solve; state_H/G/x (float64) are updated in place.
+
+    state_x [N, H, dk] holds the previous step's solution on entry and this
+    step's on exit.  mode: WARM_COLD (x0 = 0), WARM_PREVIOUS (x0 = x_prev) or
+    WARM_PROJECTED (x0 = c x_prev, c minimising the A-norm error).
+    """
+    lib = _load()
+    q, k, v, gamma, lam = _f64(q), _f64(k), _f64(v), _f64(gamma), _f64(lam)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    for a in (state_H, state_G, state_x):
+        assert a.dtype == np.float64 and a.flags.c_contiguous
+    assert state_H.shape == (N, H, dk, dk) and state_G.shape == (N, H, dv, dk)
+    assert state_x.shape == (N, H, dk)
+    out = np.zeros((N, H, dv))
+    iters = np.zeros((N, H), dtype=np.int32)
+    reason = np.zeros((N, H), dtype=np.int32)
+    rho_stop = np.zeros((N, H))
+    rho_min_prev = np.zeros((N, H))
+    rc = lib.oracle_decode_step_warm(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(lam),
+                                     _ptr(state_H), _ptr(state_G), _ptr(state_x), N, H, dk, dv,
+                                     int(max_iters), float(tol), int(mode), _ptr(out), _ptr(iters),
+                                     _ptr(rho_stop), _ptr(rho_min_prev), _ptr(reason))
+    if rc != 0:
+        raise ValueError("oracle_decode_step_warm rejected its arguments")
     return dict(out=out, iters=iters, reason=reason, rho_stop=rho_stop, rho_min_prev=rho_min_prev)

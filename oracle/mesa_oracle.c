@@ -64,28 +64,39 @@ static void apply_a(int n, const double *Hm, const double *lam, const double *p,
 }
 
 /*
- * Conjugate Gradient on (Hm + diag(lam)) x = b from x = 0.
+ * Conjugate Gradient on (Hm + diag(lam)) x = b from x = x0 (x0 == NULL: from
+ * x = 0, the page's solve; a given x0 is the warm start that the page names
+ * as future work in "Significancia e Alegacoes").  From x0 the method is the
+ * same with r0 = b - A x0 and p0 = r0.  The stop test always compares |r|
+ * with |b|.  b == 0 gives x = 0 and no update, whatever x0 is.
  * Outputs: x, number of updates (return value), the stop reason, the residual
  * ratio rho at the stop (rho_n = sqrt(r^T r)/|b| after the last update) and
  * the smallest ratio that was checked and passed before it (+inf if none).
- * scratch: 3n doubles.
+ * scratch: 3n doubles.  x may alias x0.
  */
-int oracle_cg_solve(int n, const double *Hm, const double *lam, const double *b,
-                    int max_iters, double tol, double *x, double *scratch,
-                    int *reason, double *rho_stop, double *rho_min_prev)
+int oracle_cg_solve_from(int n, const double *Hm, const double *lam, const double *b,
+                         const double *x0, int max_iters, double tol, double *x, double *scratch,
+                         int *reason, double *rho_stop, double *rho_min_prev)
 {
     double *r = scratch, *p = scratch + n, *y = scratch + 2 * n;
-    for (int i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; p[i] = b[i]; }
-    double rr = dot(n, r, r);
     double nq = sqrt(dot(n, b, b));
-    double minprev = INFINITY;
-    int it = 0, why = ORACLE_STOP_CAP;
     if (nq == 0.0) {
+        for (int i = 0; i < n; ++i) x[i] = 0.0;
         if (reason) *reason = ORACLE_STOP_Q_ZERO;
         if (rho_stop) *rho_stop = 0.0;
         if (rho_min_prev) *rho_min_prev = INFINITY;
         return 0;
     }
+    if (x0) {
+        for (int i = 0; i < n; ++i) x[i] = x0[i];
+        apply_a(n, Hm, lam, x, y);
+        for (int i = 0; i < n; ++i) { r[i] = b[i] - y[i]; p[i] = r[i]; }
+    } else {
+        for (int i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; p[i] = b[i]; }
+    }
+    double rr = dot(n, r, r);
+    double minprev = INFINITY;
+    int it = 0, why = ORACLE_STOP_CAP;
     while (it < max_iters) {
         double rho = sqrt(rr) / nq;
         if (tol > 0.0 && rho < tol) { why = ORACLE_STOP_TOL; break; }
@@ -106,6 +117,15 @@ int oracle_cg_solve(int n, const double *Hm, const double *lam, const double *b,
     if (rho_stop) *rho_stop = sqrt(rr) / nq;
     if (rho_min_prev) *rho_min_prev = minprev;
     return it;
+}
+
+/* The page's solve: CG from x = 0. */
+int oracle_cg_solve(int n, const double *Hm, const double *lam, const double *b,
+                    int max_iters, double tol, double *x, double *scratch,
+                    int *reason, double *rho_stop, double *rho_min_prev)
+{
+    return oracle_cg_solve_from(n, Hm, lam, b, NULL, max_iters, tol, x, scratch, reason,
+                                rho_stop, rho_min_prev);
 }
 
 /* H = g*H + a b^T  (rows x cols, row-major) */
@@ -235,6 +255,66 @@ int oracle_decode_step(const double *q, const double *k, const double *v,
             if (reason) reason[nh] = why;
         }
         free(x); free(scratch);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * One decode step with a warm-started solve (the warm start that the page
+ * names as future work, section "Significancia e Alegacoes"), for N x H heads.
+ * Same as oracle_decode_step, plus state_x [N,H,dk]: on entry the previous
+ * step's solution of each head, on exit this step's.  The start point is
+ *   mode 0: x0 = 0 (the page's cold start);
+ *   mode 1: x0 = x_prev;
+ *   mode 2: x0 = c x_prev with c = (x_prev . q) / (x_prev . A x_prev), the
+ *           minimiser of the A-norm error over multiples of x_prev (x0 = 0
+ *           when x_prev . A x_prev <= 0, e.g. x_prev = 0).
+ */
+int oracle_decode_step_warm(const double *q, const double *k, const double *v,
+                            const double *gamma, const double *lam,
+                            double *state_H, double *state_G, double *state_x,
+                            int N, int H, int dk, int dv, int max_iters, double tol, int mode,
+                            double *out, int32_t *iters, double *rho_stop,
+                            double *rho_min_prev, int32_t *reason)
+{
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0 || max_iters < 0 || !(tol >= 0.0) ||
+        mode < 0 || mode > 2)
+        return -1;
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long nh = 0; nh < (long)N * H; ++nh) {
+        int h = (int)(nh % H);
+        double *x0 = malloc(sizeof(double) * dk);
+        double *ax = malloc(sizeof(double) * dk);
+        double *scratch = malloc(sizeof(double) * 3 * dk);
+        if (!x0 || !ax || !scratch) {
+            bad = 1;
+        } else {
+            double *Hs = state_H + (size_t)nh * dk * dk, *Gs = state_G + (size_t)nh * dv * dk;
+            double *xs = state_x + (size_t)nh * dk;
+            const double *qh = q + (size_t)nh * dk, *lh = lam + (size_t)h * dk;
+            decay_rank1(dk, dk, Hs, gamma[nh], k + (size_t)nh * dk, k + (size_t)nh * dk);
+            decay_rank1(dv, dk, Gs, gamma[nh], v + (size_t)nh * dv, k + (size_t)nh * dk);
+            double c = 0.0;
+            if (mode == 1) {
+                c = 1.0;
+            } else if (mode == 2) {
+                apply_a(dk, Hs, lh, xs, ax);
+                double den = dot(dk, xs, ax);
+                c = den > 0.0 ? dot(dk, xs, qh) / den : 0.0;
+            }
+            for (int i = 0; i < dk; ++i) x0[i] = c * xs[i];
+            int why = 0;
+            double rs = 0.0, rm = 0.0;
+            int it = oracle_cg_solve_from(dk, Hs, lh, qh, mode == 0 ? NULL : x0, max_iters, tol,
+                                          xs, scratch, &why, &rs, &rm);
+            matvec(dv, dk, Gs, xs, out + (size_t)nh * dv);
+            if (iters) iters[nh] = it;
+            if (rho_stop) rho_stop[nh] = rs;
+            if (rho_min_prev) rho_min_prev[nh] = rm;
+            if (reason) reason[nh] = why;
+        }
+        free(x0); free(ax); free(scratch);
     }
     return bad ? -1 : 0;
 }

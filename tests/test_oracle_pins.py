@@ -349,3 +349,164 @@ def test_generator_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(ours, ref)
     np.testing.assert_array_equal(inputs.bf16_bits_to_f32(ours),
                                   torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+# --------------------------------------------------------------------------
+# Warm start (the page names warm-start strategies as future work, section
+# "Significancia e Alegacoes").  W1: from x0 the k-step CG iterate is x0 plus
+# the Krylov projection of the initial residual r0 = b - A x0 (exact
+# rationals).  W2: an exact start needs no update.  W3: the projected start
+# c x_prev minimises the A-norm error over multiples of x_prev (brute-force
+# scan) and is exact when x_prev is an eigenvector parallel to q.  W4: cold
+# and degenerate warm modes reproduce the cold decode step bit for bit.
+# --------------------------------------------------------------------------
+def test_warm_start_iterate_is_shifted_krylov_projection():
+    rng = np.random.default_rng(21)
+    n = 5
+    for trial in range(3):
+        ints = rng.integers(-3, 4, size=(n + 2, n))
+        Hq = [[Fraction(int(sum(ints[r, i] * ints[r, j] for r in range(n + 2))), 4)
+               for j in range(n)] for i in range(n)]
+        lam = [Fraction(int(x), 2) for x in rng.integers(1, 6, size=n)]
+        b = [Fraction(int(x)) for x in rng.integers(-4, 5, size=n)]
+        x0 = [Fraction(int(x), 3) for x in rng.integers(-3, 4, size=n)]
+        A = [[Hq[i][j] + (lam[i] if i == j else 0) for j in range(n)] for i in range(n)]
+        r0 = [b[i] - sum(A[i][j] * x0[j] for j in range(n)) for i in range(n)]
+        if all(x == 0 for x in r0):
+            continue
+        Hf = np.array([[float(x) for x in row] for row in Hq])
+        lf = np.array([float(x) for x in lam])
+        bf = np.array([float(x) for x in b])
+        x0f = np.array([float(x) for x in x0])
+        for kk in range(1, n + 1):
+            e = _krylov_iterate(A, r0, kk)
+            exact = np.array([float(x0[i] + e[i]) for i in range(n)])
+            x, it, *_ = oracle.cg_solve(Hf, lf, bf, kk, 0.0, x0=x0f)
+            if it < kk:
+                exact = np.array([float(x) for x in _frac_solve(A, b)])
+            assert rel(x, exact) < 1e-11, (trial, kk)
+        # the start point matters: the 1-step iterates from x0 and from 0 differ
+        x_cold, *_ = oracle.cg_solve(Hf, lf, bf, 1, 0.0)
+        x_warm, *_ = oracle.cg_solve(Hf, lf, bf, 1, 0.0, x0=x0f)
+        assert rel(x_warm, x_cold) > 1e-6
+
+
+def test_warm_start_from_the_solution_makes_no_update():
+    rng = np.random.default_rng(22)
+    n = 12
+    K = rng.standard_normal((20, n)) / np.sqrt(n)
+    Hm, lam, b = K.T @ K, rng.uniform(0.5, 2.0, n), rng.standard_normal(n)
+    xs = scipy.linalg.solve(Hm + np.diag(lam), b, assume_a="pos")
+    x, it, why, rho, _ = oracle.cg_solve(Hm, lam, b, 30, 1e-8, x0=xs)
+    assert it == 0 and why == oracle.STOP_TOL and rho < 1e-12
+    np.testing.assert_array_equal(x, xs)
+    # a zero query gives x = 0 whatever the start
+    x, it, why, *_ = oracle.cg_solve(Hm, lam, np.zeros(n), 30, 1e-8, x0=xs)
+    assert it == 0 and why == oracle.STOP_Q_ZERO and not x.any()
+
+
+def _decode_problem(rng, dk, dv, T):
+    k = rng.standard_normal((T, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((T, dv))
+    g = rng.uniform(0.8, 1.0, T)
+    Hm, Gm = brute_states(k, v, g, T - 1)
+    return Hm, Gm
+
+
+def test_projected_warm_start_minimises_energy_error():
+    rng = np.random.default_rng(23)
+    dk = dv = 10
+    for trial in range(4):
+        Hm, Gm = _decode_problem(rng, dk, dv, 15)
+        lam = rng.uniform(0.5, 2.0, (1, dk))
+        q = rng.standard_normal((1, 1, dk))
+        kn = rng.standard_normal((1, 1, dk)) / np.sqrt(dk)
+        vn = rng.standard_normal((1, 1, dv))
+        g = np.array([[0.9]])
+        x_prev = rng.standard_normal(dk)
+        # A after this step's state update, built from the recurrence's definition
+        A = 0.9 * Hm + np.outer(kn[0, 0], kn[0, 0]) + np.diag(lam[0])
+        xs = scipy.linalg.solve(A, q[0, 0], assume_a="pos")
+        SH, SG = Hm[None, None].copy(), Gm[None, None].copy()
+        SX = x_prev[None, None].copy()
+        oracle.decode_step_warm(q, kn, vn, g, lam, SH, SG, SX, 0, 0.0, oracle.WARM_PROJECTED)
+        c = SX[0, 0] @ x_prev / (x_prev @ x_prev)
+        np.testing.assert_allclose(SX[0, 0], c * x_prev, rtol=1e-12, atol=1e-14)
+
+        def energy(cc):
+            e = xs - cc * x_prev
+            return e @ A @ e
+        grid = np.linspace(c - 1.0, c + 1.0, 2001)
+        assert energy(c) <= min(energy(cc) for cc in grid) + 1e-12
+        assert energy(c) <= energy(0.0) + 1e-12   # never worse than the cold start
+
+
+def test_projected_warm_start_exact_for_parallel_eigenvector():
+    rng = np.random.default_rng(24)
+    dk = dv = 8
+    Hm, Gm = _decode_problem(rng, dk, dv, 12)
+    lam = np.full((1, dk), 0.7)               # Lambda = lambda I keeps eigenvectors of H
+    kn = np.zeros((1, 1, dk))                 # no new key: A = g Hm + Lambda
+    vn = rng.standard_normal((1, 1, dv))
+    g = np.array([[1.0]])
+    w, U = np.linalg.eigh(Hm)
+    u = U[:, 3]
+    q = (2.5 * u)[None, None]
+    SH, SG, SX = Hm[None, None].copy(), Gm[None, None].copy(), (-0.3 * u)[None, None].copy()
+    r = oracle.decode_step_warm(q, kn, vn, g, lam, SH, SG, SX, 30, 1e-9, oracle.WARM_PROJECTED)
+    assert r["iters"][0, 0] == 0
+    np.testing.assert_allclose(SX[0, 0], 2.5 / (w[3] + 0.7) * u, rtol=1e-12, atol=1e-14)
+    # the plain previous-solution start is not exact here and needs updates
+    SH, SG, SX = Hm[None, None].copy(), Gm[None, None].copy(), (-0.3 * u)[None, None].copy()
+    r = oracle.decode_step_warm(q, kn, vn, g, lam, SH, SG, SX, 30, 1e-9, oracle.WARM_PREVIOUS)
+    assert r["iters"][0, 0] >= 1
+
+
+def test_warm_decode_degenerate_modes_equal_cold():
+    rng = np.random.default_rng(25)
+    N, H, dk, dv = 2, 3, 6, 6
+    base_H = np.stack([np.stack([_decode_problem(rng, dk, dv, 9)[0] for _ in range(H)]) for _ in range(N)])
+    base_G = rng.standard_normal((N, H, dv, dk))
+    q = rng.standard_normal((N, H, dk))
+    k = rng.standard_normal((N, H, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((N, H, dv))
+    g = rng.uniform(0.9, 1.0, (N, H))
+    lam = rng.uniform(0.5, 2.0, (H, dk))
+    cold_H, cold_G = base_H.copy(), base_G.copy()
+    cold = oracle.decode_step(q, k, v, g, lam, cold_H, cold_G, 9, 1e-7)
+    cases = [(oracle.WARM_COLD, rng.standard_normal((N, H, dk))),
+             (oracle.WARM_PREVIOUS, np.zeros((N, H, dk))),
+             (oracle.WARM_PROJECTED, np.zeros((N, H, dk)))]
+    for mode, x_prev in cases:
+        SH, SG, SX = base_H.copy(), base_G.copy(), x_prev.copy()
+        r = oracle.decode_step_warm(q, k, v, g, lam, SH, SG, SX, 9, 1e-7, mode)
+        np.testing.assert_array_equal(r["out"], cold["out"])
+        np.testing.assert_array_equal(r["iters"], cold["iters"])
+        np.testing.assert_array_equal(SH, cold_H)
+        np.testing.assert_array_equal(SG, cold_G)
+        # this step's solution is left in state_x: G x reproduces the output
+        np.testing.assert_allclose(np.einsum("nhij,nhj->nhi", SG, SX), cold["out"], rtol=1e-12, atol=1e-13)
+
+
+def test_warm_previous_start_is_the_previous_solution():
+    rng = np.random.default_rng(26)
+    dk = dv = 7
+    Hm, Gm = _decode_problem(rng, dk, dv, 10)
+    lam = rng.uniform(0.5, 2.0, (1, dk))
+    q = rng.standard_normal((1, 1, dk))
+    kn = rng.standard_normal((1, 1, dk)) / np.sqrt(dk)
+    vn = rng.standard_normal((1, 1, dv))
+    g = np.array([[0.95]])
+    x_prev = rng.standard_normal(dk)
+    # no update allowed: the solution left behind is the start point itself
+    SH, SG, SX = Hm[None, None].copy(), Gm[None, None].copy(), x_prev[None, None].copy()
+    r = oracle.decode_step_warm(q, kn, vn, g, lam, SH, SG, SX, 0, 0.0, oracle.WARM_PREVIOUS)
+    np.testing.assert_array_equal(SX[0, 0], x_prev)
+    A = 0.95 * Hm + np.outer(kn[0, 0], kn[0, 0])
+    Gn = 0.95 * Gm + np.outer(vn[0, 0], kn[0, 0])
+    np.testing.assert_allclose(r["out"][0, 0], Gn @ x_prev, rtol=1e-12, atol=1e-13)
+    # with updates, the residual that decides the stop is measured from x_prev
+    SH, SG, SX = Hm[None, None].copy(), Gm[None, None].copy(), x_prev[None, None].copy()
+    r = oracle.decode_step_warm(q, kn, vn, g, lam, SH, SG, SX, 3, 0.0, oracle.WARM_PREVIOUS)
+    res = q[0, 0] - (A + np.diag(lam[0])) @ SX[0, 0]
+    assert abs(r["rho_stop"][0, 0] - np.linalg.norm(res) / np.linalg.norm(q[0, 0])) < 1e-10
