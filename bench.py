@@ -166,14 +166,18 @@ def dynamic(torch, mesa, inputs, dev):
 
 def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
     """1024 decode steps over 256 x 16 heads; states built on the device from
-    seeded 4096-token prefixes by the forward path with zero CG iterations."""
+    seeded 4096-token prefixes by the forward path with zero CG iterations.
+    The cold-start run is the measured line; the same steps are then run
+    again from the same states with the warm-started solve, on these i.i.d.
+    queries and on queries that overlap their neighbours (each the sum of 4
+    consecutive Gaussian rows, as a short causal convolution would mix them)."""
     w = inputs.WORKLOADS["decode_f32_d128_N256_prefix4096"]
     N, H, d, P = w.B, w.H, w.d, w.T
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
     log(f"[bench] decode: building {N}x{H} prefix states of {P} tokens")
-    SH = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
-    SG = torch.empty_like(SH)
+    SH0 = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    SG0 = torch.empty_like(SH0)
     lam = torch.from_numpy(inputs.decode_lambda(w)).to(dev)
     for n0 in range(0, N, 64):      # 64 sequences at a time keeps the prefix buffers at 2 GiB each
         nb = min(64, N - n0)
@@ -182,7 +186,7 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
         pv = torch.randn((nb, H, P, d), generator=g, device=dev)
         pg = w.gamma_lo + (1 - w.gamma_lo) * torch.rand((nb, H, P), generator=g, device=dev)
         mesa.mesa_forward(pk, pk, pv, pg, lam, 0, 0.0, w.chunk, return_iters=False,
-                          final_H=SH[n0:n0 + nb], final_G=SG[n0:n0 + nb], return_final=True)
+                          final_H=SH0[n0:n0 + nb], final_G=SG0[n0:n0 + nb], return_final=True)
         del pk, pv, pg
     S = steps + warmup
     q = torch.randn((S, N, H, d), generator=g, device=dev)
@@ -193,32 +197,67 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
     ga = w.gamma_lo + (1 - w.gamma_lo) * torch.rand((S, N, H), generator=g, device=dev)
     out = torch.empty((N, H, d), dtype=torch.float32, device=dev)
     its = torch.empty((S, N, H), dtype=torch.int32, device=dev)
-    for s in range(warmup):
-        mesa.mesa_decode_step(q[s], k[s], v[s], ga[s], lam, SH, SG, w.max_iters, w.tol, out=out, iters=its[s])
-    torch.cuda.synchronize()
-    mesa.profile_reset()
-    mesa.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(warmup, S):
-        mesa.mesa_decode_step(q[s], k[s], v[s], ga[s], lam, SH, SG, w.max_iters, w.tol, out=out, iters=its[s])
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    mesa.profile_enable(False)
-    kd = mesa.profile_read(mesa.KERNEL_DECODE)
-    mesa.profile_reset()
-    kd_ms = kd[0] / max(kd[1], 1)
+
+    def run(qs, mode):
+        """All S steps from the prefix states; mode None = mesa_decode_step, else the warm entry."""
+        SH, SG = SH0.clone(), SG0.clone()
+        SX = torch.zeros((N, H, d), dtype=torch.float32, device=dev)
+
+        def step(s):
+            if mode is None:
+                mesa.mesa_decode_step(qs[s], k[s], v[s], ga[s], lam, SH, SG, w.max_iters, w.tol,
+                                      out=out, iters=its[s])
+            else:
+                mesa.mesa_decode_step_warm(qs[s], k[s], v[s], ga[s], lam, SH, SG, SX, w.max_iters, w.tol,
+                                           mode, out=out, iters=its[s])
+        for s in range(warmup):
+            step(s)
+        torch.cuda.synchronize()
+        mesa.profile_reset()
+        mesa.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(warmup, S):
+            step(s)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        mesa.profile_enable(False)
+        kd = mesa.profile_read(mesa.KERNEL_DECODE)
+        mesa.profile_reset()
+        del SH, SG, SX
+        return el, kd[0] / max(kd[1], 1), its[warmup:].to(torch.float64)
+
+    el, kd_ms, itf = run(q, None)
     nh = N * H
     # per head-step: read + write H and G (fp32 d x d each), q, k, v, gamma, out, iters
     bytes_hs = 4 * 4 * d * d + 3 * 4 * d + 4 + 4 * d + 4
     gbs = bytes_hs * nh / (kd_ms * 1e-3) / 1e9
-    itf = its[warmup:].to(torch.float64)
-    del q, k, v, ga
-    return {"workload": w.name, "head_steps_per_s": round(steps * nh / el, 1), "ms_per_step": round(1e3 * el / steps, 4),
-            "iters_mean": round(float(itf.mean()), 3), "iters_max": int(itf.max()),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "decode_kernel<128,float>",
-                         "bytes_per_launch": bytes_hs * nh, "avg_launch_ms": round(kd_ms, 4)}}
+    res = {"workload": w.name, "head_steps_per_s": round(steps * nh / el, 1),
+           "ms_per_step": round(1e3 * el / steps, 4),
+           "iters_mean": round(float(itf.mean()), 3), "iters_max": int(itf.max()),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "decode_kernel<128,float>",
+                        "bytes_per_launch": bytes_hs * nh, "avg_launch_ms": round(kd_ms, 4)}}
+    z = torch.randn((S + 3, N, H, d), generator=g, device=dev)
+    q4 = z[0:S] + z[1:S + 1] + z[2:S + 2] + z[3:S + 3]
+    q4 /= q4.norm(dim=-1, keepdim=True)
+    del z
+    warm = {}
+    for qname, qs in (("iid", q), ("window4", q4)):
+        warm[qname] = {}
+        for mname, mode in (("cold", None), ("previous", mesa.MESA_WARM_PREVIOUS),
+                            ("projected", mesa.MESA_WARM_PROJECTED)):
+            if qname == "iid" and mode is None:
+                el_m, itf_m = el, itf
+            else:
+                log(f"[bench] decode warm start: queries {qname}, start {mname}")
+                el_m, _, itf_m = run(qs, mode)
+            warm[qname][mname] = {"iters_mean": round(float(itf_m.mean()), 3),
+                                  "ms_per_step": round(1e3 * el_m / steps, 4),
+                                  "head_steps_per_s": round(steps * nh / el_m, 1)}
+    res["warm_start"] = warm
+    del q, q4, k, v, ga
+    return res
 
 
 def measured_peaks(torch, mesa, dev):

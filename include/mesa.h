@@ -142,6 +142,35 @@ mesa_status mesa_decode_step(const void *q, const void *k, const void *v, int qk
                              int N, int H, int dk, int dv, int max_iters, float tol,
                              float *out, int32_t *iters, void *stream);
 
+/* Start points of the warm-started decode solve. */
+typedef enum {
+    MESA_WARM_COLD = 0,       /* x0 = 0: the solve of mesa_decode_step                 */
+    MESA_WARM_PREVIOUS = 1,   /* x0 = x_prev                                           */
+    MESA_WARM_PROJECTED = 2   /* x0 = c x_prev, c = x_prev.q / x_prev.(H+Lambda) x_prev
+                                 (0 when that denominator is not positive)            */
+} mesa_warm_mode;
+
+/*
+ * One decode step whose CG starts from each head's previous solution: the
+ * warm start that the page names as future work for the solver's cost
+ * (section "Significancia e Alegacoes").  Arguments as mesa_decode_step, plus
+ *   state_x   [N, H, dk]      float32, read and overwritten: on entry the
+ *                             previous step's solution x of each head (zeros
+ *                             at the start of a sequence), on exit this step's
+ *   warm_mode                 a mesa_warm_mode
+ * From x0 the CG is the same method with r0 = q - (H + Lambda) x0; the stop
+ * test still compares |r| with |q|, a zero q still gives x = 0 and 0
+ * iterations, and iters counts the updates made after x0.  The projected
+ * start is the multiple of x_prev closest to the solution in the energy
+ * norm, so it is never further from it, in that norm, than the cold start.
+ * out = G x as before.  state_x must not alias any other argument.
+ */
+mesa_status mesa_decode_step_warm(const void *q, const void *k, const void *v, int qkv_dtype,
+                                  const float *gamma, const float *lambda,
+                                  float *state_H, float *state_G, float *state_x,
+                                  int N, int H, int dk, int dv, int max_iters, float tol,
+                                  int warm_mode, float *out, int32_t *iters, void *stream);
+
 /*
  * Optional per-kernel timing (not part of the method).  While enabled, each
  * kernel launch made by the library is bracketed by two hipEvents recorded on

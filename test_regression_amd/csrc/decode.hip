@@ -16,17 +16,25 @@
 // while the CG runs.  The CG scalars are block reductions with a fixed order
 // (deterministic), and the stop test is block-uniform.  The step is bound by
 // HBM traffic on the two d x d states (read + write of H and G).
+//
+// Warm start (section "Significancia e Alegacoes" names warm-start
+// strategies as future work): with WARM, each head also carries its previous
+// solution x_prev.  The solve starts from x0 = c x_prev with c = 1, or with
+// c = x_prev.q / x_prev.(H + Lambda) x_prev (the multiple of x_prev closest to
+// the solution in the energy norm; 0 when the denominator is not positive),
+// so r0 = q - c (H + Lambda) x_prev; the stop test still compares |r| with
+// |q|, a zero q still gives x = 0, and the solution is written back.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
 namespace mesa {
 
-template <int D, typename In>
+template <int D, bool WARM, typename In>
 __global__ __launch_bounds__(256) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ gamma, const float* __restrict__ lambda, float* __restrict__ SH,
-    float* __restrict__ SG, int H, int max_iters, float tol, float* __restrict__ out,
-    int32_t* __restrict__ iters) {
+    float* __restrict__ SG, float* __restrict__ SX, int warm_mode, int H, int max_iters, float tol,
+    float* __restrict__ out, int32_t* __restrict__ iters) {
     constexpr int TPR = 256 / D;   // threads per state row
     constexpr int EPT = D / TPR;   // state entries per thread
     __shared__ float sq[D], sk[D], sv[D], sp[D], sx[D];
@@ -51,6 +59,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
         sq[tid] = to_f32(q[nh * D + tid]);
         sk[tid] = to_f32(k[nh * D + tid]);
         sv[tid] = to_f32(v[nh * D + tid]);
+        if constexpr (WARM) sx[tid] = warm_mode != 0 ? SX[nh * D + tid] : 0.f;
     }
     const float g = gamma[nh];
     const float lam_r = lambda[(size_t)h * D + row];
@@ -106,11 +115,31 @@ __global__ __launch_bounds__(256) void decode_kernel(
         for (int e = 0; e < EPT; ++e) Hrow[col(e)] = hr[e];
     }
 
-    // ---- CG on (H + diag lambda) x = q from x = 0 ----
-    float x_r = 0.f, r_r = sq[row], p_r = r_r;
+    // ---- CG on (H + diag lambda) x = q from x = 0 (or the warm start) ----
+    const float q_r = sq[row];
+    float x_r = 0.f, r_r = q_r;
     float rr = block_sum(part == 0 ? r_r * r_r : 0.f, 0);
     const float nq = sqrtf(rr);
-    if (tid < D) sp[tid] = sq[tid];
+    if constexpr (WARM) {
+        if (warm_mode != 0 && nq > 0.f) {   // block-uniform
+            const float xp = sx[row];
+            float y = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) y += hr[e] * sx[col(e)];
+            y = row_sum(y) + lam_r * xp;    // (H + Lambda) x_prev
+            float c = 1.f;
+            if (warm_mode == 2) {
+                const float xq = block_sum(part == 0 ? xp * q_r : 0.f, 1);
+                const float xax = block_sum(part == 0 ? xp * y : 0.f, 0);
+                c = xax > 0.f ? xq / xax : 0.f;
+            }
+            x_r = c * xp;
+            r_r = q_r - c * y;
+            rr = block_sum(part == 0 ? r_r * r_r : 0.f, 1);
+        }
+    }
+    float p_r = r_r;
+    if (part == 0) sp[row] = p_r;
     __syncthreads();
     int it = 0;
     while (it < max_iters) {
@@ -132,7 +161,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
         if (part == 0) sp[row] = p_r;
         __syncthreads();
     }
-    if (part == 0) sx[row] = x_r;
+    // (the warm start's reads of sx ended before the block sums that followed them)
+    if (part == 0) {
+        sx[row] = x_r;
+        if constexpr (WARM) SX[nh * D + row] = x_r;
+    }
     __syncthreads();
 
     // ---- G <- gamma G + v k^T (in place), out = G x ----
@@ -158,9 +191,14 @@ __global__ __launch_bounds__(256) void decode_kernel(
 
 template <int D, typename In>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<D, In>), dim3((unsigned)a.NH), dim3(256), 0, s, (const In*)a.q,
-                       (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.SH, a.SG, a.H, a.max_iters,
-                       a.tol, a.out, a.iters);
+    if (a.X)
+        hipLaunchKernelGGL((decode_kernel<D, true, In>), dim3((unsigned)a.NH), dim3(256), 0, s, (const In*)a.q,
+                           (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.SH, a.SG, a.X, a.warm_mode,
+                           a.H, a.max_iters, a.tol, a.out, a.iters);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, false, In>), dim3((unsigned)a.NH), dim3(256), 0, s, (const In*)a.q,
+                           (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.SH, a.SG, nullptr, 0, a.H,
+                           a.max_iters, a.tol, a.out, a.iters);
     return hipGetLastError();
 }
 

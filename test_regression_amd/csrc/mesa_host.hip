@@ -188,10 +188,10 @@ mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dt
     return MESA_OK;
 }
 
-mesa_status mesa_decode_step(const void* q, const void* k, const void* v, int qkv_dtype,
-                             const float* gamma, const float* lambda, float* state_H,
-                             float* state_G, int N, int H, int dk, int dv, int max_iters,
-                             float tol, float* out, int32_t* iters, void* stream) {
+static mesa_status decode_impl(const char* what, const void* q, const void* k, const void* v, int qkv_dtype,
+                               const float* gamma, const float* lambda, float* state_H, float* state_G,
+                               float* state_x, int warm_mode, int N, int H, int dk, int dv, int max_iters,
+                               float tol, float* out, int32_t* iters, void* stream) {
     g_err.clear();
     if (qkv_dtype != MESA_DTYPE_F32 && qkv_dtype != MESA_DTYPE_BF16)
         return fail(MESA_ERR_INVALID_ARGUMENT, "qkv_dtype %d is not MESA_DTYPE_F32 or MESA_DTYPE_BF16", qkv_dtype);
@@ -205,7 +205,7 @@ mesa_status mesa_decode_step(const void* q, const void* k, const void* v, int qk
         return fail(MESA_ERR_INVALID_ARGUMENT, "q, k, v, gamma, lambda, state_H, state_G and out must be non-null");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(state_H, 16) || !aligned(state_G, 16) || !aligned(gamma, 4) ||
-        !aligned(lambda, 4) || !aligned(iters, 4))
+        !aligned(lambda, 4) || !aligned(iters, 4) || !aligned(state_x, 16))
         return fail(MESA_ERR_INVALID_ARGUMENT, "misaligned pointer (16 B for tensors, 4 B for gamma/lambda/iters)");
     if (dk != dv) return fail(MESA_ERR_UNSUPPORTED, "dk (%d) != dv (%d) is not built", dk, dv);
     if (!supported_d(dk)) return fail(MESA_ERR_UNSUPPORTED, "d=%d not built (16, 32, 64, 128)", dk);
@@ -213,10 +213,32 @@ mesa_status mesa_decode_step(const void* q, const void* k, const void* v, int qk
     if (NH > 0x7fffffffL) return fail(MESA_ERR_INVALID_ARGUMENT, "grid too large (N*H=%ld)", NH);
     hipStream_t s = static_cast<hipStream_t>(stream);
     mesa::DecodeArgs a{q, k, v, gamma, lambda, state_H, state_G, NH, H, dk,
-                       qkv_dtype == MESA_DTYPE_BF16, max_iters, tol, out, iters};
+                       qkv_dtype == MESA_DTYPE_BF16, max_iters, tol, out, iters, state_x, warm_mode};
     hipError_t e = timed_launch(MESA_KERNEL_DECODE, s, [&] { return mesa::launch_decode(a, s); });
-    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    if (e != hipSuccess) return hip_fail(e, what);
     return MESA_OK;
+}
+
+mesa_status mesa_decode_step(const void* q, const void* k, const void* v, int qkv_dtype,
+                             const float* gamma, const float* lambda, float* state_H,
+                             float* state_G, int N, int H, int dk, int dv, int max_iters,
+                             float tol, float* out, int32_t* iters, void* stream) {
+    return decode_impl("decode kernel launch", q, k, v, qkv_dtype, gamma, lambda, state_H, state_G, nullptr, 0,
+                       N, H, dk, dv, max_iters, tol, out, iters, stream);
+}
+
+mesa_status mesa_decode_step_warm(const void* q, const void* k, const void* v, int qkv_dtype,
+                                  const float* gamma, const float* lambda, float* state_H,
+                                  float* state_G, float* state_x, int N, int H, int dk, int dv,
+                                  int max_iters, float tol, int warm_mode, float* out, int32_t* iters,
+                                  void* stream) {
+    g_err.clear();
+    if (!state_x) return fail(MESA_ERR_INVALID_ARGUMENT, "state_x must be non-null");
+    if (warm_mode != MESA_WARM_COLD && warm_mode != MESA_WARM_PREVIOUS && warm_mode != MESA_WARM_PROJECTED)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "warm_mode %d is not MESA_WARM_COLD, MESA_WARM_PREVIOUS or "
+                    "MESA_WARM_PROJECTED", warm_mode);
+    return decode_impl("warm decode kernel launch", q, k, v, qkv_dtype, gamma, lambda, state_H, state_G, state_x,
+                       warm_mode, N, H, dk, dv, max_iters, tol, out, iters, stream);
 }
 
 mesa_status mesa_profile_enable(int on) {

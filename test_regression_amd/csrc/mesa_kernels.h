@@ -25,6 +25,7 @@ struct DecodeArgs {
     float* SH; float* SG;
     long NH; int H; int d; int bf16; int max_iters; float tol;
     float* out; int32_t* iters;
+    float* X; int warm_mode;   // warm start: previous solutions [NH, d] (nullptr: cold)
 };
 
 hipError_t launch_chunk_states(const ChunkStatesArgs& a, hipStream_t s);

@@ -163,3 +163,21 @@ def decode_steps(w: Workload, steps: int, N: int = None, H: int = None, stream: 
     v = rng.standard_normal(shape).astype(np.float32)
     g = rng.uniform(w.gamma_lo, 1.0, size=(steps, N, H)).astype(np.float32)
     return dict(q=q, k=k, v=v, gamma=g)
+
+
+def decode_queries_windowed(w: Workload, steps: int, window: int, N: int = None, H: int = None,
+                            stream: int = 0):
+    """Decode queries [steps,N,H,d] whose neighbours overlap: each is the
+    unit-normalised sum of `window` consecutive i.i.d. N(0, 1) rows, the way a
+    short causal convolution over the token axis mixes neighbouring inputs
+    before the layer.  Consecutive queries then share window - 1 of their
+    terms.  window = 1 gives independent unit Gaussian rows.  float32.
+    """
+    N = w.B if N is None else N
+    H = w.H if H is None else H
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0xC0E, window, stream])))
+    z = rng.standard_normal((steps + window - 1, N, H, w.d))
+    s = np.zeros((steps, N, H, w.d))
+    for j in range(window):
+        s += z[j:j + steps]
+    return (s / np.linalg.norm(s, axis=-1, keepdims=True)).astype(np.float32)

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmesa.so")
 MESA_OK, MESA_ERR_INVALID_ARGUMENT, MESA_ERR_UNSUPPORTED, MESA_ERR_WORKSPACE_TOO_SMALL, MESA_ERR_HIP = range(5)
 MESA_DTYPE_F32, MESA_DTYPE_BF16 = 0, 1
 KERNEL_CHUNK_STATES, KERNEL_CG_OUTPUT, KERNEL_DECODE = 0, 1, 2
+MESA_WARM_COLD, MESA_WARM_PREVIOUS, MESA_WARM_PROJECTED = 0, 1, 2
 
 # Every symbol include/mesa.h declares, with its ctypes signature.
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -28,6 +29,8 @@ SIGNATURES = {
                       _P, _P, _P, _P, _P, _Z, _P], _I),
     "mesa_decode_step": ([_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
                           _P, _P, _P], _I),
+    "mesa_decode_step_warm": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                               _P, _P, _P], _I),
     "mesa_profile_enable": ([_I], _I),
     "mesa_profile_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "mesa_profile_reset": ([], _I),
@@ -150,6 +153,26 @@ def mesa_forward(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out=None,
     return out, iters, final_H, final_G
 
 
+def _decode_checks(q, v, gamma, lam, state_H, state_G, state_x=None):
+    import torch
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(gamma, "gamma", torch.float32, dev)
+    _need(lam, "lambda", torch.float32, dev)
+    _need(state_H, "state_H", torch.float32, dev)
+    _need(state_G, "state_G", torch.float32, dev)
+    if tuple(state_H.shape) != (N, H, dk, dk) or tuple(state_G.shape) != (N, H, dv, dk):
+        raise ValueError("state shapes disagree with q/v")
+    if state_x is not None:
+        _need(state_x, "state_x", torch.float32, dev)
+        if tuple(state_x.shape) != (N, H, dk):
+            raise ValueError("state_x must be [N,H,dk]")
+    return N, H, dk, dv, dev
+
+
 def mesa_decode_step(q, k, v, gamma, lam, state_H, state_G, max_iters, tol=0.0, *,
                      out=None, iters=None, return_iters=True, stream=None):
     """One decode step (see include/mesa.h, mesa_decode_step); state_H/G updated in place.
@@ -158,26 +181,39 @@ def mesa_decode_step(q, k, v, gamma, lam, state_H, state_G, max_iters, tol=0.0, 
     state_H: [N,H,dk,dk], state_G: [N,H,dv,dk] float32.  Returns (out, iters).
     """
     import torch
-    N, H, dk = q.shape
-    dv = v.shape[-1]
-    dev = q.device
-    dt = _qkv_dtype(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype, dev)
-    _need(gamma, "gamma", torch.float32, dev)
-    _need(lam, "lambda", torch.float32, dev)
-    _need(state_H, "state_H", torch.float32, dev)
-    _need(state_G, "state_G", torch.float32, dev)
-    if tuple(state_H.shape) != (N, H, dk, dk) or tuple(state_G.shape) != (N, H, dv, dk):
-        raise ValueError("state shapes disagree with q/v")
+    _need(k, "k", q.dtype, q.device)
+    N, H, dk, dv, dev = _decode_checks(q, v, gamma, lam, state_H, state_G)
     if out is None:
         out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     if iters is None and return_iters:
         iters = torch.empty((N, H), dtype=torch.int32, device=dev)
-    st = lib().mesa_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(gamma), _ptr(lam),
+    st = lib().mesa_decode_step(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(gamma), _ptr(lam),
                                 _ptr(state_H), _ptr(state_G), N, H, dk, dv, int(max_iters),
                                 float(tol), _ptr(out), _ptr(iters), _stream(stream))
     _check(st, "mesa_decode_step")
+    return out, iters
+
+
+def mesa_decode_step_warm(q, k, v, gamma, lam, state_H, state_G, state_x, max_iters, tol=0.0,
+                          warm_mode=MESA_WARM_PROJECTED, *, out=None, iters=None, return_iters=True,
+                          stream=None):
+    """One warm-started decode step (see include/mesa.h, mesa_decode_step_warm).
+
+    As mesa_decode_step, plus state_x [N,H,dk] float32: the previous
+    solutions on entry, this step's on exit.  Returns (out, iters).
+    """
+    import torch
+    _need(k, "k", q.dtype, q.device)
+    N, H, dk, dv, dev = _decode_checks(q, v, gamma, lam, state_H, state_G, state_x)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    if iters is None and return_iters:
+        iters = torch.empty((N, H), dtype=torch.int32, device=dev)
+    st = lib().mesa_decode_step_warm(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(gamma), _ptr(lam),
+                                     _ptr(state_H), _ptr(state_G), _ptr(state_x), N, H, dk, dv,
+                                     int(max_iters), float(tol), int(warm_mode), _ptr(out), _ptr(iters),
+                                     _stream(stream))
+    _check(st, "mesa_decode_step_warm")
     return out, iters
 
 

@@ -141,6 +141,33 @@ def test_decode_rejects_bad_arguments(kw, status, needle):
     assert needle in msg
 
 
+def dec_warm(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=0, gamma=FAKE, lam=FAKE, SH=FAKE, SG=FAKE, SX=FAKE, N=4, H=2,
+             dk=64, dv=64, max_iters=5, tol=1e-4, mode=2, out=FAKE, iters=FAKE, stream=None)
+    a.update(kw)
+    L = mesa.lib()
+    st = L.mesa_decode_step_warm(a["q"], a["k"], a["v"], a["dtype"], a["gamma"], a["lam"], a["SH"], a["SG"],
+                                 a["SX"], a["N"], a["H"], a["dk"], a["dv"], a["max_iters"],
+                                 ctypes.c_float(a["tol"]), a["mode"], a["out"], a["iters"], a["stream"])
+    return st, L.mesa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(SX=None), INVALID, "state_x"),
+    (dict(mode=3), INVALID, "warm_mode"),
+    (dict(mode=-1), INVALID, "warm_mode"),
+    (dict(SX=FAKE + 4), INVALID, "misaligned"),
+    (dict(SH=None), INVALID, "non-null"),
+    (dict(N=0), INVALID, "positive"),
+    (dict(tol=-1.0), INVALID, "tol"),
+    (dict(dk=48, dv=48), UNSUPPORTED, "d=48"),
+])
+def test_warm_decode_rejects_bad_arguments(kw, status, needle):
+    st, msg = dec_warm(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
 def test_probe_argument_validation():
     L = mesa.lib()
     assert L.mesa_probe_mfma_f32(0, 10, FAKE, None) == INVALID

@@ -162,6 +162,68 @@ def test_decode_workload_full_launch_shape():
     assert rel_l2(SH.cpu().numpy(), RH) < 1e-5 and rel_l2(SG.cpu().numpy(), RG) < 1e-5
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+def test_warm_decode_full_launch_shape(mode):
+    """Warm-started decode (x0 from each head's previous solution) at 256 x 16
+    heads, d=128, chained over steps with queries that overlap their
+    neighbours (window 4); the solution carried in state_x is compared too."""
+    import torch
+    from test_regression_amd import mesa
+    w = inputs.WORKLOADS["decode_f32_d128_N256_prefix4096"]
+    steps = 4
+    say("case warm decode", w.name, "mode", mode, "steps", steps)
+    H0, G0, st, lam = _decode_case(w, steps, S=16, prefix=w.T)
+    st["q"] = inputs.decode_queries_windowed(w, steps, 4)
+    SH, SG = to_dev(H0, "f32"), to_dev(G0, "f32")
+    SX = torch.zeros((w.B, w.H, w.d), dtype=torch.float32, device="cuda")
+    lam_d = to_dev(lam, "f32")
+    RH, RG = H0.astype(np.float64), G0.astype(np.float64)
+    RX = np.zeros((w.B, w.H, w.d))
+    for s in range(steps):
+        q, k, v, g = (to_dev(st[n][s], "f32") for n in ("q", "k", "v", "gamma"))
+        out, it = mesa.mesa_decode_step_warm(q, k, v, g, lam_d, SH, SG, SX, w.max_iters, w.tol, mode)
+        torch.cuda.synchronize()
+        r = oracle.decode_step_warm(st["q"][s], st["k"][s], st["v"][s], st["gamma"][s], lam, RH, RG, RX,
+                                    w.max_iters, w.tol, mode)
+        e = rel_l2(out.cpu().numpy(), r["out"])
+        ex = rel_l2(SX.cpu().numpy(), RX)
+        nd, nu, nm = compare_counts(it.cpu().numpy(), r, w.max_iters, w.tol)
+        say(f"warm decode step {s}: rel_l2={e:.3e} x rel_l2={ex:.3e} iters mean={r['iters'].mean():.2f} "
+            f"decidable={nd} undecidable={nu} mismatched={nm}")
+        assert e <= RTOL["f32"] and ex <= RTOL["f32"]
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+def test_warm_decode_small_dims_and_zero_query(d):
+    import torch
+    from test_regression_amd import mesa
+    N, H, P, cap, tol = 3, 2, 40, 30, 1e-5
+    say("case warm decode dims", d)
+    x = small_inputs(90 + d, N, H, P + 3, d, "f32")
+    x["q"][1, 0, P + 1] = 0.0            # a zero query: x = 0 and no update, whatever x_prev is
+    pre = oracle.forward(x["k"][:, :, :P], x["k"][:, :, :P], x["v"][:, :, :P], x["gamma"][:, :, :P],
+                         x["lam"], 0, 0.0, want=np.zeros((N, H, P), bool), final_state=True)
+    H0 = pre["final_H"].astype(np.float32)
+    G0 = pre["final_G"].astype(np.float32)
+    for mode in (0, 1, 2):
+        SH, SG = to_dev(H0, "f32"), to_dev(G0, "f32")
+        RH, RG = H0.astype(np.float64), G0.astype(np.float64)
+        X0 = np.random.default_rng(d).standard_normal((N, H, d)).astype(np.float32)
+        SX, RX = to_dev(X0, "f32"), X0.astype(np.float64)
+        lam = to_dev(x["lam"], "f32")
+        for s in (P, P + 1, P + 2):
+            args = [np.ascontiguousarray(x[n][:, :, s]) for n in ("q", "k", "v", "gamma")]
+            out, it = mesa.mesa_decode_step_warm(*(to_dev(a, "f32") for a in args), lam, SH, SG, SX,
+                                                 cap, tol, mode)
+            torch.cuda.synchronize()
+            r = oracle.decode_step_warm(*args, x["lam"], RH, RG, RX, cap, tol, mode)
+            assert rel_l2(out.cpu().numpy(), r["out"]) <= 2e-3, (mode, s)
+            assert rel_l2(SX.cpu().numpy(), RX) <= 2e-3, (mode, s)
+            compare_counts(it.cpu().numpy(), r, cap, tol)
+            if s == P + 1:
+                assert not SX.cpu().numpy()[1, 0].any() and int(it[1, 0]) == 0
+
+
 # ---------------------------------------------------------------- structure
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
