@@ -62,6 +62,8 @@ def _load():
         lib.oracle_decode_step_warm.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, D, I,
                                                 P, P, P, P, P]
         lib.oracle_decode_step_warm.restype = I
+        lib.oracle_qk_preprocess.argtypes = [P, P, I, P, P, I, I, I, I, P]
+        lib.oracle_qk_preprocess.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -196,3 +198,25 @@ def decode_step_warm(q, k, v, gamma, lam, state_H, state_G, state_x, max_iters, 
     if rc != 0:
         raise ValueError("oracle_decode_step_warm rejected its arguments")
     return dict(out=out, iters=iters, reason=reason, rho_stop=rho_stop, rho_min_prev=rho_min_prev)
+
+
+def qk_preprocess(x, w, hist=None, want_hist=False):
+    """Causal depthwise convolution of width W over tokens, then L2 normalisation per token.
+
+    x: [B,H,T,d]; w: [H,W,d]; hist: [B,H,W-1,d] rows before t = 0 (None = zeros).
+    Returns y [B,H,T,d] (float64), and with want_hist also the last W-1 input rows.
+    """
+    lib = _load()
+    x, w = _f64(x), _f64(w)
+    B, H, T, d = x.shape
+    W = w.shape[1]
+    assert w.shape == (H, W, d)
+    if hist is not None:
+        hist = _f64(hist)
+        assert hist.shape == (B, H, W - 1, d)
+    y = np.zeros((B, H, T, d))
+    ho = np.zeros((B, H, W - 1, d)) if want_hist else None
+    rc = lib.oracle_qk_preprocess(_ptr(x), _ptr(w), W, _ptr(hist), _ptr(ho), B, H, T, d, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_qk_preprocess rejected its arguments")
+    return (y, ho) if want_hist else y

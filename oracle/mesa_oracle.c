@@ -319,5 +319,61 @@ int oracle_decode_step_warm(const double *q, const double *k, const double *v,
     return bad ? -1 : 0;
 }
 
+/*
+ * Query/key pre-processing before the layer (MesaNet summary, section
+ * "Arquitetura (MesaNet)", bullet "Pre-processamento": keys and queries are
+ * normalised and convolved with a small window before the Mesa layer).
+ * Reading: a causal depthwise convolution over the token axis, per head and
+ * feature, of width W, followed by L2 normalisation of each token's vector:
+ *   c_t[f] = sum_{j=0..W-1} w[h][j][f] x_{t-j}[f]
+ *   y_t    = c_t / |c_t|_2        (y_t = 0 when c_t = 0)
+ * Rows before t = 0 come from hist ([B,H,W-1,d], oldest first; NULL = zeros),
+ * so a sequence can be processed in pieces.  hist_out (may be NULL) receives
+ * the last W-1 input rows of hist followed by x, for the next piece.
+ *   x : [B,H,T,d]   w : [H,W,d]   y : [B,H,T,d]
+ */
+int oracle_qk_preprocess(const double *x, const double *w, int W, const double *hist,
+                         double *hist_out, int B, int H, int T, int d, double *y)
+{
+    if (B < 0 || H < 0 || T < 0 || d <= 0 || W < 1) return -1;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < (long)B * H; ++bh) {
+        int h = (int)(bh % H);
+        const double *xb = x + (size_t)bh * T * d;
+        const double *hb = hist ? hist + (size_t)bh * (W - 1) * d : NULL;
+        for (int t = 0; t < T; ++t) {
+            double *yt = y + ((size_t)bh * T + t) * d;
+            double ss = 0.0;
+            for (int f = 0; f < d; ++f) {
+                double c = 0.0;
+                for (int j = 0; j < W; ++j) {
+                    int src = t - j;           /* token index; < 0 reaches into hist */
+                    double xv;
+                    if (src >= 0) xv = xb[(size_t)src * d + f];
+                    else xv = hb ? hb[(size_t)(W - 1 + src) * d + f] : 0.0;
+                    c += w[((size_t)h * W + j) * d + f] * xv;
+                }
+                yt[f] = c;
+                ss += c * c;
+            }
+            double nrm = sqrt(ss);
+            for (int f = 0; f < d; ++f) yt[f] = nrm > 0.0 ? yt[f] / nrm : 0.0;
+        }
+        if (hist_out) {
+            double *ho = hist_out + (size_t)bh * (W - 1) * d;
+            for (int r = 0; r < W - 1; ++r) {
+                int src = T - (W - 1) + r;     /* position in x; < 0 reaches into hist */
+                for (int f = 0; f < d; ++f) {
+                    double xv;
+                    if (src >= 0) xv = xb[(size_t)src * d + f];
+                    else xv = hb ? hb[(size_t)(W - 1 + src) * d + f] : 0.0;
+                    ho[(size_t)r * d + f] = xv;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 /* Threads an OpenMP parallel region of this library would use. */
 int oracle_max_threads(void) { return omp_get_max_threads(); }

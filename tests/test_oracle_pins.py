@@ -510,3 +510,66 @@ def test_warm_previous_start_is_the_previous_solution():
     r = oracle.decode_step_warm(q, kn, vn, g, lam, SH, SG, SX, 3, 0.0, oracle.WARM_PREVIOUS)
     res = q[0, 0] - (A + np.diag(lam[0])) @ SX[0, 0]
     assert abs(r["rho_stop"][0, 0] - np.linalg.norm(res) / np.linalg.norm(q[0, 0])) < 1e-10
+
+
+# --------------------------------------------------------------------------
+# q/k pre-processing (section "Arquitetura (MesaNet)", bullet
+# "Pre-processamento": keys and queries are normalised and convolved with a
+# small window before the layer).  C1: a hand-worked example (width 2,
+# d = 2).  C2: each channel's convolution equals numpy.convolve truncated to
+# the causal part, then unit-normalised.  C3: a sequence cut into pieces with
+# the carried history gives the same result as one piece.  C4: width 1 with
+# unit weights is plain L2 normalisation; zero rows stay zero.
+# --------------------------------------------------------------------------
+def test_preprocess_hand_worked_example():
+    x = np.array([[3.0, 0.0], [1.0, 4.0], [0.0, -4.0]])[None, None]
+    w = np.array([[[1.0, 1.0], [2.0, 0.5]]])         # w[h][j][f], j = 0 is the current token
+    # c_0 = (3, 0); c_1 = (1 + 6, 4 + 0) = (7, 4); c_2 = (0 + 2, -4 + 2) = (2, -2)
+    want = np.array([[1.0, 0.0], [7.0, 4.0] / np.sqrt(65.0), [2.0, -2.0] / np.sqrt(8.0)])
+    y = oracle.qk_preprocess(x, w)
+    np.testing.assert_allclose(y[0, 0], want, rtol=1e-15, atol=1e-15)
+
+
+def test_preprocess_matches_numpy_convolve():
+    rng = np.random.default_rng(31)
+    B, H, T, d, W = 2, 3, 17, 5, 4
+    x = rng.standard_normal((B, H, T, d))
+    w = rng.standard_normal((H, W, d))
+    y = oracle.qk_preprocess(x, w)
+    for b in range(B):
+        for h in range(H):
+            c = np.stack([np.convolve(x[b, h, :, f], w[h, :, f])[:T] for f in range(d)], axis=-1)
+            want = c / np.linalg.norm(c, axis=-1, keepdims=True)
+            assert rel(y[b, h], want) < 1e-13
+    # the order matters: normalising first and convolving after is different
+    xn = x / np.linalg.norm(x, axis=-1, keepdims=True)
+    c = np.stack([np.convolve(xn[0, 0, :, f], w[0, :, f])[:T] for f in range(d)], axis=-1)
+    assert rel(y[0, 0], c) > 1e-3
+
+
+def test_preprocess_history_continues_the_sequence():
+    rng = np.random.default_rng(32)
+    B, H, d = 2, 2, 6
+    for W, cuts in ((4, (5, 1, 2, 9)), (3, (1, 1, 1, 4)), (2, (7,)), (1, (3, 3))):
+        T = sum(cuts)
+        x = rng.standard_normal((B, H, T, d))
+        w = rng.standard_normal((H, W, d))
+        whole = oracle.qk_preprocess(x, w)
+        hist, t0, parts = None, 0, []
+        for n in cuts:
+            y, hist = oracle.qk_preprocess(x[:, :, t0:t0 + n], w, hist=hist, want_hist=True)
+            parts.append(y)
+            t0 += n
+        np.testing.assert_allclose(np.concatenate(parts, axis=2), whole, rtol=1e-13, atol=1e-14)
+        # the carried rows are the last W-1 inputs
+        np.testing.assert_array_equal(hist, x[:, :, T - (W - 1):])
+
+
+def test_preprocess_width_one_is_normalisation():
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((1, 2, 9, 7)) * rng.uniform(0.1, 10, (1, 2, 9, 1))
+    x[0, 1, 4] = 0.0
+    y = oracle.qk_preprocess(x, np.ones((2, 1, 7)))
+    n = np.linalg.norm(x, axis=-1, keepdims=True)
+    np.testing.assert_allclose(y, np.where(n > 0, x / np.where(n > 0, n, 1), 0), rtol=1e-15)
+    assert not y[0, 1, 4].any()
