@@ -260,6 +260,48 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
     return res
 
 
+def qk_preprocess(torch, mesa, inputs, dev, steps=20, warmup=3, W=4):
+    """The q/k pre-processing pass at the headline layer's shape: raw q and k
+    (bf16, 8 x 16 x 4096, d=128) -> causal width-4 convolution + L2
+    normalisation -> bf16, two launches per step.  HBM-bound."""
+    w = inputs.WORKLOADS["layer_bf16_d128_T4096_k30"]
+    B, H, T, d = w.B, w.H, w.T, w.d
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 77)
+    xq = torch.randn((B, H, T, d), generator=g, device=dev).to(torch.bfloat16)
+    xk = torch.randn((B, H, T, d), generator=g, device=dev).to(torch.bfloat16)
+    wq = torch.randn((H, W, d), generator=g, device=dev) / W ** 0.5
+    wk = torch.randn((H, W, d), generator=g, device=dev) / W ** 0.5
+    yq = torch.empty_like(xq)
+    yk = torch.empty_like(xk)
+
+    def step():
+        mesa.mesa_qk_preprocess(xq, wq, out=yq)
+        mesa.mesa_qk_preprocess(xk, wk, out=yk)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mesa.profile_reset()
+    mesa.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    mesa.profile_enable(False)
+    kp = mesa.profile_read(mesa.KERNEL_QK_PREPROCESS)
+    mesa.profile_reset()
+    k_ms = kp[0] / max(kp[1], 1)
+    per_launch = B * H * T * d * (2 + 2) + H * W * d * 4     # read x, write y (bf16), weights
+    gbs = per_launch / (k_ms * 1e-3) / 1e9
+    del xq, xk, yq, yk
+    return {"workload": f"qk_preprocess_bf16_d128_T4096_W{W}", "B": B, "H": H, "T": T, "width": W,
+            "tokens_per_s": round(B * H * T * steps / el, 1), "ms_per_step_q_and_k": round(1e3 * el / steps, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "qk_preprocess_kernel<128,bf16,bf16>",
+                         "bytes_per_launch": per_launch, "avg_launch_ms": round(k_ms, 4)}}
+
+
 def measured_peaks(torch, mesa, dev):
     """Attainable rates on this GPU from known-work probe kernels: fp32 and
     bf16 MFMA register-resident loops (1024 workgroups x 4 waves) and a 1 GiB
@@ -366,6 +408,8 @@ def main():
         torch.cuda.empty_cache()
         extra["decode"] = decode(torch, mesa, inputs, dev)
         torch.cuda.empty_cache()
+        extra["qk_preprocess"] = qk_preprocess(torch, mesa, inputs, dev)
+        torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on {args.cpu_heads} heads")
@@ -385,10 +429,11 @@ def main():
         "kernels": h["kernels"],
     }
     line["measured_peaks"] = peaks
-    if "decode" in extra:
-        d = extra["decode"]["roofline"]
-        d["peak_measured"] = peaks["copy_gbs"]
-        d["frac_measured"] = round(d["achieved"] / peaks["copy_gbs"], 4)
+    for sec in ("decode", "qk_preprocess"):
+        if sec in extra:
+            d = extra[sec]["roofline"]
+            d["peak_measured"] = peaks["copy_gbs"]
+            d["frac_measured"] = round(d["achieved"] / peaks["copy_gbs"], 4)
     line.update(extra)
     print(json.dumps(line), flush=True)
 

@@ -71,7 +71,8 @@ typedef enum {
     MESA_KERNEL_CHUNK_STATES = 0,    /* chunk-boundary states S^H_c, S^G_c (+ final)     */
     MESA_KERNEL_CG_OUTPUT = 1,       /* all CG iterations of a chunk + output contraction */
     MESA_KERNEL_DECODE = 2,          /* one recurrent decode step                        */
-    MESA_KERNEL_COUNT = 3
+    MESA_KERNEL_QK_PREPROCESS = 3,   /* q/k convolution + normalisation                  */
+    MESA_KERNEL_COUNT = 4
 } mesa_kernel_id;
 
 /* Library ABI version (MESA_ABI_VERSION of the build). */
@@ -170,6 +171,33 @@ mesa_status mesa_decode_step_warm(const void *q, const void *k, const void *v, i
                                   float *state_H, float *state_G, float *state_x,
                                   int N, int H, int dk, int dv, int max_iters, float tol,
                                   int warm_mode, float *out, int32_t *iters, void *stream);
+
+/*
+ * Query/key pre-processing before the layer (section "Arquitetura (MesaNet)",
+ * bullet "Pre-processamento": keys and queries are normalised and convolved
+ * with a small window before the Mesa layer).  Reading: per head h, token t
+ * and feature f, a causal convolution of width W over the tokens followed by
+ * L2 normalisation of each token's vector,
+ *   c_t[f] = sum_{j<W} conv_w[h][j][f] x_{t-j}[f],   y_t = c_t / |c_t|_2
+ * (y_t = 0 when c_t = 0), in one pass: one read of x, one write of y.  Call
+ * it once for q and once for k (each with its own weights).
+ *
+ *   x         [B, H, T, d]    in_dtype (mesa_dtype)
+ *   conv_w    [H, W, d]       float32; j = 0 weighs the current token
+ *   width     W, 1 <= W <= 8 (this build: W <= 4, else MESA_ERR_UNSUPPORTED)
+ *   hist      [B, H, W-1, d]  in_dtype, the W-1 input rows before t = 0
+ *                             (oldest first), or NULL for zeros
+ *   hist_out  [B, H, W-1, d]  in_dtype, or NULL: receives the last W-1 rows
+ *                             of hist followed by x, the hist of the next
+ *                             piece (prefill, then one token per decode step)
+ *   y         [B, H, T, d]    out_dtype (mesa_dtype; bfloat16 rounds to
+ *                             nearest even)
+ * d in {16, 32, 64, 128}; T >= 0.  y must not alias x, and hist_out must not
+ * alias hist or x.  Inputs must be finite.
+ */
+mesa_status mesa_qk_preprocess(const void *x, int in_dtype, const float *conv_w, int width,
+                               const void *hist, void *hist_out, int B, int H, int T, int d,
+                               void *y, int out_dtype, void *stream);
 
 /*
  * Optional per-kernel timing (not part of the method).  While enabled, each

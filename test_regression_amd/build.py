@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmesa.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
-SOURCES = ["mesa_host.hip", "chunk_states.hip", "cg_output.hip", "decode.hip", "probes.hip"]
+SOURCES = ["mesa_host.hip", "chunk_states.hip", "cg_output.hip", "decode.hip", "qk_preprocess.hip",
+           "probes.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -47,8 +47,8 @@ struct ProfRec { hipEvent_t a, b; int kid; };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof_pending;
-double g_prof_ms[MESA_KERNEL_COUNT] = {0, 0, 0};
-int64_t g_prof_n[MESA_KERNEL_COUNT] = {0, 0, 0};
+double g_prof_ms[MESA_KERNEL_COUNT] = {};
+int64_t g_prof_n[MESA_KERNEL_COUNT] = {};
 
 // Launches `fn` on `s`; when profiling is on, brackets it with two events.
 template <typename Fn>
@@ -241,6 +241,42 @@ mesa_status mesa_decode_step_warm(const void* q, const void* k, const void* v, i
                        warm_mode, N, H, dk, dv, max_iters, tol, out, iters, stream);
 }
 
+mesa_status mesa_qk_preprocess(const void* x, int in_dtype, const float* conv_w, int width, const void* hist,
+                               void* hist_out, int B, int H, int T, int d, void* y, int out_dtype,
+                               void* stream) {
+    g_err.clear();
+    auto dtype_ok = [](int t) { return t == MESA_DTYPE_F32 || t == MESA_DTYPE_BF16; };
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "in_dtype %d / out_dtype %d must be MESA_DTYPE_F32 or "
+                    "MESA_DTYPE_BF16", in_dtype, out_dtype);
+    if (B <= 0 || H <= 0 || T < 0 || d <= 0)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "sizes must be positive, T >= 0 (B=%d H=%d T=%d d=%d)", B, H, T, d);
+    if (width < 1 || width > 8) return fail(MESA_ERR_INVALID_ARGUMENT, "width=%d outside [1, 8]", width);
+    if (!conv_w || (T > 0 && (!x || !y)))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "conv_w, and x and y when T > 0, must be non-null");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(hist, 16) || !aligned(hist_out, 16) ||
+        !aligned(conv_w, 16))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "misaligned pointer (16 B for every tensor)");
+    if (y && y == x) return fail(MESA_ERR_INVALID_ARGUMENT, "y must not alias x");
+    if (hist_out && (hist_out == hist || hist_out == x))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "hist_out must not alias hist or x");
+    if (!supported_d(d)) return fail(MESA_ERR_UNSUPPORTED, "d=%d not built (16, 32, 64, 128)", d);
+    if (width > mesa::kQkPreMaxWidth)
+        return fail(MESA_ERR_UNSUPPORTED, "width=%d not built (at most %d)", width, mesa::kQkPreMaxWidth);
+    const int segs = (T + mesa::kQkPreSegment - 1) / mesa::kQkPreSegment;
+    const long n_segs = (long)B * H * segs;
+    const long n_hist = (width > 1 && hist_out) ? (long)B * H * (width - 1) * d : 0;
+    if (n_segs * d > 0x7fffffffL * 256L || n_hist > 0x7fffffffL * 256L)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "grid too large (B*H=%ld)", (long)B * H);
+    if (n_segs == 0 && n_hist == 0) return MESA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mesa::QkPreArgs a{x, conv_w, width, hist, n_hist ? hist_out : nullptr, H, T, segs, n_segs, n_hist, d,
+                      in_dtype == MESA_DTYPE_BF16, out_dtype == MESA_DTYPE_BF16, y};
+    hipError_t e = timed_launch(MESA_KERNEL_QK_PREPROCESS, s, [&] { return mesa::launch_qk_preprocess(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "q/k pre-processing kernel launch");
+    return MESA_OK;
+}
+
 mesa_status mesa_profile_enable(int on) {
     std::lock_guard<std::mutex> g(g_prof_mu);
     g_prof_on = on != 0;
@@ -286,6 +322,7 @@ const char* mesa_kernel_name(int kernel_id) {
         case MESA_KERNEL_CHUNK_STATES: return "chunk_states_kernel";
         case MESA_KERNEL_CG_OUTPUT: return "cg_output_kernel";
         case MESA_KERNEL_DECODE: return "decode_kernel";
+        case MESA_KERNEL_QK_PREPROCESS: return "qk_preprocess_kernel";
     }
     return "unknown";
 }

@@ -29,7 +29,22 @@ struct DecodeArgs {
 };
 
 hipError_t launch_chunk_states(const ChunkStatesArgs& a, hipStream_t s);
+struct QkPreArgs {
+    const void* x; const float* w; int W; const void* hist; void* hist_out;
+    int H; int T;
+    int segs_per_bh; long n_segs;   // token segments of the main kernel (B * H * segs_per_bh)
+    long n_hist;                    // elements of hist_out (B * H * (W - 1) * d), when it is set
+    int d; int in_bf16; int out_bf16;
+    void* y;
+};
+#ifndef MESA_QK_PRE_SEGMENT
+#define MESA_QK_PRE_SEGMENT 32
+#endif
+constexpr int kQkPreSegment = MESA_QK_PRE_SEGMENT;   // tokens per thread of the pre-processing kernel
+constexpr int kQkPreMaxWidth = 4;   // widest convolution window the kernel is built for
+
 hipError_t launch_cg_output(const CgOutputArgs& a, hipStream_t s);
+hipError_t launch_qk_preprocess(const QkPreArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace mesa

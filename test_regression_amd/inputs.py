@@ -181,3 +181,18 @@ def decode_queries_windowed(w: Workload, steps: int, window: int, N: int = None,
     for j in range(window):
         s += z[j:j + steps]
     return (s / np.linalg.norm(s, axis=-1, keepdims=True)).astype(np.float32)
+
+
+def preprocess_inputs(B: int, H: int, T: int, d: int, W: int, dtype: str, seed: int, with_hist: bool = False):
+    """Raw (not yet normalised) query or key rows for the pre-processing step.
+
+    x [B,H,T,d]: N(0, 1) rows, each scaled by a factor drawn from U(0.5, 2) so
+    that row norms differ; conv_w [H,W,d] float32 ~ N(0, 1/W); hist
+    [B,H,W-1,d] N(0, 1) rows (or None).  x and hist in the storage dtype.
+    Draw order: x, row scales, conv_w, hist.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, H, T, d)) * rng.uniform(0.5, 2.0, (B, H, T, 1))
+    w = (rng.standard_normal((H, W, d)) / np.sqrt(W)).astype(np.float32)
+    hist = rng.standard_normal((B, H, W - 1, d)) if with_hist else None
+    return dict(x=_store(x, dtype), w=w, hist=None if hist is None else _store(hist, dtype))

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libmesa.so")
 
 MESA_OK, MESA_ERR_INVALID_ARGUMENT, MESA_ERR_UNSUPPORTED, MESA_ERR_WORKSPACE_TOO_SMALL, MESA_ERR_HIP = range(5)
 MESA_DTYPE_F32, MESA_DTYPE_BF16 = 0, 1
-KERNEL_CHUNK_STATES, KERNEL_CG_OUTPUT, KERNEL_DECODE = 0, 1, 2
+KERNEL_CHUNK_STATES, KERNEL_CG_OUTPUT, KERNEL_DECODE, KERNEL_QK_PREPROCESS = 0, 1, 2, 3
 MESA_WARM_COLD, MESA_WARM_PREVIOUS, MESA_WARM_PROJECTED = 0, 1, 2
 
 # Every symbol include/mesa.h declares, with its ctypes signature.
@@ -31,6 +31,7 @@ SIGNATURES = {
                           _P, _P, _P], _I),
     "mesa_decode_step_warm": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                _P, _P, _P], _I),
+    "mesa_qk_preprocess": ([_P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
     "mesa_profile_enable": ([_I], _I),
     "mesa_profile_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "mesa_profile_reset": ([], _I),
@@ -215,6 +216,37 @@ def mesa_decode_step_warm(q, k, v, gamma, lam, state_H, state_G, state_x, max_it
                                      _stream(stream))
     _check(st, "mesa_decode_step_warm")
     return out, iters
+
+
+def mesa_qk_preprocess(x, conv_w, hist=None, *, out_dtype=None, out=None, return_hist=False,
+                       hist_out=None, stream=None):
+    """Causal convolution of width W over tokens + L2 normalisation (see include/mesa.h).
+
+    x: [B,H,T,d] float32 or bfloat16; conv_w: [H,W,d] float32; hist: [B,H,W-1,d]
+    in x's dtype or None.  Returns y (out_dtype, default x's dtype), and with
+    return_hist also hist_out, the last W-1 input rows for the next piece.
+    """
+    import torch
+    B, H, T, d = x.shape
+    W = conv_w.shape[1]
+    dev = x.device
+    _need(x, "x", None, dev)
+    _need(conv_w, "conv_w", torch.float32, dev)
+    if tuple(conv_w.shape) != (H, W, d):
+        raise ValueError("conv_w must be [H, W, d]")
+    if hist is not None:
+        _need(hist, "hist", x.dtype, dev)
+        if tuple(hist.shape) != (B, H, W - 1, d):
+            raise ValueError("hist must be [B, H, W-1, d]")
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, T, d), dtype=out_dtype, device=dev)
+    if return_hist and hist_out is None:
+        hist_out = torch.empty((B, H, W - 1, d), dtype=x.dtype, device=dev)
+    st = lib().mesa_qk_preprocess(_ptr(x), _qkv_dtype(x), _ptr(conv_w), W, _ptr(hist), _ptr(hist_out),
+                                  B, H, T, d, _ptr(out), _qkv_dtype(out), _stream(stream))
+    _check(st, "mesa_qk_preprocess")
+    return (out, hist_out) if return_hist else out
 
 
 def profile_enable(on: bool = True):

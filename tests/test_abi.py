@@ -168,6 +168,45 @@ def test_warm_decode_rejects_bad_arguments(kw, status, needle):
     assert needle in msg
 
 
+def pre(**kw):
+    a = dict(x=FAKE, dt=0, w=FAKE, W=4, hist=None, hist_out=None, B=2, H=2, T=10, d=64, y=FAKE + 4096,
+             odt=0, stream=None)
+    a.update(kw)
+    L = mesa.lib()
+    st = L.mesa_qk_preprocess(a["x"], a["dt"], a["w"], a["W"], a["hist"], a["hist_out"], a["B"], a["H"], a["T"],
+                              a["d"], a["y"], a["odt"], a["stream"])
+    return st, L.mesa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(w=None), INVALID, "conv_w"),
+    (dict(x=None), INVALID, "non-null"),
+    (dict(y=None), INVALID, "non-null"),
+    (dict(W=0), INVALID, "width"),
+    (dict(W=9), INVALID, "width"),
+    (dict(dt=2), INVALID, "dtype"),
+    (dict(odt=-1), INVALID, "dtype"),
+    (dict(B=0), INVALID, "positive"),
+    (dict(T=-1), INVALID, "T >= 0"),
+    (dict(x=FAKE + 8), INVALID, "misaligned"),
+    (dict(hist=FAKE + 4), INVALID, "misaligned"),
+    (dict(y=FAKE), INVALID, "alias"),
+    (dict(hist=FAKE + 8192, hist_out=FAKE + 8192), INVALID, "alias"),
+    (dict(d=48), UNSUPPORTED, "d=48"),
+    (dict(W=5), UNSUPPORTED, "width=5"),
+])
+def test_preprocess_rejects_bad_arguments(kw, status, needle):
+    st, msg = pre(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_preprocess_empty_piece_is_a_no_op():
+    # T = 0 with no history to carry launches nothing; x and y may be NULL
+    st, msg = pre(x=None, y=None, T=0)
+    assert st == 0, msg
+
+
 def test_probe_argument_validation():
     L = mesa.lib()
     assert L.mesa_probe_mfma_f32(0, 10, FAKE, None) == INVALID
