@@ -29,10 +29,11 @@ constexpr int kPreSegment = kQkPreSegment;   // tokens per thread
 #endif
 constexpr int kPreUnroll = MESA_QK_PRE_UNROLL;   // tokens loaded together
 
-// float32 -> bfloat16 bit pattern, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two float32 -> packed bfloat16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
 }
 
 // F consecutive values of one row, as float.
@@ -64,7 +65,7 @@ template <int F>
 __device__ __forceinline__ void storev(bf16_t* p, const Vec<F>& a) {
     uint32_t w[F / 2];
 #pragma unroll
-    for (int i = 0; i < F / 2; ++i) w[i] = bf16_rne(a.v[2 * i]) | (bf16_rne(a.v[2 * i + 1]) << 16);
+    for (int i = 0; i < F / 2; ++i) w[i] = bf16_pack_rne(a.v[2 * i], a.v[2 * i + 1]);
     if constexpr (F == 8) *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
     else *reinterpret_cast<uint2*>(p) = uint2{w[0], w[1]};
 }
