@@ -164,7 +164,7 @@ def dynamic(torch, mesa, inputs, dev):
             "cg_output_kernel_ms": round(k2_ms, 4)}
 
 
-def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
+def decode(torch, mesa, inputs, dev, steps=1024, warmup=8, warm_start=True):
     """1024 decode steps over 256 x 16 heads; states built on the device from
     seeded 4096-token prefixes by the forward path with zero CG iterations.
     The cold-start run is the measured line; the same steps are then run
@@ -243,7 +243,7 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
     q4 /= q4.norm(dim=-1, keepdim=True)
     del z
     warm = {}
-    for qname, qs in (("iid", q), ("window4", q4)):
+    for qname, qs in ((("iid", q), ("window4", q4)) if warm_start else ()):
         warm[qname] = {}
         for mname, mode in (("cold", None), ("previous", mesa.MESA_WARM_PREVIOUS),
                             ("projected", mesa.MESA_WARM_PROJECTED)):
@@ -255,7 +255,8 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8):
             warm[qname][mname] = {"iters_mean": round(float(itf_m.mean()), 3),
                                   "ms_per_step": round(1e3 * el_m / steps, 4),
                                   "head_steps_per_s": round(steps * nh / el_m, 1)}
-    res["warm_start"] = warm
+    if warm_start:
+        res["warm_start"] = warm
     del q, q4, k, v, ga
     return res
 
@@ -370,6 +371,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the dynamic-stopping and decode measurements")
+    ap.add_argument("--decode-steps", type=int, default=1024, help="timed decode steps (1024 is the workload)")
+    ap.add_argument("--no-warm-start", action="store_true", help="skip the warm-started decode runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -406,7 +409,8 @@ def main():
     if not args.no_extra:
         extra["dynamic"] = dynamic(torch, mesa, inputs, dev)
         torch.cuda.empty_cache()
-        extra["decode"] = decode(torch, mesa, inputs, dev)
+        extra["decode"] = decode(torch, mesa, inputs, dev, steps=args.decode_steps,
+                                 warm_start=not args.no_warm_start)
         torch.cuda.empty_cache()
         extra["qk_preprocess"] = qk_preprocess(torch, mesa, inputs, dev)
         torch.cuda.empty_cache()

@@ -26,9 +26,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CG_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/mesa_device.h"]
 
 
-def cg_source_hash() -> str:
+def cg_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in CG_SOURCES:
+    for p in sources or CG_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -91,7 +91,8 @@ def cmd_traffic(a):
     fb = statistics.median(f_k) * 1024 * f_scale
     wb = statistics.median(w_k) * 1024 * w_scale
     print(json.dumps({
-        "kernel": a.kernel, "command": a.command, "kernel_source_hash": cg_source_hash(),
+        "kernel": a.kernel, "command": a.command, "kernel_source_hash": cg_source_hash(a.sources),
+        "sources": a.sources or CG_SOURCES,
         "fetch_kib_per_dispatch": statistics.median(f_k), "write_kib_per_dispatch": statistics.median(w_k),
         "copy_probe_bytes": a.copy_bytes, "copy_probe_gib": copy_gib,
         "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
@@ -114,6 +115,8 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--kernel", required=True)
     t.add_argument("--command", default="")
+    t.add_argument("--sources", nargs="*", default=None,
+                   help="repository-relative sources whose hash identifies the kernel (default: the CG kernel's)")
     a = ap.parse_args(argv)
     {"stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
 
