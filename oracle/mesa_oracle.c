@@ -375,5 +375,119 @@ int oracle_qk_preprocess(const double *x, const double *w, int W, const double *
     return 0;
 }
 
+/*
+ * Backward pass of the layer for a loss L with dL/do_t = gout_t.  The page
+ * says the layer trains in parallel but gives no gradient (section "A Camada
+ * Mesa", bullet "Paralelizacao").  Reading: differentiate o_t = G_t A_t^{-1}
+ * q_t (A_t = H_t + Lambda) implicitly, evaluated at the CG solutions, with
+ * the adjoint solve done by the same k-step CG:
+ *   x_t  = CG(A_t, q_t)                (the forward's solution)
+ *   bx_t = G_t^T gout_t,   z_t = CG(A_t, bx_t)
+ *   dL/dq_t      = z_t
+ *   dL/dG_t      = gout_t x_t^T,      dL/dH_t = -z_t x_t^T
+ *   dL/dlambda   = -sum_t z_t (.) x_t            (summed over the batch)
+ *   dL/dv_i      = sum_{t>=i} zeta_ti (x_t . k_i) gout_t
+ *   dL/dk_i      = sum_{t>=i} zeta_ti [(gout_t . v_i) x_t - (x_t . k_i) z_t - (z_t . k_i) x_t]
+ *   dL/dln gamma_s = sum_{t>=s} (beta_t - a_t), with
+ *     beta_t = gout_t . (G_t x_t) - z_t . (H_t x_t)
+ *     a_i    = (v_i . dL/dv_i + k_i . dL/dk_i) / 2
+ *   (the sum over pairs i < s <= t of zeta_ti (k_i . x_t)[(gout_t . v_i) - (z_t . k_i)],
+ *   split into its query-side and key-side totals), and dL/dgamma_s =
+ *   dL/dln gamma_s / gamma_s.  The key-side sums run backwards over t with the
+ *   states P_gx = sum_{t>=i} zeta_ti gout_t x_t^T and P_zx = sum zeta_ti z_t x_t^T.
+ * Shapes as oracle_forward; gout [B,H,T,dv]; dq, dk [B,H,T,dk]; dv [B,H,T,dv];
+ * dgamma [B,H,T]; dlam [H,dk]; x_out [B,H,T,dk] and the adjoint solve's
+ * z_iters / z_rho_stop / z_rho_min_prev [B,H,T] may be NULL.
+ */
+int oracle_backward(const double *q, const double *k, const double *v, const double *gamma,
+                    const double *lam, const double *gout, int B, int H, int T, int dk, int dv,
+                    int max_iters, double tol, double *x_out, double *dq, double *dk_out,
+                    double *dv_out, double *dgamma, double *dlam, int32_t *z_iters,
+                    double *z_rho_stop, double *z_rho_min_prev)
+{
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || max_iters < 0 || !(tol >= 0.0))
+        return -1;
+    double *part = calloc((size_t)B * H * dk + 1, sizeof(double));   /* per-(b,h) dlambda */
+    if (!part) return -1;
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long bh = 0; bh < (long)B * H; ++bh) {
+        int h = (int)(bh % H);
+        const double *lh = lam + (size_t)h * dk;
+        double *Hs = calloc((size_t)dk * dk, sizeof(double));
+        double *Gs = calloc((size_t)dv * dk, sizeof(double));
+        double *X = malloc(sizeof(double) * ((size_t)T * dk + 1));
+        double *Z = malloc(sizeof(double) * ((size_t)T * dk + 1));
+        double *beta = malloc(sizeof(double) * ((size_t)T + 1));
+        double *o = malloc(sizeof(double) * dv);
+        double *bx = malloc(sizeof(double) * dk);
+        double *c = malloc(sizeof(double) * dk);
+        double *scratch = malloc(sizeof(double) * 3 * dk);
+        double *Pgx = calloc((size_t)dv * dk, sizeof(double));
+        double *Pzx = calloc((size_t)dk * dk, sizeof(double));
+        if (!Hs || !Gs || !X || !Z || !beta || !o || !bx || !c || !scratch || !Pgx || !Pzx) {
+            bad = 1;
+        } else {
+            /* forward sweep: states, x_t, the adjoint solve z_t, beta_t, dlambda */
+            for (int t = 0; t < T; ++t) {
+                size_t tok = (size_t)bh * T + t;
+                const double *kt = k + tok * dk, *vt = v + tok * dv, *gt = gout + tok * dv;
+                decay_rank1(dk, dk, Hs, gamma[tok], kt, kt);
+                decay_rank1(dv, dk, Gs, gamma[tok], vt, kt);
+                double *xt = X + (size_t)t * dk, *zt = Z + (size_t)t * dk;
+                oracle_cg_solve(dk, Hs, lh, q + tok * dk, max_iters, tol, xt, scratch, NULL, NULL, NULL);
+                matvec(dv, dk, Gs, xt, o);
+                for (int f = 0; f < dk; ++f) {
+                    double s = 0.0;
+                    for (int i = 0; i < dv; ++i) s += Gs[(size_t)i * dk + f] * gt[i];
+                    bx[f] = s;
+                }
+                int why = 0;
+                double rs = 0.0, rm = 0.0;
+                int it = oracle_cg_solve(dk, Hs, lh, bx, max_iters, tol, zt, scratch, &why, &rs, &rm);
+                if (z_iters) z_iters[tok] = it;
+                if (z_rho_stop) z_rho_stop[tok] = rs;
+                if (z_rho_min_prev) z_rho_min_prev[tok] = rm;
+                matvec(dk, dk, Hs, xt, c);
+                beta[t] = dot(dv, gt, o) - dot(dk, zt, c);
+                for (int f = 0; f < dk; ++f) part[(size_t)bh * dk + f] -= zt[f] * xt[f];
+                if (x_out) memcpy(x_out + tok * dk, xt, sizeof(double) * dk);
+                memcpy(dq + tok * dk, zt, sizeof(double) * dk);
+            }
+            /* reverse sweep: key-side sums, then the log-gate gradient */
+            double acc = 0.0;
+            for (int t = T - 1; t >= 0; --t) {
+                size_t tok = (size_t)bh * T + t;
+                const double *kt = k + tok * dk, *vt = v + tok * dv, *gt = gout + tok * dv;
+                const double *xt = X + (size_t)t * dk, *zt = Z + (size_t)t * dk;
+                double gnext = (t + 1 < T) ? gamma[tok + 1] : 0.0;
+                decay_rank1(dv, dk, Pgx, gnext, gt, xt);
+                decay_rank1(dk, dk, Pzx, gnext, zt, xt);
+                double *dvt = dv_out + tok * dv, *dkt = dk_out + tok * dk;
+                matvec(dv, dk, Pgx, kt, dvt);
+                for (int f = 0; f < dk; ++f) {
+                    double s = 0.0;
+                    for (int i = 0; i < dv; ++i) s += Pgx[(size_t)i * dk + f] * vt[i];
+                    for (int e = 0; e < dk; ++e)
+                        s -= (Pzx[(size_t)f * dk + e] + Pzx[(size_t)e * dk + f]) * kt[e];
+                    dkt[f] = s;
+                }
+                double a = 0.5 * (dot(dv, vt, dvt) + dot(dk, kt, dkt));
+                acc += beta[t] - a;
+                dgamma[tok] = acc / gamma[tok];
+            }
+        }
+        free(Hs); free(Gs); free(X); free(Z); free(beta); free(o); free(bx); free(c);
+        free(scratch); free(Pgx); free(Pzx);
+    }
+    if (!bad) {
+        for (long i = 0; i < (long)H * dk; ++i) dlam[i] = 0.0;
+        for (long bh = 0; bh < (long)B * H; ++bh)   /* fixed order over the batch */
+            for (int f = 0; f < dk; ++f) dlam[(bh % H) * dk + f] += part[(size_t)bh * dk + f];
+    }
+    free(part);
+    return bad ? -1 : 0;
+}
+
 /* Threads an OpenMP parallel region of this library would use. */
 int oracle_max_threads(void) { return omp_get_max_threads(); }

@@ -573,3 +573,67 @@ def test_preprocess_width_one_is_normalisation():
     n = np.linalg.norm(x, axis=-1, keepdims=True)
     np.testing.assert_allclose(y, np.where(n > 0, x / np.where(n > 0, n, 1), 0), rtol=1e-15)
     assert not y[0, 1, 4].any()
+
+
+# --------------------------------------------------------------------------
+# Backward pass (the page says the layer trains in parallel but gives no
+# gradient; section "A Camada Mesa", bullet "Paralelizacao").  The oracle
+# differentiates o_t = G_t (H_t + Lambda)^{-1} q_t implicitly with a k-step
+# adjoint CG.  B1: with the solves converged, every gradient equals central
+# finite differences of the oracle's own forward (a different route: no
+# adjoint, no reverse sums).  B2: gamma at the first token has no effect, so
+# its gradient is zero.  B3: the adjoint solve is the k-step CG of G_t^T g_t.
+# --------------------------------------------------------------------------
+def _loss(q, k, v, g, lam, gout, cap, tol):
+    return float(np.sum(oracle.forward(q, k, v, g, lam, cap, tol)["out"] * gout))
+
+
+def test_backward_matches_finite_differences():
+    rng = np.random.default_rng(41)
+    B, H, T, dk, dv = 1, 2, 6, 3, 2
+    q, k, v, g, lam = rand_problem(rng, T, dk, dv, glo=0.7)
+    q, k, v, g = (np.repeat(a, H, axis=1) + rng.standard_normal((B, H) + a.shape[2:]) * 0.3 for a in (q, k, v, g))
+    g = np.clip(g, 0.5, 1.0)
+    lam = rng.uniform(0.4, 1.5, (H, dk))
+    gout = rng.standard_normal((B, H, T, dv))
+    cap, tol = 4 * dk, 1e-13
+    r = oracle.backward(q, k, v, g, lam, gout, cap, tol)
+    args = dict(q=q, k=k, v=v, g=g, lam=lam)
+    grads = dict(q=r["dq"], k=r["dk"], v=r["dv"], g=r["dgamma"], lam=r["dlam"])
+    for name, a in args.items():
+        fd = np.zeros_like(a)
+        for idx in np.ndindex(a.shape):
+            hstep = 1e-6 * max(1.0, abs(a[idx]))
+            ap, am = a.copy(), a.copy()
+            ap[idx] += hstep
+            am[idx] -= hstep
+            kw_p = dict(args, **{name: ap})
+            kw_m = dict(args, **{name: am})
+            fd[idx] = (_loss(kw_p["q"], kw_p["k"], kw_p["v"], kw_p["g"], kw_p["lam"], gout, cap, tol)
+                       - _loss(kw_m["q"], kw_m["k"], kw_m["v"], kw_m["g"], kw_m["lam"], gout, cap, tol)) / (2 * hstep)
+        if name == "g":
+            fd[:, :, 0] = 0.0       # gamma_1 has no effect
+        err = np.abs(grads[name] - fd).max() / max(np.abs(fd).max(), 1e-12)
+        assert err < 2e-6, (name, err)
+
+
+def test_backward_first_gate_gradient_is_zero_and_adjoint_is_cg():
+    rng = np.random.default_rng(42)
+    B, H, T, dk, dv = 2, 1, 9, 4, 4
+    q, k, v, g, lam = rand_problem(rng, T, dk, dv, glo=0.8)
+    q, k, v, g = (np.concatenate([a, a[:, :, ::-1]], axis=0) for a in (q, k, v, g))
+    gout = rng.standard_normal((B, H, T, dv))
+    cap, tol = 3, 0.0
+    r = oracle.backward(q, k, v, g, lam, gout, cap, tol)
+    assert np.abs(r["dgamma"][:, :, 0]).max() < 1e-10 * np.abs(r["dgamma"]).max()
+    # the adjoint: z_t = 3-step CG on (H_t + Lambda) z = G_t^T gout_t, states from their definition
+    for b in range(B):
+        for t in (0, 4, 8):
+            Hm, Gm = brute_states(k[b, 0], v[b, 0], g[b, 0], t)
+            z, it, *_ = oracle.cg_solve(Hm, lam[0], Gm.T @ gout[b, 0, t], cap, 0.0)
+            assert it == cap
+            np.testing.assert_allclose(r["dq"][b, 0, t], z, rtol=1e-10, atol=1e-12)
+            xs, *_ = oracle.cg_solve(Hm, lam[0], q[b, 0, t], cap, 0.0)
+            np.testing.assert_allclose(r["x"][b, 0, t], xs, rtol=1e-10, atol=1e-12)
+    # dlambda sums -z (.) x over the batch and tokens
+    np.testing.assert_allclose(r["dlam"][0], -np.sum(r["dq"][:, 0] * r["x"][:, 0], axis=(0, 1)), rtol=1e-12)
