@@ -72,7 +72,11 @@ typedef enum {
     MESA_KERNEL_CG_OUTPUT = 1,       /* all CG iterations of a chunk + output contraction */
     MESA_KERNEL_DECODE = 2,          /* one recurrent decode step                        */
     MESA_KERNEL_QK_PREPROCESS = 3,   /* q/k convolution + normalisation                  */
-    MESA_KERNEL_COUNT = 4
+    MESA_KERNEL_BWD_ADJOINT = 4,     /* backward: adjoint CG solve, per-token totals     */
+    MESA_KERNEL_BWD_STATES = 5,      /* backward: reverse chunk states                   */
+    MESA_KERNEL_BWD_KV = 6,          /* backward: key and value gradients                */
+    MESA_KERNEL_BWD_GATE = 7,        /* backward: gate and regulariser gradients         */
+    MESA_KERNEL_COUNT = 8
 } mesa_kernel_id;
 
 /* Library ABI version (MESA_ABI_VERSION of the build). */
@@ -119,6 +123,61 @@ mesa_status mesa_forward(const void *q, const void *k, const void *v, int qkv_dt
                          int max_iters, float tol,
                          float *out, int32_t *iters, float *final_H, float *final_G,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mesa_forward for training: the same computation (without final states),
+ * and also the CG solutions the backward pass needs:
+ *   x_out     [B, H, T, dk]   float32, x_t = the k-step CG solution of
+ *                             (H_t + Lambda) x = q_t (0 when max_iters == 0)
+ */
+mesa_status mesa_forward_train(const void *q, const void *k, const void *v, int qkv_dtype,
+                               const float *gamma, const float *lambda,
+                               int B, int H, int T, int dk, int dv, int chunk,
+                               int max_iters, float tol, float *out, int32_t *iters, float *x_out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace mesa_backward needs: the forward chunk states
+ * (as mesa_forward_workspace_bytes), two d x d reverse states per chunk and
+ * head, two floats per token and d floats per chunk and head.  0 if invalid.
+ */
+size_t mesa_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/*
+ * Backward pass of the layer for a loss L with dL/d(out) = grad_out.  The
+ * page says the layer trains in parallel but gives no gradient (section "A
+ * Camada Mesa", bullet "Paralelizacao").  Reading: o_t = G_t A_t^{-1} q_t
+ * (A_t = H_t + Lambda) is differentiated implicitly at the forward's CG
+ * solution x_t, with the adjoint system solved by the same k-step CG:
+ *   z_t = CG(A_t, G_t^T g_t)                        dL/dq_t = z_t
+ *   dL/dv_i = sum_{t>=i} zeta_ti (x_t . k_i) g_t
+ *   dL/dk_i = sum_{t>=i} zeta_ti [(g_t . v_i) x_t - (x_t . k_i) z_t - (z_t . k_i) x_t]
+ *   dL/dlambda = -sum_{b,t} z_t (.) x_t
+ *   dL/dgamma_s = (1/gamma_s) sum_{t>=s} (beta_t - a_t),
+ *     beta_t = g_t . o_t - z_t . (H_t x_t),  a_i = (v_i . dL/dv_i + k_i . dL/dk_i) / 2
+ * (g_t = grad_out_t).  The adjoint solve stops like the forward's, relative
+ * to |G_t^T g_t|.
+ *
+ *   k         [B, H, T, dk]   qkv_dtype (q itself is not needed)
+ *   v         [B, H, T, dv]   qkv_dtype
+ *   gamma, lambda             as mesa_forward
+ *   x         [B, H, T, dk]   float32, x_out of mesa_forward_train
+ *   out       [B, H, T, dv]   float32, out of the same forward
+ *   grad_out  [B, H, T, dv]   float32
+ *   chunk, max_iters, tol     as mesa_forward (use the forward's values)
+ *   grad_q, grad_k [B, H, T, dk], grad_v [B, H, T, dv], grad_gamma [B, H, T],
+ *   grad_lambda [H, dk]       float32, written (grad_lambda sums the batch)
+ *   z_iters   [B, H, T]       int32 update counts of the adjoint solve, or NULL
+ *   workspace, workspace_bytes  at least mesa_backward_workspace_bytes(...)
+ * Sizes and errors as mesa_forward.  Outputs must not alias inputs.
+ */
+mesa_status mesa_backward(const void *k, const void *v, int qkv_dtype,
+                          const float *gamma, const float *lambda,
+                          const float *x, const float *out, const float *grad_out,
+                          int B, int H, int T, int dk, int dv, int chunk, int max_iters, float tol,
+                          float *grad_q, float *grad_k, float *grad_v, float *grad_gamma,
+                          float *grad_lambda, int32_t *z_iters,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent decode step for N x H independent heads (the "Paralelizacao"

@@ -64,7 +64,7 @@ def _load():
         lib.oracle_decode_step_warm.restype = I
         lib.oracle_qk_preprocess.argtypes = [P, P, I, P, P, I, I, I, I, P]
         lib.oracle_qk_preprocess.restype = I
-        lib.oracle_backward.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P, P, P, P, P, P, P, P, P]
+        lib.oracle_backward.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_backward.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
@@ -228,7 +228,7 @@ def backward(q, k, v, gamma, lam, gout, max_iters, tol=0.0):
     """Gradients of a loss with dL/d(out) = gout through the layer (implicit
     differentiation with a k-step adjoint CG; see oracle_backward in the C file).
 
-    Returns dict(dq, dk, dv, dgamma, dlam, x, z_iters, z_rho_stop, z_rho_min_prev).
+    Returns dict(dq, dk, dv, dgamma, dlam, x, z_iters, z_rho_stop, z_rho_min_prev, z_reason).
     """
     lib = _load()
     q, k, v, gamma, lam, gout = _f64(q), _f64(k), _f64(v), _f64(gamma), _f64(lam), _f64(gout)
@@ -244,10 +244,11 @@ def backward(q, k, v, gamma, lam, gout, max_iters, tol=0.0):
     zi = np.zeros((B, H, T), dtype=np.int32)
     zs = np.zeros((B, H, T))
     zm = np.zeros((B, H, T))
+    zr = np.zeros((B, H, T), dtype=np.int32)
     rc = lib.oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(lam), _ptr(gout), B, H, T, dk, dv,
                              int(max_iters), float(tol), _ptr(x), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
-                             _ptr(dl), _ptr(zi), _ptr(zs), _ptr(zm))
+                             _ptr(dl), _ptr(zi), _ptr(zs), _ptr(zm), _ptr(zr))
     if rc != 0:
         raise ValueError("oracle_backward rejected its arguments")
     return dict(dq=dq, dk=dkk, dv=dvv, dgamma=dg, dlam=dl, x=x, z_iters=zi, z_rho_stop=zs,
-                z_rho_min_prev=zm)
+                z_rho_min_prev=zm, z_reason=zr)

@@ -397,13 +397,13 @@ int oracle_qk_preprocess(const double *x, const double *w, int W, const double *
  *   states P_gx = sum_{t>=i} zeta_ti gout_t x_t^T and P_zx = sum zeta_ti z_t x_t^T.
  * Shapes as oracle_forward; gout [B,H,T,dv]; dq, dk [B,H,T,dk]; dv [B,H,T,dv];
  * dgamma [B,H,T]; dlam [H,dk]; x_out [B,H,T,dk] and the adjoint solve's
- * z_iters / z_rho_stop / z_rho_min_prev [B,H,T] may be NULL.
+ * z_iters / z_rho_stop / z_rho_min_prev / z_reason [B,H,T] may be NULL.
  */
 int oracle_backward(const double *q, const double *k, const double *v, const double *gamma,
                     const double *lam, const double *gout, int B, int H, int T, int dk, int dv,
                     int max_iters, double tol, double *x_out, double *dq, double *dk_out,
                     double *dv_out, double *dgamma, double *dlam, int32_t *z_iters,
-                    double *z_rho_stop, double *z_rho_min_prev)
+                    double *z_rho_stop, double *z_rho_min_prev, int32_t *z_reason)
 {
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || max_iters < 0 || !(tol >= 0.0))
         return -1;
@@ -448,6 +448,7 @@ int oracle_backward(const double *q, const double *k, const double *v, const dou
                 if (z_iters) z_iters[tok] = it;
                 if (z_rho_stop) z_rho_stop[tok] = rs;
                 if (z_rho_min_prev) z_rho_min_prev[tok] = rm;
+                if (z_reason) z_reason[tok] = why;
                 matvec(dk, dk, Hs, xt, c);
                 beta[t] = dot(dv, gt, o) - dot(dk, zt, c);
                 for (int f = 0; f < dk; ++f) part[(size_t)bh * dk + f] -= zt[f] * xt[f];

@@ -1,0 +1,137 @@
+// bwd_states.hip -- the backward's reverse chunk states (gfx950).
+//
+// The backward of the Mesa layer (implicit differentiation of
+// o_t = G_t (H_t + Lambda)^{-1} q_t; the page, section "A Camada Mesa",
+// bullet "Paralelizacao", says the layer trains in parallel but gives no
+// gradient) needs, for every key i, sums over the later tokens t >= i:
+//   sum_t zeta_ti (x_t . k_i) g_t,   sum_t zeta_ti (g_t . v_i) x_t,
+//   sum_t zeta_ti [(x_t . k_i) z_t + (z_t . k_i) x_t].
+// Chunkwise, the tokens after chunk c enter through two d x d states
+//   P^gx_c = sum_{t > e_c} e^{L_t - L_{e_c}} g_t x_t^T,   P^zx_c likewise with z_t,
+// (e_c the chunk's last token, L the prefix sum of ln gamma), which obey,
+// walking the chunks backwards with l the within-chunk prefix sums,
+//   P_{c-1} = e^{l_end} P_c + sum_{t in c} e^{l_t} a_t x_t^T     (a = g or z).
+// This kernel produces P^gx_c and P^zx_c for every chunk (P of the last chunk
+// is zero).  Work split as the forward's chunk-state kernel: one workgroup per
+// (head, {gx, zx}, row block), each wave a 16 x D slab of the running state in
+// MFMA accumulators, the rank-C update a fresh v_mfma_f32_16x16x4_f32 chain.
+#include "mesa_device.h"
+#include "mesa_kernels.h"
+
+namespace mesa {
+
+template <int D, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
+    const float* __restrict__ g, const float* __restrict__ z, const float* __restrict__ x,
+    const float* __restrict__ gamma, int T, int n_chunks, float* __restrict__ Pgx, float* __restrict__ Pzx,
+    long BH) {
+    constexpr int RB = D / (16 * NW);   // row blocks per state
+    constexpr int NT = D / 16;
+    constexpr int PD = lds_pitch(D);
+    constexpr int NTHR = 64 * NW;
+    __shared__ float sA[C * PD];   // g or z rows of the chunk (the state's rows)
+    __shared__ float sX[C * PD];   // x rows of the chunk (the state's columns)
+    __shared__ float sW[C];        // e^{l_t}
+    __shared__ float sGam;         // e^{l_end}
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int n = lane & 15;
+    const int kk = lane >> 4;
+    constexpr int PARTS = 2 * RB;
+    const long bh = blockIdx.x / PARTS;
+    const int part = (int)(blockIdx.x % PARTS);
+    if (bh >= BH) return;   // whole workgroup
+    const int rb = part % RB;
+    const int which = part / RB;   // 0: gx, 1: zx
+    const int m0 = rb * 16 * NW + 16 * w;
+    const float* ah = (which == 0 ? g : z) + (size_t)bh * T * D;
+    const float* xh = x + (size_t)bh * T * D;
+    const float* gh = gamma + (size_t)bh * T;
+    float* Pout = (which == 0 ? Pgx : Pzx) + (size_t)bh * n_chunks * D * D;
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = n_chunks - 1; c >= 0; --c) {
+        const int t0 = c * C;
+        const int valid = min(C, T - t0);
+        for (int e = tid * 4; e < C * D; e += NTHR * 4) {
+            const int i = e / D, f = e % D;
+            f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f}, xv = av;
+            if (i < valid) {
+                av = *reinterpret_cast<const f32x4*>(ah + (size_t)(t0 + i) * D + f);
+                xv = *reinterpret_cast<const f32x4*>(xh + (size_t)(t0 + i) * D + f);
+            }
+            *reinterpret_cast<f32x4*>(&sA[i * PD + f]) = av;
+            *reinterpret_cast<f32x4*>(&sX[i * PD + f]) = xv;
+        }
+        if (w == 0) {
+            const float l = chunk_log_decay(gh + t0, valid, lane);
+            const float lend = __shfl(l, C - 1, 64);
+            if (lane < C) sW[lane] = __expf(l);
+            if (lane == 0) sGam = __expf(lend);
+        }
+        __syncthreads();
+
+        // ---- the state of the tokens after this chunk ----
+        float* dst = Pout + (size_t)c * D * D;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+
+        // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain) ----
+        f32x4 U[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gg = 0; gg < C / 16; ++gg) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int i = 16 * gg + 4 * kk + s;
+                const float a = sA[i * PD + m0 + n] * sW[i];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sX[i * PD + 16 * j + n], U[j]);
+            }
+        }
+        const float G = sGam;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = G * acc[j] + U[j];
+        __syncthreads();
+    }
+}
+
+template <int D, int C>
+static hipError_t launch_t(const BwdStatesArgs& a, hipStream_t s) {
+    constexpr int NW = D >= 64 ? 4 : D / 16;
+    constexpr int RB = D / (16 * NW);
+    const long grid = a.BH * 2 * RB;
+    hipLaunchKernelGGL((bwd_states_kernel<D, C, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a.g, a.z, a.x,
+                       a.gamma, a.T, a.n_chunks, a.Pgx, a.Pzx, a.BH);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dispatch_c(const BwdStatesArgs& a, hipStream_t s) {
+    switch (a.chunk) {
+        case 16: return launch_t<D, 16>(a, s);
+        case 32: return launch_t<D, 32>(a, s);
+        case 64: return launch_t<D, 64>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_states(const BwdStatesArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 16: return dispatch_c<16>(a, s);
+        case 32: return dispatch_c<32>(a, s);
+        case 64: return dispatch_c<64>(a, s);
+        case 128: return dispatch_c<128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mesa

@@ -1,0 +1,347 @@
+// cg_core.h -- the chunk-local CG machinery shared by the forward CG kernel
+// and the backward's adjoint solve (gfx950).
+//
+// MesaNet summary page (gist.science, paper 2506.05233), section "A Camada
+// Mesa": the output is Delta_t = G_t q*_t with q*_t = (H_t + Lambda)^{-1}
+// q_t solved by Conjugate Gradient; bullet "Paralelizacao": CG over all time
+// steps is a gated-linear-attention pass run chunk-parallel on the states.
+// For chunk c (tokens t0..t0+C-1, l_t the within-chunk prefix sum of
+// ln gamma, S^H_c = H_{t0-1}):
+//   H_t p = e^{l_t} S^H_c p + sum_{i=t0..t} e^{l_t - l_i} (k_i . p) k_i
+//
+// Layout (see the kernels for the full story): one workgroup per (head,
+// chunk), wave w owns tokens 16w..16w+15; every product is computed
+// transposed so that a wave's vectors (lane (n, kk) holds features
+// 16j + 4kk + r of token n in block j) are the MFMA B operand and the LDS
+// tiles are the A operand.  Every MFMA chain starts from zero and is only
+// read afterwards.
+#pragma once
+#include "mesa_device.h"
+
+namespace mesa {
+
+
+constexpr int kBlockPitch = 20;   // floats per row of a stored 16x16 state block
+
+template <int D, int C>
+struct alignas(16) CgLds {
+    static constexpr int NW = C / 16;
+    static constexpr int NT = D / 16;
+    static constexpr int NBLK = NT * (NT + 1) / 2;       // upper-triangle blocks
+    static constexpr int HALF = NBLK * 16 * kBlockPitch;  // floats per stored state
+    static constexpr int NSTATE = NW >= 2 ? 2 : 1;
+    static constexpr int PD = lds_pitch(D);
+    static constexpr int PS = lds_pitch_rows(D);
+    static constexpr int PT = lds_pitch_rows(C);
+    static constexpr int REGION = NSTATE * HALF > D * PS ? NSTATE * HALF : D * PS;
+    float R[REGION];          // CG: stored S^H_c [, S_mid];  output: G_c full [D][PS]
+    float KV[C * PD];         // K_c rows [token][feature]
+    float KT[D * PT];         // K_c^T, later V_c^T   [feature][token]
+    float L[C];               // l_i
+    float Lam[D];
+};
+
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Offset (floats) of stored block (a, b), a <= b, of an NT x NT block triangle.
+template <int NT>
+__host__ __device__ constexpr int blk(int a, int b) {
+    return (a * NT - a * (a - 1) / 2 + (b - a)) * 16 * kBlockPitch;
+}
+
+// Y[j]   += S[16j + m][:] . Z^T[:][n]                 (S symmetric, upper block triangle stored)
+// Sc[ib] += K[16(KB0 + ib) + m][:] . Z^T[:][n]        (NB score blocks)
+// Z: the wave's vectors in registers (lane (n, kk), block g: features 16g + 4kk + s of token n).
+// S[16j + m][16g + 4kk + s] is stored block (j, g) read along row m when j < g,
+// else block (g, j) read down column m (S symmetric).
+template <int D, int NB, int KB0>
+__device__ __forceinline__ void contract_state_scores(const f32x4 (&Z)[D / 16], const float* Sst, const float* Kr,
+                                                      int m, int kk, f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB]) {
+    constexpr int NT = D / 16;
+    constexpr int PD = lds_pitch(D);
+    f32x4 bs[2][NT], bk[2][NB];
+    auto load = [&](int g, int buf) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            if (g > j) {
+                bs[buf][j] = lds4(Sst + blk<NT>(j, g) + m * kBlockPitch + 4 * kk);
+            } else {
+                const float* col = Sst + blk<NT>(g, j) + (4 * kk) * kBlockPitch + m;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) bs[buf][j][s] = col[s * kBlockPitch];
+            }
+        }
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) bk[buf][ib] = lds4(Kr + (16 * (KB0 + ib) + m) * PD + 16 * g + 4 * kk);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        const int cur = g & 1;
+        if (g + 1 < NT) load(g + 1, cur ^ 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) Y[j] = mfma4(bs[cur][j][s], Z[g][s], Y[j]);
+#pragma unroll
+            for (int ib = 0; ib < NB; ++ib) Sc[ib] = mfma4(bk[cur][ib][s], Z[g][s], Sc[ib]);
+        }
+    }
+}
+
+// Y[j] += Bs[16j + m][:] . Z^T[:][n]  (Bs full, row-major, pitch lds_pitch_rows(D)), when STATE;
+// Sc[ib] += K[16ib + m][:] . Z^T[:][n] for ib < NB (K rows, pitch lds_pitch(D)).
+template <int D, int NB, bool STATE>
+__device__ __forceinline__ void contract_rows(const f32x4 (&Z)[D / 16], const float* Bs, const float* Bk, int m,
+                                              int kk, f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB > 0 ? NB : 1]) {
+    constexpr int NT = D / 16;
+    constexpr int PD = lds_pitch(D);
+    constexpr int PS = lds_pitch_rows(D);
+    constexpr int NBB = NB > 0 ? NB : 1;
+    const float* bsa = STATE ? Bs + m * PS + 4 * kk : nullptr;
+    const float* bka = NB > 0 ? Bk + m * PD + 4 * kk : nullptr;
+    f32x4 bs[2][STATE ? NT : 1], bk[2][NBB];
+    auto load = [&](int g, int buf) {
+        if constexpr (STATE) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) bs[buf][j] = lds4(bsa + 16 * j * PS + 16 * g);
+        }
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) bk[buf][ib] = lds4(bka + 16 * ib * PD + 16 * g);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        const int cur = g & 1;
+        if (g + 1 < NT) load(g + 1, cur ^ 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if constexpr (STATE) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) Y[j] = mfma4(bs[cur][j][s], Z[g][s], Y[j]);
+            }
+#pragma unroll
+            for (int ib = 0; ib < NB; ++ib) Sc[ib] = mfma4(bk[cur][ib][s], Z[g][s], Sc[ib]);
+        }
+    }
+}
+
+// Y[j] += sum_{ib < NB} sum_i BT[16j + m][16(KB0 + ib) + i] * W[ib][i]
+// BT: K^T or V^T tile [feature][token] (pitch lds_pitch_rows(C));
+// W: decayed score blocks in registers (lane (n, kk): keys 16(KB0 + ib) + 4kk + s of token n).
+template <int D, int C, int NB, int KB0>
+__device__ __forceinline__ void contract_intra(const f32x4 (&W)[NB], const float* BT, int m, int kk,
+                                               f32x4 (&Y)[D / 16]) {
+    constexpr int NT = D / 16;
+    constexpr int PT = lds_pitch_rows(C);
+    const float* base = BT + m * PT + 16 * KB0 + 4 * kk;
+    f32x4 a[2][NT];
+    auto load = [&](int ib, int buf) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) a[buf][j] = lds4(base + 16 * j * PT + 16 * ib);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) {
+        const int cur = ib & 1;
+        if (ib + 1 < NB) load(ib + 1, cur ^ 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) Y[j] = mfma4(a[cur][j][s], W[ib][s], Y[j]);
+    }
+}
+
+// S_mid (upper block triangle) = e^{l_{h-1}} S0 + sum_{i<h} e^{l_{h-1}-l_i} k_i k_i^T,
+// blocks distributed over the NW waves.  Written to S1.
+template <int D, int C>
+__device__ __forceinline__ void form_mid_state(CgLds<D, C>& L, int w, int n, int kk) {
+    constexpr int NT = D / 16;
+    constexpr int NW = C / 16;
+    constexpr int H = C / 2;
+    constexpr int PD = lds_pitch(D);
+    const float* S0 = L.R;
+    float* S1 = L.R + CgLds<D, C>::HALF;
+    const float lh = L.L[H - 1];
+    const float Gh = __expf(lh);
+    float wk[H / 4];
+#pragma unroll
+    for (int st = 0; st < H / 4; ++st) wk[st] = __expf(lh - L.L[4 * st + kk]);
+    int q = 0;
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+#pragma unroll
+        for (int b = a; b < NT; ++b, ++q) {
+            if (q % NW != w) continue;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < H / 4; ++st) {
+                const int i = 4 * st + kk;
+                acc = mfma4(wk[st] * L.KV[i * PD + 16 * a + n], L.KV[i * PD + 16 * b + n], acc);
+            }
+            const float* s0 = S0 + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n;
+            float* s1 = S1 + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s1[r * kBlockPitch] = Gh * s0[r * kBlockPitch] + acc[r];
+        }
+    }
+}
+
+
+// Per-wave constants of wave W in chunk-local CG work.
+template <int D, int C, int W>
+struct CgWave {
+    static constexpr int NT = D / 16;
+    static constexpr int NW = C / 16;
+    static constexpr int SUB = (NW >= 2 && W >= NW / 2) ? 1 : 0;   // which stored state
+    static constexpr int KB0 = SUB ? NW / 2 : 0;                    // first key block of the sub-chunk
+    static constexpr int NB = W - KB0 + 1;                          // causal key blocks in the CG
+    static constexpr int NBO = W + 1;                               // causal key blocks over the chunk
+    int n, kk, tr;        // lane's token (B column), k-slot group, chunk token
+    float eL, eLo;        // e^{l_t - l_base} (sub-chunk state), e^{l_t} (chunk-start state)
+    float dec[NBO][4];    // e^{l_t - l_i} for key i = 16ib + 4kk + r <= t, else 0
+    const float* Sst;     // the stored state the CG uses
+
+    __device__ __forceinline__ CgWave(const CgLds<D, C>& L, int lane) {
+        n = lane & 15;
+        kk = lane >> 4;
+        tr = 16 * W + n;
+        Sst = L.R + SUB * CgLds<D, C>::HALF;
+        const float lbase = SUB ? L.L[16 * KB0 - 1] : 0.f;   // l at the end of the first half
+        eL = __expf(L.L[tr] - lbase);
+        eLo = __expf(L.L[tr]);
+#pragma unroll
+        for (int ib = 0; ib < NBO; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ib + 4 * kk + r;
+                dec[ib][r] = (i <= tr) ? __expf(L.L[tr] - L.L[i]) : 0.f;
+            }
+    }
+};
+
+// Dot product of each token's vectors held in B layout (the four k-slot lanes
+// of a token end with the same bits).
+template <int NT>
+__device__ __forceinline__ float token_dot(const f32x4 (&A)[NT], const f32x4 (&B)[NT]) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += A[j][r] * B[j][r];
+    return kslot_sum(s);
+}
+
+// Y = H_t P over the wave's tokens (the stored state plus the sub-chunk's
+// causal keys), plus diag(lambda) P when LAMBDA: one CG matvec.
+template <int D, int C, int W, bool LAMBDA>
+__device__ __forceinline__ void wave_matvec(const CgLds<D, C>& L, const CgWave<D, C, W>& cw,
+                                            const f32x4 (&P)[D / 16], f32x4 (&Y)[D / 16]) {
+    using CW = CgWave<D, C, W>;
+    constexpr int NT = D / 16;
+    f32x4 YS[NT], YI[NT], Sc[CW::NB];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) YS[j] = YI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ib = 0; ib < CW::NB; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+    contract_state_scores<D, CW::NB, CW::KB0>(P, cw.Sst, L.KV, cw.n, cw.kk, YS, Sc);
+    f32x4 Wt[CW::NB];
+#pragma unroll
+    for (int ib = 0; ib < CW::NB; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Wt[ib][r] = Sc[ib][r] * cw.dec[CW::KB0 + ib][r];
+    contract_intra<D, C, CW::NB, CW::KB0>(Wt, L.KT, cw.n, cw.kk, YI);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        if constexpr (LAMBDA) {
+            const f32x4 lam = lds4(&L.Lam[16 * j + 4 * cw.kk]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[j][r] = cw.eL * YS[j][r] + YI[j][r] + lam[r] * P[j][r];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[j][r] = cw.eL * YS[j][r] + YI[j][r];
+        }
+    }
+}
+
+// CG on (H_t + Lambda) x = b for the wave's 16 tokens from x = 0.  R holds b
+// on entry (B layout); X receives the solution.  Stops before an update when
+// |r| / |b| < tol (tested as r.r < (tol |b|)^2), or on r.r == 0 or
+// p.Ap <= 0; b == 0 gives x = 0 and no update.  Returns the lane's token's
+// update count.
+template <int D, int C, int W>
+__device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<D, C, W>& cw, f32x4 (&R)[D / 16],
+                                             f32x4 (&X)[D / 16], int max_iters, float tol) {
+    constexpr int NT = D / 16;
+    f32x4 P[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        P[j] = R[j];
+        X[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float rr = token_dot<NT>(R, R);
+    const float tq = tol * sqrtf(rr);
+    const float stop_rr = tq * tq;
+    bool done = !(rr > 0.f);   // b == 0 (or a padded token): x = 0, 0 iterations
+    int it = 0;
+    for (int itn = 0; itn < max_iters; ++itn) {
+        if (!done && (rr < stop_rr || rr == 0.f)) done = true;
+        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        f32x4 Y[NT];
+        wave_matvec<D, C, W, true>(L, cw, P, Y);
+        const float pap = token_dot<NT>(P, Y);
+        const bool act = !done && (pap > 0.f);
+        if (!done && !act) done = true;   // breakdown guard
+        const float alpha = act ? rr / pap : 0.f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                X[j][r] += alpha * P[j][r];
+                R[j][r] -= alpha * Y[j][r];
+            }
+        const float rrn = token_dot<NT>(R, R);
+        if (act) {
+            const float beta = rrn / rr;
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) P[j][r] = R[j][r] + beta * P[j][r];
+            rr = rrn;
+            it += 1;
+        }
+    }
+    return it;
+}
+
+// Stage the packed upper block triangle of S^H (blocks (a, b), a <= b, in
+// row-major block order, each block row-major) into L.R; workgroup-wide.
+template <int D, int C>
+__device__ __forceinline__ void stage_packed_state(CgLds<D, C>& L, const float* __restrict__ SHc, int tid,
+                                                   int nthr) {
+    constexpr int HPACK = D * (D + 16) / 2;
+    for (int e = tid * 4; e < HPACK; e += nthr * 4)
+        *reinterpret_cast<f32x4*>(&L.R[(e / 256) * 16 * kBlockPitch + ((e % 256) / 16) * kBlockPitch + e % 16]) =
+            *reinterpret_cast<const f32x4*>(SHc + e);
+}
+
+// Stage a chunk's rows of a [*, D] tensor as rows (pitch lds_pitch(D)) and/or
+// transposed (pitch lds_pitch_rows(C)); rows past `valid` are zero.
+template <int D, int C, bool ROWS, bool TRANSPOSED, typename In>
+__device__ __forceinline__ void stage_chunk_rows(float* rows, float* tr, const In* __restrict__ src, int valid,
+                                                 int tid, int nthr) {
+    constexpr int PD = lds_pitch(D);
+    constexpr int PT = lds_pitch_rows(C);
+    for (int e = tid * 4; e < C * D; e += nthr * 4) {
+        const int i = e / D, f = e % D;
+        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (i < valid) x = load4(src + (size_t)i * D + f);
+        if constexpr (ROWS) *reinterpret_cast<f32x4*>(&rows[i * PD + f]) = x;
+        if constexpr (TRANSPOSED) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) tr[(f + u) * PT + i] = x[u];
+        }
+    }
+}
+
+}  // namespace mesa

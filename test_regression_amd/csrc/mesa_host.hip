@@ -119,12 +119,11 @@ size_t mesa_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chu
     return (size_t)B * H * nc * ((size_t)dk * (dk + 16) / 2 + (size_t)dv * dk) * sizeof(float);
 }
 
-mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dtype,
-                         const float* gamma, const float* lambda, int B, int H, int T, int dk,
-                         int dv, int chunk, int max_iters, float tol, float* out, int32_t* iters,
-                         float* final_H, float* final_G, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-    g_err.clear();
+static mesa_status forward_impl(const void* q, const void* k, const void* v, int qkv_dtype,
+                                const float* gamma, const float* lambda, int B, int H, int T, int dk,
+                                int dv, int chunk, int max_iters, float tol, float* out, int32_t* iters,
+                                float* final_H, float* final_G, float* x_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
     if (qkv_dtype != MESA_DTYPE_F32 && qkv_dtype != MESA_DTYPE_BF16)
         return fail(MESA_ERR_INVALID_ARGUMENT, "qkv_dtype %d is not MESA_DTYPE_F32 or MESA_DTYPE_BF16", qkv_dtype);
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0)
@@ -140,7 +139,7 @@ mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dt
     if (!lambda) return fail(MESA_ERR_INVALID_ARGUMENT, "lambda must be non-null");
     if (need_ws && !workspace) return fail(MESA_ERR_INVALID_ARGUMENT, "workspace must be non-null when max_iters > 0");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(final_H, 16) || !aligned(final_G, 16) || !aligned(workspace, 16) ||
+        !aligned(final_H, 16) || !aligned(final_G, 16) || !aligned(workspace, 16) || !aligned(x_out, 16) ||
         !aligned(gamma, 4) || !aligned(lambda, 4) || !aligned(iters, 4))
         return fail(MESA_ERR_INVALID_ARGUMENT, "misaligned pointer (16 B for tensors/workspace, 4 B for gamma/lambda/iters)");
     if (dk != dv) return fail(MESA_ERR_UNSUPPORTED, "dk (%d) != dv (%d) is not built", dk, dv);
@@ -178,13 +177,138 @@ mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dt
         // max_iters == 0: x = 0, so out = 0 and no update is made.
         hipError_t e = zero_fill(out, (size_t)BH * T * dv * sizeof(float), s);
         if (e == hipSuccess) e = zero_fill(iters, (size_t)BH * T * sizeof(int32_t), s);
+        if (e == hipSuccess) e = zero_fill(x_out, (size_t)BH * T * dk * sizeof(float), s);
         if (e != hipSuccess) return hip_fail(e, "zero fill of out/iters");
         return MESA_OK;
     }
     mesa::CgOutputArgs a{q, k, v, gamma, lambda, SH, SG, BH, H, T, dk, chunk, (int)n_chunks,
-                         bf16, max_iters, tol, out, iters};
+                         bf16, max_iters, tol, out, iters, x_out};
     hipError_t e = timed_launch(MESA_KERNEL_CG_OUTPUT, s, [&] { return mesa::launch_cg_output(a, s); });
     if (e != hipSuccess) return hip_fail(e, "CG/output kernel launch");
+    return MESA_OK;
+}
+
+mesa_status mesa_forward(const void* q, const void* k, const void* v, int qkv_dtype,
+                         const float* gamma, const float* lambda, int B, int H, int T, int dk,
+                         int dv, int chunk, int max_iters, float tol, float* out, int32_t* iters,
+                         float* final_H, float* final_G, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    g_err.clear();
+    return forward_impl(q, k, v, qkv_dtype, gamma, lambda, B, H, T, dk, dv, chunk, max_iters, tol, out, iters,
+                        final_H, final_G, nullptr, workspace, workspace_bytes, stream);
+}
+
+mesa_status mesa_forward_train(const void* q, const void* k, const void* v, int qkv_dtype,
+                               const float* gamma, const float* lambda, int B, int H, int T, int dk,
+                               int dv, int chunk, int max_iters, float tol, float* out, int32_t* iters,
+                               float* x_out, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    if (T > 0 && !x_out) return fail(MESA_ERR_INVALID_ARGUMENT, "x_out must be non-null");
+    return forward_impl(q, k, v, qkv_dtype, gamma, lambda, B, H, T, dk, dv, chunk, max_iters, tol, out, iters,
+                        nullptr, nullptr, x_out, workspace, workspace_bytes, stream);
+}
+
+// Backward workspace: forward chunk states, reverse states, per-token totals,
+// per-chunk regulariser sums; every segment a multiple of 4 floats.
+struct BwdLayout {
+    size_t sh, sg, pgx, pzx, beta, akey, lam, total;   // offsets in floats
+};
+
+static BwdLayout bwd_layout(long BH, int T, int d, long nc) {
+    auto r4 = [](size_t n) { return (n + 3) / 4 * 4; };
+    BwdLayout l{};
+    size_t o = 0;
+    l.sh = o;   o += r4((size_t)BH * nc * ((size_t)d * (d + 16) / 2));
+    l.sg = o;   o += r4((size_t)BH * nc * d * d);
+    l.pgx = o;  o += r4((size_t)BH * nc * d * d);
+    l.pzx = o;  o += r4((size_t)BH * nc * d * d);
+    l.beta = o; o += r4((size_t)BH * T);
+    l.akey = o; o += r4((size_t)BH * T);
+    l.lam = o;  o += r4((size_t)BH * nc * d);
+    l.total = o;
+    return l;
+}
+
+size_t mesa_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+    const long nc = ((long)T + chunk - 1) / chunk;
+    return bwd_layout((long)B * H, T, std::max(dk, dv), nc).total * sizeof(float);
+}
+
+mesa_status mesa_backward(const void* k, const void* v, int qkv_dtype, const float* gamma, const float* lambda,
+                          const float* x, const float* out, const float* grad_out, int B, int H, int T, int dk,
+                          int dv, int chunk, int max_iters, float tol, float* grad_q, float* grad_k, float* grad_v,
+                          float* grad_gamma, float* grad_lambda, int32_t* z_iters, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    if (qkv_dtype != MESA_DTYPE_F32 && qkv_dtype != MESA_DTYPE_BF16)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "qkv_dtype %d is not MESA_DTYPE_F32 or MESA_DTYPE_BF16", qkv_dtype);
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d H=%d T=%d dk=%d dv=%d chunk=%d)",
+                    B, H, T, dk, dv, chunk);
+    if (max_iters < 0 || max_iters > kMaxIters)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "max_iters=%d outside [0, %d]", max_iters, kMaxIters);
+    if (!(tol >= 0.0f) || std::isinf(tol))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "tol must be finite and >= 0");
+    if (!lambda || !grad_lambda) return fail(MESA_ERR_INVALID_ARGUMENT, "lambda and grad_lambda must be non-null");
+    if (T > 0 && (!k || !v || !gamma || !x || !out || !grad_out || !grad_q || !grad_k || !grad_v || !grad_gamma))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "k, v, gamma, x, out, grad_out and the gradients must be non-null");
+    if (T > 0 && !workspace) return fail(MESA_ERR_INVALID_ARGUMENT, "workspace must be non-null");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(x, 16) || !aligned(out, 16) || !aligned(grad_out, 16) ||
+        !aligned(grad_q, 16) || !aligned(grad_k, 16) || !aligned(grad_v, 16) || !aligned(workspace, 16) ||
+        !aligned(gamma, 4) || !aligned(lambda, 4) || !aligned(grad_gamma, 4) || !aligned(grad_lambda, 4) ||
+        !aligned(z_iters, 4))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "misaligned pointer (16 B for tensors/workspace, 4 B for the rest)");
+    if (dk != dv) return fail(MESA_ERR_UNSUPPORTED, "dk (%d) != dv (%d) is not built", dk, dv);
+    if (!supported_d(dk)) return fail(MESA_ERR_UNSUPPORTED, "d=%d not built (16, 32, 64, 128)", dk);
+    if (!supported_chunk(chunk)) return fail(MESA_ERR_UNSUPPORTED, "chunk=%d not built (16, 32, 64)", chunk);
+    const long n_chunks = ((long)T + chunk - 1) / chunk;
+    const long BH = (long)B * H;
+    if (BH * 4 > 0x7fffffffL || BH * n_chunks > 0x7fffffffL)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "grid too large (B*H=%ld, chunks=%ld)", BH, n_chunks);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        hipError_t e = zero_fill(grad_lambda, (size_t)H * dk * sizeof(float), s);
+        if (e != hipSuccess) return hip_fail(e, "zero fill of grad_lambda");
+        return MESA_OK;
+    }
+    const BwdLayout lay = bwd_layout(BH, T, dk, n_chunks);
+    if (workspace_bytes < lay.total * sizeof(float))
+        return fail(MESA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
+                    lay.total * sizeof(float));
+    float* ws = static_cast<float*>(workspace);
+    const int bf16 = qkv_dtype == MESA_DTYPE_BF16;
+    hipError_t e;
+    {
+        mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
+                                ws + lay.sh, ws + lay.sg, nullptr, nullptr, 1};
+        e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
+        if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
+    }
+    {
+        mesa::BwdAdjointArgs a{k, v, gamma, lambda, x, out, grad_out, ws + lay.sh, ws + lay.sg, BH, H, T, dk, chunk,
+                               (int)n_chunks, bf16, max_iters, tol, grad_q, ws + lay.beta, z_iters, ws + lay.lam};
+        e = timed_launch(MESA_KERNEL_BWD_ADJOINT, s, [&] { return mesa::launch_bwd_adjoint(a, s); });
+        if (e != hipSuccess) return hip_fail(e, "backward adjoint kernel launch");
+    }
+    {
+        mesa::BwdStatesArgs a{grad_out, grad_q, x, gamma, BH, T, dk, chunk, (int)n_chunks, ws + lay.pgx,
+                              ws + lay.pzx};
+        e = timed_launch(MESA_KERNEL_BWD_STATES, s, [&] { return mesa::launch_bwd_states(a, s); });
+        if (e != hipSuccess) return hip_fail(e, "backward state kernel launch");
+    }
+    {
+        mesa::BwdKvArgs a{k, v, gamma, x, grad_q, grad_out, ws + lay.pgx, ws + lay.pzx, BH, T, dk, chunk,
+                          (int)n_chunks, bf16, grad_k, grad_v, ws + lay.akey};
+        e = timed_launch(MESA_KERNEL_BWD_KV, s, [&] { return mesa::launch_bwd_kv(a, s); });
+        if (e != hipSuccess) return hip_fail(e, "backward key/value kernel launch");
+    }
+    {
+        mesa::BwdGateArgs a{ws + lay.beta, ws + lay.akey, gamma, ws + lay.lam, BH, B, H, T, dk, (int)n_chunks,
+                            grad_gamma, grad_lambda};
+        e = timed_launch(MESA_KERNEL_BWD_GATE, s, [&] { return mesa::launch_bwd_gate(a, s); });
+        if (e != hipSuccess) return hip_fail(e, "backward gate kernel launch");
+    }
     return MESA_OK;
 }
 
@@ -323,6 +447,10 @@ const char* mesa_kernel_name(int kernel_id) {
         case MESA_KERNEL_CG_OUTPUT: return "cg_output_kernel";
         case MESA_KERNEL_DECODE: return "decode_kernel";
         case MESA_KERNEL_QK_PREPROCESS: return "qk_preprocess_kernel";
+        case MESA_KERNEL_BWD_ADJOINT: return "bwd_adjoint_kernel";
+        case MESA_KERNEL_BWD_STATES: return "bwd_states_kernel";
+        case MESA_KERNEL_BWD_KV: return "bwd_kv_kernel";
+        case MESA_KERNEL_BWD_GATE: return "bwd_gate_kernel";
     }
     return "unknown";
 }

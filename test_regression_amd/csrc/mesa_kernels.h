@@ -18,6 +18,7 @@ struct CgOutputArgs {
     long BH; int H; int T; int d; int chunk; int n_chunks; int bf16;
     int max_iters; float tol;
     float* out; int32_t* iters;
+    float* x_out;   // CG solutions [BH, T, d], or nullptr
 };
 
 struct DecodeArgs {
@@ -43,6 +44,34 @@ struct QkPreArgs {
 constexpr int kQkPreSegment = MESA_QK_PRE_SEGMENT;   // tokens per thread of the pre-processing kernel
 constexpr int kQkPreMaxWidth = 4;   // widest convolution window the kernel is built for
 
+// Backward pass (see the bwd_*.hip kernels).
+struct BwdAdjointArgs {
+    const void* k; const void* v; const float* gamma; const float* lambda;
+    const float* x; const float* o; const float* gout; const float* SH; const float* SG;
+    long BH; int H; int T; int d; int chunk; int n_chunks; int bf16; int max_iters; float tol;
+    float* dq; float* beta; int32_t* z_iters; float* lam_part;
+};
+struct BwdStatesArgs {
+    const float* g; const float* z; const float* x; const float* gamma;
+    long BH; int T; int d; int chunk; int n_chunks;
+    float* Pgx; float* Pzx;
+};
+struct BwdKvArgs {
+    const void* k; const void* v; const float* gamma; const float* x; const float* z; const float* gout;
+    const float* Pgx; const float* Pzx;
+    long BH; int T; int d; int chunk; int n_chunks; int bf16;
+    float* dk; float* dv; float* akey;
+};
+struct BwdGateArgs {
+    const float* beta; const float* akey; const float* gamma; const float* lam_part;
+    long BH; int B; int H; int T; int d; int n_chunks;
+    float* dgamma; float* dlam;
+};
+
+hipError_t launch_bwd_adjoint(const BwdAdjointArgs& a, hipStream_t s);
+hipError_t launch_bwd_states(const BwdStatesArgs& a, hipStream_t s);
+hipError_t launch_bwd_kv(const BwdKvArgs& a, hipStream_t s);
+hipError_t launch_bwd_gate(const BwdGateArgs& a, hipStream_t s);
 hipError_t launch_cg_output(const CgOutputArgs& a, hipStream_t s);
 hipError_t launch_qk_preprocess(const QkPreArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

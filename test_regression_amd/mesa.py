@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmesa.so")
 MESA_OK, MESA_ERR_INVALID_ARGUMENT, MESA_ERR_UNSUPPORTED, MESA_ERR_WORKSPACE_TOO_SMALL, MESA_ERR_HIP = range(5)
 MESA_DTYPE_F32, MESA_DTYPE_BF16 = 0, 1
 KERNEL_CHUNK_STATES, KERNEL_CG_OUTPUT, KERNEL_DECODE, KERNEL_QK_PREPROCESS = 0, 1, 2, 3
+KERNEL_BWD_ADJOINT, KERNEL_BWD_STATES, KERNEL_BWD_KV, KERNEL_BWD_GATE = 4, 5, 6, 7
 MESA_WARM_COLD, MESA_WARM_PREVIOUS, MESA_WARM_PROJECTED = 0, 1, 2
 
 # Every symbol include/mesa.h declares, with its ctypes signature.
@@ -27,6 +28,11 @@ SIGNATURES = {
     "mesa_forward_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
     "mesa_forward": ([_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                       _P, _P, _P, _P, _P, _Z, _P], _I),
+    "mesa_forward_train": ([_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                            _P, _P, _P, _P, _Z, _P], _I),
+    "mesa_backward_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
+    "mesa_backward": ([_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                       _P, _P, _P, _P, _P, _P, _P, _Z, _P], _I),
     "mesa_decode_step": ([_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
                           _P, _P, _P], _I),
     "mesa_decode_step_warm": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
@@ -152,6 +158,68 @@ def mesa_forward(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out=None,
                             _stream(stream))
     _check(st, "mesa_forward")
     return out, iters, final_H, final_G
+
+
+def mesa_forward_train(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out=None, iters=None,
+                       x_out=None, workspace=None, stream=None):
+    """Forward that also returns the CG solutions x (see include/mesa.h,
+    mesa_forward_train).  Returns (out, iters, x)."""
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(gamma, "gamma", torch.float32, dev)
+    _need(lam, "lambda", torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    if iters is None:
+        iters = torch.empty((B, H, T), dtype=torch.int32, device=dev)
+    if x_out is None:
+        x_out = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
+    nbytes = mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    st = lib().mesa_forward_train(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(gamma), _ptr(lam),
+                                  B, H, T, dk, dv, chunk, int(max_iters), float(tol),
+                                  _ptr(out), _ptr(iters), _ptr(x_out), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check(st, "mesa_forward_train")
+    return out, iters, x_out
+
+
+def mesa_backward_workspace_bytes(B, H, T, dk, dv, chunk) -> int:
+    return int(lib().mesa_backward_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def mesa_backward(k, v, gamma, lam, x, out, grad_out, max_iters, tol=0.0, chunk=64, *, workspace=None,
+                  return_z_iters=True, stream=None):
+    """Backward pass (see include/mesa.h, mesa_backward).  Returns a dict of
+    grad_q, grad_k, grad_v, grad_gamma, grad_lambda (float32) and z_iters."""
+    import torch
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dev = k.device
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, k.dtype, dev)
+    for t, n in ((gamma, "gamma"), (lam, "lambda"), (x, "x"), (out, "out"), (grad_out, "grad_out")):
+        _need(t, n, torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(grad_q=torch.empty((B, H, T, dk), **f32), grad_k=torch.empty((B, H, T, dk), **f32),
+             grad_v=torch.empty((B, H, T, dv), **f32), grad_gamma=torch.empty((B, H, T), **f32),
+             grad_lambda=torch.empty((H, dk), **f32))
+    g["z_iters"] = torch.empty((B, H, T), dtype=torch.int32, device=dev) if return_z_iters else None
+    nbytes = mesa_backward_workspace_bytes(B, H, T, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    st = lib().mesa_backward(_ptr(k), _ptr(v), _qkv_dtype(k), _ptr(gamma), _ptr(lam), _ptr(x), _ptr(out),
+                             _ptr(grad_out), B, H, T, dk, dv, chunk, int(max_iters), float(tol),
+                             _ptr(g["grad_q"]), _ptr(g["grad_k"]), _ptr(g["grad_v"]), _ptr(g["grad_gamma"]),
+                             _ptr(g["grad_lambda"]), _ptr(g["z_iters"]), _ptr(workspace), workspace.numel(),
+                             _stream(stream))
+    _check(st, "mesa_backward")
+    return g
 
 
 def _decode_checks(q, v, gamma, lam, state_H, state_G, state_x=None):

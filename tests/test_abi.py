@@ -45,7 +45,9 @@ def test_version_and_status_strings():
                     (HIPERR, b"MESA_ERR_HIP")]:
         assert L.mesa_status_string(s) == name
     assert L.mesa_status_string(99) == b"MESA_ERR_UNKNOWN"
-    assert [mesa.kernel_name(i) for i in range(3)] == ["chunk_states_kernel", "cg_output_kernel", "decode_kernel"]
+    assert [mesa.kernel_name(i) for i in range(8)] == [
+        "chunk_states_kernel", "cg_output_kernel", "decode_kernel", "qk_preprocess_kernel", "bwd_adjoint_kernel",
+        "bwd_states_kernel", "bwd_kv_kernel", "bwd_gate_kernel"]
 
 
 def test_workspace_bytes():
@@ -207,6 +209,58 @@ def test_preprocess_empty_piece_is_a_no_op():
     assert st == 0, msg
 
 
+def bwd(**kw):
+    a = dict(k=FAKE, v=FAKE, dt=0, gamma=FAKE, lam=FAKE, x=FAKE, out=FAKE, gout=FAKE, B=1, H=2, T=128, dk=64,
+             dv=64, chunk=64, max_iters=5, tol=0.0, gq=FAKE, gk=FAKE, gv=FAKE, gg=FAKE, gl=FAKE, zi=None, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    L = mesa.lib()
+    st = L.mesa_backward(a["k"], a["v"], a["dt"], a["gamma"], a["lam"], a["x"], a["out"], a["gout"], a["B"], a["H"],
+                         a["T"], a["dk"], a["dv"], a["chunk"], a["max_iters"], ctypes.c_float(a["tol"]), a["gq"],
+                         a["gk"], a["gv"], a["gg"], a["gl"], a["zi"], a["ws"], a["ws_bytes"], a["stream"])
+    return st, L.mesa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), INVALID, "non-null"),
+    (dict(gout=None), INVALID, "non-null"),
+    (dict(gl=None), INVALID, "grad_lambda"),
+    (dict(ws=None), INVALID, "workspace"),
+    (dict(dt=5), INVALID, "qkv_dtype"),
+    (dict(T=-1), INVALID, "positive"),
+    (dict(max_iters=-1), INVALID, "max_iters"),
+    (dict(tol=float("nan")), INVALID, "tol"),
+    (dict(x=FAKE + 4), INVALID, "misaligned"),
+    (dict(gg=FAKE + 2), INVALID, "misaligned"),
+    (dict(dk=64, dv=32), UNSUPPORTED, "dv"),
+    (dict(dk=48, dv=48), UNSUPPORTED, "d=48"),
+    (dict(chunk=128), UNSUPPORTED, "chunk"),
+    (dict(ws_bytes=1000), WS_SMALL, "workspace"),
+])
+def test_backward_rejects_bad_arguments(kw, status, needle):
+    st, msg = bwd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_backward_workspace_bytes():
+    f = mesa.lib().mesa_backward_workspace_bytes
+    r4 = lambda n: (n + 3) // 4 * 4
+    B, H, T, d, C = 2, 3, 130, 64, 64
+    nc = 3
+    want = (r4(B * H * nc * d * (d + 16) // 2) + 3 * r4(B * H * nc * d * d) + 2 * r4(B * H * T)
+            + r4(B * H * nc * d)) * 4
+    assert f(B, H, T, d, d, C) == want
+    assert f(0, H, T, d, d, C) == 0 and f(B, H, T, d, d, 0) == 0
+
+
+def test_forward_train_requires_x_out():
+    L = mesa.lib()
+    st = L.mesa_forward_train(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, 2, 128, 64, 64, 64, 5, ctypes.c_float(0.0),
+                              FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == INVALID and "x_out" in L.mesa_last_error_message().decode()
+
+
 def test_probe_argument_validation():
     L = mesa.lib()
     assert L.mesa_probe_mfma_f32(0, 10, FAKE, None) == INVALID
@@ -221,7 +275,8 @@ def test_profile_api_host_paths():
     L = mesa.lib()
     ms = ctypes.c_double(-1)
     n = ctypes.c_int64(-1)
-    assert L.mesa_profile_read(7, ctypes.byref(ms), ctypes.byref(n)) == INVALID
+    assert L.mesa_profile_read(8, ctypes.byref(ms), ctypes.byref(n)) == INVALID
+    assert L.mesa_profile_read(-1, ctypes.byref(ms), ctypes.byref(n)) == INVALID
     assert L.mesa_profile_read(0, None, ctypes.byref(n)) == INVALID
     assert L.mesa_profile_reset() == OK
     assert L.mesa_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == OK

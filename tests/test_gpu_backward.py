@@ -1,0 +1,151 @@
+"""GPU parity of the backward pass (mesa_forward_train + mesa_backward)
+against the fp64 oracle's backward.
+
+The page says the layer trains in parallel but gives no gradient (MesaNet
+summary, section "A Camada Mesa", bullet "Paralelizacao"); the reading is
+implicit differentiation with a k-step adjoint CG (oracle/mesa_oracle.c,
+oracle_backward).  Each gradient (q, k, v, gamma, lambda) must match within
+relative L2 2e-3 for float32 q/k/v and 1e-2 for bfloat16; adjoint iteration
+counts follow the forward's rule (exact for decidable tokens).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from test_regression_amd import inputs
+from tests.parity_helpers import RTOL, compare_counts, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dgamma", "dlam")
+GPU_NAMES = dict(dq="grad_q", dk="grad_k", dv="grad_v", dgamma="grad_gamma", dlam="grad_lambda")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small_inputs(seed, B, H, T, d, dtype, glo=0.9):
+    w = inputs.Workload("t", B, H, T, d, 64, dtype, glo, "uniform", 0.5, 2.0, 0, 0.0, seed)
+    x = inputs.forward_inputs(w)
+    x["gout"] = np.random.default_rng(seed + 7).standard_normal((B, H, T, d)).astype(np.float32)
+    return x
+
+
+def gpu_backward(x, dtype, max_iters, tol, chunk):
+    import torch
+    from test_regression_amd import mesa
+    q, k, v = (to_dev(x[n], dtype) for n in ("q", "k", "v"))
+    g, lam, gout = to_dev(x["gamma"], "f32"), to_dev(x["lam"], "f32"), to_dev(x["gout"], "f32")
+    out, _, xs = mesa.mesa_forward_train(q, k, v, g, lam, max_iters, tol, chunk)
+    r = mesa.mesa_backward(k, v, g, lam, xs, out, gout, max_iters, tol, chunk)
+    torch.cuda.synchronize()
+    res = {n: r[GPU_NAMES[n]].cpu().numpy().astype(np.float64) for n in NAMES}
+    res["z_iters"] = r["z_iters"].cpu().numpy()
+    return res
+
+
+def oracle_backward(x, dtype, max_iters, tol, heads=None):
+    q, k, v = (inputs.as_f64(x[n], dtype) for n in ("q", "k", "v"))
+    g, lam, gout = x["gamma"], x["lam"], x["gout"]
+    if heads is not None:
+        b, h = heads
+        q, k, v, g, gout = (a[b:b + 1, h:h + 1] for a in (q, k, v, g, gout))
+        lam = lam[h:h + 1]
+    return oracle.backward(q, k, v, g, lam, gout, max_iters, tol)
+
+
+def check(gpu, ref, dtype, max_iters, tol, what=""):
+    # gamma at a sequence's first token has no effect: its gradient is exactly
+    # zero, reached on the GPU as the difference of two equal fp32 totals, so
+    # it is held to an absolute bound and left out of the relative error.
+    g0 = np.abs(gpu["dgamma"][:, :, 0]).max()
+    assert g0 <= 1e-4 * (1.0 + np.abs(ref["dgamma"]).max()), g0
+    errs = {}
+    for n in NAMES:
+        if n == "dgamma":
+            if gpu[n].shape[2] > 1:
+                errs[n] = rel_l2(gpu[n][:, :, 1:], ref[n][:, :, 1:])
+        else:
+            errs[n] = rel_l2(gpu[n], ref[n])
+    say(f"  {what} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= RTOL[dtype], (n, e)
+    zref = dict(iters=ref["z_iters"], rho_stop=ref["z_rho_stop"], rho_min_prev=ref["z_rho_min_prev"],
+                reason=ref["z_reason"])
+    compare_counts(gpu["z_iters"], zref, max_iters, tol)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_dims_chunks_dtypes(d, chunk, dtype):
+    B, H = 1, 2
+    T = 3 * chunk + chunk // 2 + 3
+    seed = 5000 + d + chunk
+    say("case backward", dict(d=d, chunk=chunk, dtype=dtype, B=B, H=H, T=T, seed=seed))
+    x = small_inputs(seed, B, H, T, d, dtype)
+    for max_iters, tol in ((8, 0.0), (30, 1e-4)):
+        gpu = gpu_backward(x, dtype, max_iters, tol, chunk)
+        ref = oracle_backward(x, dtype, max_iters, tol)
+        check(gpu, ref, dtype, max_iters, tol, f"k={max_iters} tol={tol}")
+
+
+def test_backward_edge_cases():
+    import torch
+    from test_regression_amd import mesa
+    d, chunk = 32, 64
+    for T in (1, 5, 64, 65):
+        say("case backward edge T", T)
+        x = small_inputs(5200 + T, 2, 1, T, d, "f32")
+        gpu = gpu_backward(x, "f32", 10, 0.0, chunk)
+        ref = oracle_backward(x, "f32", 10, 0.0)
+        check(gpu, ref, "f32", 10, 0.0, f"T={T}")
+    say("case backward zero grad_out and max_iters=0")
+    x = small_inputs(5300, 1, 2, 70, d, "f32")
+    x["gout"][:] = 0.0
+    gpu = gpu_backward(x, "f32", 10, 0.0, chunk)
+    assert all(not gpu[n].any() for n in NAMES)
+    x = small_inputs(5301, 1, 2, 70, d, "f32")
+    gpu = gpu_backward(x, "f32", 0, 0.0, chunk)
+    assert all(not gpu[n].any() for n in NAMES)
+    say("case backward T=0")
+    lam = torch.ones((2, d), dtype=torch.float32, device="cuda")
+    e = torch.empty((1, 2, 0, d), dtype=torch.float32, device="cuda")
+    g0 = torch.empty((1, 2, 0), dtype=torch.float32, device="cuda")
+    r = mesa.mesa_backward(e, e, g0, lam, e, e, e, 10, 0.0, 64)
+    torch.cuda.synchronize()
+    assert not r["grad_lambda"].any()
+
+
+def test_backward_layer_shape_sampled_heads():
+    """The headline layer (8 x 16 x 4096, d=128, bf16, k=30) backward at full
+    size; four heads against the oracle (which also gives dlambda per head)."""
+    w = inputs.WORKLOADS["layer_bf16_d128_T4096_k30"]
+    say("case backward layer", w.name)
+    x = inputs.forward_inputs(w)
+    x["gout"] = np.random.default_rng(w.seed + 9).standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
+    gpu = gpu_backward(x, w.dtype, w.max_iters, w.tol, w.chunk)
+    for (b, h) in ((0, 0), (2, 5), (5, 11), (7, 15)):
+        ref = oracle_backward(x, w.dtype, w.max_iters, w.tol, heads=(b, h))
+        sub = {n: gpu[n][b:b + 1, h:h + 1] for n in ("dq", "dk", "dv", "dgamma")}
+        errs = {n: rel_l2(sub[n], ref[n]) for n in sub}
+        errs["dgamma"] = rel_l2(sub["dgamma"][:, :, 1:], ref["dgamma"][:, :, 1:])
+        say(f"  head ({b},{h}) " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= RTOL[w.dtype], (n, e)
+        assert (gpu["z_iters"][b, h] == w.max_iters).all()
+    # dlambda sums every head of the batch: check it against its definition
+    # -sum z (.) x with the GPU's own z (= dq) and the oracle's x is covered by
+    # the small cases; here it must at least be finite and of the right shape
+    assert np.isfinite(gpu["dlam"]).all() and gpu["dlam"].shape == (w.H, w.d)
