@@ -142,6 +142,73 @@ def headline(torch, mesa, inputs, args, dev):
     return res
 
 
+def backward(torch, mesa, h, dev, steps=5, warmup=2):
+    """Training step of the layer on the headline workload: mesa_forward_train
+    then mesa_backward with a seeded dL/d(out), timed separately."""
+    w, x = h["w"], h["x"]
+    t = {n: to_dev(torch, x[n], w.dtype if n in ("q", "k", "v") else "f32", dev) for n in x}
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 9)
+    gout = torch.randn((w.B, w.H, w.T, w.d), generator=g, device=dev)
+    n_tok = w.B * w.H * w.T
+    fws = torch.empty(mesa.mesa_forward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.chunk), dtype=torch.uint8,
+                      device=dev)
+    bws = torch.empty(mesa.mesa_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.chunk), dtype=torch.uint8,
+                      device=dev)
+
+    def fwd():
+        return mesa.mesa_forward_train(t["q"], t["k"], t["v"], t["gamma"], t["lam"], w.max_iters, w.tol, w.chunk,
+                                       workspace=fws)
+
+    def bwd(out, xs):
+        return mesa.mesa_backward(t["k"], t["v"], t["gamma"], t["lam"], xs, out, gout, w.max_iters, w.tol,
+                                  w.chunk, workspace=bws)
+    log(f"[bench] backward: {steps} training steps after {warmup} warmup")
+    for _ in range(warmup):
+        out, _, xs = fwd()
+        bwd(out, xs)
+    torch.cuda.synchronize()
+    ids = {"chunk_states_kernel": mesa.KERNEL_CHUNK_STATES, "bwd_adjoint_kernel": mesa.KERNEL_BWD_ADJOINT,
+           "bwd_states_kernel": mesa.KERNEL_BWD_STATES, "bwd_kv_kernel": mesa.KERNEL_BWD_KV,
+           "bwd_gate_kernel": mesa.KERNEL_BWD_GATE}
+    f_el = b_el = 0.0
+    kt = {n: [0.0, 0] for n in ids}
+    for _ in range(steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out, _, xs = fwd()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        mesa.profile_reset()
+        mesa.profile_enable(True)
+        bwd(out, xs)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        mesa.profile_enable(False)
+        for n, i in ids.items():
+            ms, c = mesa.profile_read(i)
+            kt[n][0] += ms
+            kt[n][1] += c
+        mesa.profile_reset()
+        f_el += t1 - t0
+        b_el += t2 - t1
+    d, C, k = w.d, w.chunk, w.max_iters
+    # adjoint kernel per token-head: G^T g and H x (each 2d^2 + 2(C+1)d), the k-step CG
+    adj_flops = n_tok * (k * (2 * d * d + 2 * (C + 1) * d + 11 * d) + 2 * (2 * d * d + 2 * (C + 1) * d))
+    adj_ms = kt["bwd_adjoint_kernel"][0] / max(kt["bwd_adjoint_kernel"][1], 1)
+    achieved = adj_flops / (adj_ms * 1e-3) / 1e12
+    kernels = {n: {"avg_ms": round(v[0] / max(v[1], 1), 4), "launches": v[1]} for n, v in kt.items()}
+    del t, gout, fws, bws
+    return {"workload": w.name, "grad_out": "N(0,1), seeded",
+            "forward_train_ms": round(1e3 * f_el / steps, 4), "backward_ms": round(1e3 * b_el / steps, 4),
+            "train_step_tokens_per_s": round(n_tok * steps / (f_el + b_el), 1),
+            "kernels": kernels,
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "kernel": "bwd_adjoint_kernel<128,64,bf16>", "flops_per_launch": adj_flops,
+                         "avg_launch_ms": round(adj_ms, 4)}}
+
+
 def dynamic(torch, mesa, inputs, dev):
     w = inputs.WORKLOADS["dynamic_f32_d128_T8192_tol1e-4"]
     log(f"[bench] generating {w.name}")
@@ -407,6 +474,8 @@ def main():
         del a, b
     extra = {}
     if not args.no_extra:
+        extra["backward"] = backward(torch, mesa, h, dev)
+        torch.cuda.empty_cache()
         extra["dynamic"] = dynamic(torch, mesa, inputs, dev)
         torch.cuda.empty_cache()
         extra["decode"] = decode(torch, mesa, inputs, dev, steps=args.decode_steps,
@@ -433,6 +502,10 @@ def main():
         "kernels": h["kernels"],
     }
     line["measured_peaks"] = peaks
+    if "backward" in extra:
+        d = extra["backward"]["roofline"]
+        d["peak_measured"] = peaks["mfma_f32_tflops"]
+        d["frac_measured"] = round(d["achieved"] / peaks["mfma_f32_tflops"], 4)
     for sec in ("decode", "qk_preprocess"):
         if sec in extra:
             d = extra[sec]["roofline"]
