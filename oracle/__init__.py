@@ -66,6 +66,8 @@ def _load():
         lib.oracle_qk_preprocess.restype = I
         lib.oracle_backward.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_backward.restype = I
+        lib.oracle_hawk_scan.argtypes = [P, P, P, P, D, P, I, I, I, P, P]
+        lib.oracle_hawk_scan.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -252,3 +254,21 @@ def backward(q, k, v, gamma, lam, gout, max_iters, tol=0.0):
         raise ValueError("oracle_backward rejected its arguments")
     return dict(dq=dq, dk=dkk, dv=dvv, dgamma=dg, dlam=dl, x=x, z_iters=zi, z_rho_stop=zs,
                 z_rho_min_prev=zm, z_reason=zr)
+
+
+def hawk_scan(x, ga, gx, lam, c=8.0, h0=None):
+    """The Hawk layer's gated linear recurrence over [B, T, D] (see
+    oracle_hawk_scan).  Returns (y [B,T,D], h_final [B,D]) in float64."""
+    lib = _load()
+    x, ga, gx, lam = _f64(x), _f64(ga), _f64(gx), _f64(lam)
+    B, T, D = x.shape
+    assert ga.shape == x.shape and gx.shape == x.shape and lam.shape == (D,)
+    if h0 is not None:
+        h0 = _f64(h0)
+        assert h0.shape == (B, D)
+    y = np.zeros((B, T, D))
+    hf = np.zeros((B, D))
+    rc = lib.oracle_hawk_scan(_ptr(x), _ptr(ga), _ptr(gx), _ptr(lam), float(c), _ptr(h0), B, T, D, _ptr(y), _ptr(hf))
+    if rc != 0:
+        raise ValueError("oracle_hawk_scan rejected its arguments")
+    return y, hf

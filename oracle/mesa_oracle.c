@@ -490,5 +490,40 @@ int oracle_backward(const double *q, const double *k, const double *v, const dou
     return bad ? -1 : 0;
 }
 
+/*
+ * Recurrence of the Hawk layer that the hybrid "Hawk-Mesa" model alternates
+ * with Mesa layers (section "Arquitetura (MesaNet)", bullet "Variante
+ * Hibrida": LRU (Hawk) layers).  The page names the layer only; the reading
+ * is the published real-gated linear recurrent unit of Hawk, per channel d:
+ *   r_t = sigmoid(ga_t),  i_t = sigmoid(gx_t)        (gate pre-activations)
+ *   log a_t = -c * softplus(-lam_d) * r_t            (a = sigmoid(lam), a_t = a^{c r_t})
+ *   h_t = a_t h_{t-1} + sqrt(1 - a_t^2) * (i_t * x_t),  h_0 from h0 (NULL: 0)
+ * x, ga, gx, y: [B, T, D]; lam: [D]; h0, h_final: [B, D] (may be NULL).
+ */
+static double softplus(double z) { return z > 30.0 ? z : log1p(exp(z)); }
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+int oracle_hawk_scan(const double *x, const double *ga, const double *gx, const double *lam, double c,
+                     const double *h0, int B, int T, int D, double *y, double *h_final)
+{
+    if (B < 0 || T < 0 || D <= 0) return -1;
+    #pragma omp parallel for schedule(static)
+    for (long bd = 0; bd < (long)B * D; ++bd) {
+        long b = bd / D;
+        int d = (int)(bd % D);
+        double h = h0 ? h0[bd] : 0.0;
+        double sp = softplus(-lam[d]);
+        for (int t = 0; t < T; ++t) {
+            size_t i = ((size_t)b * T + t) * D + d;
+            double r = sigmoid(ga[i]), in = sigmoid(gx[i]);
+            double a = exp(-c * sp * r);
+            h = a * h + sqrt(1.0 - a * a) * (in * x[i]);
+            y[i] = h;
+        }
+        if (h_final) h_final[bd] = h;
+    }
+    return 0;
+}
+
 /* Threads an OpenMP parallel region of this library would use. */
 int oracle_max_threads(void) { return omp_get_max_threads(); }

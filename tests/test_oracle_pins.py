@@ -637,3 +637,76 @@ def test_backward_first_gate_gradient_is_zero_and_adjoint_is_cg():
             np.testing.assert_allclose(r["x"][b, 0, t], xs, rtol=1e-10, atol=1e-12)
     # dlambda sums -z (.) x over the batch and tokens
     np.testing.assert_allclose(r["dlam"][0], -np.sum(r["dq"][:, 0] * r["x"][:, 0], axis=(0, 1)), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Hawk layer recurrence (section "Arquitetura (MesaNet)", bullet "Variante
+# Hibrida": the hybrid alternates LRU (Hawk) layers with Mesa layers; the
+# recurrence is the published real-gated LRU of Hawk).  H1: a hand-worked
+# example.  H2: constant gates reduce to a first-order filter, checked with
+# scipy.signal.lfilter.  H3: time-varying gates against the explicit
+# sum of products.  H4: pieces with the carried state equal one pass.
+# H5: closed gates keep the state.
+# --------------------------------------------------------------------------
+def test_hawk_hand_worked_example():
+    # c = 1, lam = 0, ga = gx = +50 (r = i = 1): a = sigmoid(0) = 1/2, sqrt(1 - a^2) = sqrt(3)/2
+    x = np.array([2.0, 4.0]).reshape(1, 2, 1)
+    big = np.full((1, 2, 1), 50.0)
+    y, hf = oracle.hawk_scan(x, big, big, np.zeros(1), c=1.0)
+    s3 = np.sqrt(3.0)
+    np.testing.assert_allclose(y[0, :, 0], [s3, 2.5 * s3], rtol=1e-15)
+    np.testing.assert_allclose(hf[0], [2.5 * s3], rtol=1e-15)
+
+
+def test_hawk_constant_gates_is_a_first_order_filter():
+    import scipy.signal
+    rng = np.random.default_rng(51)
+    B, T, D, c = 2, 40, 3, 8.0
+    x = rng.standard_normal((B, T, D))
+    ga0 = rng.standard_normal((1, 1, D))
+    gx0 = rng.standard_normal((1, 1, D))
+    lam = rng.standard_normal(D)
+    h0 = rng.standard_normal((B, D))
+    y, hf = oracle.hawk_scan(x, np.broadcast_to(ga0, x.shape), np.broadcast_to(gx0, x.shape), lam, c, h0)
+    for b in range(B):
+        for d in range(D):
+            r = 1 / (1 + np.exp(-ga0[0, 0, d]))
+            i = 1 / (1 + np.exp(-gx0[0, 0, d]))
+            a = (1 / (1 + np.exp(-lam[d]))) ** (c * r)
+            u = np.sqrt(1 - a * a) * i * x[b, :, d]
+            want, _ = scipy.signal.lfilter([1.0], [1.0, -a], u, zi=[a * h0[b, d]])
+            assert rel(y[b, :, d], want) < 1e-13
+
+
+def test_hawk_time_varying_gates_explicit_sum():
+    rng = np.random.default_rng(52)
+    B, T, D, c = 1, 25, 4, 8.0
+    x, ga, gx = (rng.standard_normal((B, T, D)) for _ in range(3))
+    lam = rng.standard_normal(D) + 2.0
+    h0 = rng.standard_normal((B, D))
+    y, _ = oracle.hawk_scan(x, ga, gx, lam, c, h0)
+    sig = lambda z: 1 / (1 + np.exp(-z))
+    a = np.exp(c * sig(ga) * np.log(sig(lam)))          # a^{c r_t}
+    u = np.sqrt(1 - a * a) * sig(gx) * x
+    for t in range(T):
+        # h_t = (prod_{s<=t} a_s) h0 + sum_{s<=t} (prod_{s<u<=t} a_u) u_s
+        want = np.prod(a[0, :t + 1], axis=0) * h0[0]
+        for s_ in range(t + 1):
+            want = want + np.prod(a[0, s_ + 1:t + 1], axis=0) * u[0, s_]
+        assert rel(y[0, t], want) < 1e-12, t
+
+
+def test_hawk_pieces_and_closed_gates():
+    rng = np.random.default_rng(53)
+    B, T, D = 2, 30, 5
+    x, ga, gx = (rng.standard_normal((B, T, D)) for _ in range(3))
+    lam = rng.standard_normal(D)
+    y, hf = oracle.hawk_scan(x, ga, gx, lam)
+    y1, h1 = oracle.hawk_scan(x[:, :11], ga[:, :11], gx[:, :11], lam)
+    y2, h2 = oracle.hawk_scan(x[:, 11:], ga[:, 11:], gx[:, 11:], lam, h0=h1)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(h2, hf, rtol=1e-14)
+    # closed gates (r = 0 -> a = 1, no input) keep the state
+    h0 = rng.standard_normal((B, D))
+    yc, hc = oracle.hawk_scan(x, np.full_like(x, -60.0), gx, lam, h0=h0)
+    np.testing.assert_allclose(yc, np.broadcast_to(h0[:, None, :], x.shape), rtol=1e-12)
