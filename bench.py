@@ -370,6 +370,43 @@ def qk_preprocess(torch, mesa, inputs, dev, steps=20, warmup=3, W=4):
                          "bytes_per_launch": per_launch, "avg_launch_ms": round(k_ms, 4)}}
 
 
+def hawk(torch, mesa, dev, steps=20, warmup=3, c=8.0):
+    """The Hawk layer's recurrence at the width of the headline layer
+    (8 sequences x 4096 tokens x 2048 channels, bf16 inputs, fp32 output).
+    HBM-bound; both passes of the chunked scan are in the timed launch."""
+    B, T, D = 8, 4096, 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    x, ga, gx = (torch.randn((B, T, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    s = (0.9 + 0.099 * torch.rand(D, generator=g, device=dev)) ** (1.0 / c)
+    lam = torch.log(s / (1 - s))
+    h0 = torch.randn((B, D), generator=g, device=dev)
+    y = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(mesa.lib().mesa_hawk_workspace_bytes(B, T, D), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        mesa.mesa_hawk_scan(x, ga, gx, lam, c, h0, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    mesa.profile_reset()
+    mesa.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mesa.mesa_hawk_scan(x, ga, gx, lam, c, h0, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    mesa.profile_enable(False)
+    kh = mesa.profile_read(mesa.KERNEL_HAWK)
+    mesa.profile_reset()
+    k_ms = kh[0] / max(kh[1], 1)
+    per_call = B * T * D * (3 * 2 + 4) + D * 4 + 2 * B * D * 4    # x, ga, gx (bf16) + y (fp32); lam, h0
+    gbs = per_call / (k_ms * 1e-3) / 1e9
+    del x, ga, gx, y, ws
+    return {"workload": f"hawk_bf16_B{B}_T{T}_D{D}", "tokens_per_s": round(B * T * steps / el, 1),
+            "ms_per_call": round(1e3 * el / steps, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "hawk_summary + hawk_scan",
+                         "bytes_per_launch": per_call, "avg_launch_ms": round(k_ms, 4)}}
+
+
 def measured_peaks(torch, mesa, dev):
     """Attainable rates on this GPU from known-work probe kernels: fp32 and
     bf16 MFMA register-resident loops (1024 workgroups x 4 waves) and a 1 GiB
@@ -483,6 +520,8 @@ def main():
         torch.cuda.empty_cache()
         extra["qk_preprocess"] = qk_preprocess(torch, mesa, inputs, dev)
         torch.cuda.empty_cache()
+        extra["hawk"] = hawk(torch, mesa, dev)
+        torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on {args.cpu_heads} heads")
@@ -506,7 +545,7 @@ def main():
         d = extra["backward"]["roofline"]
         d["peak_measured"] = peaks["mfma_f32_tflops"]
         d["frac_measured"] = round(d["achieved"] / peaks["mfma_f32_tflops"], 4)
-    for sec in ("decode", "qk_preprocess"):
+    for sec in ("decode", "qk_preprocess", "hawk"):
         if sec in extra:
             d = extra[sec]["roofline"]
             d["peak_measured"] = peaks["copy_gbs"]

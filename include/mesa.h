@@ -76,7 +76,8 @@ typedef enum {
     MESA_KERNEL_BWD_STATES = 5,      /* backward: reverse chunk states                   */
     MESA_KERNEL_BWD_KV = 6,          /* backward: key and value gradients                */
     MESA_KERNEL_BWD_GATE = 7,        /* backward: gate and regulariser gradients         */
-    MESA_KERNEL_COUNT = 8
+    MESA_KERNEL_HAWK = 8,            /* Hawk layer recurrence (both passes)              */
+    MESA_KERNEL_COUNT = 9
 } mesa_kernel_id;
 
 /* Library ABI version (MESA_ABI_VERSION of the build). */
@@ -257,6 +258,30 @@ mesa_status mesa_decode_step_warm(const void *q, const void *k, const void *v, i
 mesa_status mesa_qk_preprocess(const void *x, int in_dtype, const float *conv_w, int width,
                                const void *hist, void *hist_out, int B, int H, int T, int d,
                                void *y, int out_dtype, void *stream);
+
+/*
+ * Recurrence of the Hawk layer that the hybrid "Hawk-Mesa" model alternates
+ * with Mesa layers (section "Arquitetura (MesaNet)", bullet "Variante
+ * Hibrida": LRU (Hawk) layers).  The page names the layer only; this is
+ * Hawk's published real-gated linear recurrent unit, per channel d:
+ *   r_t = sigmoid(ga_t),  i_t = sigmoid(gx_t),  a_t = sigmoid(lam_d)^(c r_t)
+ *   h_t = a_t h_{t-1} + sqrt(1 - a_t^2) i_t x_t,   y_t = h_t
+ * The gate pre-activations come from the layer's input projections, which are
+ * plain matrix products outside this call.
+ *
+ *   x, ga, gx [B, T, D]       in_dtype (mesa_dtype)
+ *   lam       [D]             float32
+ *   c                         the gate's exponent scale (Hawk uses 8)
+ *   h0        [B, D]          float32 state before t = 0, or NULL for zeros
+ *   y         [B, T, D]       float32, written
+ *   h_final   [B, D]          float32 state after the last token, or NULL
+ *   workspace, workspace_bytes  at least mesa_hawk_workspace_bytes(B, T, D)
+ * T >= 0; y must not alias the inputs.
+ */
+size_t mesa_hawk_workspace_bytes(int B, int T, int D);
+mesa_status mesa_hawk_scan(const void *x, const void *ga, const void *gx, int in_dtype, const float *lam,
+                           float c, const float *h0, int B, int T, int D, float *y, float *h_final,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Optional per-kernel timing (not part of the method).  While enabled, each

@@ -16,7 +16,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmesa.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 SOURCES = ["mesa_host.hip", "chunk_states.hip", "cg_output.hip", "decode.hip", "qk_preprocess.hip",
-           "bwd_adjoint.hip", "bwd_states.hip", "bwd_kv.hip", "bwd_gate.hip", "probes.hip"]
+           "bwd_adjoint.hip", "bwd_states.hip", "bwd_kv.hip", "bwd_gate.hip", "hawk.hip", "probes.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

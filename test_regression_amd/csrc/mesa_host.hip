@@ -401,6 +401,53 @@ mesa_status mesa_qk_preprocess(const void* x, int in_dtype, const float* conv_w,
     return MESA_OK;
 }
 
+size_t mesa_hawk_workspace_bytes(int B, int T, int D) {
+    if (B <= 0 || T < 0 || D <= 0) return 0;
+    const size_t nc = ((size_t)T + mesa::kHawkChunk - 1) / mesa::kHawkChunk;
+    return 2 * (size_t)B * nc * D * sizeof(float);
+}
+
+mesa_status mesa_hawk_scan(const void* x, const void* ga, const void* gx, int in_dtype, const float* lam, float c,
+                           const float* h0, int B, int T, int D, float* y, float* h_final, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    if (in_dtype != MESA_DTYPE_F32 && in_dtype != MESA_DTYPE_BF16)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "in_dtype %d is not MESA_DTYPE_F32 or MESA_DTYPE_BF16", in_dtype);
+    if (B <= 0 || T < 0 || D <= 0)
+        return fail(MESA_ERR_INVALID_ARGUMENT, "sizes must be positive, T >= 0 (B=%d T=%d D=%d)", B, T, D);
+    if (!(c >= 0.0f) || std::isinf(c)) return fail(MESA_ERR_INVALID_ARGUMENT, "c must be finite and >= 0");
+    if (!lam || (T > 0 && (!x || !ga || !gx || !y || !workspace)))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "lam, and x, ga, gx, y and workspace when T > 0, must be non-null");
+    const size_t esz = in_dtype == MESA_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(ga, esz) || !aligned(gx, esz) || !aligned(lam, 4) || !aligned(h0, 4) ||
+        !aligned(y, 4) || !aligned(h_final, 4) || !aligned(workspace, 16))
+        return fail(MESA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    if (y && (y == x || y == ga || y == gx)) return fail(MESA_ERR_INVALID_ARGUMENT, "y must not alias the inputs");
+    const long nc = ((long)T + mesa::kHawkChunk - 1) / mesa::kHawkChunk;
+    if ((long)B * nc * D > 0x7fffffffL * 256L) return fail(MESA_ERR_INVALID_ARGUMENT, "grid too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        // no token: the final state is the initial one
+        hipError_t e = hipSuccess;
+        if (h_final) {
+            e = h0 ? hipMemcpyAsync(h_final, h0, (size_t)B * D * sizeof(float), hipMemcpyDeviceToDevice, s)
+                   : zero_fill(h_final, (size_t)B * D * sizeof(float), s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "Hawk final state for T = 0");
+        return MESA_OK;
+    }
+    if (workspace_bytes < mesa_hawk_workspace_bytes(B, T, D))
+        return fail(MESA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
+                    mesa_hawk_workspace_bytes(B, T, D));
+    float* ws = static_cast<float*>(workspace);
+    const size_t per = (size_t)B * nc * D;
+    mesa::HawkArgs a{x, ga, gx, lam, c, h0, B, T, D, (int)nc, in_dtype == MESA_DTYPE_BF16, ws, ws + per, y,
+                     h_final};
+    hipError_t e = timed_launch(MESA_KERNEL_HAWK, s, [&] { return mesa::launch_hawk(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "Hawk scan kernel launch");
+    return MESA_OK;
+}
+
 mesa_status mesa_profile_enable(int on) {
     std::lock_guard<std::mutex> g(g_prof_mu);
     g_prof_on = on != 0;
@@ -451,6 +498,7 @@ const char* mesa_kernel_name(int kernel_id) {
         case MESA_KERNEL_BWD_STATES: return "bwd_states_kernel";
         case MESA_KERNEL_BWD_KV: return "bwd_kv_kernel";
         case MESA_KERNEL_BWD_GATE: return "bwd_gate_kernel";
+        case MESA_KERNEL_HAWK: return "hawk_kernels";
     }
     return "unknown";
 }

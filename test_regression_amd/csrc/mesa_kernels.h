@@ -72,6 +72,16 @@ hipError_t launch_bwd_adjoint(const BwdAdjointArgs& a, hipStream_t s);
 hipError_t launch_bwd_states(const BwdStatesArgs& a, hipStream_t s);
 hipError_t launch_bwd_kv(const BwdKvArgs& a, hipStream_t s);
 hipError_t launch_bwd_gate(const BwdGateArgs& a, hipStream_t s);
+// Hawk layer recurrence (hawk.hip): two-pass chunked scan.
+constexpr int kHawkChunk = 256;   // tokens per chunk of the scan
+struct HawkArgs {
+    const void* x; const void* ga; const void* gx; const float* lam; float c; const float* h0;
+    int B; int T; int D; int nc; int bf16;
+    float* Plog; float* S;   // workspace: per (sequence, chunk, channel) log decay product, end state
+    float* y; float* h_final;
+};
+hipError_t launch_hawk(const HawkArgs& a, hipStream_t s);
+
 hipError_t launch_cg_output(const CgOutputArgs& a, hipStream_t s);
 hipError_t launch_qk_preprocess(const QkPreArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

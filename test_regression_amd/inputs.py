@@ -196,3 +196,18 @@ def preprocess_inputs(B: int, H: int, T: int, d: int, W: int, dtype: str, seed: 
     w = (rng.standard_normal((H, W, d)) / np.sqrt(W)).astype(np.float32)
     hist = rng.standard_normal((B, H, W - 1, d)) if with_hist else None
     return dict(x=_store(x, dtype), w=w, hist=None if hist is None else _store(hist, dtype))
+
+
+def hawk_inputs(B: int, T: int, D: int, dtype: str, seed: int, c: float = 8.0, with_h0: bool = False):
+    """Inputs of the Hawk layer's recurrence: x, ga, gx [B,T,D] ~ N(0, 1) in the
+    storage dtype; lam [D] float32 with sigmoid(lam)^c ~ U(0.9, 0.999) (slow to
+    moderate decays); h0 [B,D] N(0, 1) or None.  Draw order: x, ga, gx, lam, h0.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, T, D))
+    ga = rng.standard_normal((B, T, D))
+    gx = rng.standard_normal((B, T, D))
+    s = rng.uniform(0.9, 0.999, size=D) ** (1.0 / c)
+    lam = np.log(s / (1.0 - s)).astype(np.float32)
+    h0 = rng.standard_normal((B, D)).astype(np.float32) if with_h0 else None
+    return dict(x=_store(x, dtype), ga=_store(ga, dtype), gx=_store(gx, dtype), lam=lam, h0=h0)

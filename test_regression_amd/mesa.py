@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmesa.so")
 MESA_OK, MESA_ERR_INVALID_ARGUMENT, MESA_ERR_UNSUPPORTED, MESA_ERR_WORKSPACE_TOO_SMALL, MESA_ERR_HIP = range(5)
 MESA_DTYPE_F32, MESA_DTYPE_BF16 = 0, 1
 KERNEL_CHUNK_STATES, KERNEL_CG_OUTPUT, KERNEL_DECODE, KERNEL_QK_PREPROCESS = 0, 1, 2, 3
-KERNEL_BWD_ADJOINT, KERNEL_BWD_STATES, KERNEL_BWD_KV, KERNEL_BWD_GATE = 4, 5, 6, 7
+KERNEL_BWD_ADJOINT, KERNEL_BWD_STATES, KERNEL_BWD_KV, KERNEL_BWD_GATE, KERNEL_HAWK = 4, 5, 6, 7, 8
 MESA_WARM_COLD, MESA_WARM_PREVIOUS, MESA_WARM_PROJECTED = 0, 1, 2
 
 # Every symbol include/mesa.h declares, with its ctypes signature.
@@ -38,6 +38,8 @@ SIGNATURES = {
     "mesa_decode_step_warm": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                _P, _P, _P], _I),
     "mesa_qk_preprocess": ([_P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
+    "mesa_hawk_workspace_bytes": ([_I, _I, _I], _Z),
+    "mesa_hawk_scan": ([_P, _P, _P, _I, _P, _F, _P, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "mesa_profile_enable": ([_I], _I),
     "mesa_profile_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "mesa_profile_reset": ([], _I),
@@ -315,6 +317,33 @@ def mesa_qk_preprocess(x, conv_w, hist=None, *, out_dtype=None, out=None, return
                                   B, H, T, d, _ptr(out), _qkv_dtype(out), _stream(stream))
     _check(st, "mesa_qk_preprocess")
     return (out, hist_out) if return_hist else out
+
+
+def mesa_hawk_scan(x, ga, gx, lam, c=8.0, h0=None, *, out=None, return_final=False, workspace=None,
+                   stream=None):
+    """The Hawk layer's gated linear recurrence (see include/mesa.h, mesa_hawk_scan).
+
+    x, ga, gx: [B,T,D] float32 or bfloat16 (same dtype); lam: [D] float32;
+    h0: [B,D] float32 or None.  Returns y [B,T,D] float32 (and h_final [B,D]).
+    """
+    import torch
+    B, T, D = x.shape
+    dev = x.device
+    for t, n in ((x, "x"), (ga, "ga"), (gx, "gx")):
+        _need(t, n, x.dtype, dev)
+    _need(lam, "lam", torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    hf = torch.empty((B, D), dtype=torch.float32, device=dev) if return_final else None
+    nbytes = int(lib().mesa_hawk_workspace_bytes(B, T, D))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    st = lib().mesa_hawk_scan(_ptr(x), _ptr(ga), _ptr(gx), _qkv_dtype(x), _ptr(lam), float(c), _ptr(h0), B, T, D,
+                              _ptr(out), _ptr(hf), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "mesa_hawk_scan")
+    return (out, hf) if return_final else out
 
 
 def profile_enable(on: bool = True):

@@ -48,6 +48,7 @@ def test_version_and_status_strings():
     assert [mesa.kernel_name(i) for i in range(8)] == [
         "chunk_states_kernel", "cg_output_kernel", "decode_kernel", "qk_preprocess_kernel", "bwd_adjoint_kernel",
         "bwd_states_kernel", "bwd_kv_kernel", "bwd_gate_kernel"]
+    assert mesa.kernel_name(8) == "hawk_kernels"
 
 
 def test_workspace_bytes():
@@ -261,6 +262,41 @@ def test_forward_train_requires_x_out():
     assert st == INVALID and "x_out" in L.mesa_last_error_message().decode()
 
 
+def hawk(**kw):
+    a = dict(x=FAKE, ga=FAKE, gx=FAKE, dt=0, lam=FAKE, c=8.0, h0=None, B=2, T=100, D=64, y=FAKE + 65536, hf=None,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    L = mesa.lib()
+    st = L.mesa_hawk_scan(a["x"], a["ga"], a["gx"], a["dt"], a["lam"], ctypes.c_float(a["c"]), a["h0"], a["B"],
+                          a["T"], a["D"], a["y"], a["hf"], a["ws"], a["ws_bytes"], a["stream"])
+    return st, L.mesa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), INVALID, "non-null"),
+    (dict(lam=None), INVALID, "non-null"),
+    (dict(ws=None), INVALID, "non-null"),
+    (dict(dt=3), INVALID, "in_dtype"),
+    (dict(B=0), INVALID, "positive"),
+    (dict(T=-2), INVALID, "T >= 0"),
+    (dict(c=-1.0), INVALID, "c must"),
+    (dict(c=float("nan")), INVALID, "c must"),
+    (dict(x=FAKE + 2), INVALID, "misaligned"),
+    (dict(y=FAKE), INVALID, "alias"),
+    (dict(ws_bytes=16), WS_SMALL, "workspace"),
+])
+def test_hawk_rejects_bad_arguments(kw, status, needle):
+    st, msg = hawk(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_hawk_workspace_bytes():
+    f = mesa.lib().mesa_hawk_workspace_bytes
+    assert f(2, 257, 64) == 2 * 2 * 2 * 64 * 4     # two chunks of 256 tokens
+    assert f(1, 0, 8) == 0 and f(0, 5, 8) == 0
+
+
 def test_probe_argument_validation():
     L = mesa.lib()
     assert L.mesa_probe_mfma_f32(0, 10, FAKE, None) == INVALID
@@ -275,7 +311,7 @@ def test_profile_api_host_paths():
     L = mesa.lib()
     ms = ctypes.c_double(-1)
     n = ctypes.c_int64(-1)
-    assert L.mesa_profile_read(8, ctypes.byref(ms), ctypes.byref(n)) == INVALID
+    assert L.mesa_profile_read(9, ctypes.byref(ms), ctypes.byref(n)) == INVALID
     assert L.mesa_profile_read(-1, ctypes.byref(ms), ctypes.byref(n)) == INVALID
     assert L.mesa_profile_read(0, None, ctypes.byref(n)) == INVALID
     assert L.mesa_profile_reset() == OK
