@@ -7,7 +7,7 @@
 // unit, per channel d with gate pre-activations ga, gx:
 //   r_t = sigmoid(ga_t),  i_t = sigmoid(gx_t),  log a_t = -c softplus(-lam_d) r_t
 //   h_t = a_t h_{t-1} + sqrt(1 - a_t^2) i_t x_t
-// (sqrt(1 - a^2) is evaluated as sqrt(-expm1(2 log a)), accurate for a near 1).
+// (1 - a^2 = 1 - e^{2 log a} is evaluated without cancellation for a near 1).
 //
 // It is HBM-bound and sequential in t, so it runs as a two-pass chunked
 // scan that keeps every channel's chunks busy at once: pass 1 reduces each
@@ -26,24 +26,32 @@ constexpr int kHawkUnroll = 8;
 __device__ __forceinline__ float hawk_softplus(float z) { return z > 20.f ? z : log1pf(__expf(z)); }
 __device__ __forceinline__ float hawk_sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
-// One step's decay (as its log) and input term.
+// One step's decay (as its log and value) and input term.  1 - a^2 is the
+// short Taylor series of 1 - e^{2 log a} where the subtraction would cancel
+// (2 log a > -1/16: the first dropped term is below 2^-24 relative), and
+// 1 - a*a elsewhere (a < 0.97, so 1 - a*a > 0.06 keeps ~23 bits).
 template <typename In>
-__device__ __forceinline__ void hawk_step(In xv, In gav, In gxv, float csp, float& loga, float& u) {
+__device__ __forceinline__ void hawk_step(In xv, In gav, In gxv, float csp, float& loga, float& a, float& u) {
     const float r = hawk_sigmoid(to_f32(gav));
     const float i = hawk_sigmoid(to_f32(gxv));
     loga = -csp * r;
-    u = sqrtf(-expm1f(2.0f * loga)) * (i * to_f32(xv));
+    a = __expf(loga);
+    const float z = 2.0f * loga;
+    const float taylor = -z * (1.f + z * (0.5f + z * (1.f / 6.f + z * (1.f / 24.f + z * (1.f / 120.f)))));
+    const float oma = z > -0.0625f ? taylor : 1.f - a * a;
+    u = sqrtf(oma) * (i * to_f32(xv));
 }
 
 template <typename In>
 __global__ __launch_bounds__(256) void hawk_summary_kernel(const In* __restrict__ x, const In* __restrict__ ga,
                                                            const In* __restrict__ gx, const float* __restrict__ lam,
-                                                           float c, int T, int D, int nc, long n_threads,
-                                                           float* __restrict__ Plog, float* __restrict__ S) {
+                                                           float c, int T, int D, int d0, int Dn, int nc,
+                                                           long n_threads, float* __restrict__ Plog,
+                                                           float* __restrict__ S) {
     const long g = (long)blockIdx.x * 256 + threadIdx.x;
     if (g >= n_threads) return;
-    const int d = (int)(g % D);
-    const long rem = g / D;
+    const int d = d0 + (int)(g % Dn);
+    const long rem = g / Dn;
     const int ch = (int)(rem % nc);
     const long b = rem / nc;
     const int t0 = ch * kHawkChunk, t1 = min(T, t0 + kHawkChunk);
@@ -61,43 +69,56 @@ __global__ __launch_bounds__(256) void hawk_summary_kernel(const In* __restrict_
         }
 #pragma unroll
         for (int u = 0; u < kHawkUnroll; ++u) {
-            float la, v;
-            hawk_step(xr[u], ar[u], gr[u], csp, la, v);
-            h = __expf(la) * h + v;
+            float la, av, v;
+            hawk_step(xr[u], ar[u], gr[u], csp, la, av, v);
+            h = av * h + v;
             lsum += la;
         }
         i += (size_t)kHawkUnroll * D;
     }
     for (; t < t1; ++t, i += D) {
-        float la, v;
-        hawk_step(x[i], ga[i], gx[i], csp, la, v);
-        h = __expf(la) * h + v;
+        float la, av, v;
+        hawk_step(x[i], ga[i], gx[i], csp, la, av, v);
+        h = av * h + v;
         lsum += la;
     }
-    Plog[g] = lsum;   // log of the chunk's decay product
-    S[g] = h;         // the chunk's end state from zero
+    const size_t j = ((size_t)b * nc + ch) * D + d;
+    Plog[j] = lsum;   // log of the chunk's decay product
+    S[j] = h;         // the chunk's end state from zero
 }
 
 template <typename In>
 __global__ __launch_bounds__(256) void hawk_scan_kernel(const In* __restrict__ x, const In* __restrict__ ga,
                                                         const In* __restrict__ gx, const float* __restrict__ lam,
-                                                        float c, const float* __restrict__ h0, int T, int D, int nc,
-                                                        long n_threads, const float* __restrict__ Plog,
-                                                        const float* __restrict__ S, float* __restrict__ y,
-                                                        float* __restrict__ h_final) {
+                                                        float c, const float* __restrict__ h0, int T, int D, int d0,
+                                                        int Dn, int nc, long n_threads,
+                                                        const float* __restrict__ Plog, const float* __restrict__ S,
+                                                        float* __restrict__ y, float* __restrict__ h_final) {
     const long g = (long)blockIdx.x * 256 + threadIdx.x;
     if (g >= n_threads) return;
-    const int d = (int)(g % D);
-    const long rem = g / D;
+    const int d = d0 + (int)(g % Dn);
+    const long rem = g / Dn;
     const int ch = (int)(rem % nc);
     const long b = rem / nc;
     const int t0 = ch * kHawkChunk, t1 = min(T, t0 + kHawkChunk);
     const float csp = c * hawk_softplus(-lam[d]);
-    // the chunk's start state: fold the earlier chunks' (P, s) in order
+    // the chunk's start state: fold the earlier chunks' (P, s) in order,
+    // eight summaries requested at a time
     float h = h0 ? h0[b * D + d] : 0.f;
-    for (int cc = 0; cc < ch; ++cc) {
-        const size_t j = ((size_t)b * nc + cc) * D + d;
-        h = __expf(Plog[j]) * h + S[j];
+    {
+        const size_t j0 = (size_t)b * nc * D + d;
+        int cc = 0;
+        for (; cc + 8 <= ch; cc += 8) {
+            float pl[8], sv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                pl[u] = Plog[j0 + (size_t)(cc + u) * D];
+                sv[u] = S[j0 + (size_t)(cc + u) * D];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) h = __expf(pl[u]) * h + sv[u];
+        }
+        for (; cc < ch; ++cc) h = __expf(Plog[j0 + (size_t)cc * D]) * h + S[j0 + (size_t)cc * D];
     }
     size_t i = ((size_t)b * T + t0) * D + d;
     int t = t0;
@@ -111,17 +132,17 @@ __global__ __launch_bounds__(256) void hawk_scan_kernel(const In* __restrict__ x
         }
 #pragma unroll
         for (int u = 0; u < kHawkUnroll; ++u) {
-            float la, v;
-            hawk_step(xr[u], ar[u], gr[u], csp, la, v);
-            h = __expf(la) * h + v;
+            float la, av, v;
+            hawk_step(xr[u], ar[u], gr[u], csp, la, av, v);
+            h = av * h + v;
             y[i + (size_t)u * D] = h;
         }
         i += (size_t)kHawkUnroll * D;
     }
     for (; t < t1; ++t, i += D) {
-        float la, v;
-        hawk_step(x[i], ga[i], gx[i], csp, la, v);
-        h = __expf(la) * h + v;
+        float la, av, v;
+        hawk_step(x[i], ga[i], gx[i], csp, la, av, v);
+        h = av * h + v;
         y[i] = h;
     }
     if (h_final && ch == nc - 1) h_final[b * D + d] = h;
@@ -132,11 +153,11 @@ static hipError_t launch_t(const HawkArgs& a, hipStream_t s) {
     const long n = (long)a.B * a.nc * a.D;
     const unsigned blocks = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL((hawk_summary_kernel<In>), dim3(blocks), dim3(256), 0, s, (const In*)a.x, (const In*)a.ga,
-                       (const In*)a.gx, a.lam, a.c, a.T, a.D, a.nc, n, a.Plog, a.S);
+                       (const In*)a.gx, a.lam, a.c, a.T, a.D, 0, a.D, a.nc, n, a.Plog, a.S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((hawk_scan_kernel<In>), dim3(blocks), dim3(256), 0, s, (const In*)a.x, (const In*)a.ga,
-                       (const In*)a.gx, a.lam, a.c, a.h0, a.T, a.D, a.nc, n, a.Plog, a.S, a.y, a.h_final);
+                       (const In*)a.gx, a.lam, a.c, a.h0, a.T, a.D, 0, a.D, a.nc, n, a.Plog, a.S, a.y, a.h_final);
     return hipGetLastError();
 }
 

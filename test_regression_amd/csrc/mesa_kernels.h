@@ -73,7 +73,10 @@ hipError_t launch_bwd_states(const BwdStatesArgs& a, hipStream_t s);
 hipError_t launch_bwd_kv(const BwdKvArgs& a, hipStream_t s);
 hipError_t launch_bwd_gate(const BwdGateArgs& a, hipStream_t s);
 // Hawk layer recurrence (hawk.hip): two-pass chunked scan.
-constexpr int kHawkChunk = 256;   // tokens per chunk of the scan
+#ifndef MESA_HAWK_CHUNK
+#define MESA_HAWK_CHUNK 128
+#endif
+constexpr int kHawkChunk = MESA_HAWK_CHUNK;   // tokens per chunk of the scan
 struct HawkArgs {
     const void* x; const void* ga; const void* gx; const float* lam; float c; const float* h0;
     int B; int T; int D; int nc; int bf16;

@@ -293,7 +293,7 @@ def test_hawk_rejects_bad_arguments(kw, status, needle):
 
 def test_hawk_workspace_bytes():
     f = mesa.lib().mesa_hawk_workspace_bytes
-    assert f(2, 257, 64) == 2 * 2 * 2 * 64 * 4     # two chunks of 256 tokens
+    assert f(2, 257, 64) == 2 * 2 * 3 * 64 * 4     # three chunks of 128 tokens
     assert f(1, 0, 8) == 0 and f(0, 5, 8) == 0
 
 
