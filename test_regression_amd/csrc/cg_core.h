@@ -314,15 +314,39 @@ __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<
     return it;
 }
 
-// Stage the packed upper block triangle of S^H (blocks (a, b), a <= b, in
-// row-major block order, each block row-major) into L.R; workgroup-wide.
+// Stage the stored upper block triangle of S^H (blocks (a, b), a <= b, in
+// row-major block order, each block in accumulator order) into L.R as
+// row-major blocks of pitch kBlockPitch; workgroup-wide.
 template <int D, int C>
 __device__ __forceinline__ void stage_packed_state(CgLds<D, C>& L, const float* __restrict__ SHc, int tid,
                                                    int nthr) {
     constexpr int HPACK = D * (D + 16) / 2;
-    for (int e = tid * 4; e < HPACK; e += nthr * 4)
-        *reinterpret_cast<f32x4*>(&L.R[(e / 256) * 16 * kBlockPitch + ((e % 256) / 16) * kBlockPitch + e % 16]) =
-            *reinterpret_cast<const f32x4*>(SHc + e);
+    for (int e = tid * 4; e < HPACK; e += nthr * 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(SHc + e);   // rows 4kk..4kk+3 of column n
+        const int l = (e % 256) / 4, kk = l / 16, n = l % 16;
+        float* dst = &L.R[(e / 256) * 16 * kBlockPitch + (4 * kk) * kBlockPitch + n];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[r * kBlockPitch] = v[r];
+    }
+}
+
+// Stage a stored full d x d state (all 16 x 16 blocks, row-major block order,
+// accumulator order inside) into LDS rows of pitch `pitch`, or transposed
+// (element (row, col) to dst[col * pitch + row]) when TRANSPOSE; workgroup-wide.
+template <int D, bool TRANSPOSE>
+__device__ __forceinline__ void stage_tiled_state(float* dst, int pitch, const float* __restrict__ src, int tid,
+                                                  int nthr) {
+    constexpr int NT = D / 16;
+    for (int e = tid * 4; e < D * D; e += nthr * 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
+        const int b = e / 256, l = (e % 256) / 4;
+        const int row = 16 * (b / NT) + 4 * (l / 16), col = 16 * (b % NT) + l % 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (TRANSPOSE) dst[col * pitch + row + r] = v[r];
+            else dst[(row + r) * pitch + col] = v[r];
+        }
+    }
 }
 
 // Stage a chunk's rows of a [*, D] tensor as rows (pitch lds_pitch(D)) and/or

@@ -88,8 +88,7 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
             for (int r = 0; r < 4; ++r) Wo[ib][r] = Sc[ib][r] * cw.dec[ib][r];
     }
     __syncthreads();   // every wave is done with the states, K_c and K_c^T
-    for (int e = tid * 4; e < D * D; e += NTHR * 4)
-        *reinterpret_cast<f32x4*>(&L.R[(e / D) * PS + e % D]) = *reinterpret_cast<const f32x4*>(Gc + e);
+    stage_tiled_state<D, false>(L.R, PS, Gc, tid, NTHR);
     stage_chunk_rows<D, C, false, true>(nullptr, L.KT, v + tok0 * D, valid, tid, NTHR);
     __syncthreads();
     f32x4 OS[NT], OI[NT], none[1];

@@ -12,10 +12,11 @@
 // chunk (the state before the chunk's first token) and, optionally, the final
 // state after the last token.
 //
-// Chunk states in the workspace: G row-major ([d_v][d_k], the layout of the
-// exported final G); H, which is symmetric, as its packed upper triangle of
-// 16 x 16 blocks (block (a, b), a <= b, in row-major block order, each block
-// row-major) -- the part the CG kernel reads.  The exported final H is full.
+// Chunk states in the workspace: G as all its 16 x 16 blocks, H (symmetric)
+// as the upper triangle of them -- the part the CG kernel reads -- each in
+// row-major block order, each block in MFMA accumulator order (tile_offset),
+// so a wave stores a block as one 16-byte piece per lane.  The exported final
+// states are full and row-major ([d_v][d_k] for G).
 //
 // Work split: one workgroup per (head, {H, G}, 16*NW-row block of the
 // state); each wave holds a 16 x D slab of the running state in MFMA
@@ -155,18 +156,14 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
 
         // ---- the state before this chunk ----
         if (write_chunks) {
-            float* dst = Sout + (size_t)c * (which == 0 ? HPACK : D * D);
+            // one 16-byte piece per lane per 16 x 16 block (accumulator order)
+            float* dst = Sout + (size_t)c * (which == 0 ? HPACK : D * D) + (kk * 16 + n) * 4;
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 if (which == 0) {
-                    if (j >= a0) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            dst[packed_blk<NT>(a0, j) + (4 * kk + r) * 16 + n] = acc[j][r];
-                    }
+                    if (j >= a0) *reinterpret_cast<f32x4*>(dst + packed_blk<NT>(a0, j)) = acc[j];
                 } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+                    *reinterpret_cast<f32x4*>(dst + (a0 * NT + j) * 256) = acc[j];
                 }
             }
         }

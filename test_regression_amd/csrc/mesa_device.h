@@ -28,6 +28,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __host__ __device__ constexpr int lds_pitch(int n) { return ((n + 63) / 64) * 64 + 4; }
 __host__ __device__ constexpr int lds_pitch_rows(int n) { return ((n + 63) / 64) * 64 + 8; }
 
+// Chunk states in the forward workspace are stored as 16 x 16 blocks of 256
+// floats, each block in MFMA accumulator order: lane 16*kk + n of a wave
+// holds rows 4kk..4kk+3 of column n, as four consecutive floats.  So the
+// chunk-state kernel stores a block as one 16-byte piece per lane (1 KiB
+// contiguous per wave), and readers place element (row, col) of a block
+// from offset tile_offset(row, col).
+__host__ __device__ constexpr int tile_offset(int row, int col) { return ((row >> 2) * 16 + col) * 4 + (row & 3); }
+
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
