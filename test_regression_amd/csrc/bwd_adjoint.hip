@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_adjoint_kernel(
     const size_t soff = ((size_t)bh * n_chunks + c) * D * D;
 
     // ---- phase 1: (S^G_c)^T as rows, V_c rows, K_c^T, lambda, l ----
-    stage_tiled_state<D, true>(L.R, PS, SG + soff, tid, NTHR);
+    stage_g_state_transposed<D>(L.R, PS, SG + soff, tid, NTHR);
     stage_chunk_rows<D, C, true, false>(L.KV, nullptr, v + tok0 * D, valid, tid, NTHR);
     stage_chunk_rows<D, C, false, true>(nullptr, L.KT, k + tok0 * D, valid, tid, NTHR);
     for (int e = tid; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)h * D + e];

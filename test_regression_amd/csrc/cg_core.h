@@ -34,7 +34,7 @@ struct alignas(16) CgLds {
     static constexpr int PS = lds_pitch_rows(D);
     static constexpr int PT = lds_pitch_rows(C);
     static constexpr int REGION = NSTATE * HALF > D * PS ? NSTATE * HALF : D * PS;
-    float R[REGION];          // CG: stored S^H_c [, S_mid];  output: G_c full [D][PS]
+    float R[REGION];          // CG: stored S^H_c [, S_mid];  adjoint right side: (S^G_c)^T [D][PS]
     float KV[C * PD];         // K_c rows [token][feature]
     float KT[D * PT];         // K_c^T, later V_c^T   [feature][token]
     float L[C];               // l_i
@@ -330,24 +330,50 @@ __device__ __forceinline__ void stage_packed_state(CgLds<D, C>& L, const float* 
     }
 }
 
-// Stage a stored full d x d state (all 16 x 16 blocks, row-major block order,
-// accumulator order inside) into LDS rows of pitch `pitch`, or transposed
-// (element (row, col) to dst[col * pitch + row]) when TRANSPOSE; workgroup-wide.
-template <int D, bool TRANSPOSE>
-__device__ __forceinline__ void stage_tiled_state(float* dst, int pitch, const float* __restrict__ src, int tid,
-                                                  int nthr) {
+// Stage a stored G chunk state (all 16 x 16 blocks, row-major block order,
+// MFMA operand order inside) into LDS transposed: element (row, col) to
+// dst[col * pitch + row]; workgroup-wide.
+template <int D>
+__device__ __forceinline__ void stage_g_state_transposed(float* dst, int pitch, const float* __restrict__ src,
+                                                         int tid, int nthr) {
     constexpr int NT = D / 16;
     for (int e = tid * 4; e < D * D; e += nthr * 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);   // columns 4q..4q+3 of row m
         const int b = e / 256, l = (e % 256) / 4;
-        const int row = 16 * (b / NT) + 4 * (l / 16), col = 16 * (b % NT) + l % 16;
+        const int row = 16 * (b / NT) + l % 16, col = 16 * (b % NT) + 4 * (l / 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if constexpr (TRANSPOSE) dst[col * pitch + row + r] = v[r];
-            else dst[(row + r) * pitch + col] = v[r];
-        }
+        for (int r = 0; r < 4; ++r) dst[(col + r) * pitch + row] = v[r];
     }
 }
+
+// A chunk's rows of a [*, D] tensor held in registers between their global
+// load and their transposed store to LDS (pitch lds_pitch_rows(C)), so the
+// loads can be issued before the LDS tile is free; rows past `valid` are zero.
+template <int D, int C, int NTHR, typename In>
+struct ChunkRowsRegs {
+    static constexpr int EL4 = C * D / (4 * NTHR);
+    static_assert(C * D % (4 * NTHR) == 0, "tile must split evenly over the workgroup");
+    Raw4<In> x[EL4];   // bf16 stays packed until stored
+    __device__ __forceinline__ void load(const In* __restrict__ src, int valid, int tid) {
+#pragma unroll
+        for (int u = 0; u < EL4; ++u) {
+            const int e = (tid + u * NTHR) * 4;
+            const int i = e / D, f = e % D;
+            x[u].zero();
+            if (i < valid) x[u].load(src + (size_t)i * D + f);
+        }
+    }
+    __device__ __forceinline__ void store_transposed(float* tr, int tid) const {
+        constexpr int PT = lds_pitch_rows(C);
+#pragma unroll
+        for (int u = 0; u < EL4; ++u) {
+            const int e = (tid + u * NTHR) * 4;
+            const int i = e / D, f = e % D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tr[(f + r) * PT + i] = x[u].get()[r];
+        }
+    }
+};
 
 // Stage a chunk's rows of a [*, D] tensor as rows (pitch lds_pitch(D)) and/or
 // transposed (pitch lds_pitch_rows(C)); rows past `valid` are zero.

@@ -55,7 +55,6 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
     constexpr int NT = D / 16;
     constexpr int NW = C / 16;
     constexpr int NBO = CW::NBO;
-    constexpr int PS = lds_pitch_rows(D);
     constexpr int NTHR = 64 * NW;
     const CW cw(L, tid & 63);
     const int n = cw.n, kk = cw.kk, tr = cw.tr;
@@ -76,6 +75,13 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
     }
 
     // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
+    // V_c is loaded into registers now and stored as V_c^T once every wave
+    // is done with K_c^T; the state term takes G_c's blocks straight from
+    // memory (stored in MFMA operand order: this lane's 16 bytes of block
+    // (j, g) are G_c[16j + n][16g + 4kk .. 16g + 4kk + 3]), so it runs
+    // before the barrier, while slower waves still iterate.
+    ChunkRowsRegs<D, C, NTHR, In> vrows;
+    vrows.load(v + tok0 * D, valid, tid);
     f32x4 Wo[NBO];
     {
         f32x4 Sc[NBO], unused[NT];
@@ -87,14 +93,30 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
 #pragma unroll
             for (int r = 0; r < 4; ++r) Wo[ib][r] = Sc[ib][r] * cw.dec[ib][r];
     }
-    __syncthreads();   // every wave is done with the states, K_c and K_c^T
-    stage_tiled_state<D, false>(L.R, PS, Gc, tid, NTHR);
-    stage_chunk_rows<D, C, false, true>(nullptr, L.KT, v + tok0 * D, valid, tid, NTHR);
-    __syncthreads();
-    f32x4 OS[NT], OI[NT], none[1];
+    f32x4 OS[NT], OI[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) OS[j] = OI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    contract_rows<D, 0, true>(X, L.R, nullptr, n, kk, OS, none);
+    {
+        const float* gl = Gc + 4 * (tid & 63);
+        f32x4 ga[3][NT];
+        auto gload = [&](int g, int buf) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) ga[buf][j] = *reinterpret_cast<const f32x4*>(gl + (j * NT + g) * 256);
+        };
+        gload(0, 0);
+        if (NT > 1) gload(1, 1);
+#pragma unroll
+        for (int g = 0; g < NT; ++g) {
+            if (g + 2 < NT) gload(g + 2, (g + 2) % 3);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) OS[j] = mfma4(ga[g % 3][j][s], X[g][s], OS[j]);
+        }
+    }
+    __syncthreads();   // every wave is done with the states, K_c and K_c^T
+    vrows.store_transposed(L.KT, tid);
+    __syncthreads();
     contract_intra<D, C, NBO, 0>(Wo, L.KT, n, kk, OI);
     if (tok_ok) {
 #pragma unroll

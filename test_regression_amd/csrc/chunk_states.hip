@@ -14,40 +14,26 @@
 //
 // Chunk states in the workspace: G as all its 16 x 16 blocks, H (symmetric)
 // as the upper triangle of them -- the part the CG kernel reads -- each in
-// row-major block order, each block in MFMA accumulator order (tile_offset),
-// so a wave stores a block as one 16-byte piece per lane.  The exported final
-// states are full and row-major ([d_v][d_k] for G).
+// row-major block order, so a wave stores a block as one 16-byte piece per
+// lane (1 KiB contiguous per wave).  An H block is kept in MFMA accumulator
+// order (lane 16q + m holds rows 4q..4q+3 of column m); a G block in MFMA
+// operand order (lane 16q + m holds columns 4q..4q+3 of row m), which is the
+// A operand the CG kernel's output product takes straight from memory.  The
+// exported final states are full and row-major ([d_v][d_k] for G).
 //
 // Work split: one workgroup per (head, {H, G}, 16*NW-row block of the
-// state); each wave holds a 16 x D slab of the running state in MFMA
-// accumulator layout and walks the chunks in order.  Per chunk the update is
-// one (16 x C) x (C x D) product on v_mfma_f32_16x16x4_f32 with the weighted
-// rows (keys for H, values for G) as the A operand and the keys as the B
-// operand; the contraction runs over the chunk's tokens.  Workgroup ids are
+// state); each wave holds a 16 x D slab of the running state (of H, or of
+// G^T: 16 key features by all value features) in MFMA accumulator layout
+// and walks the chunks in order.  Per chunk the update is one
+// (16 x C) x (C x D) product on v_mfma_f32_16x16x4_f32 with the weighted keys
+// as the A operand and the keys (H) or values (G^T) as the B operand; the
+// contraction runs over the chunk's tokens.  Workgroup ids are
 // mapped so that the 2*RB workgroups of one head land on the same XCD (ids
 // congruent mod 8) and share its L2 for the key and value tiles.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
 namespace mesa {
-
-// Registers holding 4 prefetched input elements (bf16 stays packed until staged).
-template <typename In> struct Raw4;
-template <> struct Raw4<float> {
-    f32x4 v;
-    __device__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
-    __device__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
-    __device__ f32x4 get() const { return v; }
-};
-template <> struct Raw4<bf16_t> {
-    uint2 v;
-    __device__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-    __device__ void zero() { v = make_uint2(0u, 0u); }
-    __device__ f32x4 get() const {
-        return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
-                     __uint_as_float(v.y & 0xffff0000u)};
-    }
-};
 
 // Offset (floats) of block (a, b), a <= b, in the packed upper block triangle
 // of a d x d state (16 x 16 blocks stored row-major one after another).
@@ -72,8 +58,8 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     constexpr int NTHR = 64 * NW;
     constexpr int HPACK = D * (D + 16) / 2;    // floats of a packed upper block triangle
 
-    __shared__ float sK[C * PD];   // keys of the chunk (B operand; A rows for H)
-    __shared__ float sB[C * PD];   // values of the chunk (A rows for G)
+    __shared__ float sK[C * PD];   // keys of the chunk (A operand; B operand for H)
+    __shared__ float sB[C * PD];   // values of the chunk (B operand for G^T)
     __shared__ float sW[C];        // e^{l_end - l_i}
     __shared__ float sGam;         // e^{l_end}
 
@@ -92,7 +78,7 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     if (bh >= BH) return;                      // whole workgroup: no barrier is skipped
     const int rb = part % RB;
     const int which = part / RB;               // 0: H, 1: G
-    const int m0 = rb * 16 * NW + 16 * w;      // first state row of this wave
+    const int m0 = rb * 16 * NW + 16 * w;      // first state row (of H or G^T) of this wave
     const int a0 = m0 / 16;                    // its row block
 
     const In* kh = k + (size_t)bh * T * D;
@@ -100,7 +86,7 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     const float* gh = gamma + (size_t)bh * T;
     // H: packed upper block triangle per chunk; G: full d x d per chunk
     float* Sout = which == 0 ? SH + (size_t)bh * n_chunks * HPACK : SG + (size_t)bh * n_chunks * D * D;
-    const float* sArows = which == 0 ? sK : sB;
+    const float* sBcols = which == 0 ? sK : sB;
 
     f32x4 acc[NT];
 #pragma unroll
@@ -163,12 +149,13 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
                 if (which == 0) {
                     if (j >= a0) *reinterpret_cast<f32x4*>(dst + packed_blk<NT>(a0, j)) = acc[j];
                 } else {
-                    *reinterpret_cast<f32x4*>(dst + (a0 * NT + j) * 256) = acc[j];
+                    // block (a0, j) of G^T in accumulator order = block (j, a0) of G in operand order
+                    *reinterpret_cast<f32x4*>(dst + (j * NT + a0) * 256) = acc[j];
                 }
             }
         }
 
-        // ---- S <- Gamma_c S + U,  U = sum_i w_i a_i k_i^T ----
+        // ---- S <- Gamma_c S + U,  U = sum_i w_i k_i b_i^T  (b = k for H, v for G^T) ----
         // U is a fresh MFMA chain (started from zero, only read afterwards);
         // the decayed running state is combined with it on the VALU.
         f32x4 U[NT];
@@ -179,9 +166,9 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int i = 16 * g + 4 * kk + s;
-                const float a = sArows[i * PD + m0 + n] * sW[i];
+                const float a = sK[i * PD + m0 + n] * sW[i];
 #pragma unroll
-                for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sK[i * PD + 16 * j + n], U[j]);
+                for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sBcols[i * PD + 16 * j + n], U[j]);
             }
         }
         const float G = sGam;
@@ -198,13 +185,19 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     }
 
     // ---- final state (after the last token) ----
-    float* fin = which == 0 ? final_H : final_G;
-    if (fin) {
-        float* dst = fin + (size_t)bh * D * D;
+    if (which == 0 && final_H) {
+        float* dst = final_H + (size_t)bh * D * D;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+    }
+    if (which == 1 && final_G) {
+        // acc[j][r] = G[16j + n][m0 + 4kk + r]: four consecutive floats of a row of G
+        float* dst = final_G + (size_t)bh * D * D;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            *reinterpret_cast<f32x4*>(dst + (size_t)(16 * j + n) * D + m0 + 4 * kk) = acc[j];
     }
 }
 

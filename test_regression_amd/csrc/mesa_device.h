@@ -29,12 +29,12 @@ __host__ __device__ constexpr int lds_pitch(int n) { return ((n + 63) / 64) * 64
 __host__ __device__ constexpr int lds_pitch_rows(int n) { return ((n + 63) / 64) * 64 + 8; }
 
 // Chunk states in the forward workspace are stored as 16 x 16 blocks of 256
-// floats, each block in MFMA accumulator order: lane 16*kk + n of a wave
-// holds rows 4kk..4kk+3 of column n, as four consecutive floats.  So the
-// chunk-state kernel stores a block as one 16-byte piece per lane (1 KiB
-// contiguous per wave), and readers place element (row, col) of a block
-// from offset tile_offset(row, col).
-__host__ __device__ constexpr int tile_offset(int row, int col) { return ((row >> 2) * 16 + col) * 4 + (row & 3); }
+// floats, 16 bytes per lane of a wave: lane 16q + m holds floats
+// 4(16q + m)..4(16q + m) + 3 of a block.  H blocks are in MFMA accumulator
+// order (those four floats are rows 4q..4q+3 of column m), G blocks in MFMA
+// operand order (columns 4q..4q+3 of row m).
+__host__ __device__ constexpr int acc_tile_offset(int row, int col) { return ((row >> 2) * 16 + col) * 4 + (row & 3); }
+__host__ __device__ constexpr int opnd_tile_offset(int row, int col) { return ((col >> 2) * 16 + row) * 4 + (col & 3); }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -59,6 +59,24 @@ __device__ __forceinline__ f32x4 load4(const bf16_t* p) {
     r[3] = __uint_as_float(u.y & 0xffff0000u);
     return r;
 }
+
+// Registers holding 4 prefetched input elements (bf16 stays packed until staged).
+template <typename In> struct Raw4;
+template <> struct Raw4<float> {
+    f32x4 v;
+    __device__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+    __device__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ f32x4 get() const { return v; }
+};
+template <> struct Raw4<bf16_t> {
+    uint2 v;
+    __device__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ void zero() { v = make_uint2(0u, 0u); }
+    __device__ f32x4 get() const {
+        return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xffff0000u)};
+    }
+};
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
