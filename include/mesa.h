@@ -93,7 +93,8 @@ const char *mesa_last_error_message(void);
  * Bytes of device workspace mesa_forward needs for these sizes: the
  * chunk-boundary states S^H_c = H_{c*chunk-1} (symmetric; its upper triangle
  * of 16x16 blocks, dk (dk + 16) / 2 floats) and S^G_c (dv * dk floats), fp32,
- * per chunk and head.  Returns 0 if the sizes are invalid.
+ * per chunk and head, plus a 256-byte tail (the CG kernel's chunk-claim
+ * counter).  Returns 0 if the sizes are invalid or T == 0.
  */
 size_t mesa_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 
@@ -139,8 +140,9 @@ mesa_status mesa_forward_train(const void *q, const void *k, const void *v, int 
 
 /*
  * Bytes of device workspace mesa_backward needs: the forward chunk states
- * (as mesa_forward_workspace_bytes), two d x d reverse states per chunk and
- * head, two floats per token and d floats per chunk and head.  0 if invalid.
+ * (as mesa_forward_workspace_bytes counts them, without its tail), two
+ * d x d reverse states per chunk and head, two floats per token and d floats
+ * per chunk and head.  0 if invalid.
  */
 size_t mesa_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 

@@ -39,9 +39,17 @@ struct alignas(16) CgLds {
     float KT[D * PT];         // K_c^T, later V_c^T   [feature][token]
     float L[C];               // l_i
     float Lam[D];
+    int next;                 // the forward kernel's claimed next chunk
 };
 
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// An LDS float pointer held as a 32-bit LDS address.
+typedef const __attribute__((address_space(3))) float lds_cfloat;
+
+// Index of stored block (a, b), a <= b, in the packed NT x NT upper block triangle.
+template <int NT>
+__host__ __device__ constexpr int blk_index(int a, int b) { return a * NT - a * (a - 1) / 2 + (b - a); }
 
 // Offset (floats) of stored block (a, b), a <= b, of an NT x NT block triangle.
 template <int NT>
@@ -54,9 +62,12 @@ __host__ __device__ constexpr int blk(int a, int b) {
 // Z: the wave's vectors in registers (lane (n, kk), block g: features 16g + 4kk + s of token n).
 // S[16j + m][16g + 4kk + s] is stored block (j, g) read along row m when j < g,
 // else block (g, j) read down column m (S symmetric).
+// col[blk_index(g, j)]: the lane's column-read address in stored block (g, j).
 template <int D, int NB, int KB0>
-__device__ __forceinline__ void contract_state_scores(const f32x4 (&Z)[D / 16], const float* Sst, const float* Kr,
-                                                      int m, int kk, f32x4 (&Y)[D / 16], f32x4 (&Sc)[NB]) {
+__device__ __forceinline__ void contract_state_scores(const f32x4 (&Z)[D / 16], const float* Sst,
+                                                      lds_cfloat* const (&col)[D / 16 * (D / 16 + 1) / 2],
+                                                      const float* Kr, int m, int kk, f32x4 (&Y)[D / 16],
+                                                      f32x4 (&Sc)[NB]) {
     constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
     f32x4 bs[2][NT], bk[2][NB];
@@ -66,9 +77,9 @@ __device__ __forceinline__ void contract_state_scores(const f32x4 (&Z)[D / 16], 
             if (g > j) {
                 bs[buf][j] = lds4(Sst + blk<NT>(j, g) + m * kBlockPitch + 4 * kk);
             } else {
-                const float* col = Sst + blk<NT>(g, j) + (4 * kk) * kBlockPitch + m;
+                lds_cfloat* c = col[blk_index<NT>(g, j)];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) bs[buf][j][s] = col[s * kBlockPitch];
+                for (int s = 0; s < 4; ++s) bs[buf][j][s] = c[s * kBlockPitch];
             }
         }
 #pragma unroll
@@ -199,14 +210,29 @@ struct CgWave {
     static constexpr int NBO = W + 1;                               // causal key blocks over the chunk
     int n, kk, tr;        // lane's token (B column), k-slot group, chunk token
     float eL, eLo;        // e^{l_t - l_base} (sub-chunk state), e^{l_t} (chunk-start state)
+    static constexpr int NCOL = NT * (NT + 1) / 2;
     float dec[NBO][4];    // e^{l_t - l_i} for key i = 16ib + 4kk + r <= t, else 0
     const float* Sst;     // the stored state the CG uses
+    // Column-read addresses (row 4kk, column n) of the stored blocks.  Each
+    // is passed through an empty asm so that the compiler keeps it in a
+    // register across the CG loop rather than rebuilding it there from a
+    // base and a constant (the 8-bit offsets of two-address LDS reads reach
+    // only 1 KiB).
+    lds_cfloat* col[NCOL];
 
     __device__ __forceinline__ CgWave(const CgLds<D, C>& L, int lane) {
         n = lane & 15;
         kk = lane >> 4;
         tr = 16 * W + n;
         Sst = L.R + SUB * CgLds<D, C>::HALF;
+#pragma unroll
+        for (int a = 0; a < NT; ++a)
+#pragma unroll
+            for (int b = a; b < NT; ++b) {
+                lds_cfloat* c = (lds_cfloat*)(Sst + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n);
+                asm volatile("" : "+v"(c));
+                col[blk_index<NT>(a, b)] = c;
+            }
         const float lbase = SUB ? L.L[16 * KB0 - 1] : 0.f;   // l at the end of the first half
         eL = __expf(L.L[tr] - lbase);
         eLo = __expf(L.L[tr]);
@@ -244,7 +270,7 @@ __device__ __forceinline__ void wave_matvec(const CgLds<D, C>& L, const CgWave<D
     for (int j = 0; j < NT; ++j) YS[j] = YI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ib = 0; ib < CW::NB; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-    contract_state_scores<D, CW::NB, CW::KB0>(P, cw.Sst, L.KV, cw.n, cw.kk, YS, Sc);
+    contract_state_scores<D, CW::NB, CW::KB0>(P, cw.Sst, cw.col, L.KV, cw.n, cw.kk, YS, Sc);
     f32x4 Wt[CW::NB];
 #pragma unroll
     for (int ib = 0; ib < CW::NB; ++ib)
@@ -330,6 +356,34 @@ __device__ __forceinline__ void stage_packed_state(CgLds<D, C>& L, const float* 
     }
 }
 
+// The stored upper block triangle of S^H (as stage_packed_state reads it)
+// held in registers between its global load and its LDS store.
+template <int D, int NTHR>
+struct PackedStateRegs {
+    static constexpr int HPACK = D * (D + 16) / 2;
+    static constexpr int N = (HPACK + 4 * NTHR - 1) / (4 * NTHR);
+    f32x4 x[N];
+    __device__ __forceinline__ void load(const float* __restrict__ src, int tid) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int e = (tid + u * NTHR) * 4;
+            if (e < HPACK) x[u] = *reinterpret_cast<const f32x4*>(src + e);
+        }
+    }
+    __device__ __forceinline__ void store(float* R, int tid) const {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int e = (tid + u * NTHR) * 4;
+            if (e < HPACK) {
+                const int l = (e % 256) / 4, kk = l / 16, n = l % 16;
+                float* dst = R + (e / 256) * 16 * kBlockPitch + (4 * kk) * kBlockPitch + n;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[r * kBlockPitch] = x[u][r];
+            }
+        }
+    }
+};
+
 // Stage a stored G chunk state (all 16 x 16 blocks, row-major block order,
 // MFMA operand order inside) into LDS transposed: element (row, col) to
 // dst[col * pitch + row]; workgroup-wide.
@@ -361,6 +415,15 @@ struct ChunkRowsRegs {
             const int i = e / D, f = e % D;
             x[u].zero();
             if (i < valid) x[u].load(src + (size_t)i * D + f);
+        }
+    }
+    __device__ __forceinline__ void store_rows(float* rows, int tid) const {
+        constexpr int PD = lds_pitch(D);
+#pragma unroll
+        for (int u = 0; u < EL4; ++u) {
+            const int e = (tid + u * NTHR) * 4;
+            const int i = e / D, f = e % D;
+            *reinterpret_cast<f32x4*>(&rows[i * PD + f]) = x[u].get();
         }
     }
     __device__ __forceinline__ void store_transposed(float* tr, int tid) const {

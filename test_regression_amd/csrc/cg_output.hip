@@ -23,11 +23,16 @@
 // Tokens in the second half then use S_mid and need intra-chunk terms only
 // against the keys of the second half.
 //
-// Work split: one workgroup per (head, chunk); wave w owns tokens
-// 16w..16w+15 and runs their CG entirely on its own: the tiles in LDS are
-// read-only during the iterations, so the CG loop has no workgroup barrier
-// and waves stop independently.  Each wave runs a body specialised on w
-// (static sub-chunk, causal block range).
+// Work split: a workgroup works on one (head, chunk) at a time; wave w owns
+// tokens 16w..16w+15 and runs their CG entirely on its own: the tiles in LDS
+// are read-only during the iterations, so the CG loop has no workgroup
+// barrier and waves stop independently.  Each wave runs a body specialised
+// on w (static sub-chunk, causal block range).  The grid holds only as many
+// workgroups as are resident at once (the LDS tiles allow one per compute
+// unit at d = 128, C = 64), and each walks a strided list of chunks: the
+// next chunk's stored state, keys, gates and queries are requested while
+// the current chunk's output products run, instead of in a prologue that
+// nothing overlaps.
 //
 // Transposed products.  Every contraction is computed as its transpose,
 // e.g. Y^T = S P^T with the state as the MFMA A operand and the wave's CG
@@ -40,38 +45,94 @@
 // k-slot lanes.  The A operands (state rows, key rows, K^T rows) are 128-bit
 // LDS reads, issued one k-group ahead of the MFMAs that use them.  Every MFMA
 // chain starts from zero and is only read afterwards.
+#include <algorithm>
+#include <atomic>
+
 #include "cg_core.h"
 #include "mesa_kernels.h"
 
 namespace mesa {
 
-// The CG of wave W (tokens 16W..16W+15 of the chunk) and its output rows.
+constexpr int kMaxDevices = 64;
+
+// Where a chunk lives in the inputs and the workspace.
+struct ChunkPos {
+    size_t tok0;   // first token of the chunk (row of the [B*H*T, d] inputs)
+    size_t hoff;   // offset of its packed S^H_c
+    size_t soff;   // offset of its S^G_c
+    int h;         // head
+    int valid;     // tokens of the chunk inside the sequence
+};
+
+template <int D, int C>
+__device__ __forceinline__ ChunkPos chunk_pos(long idx, int n_chunks, int H, int T) {
+    constexpr int HPACK = D * (D + 16) / 2;   // packed upper block triangle of S^H
+    ChunkPos p;
+    const int c = (int)(idx % n_chunks);
+    const long bh = idx / n_chunks;
+    p.h = (int)(bh % H);
+    p.valid = min(C, T - c * C);
+    p.tok0 = (size_t)bh * T + (size_t)c * C;
+    p.hoff = (size_t)idx * HPACK;
+    p.soff = (size_t)idx * D * D;
+    return p;
+}
+
+// The query rows of the wave's tokens (B layout: lane (n, kk) holds features
+// 16j + 4kk .. 16j + 4kk + 3 of token 16w + n), zero past the sequence end.
+template <int D, typename In>
+__device__ __forceinline__ void load_queries(Raw4<In> (&qr)[D / 16], const In* __restrict__ q, size_t tok0,
+                                             int valid, int tr, int kk) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        qr[j].zero();
+        if (tr < valid) qr[j].load(q + (tok0 + tr) * D + 16 * j + 4 * kk);
+    }
+}
+
+// One chunk's work of wave W (tokens 16W..16W+15): its CG, its output rows,
+// and its share of loading and staging the next chunk of this workgroup.
+// Four workgroup barriers: (A) every wave is done with the chunk's states,
+// keys and gates; (B) V_c^T is staged; (C) the next chunk's S^H, K rows and
+// gates are staged; (D) its K^T and mid-chunk state are formed.
 template <int D, int C, int W, typename In>
-__device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __restrict__ q,
-                                        const In* __restrict__ v, const float* __restrict__ Gc, size_t tok0,
-                                        int valid, int max_iters, float tol, float* __restrict__ out,
-                                        int32_t* __restrict__ iters, float* __restrict__ x_out) {
+__device__ __forceinline__ bool cg_wave(CgLds<D, C>& L, int tid, ChunkPos& p, int n_chunks, int H, int T,
+                                        long total, int* __restrict__ work_counter, Raw4<In> (&qr)[D / 16],
+                                        const In* __restrict__ q, const In* __restrict__ k,
+                                        const In* __restrict__ v, const float* __restrict__ gamma,
+                                        const float* __restrict__ lambda, const float* __restrict__ SH,
+                                        const float* __restrict__ SG, int max_iters, float tol,
+                                        float* __restrict__ out, int32_t* __restrict__ iters,
+                                        float* __restrict__ x_out) {
     using CW = CgWave<D, C, W>;
     constexpr int NT = D / 16;
     constexpr int NW = C / 16;
     constexpr int NBO = CW::NBO;
     constexpr int NTHR = 64 * NW;
-    const CW cw(L, tid & 63);
+    constexpr int NLAM = (D + NTHR - 1) / NTHR;
+    const int lane = tid & 63;
+    const CW cw(L, lane);
     const int n = cw.n, kk = cw.kk, tr = cw.tr;
-    const bool tok_ok = tr < valid;
+    const bool tok_ok = tr < p.valid;
+
+    // ---- claim this workgroup's next chunk (its number arrives during the CG) ----
+    int ticket = 0;
+    if (W == 0 && lane == 0) ticket = atomicAdd(work_counter, 1);
 
     // ---- CG from x = 0 with r = p = q ----
     f32x4 X[NT], R[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-        R[j] = tok_ok ? load4(q + (tok0 + tr) * D + 16 * j + 4 * kk) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT; ++j) R[j] = qr[j].get();
     const int it = cg_solve_wave<D, C, W>(L, cw, R, X, max_iters, tol);
+    // Addresses of the output phase are built from here on, not held across the CG.
+    asm volatile("" : "+v"(tid));
+    if (W == 0 && lane == 0) L.next = ticket;
 
     // ---- iteration counts, solutions ----
-    if (iters && kk == 0 && tok_ok) iters[tok0 + tr] = it;
+    if (iters && kk == 0 && tok_ok) iters[p.tok0 + tr] = it;
     if (x_out && tok_ok) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(x_out + (tok0 + tr) * D + 16 * j + 4 * kk) = X[j];
+        for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk) = X[j];
     }
 
     // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
@@ -81,7 +142,7 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
     // (j, g) are G_c[16j + n][16g + 4kk .. 16g + 4kk + 3]), so it runs
     // before the barrier, while slower waves still iterate.
     ChunkRowsRegs<D, C, NTHR, In> vrows;
-    vrows.load(v + tok0 * D, valid, tid);
+    vrows.load(v + p.tok0 * D, p.valid, tid);
     f32x4 Wo[NBO];
     {
         f32x4 Sc[NBO], unused[NT];
@@ -93,30 +154,54 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
 #pragma unroll
             for (int r = 0; r < 4; ++r) Wo[ib][r] = Sc[ib][r] * cw.dec[ib][r];
     }
+    PackedStateRegs<D, NTHR> nsh;
+    ChunkRowsRegs<D, C, NTHR, In> nk;
+    float ngam = 1.0f, nlam[NLAM];
     f32x4 OS[NT], OI[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) OS[j] = OI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-        const float* gl = Gc + 4 * (tid & 63);
-        f32x4 ga[3][NT];
+        const float* gl = SG + p.soff + 4 * lane;
+        constexpr int NB_G = 3;   // G_c block columns in flight: NB_G - 1 steps ahead
+        f32x4 ga[NB_G][NT];
         auto gload = [&](int g, int buf) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) ga[buf][j] = *reinterpret_cast<const f32x4*>(gl + (j * NT + g) * 256);
         };
-        gload(0, 0);
-        if (NT > 1) gload(1, 1);
+#pragma unroll
+        for (int g = 0; g < NB_G - 1 && g < NT; ++g) gload(g, g);
 #pragma unroll
         for (int g = 0; g < NT; ++g) {
-            if (g + 2 < NT) gload(g + 2, (g + 2) % 3);
+            if (g + NB_G - 1 < NT) gload(g + NB_G - 1, (g + NB_G - 1) % NB_G);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int j = 0; j < NT; ++j) OS[j] = mfma4(ga[g % 3][j][s], X[g][s], OS[j]);
+                for (int j = 0; j < NT; ++j) OS[j] = mfma4(ga[g % NB_G][j][s], X[g][s], OS[j]);
         }
     }
-    __syncthreads();   // every wave is done with the states, K_c and K_c^T
+    __syncthreads();   // (A) every wave is done with the states, K_c, K_c^T, l and lambda
+    // Chunks 0..G-1 are the workgroups' first; the claims hand out the rest in order.
+    const long nidx = (long)gridDim.x + __builtin_amdgcn_readfirstlane(L.next);
+    const bool more = nidx < total;
+    const ChunkPos pn = chunk_pos<D, C>(more ? nidx : 0, n_chunks, H, T);
+    // The query registers are rewritten on every path (zero after the last
+    // chunk), so their previous contents are dead once the CG has started.
+    auto load_next = [&]() {
+        if (more) {
+            nsh.load(SH + pn.hoff, tid);
+            nk.load(k + pn.tok0 * D, pn.valid, tid);
+            if (W == 0) ngam = lane < pn.valid ? gamma[pn.tok0 + lane] : 1.0f;
+#pragma unroll
+            for (int u = 0; u < NLAM; ++u) {
+                const int e = tid + u * NTHR;
+                nlam[u] = e < D ? lambda[(size_t)pn.h * D + e] : 0.f;
+            }
+        }
+        load_queries<D, In>(qr, q, pn.tok0, more ? pn.valid : 0, tr, kk);
+    };
+    load_next();   // lands behind the V_c^T staging and the intra-chunk output products
     vrows.store_transposed(L.KT, tid);
-    __syncthreads();
+    __syncthreads();   // (B)
     contract_intra<D, C, NBO, 0>(Wo, L.KT, n, kk, OI);
     if (tok_ok) {
 #pragma unroll
@@ -124,67 +209,118 @@ __device__ __forceinline__ void cg_wave(CgLds<D, C>& L, int tid, const In* __res
             f32x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = cw.eLo * OS[j][r] + OI[j][r];
-            *reinterpret_cast<f32x4*>(out + (tok0 + tr) * D + 16 * j + 4 * kk) = o;
+            *reinterpret_cast<f32x4*>(out + (p.tok0 + tr) * D + 16 * j + 4 * kk) = o;
         }
     }
+    if (!more) return false;
+
+    // ---- stage the next chunk ----
+    nsh.store(L.R, tid);
+    nk.store_rows(L.KV, tid);
+    if (W == 0) {
+        const float l = chunk_log_decay_of(ngam, pn.valid, lane);
+        if (lane < C) L.L[lane] = l;
+    }
+#pragma unroll
+    for (int u = 0; u < NLAM; ++u) {
+        const int e = tid + u * NTHR;
+        if (e < D) L.Lam[e] = nlam[u];
+    }
+    __syncthreads();   // (C) every wave is done with V_c^T
+    nk.store_transposed(L.KT, tid);
+    if constexpr (NW >= 2) form_mid_state<D, C>(L, W, n, kk);
+    __syncthreads();   // (D)
+    p = pn;
+    return true;
 }
 
+// Persistent: G workgroups (as many as are resident at once) start on chunks
+// 0..G-1 and then claim chunks G, G+1, ... in order from a counter (zeroed
+// by the chunk-state kernel), so iteration counts that vary along the
+// sequence still spread evenly; each chunk's state and key loads run behind
+// the previous chunk's output products.
 template <int D, int C, typename In>
 __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ gamma, const float* __restrict__ lambda,
-    const float* __restrict__ SH, const float* __restrict__ SG, int H, int T, int n_chunks,
-    int max_iters, float tol, float* __restrict__ out, int32_t* __restrict__ iters, float* __restrict__ x_out) {
+    const float* __restrict__ SH, const float* __restrict__ SG, int H, int T, int n_chunks, long total,
+    int* __restrict__ work_counter, int max_iters, float tol, float* __restrict__ out, int32_t* __restrict__ iters,
+    float* __restrict__ x_out) {
     constexpr int NW = C / 16;
+    constexpr int NT = D / 16;
     constexpr int NTHR = 64 * NW;
     __shared__ CgLds<D, C> L;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = blockIdx.x % n_chunks;
-    const long bh = blockIdx.x / n_chunks;
-    const int h = (int)(bh % H);
-    const int t0 = c * C;
-    const int valid = min(C, T - t0);
-    const size_t tok0 = (size_t)bh * T + t0;   // first token of the chunk
-    constexpr int HPACK = D * (D + 16) / 2;    // packed upper block triangle of S^H
-    const size_t hoff = ((size_t)bh * n_chunks + c) * HPACK;
-    const size_t soff = ((size_t)bh * n_chunks + c) * D * D;
+    const int tid0 = threadIdx.x;
+    const int lane = tid0 & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    ChunkPos p = chunk_pos<D, C>(blockIdx.x, n_chunks, H, T);
 
-    // ---- stage S^H_c, K_c (rows and transposed), lambda, l ----
-    stage_packed_state<D, C>(L, SH + hoff, tid, NTHR);
-    stage_chunk_rows<D, C, true, true>(L.KV, L.KT, k + tok0 * D, valid, tid, NTHR);
-    for (int e = tid; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)h * D + e];
+    // ---- the first chunk: stage S^H_c, K_c (rows and transposed), lambda, l ----
+    stage_packed_state<D, C>(L, SH + p.hoff, tid0, NTHR);
+    stage_chunk_rows<D, C, true, true>(L.KV, L.KT, k + p.tok0 * D, p.valid, tid0, NTHR);
+    for (int e = tid0; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)p.h * D + e];
     if (w == 0) {
-        const float l = chunk_log_decay(gamma + tok0, valid, lane);
+        const float l = chunk_log_decay(gamma + p.tok0, p.valid, lane);
         if (lane < C) L.L[lane] = l;
     }
+    Raw4<In> qr[NT];
+    load_queries<D, In>(qr, q, p.tok0, p.valid, 16 * w + (lane & 15), lane >> 4);
     __syncthreads();
     if constexpr (NW >= 2) {
         form_mid_state<D, C>(L, w, lane & 15, lane >> 4);
         __syncthreads();
     }
 
-    const float* Gc = SG + soff;
-    if (w == 0) {
-        cg_wave<D, C, 0, In>(L, tid, q, v, Gc, tok0, valid, max_iters, tol, out, iters, x_out);
-    } else if constexpr (NW > 1) {
-        if (w == 1) {
-            cg_wave<D, C, 1, In>(L, tid, q, v, Gc, tok0, valid, max_iters, tol, out, iters, x_out);
-        } else if constexpr (NW > 2) {
-            if (w == 2) cg_wave<D, C, 2, In>(L, tid, q, v, Gc, tok0, valid, max_iters, tol, out, iters, x_out);
-            else cg_wave<D, C, 3, In>(L, tid, q, v, Gc, tok0, valid, max_iters, tol, out, iters, x_out);
+    for (bool more = true; more;) {
+        // An opaque copy of the thread id: the per-lane LDS addresses derived
+        // from it are rebuilt per chunk instead of being held in registers
+        // across the output phase.
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        if (w == 0) {
+            more = cg_wave<D, C, 0, In>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma, lambda,
+                                        SH, SG, max_iters, tol, out, iters, x_out);
+        } else if constexpr (NW > 1) {
+            if (w == 1) {
+                more = cg_wave<D, C, 1, In>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma,
+                                            lambda, SH, SG, max_iters, tol, out, iters, x_out);
+            } else if constexpr (NW > 2) {
+                if (w == 2)
+                    more = cg_wave<D, C, 2, In>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma,
+                                                lambda, SH, SG, max_iters, tol, out, iters, x_out);
+                else
+                    more = cg_wave<D, C, 3, In>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma,
+                                                lambda, SH, SG, max_iters, tol, out, iters, x_out);
+            }
         }
     }
 }
 
+// Workgroups of `kernel` resident at once on the current device (cached per device).
+template <typename Kernel>
+static long resident_workgroups(Kernel kernel, int block, std::atomic<long> (&cache)[kMaxDevices]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    long r = cache[dev].load(std::memory_order_relaxed);
+    if (r > 0) return r;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, 0) != hipSuccess || per < 1) per = 1;
+    r = (long)cus * per;
+    cache[dev].store(r, std::memory_order_relaxed);
+    return r;
+}
+
 template <int D, int C, typename In>
 static hipError_t launch_t(const CgOutputArgs& a, hipStream_t s) {
-    const long grid = a.BH * a.n_chunks;
-    hipLaunchKernelGGL((cg_output_kernel<D, C, In>), dim3((unsigned)grid), dim3(64 * (C / 16)), 0, s,
+    static std::atomic<long> resident[kMaxDevices];
+    const long total = a.BH * a.n_chunks;
+    const int block = 64 * (C / 16);
+    const long grid = std::min(total, resident_workgroups(cg_output_kernel<D, C, In>, block, resident));
+    hipLaunchKernelGGL((cg_output_kernel<D, C, In>), dim3((unsigned)grid), dim3(block), 0, s,
                        (const In*)a.q, (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.SH, a.SG,
-                       a.H, a.T, a.n_chunks, a.max_iters, a.tol, a.out, a.iters, a.x_out);
+                       a.H, a.T, a.n_chunks, total, a.work_counter, a.max_iters, a.tol, a.out, a.iters, a.x_out);
     return hipGetLastError();
 }
 

@@ -50,7 +50,8 @@ template <int D, int C, int NWK, typename In>
 __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
     int T, int n_chunks, float* __restrict__ SH, float* __restrict__ SG,
-    float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks, long BH) {
+    float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks, long BH,
+    int* __restrict__ work_counter) {
     constexpr int NW = NWK;                    // waves per workgroup
     constexpr int RB = D / (16 * NW);          // row blocks per state
     constexpr int NT = D / 16;                 // 16-column tiles of the state
@@ -68,6 +69,8 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     const int w = tid >> 6;
     const int n = lane & 15;
     const int kk = lane >> 4;
+    // the chunk-claim counter of the CG/output kernel that runs next
+    if (work_counter && blockIdx.x == 0 && tid == 0) *work_counter = 0;
 
     // XCD-aware id: consecutive ids go round-robin over the 8 XCDs, so the
     // 2*RB parts of head bh get ids xcd + 8*(slot) with equal xcd.
@@ -208,7 +211,7 @@ hipError_t launch_chunk_states_nw(const ChunkStatesArgs& a, hipStream_t s) {
     const long grid = ((a.BH + 7) / 8) * 8 * 2 * RB;
     hipLaunchKernelGGL((chunk_states_kernel<D, C, NW, In>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
                        (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG,
-                       a.final_H, a.final_G, a.write_chunks, a.BH);
+                       a.final_H, a.final_G, a.write_chunks, a.BH, a.work_counter);
     return hipGetLastError();
 }
 

@@ -123,14 +123,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Within-chunk log decays.  Lane i < len gets l_i = sum_{s<=i} ln(gamma_s) of
 // the chunk's tokens (tokens past the sequence end count as gamma = 1).
 // Must be called by a whole wave.
-__device__ __forceinline__ float chunk_log_decay(const float* gamma_chunk, int valid, int lane) {
-    float x = (lane < valid) ? __logf(gamma_chunk[lane]) : 0.0f;
+__device__ __forceinline__ float chunk_log_decay_of(float gamma_lane, int valid, int lane) {
+    float x = (lane < valid) ? __logf(gamma_lane) : 0.0f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         float t = __shfl_up(x, o, 64);
         if (lane >= o) x += t;
     }
     return x;
+}
+__device__ __forceinline__ float chunk_log_decay(const float* gamma_chunk, int valid, int lane) {
+    return chunk_log_decay_of(lane < valid ? gamma_chunk[lane] : 1.0f, valid, lane);
 }
 
 }  // namespace mesa

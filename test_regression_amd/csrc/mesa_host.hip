@@ -111,12 +111,20 @@ const char* mesa_status_string(int s) {
 
 const char* mesa_last_error_message(void) { return g_err.c_str(); }
 
+// Bytes of the forward's chunk states: per chunk and head the packed upper
+// 16x16-block triangle of H (dk (dk + 16) / 2 floats) and the full G
+// (dv x dk), fp32.  A 256-byte tail after them holds the CG/output kernel's
+// chunk-claim counter.
+static size_t forward_state_bytes(long BH, long nc, int dk, int dv) {
+    return (size_t)BH * nc * ((size_t)dk * (dk + 16) / 2 + (size_t)dv * dk) * sizeof(float);
+}
+constexpr size_t kForwardTailBytes = 256;
+
 size_t mesa_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
-    // per chunk and head: the packed upper 16x16-block triangle of H
-    // (dk (dk + 16) / 2 floats) and the full G (dv x dk); both fp32
-    const size_t nc = ((size_t)T + chunk - 1) / chunk;
-    return (size_t)B * H * nc * ((size_t)dk * (dk + 16) / 2 + (size_t)dv * dk) * sizeof(float);
+    const long nc = ((long)T + chunk - 1) / chunk;
+    if (nc == 0) return 0;
+    return forward_state_bytes((long)B * H, nc, dk, dv) + kForwardTailBytes;
 }
 
 static mesa_status forward_impl(const void* q, const void* k, const void* v, int qkv_dtype,
@@ -158,6 +166,9 @@ static mesa_status forward_impl(const void* q, const void* k, const void* v, int
     const int bf16 = qkv_dtype == MESA_DTYPE_BF16;
     float* SH = static_cast<float*>(workspace);
     float* SG = need_ws ? SH + (size_t)BH * n_chunks * ((size_t)dk * (dk + 16) / 2) : nullptr;
+    int* work_counter =
+        need_ws ? reinterpret_cast<int*>(static_cast<char*>(workspace) + forward_state_bytes(BH, n_chunks, dk, dv))
+                : nullptr;
 
     if (T == 0) {
         // Nothing to solve; the final states are the zero initial states.
@@ -169,7 +180,7 @@ static mesa_status forward_impl(const void* q, const void* k, const void* v, int
 
     if (need_ws || final_H || final_G) {
         mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
-                                SH, SG, final_H, final_G, need_ws ? 1 : 0};
+                                SH, SG, final_H, final_G, need_ws ? 1 : 0, work_counter};
         hipError_t e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
         if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
     }
@@ -182,7 +193,7 @@ static mesa_status forward_impl(const void* q, const void* k, const void* v, int
         return MESA_OK;
     }
     mesa::CgOutputArgs a{q, k, v, gamma, lambda, SH, SG, BH, H, T, dk, chunk, (int)n_chunks,
-                         bf16, max_iters, tol, out, iters, x_out};
+                         bf16, max_iters, tol, out, iters, x_out, work_counter};
     hipError_t e = timed_launch(MESA_KERNEL_CG_OUTPUT, s, [&] { return mesa::launch_cg_output(a, s); });
     if (e != hipSuccess) return hip_fail(e, "CG/output kernel launch");
     return MESA_OK;
@@ -281,7 +292,7 @@ mesa_status mesa_backward(const void* k, const void* v, int qkv_dtype, const flo
     hipError_t e;
     {
         mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
-                                ws + lay.sh, ws + lay.sg, nullptr, nullptr, 1};
+                                ws + lay.sh, ws + lay.sg, nullptr, nullptr, 1, nullptr};
         e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
         if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
     }

@@ -10,6 +10,7 @@ struct ChunkStatesArgs {
     const void* k; const void* v; const float* gamma;
     long BH; int T; int d; int chunk; int n_chunks; int bf16;
     float* SH; float* SG; float* final_H; float* final_G; int write_chunks;
+    int* work_counter;   // zeroed for the CG/output kernel that follows, or nullptr
 };
 
 struct CgOutputArgs {
@@ -19,6 +20,7 @@ struct CgOutputArgs {
     int max_iters; float tol;
     float* out; int32_t* iters;
     float* x_out;   // CG solutions [BH, T, d], or nullptr
+    int* work_counter;   // chunk claims; zero at launch
 };
 
 struct DecodeArgs {
