@@ -64,13 +64,13 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     __shared__ float sW[C];        // e^{l_end - l_i}
     __shared__ float sGam;         // e^{l_end}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int tid0 = threadIdx.x;
+    const int lane = tid0 & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int n = lane & 15;
     const int kk = lane >> 4;
     // the chunk-claim counter of the CG/output kernel that runs next
-    if (work_counter && blockIdx.x == 0 && tid == 0) *work_counter = 0;
+    if (work_counter && blockIdx.x == 0 && tid0 == 0) *work_counter = 0;
 
     // XCD-aware id: consecutive ids go round-robin over the 8 XCDs, so the
     // 2*RB parts of head bh get ids xcd + 8*(slot) with equal xcd.
@@ -95,14 +95,23 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Keys, values and gates of the next two chunks are held in registers
-    // (a two-slot ring), so a chunk's global loads have two chunk steps of
-    // MFMAs and stores to complete behind.
+    // Keys, values and gates of the next RING chunks are held in registers
+    // (a ring of RING slots), so a chunk's global loads have RING chunk
+    // steps of MFMAs and stores to complete behind.  Two slots of fp32
+    // inputs would cost the second wave per SIMD its registers.
+    constexpr int RING = sizeof(In) == 2 ? 2 : 1;
     constexpr int EL4 = C * D / (4 * NTHR);   // 4-element groups per thread per tile
     static_assert(C * D % (4 * NTHR) == 0, "tile must split evenly over the workgroup");
-    Raw4<In> kreg[2][EL4], vreg[2][EL4];
-    float greg[2] = {1.0f, 1.0f};
+    Raw4<In> kreg[RING][EL4], vreg[RING][EL4];
+    float greg[RING];
+#pragma unroll
+    for (int sl = 0; sl < RING; ++sl) greg[sl] = 1.0f;
+    // Lane-dependent addresses are rebuilt from an opaque copy of the thread
+    // id in every step and prefetch instead of being held in registers
+    // across the chunk loop (which would cost the second wave per SIMD).
     auto prefetch = [&](int c, int sl) {
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
         const int t0 = c * C;
         const int valid = min(C, T - t0);
 #pragma unroll
@@ -120,6 +129,9 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     };
 
     auto step = [&](int c, int sl) {
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, n = lane & 15, kk = lane >> 4;
         // ---- stage the chunk's keys (and values) in LDS as fp32 ----
 #pragma unroll
         for (int u = 0; u < EL4; ++u) {
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
             if (lane == 0) sGam = __expf(lend);
         }
         __syncthreads();
-        if (c + 2 < n_chunks) prefetch(c + 2, sl);
+        if (c + RING < n_chunks) prefetch(c + RING, sl);
 
         // ---- the state before this chunk ----
         if (write_chunks) {
@@ -180,11 +192,13 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
         __syncthreads();
     };
 
-    if (n_chunks > 0) prefetch(0, 0);
-    if (n_chunks > 1) prefetch(1, 1);
-    for (int c = 0; c < n_chunks; c += 2) {
-        step(c, 0);
-        if (c + 1 < n_chunks) step(c + 1, 1);
+#pragma unroll
+    for (int sl = 0; sl < RING; ++sl)
+        if (sl < n_chunks) prefetch(sl, sl);
+    for (int c = 0; c < n_chunks; c += RING) {
+#pragma unroll
+        for (int sl = 0; sl < RING; ++sl)
+            if (c + sl < n_chunks) step(c + sl, sl);
     }
 
     // ---- final state (after the last token) ----
