@@ -2,7 +2,7 @@
 
     python -m test_regression_amd.profile_summary stats <kernel_stats.csv | results.db> [--command CMD]
     python -m test_regression_amd.profile_summary traffic <fetch_counter_collection.csv>
-        <write_counter_collection.csv> --copy-bytes N --kernel NAME_SUBSTRING [--command CMD]
+        <write_counter_collection.csv> --copy-bytes N --kernel NAME_SUBSTRING [--first N] [--command CMD]
 
 ``stats`` prints per-kernel call counts and average durations (from a
 ``--kernel-trace --stats`` run, CSV or rocpd database).  ``traffic`` turns two
@@ -23,7 +23,8 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CG_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/mesa_device.h"]
+CG_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_core.h",
+              "test_regression_amd/csrc/mesa_device.h"]
 
 
 def cg_source_hash(sources=None) -> str:
@@ -88,6 +89,10 @@ def cmd_traffic(a):
     w_scale = a.copy_bytes / 1024 / w_copy
     f_k = [v for n, v in fetch if a.kernel in n]
     w_k = [v for n, v in write if a.kernel in n]
+    if a.first:
+        # only the first dispatches (one workload of a run that launches the
+        # same kernel for several)
+        f_k, w_k = f_k[:a.first], w_k[:a.first]
     fb = statistics.median(f_k) * 1024 * f_scale
     wb = statistics.median(w_k) * 1024 * w_scale
     print(json.dumps({
@@ -98,7 +103,7 @@ def cmd_traffic(a):
         "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
         "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
-        "bytes_per_launch": round(fb + wb), "dispatches": [len(f_k), len(w_k)],
+        "bytes_per_launch": round(fb + wb), "dispatches": [len(f_k), len(w_k)], "first": a.first,
     }, indent=1))
 
 
@@ -115,6 +120,8 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--kernel", required=True)
     t.add_argument("--command", default="")
+    t.add_argument("--first", type=int, default=0,
+                   help="use only the first N matching dispatches (0: all)")
     t.add_argument("--sources", nargs="*", default=None,
                    help="repository-relative sources whose hash identifies the kernel (default: the CG kernel's)")
     a = ap.parse_args(argv)
