@@ -64,6 +64,14 @@ def cmd_stats(a):
     for name, calls, tot, avg, pct in rows:
         if a.all or name.startswith("mesa::") or "zero_fill" in name:
             out.append(f"{name:70s} {calls:6d} {tot:12.1f} {avg:11.1f} {pct:6.2f}")
+    if a.trace and a.first_kernel:
+        # the first N dispatches of one kernel (one workload of a run that
+        # launches the kernel for several), from the per-dispatch trace
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+             for r in csv.DictReader(open(a.trace)) if a.first_kernel in r["Kernel_Name"]][:a.first]
+        if d:
+            out.append(f"first {len(d)} dispatches of {a.first_kernel}: avg {statistics.mean(d):.1f} us, "
+                       f"median {statistics.median(d):.1f} us")
     print("\n".join(out))
 
 
@@ -114,6 +122,9 @@ def main(argv=None):
     s.add_argument("path")
     s.add_argument("--command", default="")
     s.add_argument("--all", action="store_true")
+    s.add_argument("--trace", default="", help="kernel_trace.csv of the same run")
+    s.add_argument("--first-kernel", default="", help="kernel name substring for --first")
+    s.add_argument("--first", type=int, default=0, help="average only its first N dispatches")
     t = sub.add_parser("traffic")
     t.add_argument("fetch")
     t.add_argument("write")
