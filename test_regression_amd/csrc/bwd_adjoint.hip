@@ -10,38 +10,84 @@
 //   bx_t = G_t^T g_t = e^{l_t} (S^G_c)^T g_t + sum_{i=t0..t} e^{l_t - l_i} (v_i . g_t) k_i
 //   z_t  = CG(H_t + Lambda, bx_t)                   -> dL/dq_t
 //   beta_t = g_t . o_t - z_t . (H_t x_t)            (the query-side gate total)
-//   sum over the chunk's tokens of z_t (.) x_t      (minus dL/dlambda, per chunk)
-// Work split and layout as the forward CG kernel: one workgroup per (head,
-// chunk), wave w owns tokens 16w..16w+15, every product transposed so the
-// wave's vectors are the MFMA B operand.  Phase 1 holds (S^G_c)^T, V_c rows
-// and K_c^T in LDS for bx; phase 2 holds the stored S^H_c, the mid-chunk
-// state, K_c rows and K_c^T for the CG and H_t x_t.
+//   sum over the wave's tokens of z_t (.) x_t       (minus dL/dlambda, per chunk and wave)
+// Work split and layout as the forward CG kernel (persistent workgroups
+// that claim chunks; wave w owns tokens 16w..16w+15; every product
+// transposed so the wave's vectors are the MFMA B operand).  LDS holds what
+// the CG needs: the stored S^H_c, the mid-chunk state, K_c rows and K_c^T.
+// The right side takes (S^G_c)^T's blocks straight from memory (the
+// chunk-state kernel stores them in MFMA operand order for this kernel) and
+// the value rows of the scores v_i . g_t from memory too, so it needs no
+// LDS of its own.
+#include <algorithm>
+#include <atomic>
+
 #include "cg_core.h"
 #include "mesa_kernels.h"
+#include "persistent.h"
 
 namespace mesa {
 
+// B = G_t^T g_t over the wave's tokens (B layout), and g_t . o_t.
 template <int D, int C, int W, typename In>
-__device__ __forceinline__ void adjoint_rhs(CgLds<D, C>& L, const CgWave<D, C, W>& cw,
-                                            const float* __restrict__ gout, const float* __restrict__ o,
-                                            size_t tok0, bool tok_ok, f32x4 (&B)[D / 16], float& go) {
+__device__ __forceinline__ void adjoint_rhs(const CgLds<D, C>& L, const CgWave<D, C, W>& cw, int lane,
+                                            const ChunkPos& p, const In* __restrict__ v,
+                                            const float* __restrict__ SG, const float* __restrict__ gout,
+                                            const float* __restrict__ o, f32x4 (&B)[D / 16], float& go) {
     constexpr int NT = D / 16;
     constexpr int NBO = CgWave<D, C, W>::NBO;
-    f32x4 Gv[NT], Ov[NT];
+    const bool tok_ok = cw.tr < p.valid;
+    f32x4 Gv[NT];
+    {
+        f32x4 Ov[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const size_t off = (tok0 + cw.tr) * D + 16 * j + 4 * cw.kk;
-        Gv[j] = tok_ok ? *reinterpret_cast<const f32x4*>(gout + off) : f32x4{0.f, 0.f, 0.f, 0.f};
-        Ov[j] = tok_ok ? *reinterpret_cast<const f32x4*>(o + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NT; ++j) {
+            const size_t off = (p.tok0 + cw.tr) * D + 16 * j + 4 * cw.kk;
+            Gv[j] = tok_ok ? *reinterpret_cast<const f32x4*>(gout + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            Ov[j] = tok_ok ? *reinterpret_cast<const f32x4*>(o + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        go = token_dot<NT>(Gv, Ov);
     }
-    go = token_dot<NT>(Gv, Ov);
     f32x4 BS[NT], BI[NT], Sc[NBO];
 #pragma unroll
     for (int j = 0; j < NT; ++j) BS[j] = BI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ib = 0; ib < NBO; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // (S^G_c)^T g (rows of the transposed state) and the scores v_i . g_t
-    contract_rows<D, NBO, true>(Gv, L.R, L.KV, cw.n, cw.kk, BS, Sc);
+    // (S^G_c)^T g: this lane's 16 bytes of block (j, g) of (S^G_c)^T are
+    // (S^G_c)^T[16j + n][16g + 4kk .. 16g + 4kk + 3].  Scores v_i . g_t: key
+    // row 16ib + n, features 16g + 4kk .. + 3, from memory (zero past the end).
+    {
+        const float* gl = SG + p.soff + 4 * lane;
+        constexpr int NB_G = 3;   // block columns in flight: NB_G - 1 steps ahead
+        f32x4 ga[NB_G][NT];
+        Raw4<In> vb[NB_G][NBO];
+        auto gload = [&](int g, int buf) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) ga[buf][j] = *reinterpret_cast<const f32x4*>(gl + (j * NT + g) * 256);
+#pragma unroll
+            for (int ib = 0; ib < NBO; ++ib) {
+                const int key = 16 * ib + cw.n;
+                vb[buf][ib].zero();
+                if (key < p.valid) vb[buf][ib].load(v + (p.tok0 + key) * D + 16 * g + 4 * cw.kk);
+            }
+        };
+#pragma unroll
+        for (int g = 0; g < NB_G - 1 && g < NT; ++g) gload(g, g);
+#pragma unroll
+        for (int g = 0; g < NT; ++g) {
+            if (g + NB_G - 1 < NT) gload(g + NB_G - 1, (g + NB_G - 1) % NB_G);
+            f32x4 va[NBO];
+#pragma unroll
+            for (int ib = 0; ib < NBO; ++ib) va[ib] = vb[g % NB_G][ib].get();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) BS[j] = mfma4(ga[g % NB_G][j][s], Gv[g][s], BS[j]);
+#pragma unroll
+                for (int ib = 0; ib < NBO; ++ib) Sc[ib] = mfma4(va[ib][s], Gv[g][s], Sc[ib]);
+            }
+        }
+    }
     f32x4 Wg[NBO];
 #pragma unroll
     for (int ib = 0; ib < NBO; ++ib)
@@ -54,36 +100,117 @@ __device__ __forceinline__ void adjoint_rhs(CgLds<D, C>& L, const CgWave<D, C, W
         for (int r = 0; r < 4; ++r) B[j][r] = cw.eLo * BS[j][r] + BI[j][r];
 }
 
-template <int D, int C, int W>
-__device__ __forceinline__ void adjoint_solve(CgLds<D, C>& L, const CgWave<D, C, W>& cw, f32x4 (&B)[D / 16],
-                                              float go, const float* __restrict__ x, size_t tok0, bool tok_ok,
-                                              int max_iters, float tol, float* __restrict__ dq,
-                                              float* __restrict__ beta, int32_t* __restrict__ z_iters,
-                                              f32x4 (&ZX)[D / 16]) {
+// One chunk's work of wave W: right side, adjoint CG, H_t x_t, the per-token
+// outputs, and its share of loading and staging the next chunk.  Three
+// workgroup barriers: (A) every wave is done with the chunk's LDS tiles;
+// (B) the next chunk's S^H, K and gates are staged; (C) its mid-chunk state
+// is formed.
+template <int D, int C, int W, typename In>
+__device__ __forceinline__ bool adjoint_wave(CgLds<D, C>& L, int tid, ChunkPos& p, int n_chunks, int H, int T,
+                                             long total, int* __restrict__ work_counter, const In* __restrict__ k,
+                                             const In* __restrict__ v, const float* __restrict__ gamma,
+                                             const float* __restrict__ lambda, const float* __restrict__ x,
+                                             const float* __restrict__ o, const float* __restrict__ gout,
+                                             const float* __restrict__ SH, const float* __restrict__ SG,
+                                             int max_iters, float tol, float* __restrict__ dq,
+                                             float* __restrict__ beta, int32_t* __restrict__ z_iters,
+                                             float* __restrict__ lam_part) {
+    using CW = CgWave<D, C, W>;
     constexpr int NT = D / 16;
-    f32x4 Z[NT];
-    const int it = cg_solve_wave<D, C, W>(L, cw, B, Z, max_iters, tol);
+    constexpr int NW = C / 16;
+    constexpr int NTHR = 64 * NW;
+    constexpr int NLAM = (D + NTHR - 1) / NTHR;
+    const int lane = tid & 63;
+    const CW cw(L, lane);
+    const int kk = cw.kk, tr = cw.tr;
+    const bool tok_ok = tr < p.valid;
+
+    // ---- claim this workgroup's next chunk (its number arrives during the CG) ----
+    int ticket = 0;
+    if (W == 0 && lane == 0) ticket = atomicAdd(work_counter, 1);
+
+    // ---- right side and adjoint CG ----
+    f32x4 Bv[NT], Z[NT];
+    float go = 0.f;
+    adjoint_rhs<D, C, W, In>(L, cw, lane, p, v, SG, gout, o, Bv, go);
+    const int it = cg_solve_wave<D, C, W>(L, cw, Bv, Z, max_iters, tol);
+
+    // ---- H_t x_t, beta, dq ----
     f32x4 Xv[NT], Hx[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const size_t off = (tok0 + cw.tr) * D + 16 * j + 4 * cw.kk;
+        const size_t off = (p.tok0 + tr) * D + 16 * j + 4 * kk;
         Xv[j] = tok_ok ? *reinterpret_cast<const f32x4*>(x + off) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     wave_matvec<D, C, W, false>(L, cw, Xv, Hx);
+    // Addresses of what follows are built from here on, not held across the CG.
+    asm volatile("" : "+v"(tid));
     const float b = go - token_dot<NT>(Z, Hx);
     if (tok_ok) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            *reinterpret_cast<f32x4*>(dq + (tok0 + cw.tr) * D + 16 * j + 4 * cw.kk) = Z[j];
-        if (cw.kk == 0) {
-            beta[tok0 + cw.tr] = b;
-            if (z_iters) z_iters[tok0 + cw.tr] = it;
+            *reinterpret_cast<f32x4*>(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk) = Z[j];
+        if (kk == 0) {
+            beta[p.tok0 + tr] = b;
+            if (z_iters) z_iters[p.tok0 + tr] = it;
         }
     }
+    if (W == 0 && lane == 0) L.next = ticket;
+    __syncthreads();   // (A) every wave is done with the states, K_c, K_c^T, l and lambda
+
+    // ---- request the next chunk ----
+    // Chunks 0..G-1 are the workgroups' first; the claims hand out the rest in order.
+    const long nidx = (long)gridDim.x + __builtin_amdgcn_readfirstlane(L.next);
+    const bool more = nidx < total;
+    const ChunkPos pn = chunk_pos<D, C>(more ? nidx : 0, n_chunks, H, T);
+    PackedStateRegs<D, NTHR> nsh;
+    ChunkRowsRegs<D, C, NTHR, In> nk;
+    float ngam = 1.0f, nlam[NLAM];
+    if (more) {
+        nsh.load(SH + pn.hoff, tid);
+        nk.load(k + pn.tok0 * D, pn.valid, tid);
+        if (W == 0) ngam = lane < pn.valid ? gamma[pn.tok0 + lane] : 1.0f;
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+        for (int u = 0; u < NLAM; ++u) {
+            const int e = tid + u * NTHR;
+            nlam[u] = e < D ? lambda[(size_t)pn.h * D + e] : 0.f;
+        }
+    }
+
+    // ---- sum over the wave's tokens of z (.) x (lanes n = 0 of each k-slot group) ----
+    {
+        const size_t chunk = p.soff / ((size_t)D * D);
+        float* dst = lam_part + (chunk * NW + W) * D + 4 * kk;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ZX[j][r] = Z[j][r] * Xv[j][r];
+        for (int j = 0; j < NT; ++j) {
+            f32x4 s;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[r] = rowsum16(Z[j][r] * Xv[j][r]);
+            if ((lane & 15) == 0) *reinterpret_cast<f32x4*>(dst + 16 * j) = s;
+        }
+    }
+    if (!more) return false;
+
+    // ---- stage the next chunk ----
+    nsh.store(L.R, tid);
+    nk.store_rows(L.KV, tid);
+    nk.store_transposed(L.KT, tid);
+    if (W == 0) {
+        const float l = chunk_log_decay_of(ngam, pn.valid, lane);
+        if (lane < C) L.L[lane] = l;
+    }
+#pragma unroll
+    for (int u = 0; u < NLAM; ++u) {
+        const int e = tid + u * NTHR;
+        if (e < D) L.Lam[e] = nlam[u];
+    }
+    __syncthreads();   // (B)
+    if constexpr (NW >= 2) {
+        form_mid_state<D, C>(L, W, cw.n, kk);
+        __syncthreads();   // (C)
+    }
+    p = pn;
+    return true;
 }
 
 template <int D, int C, typename In>
@@ -91,104 +218,61 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_adjoint_kernel(
     const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
     const float* __restrict__ lambda, const float* __restrict__ x, const float* __restrict__ o,
     const float* __restrict__ gout, const float* __restrict__ SH, const float* __restrict__ SG, int H, int T,
-    int n_chunks, int max_iters, float tol, float* __restrict__ dq, float* __restrict__ beta,
-    int32_t* __restrict__ z_iters, float* __restrict__ lam_part) {
+    int n_chunks, long total, int* __restrict__ work_counter, int max_iters, float tol, float* __restrict__ dq,
+    float* __restrict__ beta, int32_t* __restrict__ z_iters, float* __restrict__ lam_part) {
     constexpr int NW = C / 16;
-    constexpr int NT = D / 16;
-    constexpr int PS = lds_pitch_rows(D);
     constexpr int NTHR = 64 * NW;
     __shared__ CgLds<D, C> L;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = blockIdx.x % n_chunks;
-    const long bh = blockIdx.x / n_chunks;
-    const int h = (int)(bh % H);
-    const int t0 = c * C;
-    const int valid = min(C, T - t0);
-    const size_t tok0 = (size_t)bh * T + t0;
-    constexpr int HPACK = D * (D + 16) / 2;
-    const size_t hoff = ((size_t)bh * n_chunks + c) * HPACK;
-    const size_t soff = ((size_t)bh * n_chunks + c) * D * D;
+    const int tid0 = threadIdx.x;
+    const int lane = tid0 & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    ChunkPos p = chunk_pos<D, C>(blockIdx.x, n_chunks, H, T);
 
-    // ---- phase 1: (S^G_c)^T as rows, V_c rows, K_c^T, lambda, l ----
-    stage_g_state_transposed<D>(L.R, PS, SG + soff, tid, NTHR);
-    stage_chunk_rows<D, C, true, false>(L.KV, nullptr, v + tok0 * D, valid, tid, NTHR);
-    stage_chunk_rows<D, C, false, true>(nullptr, L.KT, k + tok0 * D, valid, tid, NTHR);
-    for (int e = tid; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)h * D + e];
+    // ---- the first chunk: stage S^H_c, K_c (rows and transposed), lambda, l ----
+    stage_packed_state<D, C>(L, SH + p.hoff, tid0, NTHR);
+    stage_chunk_rows<D, C, true, true>(L.KV, L.KT, k + p.tok0 * D, p.valid, tid0, NTHR);
+    for (int e = tid0; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)p.h * D + e];
     if (w == 0) {
-        const float l = chunk_log_decay(gamma + tok0, valid, lane);
+        const float l = chunk_log_decay(gamma + p.tok0, p.valid, lane);
         if (lane < C) L.L[lane] = l;
     }
-    __syncthreads();
-
-    f32x4 B[NT];
-    float go = 0.f;
-    auto rhs = [&](auto wt) {
-        constexpr int WW = decltype(wt)::value;
-        const CgWave<D, C, WW> cw(L, lane);
-        adjoint_rhs<D, C, WW, In>(L, cw, gout, o, tok0, cw.tr < valid, B, go);
-    };
-    if (w == 0) rhs(std::integral_constant<int, 0>{});
-    else if constexpr (NW > 1) {
-        if (w == 1) rhs(std::integral_constant<int, 1>{});
-        else if constexpr (NW > 2) {
-            if (w == 2) rhs(std::integral_constant<int, 2>{});
-            else rhs(std::integral_constant<int, 3>{});
-        }
-    }
-    __syncthreads();   // every wave is done with (S^G_c)^T and V_c
-
-    // ---- phase 2: S^H_c (+ the mid-chunk state), K_c rows ----
-    stage_packed_state<D, C>(L, SH + hoff, tid, NTHR);
-    stage_chunk_rows<D, C, true, false>(L.KV, nullptr, k + tok0 * D, valid, tid, NTHR);
     __syncthreads();
     if constexpr (NW >= 2) {
         form_mid_state<D, C>(L, w, lane & 15, lane >> 4);
         __syncthreads();
     }
 
-    f32x4 ZX[NT];
-    auto solve = [&](auto wt) {
-        constexpr int WW = decltype(wt)::value;
-        const CgWave<D, C, WW> cw(L, lane);
-        adjoint_solve<D, C, WW>(L, cw, B, go, x, tok0, cw.tr < valid, max_iters, tol, dq, beta, z_iters, ZX);
-    };
-    if (w == 0) solve(std::integral_constant<int, 0>{});
-    else if constexpr (NW > 1) {
-        if (w == 1) solve(std::integral_constant<int, 1>{});
-        else if constexpr (NW > 2) {
-            if (w == 2) solve(std::integral_constant<int, 2>{});
-            else solve(std::integral_constant<int, 3>{});
+    for (bool more = true; more;) {
+        // An opaque copy of the thread id: the per-lane LDS addresses derived
+        // from it are rebuilt per chunk instead of being held in registers.
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        auto body = [&](auto wt) {
+            constexpr int WW = decltype(wt)::value;
+            return adjoint_wave<D, C, WW, In>(L, tid, p, n_chunks, H, T, total, work_counter, k, v, gamma, lambda,
+                                              x, o, gout, SH, SG, max_iters, tol, dq, beta, z_iters, lam_part);
+        };
+        if (w == 0) more = body(std::integral_constant<int, 0>{});
+        else if constexpr (NW > 1) {
+            if (w == 1) more = body(std::integral_constant<int, 1>{});
+            else if constexpr (NW > 2) {
+                if (w == 2) more = body(std::integral_constant<int, 2>{});
+                else more = body(std::integral_constant<int, 3>{});
+            }
         }
-    }
-
-    // ---- sum of z (.) x over the chunk's tokens: rows of 16 lanes, then the waves ----
-    __syncthreads();   // the K_c rows are no longer read: reuse them as scratch
-    float* part = L.KV;   // [NW][D]
-    const int kk = lane >> 4;
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float s = rowsum16(ZX[j][r]);
-            if ((lane & 15) == 0) part[w * D + 16 * j + 4 * kk + r] = s;
-        }
-    __syncthreads();
-    for (int f = tid; f < D; f += NTHR) {
-        float s = 0.f;
-        for (int ww = 0; ww < NW; ++ww) s += part[ww * D + f];
-        lam_part[((size_t)bh * n_chunks + c) * D + f] = s;
     }
 }
 
 template <int D, int C, typename In>
 static hipError_t launch_t(const BwdAdjointArgs& a, hipStream_t s) {
-    const long grid = a.BH * a.n_chunks;
-    hipLaunchKernelGGL((bwd_adjoint_kernel<D, C, In>), dim3((unsigned)grid), dim3(64 * (C / 16)), 0, s,
+    static std::atomic<long> resident[kMaxDevices];
+    const long total = a.BH * a.n_chunks;
+    const int block = 64 * (C / 16);
+    const long grid = std::min(total, resident_workgroups(bwd_adjoint_kernel<D, C, In>, block, resident));
+    hipLaunchKernelGGL((bwd_adjoint_kernel<D, C, In>), dim3((unsigned)grid), dim3(block), 0, s,
                        (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.x, a.o, a.gout, a.SH, a.SG, a.H, a.T,
-                       a.n_chunks, a.max_iters, a.tol, a.dq, a.beta, a.z_iters, a.lam_part);
+                       a.n_chunks, total, a.work_counter, a.max_iters, a.tol, a.dq, a.beta, a.z_iters, a.lam_part);
     return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@
 // beta_t the query-side and a_t the key-side per-token totals (computed by
 // the adjoint and key/value kernels), and dL/dgamma_s = that / gamma_s.
 // dL/dlambda = -(sum over the batch and chunks of the per-chunk sums of
-// z (.) x).  Both sums run in double precision in a fixed order.
+// z (.) x).  Both sums run in double precision in an order fixed by the sizes.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -42,16 +42,42 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__
     }
 }
 
-// dlambda[h][f] = -sum_{b, c} part[(b*H + h) * n_chunks + c][f]
-__global__ __launch_bounds__(256) void bwd_lambda_kernel(const float* __restrict__ lam_part, int B, int H,
-                                                         int n_chunks, int D, float* __restrict__ dlam) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (long)H * D) return;
-    const int h = (int)(i / D), f = (int)(i % D);
-    double s = 0.0;
-    for (int b = 0; b < B; ++b)
-        for (int c = 0; c < n_chunks; ++c) s += lam_part[(((size_t)b * H + h) * n_chunks + c) * D + f];
-    dlam[i] = (float)(-s);
+// dlambda[h][f] = -sum_{b, c} part[(b*H + h) * n_chunks + c][f].  One
+// 1024-thread workgroup per (head, 64 features): a thread takes 4 features
+// (one 16-byte load per row) and the rows congruent to its row group mod 64,
+// in order; then the 64 partial sums are added in order.  The order is
+// fixed by the sizes alone.
+constexpr int kLamGroups = 64;
+__global__ __launch_bounds__(1024) void bwd_lambda_kernel(const float* __restrict__ lam_part, int B, int H,
+                                                          int n_chunks, int D, float* __restrict__ dlam) {
+    __shared__ double part[kLamGroups][64];
+    const int q = threadIdx.x & 15, r = threadIdx.x >> 4;   // feature quad, row group
+    const int fblocks = (D + 63) / 64;
+    const int h = blockIdx.x / fblocks;
+    const int f0 = (blockIdx.x % fblocks) * 64 + 4 * q;
+    const long rows = (long)B * n_chunks;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    if (f0 < D) {   // D is a multiple of 16, so the quad is whole
+        for (long j = r; j < rows; j += kLamGroups) {
+            const long b = j / n_chunks, c = j % n_chunks;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(lam_part + (((size_t)b * H + h) * n_chunks + c) * D + f0);
+            s0 += v[0];
+            s1 += v[1];
+            s2 += v[2];
+            s3 += v[3];
+        }
+    }
+    part[r][4 * q] = s0;
+    part[r][4 * q + 1] = s1;
+    part[r][4 * q + 2] = s2;
+    part[r][4 * q + 3] = s3;
+    __syncthreads();
+    const int f = (blockIdx.x % fblocks) * 64 + threadIdx.x;
+    if (threadIdx.x < 64 && f < D) {
+        double t = 0.0;
+        for (int g = 0; g < kLamGroups; ++g) t += part[g][threadIdx.x];
+        dlam[(size_t)h * D + f] = (float)(-t);
+    }
 }
 
 hipError_t launch_bwd_gate(const BwdGateArgs& a, hipStream_t s) {
@@ -61,8 +87,8 @@ hipError_t launch_bwd_gate(const BwdGateArgs& a, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const long n = (long)a.H * a.d;
-    hipLaunchKernelGGL(bwd_lambda_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.lam_part, a.B, a.H,
+    const long blocks = (long)a.H * ((a.d + 63) / 64);
+    hipLaunchKernelGGL(bwd_lambda_kernel, dim3((unsigned)blocks), dim3(1024), 0, s, a.lam_part, a.B, a.H,
                        a.n_chunks, a.d, a.dlam);
     return hipGetLastError();
 }

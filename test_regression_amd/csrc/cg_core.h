@@ -33,8 +33,7 @@ struct alignas(16) CgLds {
     static constexpr int PD = lds_pitch(D);
     static constexpr int PS = lds_pitch_rows(D);
     static constexpr int PT = lds_pitch_rows(C);
-    static constexpr int REGION = NSTATE * HALF > D * PS ? NSTATE * HALF : D * PS;
-    float R[REGION];          // CG: stored S^H_c [, S_mid];  adjoint right side: (S^G_c)^T [D][PS]
+    float R[NSTATE * HALF];   // stored S^H_c [, S_mid]
     float KV[C * PD];         // K_c rows [token][feature]
     float KT[D * PT];         // K_c^T, later V_c^T   [feature][token]
     float L[C];               // l_i
@@ -383,22 +382,6 @@ struct PackedStateRegs {
         }
     }
 };
-
-// Stage a stored G chunk state (all 16 x 16 blocks, row-major block order,
-// MFMA operand order inside) into LDS transposed: element (row, col) to
-// dst[col * pitch + row]; workgroup-wide.
-template <int D>
-__device__ __forceinline__ void stage_g_state_transposed(float* dst, int pitch, const float* __restrict__ src,
-                                                         int tid, int nthr) {
-    constexpr int NT = D / 16;
-    for (int e = tid * 4; e < D * D; e += nthr * 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);   // columns 4q..4q+3 of row m
-        const int b = e / 256, l = (e % 256) / 4;
-        const int row = 16 * (b / NT) + l % 16, col = 16 * (b % NT) + 4 * (l / 16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(col + r) * pitch + row] = v[r];
-    }
-}
 
 // A chunk's rows of a [*, D] tensor held in registers between their global
 // load and their transposed store to LDS (pitch lds_pitch_rows(C)), so the

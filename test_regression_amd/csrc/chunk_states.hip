@@ -18,7 +18,9 @@
 // lane (1 KiB contiguous per wave).  An H block is kept in MFMA accumulator
 // order (lane 16q + m holds rows 4q..4q+3 of column m); a G block in MFMA
 // operand order (lane 16q + m holds columns 4q..4q+3 of row m), which is the
-// A operand the CG kernel's output product takes straight from memory.  The
+// A operand the CG kernel's output product takes straight from memory.  For
+// the backward's adjoint solve (g_transposed) the blocks of G^T are stored
+// in operand order instead, the A operand of its G^T g product.  The
 // exported final states are full and row-major ([d_v][d_k] for G).
 //
 // Work split: one workgroup per (head, {H, G}, 16*NW-row block of the
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
     int T, int n_chunks, float* __restrict__ SH, float* __restrict__ SG,
     float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks, long BH,
-    int* __restrict__ work_counter) {
+    int* __restrict__ work_counter, int g_transposed) {
     constexpr int NW = NWK;                    // waves per workgroup
     constexpr int RB = D / (16 * NW);          // row blocks per state
     constexpr int NT = D / 16;                 // 16-column tiles of the state
@@ -89,7 +91,13 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     const float* gh = gamma + (size_t)bh * T;
     // H: packed upper block triangle per chunk; G: full d x d per chunk
     float* Sout = which == 0 ? SH + (size_t)bh * n_chunks * HPACK : SG + (size_t)bh * n_chunks * D * D;
-    const float* sBcols = which == 0 ? sK : sB;
+    // H: A = weighted keys, B = keys.  G: the wave's slab is of G^T (A =
+    // weighted keys, B = values), whose accumulator blocks are G's blocks in
+    // operand order; with g_transposed, of G (A = weighted values, B = keys),
+    // whose accumulator blocks are G^T's blocks in operand order.
+    const bool gt = which == 1 && g_transposed;
+    const float* sArows = gt ? sB : sK;
+    const float* sBcols = which == 0 || gt ? sK : sB;
 
     f32x4 acc[NT];
 #pragma unroll
@@ -164,7 +172,8 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
                 if (which == 0) {
                     if (j >= a0) *reinterpret_cast<f32x4*>(dst + packed_blk<NT>(a0, j)) = acc[j];
                 } else {
-                    // block (a0, j) of G^T in accumulator order = block (j, a0) of G in operand order
+                    // block (a0, j) of the slab's matrix in accumulator order = block (j, a0)
+                    // of its transpose in operand order
                     *reinterpret_cast<f32x4*>(dst + (j * NT + a0) * 256) = acc[j];
                 }
             }
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int i = 16 * g + 4 * kk + s;
-                const float a = sK[i * PD + m0 + n] * sW[i];
+                const float a = sArows[i * PD + m0 + n] * sW[i];
 #pragma unroll
                 for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sBcols[i * PD + 16 * j + n], U[j]);
             }
@@ -209,7 +218,14 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
     }
-    if (which == 1 && final_G) {
+    if (which == 1 && final_G && g_transposed) {
+        float* dst = final_G + (size_t)bh * D * D;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+    }
+    if (which == 1 && final_G && !g_transposed) {
         // acc[j][r] = G[16j + n][m0 + 4kk + r]: four consecutive floats of a row of G
         float* dst = final_G + (size_t)bh * D * D;
 #pragma unroll
@@ -225,7 +241,7 @@ hipError_t launch_chunk_states_nw(const ChunkStatesArgs& a, hipStream_t s) {
     const long grid = ((a.BH + 7) / 8) * 8 * 2 * RB;
     hipLaunchKernelGGL((chunk_states_kernel<D, C, NW, In>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
                        (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG,
-                       a.final_H, a.final_G, a.write_chunks, a.BH, a.work_counter);
+                       a.final_H, a.final_G, a.write_chunks, a.BH, a.work_counter, a.g_transposed);
     return hipGetLastError();
 }
 

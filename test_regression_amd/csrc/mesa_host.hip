@@ -180,7 +180,7 @@ static mesa_status forward_impl(const void* q, const void* k, const void* v, int
 
     if (need_ws || final_H || final_G) {
         mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
-                                SH, SG, final_H, final_G, need_ws ? 1 : 0, work_counter};
+                                SH, SG, final_H, final_G, need_ws ? 1 : 0, work_counter, 0};
         hipError_t e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
         if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
     }
@@ -222,11 +222,14 @@ mesa_status mesa_forward_train(const void* q, const void* k, const void* v, int 
 // Backward workspace: forward chunk states, reverse states, per-token totals,
 // per-chunk regulariser sums; every segment a multiple of 4 floats.
 struct BwdLayout {
-    size_t sh, sg, pgx, pzx, beta, akey, lam, total;   // offsets in floats
+    size_t sh, sg, pgx, pzx, beta, akey, lam, counter, total;   // offsets in floats
 };
 
-static BwdLayout bwd_layout(long BH, int T, int d, long nc) {
+// lam: one d-vector per chunk and 16-token wave of the adjoint kernel;
+// counter: the adjoint kernel's chunk-claim counter (64 floats = 256 bytes).
+static BwdLayout bwd_layout(long BH, int T, int d, long nc, int chunk) {
     auto r4 = [](size_t n) { return (n + 3) / 4 * 4; };
+    const size_t waves = (size_t)std::max(1, chunk / 16);
     BwdLayout l{};
     size_t o = 0;
     l.sh = o;   o += r4((size_t)BH * nc * ((size_t)d * (d + 16) / 2));
@@ -235,7 +238,8 @@ static BwdLayout bwd_layout(long BH, int T, int d, long nc) {
     l.pzx = o;  o += r4((size_t)BH * nc * d * d);
     l.beta = o; o += r4((size_t)BH * T);
     l.akey = o; o += r4((size_t)BH * T);
-    l.lam = o;  o += r4((size_t)BH * nc * d);
+    l.lam = o;  o += r4((size_t)BH * nc * waves * d);
+    l.counter = o; o += 64;
     l.total = o;
     return l;
 }
@@ -243,7 +247,7 @@ static BwdLayout bwd_layout(long BH, int T, int d, long nc) {
 size_t mesa_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
     const long nc = ((long)T + chunk - 1) / chunk;
-    return bwd_layout((long)B * H, T, std::max(dk, dv), nc).total * sizeof(float);
+    return bwd_layout((long)B * H, T, std::max(dk, dv), nc, chunk).total * sizeof(float);
 }
 
 mesa_status mesa_backward(const void* k, const void* v, int qkv_dtype, const float* gamma, const float* lambda,
@@ -283,7 +287,8 @@ mesa_status mesa_backward(const void* k, const void* v, int qkv_dtype, const flo
         if (e != hipSuccess) return hip_fail(e, "zero fill of grad_lambda");
         return MESA_OK;
     }
-    const BwdLayout lay = bwd_layout(BH, T, dk, n_chunks);
+    const BwdLayout lay = bwd_layout(BH, T, dk, n_chunks, chunk);
+    const int waves = chunk / 16;   // per-wave partial sums of z (.) x per chunk
     if (workspace_bytes < lay.total * sizeof(float))
         return fail(MESA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
                     lay.total * sizeof(float));
@@ -292,13 +297,15 @@ mesa_status mesa_backward(const void* k, const void* v, int qkv_dtype, const flo
     hipError_t e;
     {
         mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
-                                ws + lay.sh, ws + lay.sg, nullptr, nullptr, 1, nullptr};
+                                ws + lay.sh, ws + lay.sg, nullptr, nullptr, 1,
+                                reinterpret_cast<int*>(ws + lay.counter), 1};
         e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
         if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
     }
     {
         mesa::BwdAdjointArgs a{k, v, gamma, lambda, x, out, grad_out, ws + lay.sh, ws + lay.sg, BH, H, T, dk, chunk,
-                               (int)n_chunks, bf16, max_iters, tol, grad_q, ws + lay.beta, z_iters, ws + lay.lam};
+                               (int)n_chunks, bf16, max_iters, tol, grad_q, ws + lay.beta, z_iters, ws + lay.lam,
+                               reinterpret_cast<int*>(ws + lay.counter)};
         e = timed_launch(MESA_KERNEL_BWD_ADJOINT, s, [&] { return mesa::launch_bwd_adjoint(a, s); });
         if (e != hipSuccess) return hip_fail(e, "backward adjoint kernel launch");
     }
@@ -315,8 +322,8 @@ mesa_status mesa_backward(const void* k, const void* v, int qkv_dtype, const flo
         if (e != hipSuccess) return hip_fail(e, "backward key/value kernel launch");
     }
     {
-        mesa::BwdGateArgs a{ws + lay.beta, ws + lay.akey, gamma, ws + lay.lam, BH, B, H, T, dk, (int)n_chunks,
-                            grad_gamma, grad_lambda};
+        mesa::BwdGateArgs a{ws + lay.beta, ws + lay.akey, gamma, ws + lay.lam, BH, B, H, T, dk,
+                            (int)n_chunks * waves, grad_gamma, grad_lambda};
         e = timed_launch(MESA_KERNEL_BWD_GATE, s, [&] { return mesa::launch_bwd_gate(a, s); });
         if (e != hipSuccess) return hip_fail(e, "backward gate kernel launch");
     }

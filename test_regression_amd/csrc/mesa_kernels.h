@@ -10,7 +10,8 @@ struct ChunkStatesArgs {
     const void* k; const void* v; const float* gamma;
     long BH; int T; int d; int chunk; int n_chunks; int bf16;
     float* SH; float* SG; float* final_H; float* final_G; int write_chunks;
-    int* work_counter;   // zeroed for the CG/output kernel that follows, or nullptr
+    int* work_counter;   // zeroed for the CG kernel that follows, or nullptr
+    int g_transposed;    // store G^T's blocks in operand order (the adjoint's A operand), not G's
 };
 
 struct CgOutputArgs {
@@ -51,7 +52,9 @@ struct BwdAdjointArgs {
     const void* k; const void* v; const float* gamma; const float* lambda;
     const float* x; const float* o; const float* gout; const float* SH; const float* SG;
     long BH; int H; int T; int d; int chunk; int n_chunks; int bf16; int max_iters; float tol;
-    float* dq; float* beta; int32_t* z_iters; float* lam_part;
+    float* dq; float* beta; int32_t* z_iters;
+    float* lam_part;     // per chunk and wave: sum over the wave's tokens of z (.) x  [BH*n_chunks][C/16][d]
+    int* work_counter;   // chunk claims; zero at launch
 };
 struct BwdStatesArgs {
     const float* g; const float* z; const float* x; const float* gamma;
@@ -66,7 +69,8 @@ struct BwdKvArgs {
 };
 struct BwdGateArgs {
     const float* beta; const float* akey; const float* gamma; const float* lam_part;
-    long BH; int B; int H; int T; int d; int n_chunks;
+    long BH; int B; int H; int T; int d;
+    int n_chunks;   // rows of lam_part per (batch, head): chunks times partial sums per chunk
     float* dgamma; float* dlam;
 };
 

@@ -24,6 +24,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CG_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_core.h",
+              "test_regression_amd/csrc/persistent.h",
               "test_regression_amd/csrc/mesa_device.h"]
 
 
