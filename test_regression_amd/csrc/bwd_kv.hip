@@ -14,12 +14,15 @@
 //          + e^{l_e - l_i} [(P^gx_c)^T v_i - (P^zx_c + (P^zx_c)^T) k_i]
 // Work split: one workgroup per (head, chunk); wave w owns keys 16w..16w+15
 // and holds their k_i, v_i in registers as the MFMA B operand (lane (n, kk):
-// features 16j + 4kk + r of key n).  Scores come out of the MFMA in exactly
-// the layout the next contraction (over tokens) takes as its B operand, so
-// the token tiles are the A operand both ways: read along rows for the
-// scores and down columns for the sums over tokens.  Then the two states
-// replace the token tiles in LDS.  Every MFMA chain starts from zero and is
-// only read afterwards.
+// features 16j + 4kk + r of key n).  The state terms come first: the
+// reverse-state kernel stores each state's blocks in both MFMA orders, so
+// P rows and P columns are A operands read straight from memory, while the
+// chunk's x, z, g rows travel from memory into LDS by direct loads.  Then
+// the within-chunk sums: scores come out of the MFMA in exactly the layout
+// the next contraction (over tokens) takes as its B operand, so the token
+// tiles are the A operand both ways, read along rows for the scores and
+// down columns for the sums over tokens.  Every MFMA chain starts from zero
+// and is only read afterwards.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -28,10 +31,7 @@ namespace mesa {
 template <int D, int C>
 struct alignas(16) KvLds {
     static constexpr int PD = lds_pitch(D);
-    static constexpr int PS = lds_pitch_rows(D);
-    static constexpr int TILES = 3 * C * PD;    // x, z, g rows of the chunk
-    static constexpr int STATES = 2 * D * PS;   // P^gx, P^zx rows
-    float R[TILES > STATES ? TILES : STATES];
+    float R[3 * C * PD];   // x, z, g rows of the chunk
     float L[C];
 };
 
@@ -56,56 +56,78 @@ __device__ __forceinline__ f32x4 token_scores(const float* rows, const f32x4 (&Z
     return acc;
 }
 
-// Y[j] += S[16j + m][:] . Z^T[:][n] for j in [J0, J0 + NJ) (ROWS), or
-// S[:][16j + m] . Z^T[:][n] (columns), or (S + S^T)[16j + m][:] . Z^T[:][n]
-// (SYM); S a full d x d state in LDS (pitch lds_pitch_rows(D)).  The output
-// blocks go in groups so that their A operands and accumulators fit in
-// registers.
-template <int D, int MODE, int J0, int NJ>   // MODE 0: rows, 1: columns, 2: rows + columns
-__device__ __forceinline__ void state_apply_part(const float* S, const f32x4 (&Z)[D / 16], int m, int kk,
-                                                 f32x4 (&Y)[D / 16]) {
+// The later chunks' terms for the wave's keys, straight from the stored
+// states (block (a, b) of a state at 256 (a NT + b) floats, accumulator
+// order; operand order D^2 floats further on):
+//   A1 = P^gx k_i,   A2 = (P^gx)^T v_i - (P^zx + (P^zx)^T) k_i.
+template <int D>
+__device__ __forceinline__ void state_terms(const float* __restrict__ Pg, const float* __restrict__ Pz, int lane,
+                                            const f32x4 (&Kb)[D / 16], const f32x4 (&Vb)[D / 16],
+                                            f32x4 (&A1)[D / 16], f32x4 (&A2)[D / 16]) {
     constexpr int NT = D / 16;
-    constexpr int PS = lds_pitch_rows(D);
+    constexpr int DD = D * D;
+    const float* pg = Pg + 4 * lane;
+    const float* pz = Pz + 4 * lane;
+    f32x4 A3[NT];
 #pragma unroll
-    for (int gg = 0; gg < NT; ++gg) {
-        f32x4 a[NJ];
+    for (int j = 0; j < NT; ++j) A1[j] = A2[j] = A3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // output block j, contraction group g: rows of P are operand block (j, g),
+    // rows of P^T are accumulator block (g, j)
+    auto ld = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
+    f32x4 bg[2][NT];
+    auto load_g = [&](int g, int buf) {
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            const int j = J0 + jj;
-            if constexpr (MODE != 1) a[jj] = ld4(S + (16 * j + m) * PS + 16 * gg + 4 * kk);
-            else a[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (MODE != 0) {
+        for (int j = 0; j < NT; ++j) bg[buf][j] = ld(pg + DD + (j * NT + g) * 256);
+    };
+    load_g(0, 0);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a[jj][s] += S[(16 * gg + 4 * kk + s) * PS + 16 * j + m];
-            }
-        }
+    for (int g = 0; g < NT; ++g) {
+        if (g + 1 < NT) load_g(g + 1, (g + 1) & 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) Y[J0 + jj] = mfma4(a[jj][s], Z[gg][s], Y[J0 + jj]);
+            for (int j = 0; j < NT; ++j) A1[j] = mfma4(bg[g & 1][j][s], Kb[g][s], A1[j]);
     }
-}
-
-template <int D, int MODE>
-__device__ __forceinline__ void state_apply(const float* S, const f32x4 (&Z)[D / 16], int m, int kk,
-                                            f32x4 (&Y)[D / 16]) {
-    constexpr int NT = D / 16;
-    constexpr int NJ = NT >= 4 ? NT / 2 : NT;
-    state_apply_part<D, MODE, 0, NJ>(S, Z, m, kk, Y);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NJ < NT) state_apply_part<D, MODE, NJ, NT - NJ>(S, Z, m, kk, Y);
+    auto load_t = [&](int g, int buf) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) bg[buf][j] = ld(pg + (g * NT + j) * 256);
+    };
+    load_t(0, 0);
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        if (g + 1 < NT) load_t(g + 1, (g + 1) & 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) A2[j] = mfma4(bg[g & 1][j][s], Vb[g][s], A2[j]);
+    }
+    auto load_z = [&](int g, int buf) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) bg[buf][j] = ld(pz + DD + (j * NT + g) * 256) + ld(pz + (g * NT + j) * 256);
+    };
+    load_z(0, 0);
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        if (g + 1 < NT) load_z(g + 1, (g + 1) & 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) A3[j] = mfma4(bg[g & 1][j][s], Kb[g][s], A3[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A2[j][r] -= A3[j][r];
 }
 
 template <int D, int C, int W, typename In>
 __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __restrict__ k,
                                         const In* __restrict__ v, size_t tok0, int valid,
-                                        const float* __restrict__ Pgx, const float* __restrict__ Pzx, int tid,
+                                        const float* __restrict__ Pgx, const float* __restrict__ Pzx,
                                         float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ akey) {
     constexpr int NT = D / 16;
     constexpr int NW = C / 16;
     constexpr int PD = lds_pitch(D);
-    constexpr int PS = lds_pitch_rows(D);
-    constexpr int NTHR = 64 * NW;
     const int n = lane & 15, kk = lane >> 4;
     const int il = 16 * W + n;          // chunk-local key index of the lane
     const bool key_ok = il < valid;
@@ -120,14 +142,25 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
         Kb[j] = key_ok ? load4(k + off) : f32x4{0.f, 0.f, 0.f, 0.f};
         Vb[j] = key_ok ? load4(v + off) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+
+    // ---- the later chunks, through the reverse states (while the tiles land) ----
+    f32x4 DV[NT], DK[NT];
+    state_terms<D>(Pgx, Pzx, lane, Kb, Vb, DV, DK);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct tile loads are in LDS
+    __syncthreads();                 // and every wave's, and the log decays
     const float li = L.L[il];
+    const float es = __expf(L.L[C - 1] - li);   // e^{l_end - l_i}
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            DV[j][r] *= es;
+            DK[j][r] *= es;
+        }
 
     // ---- within the chunk: tokens t >= i, one 16-token block at a time ----
     // Each block's sums are fresh MFMA chains, added into DK, DV on the VALU;
     // dk's pass and dv's pass run one after the other (register pressure).
-    f32x4 DV[NT], DK[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) DV[j] = DK[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int tb = W; tb < NW; ++tb) {
         const f32x4 s1 = token_scores<D>(X + 16 * tb * PD, Kb, n, kk);    // x_t . k_i
@@ -178,61 +211,18 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
         for (int j = 0; j < NT; ++j) DV[j] += BV[j];
     }
 
-    // ---- the later chunks, through the reverse states ----
-    __syncthreads();   // every wave is done with the token tiles
-    {
-        const float* src[2] = {Pgx, Pzx};
-        for (int e = tid * 4; e < 2 * D * D; e += NTHR * 4) {
-            const int which = e / (D * D), r = (e % (D * D)) / D, f = e % D;
-            *reinterpret_cast<f32x4*>(&L.R[which * D * PS + r * PS + f]) =
-                *reinterpret_cast<const f32x4*>(src[which] + (size_t)r * D + f);
-        }
-    }
-    __syncthreads();
-    const float* SGX = L.R;
-    const float* SZX = L.R + D * PS;
-    const float es = __expf(L.L[C - 1] - li);   // e^{l_end - l_i}
+    // ---- outputs ----
     float vd = 0.f, kd = 0.f;
-    {
-        f32x4 A1[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) A1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        state_apply<D, 0>(SGX, Kb, n, kk, A1);   // P^gx k_i
+    for (int j = 0; j < NT; ++j) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            f32x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                o[r] = DV[j][r] + es * A1[j][r];
-                vd += Vb[j][r] * o[r];
-            }
-            if (key_ok) *reinterpret_cast<f32x4*>(dv + (tok0 + il) * D + 16 * j + 4 * kk) = o;
+        for (int r = 0; r < 4; ++r) {
+            vd += Vb[j][r] * DV[j][r];
+            kd += Kb[j][r] * DK[j][r];
         }
-    }
-    {
-        f32x4 A2[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) A2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        state_apply<D, 1>(SGX, Vb, n, kk, A2);   // (P^gx)^T v_i
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) DK[j][r] += es * A2[j][r];
-    }
-    {
-        f32x4 A3[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) A3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        state_apply<D, 2>(SZX, Kb, n, kk, A3);   // (P^zx + P^zx^T) k_i
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            f32x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                o[r] = DK[j][r] - es * A3[j][r];
-                kd += Kb[j][r] * o[r];
-            }
-            if (key_ok) *reinterpret_cast<f32x4*>(dk + (tok0 + il) * D + 16 * j + 4 * kk) = o;
+        if (key_ok) {
+            *reinterpret_cast<f32x4*>(dv + (tok0 + il) * D + 16 * j + 4 * kk) = DV[j];
+            *reinterpret_cast<f32x4*>(dk + (tok0 + il) * D + 16 * j + 4 * kk) = DK[j];
         }
     }
     const float a = 0.5f * (kslot_sum(vd) + kslot_sum(kd));
@@ -247,7 +237,6 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ akey) {
     constexpr int NW = C / 16;
     constexpr int PD = lds_pitch(D);
-    constexpr int NTHR = 64 * NW;
     __shared__ KvLds<D, C> L;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -257,32 +246,37 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
     const int t0 = c * C;
     const int valid = min(C, T - t0);
     const size_t tok0 = (size_t)bh * T + t0;
-    const size_t soff = ((size_t)bh * n_chunks + c) * D * D;
+    const size_t soff = ((size_t)bh * n_chunks + c) * 2 * D * D;   // both block orders per chunk
 
-    // ---- x, z, g rows of the chunk; l ----
+    // ---- x, z, g rows of the chunk straight into LDS (rows past the end zeroed); l ----
+    // One row per wave instruction: lanes 0..D/4-1 each move 16 bytes.
     const float* srcs[3] = {x, z, gout};
-    for (int e = tid * 4; e < 3 * C * D; e += NTHR * 4) {
-        const int which = e / (C * D), i = (e % (C * D)) / D, f = e % D;
-        f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (i < valid) val = *reinterpret_cast<const f32x4*>(srcs[which] + (tok0 + i) * D + f);
-        *reinterpret_cast<f32x4*>(&L.R[which * C * PD + i * PD + f]) = val;
+    for (int e = w; e < 3 * C; e += NW) {
+        const int which = e / C, r = e % C;
+        float* row = L.R + which * C * PD + r * PD;
+        if (lane < D / 4) {
+            if (r < valid)
+                __builtin_amdgcn_global_load_lds(srcs[which] + (tok0 + r) * D + 4 * lane,
+                                                 (__attribute__((address_space(3))) void*)row, 16, 0, 0);
+            else
+                *reinterpret_cast<f32x4*>(row + 4 * lane) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     if (w == 0) {
         const float l = chunk_log_decay(gamma + tok0, valid, lane);
         if (lane < C) L.L[lane] = l;
     }
-    __syncthreads();
 
     const float* pg = Pgx + soff;
     const float* pz = Pzx + soff;
     if (w == 0) {
-        kv_wave<D, C, 0, In>(L, lane, k, v, tok0, valid, pg, pz, tid, dk, dv, akey);
+        kv_wave<D, C, 0, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
     } else if constexpr (NW > 1) {
         if (w == 1) {
-            kv_wave<D, C, 1, In>(L, lane, k, v, tok0, valid, pg, pz, tid, dk, dv, akey);
+            kv_wave<D, C, 1, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
         } else if constexpr (NW > 2) {
-            if (w == 2) kv_wave<D, C, 2, In>(L, lane, k, v, tok0, valid, pg, pz, tid, dk, dv, akey);
-            else kv_wave<D, C, 3, In>(L, lane, k, v, tok0, valid, pg, pz, tid, dk, dv, akey);
+            if (w == 2) kv_wave<D, C, 2, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
+            else kv_wave<D, C, 3, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
         }
     }
 }

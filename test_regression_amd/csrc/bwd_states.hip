@@ -15,6 +15,14 @@
 // is zero).  Work split as the forward's chunk-state kernel: one workgroup per
 // (head, {gx, zx}, row block), each wave a 16 x D slab of the running state in
 // MFMA accumulators, the rank-C update a fresh v_mfma_f32_16x16x4_f32 chain.
+//
+// Each state is stored twice per chunk, as 16 x 16 blocks of 16 bytes per
+// lane: first all blocks in MFMA accumulator order (lane 16q + m holds rows
+// 4q..4q+3 of column m), then all blocks in operand order (lane 16q + m
+// holds columns 4q..4q+3 of row m).  The key/value kernel takes P rows from
+// the second and P columns (rows of P^T) from the first, as MFMA A operands
+// straight from memory.  The operand-order copy of a block is the
+// accumulator block passed through a 1 KiB per-wave LDS scratch.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -33,6 +41,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     __shared__ float sX[C * PD];   // x rows of the chunk (the state's columns)
     __shared__ float sW[C];        // e^{l_t}
     __shared__ float sGam;         // e^{l_end}
+    constexpr int SP = 68;         // scratch pitch per k-slot group (16 lanes x 4 floats + 4)
+    __shared__ __attribute__((aligned(16))) float sT[NW][4 * SP];   // per-wave block transpose
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -49,7 +59,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     const float* ah = (which == 0 ? g : z) + (size_t)bh * T * D;
     const float* xh = x + (size_t)bh * T * D;
     const float* gh = gamma + (size_t)bh * T;
-    float* Pout = (which == 0 ? Pgx : Pzx) + (size_t)bh * n_chunks * D * D;
+    float* Pout = (which == 0 ? Pgx : Pzx) + (size_t)bh * n_chunks * 2 * D * D;
+    const int a0 = m0 / 16;        // the wave's row block
 
     f32x4 acc[NT];
 #pragma unroll
@@ -76,12 +87,24 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
         }
         __syncthreads();
 
-        // ---- the state of the tokens after this chunk ----
-        float* dst = Pout + (size_t)c * D * D;
+        // ---- the state of the tokens after this chunk: block (a0, j) in both orders ----
+        {
+            float* dst = Pout + (size_t)c * 2 * D * D + 4 * lane;
+            float* sc = sT[w];
+            const int m = lane & 15, q = lane >> 4;
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+            for (int j = 0; j < NT; ++j) {
+                *reinterpret_cast<f32x4*>(dst + (a0 * NT + j) * 256) = acc[j];
+                // element (row, col) of the block sits at sc[(row / 4) * SP + 4 col + row % 4]
+                *reinterpret_cast<f32x4*>(sc + kk * SP + 4 * n) = acc[j];
+                wave_lds_sync();
+                f32x4 o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
+                for (int u = 0; u < 4; ++u) o[u] = sc[(m / 4) * SP + 4 * (4 * q + u) + m % 4];
+                wave_lds_sync();
+                *reinterpret_cast<f32x4*>(dst + D * D + (a0 * NT + j) * 256) = o;
+            }
+        }
 
         // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain) ----
         f32x4 U[NT];
