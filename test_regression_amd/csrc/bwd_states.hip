@@ -44,9 +44,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     constexpr int SP = 68;         // scratch pitch per k-slot group (16 lanes x 4 floats + 4)
     __shared__ __attribute__((aligned(16))) float sT[NW][4 * SP];   // per-wave block transpose
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int tid0 = threadIdx.x;
+    const int lane = tid0 & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int n = lane & 15;
     const int kk = lane >> 4;
     constexpr int PARTS = 2 * RB;
@@ -66,26 +66,53 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int c = n_chunks - 1; c >= 0; --c) {
+    // The next (earlier) chunk's rows and gates are held in registers while
+    // this chunk's products run.  Lane-dependent addresses are rebuilt from an
+    // opaque copy of the thread id in every step instead of being held across
+    // the chunk loop (which would cost the second workgroup per CU).
+    constexpr int EL4 = C * D / (4 * NTHR);   // 4-element groups per thread per tile
+    static_assert(C * D % (4 * NTHR) == 0, "tile must split evenly over the workgroup");
+    f32x4 areg[EL4], xreg[EL4];
+    float greg = 1.0f;
+    auto prefetch = [&](int c) {
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
         const int t0 = c * C;
         const int valid = min(C, T - t0);
-        for (int e = tid * 4; e < C * D; e += NTHR * 4) {
+#pragma unroll
+        for (int u = 0; u < EL4; ++u) {
+            const int e = (tid + u * NTHR) * 4;
             const int i = e / D, f = e % D;
-            f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f}, xv = av;
+            areg[u] = xreg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (i < valid) {
-                av = *reinterpret_cast<const f32x4*>(ah + (size_t)(t0 + i) * D + f);
-                xv = *reinterpret_cast<const f32x4*>(xh + (size_t)(t0 + i) * D + f);
+                areg[u] = *reinterpret_cast<const f32x4*>(ah + (size_t)(t0 + i) * D + f);
+                xreg[u] = *reinterpret_cast<const f32x4*>(xh + (size_t)(t0 + i) * D + f);
             }
-            *reinterpret_cast<f32x4*>(&sA[i * PD + f]) = av;
-            *reinterpret_cast<f32x4*>(&sX[i * PD + f]) = xv;
+        }
+        if (w == 0) greg = lane < valid ? gh[t0 + lane] : 1.0f;
+    };
+
+    if (n_chunks > 0) prefetch(n_chunks - 1);
+    for (int c = n_chunks - 1; c >= 0; --c) {
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, n = lane & 15, kk = lane >> 4;
+        const int valid = min(C, T - c * C);
+#pragma unroll
+        for (int u = 0; u < EL4; ++u) {
+            const int e = (tid + u * NTHR) * 4;
+            const int i = e / D, f = e % D;
+            *reinterpret_cast<f32x4*>(&sA[i * PD + f]) = areg[u];
+            *reinterpret_cast<f32x4*>(&sX[i * PD + f]) = xreg[u];
         }
         if (w == 0) {
-            const float l = chunk_log_decay(gh + t0, valid, lane);
+            const float l = chunk_log_decay_of(greg, valid, lane);
             const float lend = __shfl(l, C - 1, 64);
             if (lane < C) sW[lane] = __expf(l);
             if (lane == 0) sGam = __expf(lend);
         }
         __syncthreads();
+        if (c > 0) prefetch(c - 1);
 
         // ---- the state of the tokens after this chunk: block (a0, j) in both orders ----
         {
