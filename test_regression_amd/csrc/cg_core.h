@@ -317,7 +317,9 @@ __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<
         const float pap = token_dot<NT>(P, Y);
         const bool act = !done && (pap > 0.f);
         if (!done && !act) done = true;   // breakdown guard
-        const float alpha = act ? rr / pap : 0.f;
+        // alpha and beta divide through the hardware reciprocal (about 1 ulp
+        // instead of a correctly rounded division sequence).
+        const float alpha = act ? rr * __builtin_amdgcn_rcpf(pap) : 0.f;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -326,15 +328,17 @@ __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<
                 R[j][r] -= alpha * Y[j][r];
             }
         const float rrn = token_dot<NT>(R, R);
-        if (act) {
-            const float beta = rrn / rr;
+        // Written for every lane (a stopped token gets beta = 0, so its
+        // direction becomes its frozen residual and stays finite): a lane-
+        // conditional update made the compiler copy P between register
+        // ranges at the end of every iteration.
+        const float beta = act ? rrn * __builtin_amdgcn_rcpf(rr) : 0.f;
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) P[j][r] = R[j][r] + beta * P[j][r];
-            rr = rrn;
-            it += 1;
-        }
+            for (int r = 0; r < 4; ++r) P[j][r] = R[j][r] + beta * P[j][r];
+        rr = act ? rrn : rr;
+        it += act ? 1 : 0;
     }
     return it;
 }
