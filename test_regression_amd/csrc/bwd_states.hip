@@ -49,9 +49,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int n = lane & 15;
     const int kk = lane >> 4;
+    // XCD-aware id (as the forward's chunk-state kernel): consecutive ids go
+    // round-robin over the 8 XCDs, so the 2*RB parts of head bh get ids
+    // xcd + 8*(slot) with equal xcd and share that XCD's L2 for x (and the
+    // g or z rows).
     constexpr int PARTS = 2 * RB;
-    const long bh = blockIdx.x / PARTS;
-    const int part = (int)(blockIdx.x % PARTS);
+    const long xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const long bh = (slot / PARTS) * 8 + xcd;
+    const int part = (int)(slot % PARTS);
     if (bh >= BH) return;   // whole workgroup
     const int rb = part % RB;
     const int which = part / RB;   // 0: gx, 1: zx
@@ -158,7 +163,7 @@ template <int D, int C>
 static hipError_t launch_t(const BwdStatesArgs& a, hipStream_t s) {
     constexpr int NW = D >= 64 ? 4 : D / 16;
     constexpr int RB = D / (16 * NW);
-    const long grid = a.BH * 2 * RB;
+    const long grid = ((a.BH + 7) / 8) * 8 * 2 * RB;   // heads rounded up to a multiple of 8
     hipLaunchKernelGGL((bwd_states_kernel<D, C, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a.g, a.z, a.x,
                        a.gamma, a.T, a.n_chunks, a.Pgx, a.Pzx, a.BH);
     return hipGetLastError();
