@@ -12,10 +12,12 @@
 // Work split: one 256-thread workgroup per head.  Thread (row, part) keeps
 // D/TPR consecutive entries of one row of H in registers for the whole solve,
 // so H is read once and written once; the matvec reads p from LDS.  The
-// matching entries of G are requested together with H's, so they arrive
-// while the CG runs.  The CG scalars are block reductions with a fixed order
-// (deterministic), and the stop test is block-uniform.  The step is bound by
-// HBM traffic on the two d x d states (read + write of H and G).
+// matching entries of G are loaded after the CG: holding only H during the
+// solve keeps the kernel at 168 registers, three workgroups per CU, whose
+// loads, solves and stores overlap.  The CG scalars are block reductions
+// with a fixed order (deterministic), and the stop test is block-uniform.
+// The step is bound by HBM traffic on the two d x d states (read + write of
+// H and G).
 //
 // Warm start (section "Significancia e Alegacoes" names warm-start
 // strategies as future work): with WARM, each head also carries its previous
@@ -30,7 +32,7 @@
 namespace mesa {
 
 template <int D, bool WARM, typename In>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(256, 3) void decode_kernel(   // three waves per SIMD
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ gamma, const float* __restrict__ lambda, float* __restrict__ SH,
     float* __restrict__ SG, float* __restrict__ SX, int warm_mode, int H, int max_iters, float tol,
@@ -79,8 +81,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
         return val;
     };
 
-    // ---- load this thread's pieces of H and G; H <- gamma H + k k^T ----
-    float hr[EPT], gr[EPT];
+    // ---- load this thread's pieces of H; H <- gamma H + k k^T ----
+    float hr[EPT];
     float* Hrow = SH + (size_t)nh * D * D + (size_t)row * D;
     float* Grow = SG + (size_t)nh * D * D + (size_t)row * D;
     if constexpr (EPT % 4 == 0) {
@@ -90,18 +92,9 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
             for (int u = 0; u < 4; ++u) hr[e + u] = x[u];
         }
-#pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-            const f32x4 y = *reinterpret_cast<const f32x4*>(Grow + col(e));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) gr[e + u] = y[u];
-        }
     } else {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            hr[e] = Hrow[col(e)];
-            gr[e] = Grow[col(e)];
-        }
+        for (int e = 0; e < EPT; ++e) hr[e] = Hrow[col(e)];
     }
     const float kr = sk[row];
 #pragma unroll
@@ -169,6 +162,18 @@ __global__ __launch_bounds__(256) void decode_kernel(
     __syncthreads();
 
     // ---- G <- gamma G + v k^T (in place), out = G x ----
+    float gr[EPT];
+    if constexpr (EPT % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+            const f32x4 y = *reinterpret_cast<const f32x4*>(Grow + col(e));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) gr[e + u] = y[u];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) gr[e] = Grow[col(e)];
+    }
     const float vr = sv[row];
     float o = 0.f;
 #pragma unroll
