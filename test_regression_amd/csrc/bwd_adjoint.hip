@@ -149,7 +149,7 @@ __device__ __forceinline__ bool adjoint_wave(CgLds<D, C>& L, int tid, ChunkPos& 
     if (tok_ok) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            *reinterpret_cast<f32x4*>(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk) = Z[j];
+            store_nt(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk, Z[j]);
         if (kk == 0) {
             beta[p.tok0 + tr] = b;
             if (z_iters) z_iters[p.tok0 + tr] = it;

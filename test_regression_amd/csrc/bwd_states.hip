@@ -126,7 +126,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
             const int m = lane & 15, q = lane >> 4;
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                *reinterpret_cast<f32x4*>(dst + (a0 * NT + j) * 256) = acc[j];
+                store_nt(dst + (a0 * NT + j) * 256, acc[j]);
                 // element (row, col) of the block sits at sc[(row / 4) * SP + 4 col + row % 4]
                 *reinterpret_cast<f32x4*>(sc + kk * SP + 4 * n) = acc[j];
                 wave_lds_sync();
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
 #pragma unroll
                 for (int u = 0; u < 4; ++u) o[u] = sc[(m / 4) * SP + 4 * (4 * q + u) + m % 4];
                 wave_lds_sync();
-                *reinterpret_cast<f32x4*>(dst + D * D + (a0 * NT + j) * 256) = o;
+                store_nt(dst + D * D + (a0 * NT + j) * 256, o);
             }
         }
 

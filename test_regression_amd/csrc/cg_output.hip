@@ -108,7 +108,7 @@ __device__ __forceinline__ bool cg_wave(CgLds<D, C>& L, int tid, ChunkPos& p, in
     if (iters && kk == 0 && tok_ok) iters[p.tok0 + tr] = it;
     if (x_out && tok_ok) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk) = X[j];
+        for (int j = 0; j < NT; ++j) store_nt(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk, X[j]);
     }
 
     // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
@@ -185,7 +185,7 @@ __device__ __forceinline__ bool cg_wave(CgLds<D, C>& L, int tid, ChunkPos& p, in
             f32x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = cw.eLo * OS[j][r] + OI[j][r];
-            *reinterpret_cast<f32x4*>(out + (p.tok0 + tr) * D + 16 * j + 4 * kk) = o;
+            store_nt(out + (p.tok0 + tr) * D + 16 * j + 4 * kk, o);
         }
     }
     if (!more) return false;

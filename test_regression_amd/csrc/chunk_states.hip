@@ -170,11 +170,11 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 if (which == 0) {
-                    if (j >= a0) *reinterpret_cast<f32x4*>(dst + packed_blk<NT>(a0, j)) = acc[j];
+                    if (j >= a0) store_nt(dst + packed_blk<NT>(a0, j), acc[j]);
                 } else {
                     // block (a0, j) of the slab's matrix in accumulator order = block (j, a0)
                     // of its transpose in operand order
-                    *reinterpret_cast<f32x4*>(dst + (j * NT + a0) * 256) = acc[j];
+                    store_nt(dst + (j * NT + a0) * 256, acc[j]);
                 }
             }
         }

@@ -60,6 +60,14 @@ __device__ __forceinline__ f32x4 load4(const bf16_t* p) {
     return r;
 }
 
+// Streaming (non-temporal) stores for outputs that no later instruction of
+// the kernel reads: marked for early eviction from the caches, which lets
+// HBM writes stream instead of competing with the kernel's reads for cache.
+__device__ __forceinline__ void store_nt(float* p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 // Registers holding 4 prefetched input elements (bf16 stays packed until staged).
 template <typename In> struct Raw4;
 template <> struct Raw4<float> {

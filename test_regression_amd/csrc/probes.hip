@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void mfma_bf16_probe(int iters, float* __restr
 __global__ __launch_bounds__(256) void copy_probe(const mesa::f32x4* __restrict__ src, mesa::f32x4* __restrict__ dst,
                                                   size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-        dst[i] = src[i];
+        __builtin_nontemporal_store(src[i], dst + i);
 }
 
 mesa_status launched(const char* what) {

@@ -55,19 +55,21 @@ __device__ __forceinline__ Vec<8> loadv(const bf16_t* p) {
     }
     return r;
 }
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 template <int F>
 __device__ __forceinline__ void storev(float* p, const Vec<F>& a) {
 #pragma unroll
     for (int i = 0; i < F; i += 4)
-        *reinterpret_cast<f32x4*>(p + i) = f32x4{a.v[i], a.v[i + 1], a.v[i + 2], a.v[i + 3]};
+        __builtin_nontemporal_store(f32x4{a.v[i], a.v[i + 1], a.v[i + 2], a.v[i + 3]}, reinterpret_cast<f32x4*>(p + i));
 }
 template <int F>
 __device__ __forceinline__ void storev(bf16_t* p, const Vec<F>& a) {
     uint32_t w[F / 2];
 #pragma unroll
     for (int i = 0; i < F / 2; ++i) w[i] = bf16_pack_rne(a.v[2 * i], a.v[2 * i + 1]);
-    if constexpr (F == 8) *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
-    else *reinterpret_cast<uint2*>(p) = uint2{w[0], w[1]};
+    if constexpr (F == 8) __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4_t*>(p));
+    else __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, reinterpret_cast<u32x2_t*>(p));
 }
 
 // Sum over the G adjacent lanes of a token row (G a power of two <= 32).
