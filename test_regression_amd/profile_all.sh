@@ -1,0 +1,38 @@
+#!/bin/bash
+# Writes the committed profile summaries (profiles/*.json, profiles/*.txt) from
+# the rocprofv3 output of one profiling run of bench.py:
+#   trace:  cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o t -- python3 $R/bench.py
+#   counts: cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/prof_fetch -o f -- python3 $R/bench.py $SHORT
+#           cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/prof_write -o w -- python3 $R/bench.py $SHORT
+# with SHORT="--steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start".
+# Usage: bash test_regression_amd/profile_all.sh <rocprof output dir>   (run from the repository root)
+set -euo pipefail
+OUT=${1:-gpurun_out}
+F=$OUT/prof_fetch/f_counter_collection.csv
+W=$OUT/prof_write/w_counter_collection.csv
+CMD='cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start ; then the same with --pmc WRITE_SIZE'
+PS="python -m test_regression_amd.profile_summary traffic $F $W --copy-bytes 1073741824"
+C=test_regression_amd/csrc
+$PS --kernel "cg_output_kernel<128, 64, mesa::bf16_t>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
+    > profiles/cg_output_layer_bf16_d128_T4096_traffic.json
+$PS --kernel "chunk_states_kernel<128, 64, 4, mesa::bf16_t>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
+    --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_traffic.json
+$PS --kernel "decode_kernel<128, false, float>" --command "$CMD" --sources $C/decode.hip $C/mesa_device.h \
+    > profiles/decode_f32_d128_N256_traffic.json
+$PS --kernel "qk_preprocess_kernel<128, mesa::bf16_t, mesa::bf16_t>" --command "$CMD" \
+    --sources $C/qk_preprocess.hip $C/mesa_device.h > profiles/qk_preprocess_bf16_d128_T4096_W4_traffic.json
+$PS --kernel "bwd_adjoint_kernel<128, 64, mesa::bf16_t>" --command "$CMD" \
+    --sources $C/bwd_adjoint.hip $C/cg_core.h $C/persistent.h $C/mesa_device.h \
+    > profiles/bwd_adjoint_layer_bf16_d128_T4096_traffic.json
+$PS --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$CMD" --sources $C/bwd_kv.hip $C/mesa_device.h \
+    > profiles/bwd_kv_layer_bf16_d128_T4096_traffic.json
+$PS --kernel "bwd_states_kernel<128, 64, 4>" --command "$CMD" --sources $C/bwd_states.hip $C/mesa_device.h \
+    > profiles/bwd_states_layer_bf16_d128_T4096_traffic.json
+$PS --kernel "hawk_summary_kernel<mesa::bf16_t, 4>" --command "$CMD" --sources $C/hawk.hip $C/mesa_device.h \
+    > profiles/hawk_summary_bf16_B8_T4096_D2048_traffic.json
+$PS --kernel "hawk_scan_kernel<mesa::bf16_t, 4>" --command "$CMD" --sources $C/hawk.hip $C/mesa_device.h \
+    > profiles/hawk_scan_bf16_B8_T4096_D2048_traffic.json
+python -m test_regression_amd.profile_summary stats $OUT/prof_trace/t_kernel_stats.csv \
+    --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "cg_output_kernel<128, 64, mesa::bf16_t>" --first 13 \
+    --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o t -- python3 $R/bench.py   (R = repository root; default bench: headline forward 3 warmup + 10 timed steps, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, forward-for-training + backward, CPU baseline; the first 13 CG/output dispatches are the headline forward)' \
+    > profiles/kernels_layer_bf16_d128_T4096_bench_stats.txt
