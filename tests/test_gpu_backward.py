@@ -149,3 +149,24 @@ def test_backward_layer_shape_sampled_heads():
     # -sum z (.) x with the GPU's own z (= dq) and the oracle's x is covered by
     # the small cases; here it must at least be finite and of the right shape
     assert np.isfinite(gpu["dlam"]).all() and gpu["dlam"].shape == (w.H, w.d)
+
+
+def test_backward_garbage_workspace_and_reuse():
+    """The adjoint kernel's chunk-claim counter lives in the backward
+    workspace tail and is reset by the library: garbage in the workspace,
+    reused for a second call, changes nothing."""
+    import torch
+    from test_regression_amd import mesa
+    B, H, T, d, C = 2, 3, 320, 64, 64
+    x = small_inputs(11, B, H, T, d, "f32")
+    q, k, v = (to_dev(x[n], "f32") for n in ("q", "k", "v"))
+    g, lam, gout = to_dev(x["gamma"], "f32"), to_dev(x["lam"], "f32"), to_dev(x["gout"], "f32")
+    out, _, xs = mesa.mesa_forward_train(q, k, v, g, lam, 12, 1e-4, C)
+    ref = mesa.mesa_backward(k, v, g, lam, xs, out, gout, 12, 1e-4, C)
+    ws = torch.full((mesa.mesa_backward_workspace_bytes(B, H, T, d, d, C),), 0x7f, dtype=torch.uint8,
+                    device=q.device)
+    for _ in range(2):
+        r = mesa.mesa_backward(k, v, g, lam, xs, out, gout, 12, 1e-4, C, workspace=ws)
+        torch.cuda.synchronize()
+        for name in ref:
+            assert torch.equal(r[name], ref[name]), name

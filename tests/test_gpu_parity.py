@@ -361,3 +361,24 @@ def test_run_twice_bitwise_identical():
     a = gpu_forward(x, w.dtype, w.max_iters, 1e-3, w.chunk)
     b = gpu_forward(x, w.dtype, w.max_iters, 1e-3, w.chunk)
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["iters"], b["iters"])
+
+
+def test_garbage_workspace_and_reuse():
+    """The CG kernel's chunk-claim counter lives in the workspace tail and is
+    reset by the chunk-state kernel: a workspace full of garbage, reused for
+    a second call, gives the same bits as a fresh one."""
+    import torch
+    from test_regression_amd import mesa
+    w = inputs.WORKLOADS["mid_bf16_d64_T2048"]
+    say("case garbage workspace", w.name)
+    x = inputs.forward_inputs(w, B=2)
+    q, k, v = (to_dev(x[n], w.dtype) for n in ("q", "k", "v"))
+    g, lam = to_dev(x["gamma"], "f32"), to_dev(x["lam"], "f32")
+    B, H, T, d = q.shape
+    ref_out, ref_it, _, _ = mesa.mesa_forward(q, k, v, g, lam, w.max_iters, 1e-3, w.chunk)
+    ws = torch.full((mesa.mesa_forward_workspace_bytes(B, H, T, d, d, w.chunk),), 0x7f, dtype=torch.uint8,
+                    device=q.device)
+    for _ in range(2):
+        out, it, _, _ = mesa.mesa_forward(q, k, v, g, lam, w.max_iters, 1e-3, w.chunk, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(it, ref_it)
