@@ -231,7 +231,12 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_adjoint_kernel(
 
     // ---- the first chunk: stage S^H_c, K_c (rows and transposed), lambda, l ----
     stage_packed_state<D, C>(L, SH + p.hoff, tid0, NTHR);
-    stage_chunk_rows<D, C, true, true>(L.KV, L.KT, k + p.tok0 * D, p.valid, tid0, NTHR);
+    {
+        ChunkRowsRegs<D, C, NTHR, In> k0;
+        k0.load(k + p.tok0 * D, p.valid, tid0);
+        k0.store_rows(L.KV, tid0);
+        k0.store_transposed(L.KT, tid0);
+    }
     for (int e = tid0; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)p.h * D + e];
     if (w == 0) {
         const float l = chunk_log_decay(gamma + p.tok0, p.valid, lane);

@@ -395,11 +395,20 @@ struct ChunkRowsRegs {
     static constexpr int EL4 = C * D / (4 * NTHR);
     static_assert(C * D % (4 * NTHR) == 0, "tile must split evenly over the workgroup");
     Raw4<In> x[EL4];   // bf16 stays packed until stored
+    // Group u of a thread: token i, features f..f+3.  Four neighbouring lanes
+    // take 16 consecutive features of one token and a wave 16 tokens, so the
+    // transposed stores of a wave hit distinct LDS banks but for a 2-way
+    // overlap (one token per lane group would put 16 lanes on a bank).
+    __device__ __forceinline__ static void place(int u, int tid, int& i, int& f) {
+        const int e4 = tid + u * NTHR;
+        i = (e4 >> 2) % C;
+        f = 16 * (e4 / (4 * C)) + 4 * (e4 & 3);
+    }
     __device__ __forceinline__ void load(const In* __restrict__ src, int valid, int tid) {
 #pragma unroll
         for (int u = 0; u < EL4; ++u) {
-            const int e = (tid + u * NTHR) * 4;
-            const int i = e / D, f = e % D;
+            int i, f;
+            place(u, tid, i, f);
             x[u].zero();
             if (i < valid) x[u].load(src + (size_t)i * D + f);
         }
@@ -408,8 +417,8 @@ struct ChunkRowsRegs {
         constexpr int PD = lds_pitch(D);
 #pragma unroll
         for (int u = 0; u < EL4; ++u) {
-            const int e = (tid + u * NTHR) * 4;
-            const int i = e / D, f = e % D;
+            int i, f;
+            place(u, tid, i, f);
             *reinterpret_cast<f32x4*>(&rows[i * PD + f]) = x[u].get();
         }
     }
@@ -417,31 +426,12 @@ struct ChunkRowsRegs {
         constexpr int PT = lds_pitch_rows(C);
 #pragma unroll
         for (int u = 0; u < EL4; ++u) {
-            const int e = (tid + u * NTHR) * 4;
-            const int i = e / D, f = e % D;
+            int i, f;
+            place(u, tid, i, f);
 #pragma unroll
             for (int r = 0; r < 4; ++r) tr[(f + r) * PT + i] = x[u].get()[r];
         }
     }
 };
-
-// Stage a chunk's rows of a [*, D] tensor as rows (pitch lds_pitch(D)) and/or
-// transposed (pitch lds_pitch_rows(C)); rows past `valid` are zero.
-template <int D, int C, bool ROWS, bool TRANSPOSED, typename In>
-__device__ __forceinline__ void stage_chunk_rows(float* rows, float* tr, const In* __restrict__ src, int valid,
-                                                 int tid, int nthr) {
-    constexpr int PD = lds_pitch(D);
-    constexpr int PT = lds_pitch_rows(C);
-    for (int e = tid * 4; e < C * D; e += nthr * 4) {
-        const int i = e / D, f = e % D;
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (i < valid) x = load4(src + (size_t)i * D + f);
-        if constexpr (ROWS) *reinterpret_cast<f32x4*>(&rows[i * PD + f]) = x;
-        if constexpr (TRANSPOSED) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) tr[(f + u) * PT + i] = x[u];
-        }
-    }
-}
 
 }  // namespace mesa
