@@ -174,9 +174,13 @@ __device__ __forceinline__ void form_mid_state(CgLds<D, C>& L, int w, int n, int
     float* S1 = L.R + CgLds<D, C>::HALF;
     const float lh = L.L[H - 1];
     const float Gh = __expf(lh);
+    // Token of k-slot group kk in step st: (st mod 4) + 4kk + 16(st / 4).  Its
+    // K row then starts at bank 4(st mod 4) + 16kk (the row pitch is 4 mod
+    // 64 banks), so the 64 lanes' reads hit distinct banks.
+    auto tok = [&](int st) { return (st & 3) + 4 * kk + 16 * (st >> 2); };
     float wk[H / 4];
 #pragma unroll
-    for (int st = 0; st < H / 4; ++st) wk[st] = __expf(lh - L.L[4 * st + kk]);
+    for (int st = 0; st < H / 4; ++st) wk[st] = __expf(lh - L.L[tok(st)]);
     int q = 0;
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
@@ -186,7 +190,7 @@ __device__ __forceinline__ void form_mid_state(CgLds<D, C>& L, int w, int n, int
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < H / 4; ++st) {
-                const int i = 4 * st + kk;
+                const int i = tok(st);
                 acc = mfma4(wk[st] * L.KV[i * PD + 16 * a + n], L.KV[i * PD + 16 * b + n], acc);
             }
             const float* s0 = S0 + blk<NT>(a, b) + (4 * kk) * kBlockPitch + n;
