@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cg_output_layer_bf16_d128_T4096_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "cg_output_layer_bf16_d128_T4096_mfma.json")
 KERNEL_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_core.h",
                   "test_regression_amd/csrc/persistent.h",
                   "test_regression_amd/csrc/mesa_device.h"]
@@ -58,17 +59,29 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the CG/output kernel from committed rocprofv3
-    counters, only if they were taken on the current kernel source."""
+def committed_counters(path):
+    """A committed rocprofv3 summary of the CG/output kernel, only if it was
+    taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t
+
+
+def measured_traffic():
+    """HBM bytes per launch of the CG/output kernel (FETCH_SIZE + WRITE_SIZE)."""
+    t = committed_counters(TRAFFIC_FILE)
+    return t.get("bytes_per_launch") if t else None
+
+
+def measured_mfma_busy():
+    """Fraction of SIMD cycles the MFMA unit was busy during the CG/output kernel."""
+    t = committed_counters(MFMA_FILE)
+    return t.get("mfma_busy_frac") if t else None
 
 
 def to_dev(torch, x, dtype, dev):
@@ -131,7 +144,8 @@ def headline(torch, mesa, inputs, args, dev):
         tflops=(fs + fcg + fo) * n_tok / (ms_step * 1e-3) / 1e12,
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_FP32_MFMA_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
-                      traffic=traffic, kernel="cg_output_kernel<128,64,bf16>",
+                      traffic=traffic, mfma_busy_frac=measured_mfma_busy(),
+                      kernel="cg_output_kernel<128,64,bf16>",
                       flops_per_launch=k2_flops, avg_launch_ms=round(k2_ms, 4)),
         kernels={
             "cg_output_kernel": dict(avg_ms=round(k2_ms, 4), launches=k2[1],

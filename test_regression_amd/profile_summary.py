@@ -10,6 +10,18 @@
 bytes per launch of one kernel, each counter scaled by what it read for a
 plain device copy of ``--copy-bytes`` bytes in the same run, and prints JSON
 (with a hash of the CG kernel's source so stale numbers can be detected).
+
+    python -m test_regression_amd.profile_summary mfma <counter_collection.csv> <agent_info.csv>
+        --kernel NAME_SUBSTRING [--first N] [--command CMD] [--alg-flops F]
+
+``mfma`` reads one ``--pmc`` run of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+SQ_INSTS_VALU_MFMA_MOPS_F32, SQ_INSTS_VALU_MFMA_F32, SQ_INSTS_VALU,
+SQ_INSTS_LDS, SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE and prints, per
+dispatch of one kernel (median): the fraction of SIMD cycles the MFMA unit was
+busy (busy cycles over GRBM_GUI_ACTIVE per XCD times the SIMD count, the
+rocprofiler ``MfmaUtil`` definition with the per-XCD maximum taken as the sum
+over XCDs divided by their count), the issued fp32 MFMA flops (512 per MOP),
+the instruction mix, and the share of LDS cycles lost to bank conflicts.
 """
 from __future__ import annotations
 
@@ -116,6 +128,43 @@ def cmd_traffic(a):
     }, indent=1))
 
 
+def cmd_mfma(a):
+    per = {}
+    for r in csv.DictReader(open(a.counters)):
+        if a.kernel not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {
+            "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    agent = next(r for r in csv.DictReader(open(a.agents)) if r.get("Name", "").startswith("gfx"))
+    nxcc, nsimd = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+    disp = [per[k] for k in sorted(per)]
+    if a.first:
+        disp = disp[:a.first]
+    med = lambda f: statistics.median(f(d) for d in disp)
+    cycles = med(lambda d: d["GRBM_GUI_ACTIVE"] / nxcc)
+    mops = med(lambda d: d["SQ_INSTS_VALU_MFMA_MOPS_F32"])
+    ns = med(lambda d: d["ns"])
+    out = {
+        "kernel": a.kernel, "command": a.command, "kernel_source_hash": cg_source_hash(a.sources),
+        "sources": a.sources or CG_SOURCES, "dispatches": len(disp), "first": a.first,
+        "gpu": agent["Name"], "xcc": nxcc, "simds": nsimd,
+        "duration_us_under_counters": round(ns / 1e3, 1),
+        "clock_mhz": round(cycles / ns * 1e3, 1),
+        "mfma_busy_frac": round(med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / nxcc * nsimd)), 4),
+        "mfma_f32_instructions": med(lambda d: d["SQ_INSTS_VALU_MFMA_F32"]),
+        "mfma_f32_issued_flops": mops * 512,
+        "valu_instructions": med(lambda d: d["SQ_INSTS_VALU"]),
+        "lds_instructions": med(lambda d: d["SQ_INSTS_LDS"]),
+        "lds_bank_conflict_frac": round(med(lambda d: d["SQ_LDS_BANK_CONFLICT"] / d["SQ_LDS_IDX_ACTIVE"]
+                                            if d["SQ_LDS_IDX_ACTIVE"] else 0.0), 4),
+    }
+    if a.alg_flops:
+        out["algorithmic_flops"] = a.alg_flops
+        out["issued_mfma_over_algorithmic"] = round(mops * 512 / a.alg_flops, 4)
+    print(json.dumps(out, indent=1))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -136,8 +185,16 @@ def main(argv=None):
                    help="use only the first N matching dispatches (0: all)")
     t.add_argument("--sources", nargs="*", default=None,
                    help="repository-relative sources whose hash identifies the kernel (default: the CG kernel's)")
+    m = sub.add_parser("mfma")
+    m.add_argument("counters")
+    m.add_argument("agents")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--command", default="")
+    m.add_argument("--first", type=int, default=0)
+    m.add_argument("--alg-flops", type=float, default=0.0, help="algorithmic flops per launch")
+    m.add_argument("--sources", nargs="*", default=None)
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.what](a)
 
 
 if __name__ == "__main__":
