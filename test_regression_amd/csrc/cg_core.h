@@ -261,6 +261,16 @@ __device__ __forceinline__ float token_dot(const f32x4 (&A)[NT], const f32x4 (&B
     return kslot_sum(s);
 }
 
+// num / den through the hardware reciprocal (about 1 ulp).  The reciprocal
+// flushes a denormal input to zero, so a denominator below the smallest normal
+// float is scaled by 2^64 first and the quotient scaled back: a token that
+// keeps iterating after its residual has shrunk to denormal size (fixed
+// iteration counts far past convergence) keeps finite alpha and beta.
+__device__ __forceinline__ float rcp_div(float num, float den) {
+    const float s = den < 1.17549435e-38f ? 0x1p64f : 1.0f;
+    return (num * __builtin_amdgcn_rcpf(den * s)) * s;
+}
+
 // Y = H_t P over the wave's tokens (the stored state plus the sub-chunk's
 // causal keys), plus diag(lambda) P when LAMBDA: one CG matvec.
 template <int D, int C, int W, bool LAMBDA>
@@ -322,8 +332,8 @@ __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<
         const bool act = !done && (pap > 0.f);
         if (!done && !act) done = true;   // breakdown guard
         // alpha and beta divide through the hardware reciprocal (about 1 ulp
-        // instead of a correctly rounded division sequence).
-        const float alpha = act ? rr * __builtin_amdgcn_rcpf(pap) : 0.f;
+        // instead of a correctly rounded division sequence), see rcp_div.
+        const float alpha = act ? rcp_div(rr, pap) : 0.f;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -336,7 +346,7 @@ __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<
         // direction becomes its frozen residual and stays finite): a lane-
         // conditional update made the compiler copy P between register
         // ranges at the end of every iteration.
-        const float beta = act ? rrn * __builtin_amdgcn_rcpf(rr) : 0.f;
+        const float beta = act ? rcp_div(rrn, rr) : 0.f;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll

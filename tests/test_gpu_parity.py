@@ -268,6 +268,22 @@ def test_single_iteration_is_one_matvec():
     assert (g["iters"] == 1).all()
 
 
+@pytest.mark.parametrize("d", [16, 128])
+def test_iterating_far_past_convergence_stays_finite(d):
+    """Lambda = I and a fixed cap far above d: every token's CG converges
+    exactly and then keeps iterating on a residual that shrinks into the
+    denormal range, where the hardware reciprocal would flush it to zero.
+    alpha and beta must stay finite and the output must still match."""
+    B, H, T = 1, 2, 96
+    say("case past convergence", (B, H, T, d))
+    x = small_inputs(41, B, H, T, d, "f32", lam=(1.0, 1.0))
+    g = gpu_forward(x, "f32", 4 * d + 40, 0.0, 64)
+    r = oracle_forward(x, "f32", 4 * d + 40, 0.0)
+    assert np.isfinite(g["out"]).all()
+    assert rel_l2(g["out"], r["out"]) <= 1e-4
+    compare_counts(g["iters"], r, 4 * d + 40, 0.0)
+
+
 def test_edge_cases():
     d = 32
     say("case edges")
