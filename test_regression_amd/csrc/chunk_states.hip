@@ -29,7 +29,14 @@
 // and walks the chunks in order.  Per chunk the update is one
 // (16 x C) x (C x D) product on v_mfma_f32_16x16x4_f32 with the weighted keys
 // as the A operand and the keys (H) or values (G^T) as the B operand; the
-// contraction runs over the chunk's tokens.  Workgroup ids are
+// contraction runs over the chunk's tokens.  For bf16 keys and values the
+// product runs on v_mfma_f32_16x16x32_bf16 instead: the values a_i, b_i are
+// exact bf16, and each weighted value w_i a_i (a float) is split exactly into
+// three bf16 parts (the top 8, next 8 and last 8 bits of its significand),
+// so the three bf16 products sum to the float product terms up to the
+// accumulation order.  The chunk's values are then staged as bf16 with two
+// consecutive tokens per 32-bit LDS word, so a lane's eight-token MFMA
+// operand is four word reads.  Workgroup ids are
 // mapped so that the 2*RB workgroups of one head land on the same XCD (ids
 // congruent mod 8) and share its L2 for the key and value tiles.
 #include "mesa_device.h"
@@ -60,10 +67,16 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
     constexpr int PD = lds_pitch(D);
     constexpr int NTHR = 64 * NW;
     constexpr int HPACK = D * (D + 16) / 2;    // floats of a packed upper block triangle
+    constexpr bool BF = sizeof(In) == 2;       // bf16 keys and values: the split bf16 product
+    // bf16 tiles: word (p, f) holds feature f of tokens 2p (low half) and
+    // 2p + 1 (high half); the pitch D + 8 puts the four lane groups' rows
+    // (2 token pairs apart) 16 banks apart.
+    constexpr int PP = D + 8;
+    constexpr int TILE = BF ? (C / 2) * PP : C * PD;
 
-    __shared__ float sK[C * PD];   // keys of the chunk (A operand; B operand for H)
-    __shared__ float sB[C * PD];   // values of the chunk (B operand for G^T)
-    __shared__ float sW[C];        // e^{l_end - l_i}
+    __shared__ float sK[TILE];     // keys of the chunk (A operand; B operand for H)
+    __shared__ float sB[TILE];     // values of the chunk (B operand for G^T)
+    __shared__ alignas(16) float sW[C];   // e^{l_end - l_i}
     __shared__ float sGam;         // e^{l_end}
 
     const int tid0 = threadIdx.x;
@@ -140,13 +153,29 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, n = lane & 15, kk = lane >> 4;
-        // ---- stage the chunk's keys (and values) in LDS as fp32 ----
+        // ---- stage the chunk's keys (and values) in LDS ----
 #pragma unroll
         for (int u = 0; u < EL4; ++u) {
             const int e = (tid + u * NTHR) * 4;
             const int i = e / D, f = e % D;
-            *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = kreg[sl][u].get();
-            if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = vreg[sl][u].get();
+            if constexpr (BF) {
+                uint16_t* k16 = reinterpret_cast<uint16_t*>(sK) + ((i >> 1) * PP + f) * 2 + (i & 1);
+                uint16_t* v16 = reinterpret_cast<uint16_t*>(sB) + ((i >> 1) * PP + f) * 2 + (i & 1);
+                const uint2 kb = kreg[sl][u].raw(), vb = vreg[sl][u].raw();
+                k16[0] = (uint16_t)kb.x;
+                k16[2] = (uint16_t)(kb.x >> 16);
+                k16[4] = (uint16_t)kb.y;
+                k16[6] = (uint16_t)(kb.y >> 16);
+                if (which) {
+                    v16[0] = (uint16_t)vb.x;
+                    v16[2] = (uint16_t)(vb.x >> 16);
+                    v16[4] = (uint16_t)vb.y;
+                    v16[6] = (uint16_t)(vb.y >> 16);
+                }
+            } else {
+                *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = kreg[sl][u].get();
+                if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = vreg[sl][u].get();
+            }
         }
         if (w == 0) {
             // within-chunk log decays (tokens past the end count as gamma = 1)
@@ -185,14 +214,69 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
         f32x4 U[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {
+            // 32 tokens per MFMA: lane group kk's eight k-slots e are tokens
+            // 32 g2 + 16 (e / 4) + 4 kk + e % 4, i.e. the token pairs
+            // p = 16 g2 + 8 h + 2 kk + {0, 1} for h = 0, 1 (a chunk of 16
+            // tokens leaves h = 1 empty).
+            const uint32_t* tA = reinterpret_cast<const uint32_t*>(sArows);
+            const uint32_t* tB = reinterpret_cast<const uint32_t*>(sBcols);
 #pragma unroll
-        for (int g = 0; g < C / 16; ++g) {
+            for (int g2 = 0; g2 < (C + 31) / 32; ++g2) {
+                constexpr int NH = C >= 32 ? 2 : 1;
+                uint32_t ah[4], am[4], al[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int i = 16 * g + 4 * kk + s;
-                const float a = sArows[i * PD + m0 + n] * sW[i];
+                for (int q = 0; q < 4; ++q) ah[q] = am[q] = al[q] = 0u;
 #pragma unroll
-                for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sBcols[i * PD + 16 * j + n], U[j]);
+                for (int h = 0; h < NH; ++h) {
+                    const int p0 = 16 * g2 + 8 * h + 2 * kk;
+                    const f32x4 wv = *reinterpret_cast<const f32x4*>(&sW[2 * p0]);
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        const uint32_t pr = tA[(p0 + d) * PP + m0 + n];
+                        uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const float a = __uint_as_float(t ? (pr & 0xffff0000u) : (pr << 16));
+                            const float x = a * wv[2 * d + t];
+                            // exact split: x = hi + mid + lo, each a bf16
+                            hb[t] = __float_as_uint(x) & 0xffff0000u;
+                            const float r1 = x - __uint_as_float(hb[t]);
+                            mb[t] = __float_as_uint(r1) & 0xffff0000u;
+                            lb[t] = __float_as_uint(r1 - __uint_as_float(mb[t])) & 0xffff0000u;
+                        }
+                        const int q = 2 * h + d;
+                        ah[q] = (hb[0] >> 16) | hb[1];
+                        am[q] = (mb[0] >> 16) | mb[1];
+                        al[q] = (lb[0] >> 16) | lb[1];
+                    }
+                }
+                const bf16x8 Ah = as_bf16x8(ah), Am = as_bf16x8(am), Al = as_bf16x8(al);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    uint32_t b[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) {
+                        const int p0 = 16 * g2 + 8 * h + 2 * kk;
+                        b[2 * h] = tB[p0 * PP + 16 * j + n];
+                        b[2 * h + 1] = tB[(p0 + 1) * PP + 16 * j + n];
+                    }
+                    const bf16x8 Bj = as_bf16x8(b);
+                    U[j] = mfma_bf16x32(Ah, Bj, U[j]);
+                    U[j] = mfma_bf16x32(Am, Bj, U[j]);
+                    U[j] = mfma_bf16x32(Al, Bj, U[j]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < C / 16; ++g) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int i = 16 * g + 4 * kk + s;
+                    const float a = sArows[i * PD + m0 + n] * sW[i];
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sBcols[i * PD + 16 * j + n], U[j]);
+                }
             }
         }
         const float G = sGam;

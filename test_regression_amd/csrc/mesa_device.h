@@ -40,6 +40,17 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA: lane 16g + m supplies row m (A) or column m (B) at
+// k-slots 8g..8g+7, element e of its eight in bits 16(e % 2) of word e / 2.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+__device__ __forceinline__ f32x4 mfma_bf16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // bf16 stored as raw 16-bit patterns.
 struct bf16_t { uint16_t bits; };
 
@@ -80,6 +91,7 @@ template <> struct Raw4<bf16_t> {
     uint2 v;
     __device__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
     __device__ void zero() { v = make_uint2(0u, 0u); }
+    __device__ uint2 raw() const { return v; }
     __device__ f32x4 get() const {
         return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
                      __uint_as_float(v.y & 0xffff0000u)};

@@ -320,6 +320,22 @@ def test_empty_sequence_exports_zero_state():
     assert out.numel() == 0 and bool((fH == 0).all()) and bool((fG == 0).all())
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("d", [16, 128])
+def test_bf16_states_at_float_accuracy(d, chunk):
+    """bf16 keys and values: the chunk states come from bf16 MFMAs on an
+    exact three-part split of the weighted keys, so the exported states must
+    keep float accuracy (a two-part split would leave errors near 2^-17)."""
+    B, H, T = 1, 2, 200
+    say("case bf16 states", (B, H, T, d, chunk))
+    x = small_inputs(43, B, H, T, d, "bf16")
+    g = gpu_forward(x, "bf16", 0, 0.0, chunk, return_final=True)
+    r = oracle_forward(x, "bf16", 0, 0.0, final_state=True)
+    eh, eg = rel_l2(g["final_H"], r["final_H"]), rel_l2(g["final_G"], r["final_G"])
+    say(f"final_H rel_l2={eh:.2e} final_G rel_l2={eg:.2e}")
+    assert eh <= 5e-7 and eg <= 5e-7
+
+
 def test_final_states_and_decode_continue_forward():
     import torch
     from test_regression_amd import mesa
