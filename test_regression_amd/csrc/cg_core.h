@@ -208,9 +208,10 @@ __device__ __forceinline__ void contract_state(const f32x4 (&Z)[D / 16], const f
 template <int D, typename In>
 __host__ __device__ constexpr bool split_keys() { return sizeof(In) == 2 && D % 32 == 0; }
 
-// High halves of a (low) and b (high) in one word.
+// High halves of a (low) and b (high) in one word: one v_perm_b32, whose
+// byte selectors 0-3 pick bytes of its second source and 4-7 of its first.
 __device__ __forceinline__ uint32_t pack_hi(float a, float b) {
-    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
 // The exact-bf16 values of two 4-element pieces as one operand.
