@@ -523,11 +523,10 @@ __device__ __forceinline__ void wave_matvec(const CgLds<D, C>& L, const CgWave<D
 // on entry (B layout); X receives the solution.  Stops before an update when
 // |r| / |b| < tol (tested as r.r < (tol |b|)^2), or on r.r == 0 or
 // p.Ap <= 0; b == 0 gives x = 0 and no update.  Returns the lane's token's
-// update count.
-template <int D, int C, int W, bool BFK = false>
-__device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<D, C, W>& cw, f32x4 (&R)[D / 16],
-                                             f32x4 (&X)[D / 16], int max_iters, float tol) {
-    constexpr int NT = D / 16;
+// update count.  matvec(P, Y) sets Y = (H_t + Lambda) P for the wave.
+template <int NT, typename Matvec>
+__device__ __forceinline__ int cg_solve(f32x4 (&R)[NT], f32x4 (&X)[NT], int max_iters, float tol,
+                                        const Matvec& matvec) {
     f32x4 P[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -543,7 +542,7 @@ __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<
         if (!done && (rr < stop_rr || rr == 0.f)) done = true;
         if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
         f32x4 Y[NT];
-        wave_matvec<D, C, W, true, BFK>(L, cw, P, Y);
+        matvec(P, Y);
         const float pap = token_dot<NT>(P, Y);
         const bool act = !done && (pap > 0.f);
         if (!done && !act) done = true;   // breakdown guard
@@ -571,6 +570,15 @@ __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<
         it += act ? 1 : 0;
     }
     return it;
+}
+
+// The chunk-local CG of wave W: Y = (H_t + Lambda) P from the LDS tiles.
+template <int D, int C, int W, bool BFK = false>
+__device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<D, C, W>& cw, f32x4 (&R)[D / 16],
+                                             f32x4 (&X)[D / 16], int max_iters, float tol) {
+    return cg_solve<D / 16>(R, X, max_iters, tol, [&](const f32x4 (&P)[D / 16], f32x4 (&Y)[D / 16]) {
+        wave_matvec<D, C, W, true, BFK>(L, cw, P, Y);
+    });
 }
 
 // Stage the stored upper block triangle of S^H (blocks (a, b), a <= b, in

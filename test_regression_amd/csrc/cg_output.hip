@@ -49,6 +49,7 @@
 #include <atomic>
 
 #include "cg_core.h"
+#include "cg_split.h"
 #include "mesa_kernels.h"
 #include "persistent.h"
 
@@ -278,16 +279,229 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 keys: the same persistent chunk loop with every matvec product on
+// bf16 MFMAs (cg_split.h).  The chunk state is held whole (three bf16 planes
+// of the full matrix), so there is no mid-chunk state: every wave's state
+// term starts from S^H_c and its intra-chunk terms run over the causal keys
+// from the chunk start.  Four workgroup barriers per chunk, as in cg_wave.
+template <int D, int C, int W>
+__device__ __forceinline__ bool cg_split_wave(SplitLds<D, C>& L, int tid, ChunkPos& p, int n_chunks, int H, int T,
+                                              long total, int* __restrict__ work_counter,
+                                              Raw4<bf16_t> (&qr)[D / 16], const bf16_t* __restrict__ q,
+                                              const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                              const float* __restrict__ gamma, const float* __restrict__ lambda,
+                                              const float* __restrict__ SH, const float* __restrict__ SG,
+                                              int max_iters, float tol, float* __restrict__ out,
+                                              int32_t* __restrict__ iters, float* __restrict__ x_out) {
+    using SWv = SplitWave<D, C, W>;
+    constexpr int NT = D / 16;
+    constexpr int NW = C / 16;
+    constexpr int NTHR = 64 * NW;
+    constexpr int NLAM = (D + NTHR - 1) / NTHR;
+    const int lane = tid & 63;
+    const SWv sw(L, lane);
+    const int n = sw.n, kk = sw.kk, tr = sw.tr;
+    const bool tok_ok = tr < p.valid;
+
+    int ticket = 0;
+    if (W == 0 && lane == 0) ticket = atomicAdd(work_counter, 1);
+
+    // ---- CG from x = 0 with r = p = q ----
+    f32x4 X[NT], R[NT], lam[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        R[j] = qr[j].get();
+        lam[j] = lds4(&L.Lam[16 * j + 4 * kk]);   // held across the CG, off the update's path
+    }
+    const int it = cg_solve<NT>(R, X, max_iters, tol, [&](const f32x4 (&P)[NT], f32x4 (&Y)[NT]) {
+        f32x4 YS[NT], YI[NT];
+        split_matvec<D, C, W>(L, sw, P, YS, YI);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[j][r] = sw.eLo * YS[j][r] + YI[j][r] + lam[j][r] * P[j][r];
+    });
+    asm volatile("" : "+v"(tid));
+    if (W == 0 && lane == 0) L.next = ticket;
+
+    if (iters && kk == 0 && tok_ok) iters[p.tok0 + tr] = it;
+    if (x_out && tok_ok) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) store_nt(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk, X[j]);
+    }
+
+    // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
+    ChunkRowsRegs<D, C, NTHR, bf16_t> vrows;
+    vrows.load(v + p.tok0 * D, p.valid, tid);
+    f32x4 Wo[2 * SWv::NS];
+    {
+        bf16x8 Xs[D / 32][3];
+#pragma unroll
+        for (int qq = 0; qq < D / 32; ++qq) split_operands(X[2 * qq], X[2 * qq + 1], Xs[qq][0], Xs[qq][1], Xs[qq][2]);
+        f32x4 Sc[SWv::NBO];
+#pragma unroll
+        for (int ib = 0; ib < SWv::NBO; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        split_scores<D, C, SWv::NBO>(L, Xs, n, kk, Sc);
+#pragma unroll
+        for (int ib = 0; ib < 2 * SWv::NS; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wo[ib][r] = ib < SWv::NBO ? Sc[ib < SWv::NBO ? ib : 0][r] * sw.dec[ib][r] : 0.f;
+    }
+    PackedStateRegs<D, NTHR> nsh;
+    ChunkRowsRegs<D, C, NTHR, bf16_t> nk;
+    float ngam = 1.0f, nlam[NLAM];
+    f32x4 OS[NT], OI[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) OS[j] = OI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+        const float* gl = SG + p.soff + 4 * lane;
+        constexpr int NB_G = 3;
+        f32x4 ga[NB_G][NT];
+        auto gload = [&](int g, int buf) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) ga[buf][j] = *reinterpret_cast<const f32x4*>(gl + (j * NT + g) * 256);
+        };
+#pragma unroll
+        for (int g = 0; g < NB_G - 1 && g < NT; ++g) gload(g, g);
+#pragma unroll
+        for (int g = 0; g < NT; ++g) {
+            if (g + NB_G - 1 < NT) gload(g + NB_G - 1, (g + NB_G - 1) % NB_G);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) OS[j] = mfma4(ga[g % NB_G][j][s2], X[g][s2], OS[j]);
+        }
+    }
+    __syncthreads();   // (A) every wave is done with the state planes, K_c rows, K_c^T, l and lambda
+    const long nidx = (long)gridDim.x + __builtin_amdgcn_readfirstlane(L.next);
+    const bool more = nidx < total;
+    const ChunkPos pn = chunk_pos<D, C>(more ? nidx : 0, n_chunks, H, T);
+    if (more) {
+        nsh.load(SH + pn.hoff, tid);
+        nk.load(k + pn.tok0 * D, pn.valid, tid);
+        if (W == 0) ngam = lane < pn.valid ? gamma[pn.tok0 + lane] : 1.0f;
+#pragma unroll
+        for (int u = 0; u < NLAM; ++u) {
+            const int e = tid + u * NTHR;
+            nlam[u] = e < D ? lambda[(size_t)pn.h * D + e] : 0.f;
+        }
+    }
+    load_queries<D, bf16_t>(qr, q, pn.tok0, more ? pn.valid : 0, tr, kk);
+    stage_transposed<D, C, NTHR>(L.KT, vrows, tid);
+    __syncthreads();   // (B)
+    split_apply<D, C, SWv::NS>(L, Wo, n, kk, OI);
+    if (tok_ok) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            f32x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = sw.eLo * OS[j][r] + OI[j][r];
+            store_nt(out + (p.tok0 + tr) * D + 16 * j + 4 * kk, o);
+        }
+    }
+    if (!more) return false;
+
+    // ---- stage the next chunk ----
+    stage_state_planes<D, NTHR>(L.S, nsh, tid);
+    stage_key_rows<D, C, NTHR>(L.KR, nk, tid);
+    if (W == 0) {
+        const float l = chunk_log_decay_of(ngam, pn.valid, lane);
+        if (lane < C) L.L[lane] = l;
+    }
+#pragma unroll
+    for (int u = 0; u < NLAM; ++u) {
+        const int e = tid + u * NTHR;
+        if (e < D) L.Lam[e] = nlam[u];
+    }
+    __syncthreads();   // (C) every wave is done with V_c^T
+    stage_transposed<D, C, NTHR>(L.KT, nk, tid);
+    __syncthreads();   // (D)
+    p = pn;
+    return true;
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(64 * (C / 16)) void cg_split_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ gamma, const float* __restrict__ lambda,
+    const float* __restrict__ SH, const float* __restrict__ SG, int H, int T, int n_chunks, long total,
+    int* __restrict__ work_counter, int max_iters, float tol, float* __restrict__ out, int32_t* __restrict__ iters,
+    float* __restrict__ x_out) {
+    constexpr int NW = C / 16;
+    constexpr int NT = D / 16;
+    constexpr int NTHR = 64 * NW;
+    __shared__ SplitLds<D, C> L;
+
+    const int tid0 = threadIdx.x;
+    const int lane = tid0 & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    ChunkPos p = chunk_pos<D, C>(blockIdx.x, n_chunks, H, T);
+
+    // ---- the first chunk ----
+    {
+        PackedStateRegs<D, NTHR> s0;
+        s0.load(SH + p.hoff, tid0);
+        ChunkRowsRegs<D, C, NTHR, bf16_t> k0;
+        k0.load(k + p.tok0 * D, p.valid, tid0);
+        stage_state_planes<D, NTHR>(L.S, s0, tid0);
+        stage_key_rows<D, C, NTHR>(L.KR, k0, tid0);
+        stage_transposed<D, C, NTHR>(L.KT, k0, tid0);
+    }
+    for (int e = tid0; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)p.h * D + e];
+    if (w == 0) {
+        const float l = chunk_log_decay(gamma + p.tok0, p.valid, lane);
+        if (lane < C) L.L[lane] = l;
+    }
+    Raw4<bf16_t> qr[NT];
+    load_queries<D, bf16_t>(qr, q, p.tok0, p.valid, 16 * w + (lane & 15), lane >> 4);
+    __syncthreads();
+
+    for (bool more = true; more;) {
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        if (w == 0) {
+            more = cg_split_wave<D, C, 0>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma, lambda,
+                                          SH, SG, max_iters, tol, out, iters, x_out);
+        } else if constexpr (NW > 1) {
+            if (w == 1) {
+                more = cg_split_wave<D, C, 1>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma,
+                                              lambda, SH, SG, max_iters, tol, out, iters, x_out);
+            } else if constexpr (NW > 2) {
+                if (w == 2)
+                    more = cg_split_wave<D, C, 2>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma,
+                                                  lambda, SH, SG, max_iters, tol, out, iters, x_out);
+                else
+                    more = cg_split_wave<D, C, 3>(L, tid, p, n_chunks, H, T, total, work_counter, qr, q, k, v, gamma,
+                                                  lambda, SH, SG, max_iters, tol, out, iters, x_out);
+            }
+        }
+    }
+}
+
 template <int D, int C, typename In>
 static hipError_t launch_t(const CgOutputArgs& a, hipStream_t s) {
-    static std::atomic<long> resident[kMaxDevices];
-    const long total = a.BH * a.n_chunks;
-    const int block = 64 * (C / 16);
-    const long grid = std::min(total, resident_workgroups(cg_output_kernel<D, C, In>, block, resident));
-    hipLaunchKernelGGL((cg_output_kernel<D, C, In>), dim3((unsigned)grid), dim3(block), 0, s,
-                       (const In*)a.q, (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.SH, a.SG,
-                       a.H, a.T, a.n_chunks, total, a.work_counter, a.max_iters, a.tol, a.out, a.iters, a.x_out);
-    return hipGetLastError();
+    if constexpr (split_keys<D, In>()) {
+        static std::atomic<long> resident_split[kMaxDevices];
+        const long total = a.BH * a.n_chunks;
+        const int block = 64 * (C / 16);
+        const long grid = std::min(total, resident_workgroups(cg_split_kernel<D, C>, block, resident_split));
+        hipLaunchKernelGGL((cg_split_kernel<D, C>), dim3((unsigned)grid), dim3(block), 0, s,
+                           (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, a.gamma, a.lambda, a.SH,
+                           a.SG, a.H, a.T, a.n_chunks, total, a.work_counter, a.max_iters, a.tol, a.out, a.iters,
+                           a.x_out);
+        return hipGetLastError();
+    } else {
+        static std::atomic<long> resident[kMaxDevices];
+        const long total = a.BH * a.n_chunks;
+        const int block = 64 * (C / 16);
+        const long grid = std::min(total, resident_workgroups(cg_output_kernel<D, C, In>, block, resident));
+        hipLaunchKernelGGL((cg_output_kernel<D, C, In>), dim3((unsigned)grid), dim3(block), 0, s,
+                           (const In*)a.q, (const In*)a.k, (const In*)a.v, a.gamma, a.lambda, a.SH, a.SG,
+                           a.H, a.T, a.n_chunks, total, a.work_counter, a.max_iters, a.tol, a.out, a.iters,
+                           a.x_out);
+        return hipGetLastError();
+    }
 }
 
 template <int D, typename In>
