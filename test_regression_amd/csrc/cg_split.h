@@ -22,8 +22,9 @@
 // CG vectors hold exactly these in registers).  Rows of the state planes and
 // of the key tiles store each 32-column block permuted so that those eight
 // columns are contiguous (perm32): a lane's operand is one 128-bit read.  Row
-// pitches are an odd multiple of 4 words, so the 16 rows a 16-lane group
-// reads start 16 bytes apart modulo the 64 banks.
+// pitches are 8 words more than the row (an odd multiple of 8 words), so the
+// 16-byte pieces that rows m = 0..7 and lane groups kk = 0, 1 read fall on
+// distinct banks.
 #pragma once
 #include "cg_core.h"
 
@@ -36,8 +37,8 @@ __host__ __device__ constexpr int perm32(int c) {
 
 template <int D, int C>
 struct alignas(16) SplitLds {
-    static constexpr int SW = D / 2 + 4;                    // words per state / key row
-    static constexpr int KW = (C >= 32 ? C : 32) / 2 + 4;   // words per K^T row (at least one 32-key step)
+    static constexpr int SW = D / 2 + 8;                    // words per state / key row
+    static constexpr int KW = (C >= 32 ? C : 32) / 2 + 8;   // words per K^T row (at least one 32-key step)
     uint32_t S[3][D * SW];   // S^H_c: bf16 planes hi, mid, lo; row r = feature r, columns perm32
     uint32_t KR[C * SW];     // K_c rows (bf16, columns perm32)
     uint32_t KT[D * KW];     // K_c^T, later V_c^T (bf16, tokens perm32)
@@ -216,10 +217,10 @@ __device__ __forceinline__ uint16_t hi16(float x) { return (uint16_t)(__float_as
 // in accumulator order) written as the three bf16 planes of the full
 // symmetric matrix.
 template <int D, int NTHR>
-__device__ __forceinline__ void stage_state_planes(uint32_t (&S)[3][D * (D / 2 + 4)],
+__device__ __forceinline__ void stage_state_planes(uint32_t (&S)[3][D * (D / 2 + 8)],
                                                    const PackedStateRegs<D, NTHR>& st, int tid) {
     constexpr int NT = D / 16;
-    constexpr int SW = D / 2 + 4;
+    constexpr int SW = D / 2 + 8;
     constexpr int HPACK = D * (D + 16) / 2;
 #pragma unroll
     for (int u = 0; u < PackedStateRegs<D, NTHR>::N; ++u) {
@@ -262,7 +263,7 @@ __device__ __forceinline__ void stage_state_planes(uint32_t (&S)[3][D * (D / 2 +
 // A chunk's bf16 rows as K rows (columns perm32).
 template <int D, int C, int NTHR>
 __device__ __forceinline__ void stage_key_rows(uint32_t* KR, const ChunkRowsRegs<D, C, NTHR, bf16_t>& rg, int tid) {
-    constexpr int SW = D / 2 + 4;
+    constexpr int SW = D / 2 + 8;
 #pragma unroll
     for (int u = 0; u < ChunkRowsRegs<D, C, NTHR, bf16_t>::EL4; ++u) {
         int i, f;
@@ -275,7 +276,7 @@ __device__ __forceinline__ void stage_key_rows(uint32_t* KR, const ChunkRowsRegs
 template <int D, int C, int NTHR>
 __device__ __forceinline__ void stage_transposed(uint32_t* KT, const ChunkRowsRegs<D, C, NTHR, bf16_t>& rg,
                                                  int tid) {
-    constexpr int KW = (C >= 32 ? C : 32) / 2 + 4;
+    constexpr int KW = (C >= 32 ? C : 32) / 2 + 8;
 #pragma unroll
     for (int u = 0; u < ChunkRowsRegs<D, C, NTHR, bf16_t>::EL4; ++u) {
         int i, f;
