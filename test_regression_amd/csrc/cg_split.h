@@ -159,23 +159,25 @@ __device__ __forceinline__ void split_matvec(const SplitLds<D, C>& L, const Spli
             Sc[ib] = mfma_bf16x32(A, Z[0], Sc[ib]);
         }
     };
+    // Two row blocks at a time, their nine products interleaved, so that
+    // consecutive MFMAs never wait on each other's accumulator.
     auto state_step = [&](int q, const bf16x8 (&Z)[3]) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int off = (16 * j + sw.n) * SW + 16 * q + 4 * sw.kk;
-            const bf16x8 A0 = lds_bf16x8(&L.S[0][off]);
-            const bf16x8 A1 = lds_bf16x8(&L.S[1][off]);
-            const bf16x8 A2 = lds_bf16x8(&L.S[2][off]);
-            // smallest terms first
-            YS[j] = mfma_bf16x32(A2, Z[2], YS[j]);
-            YS[j] = mfma_bf16x32(A2, Z[1], YS[j]);
-            YS[j] = mfma_bf16x32(A1, Z[2], YS[j]);
-            YS[j] = mfma_bf16x32(A2, Z[0], YS[j]);
-            YS[j] = mfma_bf16x32(A1, Z[1], YS[j]);
-            YS[j] = mfma_bf16x32(A0, Z[2], YS[j]);
-            YS[j] = mfma_bf16x32(A1, Z[0], YS[j]);
-            YS[j] = mfma_bf16x32(A0, Z[1], YS[j]);
-            YS[j] = mfma_bf16x32(A0, Z[0], YS[j]);
+        for (int j = 0; j < NT; j += 2) {
+            bf16x8 A[2][3];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int off = (16 * (j + h) + sw.n) * SW + 16 * q + 4 * sw.kk;
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) A[h][pl] = lds_bf16x8(&L.S[pl][off]);
+            }
+            // smallest terms first: (plane, part) = (2,2) (2,1) (1,2) (2,0) (1,1) (0,2) (1,0) (0,1) (0,0)
+            constexpr int PL[9] = {2, 2, 1, 2, 1, 0, 1, 0, 0};
+            constexpr int PT[9] = {2, 1, 2, 0, 1, 2, 0, 1, 0};
+#pragma unroll
+            for (int t = 0; t < 9; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) YS[j + h] = mfma_bf16x32(A[h][PL[t]], Z[PT[t]], YS[j + h]);
         }
     };
     auto apply = [&]() {
