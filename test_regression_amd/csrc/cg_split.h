@@ -159,14 +159,15 @@ __device__ __forceinline__ void split_matvec(const SplitLds<D, C>& L, const Spli
             Sc[ib] = mfma_bf16x32(A, Z[0], Sc[ib]);
         }
     };
-    // Two row blocks at a time, their nine products interleaved, so that
+    // JI row blocks at a time, their nine products interleaved, so that
     // consecutive MFMAs never wait on each other's accumulator.
+    constexpr int JI = NT >= 4 ? 4 : NT;
     auto state_step = [&](int q, const bf16x8 (&Z)[3]) {
 #pragma unroll
-        for (int j = 0; j < NT; j += 2) {
-            bf16x8 A[2][3];
+        for (int j = 0; j < NT; j += JI) {
+            bf16x8 A[JI][3];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < JI; ++h) {
                 const int off = (16 * (j + h) + sw.n) * SW + 16 * q + 4 * sw.kk;
 #pragma unroll
                 for (int pl = 0; pl < 3; ++pl) A[h][pl] = lds_bf16x8(&L.S[pl][off]);
@@ -177,7 +178,7 @@ __device__ __forceinline__ void split_matvec(const SplitLds<D, C>& L, const Spli
 #pragma unroll
             for (int t = 0; t < 9; ++t)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) YS[j + h] = mfma_bf16x32(A[h][PL[t]], Z[PT[t]], YS[j + h]);
+                for (int h = 0; h < JI; ++h) YS[j + h] = mfma_bf16x32(A[h][PL[t]], Z[PT[t]], YS[j + h]);
         }
     };
     auto apply = [&]() {
