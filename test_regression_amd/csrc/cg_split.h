@@ -115,16 +115,20 @@ template <int D, int C, int NS>
 __device__ __forceinline__ void split_apply(const SplitLds<D, C>& L, const f32x4 (&W)[2 * NS], int m, int kk,
                                             f32x4 (&Y)[D / 16]) {
     constexpr int NT = D / 16;
+    constexpr int JI = NT >= 4 ? 4 : NT;   // row blocks whose chains interleave
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        bf16x8 Wh, Wm, Wl;
-        split_operands(W[2 * s], W[2 * s + 1], Wh, Wm, Wl);
+        bf16x8 Wp[3];
+        split_operands(W[2 * s], W[2 * s + 1], Wp[0], Wp[1], Wp[2]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const bf16x8 A = kt_operand<D, C>(L, j, s, m, kk);
-            Y[j] = mfma_bf16x32(A, Wl, Y[j]);
-            Y[j] = mfma_bf16x32(A, Wm, Y[j]);
-            Y[j] = mfma_bf16x32(A, Wh, Y[j]);
+        for (int j = 0; j < NT; j += JI) {
+            bf16x8 A[JI];
+#pragma unroll
+            for (int h = 0; h < JI; ++h) A[h] = kt_operand<D, C>(L, j + h, s, m, kk);
+#pragma unroll
+            for (int t = 2; t >= 0; --t)
+#pragma unroll
+                for (int h = 0; h < JI; ++h) Y[j + h] = mfma_bf16x32(A[h], Wp[t], Y[j + h]);
         }
     }
 }
@@ -144,20 +148,21 @@ __device__ __forceinline__ void split_matvec(const SplitLds<D, C>& L, const Spli
     constexpr int NQ = D / 32;
     constexpr int SW = SplitLds<D, C>::SW;
     const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 Sc[2 * SWv::NS];
+    // scores: one accumulator per key block and split part (independent chains)
+    f32x4 Sp[SWv::NBO][3];
 #pragma unroll
-    for (int ib = 0; ib < 2 * SWv::NS; ++ib) Sc[ib] = zero;
+    for (int ib = 0; ib < SWv::NBO; ++ib) Sp[ib][0] = Sp[ib][1] = Sp[ib][2] = zero;
 #pragma unroll
     for (int j = 0; j < NT; ++j) YS[j] = YI[j] = zero;
     auto split_step = [&](int q, bf16x8 (&Z)[3]) { split_operands(P[2 * q], P[2 * q + 1], Z[0], Z[1], Z[2]); };
     auto scores_step = [&](int q, const bf16x8 (&Z)[3]) {
+        bf16x8 A[SWv::NBO];
 #pragma unroll
-        for (int ib = 0; ib < SWv::NBO; ++ib) {
-            const bf16x8 A = lds_bf16x8(&L.KR[(16 * ib + sw.n) * SW + 16 * q + 4 * sw.kk]);
-            Sc[ib] = mfma_bf16x32(A, Z[2], Sc[ib]);
-            Sc[ib] = mfma_bf16x32(A, Z[1], Sc[ib]);
-            Sc[ib] = mfma_bf16x32(A, Z[0], Sc[ib]);
-        }
+        for (int ib = 0; ib < SWv::NBO; ++ib) A[ib] = lds_bf16x8(&L.KR[(16 * ib + sw.n) * SW + 16 * q + 4 * sw.kk]);
+#pragma unroll
+        for (int t = 2; t >= 0; --t)
+#pragma unroll
+            for (int ib = 0; ib < SWv::NBO; ++ib) Sp[ib][t] = mfma_bf16x32(A[ib], Z[t], Sp[ib][t]);
     };
     // JI row blocks at a time, their nine products interleaved, so that
     // consecutive MFMAs never wait on each other's accumulator.
@@ -186,7 +191,11 @@ __device__ __forceinline__ void split_matvec(const SplitLds<D, C>& L, const Spli
 #pragma unroll
         for (int ib = 0; ib < 2 * SWv::NS; ++ib)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Wt[ib][r] = Sc[ib][r] * sw.dec[ib][r];
+            for (int r = 0; r < 4; ++r)
+                Wt[ib][r] = ib < SWv::NBO
+                                ? ((Sp[ib < SWv::NBO ? ib : 0][2][r] + Sp[ib < SWv::NBO ? ib : 0][1][r]) +
+                                   Sp[ib < SWv::NBO ? ib : 0][0][r]) * sw.dec[ib][r]
+                                : 0.f;
         split_apply<D, C, SWv::NS>(L, Wt, sw.n, sw.kk, YI);
     };
     bf16x8 Za[3], Zb[3];
