@@ -21,21 +21,25 @@
 // LDS of its own.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "cg_core.h"
+#include "cg_split.h"
 #include "mesa_kernels.h"
 #include "persistent.h"
 
 namespace mesa {
 
 // B = G_t^T g_t over the wave's tokens (B layout), and g_t . o_t.
-template <int D, int C, int W, typename In>
-__device__ __forceinline__ void adjoint_rhs(const CgLds<D, C>& L, const CgWave<D, C, W>& cw, int lane,
+// Lds/Wave: CgLds/CgWave (fp32 K^T tile) or SplitLds/SplitWave (bf16 K^T
+// tile, split apply).
+template <int D, int C, int W, typename In, typename Lds, typename Wave>
+__device__ __forceinline__ void adjoint_rhs(const Lds& L, const Wave& cw, int lane,
                                             const ChunkPos& p, const In* __restrict__ v,
                                             const float* __restrict__ SG, const float* __restrict__ gout,
                                             const float* __restrict__ o, f32x4 (&B)[D / 16], float& go) {
     constexpr int NT = D / 16;
-    constexpr int NBO = CgWave<D, C, W>::NBO;
+    constexpr int NBO = W + 1;
     const bool tok_ok = cw.tr < p.valid;
     f32x4 Gv[NT];
     {
@@ -88,12 +92,22 @@ __device__ __forceinline__ void adjoint_rhs(const CgLds<D, C>& L, const CgWave<D
             }
         }
     }
-    f32x4 Wg[NBO];
+    if constexpr (std::is_same<Lds, SplitLds<D, C>>::value) {
+        constexpr int NS = SplitWave<D, C, W>::NS;
+        f32x4 Wg[2 * NS];
 #pragma unroll
-    for (int ib = 0; ib < NBO; ++ib)
+        for (int ib = 0; ib < 2 * NS; ++ib)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Wg[ib][r] = Sc[ib][r] * cw.dec[ib][r];
-    contract_intra<D, C, NBO, 0>(Wg, L.KT, cw.n, cw.kk, BI);
+            for (int r = 0; r < 4; ++r) Wg[ib][r] = ib < NBO ? Sc[ib < NBO ? ib : 0][r] * cw.dec[ib][r] : 0.f;
+        split_apply<D, C, NS>(L, Wg, cw.n, cw.kk, BI);
+    } else {
+        f32x4 Wg[NBO];
+#pragma unroll
+        for (int ib = 0; ib < NBO; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wg[ib][r] = Sc[ib][r] * cw.dec[ib][r];
+        contract_intra<D, C, NBO, 0>(Wg, L.KT, cw.n, cw.kk, BI);
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -269,8 +283,200 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_adjoint_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 keys: the adjoint CG and H x on the forward's split-state machinery
+// (cg_split.h: the chunk state as three exact bf16 planes, every product of
+// the matvec on bf16 MFMAs).  Two workgroup barriers per chunk: (A) every
+// wave is done with the LDS tiles; (B) the next chunk is staged.
+template <int D, int C, int W>
+__device__ __forceinline__ bool adjoint_split_wave(SplitLds<D, C>& L, int tid, ChunkPos& p, int n_chunks, int H,
+                                                   int T, long total, int* __restrict__ work_counter,
+                                                   const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                   const float* __restrict__ gamma, const float* __restrict__ lambda,
+                                                   const float* __restrict__ x, const float* __restrict__ o,
+                                                   const float* __restrict__ gout, const float* __restrict__ SH,
+                                                   const float* __restrict__ SG, int max_iters, float tol,
+                                                   float* __restrict__ dq, float* __restrict__ beta,
+                                                   int32_t* __restrict__ z_iters, float* __restrict__ lam_part) {
+    using SWv = SplitWave<D, C, W>;
+    constexpr int NT = D / 16;
+    constexpr int NW = C / 16;
+    constexpr int NTHR = 64 * NW;
+    constexpr int NLAM = (D + NTHR - 1) / NTHR;
+    const int lane = tid & 63;
+    const SWv sw(L, lane);
+    const int kk = sw.kk, tr = sw.tr;
+    const bool tok_ok = tr < p.valid;
+
+    int ticket = 0;
+    if (W == 0 && lane == 0) ticket = atomicAdd(work_counter, 1);
+
+    // ---- right side and adjoint CG ----
+    f32x4 Bv[NT], Z[NT], lam[NT];
+    float go = 0.f;
+    adjoint_rhs<D, C, W, bf16_t>(L, sw, lane, p, v, SG, gout, o, Bv, go);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) lam[j] = lds4(&L.Lam[16 * j + 4 * kk]);
+    const int it = cg_solve<NT>(Bv, Z, max_iters, tol, [&](const f32x4 (&P)[NT], f32x4 (&Y)[NT]) {
+        f32x4 YS[NT], YI[NT];
+        split_matvec<D, C, W>(L, sw, P, YS, YI);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[j][r] = sw.eLo * YS[j][r] + YI[j][r] + lam[j][r] * P[j][r];
+    });
+
+    // ---- H_t x_t, beta, dq ----
+    f32x4 Xv[NT], Hx[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const size_t off = (p.tok0 + tr) * D + 16 * j + 4 * kk;
+        Xv[j] = tok_ok ? *reinterpret_cast<const f32x4*>(x + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+        f32x4 YS[NT], YI[NT];
+        split_matvec<D, C, W>(L, sw, Xv, YS, YI);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Hx[j][r] = sw.eLo * YS[j][r] + YI[j][r];
+    }
+    asm volatile("" : "+v"(tid));
+    const float b = go - token_dot<NT>(Z, Hx);
+    if (tok_ok) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            store_nt(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk, Z[j]);
+        if (kk == 0) {
+            beta[p.tok0 + tr] = b;
+            if (z_iters) z_iters[p.tok0 + tr] = it;
+        }
+    }
+    if (W == 0 && lane == 0) L.next = ticket;
+    __syncthreads();   // (A) every wave is done with the state planes, K_c tiles, l and lambda
+
+    const long nidx = (long)gridDim.x + __builtin_amdgcn_readfirstlane(L.next);
+    const bool more = nidx < total;
+    const ChunkPos pn = chunk_pos<D, C>(more ? nidx : 0, n_chunks, H, T);
+    PackedStateRegs<D, NTHR> nsh;
+    ChunkRowsRegs<D, C, NTHR, bf16_t> nk;
+    float ngam = 1.0f, nlam[NLAM];
+    if (more) {
+        nsh.load(SH + pn.hoff, tid);
+        nk.load(k + pn.tok0 * D, pn.valid, tid);
+        if (W == 0) ngam = lane < pn.valid ? gamma[pn.tok0 + lane] : 1.0f;
+#pragma unroll
+        for (int u = 0; u < NLAM; ++u) {
+            const int e = tid + u * NTHR;
+            nlam[u] = e < D ? lambda[(size_t)pn.h * D + e] : 0.f;
+        }
+    }
+
+    // ---- sum over the wave's tokens of z (.) x (lanes n = 0 of each k-slot group) ----
+    {
+        const size_t chunk = p.soff / ((size_t)D * D);
+        float* dst = lam_part + (chunk * NW + W) * D + 4 * kk;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            f32x4 s;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[r] = rowsum16(Z[j][r] * Xv[j][r]);
+            if ((lane & 15) == 0) *reinterpret_cast<f32x4*>(dst + 16 * j) = s;
+        }
+    }
+    if (!more) return false;
+
+    // ---- stage the next chunk ----
+    stage_state_planes<D, NTHR>(L.S, nsh, tid);
+    stage_key_rows<D, C, NTHR>(L.KR, nk, tid);
+    stage_transposed<D, C, NTHR>(L.KT, nk, tid);
+    if (W == 0) {
+        const float l = chunk_log_decay_of(ngam, pn.valid, lane);
+        if (lane < C) L.L[lane] = l;
+    }
+#pragma unroll
+    for (int u = 0; u < NLAM; ++u) {
+        const int e = tid + u * NTHR;
+        if (e < D) L.Lam[e] = nlam[u];
+    }
+    __syncthreads();   // (B)
+    p = pn;
+    return true;
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(64 * (C / 16)) void bwd_adjoint_split_kernel(
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gamma,
+    const float* __restrict__ lambda, const float* __restrict__ x, const float* __restrict__ o,
+    const float* __restrict__ gout, const float* __restrict__ SH, const float* __restrict__ SG, int H, int T,
+    int n_chunks, long total, int* __restrict__ work_counter, int max_iters, float tol, float* __restrict__ dq,
+    float* __restrict__ beta, int32_t* __restrict__ z_iters, float* __restrict__ lam_part) {
+    constexpr int NW = C / 16;
+    constexpr int NTHR = 64 * NW;
+    __shared__ SplitLds<D, C> L;
+
+    const int tid0 = threadIdx.x;
+    const int lane = tid0 & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    ChunkPos p = chunk_pos<D, C>(blockIdx.x, n_chunks, H, T);
+    {
+        PackedStateRegs<D, NTHR> s0;
+        s0.load(SH + p.hoff, tid0);
+        ChunkRowsRegs<D, C, NTHR, bf16_t> k0;
+        k0.load(k + p.tok0 * D, p.valid, tid0);
+        stage_state_planes<D, NTHR>(L.S, s0, tid0);
+        stage_key_rows<D, C, NTHR>(L.KR, k0, tid0);
+        stage_transposed<D, C, NTHR>(L.KT, k0, tid0);
+    }
+    for (int e = tid0; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)p.h * D + e];
+    if (w == 0) {
+        const float l = chunk_log_decay(gamma + p.tok0, p.valid, lane);
+        if (lane < C) L.L[lane] = l;
+    }
+    __syncthreads();
+
+    for (bool more = true; more;) {
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        auto body = [&](auto wt) {
+            constexpr int WW = decltype(wt)::value;
+            return adjoint_split_wave<D, C, WW>(L, tid, p, n_chunks, H, T, total, work_counter, k, v, gamma, lambda,
+                                                x, o, gout, SH, SG, max_iters, tol, dq, beta, z_iters, lam_part);
+        };
+        if (w == 0) more = body(std::integral_constant<int, 0>{});
+        else if constexpr (NW > 1) {
+            if (w == 1) more = body(std::integral_constant<int, 1>{});
+            else if constexpr (NW > 2) {
+                if (w == 2) more = body(std::integral_constant<int, 2>{});
+                else more = body(std::integral_constant<int, 3>{});
+            }
+        }
+    }
+}
+
+template <int D, int C, typename In>
+static hipError_t launch_fp32_keys(const BwdAdjointArgs& a, hipStream_t s);
+
 template <int D, int C, typename In>
 static hipError_t launch_t(const BwdAdjointArgs& a, hipStream_t s) {
+    if constexpr (split_keys<D, In>()) {
+        static std::atomic<long> resident_split[kMaxDevices];
+        const long total = a.BH * a.n_chunks;
+        const int block = 64 * (C / 16);
+        const long grid =
+            std::min(total, resident_workgroups(bwd_adjoint_split_kernel<D, C>, block, resident_split));
+        hipLaunchKernelGGL((bwd_adjoint_split_kernel<D, C>), dim3((unsigned)grid), dim3(block), 0, s,
+                           (const bf16_t*)a.k, (const bf16_t*)a.v, a.gamma, a.lambda, a.x, a.o, a.gout, a.SH, a.SG,
+                           a.H, a.T, a.n_chunks, total, a.work_counter, a.max_iters, a.tol, a.dq, a.beta,
+                           a.z_iters, a.lam_part);
+        return hipGetLastError();
+    } else {
+        return launch_fp32_keys<D, C, In>(a, s);
+    }
+}
+
+template <int D, int C, typename In>
+static hipError_t launch_fp32_keys(const BwdAdjointArgs& a, hipStream_t s) {
     static std::atomic<long> resident[kMaxDevices];
     const long total = a.BH * a.n_chunks;
     const int block = 64 * (C / 16);
