@@ -165,25 +165,32 @@ __device__ __forceinline__ void split_matvec(const SplitLds<D, C>& L, const Spli
             for (int ib = 0; ib < SWv::NBO; ++ib) Sp[ib][t] = mfma_bf16x32(A[ib], Z[t], Sp[ib][t]);
     };
     // JI row blocks at a time, their nine products interleaved, so that
-    // consecutive MFMAs never wait on each other's accumulator.
-    constexpr int JI = NT >= 4 ? 4 : NT;
+    // consecutive MFMAs never wait on each other's accumulator; the next
+    // group's state rows are read while the current group's products run.
+    constexpr int JI = NT >= 2 ? 2 : NT;
+    constexpr int NG = NT / JI;
+    auto load_group = [&](int q, int g, bf16x8 (&A)[JI][3]) {
+#pragma unroll
+        for (int h = 0; h < JI; ++h) {
+            const int off = (16 * (g * JI + h) + sw.n) * SW + 16 * q + 4 * sw.kk;
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) A[h][pl] = lds_bf16x8(&L.S[pl][off]);
+        }
+    };
     auto state_step = [&](int q, const bf16x8 (&Z)[3]) {
+        bf16x8 A[2][JI][3];
+        load_group(q, 0, A[0]);
 #pragma unroll
-        for (int j = 0; j < NT; j += JI) {
-            bf16x8 A[JI][3];
-#pragma unroll
-            for (int h = 0; h < JI; ++h) {
-                const int off = (16 * (j + h) + sw.n) * SW + 16 * q + 4 * sw.kk;
-#pragma unroll
-                for (int pl = 0; pl < 3; ++pl) A[h][pl] = lds_bf16x8(&L.S[pl][off]);
-            }
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) load_group(q, g + 1, A[(g + 1) & 1]);
             // smallest terms first: (plane, part) = (2,2) (2,1) (1,2) (2,0) (1,1) (0,2) (1,0) (0,1) (0,0)
             constexpr int PL[9] = {2, 2, 1, 2, 1, 0, 1, 0, 0};
             constexpr int PT[9] = {2, 1, 2, 0, 1, 2, 0, 1, 0};
 #pragma unroll
             for (int t = 0; t < 9; ++t)
 #pragma unroll
-                for (int h = 0; h < JI; ++h) YS[j + h] = mfma_bf16x32(A[h][PL[t]], Z[PT[t]], YS[j + h]);
+                for (int h = 0; h < JI; ++h)
+                    YS[g * JI + h] = mfma_bf16x32(A[g & 1][h][PL[t]], Z[PT[t]], YS[g * JI + h]);
         }
     };
     auto apply = [&]() {
