@@ -457,12 +457,12 @@ struct CgWave {
 // of a token end with the same bits).
 template <int NT>
 __device__ __forceinline__ float token_dot(const f32x4 (&A)[NT], const f32x4 (&B)[NT]) {
-    float s = 0.f;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s += A[j][r] * B[j][r];
-    return kslot_sum(s);
+        for (int r = 0; r < 4; ++r) s[r] += A[j][r] * B[j][r];
+    return kslot_sum((s[0] + s[1]) + (s[2] + s[3]));
 }
 
 // num / den through the hardware reciprocal (about 1 ulp).  The reciprocal
