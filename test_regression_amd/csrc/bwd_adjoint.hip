@@ -317,6 +317,7 @@ __device__ __forceinline__ bool adjoint_split_wave(SplitLds<D, C>& L, int tid, C
     adjoint_rhs<D, C, W, bf16_t>(L, sw, lane, p, v, SG, gout, o, Bv, go);
 #pragma unroll
     for (int j = 0; j < NT; ++j) lam[j] = lds4(&L.Lam[16 * j + 4 * kk]);
+    // (the pipelined loop of the forward kernel was slower here)
     const int it = cg_solve<NT>(Bv, Z, max_iters, tol, [&](const f32x4 (&P)[NT], f32x4 (&Y)[NT]) {
         f32x4 YS[NT], YI[NT];
         split_matvec<D, C, W>(L, sw, P, YS, YI);

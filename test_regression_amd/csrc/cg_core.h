@@ -572,6 +572,64 @@ __device__ __forceinline__ int cg_solve(f32x4 (&R)[NT], f32x4 (&X)[NT], int max_
     return it;
 }
 
+// cg_solve with the matvec in two parts: head(P) reads only P's first two
+// 16-feature blocks, rest(P, Y) completes Y = (H_t + Lambda) P.  Each
+// iteration updates those two blocks of P first and issues the next head
+// before the other blocks' x and p updates, so the next matvec's first
+// MFMAs overlap them.  The arithmetic is cg_solve's, element for element;
+// after the last iteration the head's work is discarded.
+template <int NT, typename Head, typename Rest>
+__device__ __forceinline__ int cg_solve_pipelined(f32x4 (&R)[NT], f32x4 (&X)[NT], int max_iters, float tol,
+                                                  const Head& head, const Rest& rest) {
+    f32x4 P[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        P[j] = R[j];
+        X[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float rr = token_dot<NT>(R, R);
+    const float tq = tol * sqrtf(rr);
+    const float stop_rr = tq * tq;
+    bool done = !(rr > 0.f);   // b == 0 (or a padded token): x = 0, 0 iterations
+    int it = 0;
+    if (max_iters > 0) head(P);
+    for (int itn = 0; itn < max_iters; ++itn) {
+        if (!done && (rr < stop_rr || rr == 0.f)) done = true;
+        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        f32x4 Y[NT];
+        rest(P, Y);
+        const float pap = token_dot<NT>(P, Y);
+        const bool act = !done && (pap > 0.f);
+        if (!done && !act) done = true;   // breakdown guard
+        const float alpha = act ? rcp_div(rr, pap) : 0.f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R[j][r] -= alpha * Y[j][r];
+        const float rrn = token_dot<NT>(R, R);
+        const float beta = act ? rcp_div(rrn, rr) : 0.f;
+        constexpr int J0 = NT >= 2 ? 2 : NT;
+#pragma unroll
+        for (int j = 0; j < J0; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                X[j][r] += alpha * P[j][r];
+                P[j][r] = R[j][r] + beta * P[j][r];
+            }
+        head(P);
+#pragma unroll
+        for (int j = J0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                X[j][r] += alpha * P[j][r];
+                P[j][r] = R[j][r] + beta * P[j][r];
+            }
+        rr = act ? rrn : rr;
+        it += act ? 1 : 0;
+    }
+    return it;
+}
+
 // The chunk-local CG of wave W: Y = (H_t + Lambda) P from the LDS tiles.
 template <int D, int C, int W, bool BFK = false>
 __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<D, C, W>& cw, f32x4 (&R)[D / 16],

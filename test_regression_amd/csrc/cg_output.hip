@@ -314,14 +314,17 @@ __device__ __forceinline__ bool cg_split_wave(SplitLds<D, C>& L, int tid, ChunkP
         R[j] = qr[j].get();
         lam[j] = lds4(&L.Lam[16 * j + 4 * kk]);   // held across the CG, off the update's path
     }
-    const int it = cg_solve<NT>(R, X, max_iters, tol, [&](const f32x4 (&P)[NT], f32x4 (&Y)[NT]) {
-        f32x4 YS[NT], YI[NT];
-        split_matvec<D, C, W>(L, sw, P, YS, YI);
+    SplitMatvec<D, C, W> mv(L, sw);
+    const int it = cg_solve_pipelined<NT>(
+        R, X, max_iters, tol, [&](const f32x4 (&P)[NT]) { mv.head(P); },
+        [&](const f32x4 (&P)[NT], f32x4 (&Y)[NT]) {
+            f32x4 YS[NT], YI[NT];
+            mv.rest(P, YS, YI);
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+            for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Y[j][r] = sw.eLo * YS[j][r] + YI[j][r] + lam[j][r] * P[j][r];
-    });
+                for (int r = 0; r < 4; ++r) Y[j][r] = sw.eLo * YS[j][r] + YI[j][r] + lam[j][r] * P[j][r];
+        });
     asm volatile("" : "+v"(tid));
     if (W == 0 && lane == 0) L.next = ticket;
 

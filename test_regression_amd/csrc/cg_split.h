@@ -134,6 +134,125 @@ __device__ __forceinline__ void split_apply(const SplitLds<D, C>& L, const f32x4
 }
 
 // One CG matvec of wave W: YS = S P^T (nine split products per step), and
+// YI = K^T (M o (K P^T)) over the causal keys from the chunk start.  head()
+// starts it from P's first two 16-feature blocks alone (their split and the
+// first scores step), so the CG loop can issue it before it has finished
+// updating the rest of P; rest() completes it.  Order inside: per
+// 32-feature step q the split of P, the scores and the state products; the
+// last two steps' scores come before the second-to-last state step, so that
+// the decayed scores are split under its MFMAs; then the apply, then the
+// last state step.
+template <int D, int C, int W>
+struct SplitMatvec {
+    using SWv = SplitWave<D, C, W>;
+    static constexpr int NT = D / 16;
+    static constexpr int NQ = D / 32;
+    static constexpr int SW = SplitLds<D, C>::SW;
+    // JI row blocks at a time, their nine products interleaved, so that
+    // consecutive MFMAs never wait on each other's accumulator; the next
+    // group's state rows are read while the current group's products run.
+    static constexpr int JI = NT >= 2 ? 2 : NT;
+    static constexpr int NG = NT / JI;
+    const SplitLds<D, C>& L;
+    const SWv& sw;
+    f32x4 Sp[SWv::NBO][3];   // scores: one accumulator per key block and split part
+    bf16x8 Z0[3];            // split of P's first 32 features
+
+    __device__ __forceinline__ SplitMatvec(const SplitLds<D, C>& l, const SWv& w) : L(l), sw(w) {}
+
+    __device__ __forceinline__ static void split_step(const f32x4 (&P)[NT], int q, bf16x8 (&Z)[3]) {
+        split_operands(P[2 * q], P[2 * q + 1], Z[0], Z[1], Z[2]);
+    }
+    __device__ __forceinline__ void scores_step(int q, const bf16x8 (&Z)[3]) {
+        bf16x8 A[SWv::NBO];
+#pragma unroll
+        for (int ib = 0; ib < SWv::NBO; ++ib) A[ib] = lds_bf16x8(&L.KR[(16 * ib + sw.n) * SW + 16 * q + 4 * sw.kk]);
+#pragma unroll
+        for (int t = 2; t >= 0; --t)
+#pragma unroll
+            for (int ib = 0; ib < SWv::NBO; ++ib) Sp[ib][t] = mfma_bf16x32(A[ib], Z[t], Sp[ib][t]);
+    }
+    __device__ __forceinline__ void load_group(int q, int g, bf16x8 (&A)[JI][3]) const {
+#pragma unroll
+        for (int h = 0; h < JI; ++h) {
+            const int off = (16 * (g * JI + h) + sw.n) * SW + 16 * q + 4 * sw.kk;
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) A[h][pl] = lds_bf16x8(&L.S[pl][off]);
+        }
+    }
+    __device__ __forceinline__ void state_step(int q, const bf16x8 (&Z)[3], f32x4 (&YS)[NT]) const {
+        bf16x8 A[2][JI][3];
+        load_group(q, 0, A[0]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) load_group(q, g + 1, A[(g + 1) & 1]);
+            // smallest terms first: (plane, part) = (2,2) (2,1) (1,2) (2,0) (1,1) (0,2) (1,0) (0,1) (0,0)
+            constexpr int PL[9] = {2, 2, 1, 2, 1, 0, 1, 0, 0};
+            constexpr int PT[9] = {2, 1, 2, 0, 1, 2, 0, 1, 0};
+#pragma unroll
+            for (int t = 0; t < 9; ++t)
+#pragma unroll
+                for (int h = 0; h < JI; ++h)
+                    YS[g * JI + h] = mfma_bf16x32(A[g & 1][h][PL[t]], Z[PT[t]], YS[g * JI + h]);
+        }
+    }
+    __device__ __forceinline__ void apply(f32x4 (&YI)[NT]) const {
+        f32x4 Wt[2 * SWv::NS];
+#pragma unroll
+        for (int ib = 0; ib < 2 * SWv::NS; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Wt[ib][r] = ib < SWv::NBO
+                                ? ((Sp[ib < SWv::NBO ? ib : 0][2][r] + Sp[ib < SWv::NBO ? ib : 0][1][r]) +
+                                   Sp[ib < SWv::NBO ? ib : 0][0][r]) * sw.dec[ib][r]
+                                : 0.f;
+        split_apply<D, C, SWv::NS>(L, Wt, sw.n, sw.kk, YI);
+    }
+
+    __device__ __forceinline__ void head(const f32x4 (&P)[NT]) {
+        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ib = 0; ib < SWv::NBO; ++ib) Sp[ib][0] = Sp[ib][1] = Sp[ib][2] = zero;
+        split_step(P, 0, Z0);
+        scores_step(0, Z0);
+    }
+
+    __device__ __forceinline__ void rest(const f32x4 (&P)[NT], f32x4 (&YS)[NT], f32x4 (&YI)[NT]) {
+        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) YS[j] = YI[j] = zero;
+        if constexpr (NQ == 1) {
+            apply(YI);
+            state_step(0, Z0, YS);
+        } else {
+            bf16x8 Za[3], Zb[3];
+            if constexpr (NQ == 2) {
+                split_step(P, 1, Zb);
+                scores_step(1, Zb);
+                state_step(0, Z0, YS);
+            } else {
+                state_step(0, Z0, YS);
+#pragma unroll
+                for (int q = 1; q + 2 < NQ; ++q) {
+                    split_step(P, q, Za);
+                    scores_step(q, Za);
+                    state_step(q, Za, YS);
+                }
+                split_step(P, NQ - 2, Za);
+                split_step(P, NQ - 1, Zb);
+                scores_step(NQ - 2, Za);
+                scores_step(NQ - 1, Zb);
+                state_step(NQ - 2, Za, YS);
+            }
+            apply(YI);
+            state_step(NQ - 1, Zb, YS);
+        }
+    }
+};
+
+// One whole matvec as a single function (the adjoint kernel; its loop was
+// slower with SplitMatvec's head/rest form): YS = S P^T (nine split
+// products per step), and
 // YI = K^T (M o (K P^T)) over the causal keys from the chunk start.  Order:
 // per 32-feature step q the split of P, the scores and the state products;
 // the last two steps' scores come before the second-to-last state step, so
