@@ -63,7 +63,10 @@ typedef enum {
 
 typedef enum {
     MESA_DTYPE_F32 = 0,              /* q, k, v stored as float32                        */
-    MESA_DTYPE_BF16 = 1              /* q, k, v stored as bfloat16; all math in fp32     */
+    MESA_DTYPE_BF16 = 1              /* q, k, v stored as bfloat16; all math in fp32:
+                                        products of float values run as bf16 MFMAs on
+                                        exact three-part bf16 splits, so every product
+                                        term is the exact float product, summed in fp32 */
 } mesa_dtype;
 
 /* Kernel ids for the optional profiling records. */
