@@ -257,15 +257,23 @@ def test_chunk_size_invariance():
     assert rel_l2(outs[16], outs[64]) <= 1e-5 and rel_l2(outs[32], outs[64]) <= 1e-5
 
 
-def test_single_iteration_is_one_matvec():
-    """max_iters = 1: x_1 = (q.q / q.Aq) q, so every output checks one chunked matvec."""
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [1, 2])
+def test_one_and_two_iterations(dtype, k):
+    """max_iters = 1: x_1 = (q.q / q.Aq) q, so every output checks one chunked
+    matvec; 2 checks the direction update too.  With bf16 keys this is the
+    split-product kernel, whose loop issues the next matvec's first step
+    before it finishes the update (discarded after the last iteration)."""
     B, H, T, d = 2, 2, 130, 128
-    say("case one matvec", (B, H, T, d))
-    x = small_inputs(11, B, H, T, d, "f32")
-    g = gpu_forward(x, "f32", 1, 0.0, 64)
-    r = oracle_forward(x, "f32", 1, 0.0)
-    assert rel_l2(g["out"], r["out"]) <= 1e-5
-    assert (g["iters"] == 1).all()
+    say("case one/two matvecs", (B, H, T, d, dtype, k))
+    x = small_inputs(11, B, H, T, d, dtype)
+    for chunk in (16, 32, 64):
+        g = gpu_forward(x, dtype, k, 0.0, chunk)
+        r = oracle_forward(x, dtype, k, 0.0)
+        e = rel_l2(g["out"], r["out"])
+        say(f"chunk {chunk} rel_l2={e:.2e}")
+        assert e <= 1e-5, chunk
+        assert (g["iters"] == k).all()
 
 
 @pytest.mark.parametrize("d", [16, 128])
