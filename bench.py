@@ -616,6 +616,8 @@ def main():
         "value": round(h["value"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(h["ms_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "arithmetic": "fp32: exact float product terms (three-part bf16 splits on bf16 MFMAs for the bf16 "
+                      "keys), fp32 accumulation",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d, "d_v": w.d,
                    "chunk": w.chunk, "qkv_storage": w.dtype, "cg_iters": w.max_iters, "tol": w.tol,
                    "seed": w.seed},
