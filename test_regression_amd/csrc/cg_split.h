@@ -155,7 +155,10 @@ struct SplitMatvec {
     static constexpr int NG = NT / JI;
     const SplitLds<D, C>& L;
     const SWv& sw;
-    f32x4 Sp[SWv::NBO][3];   // scores: one accumulator per key block and split part
+    // Scores: one accumulator per key block, and per split part too when a
+    // single key block would otherwise make one dependent chain.
+    static constexpr int NP = SWv::NBO == 1 ? 3 : 1;
+    f32x4 Sp[SWv::NBO][NP];
     bf16x8 Z0[3];            // split of P's first 32 features
 
     __device__ __forceinline__ SplitMatvec(const SplitLds<D, C>& l, const SWv& w) : L(l), sw(w) {}
@@ -170,7 +173,8 @@ struct SplitMatvec {
 #pragma unroll
         for (int t = 2; t >= 0; --t)
 #pragma unroll
-            for (int ib = 0; ib < SWv::NBO; ++ib) Sp[ib][t] = mfma_bf16x32(A[ib], Z[t], Sp[ib][t]);
+            for (int ib = 0; ib < SWv::NBO; ++ib)
+                Sp[ib][NP == 3 ? t : 0] = mfma_bf16x32(A[ib], Z[t], Sp[ib][NP == 3 ? t : 0]);
     }
     __device__ __forceinline__ void load_group(int q, int g, bf16x8 (&A)[JI][3]) const {
 #pragma unroll
@@ -199,20 +203,24 @@ struct SplitMatvec {
     __device__ __forceinline__ void apply(f32x4 (&YI)[NT]) const {
         f32x4 Wt[2 * SWv::NS];
 #pragma unroll
-        for (int ib = 0; ib < 2 * SWv::NS; ++ib)
+        for (int ib = 0; ib < 2 * SWv::NS; ++ib) {
+            const int b = ib < SWv::NBO ? ib : 0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Wt[ib][r] = ib < SWv::NBO
-                                ? ((Sp[ib < SWv::NBO ? ib : 0][2][r] + Sp[ib < SWv::NBO ? ib : 0][1][r]) +
-                                   Sp[ib < SWv::NBO ? ib : 0][0][r]) * sw.dec[ib][r]
-                                : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                float sc = Sp[b][0][r];
+                if constexpr (NP == 3) sc = (Sp[b][2][r] + Sp[b][1][r]) + Sp[b][0][r];
+                Wt[ib][r] = ib < SWv::NBO ? sc * sw.dec[ib][r] : 0.f;
+            }
+        }
         split_apply<D, C, SWv::NS>(L, Wt, sw.n, sw.kk, YI);
     }
 
     __device__ __forceinline__ void head(const f32x4 (&P)[NT]) {
         const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ib = 0; ib < SWv::NBO; ++ib) Sp[ib][0] = Sp[ib][1] = Sp[ib][2] = zero;
+        for (int ib = 0; ib < SWv::NBO; ++ib)
+#pragma unroll
+            for (int t = 0; t < NP; ++t) Sp[ib][t] = zero;
         split_step(P, 0, Z0);
         scores_step(0, Z0);
     }
