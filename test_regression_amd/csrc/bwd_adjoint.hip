@@ -147,7 +147,7 @@ __device__ __forceinline__ bool adjoint_wave(CgLds<D, C>& L, int tid, ChunkPos& 
     f32x4 Bv[NT], Z[NT];
     float go = 0.f;
     adjoint_rhs<D, C, W, In>(L, cw, lane, p, v, SG, gout, o, Bv, go);
-    const int it = cg_solve_wave<D, C, W, split_keys<D, In>()>(L, cw, Bv, Z, max_iters, tol);
+    const int it = cg_solve_wave<D, C, W>(L, cw, Bv, Z, max_iters, tol);
 
     // ---- H_t x_t, beta, dq ----
     f32x4 Xv[NT], Hx[NT];
@@ -156,7 +156,7 @@ __device__ __forceinline__ bool adjoint_wave(CgLds<D, C>& L, int tid, ChunkPos& 
         const size_t off = (p.tok0 + tr) * D + 16 * j + 4 * kk;
         Xv[j] = tok_ok ? *reinterpret_cast<const f32x4*>(x + off) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    wave_matvec<D, C, W, false, split_keys<D, In>()>(L, cw, Xv, Hx);
+    wave_matvec<D, C, W, false>(L, cw, Xv, Hx);
     // Addresses of what follows are built from here on, not held across the CG.
     asm volatile("" : "+v"(tid));
     const float b = go - token_dot<NT>(Z, Hx);

@@ -162,49 +162,16 @@ __device__ __forceinline__ void contract_intra(const f32x4 (&W)[NB], const float
     }
 }
 
-// Y[j] += S[16j + m][:] . Z^T[:][n] only (contract_state_scores without scores).
-template <int D>
-__device__ __forceinline__ void contract_state(const f32x4 (&Z)[D / 16], const float* Sst,
-                                               lds_cfloat* const (&col)[D / 16 * (D / 16 + 1) / 2], int m,
-                                               int kk, f32x4 (&Y)[D / 16]) {
-    constexpr int NT = D / 16;
-    f32x4 bs[2][NT];
-    auto load = [&](int g, int buf) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            if (g > j) {
-                bs[buf][j] = lds4(Sst + blk<NT>(j, g) + m * kBlockPitch + 4 * kk);
-            } else {
-                lds_cfloat* c = col[blk_index<NT>(g, j)];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) bs[buf][j][s] = c[s * kBlockPitch];
-            }
-        }
-    };
-    load(0, 0);
-#pragma unroll
-    for (int g = 0; g < NT; ++g) {
-        const int cur = g & 1;
-        if (g + 1 < NT) load(g + 1, cur ^ 1);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) Y[j] = mfma4(bs[cur][j][s], Z[g][s], Y[j]);
-    }
-}
-
-// ---- split-bf16 products (bf16 keys: the key tiles hold exact bf16 values) ----
+// ---- split-bf16 operands (used by the bf16-key kernels of cg_split.h) ----
 // A float x is split by truncation into hi = x with its low 16 bits cleared,
 // mid = the same of x - hi, lo = x - hi - mid.  Both subtractions are exact
 // and lo has at most 8 significant bits, so hi + mid + lo = x exactly and
-// each part is a bf16; a product of an exact-bf16 key with each part is
-// exact in float.  So three v_mfma_f32_16x16x32_bf16 give the float
-// product's terms (up to the order of their sum) at 5.3x the fp32 MFMA rate.
-// A 32-slot MFMA operand here is two 4-element pieces: lane group kk takes
-// slots 4kk..4kk+3 of a first and of a second 16-slot block.
+// each part is a bf16; a product of a bf16 value with each part is exact in
+// float.  A 32-slot MFMA operand here is two 4-element pieces: lane group kk
+// takes slots 4kk..4kk+3 of a first and of a second 16-slot block.
 
-// Whether a kernel over keys of type In at head dimension D takes the
-// split-bf16 intra-chunk products (bf16 keys, whole 32-feature steps).
+// Whether keys of type In at head dimension D go to the split-bf16 kernels
+// (bf16 keys, whole 32-feature steps) rather than the fp32 ones.
 template <int D, typename In>
 __host__ __device__ constexpr bool split_keys() { return sizeof(In) == 2 && D % 32 == 0; }
 
@@ -212,12 +179,6 @@ __host__ __device__ constexpr bool split_keys() { return sizeof(In) == 2 && D % 
 // byte selectors 0-3 pick bytes of its second source and 4-7 of its first.
 __device__ __forceinline__ uint32_t pack_hi(float a, float b) {
     return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-
-// The exact-bf16 values of two 4-element pieces as one operand.
-__device__ __forceinline__ bf16x8 bf16_operand(const f32x4& a, const f32x4& b) {
-    const uint32_t w[4] = {pack_hi(a[0], a[1]), pack_hi(a[2], a[3]), pack_hi(b[0], b[1]), pack_hi(b[2], b[3])};
-    return as_bf16x8(w);
 }
 
 // The three split parts of two 4-element float pieces as operands.
@@ -241,129 +202,6 @@ __device__ __forceinline__ void split_operands(const f32x4& a, const f32x4& b, b
     H = as_bf16x8(wh);
     M = as_bf16x8(wm);
     L = as_bf16x8(wl);
-}
-
-// Sc[ib] = K[16(KB0 + ib) + m][:] . Z^T[:][n] for ib < NB, K rows exact bf16
-// (pitch lds_pitch(D)); the slots of MFMA q are features 32q + 4kk + s and
-// 32q + 16 + 4kk + s, i.e. blocks 2q and 2q + 1 of Z.
-template <int D, int NB, int KB0>
-__device__ __forceinline__ void scores_split(const f32x4 (&Z)[D / 16], const float* Kr, int m, int kk,
-                                             f32x4 (&Sc)[NB]) {
-    constexpr int PD = lds_pitch(D);
-    static_assert(D % 32 == 0, "split path needs 32-feature steps");
-#pragma unroll
-    for (int q = 0; q < D / 32; ++q) {
-        bf16x8 Zh, Zm, Zl;
-        split_operands(Z[2 * q], Z[2 * q + 1], Zh, Zm, Zl);
-#pragma unroll
-        for (int ib = 0; ib < NB; ++ib) {
-            const float* row = Kr + (16 * (KB0 + ib) + m) * PD + 32 * q + 4 * kk;
-            const bf16x8 A = bf16_operand(lds4(row), lds4(row + 16));
-            Sc[ib] = mfma_bf16x32(A, Zh, Sc[ib]);
-            Sc[ib] = mfma_bf16x32(A, Zm, Sc[ib]);
-            Sc[ib] = mfma_bf16x32(A, Zl, Sc[ib]);
-        }
-    }
-}
-
-// Y[j] += sum_i KT[16j + m][16 KB0 + i] W[i][n] over the NB <= 2 key blocks,
-// KT exact bf16 (pitch lds_pitch_rows(C)); one MFMA step with block KB0 in
-// the first 16 slots and block KB0 + 1 (or zeros) in the second.
-template <int D, int C, int NB, int KB0>
-__device__ __forceinline__ void apply_split(const f32x4 (&W)[NB], const float* BT, int m, int kk,
-                                            f32x4 (&Y)[D / 16]) {
-    constexpr int NT = D / 16;
-    constexpr int PT = lds_pitch_rows(C);
-    static_assert(NB >= 1 && NB <= 2, "one MFMA step covers two key blocks");
-    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 Wh, Wm, Wl;
-    split_operands(W[0], NB == 2 ? W[NB - 1] : zero, Wh, Wm, Wl);
-    const float* base = BT + m * PT + 16 * KB0 + 4 * kk;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const float* row = base + 16 * j * PT;
-        const bf16x8 A = bf16_operand(lds4(row), NB == 2 ? lds4(row + 16) : zero);
-        Y[j] = mfma_bf16x32(A, Wh, Y[j]);
-        Y[j] = mfma_bf16x32(A, Wm, Y[j]);
-        Y[j] = mfma_bf16x32(A, Wl, Y[j]);
-    }
-}
-
-// One matvec's MFMA work with split-bf16 intra-chunk products, interleaved
-// so that their VALU work runs under the fp32 state MFMAs:
-//   YS[j] += S[16j + m][:] . Z^T[:][n]                      (fp32, blocks g = 0..NT-1)
-//   Sc     = K rows . Z^T (split), 32 features at block g = q < NT/2
-//   W      = Sc * dec, split at block g = NT/2
-//   YI[j] += K^T W (split), two row blocks j per block g >= NT/2
-template <int D, int C, int NB, int KB0>
-__device__ __forceinline__ void matvec_split(const f32x4 (&Z)[D / 16], const float* Sst,
-                                             lds_cfloat* const (&col)[D / 16 * (D / 16 + 1) / 2],
-                                             const float* Kr, const float* BT, const float (&dec)[NB][4], int m,
-                                             int kk, f32x4 (&YS)[D / 16], f32x4 (&YI)[D / 16]) {
-    constexpr int NT = D / 16;
-    constexpr int PD = lds_pitch(D);
-    constexpr int PT = lds_pitch_rows(C);
-    constexpr int JPG = NT / (NT / 2);   // apply row blocks per state block (2)
-    static_assert(NT % 2 == 0 && NB >= 1 && NB <= 2, "split matvec shape");
-    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 Sc[NB];
-#pragma unroll
-    for (int ib = 0; ib < NB; ++ib) Sc[ib] = zero;
-    bf16x8 Wh, Wm, Wl;
-    f32x4 bs[2][NT];
-    auto load = [&](int g, int buf) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            if (g > j) {
-                bs[buf][j] = lds4(Sst + blk<NT>(j, g) + m * kBlockPitch + 4 * kk);
-            } else {
-                lds_cfloat* c = col[blk_index<NT>(g, j)];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) bs[buf][j][s] = c[s * kBlockPitch];
-            }
-        }
-    };
-    load(0, 0);
-#pragma unroll
-    for (int g = 0; g < NT; ++g) {
-        const int cur = g & 1;
-        if (g + 1 < NT) load(g + 1, cur ^ 1);
-        if (g < NT / 2) {
-            const int q = g;
-            bf16x8 Zh, Zm, Zl;
-            split_operands(Z[2 * q], Z[2 * q + 1], Zh, Zm, Zl);
-#pragma unroll
-            for (int ib = 0; ib < NB; ++ib) {
-                const float* row = Kr + (16 * (KB0 + ib) + m) * PD + 32 * q + 4 * kk;
-                const bf16x8 A = bf16_operand(lds4(row), lds4(row + 16));
-                Sc[ib] = mfma_bf16x32(A, Zh, Sc[ib]);
-                Sc[ib] = mfma_bf16x32(A, Zm, Sc[ib]);
-                Sc[ib] = mfma_bf16x32(A, Zl, Sc[ib]);
-            }
-        } else {
-            if (g == NT / 2) {
-                f32x4 W[2] = {zero, zero};
-#pragma unroll
-                for (int ib = 0; ib < NB; ++ib)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) W[ib][r] = Sc[ib][r] * dec[ib][r];
-                split_operands(W[0], W[1], Wh, Wm, Wl);
-            }
-#pragma unroll
-            for (int jj = 0; jj < JPG; ++jj) {
-                const int j = (g - NT / 2) * JPG + jj;
-                const float* row = BT + (16 * j + m) * PT + 16 * KB0 + 4 * kk;
-                const bf16x8 A = bf16_operand(lds4(row), NB == 2 ? lds4(row + 16) : zero);
-                YI[j] = mfma_bf16x32(A, Wh, YI[j]);
-                YI[j] = mfma_bf16x32(A, Wm, YI[j]);
-                YI[j] = mfma_bf16x32(A, Wl, YI[j]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) YS[j] = mfma4(bs[cur][j][s], Z[g][s], YS[j]);
-    }
 }
 
 // S_mid (upper block triangle) = e^{l_{h-1}} S0 + sum_{i<h} e^{l_{h-1}-l_i} k_i k_i^T,
@@ -477,10 +315,7 @@ __device__ __forceinline__ float rcp_div(float num, float den) {
 
 // Y = H_t P over the wave's tokens (the stored state plus the sub-chunk's
 // causal keys), plus diag(lambda) P when LAMBDA: one CG matvec.
-// BFK: the key tiles hold exact bf16 values, and the intra-chunk products
-// (scores and their apply) run as split-bf16 products; the state term stays
-// on fp32 MFMAs.
-template <int D, int C, int W, bool LAMBDA, bool BFK = false>
+template <int D, int C, int W, bool LAMBDA>
 __device__ __forceinline__ void wave_matvec(const CgLds<D, C>& L, const CgWave<D, C, W>& cw,
                                             const f32x4 (&P)[D / 16], f32x4 (&Y)[D / 16]) {
     using CW = CgWave<D, C, W>;
@@ -490,22 +325,13 @@ __device__ __forceinline__ void wave_matvec(const CgLds<D, C>& L, const CgWave<D
     for (int j = 0; j < NT; ++j) YS[j] = YI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ib = 0; ib < CW::NB; ++ib) Sc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BFK) {
-        float dec[CW::NB][4];
+    contract_state_scores<D, CW::NB, CW::KB0>(P, cw.Sst, cw.col, L.KV, cw.n, cw.kk, YS, Sc);
+    f32x4 Wt[CW::NB];
 #pragma unroll
-        for (int ib = 0; ib < CW::NB; ++ib)
+    for (int ib = 0; ib < CW::NB; ++ib)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dec[ib][r] = cw.dec[CW::KB0 + ib][r];
-        matvec_split<D, C, CW::NB, CW::KB0>(P, cw.Sst, cw.col, L.KV, L.KT, dec, cw.n, cw.kk, YS, YI);
-    } else {
-        contract_state_scores<D, CW::NB, CW::KB0>(P, cw.Sst, cw.col, L.KV, cw.n, cw.kk, YS, Sc);
-        f32x4 Wt[CW::NB];
-#pragma unroll
-        for (int ib = 0; ib < CW::NB; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Wt[ib][r] = Sc[ib][r] * cw.dec[CW::KB0 + ib][r];
-        contract_intra<D, C, CW::NB, CW::KB0>(Wt, L.KT, cw.n, cw.kk, YI);
-    }
+        for (int r = 0; r < 4; ++r) Wt[ib][r] = Sc[ib][r] * cw.dec[CW::KB0 + ib][r];
+    contract_intra<D, C, CW::NB, CW::KB0>(Wt, L.KT, cw.n, cw.kk, YI);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         if constexpr (LAMBDA) {
@@ -631,11 +457,11 @@ __device__ __forceinline__ int cg_solve_pipelined(f32x4 (&R)[NT], f32x4 (&X)[NT]
 }
 
 // The chunk-local CG of wave W: Y = (H_t + Lambda) P from the LDS tiles.
-template <int D, int C, int W, bool BFK = false>
+template <int D, int C, int W>
 __device__ __forceinline__ int cg_solve_wave(const CgLds<D, C>& L, const CgWave<D, C, W>& cw, f32x4 (&R)[D / 16],
                                              f32x4 (&X)[D / 16], int max_iters, float tol) {
     return cg_solve<D / 16>(R, X, max_iters, tol, [&](const f32x4 (&P)[D / 16], f32x4 (&Y)[D / 16]) {
-        wave_matvec<D, C, W, true, BFK>(L, cw, P, Y);
+        wave_matvec<D, C, W, true>(L, cw, P, Y);
     });
 }
 

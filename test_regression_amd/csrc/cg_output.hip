@@ -100,7 +100,7 @@ __device__ __forceinline__ bool cg_wave(CgLds<D, C>& L, int tid, ChunkPos& p, in
     f32x4 X[NT], R[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) R[j] = qr[j].get();
-    const int it = cg_solve_wave<D, C, W, split_keys<D, In>()>(L, cw, R, X, max_iters, tol);
+    const int it = cg_solve_wave<D, C, W>(L, cw, R, X, max_iters, tol);
     // Addresses of the output phase are built from here on, not held across the CG.
     asm volatile("" : "+v"(tid));
     if (W == 0 && lane == 0) L.next = ticket;
