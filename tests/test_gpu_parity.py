@@ -292,23 +292,27 @@ def test_iterating_far_past_convergence_stays_finite(d):
     compare_counts(g["iters"], r, 4 * d + 40, 0.0)
 
 
-def test_edge_cases():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_cases(dtype):
+    """Short sequences inside one chunk, zero queries, no forgetting, zero
+    iterations; bf16 runs the split-product kernel (chunk 16 its masked
+    second key block)."""
     d = 32
-    say("case edges")
-    # short sequences (inside one chunk), zero queries, no forgetting
-    for T in (1, 5, 64, 65):
-        x = small_inputs(20 + T, 1, 2, T, d, "f32")
-        x["q"][0, 0, T // 2] = 0.0
-        x["gamma"][0, 1] = 1.0
-        g = gpu_forward(x, "f32", 10, 1e-4, 64)
-        r = oracle_forward(x, "f32", 10, 1e-4)
-        assert rel_l2(g["out"], r["out"]) <= 1e-4, T
-        assert g["iters"][0, 0, T // 2] == 0 and np.all(g["out"][0, 0, T // 2] == 0)
-        compare_counts(g["iters"], r, 10, 1e-4)
+    say("case edges", dtype)
+    for chunk in (16, 64):
+        for T in (1, 5, 16, 17, 64, 65):
+            x = small_inputs(20 + T, 1, 2, T, d, dtype)
+            x["q"][0, 0, T // 2] = 0
+            x["gamma"][0, 1] = 1.0
+            g = gpu_forward(x, dtype, 10, 1e-4, chunk)
+            r = oracle_forward(x, dtype, 10, 1e-4)
+            assert rel_l2(g["out"], r["out"]) <= 1e-4, (chunk, T)
+            assert g["iters"][0, 0, T // 2] == 0 and np.all(g["out"][0, 0, T // 2] == 0)
+            compare_counts(g["iters"], r, 10, 1e-4)
     # zero iterations: out = 0, counts 0, final states still exported
-    x = small_inputs(31, 1, 2, 70, d, "f32")
-    g = gpu_forward(x, "f32", 0, 0.0, 64, return_final=True)
-    r = oracle_forward(x, "f32", 0, 0.0, final_state=True)
+    x = small_inputs(31, 1, 2, 70, d, dtype)
+    g = gpu_forward(x, dtype, 0, 0.0, 64, return_final=True)
+    r = oracle_forward(x, dtype, 0, 0.0, final_state=True)
     assert np.all(g["out"] == 0) and np.all(g["iters"] == 0)
     assert rel_l2(g["final_H"], r["final_H"]) < 1e-5 and rel_l2(g["final_G"], r["final_G"]) < 1e-5
 
