@@ -101,23 +101,28 @@ def test_backward_dims_chunks_dtypes(d, chunk, dtype):
         check(gpu, ref, dtype, max_iters, tol, f"k={max_iters} tol={tol}")
 
 
-def test_backward_edge_cases():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_edge_cases(dtype):
+    """bf16 runs the split-product adjoint kernel, chunk 16 its masked second
+    key block."""
     import torch
     from test_regression_amd import mesa
-    d, chunk = 32, 64
-    for T in (1, 5, 64, 65):
-        say("case backward edge T", T)
-        x = small_inputs(5200 + T, 2, 1, T, d, "f32")
-        gpu = gpu_backward(x, "f32", 10, 0.0, chunk)
-        ref = oracle_backward(x, "f32", 10, 0.0)
-        check(gpu, ref, "f32", 10, 0.0, f"T={T}")
+    d = 32
+    for chunk in (16, 64):
+        for T in (1, 5, 64, 65):
+            say("case backward edge", dtype, "chunk", chunk, "T", T)
+            x = small_inputs(5200 + T, 2, 1, T, d, dtype)
+            gpu = gpu_backward(x, dtype, 10, 0.0, chunk)
+            ref = oracle_backward(x, dtype, 10, 0.0)
+            check(gpu, ref, dtype, 10, 0.0, f"chunk={chunk} T={T}")
+    chunk = 64
     say("case backward zero grad_out and max_iters=0")
-    x = small_inputs(5300, 1, 2, 70, d, "f32")
+    x = small_inputs(5300, 1, 2, 70, d, dtype)
     x["gout"][:] = 0.0
-    gpu = gpu_backward(x, "f32", 10, 0.0, chunk)
+    gpu = gpu_backward(x, dtype, 10, 0.0, chunk)
     assert all(not gpu[n].any() for n in NAMES)
-    x = small_inputs(5301, 1, 2, 70, d, "f32")
-    gpu = gpu_backward(x, "f32", 0, 0.0, chunk)
+    x = small_inputs(5301, 1, 2, 70, d, dtype)
+    gpu = gpu_backward(x, dtype, 0, 0.0, chunk)
     assert all(not gpu[n].any() for n in NAMES)
     say("case backward T=0")
     lam = torch.ones((2, d), dtype=torch.float32, device="cuda")
