@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_BF16_MFMA_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cg_output_layer_bf16_d128_T4096_traffic.json")
-MFMA_FILE = os.path.join(ROOT, "profiles", "cg_output_layer_bf16_d128_T4096_mfma.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cg_split_layer_bf16_d128_T4096_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "cg_split_layer_bf16_d128_T4096_mfma.json")
 KERNEL_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_core.h",
                   "test_regression_amd/csrc/persistent.h",
                   "test_regression_amd/csrc/mesa_device.h", "test_regression_amd/csrc/cg_split.h"]

@@ -16,7 +16,7 @@ CMD='cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -- python3 $R/bench.py --steps
 PS="python -m test_regression_amd.profile_summary traffic $F $W --copy-bytes 1073741824"
 C=test_regression_amd/csrc
 $PS --kernel "cg_split_kernel<128, 64>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
-    > profiles/cg_output_layer_bf16_d128_T4096_traffic.json
+    > profiles/cg_split_layer_bf16_d128_T4096_traffic.json
 $PS --kernel "chunk_states_kernel<128, 64, 4, mesa::bf16_t>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_traffic.json
 $PS --kernel "decode_kernel<128, false, float>" --command "$CMD" --sources $C/decode.hip $C/mesa_device.h \
@@ -41,7 +41,7 @@ PM="python -m test_regression_amd.profile_summary mfma $M $MA"
 # algorithmic flops per launch at 8x16x4096, d=128, C=64, k=30 (524288 token-heads):
 #   CG/output: k(2d^2 + 2(C+1)d + 11d) + 2d^2 + 2(C+1)d per token-head; adjoint: k(...) + 2(2d^2 + 2(C+1)d)
 $PM --kernel "cg_split_kernel<128, 64>" --first 4 --alg-flops 825170591744 \
-    --command "$MCMD; first 4 dispatches = the headline forward" > profiles/cg_output_layer_bf16_d128_T4096_mfma.json
+    --command "$MCMD; first 4 dispatches = the headline forward" > profiles/cg_split_layer_bf16_d128_T4096_mfma.json
 $PM --kernel "bwd_adjoint_split_kernel<128, 64>" --alg-flops 851074613248 --command "$MCMD" \
     --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_split.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_adjoint_layer_bf16_d128_T4096_mfma.json
