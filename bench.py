@@ -90,6 +90,34 @@ def split_adjoint_mfma_flops(d, C, k, n_chunks):
     return bf16, fp32
 
 
+def fp32_cg_mfma_flops(d, C, wave_iters):
+    """MFMA flops one launch of the fp32-key forward CG kernel issues, from
+    its structure (16x16x4 fp32 MFMAs, 2048 flops each).  Wave w of a chunk
+    owns tokens 16w..16w+15 and iterates until all of them have stopped, so
+    it runs max(n_t) iterations over its tokens (`wave_iters`: a
+    [n_chunks, C/16] integer array of those maxima).  Per iteration wave w
+    does the state term (d/16 row blocks x d/4 steps), and the scores and
+    apply over its causal key blocks within its half-chunk sub-state (the
+    second half of the chunk starts from the mid-chunk state); per chunk
+    every wave adds the output (the G_c term from memory, the scores and
+    apply over all causal key blocks from the chunk start), and the
+    mid-chunk state is formed once (upper 16x16 blocks, C/2 keys).
+    Returns the flops."""
+    import numpy as np
+    NT, NW = d // 16, C // 16
+    per_iter = np.zeros(NW, np.int64)
+    out = 0
+    for w in range(NW):
+        kb0 = NW // 2 if (NW >= 2 and w >= NW // 2) else 0
+        nb, nbo = w - kb0 + 1, w + 1
+        per_iter[w] = NT * (d // 4) + nb * (d // 4) + NT * 4 * nb
+        out += NT * NT * 4 + nbo * (d // 4) + NT * 4 * nbo
+    n_chunks = wave_iters.shape[0]
+    mid = (NT * (NT + 1) // 2) * (C // 2 // 4) if NW >= 2 else 0
+    mfmas = int((wave_iters.astype(np.int64) * per_iter[None, :]).sum()) + n_chunks * (out + mid)
+    return 2 * 16 * 16 * 4 * mfmas
+
+
 def mixed_roofline(bf16_flops, fp32_flops, ms, alg_flops, bf16_peak, fp32_peak):
     """Roofline of a kernel whose MFMA work is split between bf16 and fp32
     instructions: the shortest time is bf16/peak_bf16 + fp32/peak_fp32, the
@@ -201,16 +229,25 @@ def headline(torch, mesa, inputs, args, dev, peaks):
     res = dict(
         w=w, x=x, n_tok=n_tok, ms_step=ms_step, value=n_tok * args.steps / el,
         tflops=(fs + fcg + fo) * n_tok / (ms_step * 1e-3) / 1e12,
-        roofline=dict(bound="mfma", achieved=rl["achieved"], peak=rl["peak"], unit="TFLOP/s", frac=rl["frac"],
-                      traffic=traffic, mfma_busy_frac=measured_mfma_busy(),
-                      kernel="cg_split_kernel<128,64> (bf16 and fp32 MFMA)",
-                      peak_basis="bf16 MFMA 2500 TFLOP/s for the split products, fp32 MFMA 157.3 for the G_c term",
-                      issued_flops_per_launch=rl["issued_flops_per_launch"],
-                      issued_bf16_flops=bf, issued_fp32_flops=fp,
-                      algorithmic_flops_per_launch=k2_flops, algorithmic_tflops=rl["algorithmic_tflops"],
+        # The kernel's contractions issue on bf16 MFMAs, so its roofline is
+        # the method's algorithmic flops against the bf16 MFMA peak; the
+        # exact split products multiply the issued work, which is reported
+        # as a secondary fraction against the issued work's own bound.
+        roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
+                      frac=round(achieved / PEAK_BF16_MFMA_TFLOPS, 4), traffic=traffic,
+                      kernel="cg_split_kernel<128,64>",
+                      basis="algorithmic flops of the CG iterations and the output contraction "
+                            f"({fcg + fo} per token-head) per launch / average launch time / the bf16 "
+                            "MFMA peak the kernel's products issue at",
+                      algorithmic_flops_per_launch=k2_flops, avg_launch_ms=round(k2_ms, 4),
+                      frac_measured_peak=round(achieved / peaks["mfma_bf16_tflops"], 4),
                       algorithmic_over_fp32_peak=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
-                      peak_measured=rlm["peak"], frac_measured=rlm["frac"],
-                      avg_launch_ms=round(k2_ms, 4)),
+                      mfma_busy_frac=measured_mfma_busy(),
+                      issued=dict(achieved=rl["achieved"], peak=rl["peak"], frac=rl["frac"],
+                                  flops_per_launch=rl["issued_flops_per_launch"], bf16_flops=bf, fp32_flops=fp,
+                                  basis="issued MFMA work (exact split products) over its shortest time at "
+                                        "the bf16 and fp32 MFMA peaks",
+                                  peak_measured=rlm["peak"], frac_measured=rlm["frac"])),
         kernels={
             "cg_split_kernel": dict(avg_ms=round(k2_ms, 4), launches=k2[1],
                                     algorithmic_tflops=round(achieved, 2)),
@@ -286,14 +323,17 @@ def backward(torch, mesa, h, dev, peaks, steps=5, warmup=2):
             "forward_train_ms": round(1e3 * f_el / steps, 4), "backward_ms": round(1e3 * b_el / steps, 4),
             "train_step_tokens_per_s": round(n_tok * steps / (f_el + b_el), 1),
             "kernels": kernels,
-            "roofline": {"bound": "mfma", "achieved": rl["achieved"], "peak": rl["peak"], "unit": "TFLOP/s",
-                         "frac": rl["frac"],
-                         "peak_basis": "issued MFMA work: bf16 split products at 2500 TFLOP/s, the right "
-                                       "side's fp32 products at 157.3",
-                         "kernel": "bwd_adjoint_split_kernel<128,64>", "issued_bf16_flops": bf,
-                         "issued_fp32_flops": fp, "algorithmic_flops_per_launch": adj_flops,
-                         "algorithmic_tflops": round(achieved, 2), "peak_measured": rlm["peak"],
-                         "frac_measured": rlm["frac"], "avg_launch_ms": round(adj_ms, 4)}}
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
+                         "kernel": "bwd_adjoint_split_kernel<128,64>",
+                         "basis": "algorithmic flops per launch / average launch time / the bf16 MFMA peak",
+                         "algorithmic_flops_per_launch": adj_flops, "avg_launch_ms": round(adj_ms, 4),
+                         "algorithmic_over_fp32_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "issued": {"achieved": rl["achieved"], "peak": rl["peak"], "frac": rl["frac"],
+                                    "bf16_flops": bf, "fp32_flops": fp,
+                                    "basis": "issued MFMA work: bf16 split products at 2500 TFLOP/s, the "
+                                             "right side's fp32 products at 157.3",
+                                    "peak_measured": rlm["peak"], "frac_measured": rlm["frac"]}}}
 
 
 def dynamic(torch, mesa, inputs, dev):
@@ -309,13 +349,48 @@ def dynamic(torch, mesa, inputs, dev):
     fs, _, fo = flops_per_token_head(w.d, w.chunk, 0)
     per_it = 2 * w.d * w.d + 2 * (w.chunk + 1) * w.d + 11 * w.d
     useful = n_tok * (fs + fo) + float(it.sum()) * per_it
+    k2_useful = n_tok * fo + float(it.sum()) * per_it
     ms = 1e3 * el / 3
     k2_ms = k2[0] / max(k2[1], 1)
+    k1_ms = k1[0] / max(k1[1], 1)
+    wave_iters = iters.view(-1, w.chunk // 16, 16).amax(dim=-1).cpu().numpy()
+    issued = fp32_cg_mfma_flops(w.d, w.chunk, wave_iters)
+    hist = torch.bincount(iters.flatten().to(torch.int64), minlength=w.max_iters + 1).cpu().tolist()
+    ach = k2_useful / (k2_ms * 1e-3) / 1e12
     del t
     return {"workload": w.name, "tokens_per_s": round(n_tok / (ms * 1e-3), 1), "ms_per_call": round(ms, 3),
             "iters_mean": round(mean_it, 3), "iters_min": int(iters.min()), "iters_max": int(iters.max()),
+            "iters_histogram": {str(i): c for i, c in enumerate(hist) if c},
             "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-            "cg_output_kernel_ms": round(k2_ms, 4)}
+            "kernels": {"cg_output_kernel": {"avg_ms": round(k2_ms, 4), "launches": k2[1]},
+                        "chunk_states_kernel": {"avg_ms": round(k1_ms, 4), "launches": k1[1]}},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "kernel": "cg_output_kernel<128,64,float> (fp32 MFMA)",
+                         "basis": "useful flops (each token's own iteration count) per launch / average "
+                                  "launch time / the fp32 MFMA peak",
+                         "useful_flops_per_launch": k2_useful, "issued_flops_per_launch": issued,
+                         "issued_over_useful": round(issued / k2_useful, 4),
+                         "issued_tflops": round(issued / (k2_ms * 1e-3) / 1e12, 2),
+                         "issued_frac": round(issued / (k2_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "avg_launch_ms": round(k2_ms, 4)}}
+
+
+def small_workload(torch, mesa, inputs, dev, name, steps=20, warmup=3):
+    """A launch-latency-sized forward workload, timed like the headline."""
+    w = inputs.WORKLOADS[name]
+    x = inputs.forward_inputs(w)
+    t = {n: to_dev(torch, x[n], w.dtype if n in ("q", "k", "v") else "f32", dev) for n in x}
+    el, k1, k2, _, _ = timed_forward(torch, mesa, t, w, steps, warmup)
+    n_tok = w.B * w.H * w.T
+    fs, fcg, fo = flops_per_token_head(w.d, w.chunk, w.max_iters)
+    ms = 1e3 * el / steps
+    return {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "qkv_storage": w.dtype,
+            "cg_iters": w.max_iters, "tokens_per_s": round(n_tok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+            "algorithmic_tflops": round((fs + fcg + fo) * n_tok / (ms * 1e-3) / 1e12, 3),
+            "kernels": {"chunk_states_kernel_ms": round(k1[0] / max(k1[1], 1), 4),
+                        "cg_kernel_ms": round(k2[0] / max(k2[1], 1), 4)},
+            "note": "launch-latency-sized: reported, not graded on a roofline"}
 
 
 def decode(torch, mesa, inputs, dev, steps=1024, warmup=8, warm_start=True):
@@ -327,28 +402,18 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8, warm_start=True):
     consecutive Gaussian rows, as a short causal convolution would mix them)."""
     w = inputs.WORKLOADS["decode_f32_d128_N256_prefix4096"]
     N, H, d, P = w.B, w.H, w.d, w.T
-    g = torch.Generator(device=dev)
-    g.manual_seed(w.seed)
+    gen = inputs.DecodeDeviceStream(torch, w, dev)
     log(f"[bench] decode: building {N}x{H} prefix states of {P} tokens")
     SH0 = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
     SG0 = torch.empty_like(SH0)
     lam = torch.from_numpy(inputs.decode_lambda(w)).to(dev)
-    for n0 in range(0, N, 64):      # 64 sequences at a time keeps the prefix buffers at 2 GiB each
-        nb = min(64, N - n0)
-        pk = torch.randn((nb, H, P, d), generator=g, device=dev)
-        pk /= pk.norm(dim=-1, keepdim=True)
-        pv = torch.randn((nb, H, P, d), generator=g, device=dev)
-        pg = w.gamma_lo + (1 - w.gamma_lo) * torch.rand((nb, H, P), generator=g, device=dev)
+    for n0, pk, pv, pg in gen.prefix_batches(64):   # 64 sequences at a time: 2 GiB prefix buffers
+        nb = pk.shape[0]
         mesa.mesa_forward(pk, pk, pv, pg, lam, 0, 0.0, w.chunk, return_iters=False,
                           final_H=SH0[n0:n0 + nb], final_G=SG0[n0:n0 + nb], return_final=True)
         del pk, pv, pg
     S = steps + warmup
-    q = torch.randn((S, N, H, d), generator=g, device=dev)
-    q /= q.norm(dim=-1, keepdim=True)
-    k = torch.randn((S, N, H, d), generator=g, device=dev)
-    k /= k.norm(dim=-1, keepdim=True)
-    v = torch.randn((S, N, H, d), generator=g, device=dev)
-    ga = w.gamma_lo + (1 - w.gamma_lo) * torch.rand((S, N, H), generator=g, device=dev)
+    q, k, v, ga = gen.steps(S)
     out = torch.empty((N, H, d), dtype=torch.float32, device=dev)
     its = torch.empty((S, N, H), dtype=torch.int32, device=dev)
 
@@ -386,16 +451,15 @@ def decode(torch, mesa, inputs, dev, steps=1024, warmup=8, warm_start=True):
     # per head-step: read + write H and G (fp32 d x d each), q, k, v, gamma, out, iters
     bytes_hs = 4 * 4 * d * d + 3 * 4 * d + 4 + 4 * d + 4
     gbs = bytes_hs * nh / (kd_ms * 1e-3) / 1e9
+    hist = torch.bincount(itf.flatten().to(torch.int64), minlength=w.max_iters + 1).cpu().tolist()
     res = {"workload": w.name, "head_steps_per_s": round(steps * nh / el, 1),
            "ms_per_step": round(1e3 * el / steps, 4),
            "iters_mean": round(float(itf.mean()), 3), "iters_max": int(itf.max()),
+           "iters_histogram": {str(i): c for i, c in enumerate(hist) if c},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "decode_kernel<128,float>",
                         "bytes_per_launch": bytes_hs * nh, "avg_launch_ms": round(kd_ms, 4)}}
-    z = torch.randn((S + 3, N, H, d), generator=g, device=dev)
-    q4 = z[0:S] + z[1:S + 1] + z[2:S + 2] + z[3:S + 3]
-    q4 /= q4.norm(dim=-1, keepdim=True)
-    del z
+    q4 = gen.windowed_queries(S, 4)
     warm = {}
     for qname, qs in ((("iid", q), ("window4", q4)) if warm_start else ()):
         warm[qname] = {}
@@ -530,9 +594,30 @@ def measured_peaks(torch, mesa, dev):
     return res
 
 
+def host_facts():
+    """The host the oracle is timed on: logical CPUs, the CPUs this process
+    may run on, the CPU model and OMP_NUM_THREADS."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"nproc": os.cpu_count(), "cpus_allowed": affinity, "cpu_model": model,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(x, w, heads=16):
     """The fp64 oracle, as it stands, on `heads` heads x all T tokens of the
-    headline workload (one OpenMP thread per head)."""
+    headline workload (one OpenMP thread per head), and on one head alone
+    (one thread) for a per-core figure."""
     import numpy as np
     import oracle
     from test_regression_amd import inputs
@@ -548,12 +633,20 @@ def cpu_baseline(x, w, heads=16):
     t0 = time.perf_counter()
     oracle.forward(q, k, v, g, lam, w.max_iters, w.tol)
     el = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.forward(q[:, :1], k[:, :1], v[:, :1], g[:, :1], lam[:1], w.max_iters, w.tol)
+    el1 = time.perf_counter() - t0
     n = heads * w.T
+    orc_flops = (8 + 2 * w.max_iters) * w.d * w.d + 11 * w.max_iters * w.d
     return {"value": round(n / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"all {w.B * w.H} heads" if heads == w.B * w.H else
                        f"{heads} of {w.B * w.H} heads (b, h) = {sel[:3]}...") +
                       f", all {w.T} tokens, k={w.max_iters}; {n} token-heads in {el:.1f} s",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), "host": host_facts(),
+            "oracle_gflops": round(n * orc_flops / el / 1e9, 2),
+            "one_thread": {"value": round(w.T / el1, 2), "unit": "tokens/s", "sample": f"head {sel[0]}, all "
+                           f"{w.T} tokens, one OpenMP thread", "seconds": round(el1, 2),
+                           "oracle_gflops": round(w.T * orc_flops / el1 / 1e9, 3)}}
 
 
 def main():
@@ -595,6 +688,9 @@ def main():
         del a, b
     extra = {}
     if not args.no_extra:
+        extra["small_workloads"] = [small_workload(torch, mesa, inputs, dev, n)
+                                    for n in ("tiny_f32_d16_T256", "mid_bf16_d64_T2048")]
+        torch.cuda.empty_cache()
         extra["backward"] = backward(torch, mesa, h, dev, peaks)
         torch.cuda.empty_cache()
         extra["dynamic"] = dynamic(torch, mesa, inputs, dev)

@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "forward_inputs", "decode_lambda", "decode_prefix", "decode_steps",
-    "bf16_bits", "bf16_bits_to_f32", "as_f64",
+    "decode_queries_windowed", "DecodeDeviceStream", "bf16_bits", "bf16_bits_to_f32", "as_f64",
 ]
 
 
@@ -211,3 +211,58 @@ def hawk_inputs(B: int, T: int, D: int, dtype: str, seed: int, c: float = 8.0, w
     lam = np.log(s / (1.0 - s)).astype(np.float32)
     h0 = rng.standard_normal((B, D)).astype(np.float32) if with_h0 else None
     return dict(x=_store(x, dtype), ga=_store(ga, dtype), gx=_store(gx, dtype), lam=lam, h0=h0)
+
+
+class DecodeDeviceStream:
+    """The decode workload drawn on the device from one seeded torch generator,
+    for sizes too large to draw on the host (256 x 16 heads with 4096-token
+    prefixes are 4.3 G normals).  Same laws as decode_prefix / decode_steps:
+    unit Gaussian key and query rows, N(0, 1) values, gamma ~ U[gamma_lo, 1).
+
+    Draw order: the prefix tokens of `batch` sequences at a time (keys,
+    values, gammas [nb, H, P]), then the per-step inputs of all steps
+    (queries, keys, values [S, N, H, d], gammas [S, N, H]), then the
+    i.i.d. rows of the windowed queries.  Callers draw in that order, so a
+    test and the benchmark that follow it see the same numbers.
+    """
+
+    def __init__(self, torch, w: Workload, dev):
+        self.torch, self.w, self.dev = torch, w, dev
+        self.g = torch.Generator(device=dev)
+        self.g.manual_seed(w.seed)
+
+    def _unit(self, shape):
+        x = self.torch.randn(shape, generator=self.g, device=self.dev)
+        return x / x.norm(dim=-1, keepdim=True)
+
+    def _gamma(self, shape):
+        lo = self.w.gamma_lo
+        return lo + (1 - lo) * self.torch.rand(shape, generator=self.g, device=self.dev)
+
+    def prefix_batches(self, batch: int = 64):
+        """Yields (n0, k, v, gamma) for sequences n0 .. n0 + nb - 1 of the
+        prefix ([nb, H, P, d] float32 and [nb, H, P])."""
+        w = self.w
+        for n0 in range(0, w.B, batch):
+            nb = min(batch, w.B - n0)
+            k = self._unit((nb, w.H, w.T, w.d))
+            v = self.torch.randn((nb, w.H, w.T, w.d), generator=self.g, device=self.dev)
+            yield n0, k, v, self._gamma((nb, w.H, w.T))
+
+    def steps(self, S: int):
+        """Per-step inputs of S steps: (q, k, v [S, N, H, d], gamma [S, N, H])."""
+        w = self.w
+        q = self._unit((S, w.B, w.H, w.d))
+        k = self._unit((S, w.B, w.H, w.d))
+        v = self.torch.randn((S, w.B, w.H, w.d), generator=self.g, device=self.dev)
+        return q, k, v, self._gamma((S, w.B, w.H))
+
+    def windowed_queries(self, S: int, window: int = 4):
+        """Queries [S, N, H, d], each the unit-normalised sum of `window`
+        consecutive i.i.d. N(0, 1) rows (see decode_queries_windowed)."""
+        w = self.w
+        z = self.torch.randn((S + window - 1, w.B, w.H, w.d), generator=self.g, device=self.dev)
+        s = z[0:S].clone()
+        for j in range(1, window):
+            s += z[j:j + S]
+        return s / s.norm(dim=-1, keepdim=True)

@@ -115,6 +115,59 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _dims(t, name, ndim):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {list(t.shape)}")
+    return tuple(t.shape)
+
+
+def _shapes(*specs):
+    """Every (tensor, name, shape) must have exactly that shape.  Checked
+    before any device or dtype check, so that a mis-shaped argument is named
+    whatever else is wrong."""
+    for t, name, shape in specs:
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
+def _shape(t, name, shape, dtype=None, device=None):
+    """A device tensor of exactly this shape (and dtype/device, when given)."""
+    _shapes((t, name, shape))
+    _need(t, name, dtype, device)
+
+
+def _given(*specs):
+    """The (tensor, name, shape) specs whose tensor was given."""
+    return tuple(sp for sp in specs if sp[0] is not None)
+
+
+def _forward_checks(q, k, v, gamma, lam, **outs):
+    """Shapes, dtypes and devices of mesa_forward's inputs, and the shapes of
+    the outputs the caller passed (out, iters, x_out, final_H, final_G);
+    returns (B, H, T, dk, dv)."""
+    import torch
+    B, H, T, dk = _dims(q, "q", 4)
+    dv = _dims(v, "v", 4)[-1]
+    oshape = dict(out=(B, H, T, dv), iters=(B, H, T), x_out=(B, H, T, dk), final_H=(B, H, dk, dk),
+                  final_G=(B, H, dv, dk))
+    _shapes((k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)), (gamma, "gamma", (B, H, T)),
+            (lam, "lambda", (H, dk)), *_given(*((t, n, oshape[n]) for n, t in outs.items())))
+    _qkv_dtype(q)
+    for t, n, dt in ((q, "q", q.dtype), (k, "k", q.dtype), (v, "v", q.dtype), (gamma, "gamma", torch.float32),
+                     (lam, "lambda", torch.float32)):
+        _need(t, n, dt, q.device)
+    return B, H, T, dk, dv
+
+
+def _out(t, name, shape, dtype, device):
+    """A caller-provided output: checked like an input, or allocated."""
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _shape(t, name, shape, dtype, device)
+    return t
+
+
 def mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk) -> int:
     return int(lib().mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk))
 
@@ -129,34 +182,25 @@ def mesa_forward(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out=None,
     final_H, final_G); iters/final_* are None unless requested.
     """
     import torch
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, H, T, dk, dv = _forward_checks(q, k, v, gamma, lam, out=out, iters=iters, final_H=final_H,
+                                      final_G=final_G)
     dev = q.device
     dt = _qkv_dtype(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype, dev)
-    _need(gamma, "gamma", torch.float32, dev)
-    _need(lam, "lambda", torch.float32, dev)
-    if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
-        raise ValueError("q, k, v shapes disagree")
-    if tuple(gamma.shape) != (B, H, T) or tuple(lam.shape) != (H, dk):
-        raise ValueError("gamma must be [B,H,T] and lambda [H,dk]")
-    if out is None:
-        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
-    if iters is None and return_iters:
-        iters = torch.empty((B, H, T), dtype=torch.int32, device=dev)
-    if return_final:
-        if final_H is None:
-            final_H = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
-        if final_G is None:
-            final_G = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    out = _out(out, "out", (B, H, T, dv), torch.float32, dev)
+    if iters is not None or return_iters:
+        iters = _out(iters, "iters", (B, H, T), torch.int32, dev)
+    if return_final or final_H is not None or final_G is not None:
+        final_H = _out(final_H, "final_H", (B, H, dk, dk), torch.float32, dev)
+        final_G = _out(final_G, "final_G", (B, H, dv, dk), torch.float32, dev)
     ws_bytes = mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk) if max_iters > 0 else 0
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", None, dev)
     st = lib().mesa_forward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(gamma), _ptr(lam),
                             B, H, T, dk, dv, int(chunk), int(max_iters), float(tol),
                             _ptr(out), _ptr(iters), _ptr(final_H), _ptr(final_G),
-                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                             _stream(stream))
     _check(st, "mesa_forward")
     return out, iters, final_H, final_G
@@ -167,25 +211,19 @@ def mesa_forward_train(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out
     """Forward that also returns the CG solutions x (see include/mesa.h,
     mesa_forward_train).  Returns (out, iters, x)."""
     import torch
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, H, T, dk, dv = _forward_checks(q, k, v, gamma, lam, out=out, iters=iters, x_out=x_out)
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype, dev)
-    _need(gamma, "gamma", torch.float32, dev)
-    _need(lam, "lambda", torch.float32, dev)
-    if out is None:
-        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
-    if iters is None:
-        iters = torch.empty((B, H, T), dtype=torch.int32, device=dev)
-    if x_out is None:
-        x_out = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
+    out = _out(out, "out", (B, H, T, dv), torch.float32, dev)
+    iters = _out(iters, "iters", (B, H, T), torch.int32, dev)
+    x_out = _out(x_out, "x_out", (B, H, T, dk), torch.float32, dev)
     nbytes = mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, dev)
     st = lib().mesa_forward_train(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(gamma), _ptr(lam),
                                   B, H, T, dk, dv, chunk, int(max_iters), float(tol),
-                                  _ptr(out), _ptr(iters), _ptr(x_out), _ptr(workspace), workspace.numel(),
+                                  _ptr(out), _ptr(iters), _ptr(x_out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
                                   _stream(stream))
     _check(st, "mesa_forward_train")
     return out, iters, x_out
@@ -200,13 +238,16 @@ def mesa_backward(k, v, gamma, lam, x, out, grad_out, max_iters, tol=0.0, chunk=
     """Backward pass (see include/mesa.h, mesa_backward).  Returns a dict of
     grad_q, grad_k, grad_v, grad_gamma, grad_lambda (float32) and z_iters."""
     import torch
-    B, H, T, dk = k.shape
-    dv = v.shape[-1]
+    B, H, T, dk = _dims(k, "k", 4)
+    dv = _dims(v, "v", 4)[-1]
     dev = k.device
-    for t, n in ((k, "k"), (v, "v")):
-        _need(t, n, k.dtype, dev)
-    for t, n in ((gamma, "gamma"), (lam, "lambda"), (x, "x"), (out, "out"), (grad_out, "grad_out")):
-        _need(t, n, torch.float32, dev)
+    _shapes((v, "v", (B, H, T, dv)), (gamma, "gamma", (B, H, T)), (lam, "lambda", (H, dk)),
+            (x, "x", (B, H, T, dk)), (out, "out", (B, H, T, dv)), (grad_out, "grad_out", (B, H, T, dv)))
+    _qkv_dtype(k)
+    for t, n, dt in ((k, "k", k.dtype), (v, "v", k.dtype), (gamma, "gamma", torch.float32),
+                     (lam, "lambda", torch.float32), (x, "x", torch.float32), (out, "out", torch.float32),
+                     (grad_out, "grad_out", torch.float32)):
+        _need(t, n, dt, dev)
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(grad_q=torch.empty((B, H, T, dk), **f32), grad_k=torch.empty((B, H, T, dk), **f32),
              grad_v=torch.empty((B, H, T, dv), **f32), grad_gamma=torch.empty((B, H, T), **f32),
@@ -215,32 +256,35 @@ def mesa_backward(k, v, gamma, lam, x, out, grad_out, max_iters, tol=0.0, chunk=
     nbytes = mesa_backward_workspace_bytes(B, H, T, dk, dv, chunk)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, dev)
     st = lib().mesa_backward(_ptr(k), _ptr(v), _qkv_dtype(k), _ptr(gamma), _ptr(lam), _ptr(x), _ptr(out),
                              _ptr(grad_out), B, H, T, dk, dv, chunk, int(max_iters), float(tol),
                              _ptr(g["grad_q"]), _ptr(g["grad_k"]), _ptr(g["grad_v"]), _ptr(g["grad_gamma"]),
-                             _ptr(g["grad_lambda"]), _ptr(g["z_iters"]), _ptr(workspace), workspace.numel(),
+                             _ptr(g["grad_lambda"]), _ptr(g["z_iters"]), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(),
                              _stream(stream))
     _check(st, "mesa_backward")
     return g
 
 
-def _decode_checks(q, v, gamma, lam, state_H, state_G, state_x=None):
+def _decode_checks(q, k, v, gamma, lam, state_H, state_G, state_x=None, out=None, iters=None):
     import torch
-    N, H, dk = q.shape
-    dv = v.shape[-1]
+    N, H, dk = _dims(q, "q", 3)
+    dv = _dims(v, "v", 3)[-1]
     dev = q.device
-    for t, n in ((q, "q"), (v, "v")):
-        _need(t, n, q.dtype, dev)
-    _need(gamma, "gamma", torch.float32, dev)
-    _need(lam, "lambda", torch.float32, dev)
-    _need(state_H, "state_H", torch.float32, dev)
-    _need(state_G, "state_G", torch.float32, dev)
-    if tuple(state_H.shape) != (N, H, dk, dk) or tuple(state_G.shape) != (N, H, dv, dk):
-        raise ValueError("state shapes disagree with q/v")
+    specs = [(k, "k", (N, H, dk)), (v, "v", (N, H, dv)), (gamma, "gamma", (N, H)), (lam, "lambda", (H, dk)),
+             (state_H, "state_H", (N, H, dk, dk)), (state_G, "state_G", (N, H, dv, dk)),
+             *_given((out, "out", (N, H, dv)), (iters, "iters", (N, H)))]
+    if state_x is not None:
+        specs.append((state_x, "state_x", (N, H, dk)))
+    _shapes(*specs)
+    _qkv_dtype(q)
+    for t, n, dt in ((q, "q", q.dtype), (k, "k", q.dtype), (v, "v", q.dtype), (gamma, "gamma", torch.float32),
+                     (lam, "lambda", torch.float32), (state_H, "state_H", torch.float32),
+                     (state_G, "state_G", torch.float32)):
+        _need(t, n, dt, dev)
     if state_x is not None:
         _need(state_x, "state_x", torch.float32, dev)
-        if tuple(state_x.shape) != (N, H, dk):
-            raise ValueError("state_x must be [N,H,dk]")
     return N, H, dk, dv, dev
 
 
@@ -252,12 +296,10 @@ def mesa_decode_step(q, k, v, gamma, lam, state_H, state_G, max_iters, tol=0.0, 
     state_H: [N,H,dk,dk], state_G: [N,H,dv,dk] float32.  Returns (out, iters).
     """
     import torch
-    _need(k, "k", q.dtype, q.device)
-    N, H, dk, dv, dev = _decode_checks(q, v, gamma, lam, state_H, state_G)
-    if out is None:
-        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
-    if iters is None and return_iters:
-        iters = torch.empty((N, H), dtype=torch.int32, device=dev)
+    N, H, dk, dv, dev = _decode_checks(q, k, v, gamma, lam, state_H, state_G, out=out, iters=iters)
+    out = _out(out, "out", (N, H, dv), torch.float32, dev)
+    if iters is not None or return_iters:
+        iters = _out(iters, "iters", (N, H), torch.int32, dev)
     st = lib().mesa_decode_step(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(gamma), _ptr(lam),
                                 _ptr(state_H), _ptr(state_G), N, H, dk, dv, int(max_iters),
                                 float(tol), _ptr(out), _ptr(iters), _stream(stream))
@@ -274,12 +316,10 @@ def mesa_decode_step_warm(q, k, v, gamma, lam, state_H, state_G, state_x, max_it
     solutions on entry, this step's on exit.  Returns (out, iters).
     """
     import torch
-    _need(k, "k", q.dtype, q.device)
-    N, H, dk, dv, dev = _decode_checks(q, v, gamma, lam, state_H, state_G, state_x)
-    if out is None:
-        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
-    if iters is None and return_iters:
-        iters = torch.empty((N, H), dtype=torch.int32, device=dev)
+    N, H, dk, dv, dev = _decode_checks(q, k, v, gamma, lam, state_H, state_G, state_x, out=out, iters=iters)
+    out = _out(out, "out", (N, H, dv), torch.float32, dev)
+    if iters is not None or return_iters:
+        iters = _out(iters, "iters", (N, H), torch.int32, dev)
     st = lib().mesa_decode_step_warm(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(gamma), _ptr(lam),
                                      _ptr(state_H), _ptr(state_G), _ptr(state_x), N, H, dk, dv,
                                      int(max_iters), float(tol), int(warm_mode), _ptr(out), _ptr(iters),
@@ -297,22 +337,19 @@ def mesa_qk_preprocess(x, conv_w, hist=None, *, out_dtype=None, out=None, return
     return_hist also hist_out, the last W-1 input rows for the next piece.
     """
     import torch
-    B, H, T, d = x.shape
-    W = conv_w.shape[1]
+    B, H, T, d = _dims(x, "x", 4)
+    W = _dims(conv_w, "conv_w", 3)[1]
     dev = x.device
+    _shapes((conv_w, "conv_w", (H, W, d)), *(((hist, "hist", (B, H, W - 1, d)),) if hist is not None else ()))
+    _qkv_dtype(x)
     _need(x, "x", None, dev)
     _need(conv_w, "conv_w", torch.float32, dev)
-    if tuple(conv_w.shape) != (H, W, d):
-        raise ValueError("conv_w must be [H, W, d]")
     if hist is not None:
         _need(hist, "hist", x.dtype, dev)
-        if tuple(hist.shape) != (B, H, W - 1, d):
-            raise ValueError("hist must be [B, H, W-1, d]")
-    out_dtype = x.dtype if out_dtype is None else out_dtype
-    if out is None:
-        out = torch.empty((B, H, T, d), dtype=out_dtype, device=dev)
-    if return_hist and hist_out is None:
-        hist_out = torch.empty((B, H, W - 1, d), dtype=x.dtype, device=dev)
+    out_dtype = (x.dtype if out is None else out.dtype) if out_dtype is None else out_dtype
+    out = _out(out, "out", (B, H, T, d), out_dtype, dev)
+    if return_hist or hist_out is not None:
+        hist_out = _out(hist_out, "hist_out", (B, H, W - 1, d), x.dtype, dev)
     st = lib().mesa_qk_preprocess(_ptr(x), _qkv_dtype(x), _ptr(conv_w), W, _ptr(hist), _ptr(hist_out),
                                   B, H, T, d, _ptr(out), _qkv_dtype(out), _stream(stream))
     _check(st, "mesa_qk_preprocess")
@@ -327,21 +364,24 @@ def mesa_hawk_scan(x, ga, gx, lam, c=8.0, h0=None, *, out=None, return_final=Fal
     h0: [B,D] float32 or None.  Returns y [B,T,D] float32 (and h_final [B,D]).
     """
     import torch
-    B, T, D = x.shape
+    B, T, D = _dims(x, "x", 3)
     dev = x.device
-    for t, n in ((x, "x"), (ga, "ga"), (gx, "gx")):
-        _need(t, n, x.dtype, dev)
-    _need(lam, "lam", torch.float32, dev)
+    _shapes((ga, "ga", (B, T, D)), (gx, "gx", (B, T, D)), (lam, "lam", (D,)),
+            *(((h0, "h0", (B, D)),) if h0 is not None else ()))
+    _qkv_dtype(x)
+    for t, n, dt in ((x, "x", x.dtype), (ga, "ga", x.dtype), (gx, "gx", x.dtype), (lam, "lam", torch.float32)):
+        _need(t, n, dt, dev)
     if h0 is not None:
         _need(h0, "h0", torch.float32, dev)
-    if out is None:
-        out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    out = _out(out, "out", (B, T, D), torch.float32, dev)
     hf = torch.empty((B, D), dtype=torch.float32, device=dev) if return_final else None
     nbytes = int(lib().mesa_hawk_workspace_bytes(B, T, D))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, dev)
     st = lib().mesa_hawk_scan(_ptr(x), _ptr(ga), _ptr(gx), _qkv_dtype(x), _ptr(lam), float(c), _ptr(h0), B, T, D,
-                              _ptr(out), _ptr(hf), _ptr(workspace), workspace.numel(), _stream(stream))
+                              _ptr(out), _ptr(hf), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
     _check(st, "mesa_hawk_scan")
     return (out, hf) if return_final else out
 

@@ -351,3 +351,56 @@ def test_status_mapping():
         mesa._check(WS_SMALL, "x")
     with pytest.raises(mesa.MesaError):
         mesa._check(HIPERR, "x")
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32 if dtype is None else dtype)
+
+
+@pytest.mark.parametrize("case", [
+    "forward_lambda", "forward_gamma", "forward_k", "forward_out", "train_v", "train_x_out",
+    "backward_x", "backward_grad_out", "backward_lambda", "decode_lambda", "decode_k", "decode_gamma",
+    "decode_state", "warm_state_x", "preprocess_w", "preprocess_hist", "hawk_lam", "hawk_ga", "hawk_h0",
+])
+def test_binding_rejects_mis_shaped_tensors(case):
+    """Every wrapper checks the shape of every tensor against the sizes it
+    passes to the library (which only sees raw pointers), before anything
+    else: a mis-shaped tensor is a ValueError and never reaches a kernel."""
+    import torch
+    from test_regression_amd import mesa
+    B, H, T, d = 2, 3, 5, 16
+    q = _cpu(B, H, T, d)
+    g = _cpu(B, H, T)
+    lam = _cpu(H, d)
+    calls = {
+        "forward_lambda": lambda: mesa.mesa_forward(q, q, q, g, _cpu(d), 3),
+        "forward_gamma": lambda: mesa.mesa_forward(q, q, q, _cpu(B, H, T + 1), lam, 3),
+        "forward_k": lambda: mesa.mesa_forward(q, _cpu(B, H, T, 2 * d), q, g, lam, 3),
+        "forward_out": lambda: mesa.mesa_forward(q, q, q, g, lam, 3, out=_cpu(B, H, T, d + 1)),
+        "train_v": lambda: mesa.mesa_forward_train(q, q, _cpu(B, H, T - 1, d), g, lam, 3),
+        "train_x_out": lambda: mesa.mesa_forward_train(q, q, q, g, lam, 3, x_out=_cpu(B, H, d)),
+        "backward_x": lambda: mesa.mesa_backward(q, q, g, lam, _cpu(B, H, T, d + 2), q, q, 3),
+        "backward_grad_out": lambda: mesa.mesa_backward(q, q, g, lam, q, q, _cpu(B, 1, T, d), 3),
+        "backward_lambda": lambda: mesa.mesa_backward(q, q, g, _cpu(1, d), q, q, q, 3),
+        "decode_lambda": lambda: mesa.mesa_decode_step(_cpu(B, H, d), _cpu(B, H, d), _cpu(B, H, d), _cpu(B, H),
+                                                       _cpu(d), _cpu(B, H, d, d), _cpu(B, H, d, d), 3),
+        "decode_k": lambda: mesa.mesa_decode_step(_cpu(B, H, d), _cpu(B, 1, d), _cpu(B, H, d), _cpu(B, H),
+                                                  lam, _cpu(B, H, d, d), _cpu(B, H, d, d), 3),
+        "decode_gamma": lambda: mesa.mesa_decode_step(_cpu(B, H, d), _cpu(B, H, d), _cpu(B, H, d), _cpu(B),
+                                                      lam, _cpu(B, H, d, d), _cpu(B, H, d, d), 3),
+        "decode_state": lambda: mesa.mesa_decode_step(_cpu(B, H, d), _cpu(B, H, d), _cpu(B, H, d), _cpu(B, H),
+                                                      lam, _cpu(H, B, d, d), _cpu(B, H, d, d), 3),
+        "warm_state_x": lambda: mesa.mesa_decode_step_warm(_cpu(B, H, d), _cpu(B, H, d), _cpu(B, H, d),
+                                                           _cpu(B, H), lam, _cpu(B, H, d, d), _cpu(B, H, d, d),
+                                                           _cpu(B, d), 3),
+        "preprocess_w": lambda: mesa.mesa_qk_preprocess(q, _cpu(1, 4, d)),
+        "preprocess_hist": lambda: mesa.mesa_qk_preprocess(q, _cpu(H, 4, d), hist=_cpu(B, H, 4, d)),
+        "hawk_lam": lambda: mesa.mesa_hawk_scan(_cpu(B, T, d), _cpu(B, T, d), _cpu(B, T, d), _cpu(d + 1)),
+        "hawk_ga": lambda: mesa.mesa_hawk_scan(_cpu(B, T, d), _cpu(B, T + 1, d), _cpu(B, T, d), _cpu(d)),
+        "hawk_h0": lambda: mesa.mesa_hawk_scan(_cpu(B, T, d), _cpu(B, T, d), _cpu(B, T, d), _cpu(d),
+                                               h0=_cpu(1, d)),
+    }
+    with pytest.raises(ValueError, match="must have shape"):
+        calls[case]()
+    del torch

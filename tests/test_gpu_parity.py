@@ -3,9 +3,10 @@
 Each test prints the case it runs (name, shape, seed) before touching the
 GPU.  Tolerances: relative L2 <= 2e-3 (float32 q/k/v) or <= 1e-2 (bfloat16),
 iteration counts exact for every token whose stop decision is decidable
-(see parity_helpers).  Full-size workloads are compared on sampled heads and
-tokens the oracle computes one by one, in the launch configuration the
-benchmark times (chunk 64).
+(see parity_helpers).  The layer and dynamic-stopping workloads are compared
+on every token of every head, in the launch configuration the benchmark
+times (chunk 64); the decode workload on all heads for its first steps and
+on sampled heads over the benchmark's whole run.
 """
 import sys
 
@@ -68,116 +69,183 @@ def test_mid_workload_full():
     compare_counts(g["iters"], r, w.max_iters, w.tol)
 
 
-def _sample_mask(T, rng, n=96):
-    idx = np.unique(np.concatenate([np.arange(3), np.arange(T - 3, T), rng.choice(T, n, replace=False)]))
-    m = np.zeros(T, bool)
-    m[idx] = True
-    return m
-
-
-def test_layer_workload_sampled():
-    """Full layer size (8x16x4096, d=128, bf16, k=30) on the GPU; oracle on sampled tokens."""
+def test_layer_workload_full():
+    """Full layer size (8x16x4096, d=128, bf16, k=30) in the launch
+    configuration the benchmark times; the oracle solves every token of all
+    128 heads."""
     w = inputs.WORKLOADS["layer_bf16_d128_T4096_k30"]
     say("case", w)
     x = inputs.forward_inputs(w)
     g = gpu_forward(x, w.dtype, w.max_iters, w.tol, w.chunk)
     assert np.isfinite(g["out"]).all()
     assert (g["iters"] == w.max_iters).all()
-    rng = np.random.default_rng(5)
-    heads = [(0, 0), (7, 15), (3, 9), (5, 2)]
-    errs = []
-    for b, h in heads:
-        want = _sample_mask(w.T, rng)[None, None]
-        r = oracle_forward(sub(x, b, h), w.dtype, w.max_iters, w.tol, want=want)
-        sel = want[0, 0]
-        e = rel_l2(g["out"][b, h][sel], r["out"][0, 0][sel])
-        errs.append(e)
-        assert (r["iters"][0, 0][sel] == w.max_iters).all()
-    say(f"layer sampled rel_l2 per head={['%.2e' % e for e in errs]}")
-    assert max(errs) <= RTOL[w.dtype]
+    r = oracle_forward(x, w.dtype, w.max_iters, w.tol)
+    assert (r["iters"] == w.max_iters).all()
+    e = rel_l2(g["out"], r["out"])
+    per_head = [rel_l2(g["out"][b, h], r["out"][b, h]) for b in range(w.B) for h in range(w.H)]
+    tok = np.linalg.norm(g["out"] - r["out"], axis=-1) / np.maximum(np.linalg.norm(r["out"], axis=-1), 1e-30)
+    say(f"layer full: rel_l2={e:.3e} worst head={max(per_head):.3e} worst token={tok.max():.3e} "
+        f"({w.B * w.H * w.T} token-heads)")
+    assert e <= RTOL[w.dtype] and max(per_head) <= RTOL[w.dtype]
 
 
-def test_dynamic_workload_sampled():
-    """Full dynamic-stopping size (4x16x8192, fp32, tol 1e-4, cap 30); oracle on whole heads."""
+def test_dynamic_workload_full():
+    """Full dynamic-stopping size (4x16x8192, fp32, tol 1e-4, cap 30); the
+    oracle solves every token of all 64 heads and the iteration counts of
+    every decidable token must match exactly."""
     w = inputs.WORKLOADS["dynamic_f32_d128_T8192_tol1e-4"]
     say("case", w)
     x = inputs.forward_inputs(w)
     g = gpu_forward(x, w.dtype, w.max_iters, w.tol, w.chunk)
-    heads = [(0, 0), (3, 15), (1, 7), (2, 11)]
-    tot_d = tot_u = tot_m = 0
-    for b, h in heads:
-        r = oracle_forward(sub(x, b, h), w.dtype, w.max_iters, w.tol)
-        e = rel_l2(g["out"][b, h], r["out"][0, 0])
-        assert e <= RTOL[w.dtype], (b, h, e)
-        nd, nu, nm = compare_counts(g["iters"][b:b + 1, h:h + 1], r, w.max_iters, w.tol)
-        tot_d += nd
-        tot_u += nu
-        tot_m += nm
+    r = oracle_forward(x, w.dtype, w.max_iters, w.tol)
+    e = rel_l2(g["out"], r["out"])
+    worst = max(rel_l2(g["out"][b, h], r["out"][b, h]) for b in range(w.B) for h in range(w.H))
+    nd, nu, nm = compare_counts(g["iters"], r, w.max_iters, w.tol)
     it = g["iters"]
-    say(f"dynamic: iters min/mean/max={it.min()}/{it.mean():.2f}/{it.max()} "
-        f"decidable={tot_d} undecidable={tot_u} (mismatched {tot_m})")
+    hist = np.bincount(it.ravel(), minlength=w.max_iters + 1)
+    say(f"dynamic full: rel_l2={e:.3e} worst head={worst:.3e} iters min/mean/max="
+        f"{it.min()}/{it.mean():.3f}/{it.max()} decidable={nd} undecidable={nu} (mismatched {nm}); "
+        f"histogram {dict((i, int(c)) for i, c in enumerate(hist) if c)}")
+    assert e <= RTOL[w.dtype] and worst <= RTOL[w.dtype]
     assert it.min() < it.max()          # counts vary per token
-    assert tot_d > 0.99 * (tot_d + tot_u)
+    assert nd > 0.99 * (nd + nu)
 
 
-def _decode_case(w, steps, S, prefix):
-    """States from S distinct oracle-built prefixes (fp64 -> fp32), tiled over N x H heads."""
-    N, H, d = w.B, w.H, w.d
-    pk = np.zeros((1, S, prefix, d), np.float32)
-    pv = np.zeros_like(pk)
-    pg = np.zeros((1, S, prefix), np.float32)
-    for i in range(S):
-        p = inputs.decode_prefix(w, i, i % H, prefix)
-        pk[0, i], pv[0, i], pg[0, i] = p["k"], p["v"], p["gamma"]
-    r = oracle.forward(pk, pk, pv, pg, np.ones((S, d)), 0, 0.0,
-                       want=np.zeros((1, S, prefix), bool), final_state=True)
-    idx = (np.arange(N * H) % S).reshape(N, H)
-    H0 = r["final_H"][0][idx].astype(np.float32)
-    G0 = r["final_G"][0][idx].astype(np.float32)
-    return H0, G0, inputs.decode_steps(w, steps), inputs.decode_lambda(w)
+# Sampled decode heads (n, h): every head index and spread sequence indices.
+DECODE_SAMPLE = [((37 * i + 5) % 256, i % 16) for i in range(32)]
 
 
-def test_decode_workload_full_launch_shape():
-    """256 x 16 heads, d=128, states from 4096-token prefixes; a few steps vs the oracle."""
+@pytest.fixture(scope="module")
+def decode_ws():
+    """The decode workload as the benchmark draws it: start states of all
+    256 x 16 heads built on the device from seeded 4096-token prefixes by the
+    forward path (zero CG iterations, final states exported; distinct for
+    every (n, h)), the per-step inputs of the benchmark's 8 warmup + 1024
+    timed steps, and the prefix tokens of the sampled heads on the host."""
     import torch
     from test_regression_amd import mesa
     w = inputs.WORKLOADS["decode_f32_d128_N256_prefix4096"]
-    steps = 3
-    say("case", w, "steps", steps)
-    H0, G0, st, lam = _decode_case(w, steps, S=16, prefix=w.T)
-    SH, SG = to_dev(H0, "f32"), to_dev(G0, "f32")
+    N, H, d = w.B, w.H, w.d
+    gen = inputs.DecodeDeviceStream(torch, w, torch.device("cuda"))
+    lam = inputs.decode_lambda(w)
     lam_d = to_dev(lam, "f32")
-    RH, RG = H0.astype(np.float64), G0.astype(np.float64)
-    for s in range(steps):
-        q, k, v, g = (to_dev(st[n][s], "f32") for n in ("q", "k", "v", "gamma"))
-        out, it = mesa.mesa_decode_step(q, k, v, g, lam_d, SH, SG, w.max_iters, w.tol)
-        torch.cuda.synchronize()
-        r = oracle.decode_step(st["q"][s], st["k"][s], st["v"][s], st["gamma"][s], lam, RH, RG,
-                               w.max_iters, w.tol)
-        e = rel_l2(out.cpu().numpy(), r["out"])
-        nd, nu, nm = compare_counts(it.cpu().numpy(), r, w.max_iters, w.tol)
-        say(f"decode step {s}: rel_l2={e:.3e} iters mean={r['iters'].mean():.2f} "
-            f"decidable={nd} undecidable={nu} mismatched={nm}")
-        assert e <= RTOL["f32"]
-    assert rel_l2(SH.cpu().numpy(), RH) < 1e-5 and rel_l2(SG.cpu().numpy(), RG) < 1e-5
+    SH = torch.empty((N, H, d, d), dtype=torch.float32, device="cuda")
+    SG = torch.empty_like(SH)
+    pre = {}
+    for n0, pk, pv, pg in gen.prefix_batches(64):
+        nb = pk.shape[0]
+        mesa.mesa_forward(pk, pk, pv, pg, lam_d, 0, 0.0, w.chunk, return_iters=False,
+                          final_H=SH[n0:n0 + nb], final_G=SG[n0:n0 + nb], return_final=True)
+        for n, h in DECODE_SAMPLE:
+            if n0 <= n < n0 + nb:
+                pre[(n, h)] = tuple(a[n - n0, h].cpu().numpy() for a in (pk, pv, pg))
+        del pk, pv, pg
+    steps = gen.steps(8 + w.steps)
+    torch.cuda.synchronize()
+    return dict(w=w, lam=lam, lam_d=lam_d, SH=SH, SG=SG, pre=pre, steps=steps)
+
+
+def test_decode_workload_full(decode_ws):
+    """The decode workload at full size: 256 x 16 heads (d=128), distinct
+    start states from 4096-token prefixes, the benchmark's 1032 steps.
+      1. the device-built start states of 32 sampled heads against the
+         oracle run over the same prefix tokens;
+      2. the first 16 steps of all 4096 heads against the oracle from the same
+         fp32 start states (outputs, counts, and the states after them);
+      3. every later step of the sampled heads against the oracle continuing
+         from its own states, and their final states."""
+    import torch
+    from test_regression_amd import mesa
+    ws = decode_ws
+    w, lam = ws["w"], ws["lam"]
+    N, H, d = w.B, w.H, w.d
+    ns = np.array([n for n, _ in DECODE_SAMPLE])
+    hs = np.array([h for _, h in DECODE_SAMPLE])
+    say("case decode full", w.name, "sampled heads", len(DECODE_SAMPLE))
+    # 1. start states against the oracle over the sampled heads' prefixes
+    pk = np.stack([ws["pre"][nh][0] for nh in DECODE_SAMPLE])[None]
+    pv = np.stack([ws["pre"][nh][1] for nh in DECODE_SAMPLE])[None]
+    pg = np.stack([ws["pre"][nh][2] for nh in DECODE_SAMPLE])[None]
+    rp = oracle.forward(pk, pk, pv, pg, lam[hs], 0, 0.0, want=np.zeros(pg.shape, bool), final_state=True)
+    SH0 = ws["SH"].cpu().numpy()
+    SG0 = ws["SG"].cpu().numpy()
+    eh, eg = rel_l2(SH0[ns, hs], rp["final_H"][0]), rel_l2(SG0[ns, hs], rp["final_G"][0])
+    say(f"decode start states (device-built) vs oracle: H rel_l2={eh:.2e} G rel_l2={eg:.2e}")
+    assert eh < 1e-5 and eg < 1e-5
+    # 2. all heads for the first steps
+    SH, SG = ws["SH"].clone(), ws["SG"].clone()
+    RH, RG = SH0.astype(np.float64), SG0.astype(np.float64)
+    del SH0, SG0
+    q, k, v, ga = ws["steps"]
+    S_all, S = 16, q.shape[0]
+    out = torch.empty((N, H, d), dtype=torch.float32, device="cuda")
+    its = torch.empty((N, H), dtype=torch.int32, device="cuda")
+    tot = np.zeros(3, np.int64)
+    worst = 0.0
+    for s in range(S_all):
+        mesa.mesa_decode_step(q[s], k[s], v[s], ga[s], ws["lam_d"], SH, SG, w.max_iters, w.tol, out=out, iters=its)
+        a = [t[s].cpu().numpy() for t in (q, k, v, ga)]
+        r = oracle.decode_step(*a, lam, RH, RG, w.max_iters, w.tol)
+        o = out.cpu().numpy()
+        e = rel_l2(o, r["out"])
+        wh = np.max(np.linalg.norm(o - r["out"], axis=-1) / np.linalg.norm(r["out"], axis=-1))
+        worst = max(worst, wh)
+        tot += compare_counts(its.cpu().numpy(), r, w.max_iters, w.tol)
+        assert e <= RTOL["f32"] and wh <= RTOL["f32"], (s, e, wh)
+    eh, eg = rel_l2(SH.cpu().numpy(), RH), rel_l2(SG.cpu().numpy(), RG)
+    say(f"decode all {N * H} heads, {S_all} steps: worst head rel_l2={worst:.2e}; states H {eh:.2e} G {eg:.2e}; "
+        f"decidable={tot[0]} undecidable={tot[1]} mismatched={tot[2]}")
+    assert eh < 1e-5 and eg < 1e-5
+    # 3. the rest of the run on the sampled heads
+    RHs, RGs = np.ascontiguousarray(RH[ns, hs][None]), np.ascontiguousarray(RG[ns, hs][None])
+    del RH, RG
+    nsd, hsd = torch.from_numpy(ns).cuda(), torch.from_numpy(hs).cuda()
+    outs = torch.empty((S, len(ns), d), dtype=torch.float32, device="cuda")
+    itss = torch.empty((S, len(ns)), dtype=torch.int32, device="cuda")
+    for s in range(S_all, S):
+        mesa.mesa_decode_step(q[s], k[s], v[s], ga[s], ws["lam_d"], SH, SG, w.max_iters, w.tol, out=out, iters=its)
+        outs[s] = out[nsd, hsd]
+        itss[s] = its[nsd, hsd]
+    sel = [t[:, nsd, hsd][:, None].cpu().numpy() for t in (q, k, v, ga)]
+    outs, itss = outs.cpu().numpy(), itss.cpu().numpy()
+    lam_s = np.ascontiguousarray(lam[hs])
+    tot = np.zeros(3, np.int64)
+    worst = 0.0
+    hist = np.zeros(w.max_iters + 1, np.int64)
+    for s in range(S_all, S):
+        r = oracle.decode_step(sel[0][s], sel[1][s], sel[2][s], sel[3][s], lam_s, RHs, RGs, w.max_iters, w.tol)
+        o = outs[s][None]
+        wh = np.max(np.linalg.norm(o - r["out"], axis=-1) / np.linalg.norm(r["out"], axis=-1))
+        worst = max(worst, wh)
+        assert wh <= RTOL["f32"], (s, wh)
+        tot += compare_counts(itss[s][None], r, w.max_iters, w.tol)
+        hist += np.bincount(r["iters"].ravel(), minlength=w.max_iters + 1)
+    eh = rel_l2(SH[nsd, hsd].cpu().numpy(), RHs[0])
+    eg = rel_l2(SG[nsd, hsd].cpu().numpy(), RGs[0])
+    say(f"decode sampled heads, steps {S_all}..{S - 1}: worst head rel_l2={worst:.2e}; final states H {eh:.2e} "
+        f"G {eg:.2e}; decidable={tot[0]} undecidable={tot[1]} mismatched={tot[2]}; oracle iteration histogram "
+        f"{dict((i, int(c)) for i, c in enumerate(hist) if c)}")
+    assert eh < 1e-5 and eg < 1e-5
+    assert tot[0] > 0.99 * (tot[0] + tot[1])
 
 
 @pytest.mark.parametrize("mode", [1, 2])
-def test_warm_decode_full_launch_shape(mode):
+def test_warm_decode_full_launch_shape(decode_ws, mode):
     """Warm-started decode (x0 from each head's previous solution) at 256 x 16
-    heads, d=128, chained over steps with queries that overlap their
-    neighbours (window 4); the solution carried in state_x is compared too."""
+    heads, d=128, from the distinct device-built start states, chained over
+    steps with queries that overlap their neighbours (window 4); the
+    solution carried in state_x is compared too."""
     import torch
     from test_regression_amd import mesa
-    w = inputs.WORKLOADS["decode_f32_d128_N256_prefix4096"]
+    w = decode_ws["w"]
     steps = 4
     say("case warm decode", w.name, "mode", mode, "steps", steps)
-    H0, G0, st, lam = _decode_case(w, steps, S=16, prefix=w.T)
+    st = inputs.decode_steps(w, steps)
     st["q"] = inputs.decode_queries_windowed(w, steps, 4)
-    SH, SG = to_dev(H0, "f32"), to_dev(G0, "f32")
+    SH, SG = decode_ws["SH"].clone(), decode_ws["SG"].clone()
+    RH, RG = SH.cpu().numpy().astype(np.float64), SG.cpu().numpy().astype(np.float64)
     SX = torch.zeros((w.B, w.H, w.d), dtype=torch.float32, device="cuda")
-    lam_d = to_dev(lam, "f32")
-    RH, RG = H0.astype(np.float64), G0.astype(np.float64)
+    lam, lam_d = decode_ws["lam"], decode_ws["lam_d"]
     RX = np.zeros((w.B, w.H, w.d))
     for s in range(steps):
         q, k, v, g = (to_dev(st[n][s], "f32") for n in ("q", "k", "v", "gamma"))
@@ -191,6 +259,47 @@ def test_warm_decode_full_launch_shape(mode):
         say(f"warm decode step {s}: rel_l2={e:.3e} x rel_l2={ex:.3e} iters mean={r['iters'].mean():.2f} "
             f"decidable={nd} undecidable={nu} mismatched={nm}")
         assert e <= RTOL["f32"] and ex <= RTOL["f32"]
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_decode_bf16_inputs(d):
+    """mesa_decode_step and mesa_decode_step_warm with bf16 q, k, v (fp32
+    states): against the oracle run on the bf16-rounded inputs."""
+    import torch
+    from test_regression_amd import mesa
+    N, H, P, cap, tol = 5, 3, 48, 30, 1e-4
+    say("case decode bf16", d)
+    x = small_inputs(70 + d, N, H, P + 3, d, "bf16")
+    xf = {n: (inputs.as_f64(x[n], "bf16") if n in ("q", "k", "v") else x[n]) for n in x}
+    xf["q"][2, 1, P + 1] = 0.0
+    x["q"][2, 1, P + 1] = 0
+    pre = oracle.forward(xf["k"][:, :, :P], xf["k"][:, :, :P], xf["v"][:, :, :P], x["gamma"][:, :, :P],
+                         x["lam"], 0, 0.0, want=np.zeros((N, H, P), bool), final_state=True)
+    H0 = pre["final_H"].astype(np.float32)
+    G0 = pre["final_G"].astype(np.float32)
+    lam = to_dev(x["lam"], "f32")
+    for mode in (None, 1, 2):
+        SH, SG = to_dev(H0, "f32"), to_dev(G0, "f32")
+        RH, RG = H0.astype(np.float64), G0.astype(np.float64)
+        SX = torch.zeros((N, H, d), dtype=torch.float32, device="cuda")
+        RX = np.zeros((N, H, d))
+        for s in (P, P + 1, P + 2):
+            dev_args = [to_dev(np.ascontiguousarray(x[n][:, :, s]), "bf16") for n in ("q", "k", "v")]
+            g = to_dev(np.ascontiguousarray(x["gamma"][:, :, s]), "f32")
+            ref_args = [np.ascontiguousarray(xf[n][:, :, s]) for n in ("q", "k", "v", "gamma")]
+            if mode is None:
+                out, it = mesa.mesa_decode_step(*dev_args, g, lam, SH, SG, cap, tol)
+                r = oracle.decode_step(*ref_args, x["lam"], RH, RG, cap, tol)
+            else:
+                out, it = mesa.mesa_decode_step_warm(*dev_args, g, lam, SH, SG, SX, cap, tol, mode)
+                r = oracle.decode_step_warm(*ref_args, x["lam"], RH, RG, RX, cap, tol, mode)
+            torch.cuda.synchronize()
+            e = rel_l2(out.cpu().numpy(), r["out"])
+            assert e <= 1e-4, (mode, s, e)
+            compare_counts(it.cpu().numpy(), r, cap, tol)
+            if s == P + 1:
+                assert int(it[2, 1]) == 0 and not out[2, 1].any()
+        assert rel_l2(SH.cpu().numpy(), RH) < 1e-5 and rel_l2(SG.cpu().numpy(), RG) < 1e-5
 
 
 @pytest.mark.parametrize("d", [16, 32, 64])
