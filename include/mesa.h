@@ -141,6 +141,29 @@ mesa_status mesa_forward_train(const void *q, const void *k, const void *v, int 
                                int max_iters, float tol, float *out, int32_t *iters, float *x_out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the device array that mesa_forward_noalloc keeps its chunk
+ * states in (64 MiB on every GPU the library runs on). */
+#define MESA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * mesa_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments without the workspace.  The chunk
+ * states live in a device array of MESA_NOALLOC_SCRATCH_BYTES built into
+ * the library; sizes whose mesa_forward_workspace_bytes(...) exceeds it
+ * return MESA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The
+ * call allocates nothing and records no profiling events.  Every call on a
+ * GPU shares that GPU's array (the chunk-state kernel rewrites all of it
+ * that a call reads, including the claim counter), so calls that overlap on
+ * one GPU -- on different streams or host threads -- race; serialise them.
+ */
+mesa_status mesa_forward_noalloc(const void *q, const void *k, const void *v, int qkv_dtype,
+                                 const float *gamma, const float *lambda,
+                                 int B, int H, int T, int dk, int dv, int chunk,
+                                 int max_iters, float tol,
+                                 float *out, int32_t *iters, float *final_H, float *final_G,
+                                 void *stream);
+
 /*
  * Bytes of device workspace mesa_backward needs: the forward chunk states
  * (as mesa_forward_workspace_bytes counts them, without its tail), two

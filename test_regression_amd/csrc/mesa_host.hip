@@ -50,13 +50,14 @@ std::vector<ProfRec> g_prof_pending;
 double g_prof_ms[MESA_KERNEL_COUNT] = {};
 int64_t g_prof_n[MESA_KERNEL_COUNT] = {};
 
-// Launches `fn` on `s`; when profiling is on, brackets it with two events.
+// Launches `fn` on `s`; when profiling is on (and `may_record`), brackets it
+// with two events.
 template <typename Fn>
-hipError_t timed_launch(int kid, hipStream_t s, Fn fn) {
+hipError_t timed_launch(int kid, hipStream_t s, Fn fn, bool may_record = true) {
     bool on;
     {
         std::lock_guard<std::mutex> g(g_prof_mu);
-        on = g_prof_on;
+        on = g_prof_on && may_record;
     }
     if (!on) return fn();
     ProfRec r{nullptr, nullptr, kid};
@@ -131,7 +132,7 @@ static mesa_status forward_impl(const void* q, const void* k, const void* v, int
                                 const float* gamma, const float* lambda, int B, int H, int T, int dk,
                                 int dv, int chunk, int max_iters, float tol, float* out, int32_t* iters,
                                 float* final_H, float* final_G, float* x_out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                size_t workspace_bytes, void* stream, bool may_record = true) {
     if (qkv_dtype != MESA_DTYPE_F32 && qkv_dtype != MESA_DTYPE_BF16)
         return fail(MESA_ERR_INVALID_ARGUMENT, "qkv_dtype %d is not MESA_DTYPE_F32 or MESA_DTYPE_BF16", qkv_dtype);
     if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0)
@@ -181,7 +182,8 @@ static mesa_status forward_impl(const void* q, const void* k, const void* v, int
     if (need_ws || final_H || final_G) {
         mesa::ChunkStatesArgs a{k, v, gamma, BH, T, dk, chunk, (int)n_chunks, bf16,
                                 SH, SG, final_H, final_G, need_ws ? 1 : 0, work_counter, 0};
-        hipError_t e = timed_launch(MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); });
+        hipError_t e = timed_launch(
+            MESA_KERNEL_CHUNK_STATES, s, [&] { return mesa::launch_chunk_states(a, s); }, may_record);
         if (e != hipSuccess) return hip_fail(e, "chunk-state kernel launch");
     }
     if (!need_ws) {
@@ -194,7 +196,8 @@ static mesa_status forward_impl(const void* q, const void* k, const void* v, int
     }
     mesa::CgOutputArgs a{q, k, v, gamma, lambda, SH, SG, BH, H, T, dk, chunk, (int)n_chunks,
                          bf16, max_iters, tol, out, iters, x_out, work_counter};
-    hipError_t e = timed_launch(MESA_KERNEL_CG_OUTPUT, s, [&] { return mesa::launch_cg_output(a, s); });
+    hipError_t e =
+        timed_launch(MESA_KERNEL_CG_OUTPUT, s, [&] { return mesa::launch_cg_output(a, s); }, may_record);
     if (e != hipSuccess) return hip_fail(e, "CG/output kernel launch");
     return MESA_OK;
 }
@@ -217,6 +220,65 @@ mesa_status mesa_forward_train(const void* q, const void* k, const void* v, int 
     if (T > 0 && !x_out) return fail(MESA_ERR_INVALID_ARGUMENT, "x_out must be non-null");
     return forward_impl(q, k, v, qkv_dtype, gamma, lambda, B, H, T, dk, dv, chunk, max_iters, tol, out, iters,
                         nullptr, nullptr, x_out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the forward without a caller workspace ----
+// The chunk states and the claim counter live in this file-scope device
+// array instead.  Each GPU the library runs on holds its own copy until the
+// process ends; in host code the name only stands for the array, so the
+// library reads each device's address once (with that device current) and
+// passes that address to the kernels.
+static __device__ __align__(256) unsigned char scratch[MESA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+mesa_status scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(MESA_ERR_UNSUPPORTED, "device %d beyond the %d this build tracks", dev, kScratchDevices);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+        if (!p) return fail(MESA_ERR_HIP, "hipGetSymbolAddress gave a null scratch address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MESA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mesa_status mesa_forward_noalloc(const void* q, const void* k, const void* v, int qkv_dtype,
+                                 const float* gamma, const float* lambda, int B, int H, int T, int dk,
+                                 int dv, int chunk, int max_iters, float tol, float* out, int32_t* iters,
+                                 float* final_H, float* final_G, void* stream) {
+    g_err.clear();
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (max_iters > 0 && T > 0) {
+        ws_bytes = mesa_forward_workspace_bytes(B, H, T, dk, dv, chunk);
+        if (ws_bytes > MESA_NOALLOC_SCRATCH_BYTES)
+            return fail(MESA_ERR_WORKSPACE_TOO_SMALL,
+                        "these sizes need %zu bytes of chunk states; the built-in scratch holds %zu "
+                        "(use mesa_forward with a caller workspace)",
+                        ws_bytes, (size_t)MESA_NOALLOC_SCRATCH_BYTES);
+        if (ws_bytes > 0) {
+            const mesa_status st = scratch_of_current_device(&ws);
+            if (st != MESA_OK) return st;
+        }
+    }
+    return forward_impl(q, k, v, qkv_dtype, gamma, lambda, B, H, T, dk, dv, chunk, max_iters, tol, out, iters,
+                        final_H, final_G, nullptr, ws, ws_bytes, stream, /*may_record=*/false);
 }
 
 // Backward workspace: forward chunk states, reverse states, per-token totals,

@@ -30,6 +30,8 @@ SIGNATURES = {
                       _P, _P, _P, _P, _P, _Z, _P], _I),
     "mesa_forward_train": ([_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                             _P, _P, _P, _P, _Z, _P], _I),
+    "mesa_forward_noalloc": ([_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                              _P, _P, _P, _P, _P], _I),
     "mesa_backward_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
     "mesa_backward": ([_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                        _P, _P, _P, _P, _P, _P, _P, _Z, _P], _I),
@@ -203,6 +205,28 @@ def mesa_forward(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out=None,
                             _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                             _stream(stream))
     _check(st, "mesa_forward")
+    return out, iters, final_H, final_G
+
+
+def mesa_forward_noalloc(q, k, v, gamma, lam, max_iters, tol=0.0, chunk=64, *, out, iters=None, final_H=None,
+                         final_G=None, stream=None):
+    """mesa_forward with the chunk states in the library's built-in device
+    array (see include/mesa.h, mesa_forward_noalloc): the caller passes every
+    output, and the call allocates nothing.  Returns (out, iters, final_H,
+    final_G) as given."""
+    B, H, T, dk, dv = _forward_checks(q, k, v, gamma, lam, out=out, iters=iters, final_H=final_H,
+                                      final_G=final_G)
+    import torch
+    dev = q.device
+    _need(out, "out", torch.float32, dev)
+    for t, n, dt in ((iters, "iters", torch.int32), (final_H, "final_H", torch.float32),
+                     (final_G, "final_G", torch.float32)):
+        if t is not None:
+            _need(t, n, dt, dev)
+    st = lib().mesa_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(gamma), _ptr(lam),
+                                    B, H, T, dk, dv, int(chunk), int(max_iters), float(tol),
+                                    _ptr(out), _ptr(iters), _ptr(final_H), _ptr(final_G), _stream(stream))
+    _check(st, "mesa_forward_noalloc")
     return out, iters, final_H, final_G
 
 
