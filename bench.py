@@ -31,10 +31,11 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_BF16_MFMA_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cg_split_layer_bf16_d128_T4096_traffic.json")
-MFMA_FILE = os.path.join(ROOT, "profiles", "cg_split_layer_bf16_d128_T4096_mfma.json")
-KERNEL_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_core.h",
-                  "test_regression_amd/csrc/persistent.h",
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cg_h2_layer_bf16_d128_T4096_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "cg_h2_layer_bf16_d128_T4096_mfma.json")
+KERNEL_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_output_bf16.hip",
+                  "test_regression_amd/csrc/cg_output_kernels.h", "test_regression_amd/csrc/cg_h2.h",
+                  "test_regression_amd/csrc/cg_core.h", "test_regression_amd/csrc/persistent.h",
                   "test_regression_amd/csrc/mesa_device.h", "test_regression_amd/csrc/cg_split.h"]
 
 
@@ -52,24 +53,32 @@ def flops_per_token_head(d, C, k):
     return states, cg, output
 
 
-def split_cg_mfma_flops(d, C, k, n_chunks):
-    """MFMA flops one launch of the bf16 forward CG kernel issues at a fixed
-    iteration count k, from its structure: per 32-feature step q and row
-    block, nine 16x16x32 bf16 products for the state term (three split
-    planes times three split parts), three for each causal key block of the
-    scores and each 32-key step of the apply (wave w covers w + 1 key blocks
-    from the chunk start); the output adds the scores and apply of the
-    solution (bf16) and the G_c term on 16x16x4 fp32 MFMAs.
-    Returns (bf16 flops, fp32 flops)."""
+def h2_cg_mfma_flops(d, C, key_planes, wave_iters):
+    """MFMA flops one launch of the forward CG kernel (d >= 32) issues, from
+    its structure.  Wave w of a chunk owns tokens 16w..16w+15 and runs as many
+    matvecs as the largest iteration count among them (`wave_iters`: a
+    [n_chunks, C/16] integer array; k everywhere for a fixed count).  A matvec
+    of wave w issues 16x16x32 fp16 MFMAs: three per 32-feature step and
+    16-row block for the state term (hi.hi, hi.lo, lo.hi of the two-part
+    splits), and (1 + key planes) per causal key block and feature step for
+    the scores and per row block and 32-key step for the apply (keys stored
+    as bf16 are one exact fp16 plane, fp32 keys two).  Per chunk the output
+    adds the scores and apply of the solution (fp16) and the G_c term on
+    16x16x4 fp32 MFMAs.  Returns (fp16 flops, fp32 flops)."""
+    import numpy as np
     NT, NQ, NW = d // 16, d // 32, C // 16
-    per_iter, out_bf16 = 0, 0
+    np_ = 1 + key_planes
+    per_iter = np.zeros(NW, np.int64)
+    out16 = 0
     for w in range(NW):
         nbo, ns = w + 1, (w + 2) // 2
-        per_iter += 9 * NT * NQ + 3 * NQ * nbo + 3 * NT * ns
-        out_bf16 += 3 * NQ * nbo + 3 * NT * ns
-    bf16 = 2 * 16 * 16 * 32 * (k * per_iter + out_bf16) * n_chunks
+        per_iter[w] = 3 * NT * NQ + np_ * NQ * nbo + np_ * NT * ns
+        out16 += np_ * NQ * nbo + np_ * NT * ns
+    wave_iters = np.asarray(wave_iters, np.int64)
+    n_chunks = wave_iters.shape[0]
+    f16 = 2 * 16 * 16 * 32 * (int((wave_iters * per_iter[None, :]).sum()) + n_chunks * out16)
     fp32 = 2 * 16 * 16 * 4 * (NW * NT * NT * 4) * n_chunks
-    return bf16, fp32
+    return f16, fp32
 
 
 def split_adjoint_mfma_flops(d, C, k, n_chunks):
@@ -88,34 +97,6 @@ def split_adjoint_mfma_flops(d, C, k, n_chunks):
     bf16 = 2 * 16 * 16 * 32 * ((k + 1) * per_iter + rhs_bf16) * n_chunks
     fp32 = 2 * 16 * 16 * 4 * rhs_fp32 * n_chunks
     return bf16, fp32
-
-
-def fp32_cg_mfma_flops(d, C, wave_iters):
-    """MFMA flops one launch of the fp32-key forward CG kernel issues, from
-    its structure (16x16x4 fp32 MFMAs, 2048 flops each).  Wave w of a chunk
-    owns tokens 16w..16w+15 and iterates until all of them have stopped, so
-    it runs max(n_t) iterations over its tokens (`wave_iters`: a
-    [n_chunks, C/16] integer array of those maxima).  Per iteration wave w
-    does the state term (d/16 row blocks x d/4 steps), and the scores and
-    apply over its causal key blocks within its half-chunk sub-state (the
-    second half of the chunk starts from the mid-chunk state); per chunk
-    every wave adds the output (the G_c term from memory, the scores and
-    apply over all causal key blocks from the chunk start), and the
-    mid-chunk state is formed once (upper 16x16 blocks, C/2 keys).
-    Returns the flops."""
-    import numpy as np
-    NT, NW = d // 16, C // 16
-    per_iter = np.zeros(NW, np.int64)
-    out = 0
-    for w in range(NW):
-        kb0 = NW // 2 if (NW >= 2 and w >= NW // 2) else 0
-        nb, nbo = w - kb0 + 1, w + 1
-        per_iter[w] = NT * (d // 4) + nb * (d // 4) + NT * 4 * nb
-        out += NT * NT * 4 + nbo * (d // 4) + NT * 4 * nbo
-    n_chunks = wave_iters.shape[0]
-    mid = (NT * (NT + 1) // 2) * (C // 2 // 4) if NW >= 2 else 0
-    mfmas = int((wave_iters.astype(np.int64) * per_iter[None, :]).sum()) + n_chunks * (out + mid)
-    return 2 * 16 * 16 * 4 * mfmas
 
 
 def mixed_roofline(bf16_flops, fp32_flops, ms, alg_flops, bf16_peak, fp32_peak):
@@ -220,36 +201,38 @@ def headline(torch, mesa, inputs, args, dev, peaks):
     k1_bytes = n_tok * (2 * w.d * 2 + 4) + w.B * w.H * (w.T // w.chunk) * (w.d * (w.d + 16) // 2 + w.d * w.d) * 4
     achieved = k2_flops / (k2_ms * 1e-3) / 1e12
     traffic = measured_traffic()
-    # The CG kernel's contractions run on bf16 MFMAs over exact bf16 splits
-    # (the keys are bf16): its roofline is the issued MFMA work at the bf16
-    # and fp32 MFMA peaks, not the algorithmic flops at one of them.
-    bf, fp = split_cg_mfma_flops(w.d, w.chunk, w.max_iters, w.B * w.H * (w.T // w.chunk))
+    # The CG kernel's products run on fp16 MFMAs over two-part splits: its
+    # roofline is the algorithmic flops at the fp16 (= bf16) MFMA peak; the
+    # issued work (three products per state product) is reported beside it.
+    import numpy as np
+    n_chunks = w.B * w.H * (w.T // w.chunk)
+    bf, fp = h2_cg_mfma_flops(w.d, w.chunk, 1, np.full((n_chunks, w.chunk // 16), w.max_iters))
     rl = mixed_roofline(bf, fp, k2_ms, k2_flops, PEAK_BF16_MFMA_TFLOPS, PEAK_FP32_MFMA_TFLOPS)
     rlm = mixed_roofline(bf, fp, k2_ms, k2_flops, peaks["mfma_bf16_tflops"], peaks["mfma_f32_tflops"])
     res = dict(
         w=w, x=x, n_tok=n_tok, ms_step=ms_step, value=n_tok * args.steps / el,
         tflops=(fs + fcg + fo) * n_tok / (ms_step * 1e-3) / 1e12,
-        # The kernel's contractions issue on bf16 MFMAs, so its roofline is
-        # the method's algorithmic flops against the bf16 MFMA peak; the
-        # exact split products multiply the issued work, which is reported
-        # as a secondary fraction against the issued work's own bound.
+        # The kernel's contractions issue on fp16 MFMAs (2500 TFLOP/s, the
+        # bf16 figure), so its roofline is the method's algorithmic flops
+        # against that peak; the split products multiply the issued work,
+        # which is reported as a secondary fraction against its own bound.
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
                       frac=round(achieved / PEAK_BF16_MFMA_TFLOPS, 4), traffic=traffic,
-                      kernel="cg_split_kernel<128,64>",
+                      kernel="cg_h2_kernel<128,64,bf16> (fp16 MFMA on two-part splits)",
                       basis="algorithmic flops of the CG iterations and the output contraction "
-                            f"({fcg + fo} per token-head) per launch / average launch time / the bf16 "
-                            "MFMA peak the kernel's products issue at",
+                            f"({fcg + fo} per token-head) per launch / average launch time / the fp16 "
+                            "(= bf16) MFMA peak the kernel's products issue at",
                       algorithmic_flops_per_launch=k2_flops, avg_launch_ms=round(k2_ms, 4),
                       frac_measured_peak=round(achieved / peaks["mfma_bf16_tflops"], 4),
                       algorithmic_over_fp32_peak=round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
                       mfma_busy_frac=measured_mfma_busy(),
                       issued=dict(achieved=rl["achieved"], peak=rl["peak"], frac=rl["frac"],
-                                  flops_per_launch=rl["issued_flops_per_launch"], bf16_flops=bf, fp32_flops=fp,
-                                  basis="issued MFMA work (exact split products) over its shortest time at "
-                                        "the bf16 and fp32 MFMA peaks",
+                                  flops_per_launch=rl["issued_flops_per_launch"], fp16_flops=bf, fp32_flops=fp,
+                                  basis="issued MFMA work (split products) over its shortest time at the "
+                                        "fp16 and fp32 MFMA peaks",
                                   peak_measured=rlm["peak"], frac_measured=rlm["frac"])),
         kernels={
-            "cg_split_kernel": dict(avg_ms=round(k2_ms, 4), launches=k2[1],
+            "cg_h2_kernel": dict(avg_ms=round(k2_ms, 4), launches=k2[1],
                                     algorithmic_tflops=round(achieved, 2)),
             "chunk_states_kernel": dict(avg_ms=round(k1_ms, 4), launches=k1[1],
                                         gbs=round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
@@ -354,7 +337,9 @@ def dynamic(torch, mesa, inputs, dev):
     k2_ms = k2[0] / max(k2[1], 1)
     k1_ms = k1[0] / max(k1[1], 1)
     wave_iters = iters.view(-1, w.chunk // 16, 16).amax(dim=-1).cpu().numpy()
-    issued = fp32_cg_mfma_flops(w.d, w.chunk, wave_iters)
+    f16, f32 = h2_cg_mfma_flops(w.d, w.chunk, 2, wave_iters)
+    issued = f16 + f32
+    t_min = f16 / (PEAK_BF16_MFMA_TFLOPS * 1e12) + f32 / (PEAK_FP32_MFMA_TFLOPS * 1e12)
     hist = torch.bincount(iters.flatten().to(torch.int64), minlength=w.max_iters + 1).cpu().tolist()
     ach = k2_useful / (k2_ms * 1e-3) / 1e12
     del t
@@ -362,17 +347,19 @@ def dynamic(torch, mesa, inputs, dev):
             "iters_mean": round(mean_it, 3), "iters_min": int(iters.min()), "iters_max": int(iters.max()),
             "iters_histogram": {str(i): c for i, c in enumerate(hist) if c},
             "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
-            "kernels": {"cg_output_kernel": {"avg_ms": round(k2_ms, 4), "launches": k2[1]},
+            "kernels": {"cg_h2_kernel": {"avg_ms": round(k2_ms, 4), "launches": k2[1]},
                         "chunk_states_kernel": {"avg_ms": round(k1_ms, 4), "launches": k1[1]}},
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4),
-                         "kernel": "cg_output_kernel<128,64,float> (fp32 MFMA)",
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_MFMA_TFLOPS, 4),
+                         "kernel": "cg_h2_kernel<128,64,float> (fp16 MFMA on two-part splits of the fp32 "
+                                   "keys, state and vectors)",
                          "basis": "useful flops (each token's own iteration count) per launch / average "
-                                  "launch time / the fp32 MFMA peak",
-                         "useful_flops_per_launch": k2_useful, "issued_flops_per_launch": issued,
+                                  "launch time / the fp16 MFMA peak",
+                         "useful_flops_per_launch": k2_useful,
+                         "useful_over_fp32_peak": round(ach / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "issued_flops_per_launch": issued, "issued_fp16_flops": f16, "issued_fp32_flops": f32,
                          "issued_over_useful": round(issued / k2_useful, 4),
-                         "issued_tflops": round(issued / (k2_ms * 1e-3) / 1e12, 2),
-                         "issued_frac": round(issued / (k2_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "issued_frac": round(t_min / (k2_ms * 1e-3), 4),
                          "avg_launch_ms": round(k2_ms, 4)}}
 
 
@@ -712,8 +699,8 @@ def main():
         "value": round(h["value"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(h["ms_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "arithmetic": "fp32: exact float product terms (three-part bf16 splits on bf16 MFMAs for the bf16 "
-                      "keys), fp32 accumulation",
+        "arithmetic": "fp32 vectors and accumulation; matvec products on fp16 MFMAs over two-part splits "
+                      "(hi + lo to 22 bits, three products hi.hi + hi.lo + lo.hi; bf16 keys exact in one part)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d, "d_v": w.d,
                    "chunk": w.chunk, "qkv_storage": w.dtype, "cg_iters": w.max_iters, "tol": w.tol,
                    "seed": w.seed},

@@ -1,0 +1,487 @@
+// cg_h2.h -- the forward CG kernel's chunk machinery with every matvec
+// product on fp16 MFMAs over two-part splits (gfx950).
+//
+// MesaNet summary page (gist.science, paper 2506.05233), section "A Camada
+// Mesa", bullet "Paralelizacao": the CG over all time steps is a gated-
+// linear-attention pass run chunk-parallel on the states.  For chunk c
+// (tokens t0..t0+C-1, l_t the within-chunk prefix sum of ln gamma,
+// S = S^H_c = H_{t0-1}):
+//   H_t p = e^{l_t} S p + sum_{i=t0..t} e^{l_t - l_i} (k_i . p) k_i
+//
+// Two-part fp16 splits.  A float x is first scaled by a power of two 2^E
+// (exact), chosen so that the largest magnitude of the group it belongs to
+// lands in [2^14, 2^15); then hi = fp16(x 2^E) and lo = fp16(x 2^E - hi),
+// both rounded to nearest.  x 2^E - hi is exact in float and |lo - (x 2^E -
+// hi)| <= 2^-11 |x 2^E - hi| <= 2^-22 |x 2^E|, so hi + lo is x 2^E to 22
+// bits.  A product a b is then taken as hi_a hi_b + hi_a lo_b + lo_a hi_b
+// (three fp16 MFMAs; the dropped lo_a lo_b is below 2^-22 |a b|), so every
+// product term carries at most about 3 2^-22 relative error and the sums run
+// in fp32.  Magnitudes far below a group's largest fall into fp16's
+// subnormal range and keep an absolute error near 2^-25 2^-E: below 2^-39 of
+// the group's largest element.  Keys stored as bf16 (8 significant bits) are
+// exact in one fp16 part after scaling, so their products take two MFMAs.
+//
+// Groups and their scales: the chunk state S (one exponent per chunk, from
+// max |S_ij|, which for a positive semidefinite S is its largest diagonal
+// entry), the chunk's keys and its values (one exponent each per chunk), a
+// token's CG direction p and its decayed scores (one exponent per token and
+// matvec).  The products' exponents are undone when the fp32 accumulators
+// are combined.
+//
+// LDS layout as in the bf16-split kernel (cg_split.h): rows of the state
+// planes and key tiles store each 32-column block permuted (perm32) so that
+// a lane's 8-slot MFMA operand (the 4-element pieces 4kk..4kk+3 of two
+// 16-column blocks, which is what the CG vectors hold in registers) is one
+// 128-bit read; row pitches are 8 words more than the row.
+#pragma once
+#include "cg_split.h"
+
+namespace mesa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_f16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Exponent E with amax 2^E in [2^14, 2^15) (amax > 0), clamped so that 2^E
+// and 2^-E are normal floats; 15 for amax = 0.
+__device__ __forceinline__ int h2_exp(float amax) {
+    const int e = __builtin_amdgcn_frexp_expf(amax);   // amax = f 2^e, f in [0.5, 1)
+    return min(max(15 - e, -126), 126);
+}
+__device__ __forceinline__ float pow2(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
+
+// Largest magnitude over the four k-slot lanes n, n+16, n+32, n+48 (the
+// lanes of one token); every lane gets the same value.
+__device__ __forceinline__ float kslot_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Largest magnitude over all 64 lanes.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float absmax(const f32x4 (&A)[N]) {
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(A[j][r]));
+    return m;
+}
+
+// The two fp16 parts of two 4-element float pieces scaled by s (a power of two).
+__device__ __forceinline__ void h2_split(const f32x4& a, const f32x4& b, float s, f16x8& H, f16x8& L) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float y = (e < 4 ? a[e] : b[e - 4]) * s;
+        const _Float16 h = (_Float16)y;
+        H[e] = h;
+        L[e] = (_Float16)(y - (float)h);
+    }
+}
+
+__device__ __forceinline__ f16x8 lds_f16x8(const uint32_t* p) {
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Key planes: one (keys stored as bf16, exact in fp16 once scaled) or two.
+template <typename In>
+__host__ __device__ constexpr int h2_key_planes() { return sizeof(In) == 2 ? 1 : 2; }
+
+template <int D, int C, int NKP>
+struct alignas(16) H2Lds {
+    static constexpr int SW = D / 2 + 8;                    // words per state / key row
+    static constexpr int KW = (C >= 32 ? C : 32) / 2 + 8;   // words per K^T row (at least one 32-key step)
+    uint32_t S[2][D * SW];     // S^H_c 2^ES: fp16 planes hi, lo; row r = feature r, columns perm32
+    uint32_t KR[NKP][C * SW];  // K_c rows 2^EK (fp16 parts, columns perm32)
+    uint32_t KT[NKP][D * KW];  // K_c^T 2^EK, later V_c^T 2^EV (fp16 parts, tokens perm32)
+    float L[C];                // l_i
+    float Lam[D];
+    float red[3][4];           // per-wave maxima: chunk state, keys, values
+    int next;                  // the claimed next chunk
+};
+
+// Per-wave constants of wave W.
+template <int D, int C, int W>
+struct H2Wave {
+    static constexpr int NBO = W + 1;          // causal key blocks from the chunk start
+    static constexpr int NS = (NBO + 1) / 2;   // 32-key steps of the intra-chunk apply
+    int n, kk, tr;
+    float eLo;                 // e^{l_t}
+    float dec[2 * NS][4];      // e^{l_t - l_i}, key i = 16 ib + 4kk + r <= t, else 0
+    __device__ __forceinline__ H2Wave(const float* Lv, int lane) {
+        n = lane & 15;
+        kk = lane >> 4;
+        tr = 16 * W + n;
+        eLo = __expf(Lv[tr]);
+#pragma unroll
+        for (int ib = 0; ib < 2 * NS; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ib + 4 * kk + r;
+                dec[ib][r] = (i <= tr) ? __expf(Lv[tr] - Lv[i < C ? i : C - 1]) : 0.f;
+            }
+    }
+};
+
+// The A operand of K^T (or V^T) row block j, 32-key step s, plane pl; the
+// second 16 keys are zero when the chunk has no such block (C = 16).
+template <int D, int C, int NKP>
+__device__ __forceinline__ f16x8 h2_kt_operand(const H2Lds<D, C, NKP>& L, int pl, int j, int s, int m, int kk) {
+    constexpr int KW = H2Lds<D, C, NKP>::KW;
+    if constexpr (C >= 32) {
+        return lds_f16x8(&L.KT[pl][(16 * j + m) * KW + 16 * s + 4 * kk]);
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(&L.KT[pl][(16 * j + m) * KW + 4 * kk]);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        return __builtin_bit_cast(f16x8, u32x4{v.x, v.y, 0u, 0u});
+    }
+}
+
+// Accumulators per key block for the scores: one when several key blocks
+// interleave (consecutive MFMAs then never share one), else one per product
+// part, summed by h2_score.
+template <int NB, int NKP>
+__host__ __device__ constexpr int h2_score_parts() { return NB == 1 ? 1 + NKP : 1; }
+
+// Scores of the wave's tokens with key block ib (ib < NB), Sc = K Z^T
+// 2^(EK + EZ), from the split of Z per 32-feature step.
+template <int D, int C, int NKP, int NB>
+__device__ __forceinline__ void h2_scores_step(const H2Lds<D, C, NKP>& L, int q, const f16x8& Zh, const f16x8& Zl,
+                                               int m, int kk, f32x4 (&Sc)[NB][h2_score_parts<NB, NKP>()]) {
+    constexpr int SW = H2Lds<D, C, NKP>::SW;
+    constexpr int NP = h2_score_parts<NB, NKP>();
+    f16x8 A[NB][NKP];
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+        for (int pl = 0; pl < NKP; ++pl) A[ib][pl] = lds_f16x8(&L.KR[pl][(16 * ib + m) * SW + 16 * q + 4 * kk]);
+    // smallest terms first
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) Sc[ib][0] = mfma_f16x32(A[ib][0], Zl, Sc[ib][0]);
+    if constexpr (NKP == 2) {
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib) Sc[ib][NP - 1] = mfma_f16x32(A[ib][1], Zh, Sc[ib][NP - 1]);
+    }
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) Sc[ib][NP > 1 ? 1 : 0] = mfma_f16x32(A[ib][0], Zh, Sc[ib][NP > 1 ? 1 : 0]);
+}
+
+// Element r of key block ib's scores.
+template <int NB, int NKP>
+__device__ __forceinline__ float h2_score(const f32x4 (&Sc)[NB][h2_score_parts<NB, NKP>()], int ib, int r) {
+    constexpr int NP = h2_score_parts<NB, NKP>();
+    if constexpr (NP == 1) return Sc[ib][0][r];
+    else if constexpr (NP == 2) return Sc[ib][0][r] + Sc[ib][1][r];
+    else return (Sc[ib][0][r] + Sc[ib][2][r]) + Sc[ib][1][r];
+}
+
+// Y[j] += K^T / V^T row block j times the decayed scores W over NS 32-key
+// steps; W is split here with the per-token exponent EW (W 2^EW):
+// Y = T W 2^(ET + EW).
+template <int D, int C, int NKP, int NS>
+__device__ __forceinline__ void h2_apply(const H2Lds<D, C, NKP>& L, const f32x4 (&W)[2 * NS], float sW, int m,
+                                         int kk, f32x4 (&Y)[D / 16]) {
+    constexpr int NT = D / 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        f16x8 Wh, Wl;
+        h2_split(W[2 * s], W[2 * s + 1], sW, Wh, Wl);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const f16x8 A0 = h2_kt_operand<D, C, NKP>(L, 0, j, s, m, kk);
+            Y[j] = mfma_f16x32(A0, Wl, Y[j]);
+            if constexpr (NKP == 2) Y[j] = mfma_f16x32(h2_kt_operand<D, C, NKP>(L, 1, j, s, m, kk), Wh, Y[j]);
+            Y[j] = mfma_f16x32(A0, Wh, Y[j]);
+        }
+    }
+}
+
+// The CG of wave W on (H_t + Lambda) x = b for its 16 tokens, from x = 0,
+// with every matvec on the split products above.  R holds b on entry (B
+// layout), X receives the solution; the stop rules are cg_solve's
+// (cg_core.h), and so is the arithmetic of x, r and p element for element.
+//
+// The loop is pipelined so that its vector work runs under the MFMAs:
+//  - an iteration forms the new direction p = r + beta p (after the
+//    deferred x += alpha p of the previous iteration) one 32-feature step at
+//    a time, splits that step and issues its scores and state products
+//    before forming the next;
+//  - p's exponent therefore cannot wait for max |p|: it comes from the bound
+//    b' = |r|_2 + beta b (b = |q|_2 at the start), which bounds |p|_2 and so
+//    every element of the new p (up to one rounding): the split never
+//    overflows, and while the residuals shrink b' stays within a small
+//    factor of |p|_2, which spends a few of fp16's bits of headroom;
+//  - the state planes of the next four row blocks are read while the current
+//    ones' products run;
+//  - the apply runs row block by row block, and each block's combination
+//    e^{l_t} S p + intra + lambda p and its share of p.Ap follow its MFMAs.
+// The intra-chunk terms run over the causal keys from the chunk start.
+template <int D, int C, int NKP, int W>
+__device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wave<D, C, W>& wv, int ES, int EK,
+                                           f32x4 (&R)[D / 16], f32x4 (&X)[D / 16], const f32x4 (&lam)[D / 16],
+                                           int max_iters, float tol) {
+    using Wv = H2Wave<D, C, W>;
+    constexpr int NT = D / 16;
+    constexpr int NQ = D / 32;
+    constexpr int NB = Wv::NBO;
+    constexpr int NS = Wv::NS;
+    constexpr int SW = H2Lds<D, C, NKP>::SW;
+    constexpr int JI = NT >= 4 ? 4 : NT;   // row blocks per group of state products
+    constexpr int NG = NT / JI;            // groups per 32-feature step
+    const int n = wv.n, kk = wv.kk;
+    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    f32x4 P[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        P[j] = R[j];
+        X[j] = zero;
+    }
+    float rr = token_dot<NT>(R, R);
+    const float tq = tol * sqrtf(rr);
+    const float stop_rr = tq * tq;
+    bool done = !(rr > 0.f);   // b == 0 (or a padded token): x = 0, 0 iterations
+    int it = 0;
+    float alpha = 0.f, beta = 0.f;   // of the previous iteration
+    float pbound = sqrtf(rr);        // bounds |p|_2, hence max |p|, of the next direction
+
+    auto load_group = [&](int f, f16x8 (&A)[JI][2]) {
+        const int q = f / NG, g = f % NG;
+#pragma unroll
+        for (int h = 0; h < JI; ++h) {
+            const int off = (16 * (g * JI + h) + n) * SW + 16 * q + 4 * kk;
+            A[h][0] = lds_f16x8(&L.S[0][off]);
+            A[h][1] = lds_f16x8(&L.S[1][off]);
+        }
+    };
+
+    for (int itn = 0; itn < max_iters; ++itn) {
+        if (!done && (rr < stop_rr || rr == 0.f)) done = true;
+        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        const int EP = h2_exp(pbound);
+        const float sP = pow2(EP);
+        constexpr int NP = h2_score_parts<NB, NKP>();
+        f32x4 Sc[NB][NP], YS[NT];
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+            for (int t = 0; t < NP; ++t) Sc[ib][t] = zero;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) YS[j] = zero;
+        f16x8 SA[2][JI][2];
+        load_group(0, SA[0]);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            // the direction's features 32q .. 32q + 31, after the deferred x update
+#pragma unroll
+            for (int jj = 2 * q; jj < 2 * q + 2; ++jj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    X[jj][r] += alpha * P[jj][r];
+                    P[jj][r] = R[jj][r] + beta * P[jj][r];
+                }
+            f16x8 Zh, Zl;
+            h2_split(P[2 * q], P[2 * q + 1], sP, Zh, Zl);
+            h2_scores_step<D, C, NKP, NB>(L, q, Zh, Zl, n, kk, Sc);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int f = q * NG + g;
+                if (f + 1 < NQ * NG) load_group(f + 1, SA[(f + 1) & 1]);
+                const f16x8(&A)[JI][2] = SA[f & 1];
+                // smallest terms first
+#pragma unroll
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][1], Zh, YS[g * JI + h]);
+#pragma unroll
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Zl, YS[g * JI + h]);
+#pragma unroll
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Zh, YS[g * JI + h]);
+            }
+        }
+        // decayed scores W 2^(EK + EP) and their per-token exponent
+        f32x4 Wt[2 * NS];
+#pragma unroll
+        for (int ib = 0; ib < 2 * NS; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Wt[ib][r] = ib < NB ? h2_score<NB, NKP>(Sc, ib < NB ? ib : 0, r) * wv.dec[ib][r] : 0.f;
+            }
+        const int EW = h2_exp(kslot_max(absmax<2 * NS>(Wt)));
+        const float sW = pow2(EW);
+        f16x8 Wh[NS], Wl[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) h2_split(Wt[2 * s], Wt[2 * s + 1], sW, Wh[s], Wl[s]);
+        const float a = __builtin_amdgcn_ldexpf(wv.eLo, -(ES + EP));
+        const float b = pow2(-(2 * EK + EP + EW));
+        // apply, combination and p.Ap, one row block at a time
+        f32x4 Y[NT];
+        float pp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            f32x4 yi = zero;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const f16x8 A0 = h2_kt_operand<D, C, NKP>(L, 0, j, s, n, kk);
+                yi = mfma_f16x32(A0, Wl[s], yi);
+                if constexpr (NKP == 2) yi = mfma_f16x32(h2_kt_operand<D, C, NKP>(L, 1, j, s, n, kk), Wh[s], yi);
+                yi = mfma_f16x32(A0, Wh[s], yi);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Y[j][r] = a * YS[j][r] + (b * yi[r] + lam[j][r] * P[j][r]);
+                pp[r] += P[j][r] * Y[j][r];
+            }
+        }
+        const float pap = kslot_sum((pp[0] + pp[1]) + (pp[2] + pp[3]));
+        const bool act = !done && (pap > 0.f);
+        if (!done && !act) done = true;   // breakdown guard
+        alpha = act ? rcp_div(rr, pap) : 0.f;
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                R[j][r] -= alpha * Y[j][r];
+                rs[r] += R[j][r] * R[j][r];
+            }
+        const float rrn = kslot_sum((rs[0] + rs[1]) + (rs[2] + rs[3]));
+        // a stopped token gets beta = 0: its direction becomes its frozen residual
+        beta = act ? rcp_div(rrn, rr) : 0.f;
+        pbound = sqrtf(rrn) + beta * pbound;
+        rr = act ? rrn : rr;
+        it += act ? 1 : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X[j][r] += alpha * P[j][r];
+    return it;
+}
+
+// ---- staging ----
+
+// Largest magnitude this thread holds of the packed upper block triangle.
+template <int D, int NTHR>
+__device__ __forceinline__ float packed_absmax(const PackedStateRegs<D, NTHR>& st, int tid) {
+    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < PackedStateRegs<D, NTHR>::N; ++u)
+        if ((tid + u * NTHR) * 4 < PackedStateRegs<D, NTHR>::HPACK)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(st.x[u][r]));
+    return m;
+}
+
+// Largest magnitude this thread holds of a chunk's rows.
+template <int D, int C, int NTHR, typename In>
+__device__ __forceinline__ float rows_absmax(const ChunkRowsRegs<D, C, NTHR, In>& rg) {
+    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < ChunkRowsRegs<D, C, NTHR, In>::EL4; ++u) {
+        const f32x4 v = rg.x[u].get();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(v[r]));
+    }
+    return m;
+}
+
+// The packed upper block triangle of S^H (PackedStateRegs: the thread's
+// group u = 16 bytes of stored block bi, rows 4q..4q+3 of column c in
+// accumulator order) scaled by s, written as the two fp16 planes of the full
+// symmetric matrix.
+template <int D, int NTHR>
+__device__ __forceinline__ void stage_h2_state(uint32_t (&S)[2][D * (D / 2 + 8)], const PackedStateRegs<D, NTHR>& st,
+                                               int tid, float s) {
+    constexpr int NT = D / 16;
+    constexpr int SW = D / 2 + 8;
+    constexpr int HPACK = D * (D + 16) / 2;
+#pragma unroll
+    for (int u = 0; u < PackedStateRegs<D, NTHR>::N; ++u) {
+        const int e = (tid + u * NTHR) * 4;
+        if (e >= HPACK) continue;
+        const int bi = e / 256, l = (e % 256) / 4, q4 = 4 * (l / 16), c = l % 16;
+        int a = 0;
+#pragma unroll
+        for (int aa = 1; aa < NT; ++aa)
+            if (bi >= blk_index<NT>(aa, aa)) a = aa;
+        const int b = a + (bi - blk_index<NT>(a, a));
+        _Float16 h[4], lo[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float y = st.x[u][r] * s;
+            h[r] = (_Float16)y;
+            lo[r] = (_Float16)(y - (float)h[r]);
+        }
+        // S[16a + q4 + r][16b + c]
+        const int col = perm32(16 * b + c);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * a + q4 + r;
+            reinterpret_cast<_Float16*>(S[0])[row * 2 * SW + col] = h[r];
+            reinterpret_cast<_Float16*>(S[1])[row * 2 * SW + col] = lo[r];
+        }
+        // the mirror S[16b + c][16a + q4 + r]: four consecutive permuted columns
+        if (a != b) {
+            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+            const int w0 = (16 * b + c) * SW + perm32(16 * a + q4) / 2;
+            *reinterpret_cast<f16x4*>(&S[0][w0]) = f16x4{h[0], h[1], h[2], h[3]};
+            *reinterpret_cast<f16x4*>(&S[1][w0]) = f16x4{lo[0], lo[1], lo[2], lo[3]};
+        }
+    }
+}
+
+// A chunk's rows scaled by s as NKP fp16 planes of K rows (columns perm32).
+template <int D, int C, int NTHR, int NKP, typename In>
+__device__ __forceinline__ void stage_h2_rows(uint32_t (&KR)[NKP][C * (D / 2 + 8)],
+                                              const ChunkRowsRegs<D, C, NTHR, In>& rg, int tid, float s) {
+    constexpr int SW = D / 2 + 8;
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int u = 0; u < ChunkRowsRegs<D, C, NTHR, In>::EL4; ++u) {
+        int i, f;
+        ChunkRowsRegs<D, C, NTHR, In>::place(u, tid, i, f);
+        const f32x4 v = rg.x[u].get();
+        f16x4 h, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float y = v[r] * s;
+            h[r] = (_Float16)y;
+            lo[r] = (_Float16)(y - (float)h[r]);
+        }
+        *reinterpret_cast<f16x4*>(&KR[0][i * SW + perm32(f) / 2]) = h;
+        if constexpr (NKP == 2) *reinterpret_cast<f16x4*>(&KR[1][i * SW + perm32(f) / 2]) = lo;
+    }
+}
+
+// A chunk's rows scaled by s, transposed (feature rows, tokens perm32), as
+// NKP fp16 planes.
+template <int D, int C, int NTHR, int NKP, typename In>
+__device__ __forceinline__ void stage_h2_transposed(uint32_t (&KT)[NKP][D * ((C >= 32 ? C : 32) / 2 + 8)],
+                                                    const ChunkRowsRegs<D, C, NTHR, In>& rg, int tid, float s) {
+    constexpr int KW = (C >= 32 ? C : 32) / 2 + 8;
+#pragma unroll
+    for (int u = 0; u < ChunkRowsRegs<D, C, NTHR, In>::EL4; ++u) {
+        int i, f;
+        ChunkRowsRegs<D, C, NTHR, In>::place(u, tid, i, f);
+        const f32x4 v = rg.x[u].get();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float y = v[r] * s;
+            const _Float16 h = (_Float16)y;
+            reinterpret_cast<_Float16*>(KT[0])[(f + r) * 2 * KW + perm32(i)] = h;
+            if constexpr (NKP == 2) reinterpret_cast<_Float16*>(KT[1])[(f + r) * 2 * KW + perm32(i)] = (_Float16)(y - (float)h);
+        }
+    }
+}
+
+}  // namespace mesa
+

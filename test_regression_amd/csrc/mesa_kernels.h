@@ -92,6 +92,7 @@ struct HawkArgs {
 hipError_t launch_hawk(const HawkArgs& a, hipStream_t s);
 
 hipError_t launch_cg_output(const CgOutputArgs& a, hipStream_t s);
+hipError_t launch_cg_output_bf16(const CgOutputArgs& a, hipStream_t s);   // bf16 q/k/v, d >= 32
 hipError_t launch_qk_preprocess(const QkPreArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
