@@ -278,11 +278,10 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
             for (int t = 0; t < NP; ++t) Sc[ib][t] = zero;
 #pragma unroll
         for (int j = 0; j < NT; ++j) YS[j] = zero;
-        f16x8 SA[2][JI][2];
-        load_group(0, SA[0]);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            // the direction's features 32q .. 32q + 31, after the deferred x update
+        // the direction's features 32q .. 32q + 31, after the deferred x
+        // update, and their split
+        f16x8 Z[NQ][2];
+        auto form = [&](int q) {
 #pragma unroll
             for (int jj = 2 * q; jj < 2 * q + 2; ++jj)
 #pragma unroll
@@ -290,9 +289,32 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
                     X[jj][r] += alpha * P[jj][r];
                     P[jj][r] = R[jj][r] + beta * P[jj][r];
                 }
-            f16x8 Zh, Zl;
-            h2_split(P[2 * q], P[2 * q + 1], sP, Zh, Zl);
-            h2_scores_step<D, C, NKP, NB>(L, q, Zh, Zl, n, kk, Sc);
+            h2_split(P[2 * q], P[2 * q + 1], sP, Z[q][0], Z[q][1]);
+        };
+        // decayed scores W 2^(EK + EP), their per-token exponent and split
+        f16x8 Wh[NS], Wl[NS];
+        int EW = 0;
+        auto decayed_scores = [&]() {
+            f32x4 Wt[2 * NS];
+#pragma unroll
+            for (int ib = 0; ib < 2 * NS; ++ib)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Wt[ib][r] = ib < NB ? h2_score<NB, NKP>(Sc, ib < NB ? ib : 0, r) * wv.dec[ib][r] : 0.f;
+            EW = h2_exp(kslot_max(absmax<2 * NS>(Wt)));
+            const float sW = pow2(EW);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) h2_split(Wt[2 * s], Wt[2 * s + 1], sW, Wh[s], Wl[s]);
+        };
+        f16x8 SA[2][JI][2];
+        load_group(0, SA[0]);
+        form(0);
+        // Per step q: the scores, then the state products, with the next
+        // step's direction (or, after the last scores, the decayed scores)
+        // formed between the first row group's products and the rest.
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            h2_scores_step<D, C, NKP, NB>(L, q, Z[q][0], Z[q][1], n, kk, Sc);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int f = q * NG + g;
@@ -300,26 +322,17 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
                 const f16x8(&A)[JI][2] = SA[f & 1];
                 // smallest terms first
 #pragma unroll
-                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][1], Zh, YS[g * JI + h]);
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][1], Z[q][0], YS[g * JI + h]);
 #pragma unroll
-                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Zl, YS[g * JI + h]);
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Z[q][1], YS[g * JI + h]);
 #pragma unroll
-                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Zh, YS[g * JI + h]);
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Z[q][0], YS[g * JI + h]);
+                if (g == 0) {
+                    if (q + 1 < NQ) form(q + 1);
+                    else decayed_scores();
+                }
             }
         }
-        // decayed scores W 2^(EK + EP) and their per-token exponent
-        f32x4 Wt[2 * NS];
-#pragma unroll
-        for (int ib = 0; ib < 2 * NS; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                Wt[ib][r] = ib < NB ? h2_score<NB, NKP>(Sc, ib < NB ? ib : 0, r) * wv.dec[ib][r] : 0.f;
-            }
-        const int EW = h2_exp(kslot_max(absmax<2 * NS>(Wt)));
-        const float sW = pow2(EW);
-        f16x8 Wh[NS], Wl[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) h2_split(Wt[2 * s], Wt[2 * s + 1], sW, Wh[s], Wl[s]);
         const float a = __builtin_amdgcn_ldexpf(wv.eLo, -(ES + EP));
         const float b = pow2(-(2 * EK + EP + EW));
         // apply, combination and p.Ap, one row block at a time

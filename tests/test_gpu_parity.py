@@ -385,6 +385,33 @@ def test_one_and_two_iterations(dtype, k):
         assert (g["iters"] == k).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [(2.0 ** -10, 2.0 ** -20, 2.0 ** 15), (2.0 ** 10, 2.0 ** 8, 2.0 ** -12)])
+def test_inputs_far_from_unit_size(dtype, scale):
+    """Keys, queries, values and lambda scaled by powers of two far from 1
+    (the fp16 split products rescale every group by its own exponent, so the
+    result must keep its accuracy): keys x sk with lambda x sk^2 is the same
+    system up to the scale of x, so the outputs are compared with the oracle
+    at the same bar as unit inputs."""
+    sk, sq, sv = scale
+    B, H, T, d = 1, 2, 150, 64
+    say("case scaled inputs", dtype, scale)
+    x = small_inputs(61, B, H, T, d, "f32")
+    x["k"] = x["k"] * np.float32(sk)
+    x["q"] = x["q"] * np.float32(sq)
+    x["v"] = x["v"] * np.float32(sv)
+    x["lam"] = (x["lam"] * np.float32(sk * sk)).astype(np.float32)
+    if dtype == "bf16":
+        x = {n: (inputs.bf16_bits(x[n]) if n in ("q", "k", "v") else x[n]) for n in x}
+    for cap, tol in ((2, 0.0), (12, 0.0), (30, 1e-4)):
+        g = gpu_forward(x, dtype, cap, tol, 64)
+        r = oracle_forward(x, dtype, cap, tol)
+        e = rel_l2(g["out"], r["out"])
+        say(f"scaled {dtype} cap {cap} tol {tol}: rel_l2={e:.2e}")
+        assert np.isfinite(g["out"]).all() and e <= 1e-5, (cap, tol, e)
+        compare_counts(g["iters"], r, cap, tol)
+
+
 @pytest.mark.parametrize("d", [16, 128])
 def test_iterating_far_past_convergence_stays_finite(d):
     """Lambda = I and a fixed cap far above d: every token's CG converges
