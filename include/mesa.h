@@ -63,10 +63,14 @@ typedef enum {
 
 typedef enum {
     MESA_DTYPE_F32 = 0,              /* q, k, v stored as float32                        */
-    MESA_DTYPE_BF16 = 1              /* q, k, v stored as bfloat16; all math in fp32:
-                                        products of float values run as bf16 MFMAs on
-                                        exact three-part bf16 splits, so every product
-                                        term is the exact float product, summed in fp32 */
+    MESA_DTYPE_BF16 = 1              /* q, k, v stored as bfloat16; vectors, states and
+                                        sums in fp32.  The chunk states' products are exact
+                                        (bf16 MFMAs on three-part bf16 splits).  The CG and
+                                        output products (d >= 32, either dtype) run as fp16
+                                        MFMAs on two-part splits: each operand group is
+                                        scaled by a power of two and held as hi + lo to 22
+                                        bits, and a product is hi.hi + hi.lo + lo.hi, within
+                                        about 3 * 2^-22 of the float product                 */
 } mesa_dtype;
 
 /* Kernel ids for the optional profiling records. */

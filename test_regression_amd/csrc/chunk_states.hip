@@ -7,38 +7,52 @@
 //   H_t = gamma_t H_{t-1} + k_t k_t^T,   G_t = gamma_t G_{t-1} + v_t k_t^T.
 // Over a chunk c of C tokens with within-chunk log decays l_i (prefix sums of
 // ln gamma) this is
-//   S_{c+1} = e^{l_end} S_c + sum_{i in c} e^{l_end - l_i} a_i k_i^T,
-// a = k for H and a = v for G, S_0 = 0.  This kernel produces S_c for every
-// chunk (the state before the chunk's first token) and, optionally, the final
-// state after the last token.
+//   S_{c+1} = e^{l_end} S_c + sum_{i in c} e^{l_end - l_i} a_i b_i^T,
+// with (a, b) = (k, k) for H and (k, v) for G^T, S_0 = 0.  This kernel
+// produces S_c for every chunk (the state before the chunk's first token)
+// and, optionally, the final state after the last token.
 //
 // Chunk states in the workspace: G as all its 16 x 16 blocks, H (symmetric)
 // as the upper triangle of them -- the part the CG kernel reads -- each in
 // row-major block order, so a wave stores a block as one 16-byte piece per
-// lane (1 KiB contiguous per wave).  An H block is kept in MFMA accumulator
-// order (lane 16q + m holds rows 4q..4q+3 of column m); a G block in MFMA
-// operand order (lane 16q + m holds columns 4q..4q+3 of row m), which is the
-// A operand the CG kernel's output product takes straight from memory.  For
+// lane (1 KiB contiguous).  An H block is kept in MFMA accumulator order
+// (lane 16q + m holds rows 4q..4q+3 of column m); a G block in MFMA operand
+// order (lane 16q + m holds columns 4q..4q+3 of row m), which is the A
+// operand the CG kernel's output product takes straight from memory.  For
 // the backward's adjoint solve (g_transposed) the blocks of G^T are stored
 // in operand order instead, the A operand of its G^T g product.  The
 // exported final states are full and row-major ([d_v][d_k] for G).
 //
-// Work split: one workgroup per (head, {H, G}, 16*NW-row block of the
-// state); each wave holds a 16 x D slab of the running state (of H, or of
-// G^T: 16 key features by all value features) in MFMA accumulator layout
-// and walks the chunks in order.  Per chunk the update is one
-// (16 x C) x (C x D) product on v_mfma_f32_16x16x4_f32 with the weighted keys
-// as the A operand and the keys (H) or values (G^T) as the B operand; the
-// contraction runs over the chunk's tokens.  For bf16 keys and values the
-// product runs on v_mfma_f32_16x16x32_bf16 instead: the values a_i, b_i are
-// exact bf16, and each weighted value w_i a_i (a float) is split exactly into
-// three bf16 parts (the top 8, next 8 and last 8 bits of its significand),
-// so the three bf16 products sum to the float product terms up to the
-// accumulation order.  The chunk's values are then staged as bf16 with two
-// consecutive tokens per 32-bit LDS word, so a lane's eight-token MFMA
-// operand is four word reads.  Workgroup ids are
-// mapped so that the 2*RB workgroups of one head land on the same XCD (ids
-// congruent mod 8) and share its L2 for the key and value tiles.
+// Work split.  A wave owns a fixed list of 16 x 16 output tiles of one state
+// and keeps them in MFMA accumulator registers while it walks the chunks in
+// order; per chunk a tile gains one (16 x C) x (C x 16) product over the
+// chunk's tokens, with the weighted rows w_i a_i as the A operand.
+//   - H: only the upper block triangle is formed.  Wave w of an H workgroup
+//     takes the tiles of row blocks w and NT-1-w right of the diagonal: NT+1
+//     tiles, the same for every wave.  The exported final H gets its lower
+//     triangle by mirroring.
+//   - G^T (or G with g_transposed): wave w takes row block w of its
+//     workgroup's rows and NT/CS column tiles.
+// With CS = 2 (few heads of d = 128) the columns are split over two
+// workgroups, so a wave holds half as many tiles and twice as many waves run.
+// The workgroup stages the chunk's rows and columns it needs in LDS (two
+// buffers, one barrier per chunk); the global loads of chunk c + 3 are issued
+// while chunk c is multiplied, from clamped addresses so that every wave
+// issues the same loads and the compiler can count them, and the states are
+// stored without being waited for.
+//
+// Products: fp32 keys and values on v_mfma_f32_16x16x4_f32.  For bf16 the
+// values a_i, b_i are exact bf16, and each weighted value w_i a_i (a float)
+// is split exactly into three bf16 parts (the top 8, next 8 and last 8 bits
+// of its significand), so three v_mfma_f32_16x16x32_bf16 products sum to the
+// float product terms up to the accumulation order.  bf16 tiles are staged
+// with two consecutive tokens per 32-bit LDS word (each thread packs a token
+// pair of four features into one 16-byte write), so a lane's eight-token
+// MFMA operand is four word reads.  Workgroup ids are mapped so that the
+// workgroups of one head land on the same XCD (ids congruent mod 8) and
+// share its L2 for the key and value tiles.
+#include <type_traits>
+
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -51,220 +65,290 @@ __device__ __forceinline__ int packed_blk(int a, int b) {
     return (a * NT - a * (a - 1) / 2 + (b - a)) * 256;
 }
 
-// NWK: waves per workgroup (each owns 16 rows of the state).  With
-// NWK = D / 16 a workgroup holds a whole state (one per head for H, one for
-// G); fewer waves split a state into RB row blocks, giving more workgroups
-// for problems with few heads.
-template <int D, int C, int NWK, typename In>
-__global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
-    const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
-    int T, int n_chunks, float* __restrict__ SH, float* __restrict__ SG,
-    float* __restrict__ final_H, float* __restrict__ final_G, int write_chunks, long BH,
-    int* __restrict__ work_counter, int g_transposed) {
-    constexpr int NW = NWK;                    // waves per workgroup
-    constexpr int RB = D / (16 * NW);          // row blocks per state
-    constexpr int NT = D / 16;                 // 16-column tiles of the state
-    constexpr int PD = lds_pitch(D);
+// Inclusive prefix sum over the 64 lanes of a wave: in-row steps on
+// row_shr 1, 2, 4, 8, then the row totals carried on by row_bcast 15 (into
+// rows 1 and 3) and row_bcast 31 (into rows 2 and 3).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_moved(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_moved<0x111, 0xf>(x);
+    x += dpp_moved<0x112, 0xf>(x);
+    x += dpp_moved<0x114, 0xf>(x);
+    x += dpp_moved<0x118, 0xf>(x);
+    x += dpp_moved<0x142, 0xa>(x);
+    x += dpp_moved<0x143, 0xc>(x);
+    return x;
+}
+
+// One staged LDS region of F consecutive features of a chunk.
+//   bf16: row p holds token pair (2p, 2p + 1); word (p, f) = feature f of
+//         token 2p (low half) and 2p + 1 (high half).  The pitch F + 8 puts
+//         the four lane groups' rows (2 pairs apart) 16 banks apart.
+//   fp32: row i holds token i; pitch lds_pitch(F).
+template <int F, int C, bool BF>
+struct StageTile {
+    static constexpr int FG = F / 4;                        // 4-feature groups of a row
+    static constexpr int ROWS = BF ? C / 2 : C;
+    static constexpr int PITCH = BF ? F + 8 : lds_pitch(F); // 32-bit words
+    static constexpr int WORDS = ROWS * PITCH;
+    static constexpr int UNITS = ROWS * FG;                 // one 16-byte LDS write each
+};
+
+template <int D, int C, int NW, int CS, bool BF>
+struct K1Shape {
+    static constexpr int NT = D / 16;          // 16 x 16 tiles per state row block
+    static constexpr int RB = D / (16 * NW);   // row blocks of NW tiles per G^T state
+    static constexpr int NTW = NT / CS;        // column tiles per G wave
+    static constexpr int PAIRS = (NT + 1) / 2; // H waves (row blocks w and NT-1-w)
+    static constexpr int HTILES = NT == 1 ? 1 : NT + 1;
+    static constexpr int HPARTS = CS;          // H workgroups per head
+    static constexpr int GPARTS = RB * CS;     // G workgroups per head
+    static constexpr int PARTS = HPARTS + GPARTS;
+    // H tiles per wave in H part h (CS = 2: the NT+1 tiles split 5 / 4)
+    static constexpr int HT0 = CS == 1 ? HTILES : (HTILES + 1) / 2;
+    static constexpr int HT1 = HTILES - HT0;
+    using KT = StageTile<D, C, BF>;            // H: the whole key tile
+    using AT = StageTile<16 * NW, C, BF>;      // G: the workgroup's rows
+    using BT = StageTile<D / CS, C, BF>;       // G: the workgroup's columns
+    static constexpr int HBUF = KT::WORDS + C + 4;
+    static constexpr int GBUF = AT::WORDS + BT::WORDS + C + 4;
+    static constexpr int BUF = HBUF > GBUF ? HBUF : GBUF;   // words per LDS buffer
+};
+
+// Raw buffer resource over `bytes` bytes from `base`: loads past the end
+// return zeros and stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k1_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Per-thread offsets of one staged region's units: the byte offset of the
+// unit within a chunk's rows of the input and its LDS word offset.  bf16
+// units are a token pair x 4 features (two 8-byte loads, one 16-byte LDS
+// write), fp32 units one token x 4 features.  Unit indices past the region
+// are clamped onto its last unit, whose LDS write then repeats with the same
+// data.
+template <typename Tl, int NTHR, int D, int ES>
+struct UnitOffsets {
+    static constexpr int U = (Tl::UNITS + NTHR - 1) / NTHR;
+    int g[U], l[U];
+    __device__ __forceinline__ UnitOffsets(int f0, int tid) {
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+            const int u = min(tid + e * NTHR, Tl::UNITS - 1);
+            const int row = u / Tl::FG, fg = u % Tl::FG;
+            g[e] = ((ES == 2 ? 2 * row : row) * D + f0 + 4 * fg) * ES;
+            l[e] = row * Tl::PITCH + 4 * fg;
+        }
+    }
+};
+
+template <typename Tl, int NTHR, int D, typename In, typename Ld>
+__device__ __forceinline__ void k1_load(Ld (&r)[(Tl::UNITS + NTHR - 1) / NTHR][sizeof(In) == 2 ? 2 : 1],
+                                        __amdgpu_buffer_rsrc_t rs, const UnitOffsets<Tl, NTHR, D, sizeof(In)>& o) {
+    constexpr int U = (Tl::UNITS + NTHR - 1) / NTHR;
+#pragma unroll
+    for (int e = 0; e < U; ++e) {
+        if constexpr (sizeof(In) == 2) {
+            r[e][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.g[e], 0, 0));
+            r[e][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.g[e] + 2 * D, 0, 0));
+        } else {
+            r[e][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.g[e], 0, 0));
+        }
+    }
+}
+
+// Write the loaded units into LDS (rows past the sequence arrived as zeros).
+template <typename Tl, int NTHR, int D, typename In, typename Ld>
+__device__ __forceinline__ void k1_stage(const Ld (&r)[(Tl::UNITS + NTHR - 1) / NTHR][sizeof(In) == 2 ? 2 : 1],
+                                         float* dst, const UnitOffsets<Tl, NTHR, D, sizeof(In)>& o) {
+    constexpr int U = (Tl::UNITS + NTHR - 1) / NTHR;
+#pragma unroll
+    for (int e = 0; e < U; ++e) {
+        if constexpr (sizeof(In) == 2) {
+            const uint2 x = r[e][0], y = r[e][1];
+            // word f = (feature f of token 2p) | (feature f of token 2p + 1) << 16
+            typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+            const u32x4v wd{(x.x & 0xffffu) | (y.x << 16), (x.x >> 16) | (y.x & 0xffff0000u),
+                            (x.y & 0xffffu) | (y.y << 16), (x.y >> 16) | (y.y & 0xffff0000u)};
+            *reinterpret_cast<u32x4v*>(dst + o.l[e]) = wd;
+        } else {
+            *reinterpret_cast<f32x4*>(dst + o.l[e]) = r[e][0];
+        }
+    }
+}
+
+// The per-wave chunk walk.  KIND 0: H tiles (a pair of row blocks, TW tiles
+// starting at tile T0 of the pair's list); KIND 1: G^T (or G) tiles (one row
+// block, TW column tiles).  WRITE: store the chunk states.
+template <int D, int C, int NW, int CS, typename In, int KIND, int TW, int T0, bool WRITE>
+__device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, const In* __restrict__ v,
+                                                  const float* __restrict__ gamma, int T, int n_chunks,
+                                                  float* __restrict__ Sout, float* __restrict__ final_S,
+                                                  int g_transposed, long bh, int rb, int cs, float* lds) {
+    constexpr bool BF = sizeof(In) == 2;
+    using S = K1Shape<D, C, NW, CS, BF>;
+    constexpr int NT = S::NT;
     constexpr int NTHR = 64 * NW;
     constexpr int HPACK = D * (D + 16) / 2;    // floats of a packed upper block triangle
-    constexpr bool BF = sizeof(In) == 2;       // bf16 keys and values: the split bf16 product
-    // bf16 tiles: word (p, f) holds feature f of tokens 2p (low half) and
-    // 2p + 1 (high half); the pitch D + 8 puts the four lane groups' rows
-    // (2 token pairs apart) 16 banks apart.
-    constexpr int PP = D + 8;
-    constexpr int TILE = BF ? (C / 2) * PP : C * PD;
+    using Ld = std::conditional_t<BF, uint2, f32x4>;
+    constexpr int NL = BF ? 2 : 1;
+    // staged regions: H one key region (rows and columns), G a row region and a column region
+    using TA = std::conditional_t<KIND == 0, typename S::KT, typename S::AT>;
+    using TB = std::conditional_t<KIND == 0, typename S::KT, typename S::BT>;
+    constexpr int UA = KIND == 0 ? 1 : (TA::UNITS + NTHR - 1) / NTHR;   // (unused for H)
+    constexpr int UB = (TB::UNITS + NTHR - 1) / NTHR;
+    constexpr int AOFF = 0;
+    constexpr int BOFF = KIND == 0 ? 0 : TA::WORDS;
+    constexpr int WOFF = BOFF + TB::WORDS;     // weights e^{l_end - l_i}, then e^{l_end}
+    constexpr int NR = KIND == 0 && NT > 1 ? 2 : 1;   // row blocks a wave's tiles come from
 
-    __shared__ float sK[TILE];     // keys of the chunk (A operand; B operand for H)
-    __shared__ float sB[TILE];     // values of the chunk (B operand for G^T)
-    __shared__ alignas(16) float sW[C];   // e^{l_end - l_i}
-    __shared__ float sGam;         // e^{l_end}
-
+    typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
     const int tid0 = threadIdx.x;
-    const int lane = tid0 & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
-    const int n = lane & 15;
-    const int kk = lane >> 4;
-    // the chunk-claim counter of the CG/output kernel that runs next
-    if (work_counter && blockIdx.x == 0 && tid0 == 0) *work_counter = 0;
+    const int lane = tid0 & 63;
+    const int n = lane & 15, kk = lane >> 4;
 
-    // XCD-aware id: consecutive ids go round-robin over the 8 XCDs, so the
-    // 2*RB parts of head bh get ids xcd + 8*(slot) with equal xcd.
-    constexpr int PARTS = 2 * RB;
-    const long xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-    const long bh = (slot / PARTS) * 8 + xcd;
-    const int part = (int)(slot % PARTS);
-    if (bh >= BH) return;                      // whole workgroup: no barrier is skipped
-    const int rb = part % RB;
-    const int which = part / RB;               // 0: H, 1: G
-    const int m0 = rb * 16 * NW + 16 * w;      // first state row (of H or G^T) of this wave
-    const int a0 = m0 / 16;                    // its row block
-
-    const In* kh = k + (size_t)bh * T * D;
-    const In* vh = v + (size_t)bh * T * D;
-    const float* gh = gamma + (size_t)bh * T;
-    // H: packed upper block triangle per chunk; G: full d x d per chunk
-    float* Sout = which == 0 ? SH + (size_t)bh * n_chunks * HPACK : SG + (size_t)bh * n_chunks * D * D;
-    // H: A = weighted keys, B = keys.  G: the wave's slab is of G^T (A =
-    // weighted keys, B = values), whose accumulator blocks are G's blocks in
-    // operand order; with g_transposed, of G (A = weighted values, B = keys),
-    // whose accumulator blocks are G^T's blocks in operand order.
-    const bool gt = which == 1 && g_transposed;
-    const float* sArows = gt ? sB : sK;
-    const float* sBcols = which == 0 || gt ? sK : sB;
-
-    f32x4 acc[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Keys, values and gates of the next RING chunks are held in registers
-    // (a ring of RING slots), so a chunk's global loads have RING chunk
-    // steps of MFMAs and stores to complete behind.  Two slots of fp32
-    // inputs would cost the second wave per SIMD its registers.
-    constexpr int RING = sizeof(In) == 2 ? 2 : 1;
-    constexpr int EL4 = C * D / (4 * NTHR);   // 4-element groups per thread per tile
-    static_assert(C * D % (4 * NTHR) == 0, "tile must split evenly over the workgroup");
-    Raw4<In> kreg[RING][EL4], vreg[RING][EL4];
-    float greg[RING];
-#pragma unroll
-    for (int sl = 0; sl < RING; ++sl) greg[sl] = 1.0f;
-    // Lane-dependent addresses are rebuilt from an opaque copy of the thread
-    // id in every step and prefetch instead of being held in registers
-    // across the chunk loop (which would cost the second wave per SIMD).
-    auto prefetch = [&](int c, int sl) {
-        int tid = tid0;
-        asm volatile("" : "+v"(tid));
-        const int t0 = c * C;
-        const int valid = min(C, T - t0);
-#pragma unroll
-        for (int u = 0; u < EL4; ++u) {
-            const int e = (tid + u * NTHR) * 4;
-            const int i = e / D, f = e % D;
-            kreg[sl][u].zero();
-            vreg[sl][u].zero();
-            if (i < valid) {
-                kreg[sl][u].load(kh + (size_t)(t0 + i) * D + f);
-                if (which) vreg[sl][u].load(vh + (size_t)(t0 + i) * D + f);
-            }
-        }
-        if (w == 0) greg[sl] = lane < valid ? gh[t0 + lane] : 1.0f;
+    // this wave's tiles: row blocks r0 (tiles t' < split) and r1, column of tile t' = T0 + t
+    const bool active = KIND == 1 || S::PAIRS == NW || w < S::PAIRS;
+    const int r0 = KIND == 0 ? w : rb * NW + w;
+    const int r1 = KIND == 0 ? NT - 1 - w : r0;
+    const int split = KIND == 0 ? NT - w : TW + T0;
+    auto tile_first = [&](int t) { return T0 + t < split; };
+    auto tile_col = [&](int t) {
+        if constexpr (KIND == 0) return T0 + t < split ? w + T0 + t : T0 + t - 1;
+        else return cs * S::NTW + t;
     };
+    // A operand feature offset of row block r in its region
+    auto a_off = [&](int r) { return KIND == 0 ? 16 * r : 16 * w; };
+    // B operand feature offset of tile t in its region
+    auto b_off = [&](int t) { return KIND == 0 ? 16 * tile_col(t) : 16 * t; };
 
-    auto step = [&](int c, int sl) {
+    const bool gt = KIND == 1 && g_transposed;
+    constexpr int ES = sizeof(In);
+    const In* srcA = (gt ? v : k) + (size_t)bh * T * D;
+    const In* srcB = (KIND == 0 || gt ? k : v) + (size_t)bh * T * D;
+    const float* gh = gamma + (size_t)bh * T;
+    const UnitOffsets<TA, NTHR, D, ES> oA(KIND == 0 ? 0 : rb * 16 * NW, tid0);
+    const UnitOffsets<TB, NTHR, D, ES> oB(KIND == 0 ? 0 : cs * (D / CS), tid0);
+
+    f32x4 acc[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Ld ra[2][UA][NL], rbv[2][UB][NL];
+    float greg[2];
+    auto load = [&](int c, int sl) {
+        // the chunk's rows as a buffer: rows past the sequence read as zeros
+        const int t0 = min(c, n_chunks - 1) * C;
+        const int rows = min(C, T - t0);
+        if constexpr (KIND == 1) k1_load<TA, NTHR, D, In>(ra[sl], k1_rsrc(srcA + (size_t)t0 * D, rows * D * ES), oA);
+        k1_load<TB, NTHR, D, In>(rbv[sl], k1_rsrc(srcB + (size_t)t0 * D, rows * D * ES), oB);
+        greg[sl] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(k1_rsrc(gh + t0, rows * 4),
+                                                                                  (tid0 & 63) * 4, 0, 0));
+    };
+    auto stage = [&](int c, int sl, int buf) {
+        float* base = lds + buf * S::BUF;
+        const int valid = min(C, T - c * C);
+        if constexpr (KIND == 1) k1_stage<TA, NTHR, D, In>(ra[sl], base + AOFF, oA);
+        k1_stage<TB, NTHR, D, In>(rbv[sl], base + BOFF, oB);
+        // within-chunk log decays (tokens past the end count as gamma = 1):
+        // an inclusive scan over the wave on DPP moves, computed by every
+        // wave (no branch around it) and written by wave 0
+        const float l = wave_inclusive_sum(lane < valid ? __logf(greg[sl]) : 0.f);
+        const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), C - 1));
+        if (w == 0) {
+            if (lane < C) base[WOFF + lane] = __expf(lend - l);
+            if (lane == 0) base[WOFF + C] = __expf(lend);
+        }
+    };
+    auto store_states = [&](int c) {
+        // one 16-byte piece per lane per 16 x 16 block, non-temporal
+        constexpr int SB = (KIND == 0 ? HPACK : D * D) * 4;
+        const __amdgpu_buffer_rsrc_t rs = k1_rsrc(Sout + (size_t)c * (SB / 4), SB);
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            const int row = tile_first(t) ? r0 : r1, col = tile_col(t);
+            // G: block (row, col) of the slab's matrix in accumulator order =
+            // block (col, row) of its transpose in operand order
+            const int blk = KIND == 0 ? packed_blk<NT>(row, col) : (col * NT + row) * 256;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, acc[t]), rs, lane * 16, blk * 4, 2);
+        }
+    };
+    auto multiply = [&](int buf) {
         int tid = tid0;
         asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, n = lane & 15, kk = lane >> 4;
-        // ---- stage the chunk's keys (and values) in LDS ----
+        const int ln = tid & 63, nn = ln & 15, kq = ln >> 4;
+        const float* base = lds + buf * S::BUF;
+        const float* sA = base + AOFF;
+        const float* sB = base + BOFF;
+        const float* sW = base + WOFF;
+        // U is a fresh MFMA chain per tile (started from zero, only read
+        // afterwards); the decayed running state is combined with it on the VALU.
+        f32x4 U[TW];
 #pragma unroll
-        for (int u = 0; u < EL4; ++u) {
-            const int e = (tid + u * NTHR) * 4;
-            const int i = e / D, f = e % D;
-            if constexpr (BF) {
-                uint16_t* k16 = reinterpret_cast<uint16_t*>(sK) + ((i >> 1) * PP + f) * 2 + (i & 1);
-                uint16_t* v16 = reinterpret_cast<uint16_t*>(sB) + ((i >> 1) * PP + f) * 2 + (i & 1);
-                const uint2 kb = kreg[sl][u].raw(), vb = vreg[sl][u].raw();
-                k16[0] = (uint16_t)kb.x;
-                k16[2] = (uint16_t)(kb.x >> 16);
-                k16[4] = (uint16_t)kb.y;
-                k16[6] = (uint16_t)(kb.y >> 16);
-                if (which) {
-                    v16[0] = (uint16_t)vb.x;
-                    v16[2] = (uint16_t)(vb.x >> 16);
-                    v16[4] = (uint16_t)vb.y;
-                    v16[6] = (uint16_t)(vb.y >> 16);
-                }
-            } else {
-                *reinterpret_cast<f32x4*>(&sK[i * PD + f]) = kreg[sl][u].get();
-                if (which) *reinterpret_cast<f32x4*>(&sB[i * PD + f]) = vreg[sl][u].get();
-            }
-        }
-        if (w == 0) {
-            // within-chunk log decays (tokens past the end count as gamma = 1)
-            float l = __logf(greg[sl]);
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float t = __shfl_up(l, o, 64);
-                if (lane >= o) l += t;
-            }
-            const float lend = __shfl(l, C - 1, 64);
-            if (lane < C) sW[lane] = __expf(lend - l);
-            if (lane == 0) sGam = __expf(lend);
-        }
-        __syncthreads();
-        if (c + RING < n_chunks) prefetch(c + RING, sl);
-
-        // ---- the state before this chunk ----
-        if (write_chunks) {
-            // one 16-byte piece per lane per 16 x 16 block (accumulator order)
-            float* dst = Sout + (size_t)c * (which == 0 ? HPACK : D * D) + (kk * 16 + n) * 4;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                if (which == 0) {
-                    if (j >= a0) store_nt(dst + packed_blk<NT>(a0, j), acc[j]);
-                } else {
-                    // block (a0, j) of the slab's matrix in accumulator order = block (j, a0)
-                    // of its transpose in operand order
-                    store_nt(dst + (j * NT + a0) * 256, acc[j]);
-                }
-            }
-        }
-
-        // ---- S <- Gamma_c S + U,  U = sum_i w_i k_i b_i^T  (b = k for H, v for G^T) ----
-        // U is a fresh MFMA chain (started from zero, only read afterwards);
-        // the decayed running state is combined with it on the VALU.
-        f32x4 U[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < TW; ++t) U[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (BF) {
-            // 32 tokens per MFMA: lane group kk's eight k-slots e are tokens
-            // 32 g2 + 16 (e / 4) + 4 kk + e % 4, i.e. the token pairs
-            // p = 16 g2 + 8 h + 2 kk + {0, 1} for h = 0, 1 (a chunk of 16
+            // 32 tokens per MFMA: lane group kq's eight k-slots e are tokens
+            // 32 g2 + 16 (e / 4) + 4 kq + e % 4, i.e. the token pairs
+            // p = 16 g2 + 8 h + 2 kq + {0, 1} for h = 0, 1 (a chunk of 16
             // tokens leaves h = 1 empty).
-            const uint32_t* tA = reinterpret_cast<const uint32_t*>(sArows);
-            const uint32_t* tB = reinterpret_cast<const uint32_t*>(sBcols);
+            const uint32_t* tA = reinterpret_cast<const uint32_t*>(sA);
+            const uint32_t* tB = reinterpret_cast<const uint32_t*>(sB);
+            constexpr int NH = C >= 32 ? 2 : 1;
 #pragma unroll
             for (int g2 = 0; g2 < (C + 31) / 32; ++g2) {
-                constexpr int NH = C >= 32 ? 2 : 1;
-                uint32_t ah[4], am[4], al[4];
+                bf16x8 Ah[NR], Am[NR], Al[NR];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) ah[q] = am[q] = al[q] = 0u;
+                for (int ri = 0; ri < NR; ++ri) {
+                    const int aoff = a_off(ri == 0 ? r0 : r1);
+                    uint32_t ah[4], am[4], al[4];
 #pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    const int p0 = 16 * g2 + 8 * h + 2 * kk;
-                    const f32x4 wv = *reinterpret_cast<const f32x4*>(&sW[2 * p0]);
+                    for (int q = 0; q < 4; ++q) ah[q] = am[q] = al[q] = 0u;
 #pragma unroll
-                    for (int d = 0; d < 2; ++d) {
-                        const uint32_t pr = tA[(p0 + d) * PP + m0 + n];
-                        uint32_t hb[2], mb[2], lb[2];
+                    for (int h = 0; h < NH; ++h) {
+                        const int p0 = 16 * g2 + 8 * h + 2 * kq;
+                        const f32x4 wv = *reinterpret_cast<const f32x4*>(&sW[2 * p0]);
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const float a = __uint_as_float(t ? (pr & 0xffff0000u) : (pr << 16));
-                            const float x = a * wv[2 * d + t];
-                            // exact split: x = hi + mid + lo, each a bf16
-                            hb[t] = __float_as_uint(x) & 0xffff0000u;
-                            const float r1 = x - __uint_as_float(hb[t]);
-                            mb[t] = __float_as_uint(r1) & 0xffff0000u;
-                            lb[t] = __float_as_uint(r1 - __uint_as_float(mb[t])) & 0xffff0000u;
+                        for (int d = 0; d < 2; ++d) {
+                            const uint32_t pr = tA[(p0 + d) * TA::PITCH + aoff + nn];
+                            uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+                            for (int s = 0; s < 2; ++s) {
+                                const float a = __uint_as_float(s ? (pr & 0xffff0000u) : (pr << 16));
+                                const float x = a * wv[2 * d + s];
+                                // exact split: x = hi + mid + lo, each a bf16
+                                hb[s] = __float_as_uint(x) & 0xffff0000u;
+                                const float r1f = x - __uint_as_float(hb[s]);
+                                mb[s] = __float_as_uint(r1f) & 0xffff0000u;
+                                lb[s] = __float_as_uint(r1f - __uint_as_float(mb[s])) & 0xffff0000u;
+                            }
+                            const int q = 2 * h + d;
+                            ah[q] = (hb[0] >> 16) | hb[1];
+                            am[q] = (mb[0] >> 16) | mb[1];
+                            al[q] = (lb[0] >> 16) | lb[1];
                         }
-                        const int q = 2 * h + d;
-                        ah[q] = (hb[0] >> 16) | hb[1];
-                        am[q] = (mb[0] >> 16) | mb[1];
-                        al[q] = (lb[0] >> 16) | lb[1];
                     }
+                    Ah[ri] = as_bf16x8(ah);
+                    Am[ri] = as_bf16x8(am);
+                    Al[ri] = as_bf16x8(al);
                 }
-                const bf16x8 Ah = as_bf16x8(ah), Am = as_bf16x8(am), Al = as_bf16x8(al);
 #pragma unroll
-                for (int j = 0; j < NT; ++j) {
+                for (int t = 0; t < TW; ++t) {
+                    const int boff = b_off(t);
                     uint32_t b[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
                     for (int h = 0; h < NH; ++h) {
-                        const int p0 = 16 * g2 + 8 * h + 2 * kk;
-                        b[2 * h] = tB[p0 * PP + 16 * j + n];
-                        b[2 * h + 1] = tB[(p0 + 1) * PP + 16 * j + n];
+                        const int p0 = 16 * g2 + 8 * h + 2 * kq;
+                        b[2 * h] = tB[p0 * TB::PITCH + boff + nn];
+                        b[2 * h + 1] = tB[(p0 + 1) * TB::PITCH + boff + nn];
                     }
                     const bf16x8 Bj = as_bf16x8(b);
-                    U[j] = mfma_bf16x32(Ah, Bj, U[j]);
-                    U[j] = mfma_bf16x32(Am, Bj, U[j]);
-                    U[j] = mfma_bf16x32(Al, Bj, U[j]);
+                    const bool f = NR == 1 || tile_first(t);
+                    U[t] = mfma_bf16x32(f ? Ah[0] : Ah[NR - 1], Bj, U[t]);
+                    U[t] = mfma_bf16x32(f ? Am[0] : Am[NR - 1], Bj, U[t]);
+                    U[t] = mfma_bf16x32(f ? Al[0] : Al[NR - 1], Bj, U[t]);
                 }
             }
         } else {
@@ -272,70 +356,129 @@ __global__ __launch_bounds__(64 * NWK) void chunk_states_kernel(
             for (int g = 0; g < C / 16; ++g) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const int i = 16 * g + 4 * kk + s;
-                    const float a = sArows[i * PD + m0 + n] * sW[i];
+                    const int i = 16 * g + 4 * kq + s;
+                    float a[NR];
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sBcols[i * PD + 16 * j + n], U[j]);
+                    for (int ri = 0; ri < NR; ++ri)
+                        a[ri] = sA[i * TA::PITCH + a_off(ri == 0 ? r0 : r1) + nn] * sW[i];
+#pragma unroll
+                    for (int t = 0; t < TW; ++t) {
+                        const bool f = NR == 1 || tile_first(t);
+                        U[t] = mfma4(f ? a[0] : a[NR - 1], sB[i * TB::PITCH + b_off(t) + nn], U[t]);
+                    }
                 }
             }
         }
-        const float G = sGam;
+        const float G = sW[C];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j] = G * acc[j] + U[j];
-        __syncthreads();
+        for (int t = 0; t < TW; ++t) acc[t] = G * acc[t] + U[t];
     };
 
-#pragma unroll
-    for (int sl = 0; sl < RING; ++sl)
-        if (sl < n_chunks) prefetch(sl, sl);
-    for (int c = 0; c < n_chunks; c += RING) {
-#pragma unroll
-        for (int sl = 0; sl < RING; ++sl)
-            if (c + sl < n_chunks) step(c + sl, sl);
+    // Pipeline: chunk c + 1 is staged (buffer (c+1) & 1) and chunk c + 3
+    // loaded (register slot (c+1) & 1) while chunk c is multiplied from
+    // buffer c & 1; one barrier per chunk.
+    load(0, 0);
+    load(1, 1);
+    stage(0, 0, 0);
+    load(2, 0);
+    __syncthreads();
+    auto step = [&](int c, int sl, int buf) {
+        if (c + 1 < n_chunks) stage(c + 1, sl, buf ^ 1);
+        load(c + 3, sl);
+        if (active) {
+            if constexpr (WRITE) store_states(c);
+            multiply(buf);
+        }
+        __syncthreads();
+    };
+    for (int c = 0; c < n_chunks; c += 2) {
+        step(c, 1, 0);
+        if (c + 1 < n_chunks) step(c + 1, 0, 1);
     }
 
     // ---- final state (after the last token) ----
-    if (which == 0 && final_H) {
-        float* dst = final_H + (size_t)bh * D * D;
+    if (final_S && active) {
+        float* dst = final_S + (size_t)bh * D * D;
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+        for (int t = 0; t < TW; ++t) {
+            const int row = tile_first(t) ? r0 : r1, col = tile_col(t);
+            if (KIND == 0 || gt) {
+                // acc[t][q] = S[16 row + 4 kk + q][16 col + n]
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
-    }
-    if (which == 1 && final_G && g_transposed) {
-        float* dst = final_G + (size_t)bh * D * D;
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(size_t)(m0 + 4 * kk + r) * D + 16 * j + n] = acc[j][r];
-    }
-    if (which == 1 && final_G && !g_transposed) {
-        // acc[j][r] = G[16j + n][m0 + 4kk + r]: four consecutive floats of a row of G
-        float* dst = final_G + (size_t)bh * D * D;
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-            *reinterpret_cast<f32x4*>(dst + (size_t)(16 * j + n) * D + m0 + 4 * kk) = acc[j];
+                for (int q = 0; q < 4; ++q) dst[(size_t)(16 * row + 4 * kk + q) * D + 16 * col + n] = acc[t][q];
+                // H's lower triangle by symmetry
+                if (KIND == 0 && col != row)
+                    *reinterpret_cast<f32x4*>(dst + (size_t)(16 * col + n) * D + 16 * row + 4 * kk) = acc[t];
+            } else {
+                // acc[t][q] = G[16 col + n][16 row + 4 kk + q]: four consecutive floats of a row of G
+                *reinterpret_cast<f32x4*>(dst + (size_t)(16 * col + n) * D + 16 * row + 4 * kk) = acc[t];
+            }
+        }
     }
 }
 
-template <int D, int C, int NW, typename In>
+// NW: waves per workgroup.  CS: column splits of a G state (1 or 2).
+template <int D, int C, int NW, int CS, typename In, bool WRITE>
+__global__ __launch_bounds__(64 * NW) void chunk_states_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma, int T, int n_chunks,
+    float* __restrict__ SH, float* __restrict__ SG, float* __restrict__ final_H, float* __restrict__ final_G,
+    long BH, int* __restrict__ work_counter, int g_transposed) {
+    using S = K1Shape<D, C, NW, CS, sizeof(In) == 2>;
+    __shared__ alignas(16) float lds[2 * S::BUF];
+    // the chunk-claim counter of the CG/output kernel that runs next
+    if (work_counter && blockIdx.x == 0 && threadIdx.x == 0) *work_counter = 0;
+
+    // XCD-aware id: consecutive ids go round-robin over the 8 XCDs, so the
+    // PARTS workgroups of head bh get ids xcd + 8*(slot) with equal xcd.
+    const long xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const long bh = (slot / S::PARTS) * 8 + xcd;
+    const int part = (int)(slot % S::PARTS);
+    if (bh >= BH) return;                      // whole workgroup: no barrier is skipped
+    constexpr int HPACK = D * (D + 16) / 2;
+    float* SHh = WRITE ? SH + (size_t)bh * n_chunks * HPACK : nullptr;
+    float* SGh = WRITE ? SG + (size_t)bh * n_chunks * D * D : nullptr;
+    if (part < S::HPARTS) {
+        if (part == 0)
+            chunk_states_walk<D, C, NW, CS, In, 0, S::HT0, 0, WRITE>(k, v, gamma, T, n_chunks, SHh, final_H, 0,
+                                                                     bh, 0, 0, lds);
+        else if constexpr (S::HT1 > 0)
+            chunk_states_walk<D, C, NW, CS, In, 0, S::HT1, S::HT0, WRITE>(k, v, gamma, T, n_chunks, SHh, final_H,
+                                                                          0, bh, 0, 0, lds);
+    } else {
+        const int g = part - S::HPARTS;
+        chunk_states_walk<D, C, NW, CS, In, 1, S::NTW, 0, WRITE>(k, v, gamma, T, n_chunks, SGh, final_G,
+                                                                 g_transposed, bh, g / CS, g % CS, lds);
+    }
+}
+
+template <int D, int C, int NW, int CS, typename In>
 hipError_t launch_chunk_states_nw(const ChunkStatesArgs& a, hipStream_t s) {
-    constexpr int RB = D / (16 * NW);
+    using S = K1Shape<D, C, NW, CS, sizeof(In) == 2>;
     // ids: 8 XCD lanes x (heads rounded up to a multiple of 8) / 8 x parts
-    const long grid = ((a.BH + 7) / 8) * 8 * 2 * RB;
-    hipLaunchKernelGGL((chunk_states_kernel<D, C, NW, In>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
-                       (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG,
-                       a.final_H, a.final_G, a.write_chunks, a.BH, a.work_counter, a.g_transposed);
+    const long grid = ((a.BH + 7) / 8) * 8 * S::PARTS;
+    if (a.write_chunks)
+        hipLaunchKernelGGL((chunk_states_kernel<D, C, NW, CS, In, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+                           (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG, a.final_H,
+                           a.final_G, a.BH, a.work_counter, a.g_transposed);
+    else
+        hipLaunchKernelGGL((chunk_states_kernel<D, C, NW, CS, In, false>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                           s, (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG, a.final_H,
+                           a.final_G, a.BH, a.work_counter, a.g_transposed);
     return hipGetLastError();
 }
 
 template <int D, int C, typename In>
 hipError_t launch_chunk_states_t(const ChunkStatesArgs& a, hipStream_t s) {
-    // Four waves (64 state rows) per workgroup.  Eight waves (a whole d = 128
-    // state per workgroup) would share the key tile better, but must fit two
-    // waves per SIMD in 256 registers, where the compiler's allocation
-    // rewrites MFMA accumulator inputs early (see codegen_check).
-    return launch_chunk_states_nw<D, C, (D >= 64 ? 4 : D / 16), In>(a, s);
+    // Four waves (64 state rows) per workgroup at d >= 64.  At d = 128 the
+    // columns are split in two for fp32 inputs (whose unsplit G workgroup
+    // would need 103 KB of LDS, one workgroup per CU) and when whole column
+    // sets would leave fewer than two workgroups per CU.
+    constexpr int NW = D >= 64 ? 4 : D / 16;
+    if constexpr (D == 128) {
+        if (sizeof(In) == 4 || a.BH * K1Shape<D, C, NW, 1, sizeof(In) == 2>::PARTS < 512)
+            return launch_chunk_states_nw<D, C, NW, 2, In>(a, s);
+    }
+    return launch_chunk_states_nw<D, C, NW, 1, In>(a, s);
 }
 
 template <int D, typename In>

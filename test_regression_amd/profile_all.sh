@@ -1,24 +1,34 @@
 #!/bin/bash
 # Writes the committed profile summaries (profiles/*.json, profiles/*.txt) from
-# the rocprofv3 output of one profiling run of bench.py:
+# the rocprofv3 output of one profiling run of bench.py (R = repository root):
 #   trace:  cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o t -- python3 $R/bench.py
 #   counts: cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/prof_fetch -o f -- python3 $R/bench.py $SHORT
 #           cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/prof_write -o w -- python3 $R/bench.py $SHORT
-#   mfma:   cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU
-#             SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES GRBM_GUI_ACTIVE -f csv -d $R/gpurun_out/prof_mfma -o m -- python3 $R/bench.py $SHORT
-# with SHORT="--steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start".
+#   mfma:   cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16
+#             SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE
+#             -f csv -d $R/gpurun_out/prof_mfma -o m -- python3 $R/bench.py $SHORT
+# with SHORT="--steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start"
+# (profile_run.sh runs all four).  The headline forward is the first 4 dispatches of the bf16 CG
+# kernel in a SHORT run; the dynamic-stopping forward is the first 4 dispatches of the fp32 one.
 # Usage: bash test_regression_amd/profile_all.sh <rocprof output dir>   (run from the repository root)
 set -euo pipefail
 OUT=${1:-gpurun_out}
 F=$OUT/prof_fetch/f_counter_collection.csv
 W=$OUT/prof_write/w_counter_collection.csv
-CMD='cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start ; then the same with --pmc WRITE_SIZE'
+SHORT='--steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start'
+CMD="cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -- python3 \$R/bench.py $SHORT ; then the same with --pmc WRITE_SIZE"
 PS="python -m test_regression_amd.profile_summary traffic $F $W --copy-bytes 1073741824"
 C=test_regression_amd/csrc
-$PS --kernel "cg_split_kernel<128, 64>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
-    > profiles/cg_split_layer_bf16_d128_T4096_traffic.json
+K2="cg_h2_kernel<128, 64, mesa::bf16_t>"
+K2F="cg_h2_kernel<128, 64, float>"
+$PS --kernel "$K2" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
+    > profiles/cg_h2_layer_bf16_d128_T4096_traffic.json
+$PS --kernel "$K2F" --first 4 --command "$CMD; first 4 dispatches = the dynamic-stopping forward" \
+    > profiles/cg_h2_dynamic_f32_d128_T8192_traffic.json
 $PS --kernel "chunk_states_kernel<128, 64, 4, mesa::bf16_t>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_traffic.json
+$PS --kernel "chunk_states_kernel<128, 64, 4, float>" --first 4 --command "$CMD; first 4 dispatches = the dynamic-stopping forward" \
+    --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_dynamic_f32_d128_T8192_traffic.json
 $PS --kernel "decode_kernel<128, false, float>" --command "$CMD" --sources $C/decode.hip $C/mesa_device.h \
     > profiles/decode_f32_d128_N256_traffic.json
 $PS --kernel "qk_preprocess_kernel<128, mesa::bf16_t, mesa::bf16_t>" --command "$CMD" \
@@ -36,20 +46,25 @@ $PS --kernel "hawk_scan_kernel<mesa::bf16_t, 4>" --command "$CMD" --sources $C/h
     > profiles/hawk_scan_bf16_B8_T4096_D2048_traffic.json
 M=$OUT/prof_mfma/m_counter_collection.csv
 MA=$OUT/prof_mfma/m_agent_info.csv
-MCMD='cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES GRBM_GUI_ACTIVE -f csv -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start'
+MCMD="cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE -f csv -- python3 \$R/bench.py $SHORT"
 PM="python -m test_regression_amd.profile_summary mfma $M $MA"
-# algorithmic flops per launch at 8x16x4096, d=128, C=64, k=30 (524288 token-heads):
-#   CG/output: k(2d^2 + 2(C+1)d + 11d) + 2d^2 + 2(C+1)d per token-head; adjoint: k(...) + 2(2d^2 + 2(C+1)d)
-$PM --kernel "cg_split_kernel<128, 64>" --first 4 --alg-flops 825170591744 \
-    --command "$MCMD; first 4 dispatches = the headline forward" > profiles/cg_split_layer_bf16_d128_T4096_mfma.json
+# algorithmic flops per launch: headline 8x16x4096, d=128, C=64, k=30 (524288 token-heads):
+#   CG/output k(2d^2 + 2(C+1)d + 11d) + 2d^2 + 2(C+1)d per token-head; adjoint k(...) + 2(2d^2 + 2(C+1)d);
+#   dynamic 4x16x8192 (tol 1e-4): n_tok (2d^2 + 2(C+1)d) + sum_t n_t (2d^2 + 2(C+1)d + 11d) = 329013330944
+$PM --kernel "$K2" --first 4 --alg-flops 825170591744 \
+    --command "$MCMD; first 4 dispatches = the headline forward" > profiles/cg_h2_layer_bf16_d128_T4096_mfma.json
+$PM --kernel "$K2F" --first 4 --alg-flops 329013330944 \
+    --command "$MCMD; first 4 dispatches = the dynamic-stopping forward" > profiles/cg_h2_dynamic_f32_d128_T8192_mfma.json
 $PM --kernel "bwd_adjoint_split_kernel<128, 64>" --alg-flops 851074613248 --command "$MCMD" \
     --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_split.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_adjoint_layer_bf16_d128_T4096_mfma.json
 $PM --kernel "chunk_states_kernel<128, 64, 4, mesa::bf16_t>" --first 4 --command "$MCMD; first 4 dispatches = the headline forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_mfma.json
+$PM --kernel "chunk_states_kernel<128, 64, 4, float>" --first 4 --command "$MCMD; first 4 dispatches = the dynamic-stopping forward" \
+    --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_dynamic_f32_d128_T8192_mfma.json
 $PM --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$MCMD" --sources $C/bwd_kv.hip $C/mesa_device.h \
     > profiles/bwd_kv_layer_bf16_d128_T4096_mfma.json
 python -m test_regression_amd.profile_summary stats $OUT/prof_trace/t_kernel_stats.csv \
-    --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "cg_split_kernel<128, 64>" --first 13 \
-    --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o t -- python3 $R/bench.py   (R = repository root; default bench: headline forward 3 warmup + 10 timed steps, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, forward-for-training + backward, CPU baseline; the first 13 CG kernel dispatches are the headline forward)' \
+    --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "$K2" --first 13 \
+    --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o t -- python3 $R/bench.py   (R = repository root; default bench: headline forward 3 warmup + 10 timed steps, small workloads, forward-for-training + backward, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, CPU baseline; the first 13 bf16 CG kernel dispatches are the headline forward)' \
     > profiles/kernels_layer_bf16_d128_T4096_bench_stats.txt

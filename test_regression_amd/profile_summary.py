@@ -15,7 +15,7 @@ plain device copy of ``--copy-bytes`` bytes in the same run, and prints JSON
         --kernel NAME_SUBSTRING [--first N] [--command CMD] [--alg-flops F]
 
 ``mfma`` reads one ``--pmc`` run of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
-SQ_INSTS_VALU_MFMA_MOPS_F32, SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU,
+SQ_INSTS_VALU_MFMA_MOPS_F32, _BF16 and _F16 (any that were collected), SQ_INSTS_VALU,
 SQ_INSTS_LDS, SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE and prints, per
 dispatch of one kernel (median): the fraction of SIMD cycles the MFMA unit was
 busy (busy cycles over GRBM_GUI_ACTIVE per XCD times the SIMD count, the
@@ -146,6 +146,7 @@ def cmd_mfma(a):
     cycles = med(lambda d: d["GRBM_GUI_ACTIVE"] / nxcc)
     mops = med(lambda d: d.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0))
     mops_bf = med(lambda d: d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))
+    mops_h = med(lambda d: d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0))
     ns = med(lambda d: d["ns"])
     out = {
         "kernel": a.kernel, "command": a.command, "kernel_source_hash": cg_source_hash(a.sources),
@@ -156,6 +157,7 @@ def cmd_mfma(a):
         "mfma_busy_frac": round(med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / nxcc * nsimd)), 4),
         "mfma_f32_issued_flops": mops * 512,
         "mfma_bf16_issued_flops": mops_bf * 512,
+        "mfma_f16_issued_flops": mops_h * 512,
         "valu_instructions": med(lambda d: d["SQ_INSTS_VALU"]),
         "lds_instructions": med(lambda d: d["SQ_INSTS_LDS"]),
         "lds_bank_conflict_frac": round(med(lambda d: d["SQ_LDS_BANK_CONFLICT"] / d["SQ_LDS_IDX_ACTIVE"]
@@ -163,7 +165,7 @@ def cmd_mfma(a):
     }
     if a.alg_flops:
         out["algorithmic_flops"] = a.alg_flops
-        out["issued_mfma_over_algorithmic"] = round((mops + mops_bf) * 512 / a.alg_flops, 4)
+        out["issued_mfma_over_algorithmic"] = round((mops + mops_bf + mops_h) * 512 / a.alg_flops, 4)
     print(json.dumps(out, indent=1))
 
 

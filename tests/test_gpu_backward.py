@@ -133,27 +133,28 @@ def test_backward_edge_cases(dtype):
     assert not r["grad_lambda"].any()
 
 
-def test_backward_layer_shape_sampled_heads():
+@pytest.mark.timeout(600)
+def test_backward_layer_shape_full():
     """The headline layer (8 x 16 x 4096, d=128, bf16, k=30) backward at full
-    size; four heads against the oracle (which also gives dlambda per head)."""
+    size against the oracle on every head: dq, dk, dv, dgamma per head and
+    dlambda, which sums each head over the batch, compared whole."""
     w = inputs.WORKLOADS["layer_bf16_d128_T4096_k30"]
     say("case backward layer", w.name)
     x = inputs.forward_inputs(w)
     x["gout"] = np.random.default_rng(w.seed + 9).standard_normal((w.B, w.H, w.T, w.d)).astype(np.float32)
     gpu = gpu_backward(x, w.dtype, w.max_iters, w.tol, w.chunk)
-    for (b, h) in ((0, 0), (2, 5), (5, 11), (7, 15)):
-        ref = oracle_backward(x, w.dtype, w.max_iters, w.tol, heads=(b, h))
-        sub = {n: gpu[n][b:b + 1, h:h + 1] for n in ("dq", "dk", "dv", "dgamma")}
-        errs = {n: rel_l2(sub[n], ref[n]) for n in sub}
-        errs["dgamma"] = rel_l2(sub["dgamma"][:, :, 1:], ref["dgamma"][:, :, 1:])
-        say(f"  head ({b},{h}) " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
-        for n, e in errs.items():
-            assert e <= RTOL[w.dtype], (n, e)
-        assert (gpu["z_iters"][b, h] == w.max_iters).all()
-    # dlambda sums every head of the batch: check it against its definition
-    # -sum z (.) x with the GPU's own z (= dq) and the oracle's x is covered by
-    # the small cases; here it must at least be finite and of the right shape
-    assert np.isfinite(gpu["dlam"]).all() and gpu["dlam"].shape == (w.H, w.d)
+    say("  gpu done, oracle on all heads")
+    ref = oracle_backward(x, w.dtype, w.max_iters, w.tol)
+    errs = {n: rel_l2(gpu[n], ref[n]) for n in ("dq", "dk", "dv", "dlam")}
+    errs["dgamma"] = rel_l2(gpu["dgamma"][:, :, 1:], ref["dgamma"][:, :, 1:])
+    worst = {n: max(rel_l2(gpu[n][:, h], ref[n][:, h]) for h in range(w.H)) for n in ("dq", "dk", "dv")}
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items())
+        + " | worst head " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
+    for n, e in errs.items():
+        assert e <= RTOL[w.dtype], (n, e)
+    g0 = np.abs(gpu["dgamma"][:, :, 0]).max()
+    assert g0 <= 1e-4 * (1.0 + np.abs(ref["dgamma"]).max()), g0
+    assert (gpu["z_iters"] == w.max_iters).all() and (ref["z_iters"] == w.max_iters).all()
 
 
 def test_backward_garbage_workspace_and_reuse():
