@@ -86,14 +86,18 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 //   bf16: row p holds token pair (2p, 2p + 1); word (p, f) = feature f of
 //         token 2p (low half) and 2p + 1 (high half).  The pitch F + 8 puts
 //         the four lane groups' rows (2 pairs apart) 16 banks apart.
-//   fp32: row i holds token i; pitch lds_pitch(F).
+//   fp32: feature-major, row f holds feature f of the C tokens, so that a
+//         lane's four consecutive tokens are one 16-byte read.  The pitch
+//         (C rounded up to 64, plus 8) is the one a probe of gfx950's LDS
+//         measured free of bank conflicts for 16-byte reads where 16 lanes
+//         take 16 consecutive rows (a pitch of 64 + 4 lost 17% of the cycles).
 template <int F, int C, bool BF>
 struct StageTile {
-    static constexpr int FG = F / 4;                        // 4-feature groups of a row
-    static constexpr int ROWS = BF ? C / 2 : C;
-    static constexpr int PITCH = BF ? F + 8 : lds_pitch(F); // 32-bit words
-    static constexpr int WORDS = ROWS * PITCH;
-    static constexpr int UNITS = ROWS * FG;                 // one 16-byte LDS write each
+    static constexpr int FG = F / 4;                        // 4-feature groups of a token
+    static constexpr int PITCH = BF ? F + 8 : (C + 63) / 64 * 64 + 8;   // 32-bit words per LDS row
+    static constexpr int WORDS = (BF ? C / 2 : F) * PITCH;
+    // bf16: a token pair x 4 features; fp32: 4 tokens x 4 features
+    static constexpr int UNITS = (BF ? C / 2 : C / 4) * FG;
 };
 
 template <int D, int C, int NW, int CS, bool BF>
@@ -124,11 +128,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t k1_rsrc(const void* base, int 
 }
 
 // Per-thread offsets of one staged region's units: the byte offset of the
-// unit within a chunk's rows of the input and its LDS word offset.  bf16
-// units are a token pair x 4 features (two 8-byte loads, one 16-byte LDS
-// write), fp32 units one token x 4 features.  Unit indices past the region
-// are clamped onto its last unit, whose LDS write then repeats with the same
-// data.
+// unit within a chunk's rows of the input and its LDS word offset.  Unit
+// indices past the region are clamped onto its last unit, whose LDS write
+// then repeats with the same data.
+//   bf16: a token pair x 4 features, 4-feature groups fastest (a wave reads
+//         whole pair rows): two 8-byte loads, one 16-byte LDS write.
+//   fp32: 4 tokens x 4 features (four 16-byte loads, one per token), with
+//         eight token quads fastest, so that a wave reads 128-byte pieces of
+//         8 rows and its four 16-byte LDS writes (one per feature row, four
+//         tokens each) go to eight distinct 16-byte slots per lane octet.
 template <typename Tl, int NTHR, int D, int ES>
 struct UnitOffsets {
     static constexpr int U = (Tl::UNITS + NTHR - 1) / NTHR;
@@ -137,15 +145,23 @@ struct UnitOffsets {
 #pragma unroll
         for (int e = 0; e < U; ++e) {
             const int u = min(tid + e * NTHR, Tl::UNITS - 1);
-            const int row = u / Tl::FG, fg = u % Tl::FG;
-            g[e] = ((ES == 2 ? 2 * row : row) * D + f0 + 4 * fg) * ES;
-            l[e] = row * Tl::PITCH + 4 * fg;
+            if constexpr (ES == 2) {
+                const int row = u / Tl::FG, fg = u % Tl::FG;
+                g[e] = (2 * row * D + f0 + 4 * fg) * ES;
+                l[e] = row * Tl::PITCH + 4 * fg;
+            } else {
+                constexpr int TQ = Tl::UNITS / Tl::FG;           // token quads
+                constexpr int QL = TQ < 8 ? TQ : 8;
+                const int tq = (u / (QL * Tl::FG)) * QL + u % QL, fg = (u / QL) % Tl::FG;
+                g[e] = (4 * tq * D + f0 + 4 * fg) * ES;
+                l[e] = 4 * fg * Tl::PITCH + 4 * tq;
+            }
         }
     }
 };
 
 template <typename Tl, int NTHR, int D, typename In, typename Ld>
-__device__ __forceinline__ void k1_load(Ld (&r)[(Tl::UNITS + NTHR - 1) / NTHR][sizeof(In) == 2 ? 2 : 1],
+__device__ __forceinline__ void k1_load(Ld (&r)[(Tl::UNITS + NTHR - 1) / NTHR][sizeof(In) == 2 ? 2 : 4],
                                         __amdgpu_buffer_rsrc_t rs, const UnitOffsets<Tl, NTHR, D, sizeof(In)>& o) {
     constexpr int U = (Tl::UNITS + NTHR - 1) / NTHR;
 #pragma unroll
@@ -154,14 +170,16 @@ __device__ __forceinline__ void k1_load(Ld (&r)[(Tl::UNITS + NTHR - 1) / NTHR][s
             r[e][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.g[e], 0, 0));
             r[e][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.g[e] + 2 * D, 0, 0));
         } else {
-            r[e][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.g[e], 0, 0));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[e][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.g[e] + q * 4 * D, 0, 0));
         }
     }
 }
 
 // Write the loaded units into LDS (rows past the sequence arrived as zeros).
 template <typename Tl, int NTHR, int D, typename In, typename Ld>
-__device__ __forceinline__ void k1_stage(const Ld (&r)[(Tl::UNITS + NTHR - 1) / NTHR][sizeof(In) == 2 ? 2 : 1],
+__device__ __forceinline__ void k1_stage(const Ld (&r)[(Tl::UNITS + NTHR - 1) / NTHR][sizeof(In) == 2 ? 2 : 4],
                                          float* dst, const UnitOffsets<Tl, NTHR, D, sizeof(In)>& o) {
     constexpr int U = (Tl::UNITS + NTHR - 1) / NTHR;
 #pragma unroll
@@ -174,35 +192,49 @@ __device__ __forceinline__ void k1_stage(const Ld (&r)[(Tl::UNITS + NTHR - 1) / 
                             (x.y & 0xffffu) | (y.y << 16), (x.y >> 16) | (y.y & 0xffff0000u)};
             *reinterpret_cast<u32x4v*>(dst + o.l[e]) = wd;
         } else {
-            *reinterpret_cast<f32x4*>(dst + o.l[e]) = r[e][0];
+            // feature row 4 fg + j gets tokens 4 tq .. 4 tq + 3
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(dst + o.l[e] + j * Tl::PITCH) =
+                    f32x4{r[e][0][j], r[e][1][j], r[e][2][j], r[e][3][j]};
         }
     }
 }
 
-// The per-wave chunk walk.  KIND 0: H tiles (a pair of row blocks, TW tiles
-// starting at tile T0 of the pair's list); KIND 1: G^T (or G) tiles (one row
-// block, TW column tiles).  WRITE: store the chunk states.
-template <int D, int C, int NW, int CS, typename In, int KIND, int TW, int T0, bool WRITE>
+// The per-wave chunk walk.  KIND 0: H tiles (TW tiles starting at tile T0
+// of the list of row-block pair pr); KIND 1: G^T (or G) tiles (row block
+// grow, column tiles gcol0 ..).  WRITE: store the chunk states.
+// MODE 0: the workgroup stages only the rows and columns of its own kind
+// (H: the key tile; G: fA.. of the row source, fB.. of the column source).
+// MODE 1: the workgroup stages the whole key and value tiles and mixes H and
+// G waves (fA = fB = 0).
+template <int D, int C, int NW, int CS, typename In, int KIND, int TW, int T0, bool WRITE, int MODE>
 __device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, const In* __restrict__ v,
                                                   const float* __restrict__ gamma, int T, int n_chunks,
                                                   float* __restrict__ Sout, float* __restrict__ final_S,
-                                                  int g_transposed, long bh, int rb, int cs, float* lds) {
+                                                  int g_transposed, long bh, int pr, int grow, int gcol0, int fA,
+                                                  int fB, float* lds) {
     constexpr bool BF = sizeof(In) == 2;
     using S = K1Shape<D, C, NW, CS, BF>;
     constexpr int NT = S::NT;
     constexpr int NTHR = 64 * NW;
     constexpr int HPACK = D * (D + 16) / 2;    // floats of a packed upper block triangle
     using Ld = std::conditional_t<BF, uint2, f32x4>;
-    constexpr int NL = BF ? 2 : 1;
-    // staged regions: H one key region (rows and columns), G a row region and a column region
-    using TA = std::conditional_t<KIND == 0, typename S::KT, typename S::AT>;
-    using TB = std::conditional_t<KIND == 0, typename S::KT, typename S::BT>;
-    constexpr int UA = KIND == 0 ? 1 : (TA::UNITS + NTHR - 1) / NTHR;   // (unused for H)
+    constexpr int NL = BF ? 2 : 4;
+    // staged regions: MODE 0 H one key region (rows and columns), G a row
+    // region and a column region; MODE 1 the key region, then the value region
+    using TA = std::conditional_t<KIND == 0 || MODE == 1, typename S::KT, typename S::AT>;
+    using TB = std::conditional_t<KIND == 0 || MODE == 1, typename S::KT, typename S::BT>;
+    constexpr bool LOADA = MODE == 1 || KIND == 1;
+    constexpr int UA = LOADA ? (TA::UNITS + NTHR - 1) / NTHR : 1;
     constexpr int UB = (TB::UNITS + NTHR - 1) / NTHR;
-    constexpr int AOFF = 0;
-    constexpr int BOFF = KIND == 0 ? 0 : TA::WORDS;
-    constexpr int WOFF = BOFF + TB::WORDS;     // weights e^{l_end - l_i}, then e^{l_end}
+    constexpr int BUF = MODE == 1 ? 2 * S::KT::WORDS + C + 4 : S::BUF;
+    constexpr int WOFF = MODE == 1 ? 2 * S::KT::WORDS : (KIND == 0 ? 0 : TA::WORDS) + TB::WORDS;
     constexpr int NR = KIND == 0 && NT > 1 ? 2 : 1;   // row blocks a wave's tiles come from
+    const bool gt = KIND == 1 && g_transposed;
+    // region offsets of the A and B operands (MODE 1: key region 0, value region 1)
+    const int AOFF = MODE == 1 ? (gt ? S::KT::WORDS : 0) : 0;
+    const int BOFF = MODE == 1 ? (KIND == 0 || gt ? 0 : S::KT::WORDS) : (KIND == 0 ? 0 : TA::WORDS);
 
     typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
     const int tid0 = threadIdx.x;
@@ -211,27 +243,26 @@ __device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, cons
     const int n = lane & 15, kk = lane >> 4;
 
     // this wave's tiles: row blocks r0 (tiles t' < split) and r1, column of tile t' = T0 + t
-    const bool active = KIND == 1 || S::PAIRS == NW || w < S::PAIRS;
-    const int r0 = KIND == 0 ? w : rb * NW + w;
-    const int r1 = KIND == 0 ? NT - 1 - w : r0;
-    const int split = KIND == 0 ? NT - w : TW + T0;
+    const bool active = KIND == 1 || MODE == 1 || S::PAIRS == NW || w < S::PAIRS;
+    const int r0 = KIND == 0 ? pr : grow;
+    const int r1 = KIND == 0 ? NT - 1 - pr : grow;
+    const int split = KIND == 0 ? NT - pr : TW + T0;
     auto tile_first = [&](int t) { return T0 + t < split; };
     auto tile_col = [&](int t) {
-        if constexpr (KIND == 0) return T0 + t < split ? w + T0 + t : T0 + t - 1;
-        else return cs * S::NTW + t;
+        if constexpr (KIND == 0) return T0 + t < split ? pr + T0 + t : T0 + t - 1;
+        else return gcol0 + t;
     };
-    // A operand feature offset of row block r in its region
-    auto a_off = [&](int r) { return KIND == 0 ? 16 * r : 16 * w; };
-    // B operand feature offset of tile t in its region
-    auto b_off = [&](int t) { return KIND == 0 ? 16 * tile_col(t) : 16 * t; };
+    // A operand feature offset of row block r in its region; B operand of tile t
+    auto a_off = [&](int r) { return 16 * r - fA; };
+    auto b_off = [&](int t) { return 16 * tile_col(t) - fB; };
 
-    const bool gt = KIND == 1 && g_transposed;
     constexpr int ES = sizeof(In);
-    const In* srcA = (gt ? v : k) + (size_t)bh * T * D;
-    const In* srcB = (KIND == 0 || gt ? k : v) + (size_t)bh * T * D;
+    // MODE 1: A loads the keys and B the values; MODE 0: each its operand's source
+    const In* srcA = (MODE == 1 ? k : gt ? v : k) + (size_t)bh * T * D;
+    const In* srcB = (MODE == 1 ? v : KIND == 0 || gt ? k : v) + (size_t)bh * T * D;
     const float* gh = gamma + (size_t)bh * T;
-    const UnitOffsets<TA, NTHR, D, ES> oA(KIND == 0 ? 0 : rb * 16 * NW, tid0);
-    const UnitOffsets<TB, NTHR, D, ES> oB(KIND == 0 ? 0 : cs * (D / CS), tid0);
+    const UnitOffsets<TA, NTHR, D, ES> oA(fA, tid0);
+    const UnitOffsets<TB, NTHR, D, ES> oB(fB, tid0);
 
     f32x4 acc[TW];
 #pragma unroll
@@ -243,16 +274,17 @@ __device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, cons
         // the chunk's rows as a buffer: rows past the sequence read as zeros
         const int t0 = min(c, n_chunks - 1) * C;
         const int rows = min(C, T - t0);
-        if constexpr (KIND == 1) k1_load<TA, NTHR, D, In>(ra[sl], k1_rsrc(srcA + (size_t)t0 * D, rows * D * ES), oA);
+        if constexpr (LOADA) k1_load<TA, NTHR, D, In>(ra[sl], k1_rsrc(srcA + (size_t)t0 * D, rows * D * ES), oA);
         k1_load<TB, NTHR, D, In>(rbv[sl], k1_rsrc(srcB + (size_t)t0 * D, rows * D * ES), oB);
         greg[sl] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(k1_rsrc(gh + t0, rows * 4),
                                                                                   (tid0 & 63) * 4, 0, 0));
     };
     auto stage = [&](int c, int sl, int buf) {
-        float* base = lds + buf * S::BUF;
+        float* base = lds + buf * BUF;
         const int valid = min(C, T - c * C);
-        if constexpr (KIND == 1) k1_stage<TA, NTHR, D, In>(ra[sl], base + AOFF, oA);
-        k1_stage<TB, NTHR, D, In>(rbv[sl], base + BOFF, oB);
+        // MODE 1: keys into region 0, values into region 1
+        if constexpr (LOADA) k1_stage<TA, NTHR, D, In>(ra[sl], base + (MODE == 1 ? 0 : AOFF), oA);
+        k1_stage<TB, NTHR, D, In>(rbv[sl], base + (MODE == 1 ? S::KT::WORDS : BOFF), oB);
         // within-chunk log decays (tokens past the end count as gamma = 1):
         // an inclusive scan over the wave on DPP moves, computed by every
         // wave (no branch around it) and written by wave 0
@@ -264,7 +296,8 @@ __device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, cons
         }
     };
     auto store_states = [&](int c) {
-        // one 16-byte piece per lane per 16 x 16 block, non-temporal
+        // one 16-byte piece per lane per 16 x 16 block (non-temporal for fp32
+        // inputs; plain write-back stores measured faster with bf16 inputs)
         constexpr int SB = (KIND == 0 ? HPACK : D * D) * 4;
         const __amdgpu_buffer_rsrc_t rs = k1_rsrc(Sout + (size_t)c * (SB / 4), SB);
 #pragma unroll
@@ -273,14 +306,14 @@ __device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, cons
             // G: block (row, col) of the slab's matrix in accumulator order =
             // block (col, row) of its transpose in operand order
             const int blk = KIND == 0 ? packed_blk<NT>(row, col) : (col * NT + row) * 256;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, acc[t]), rs, lane * 16, blk * 4, 2);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, acc[t]), rs, lane * 16, blk * 4, BF ? 0 : 2);
         }
     };
     auto multiply = [&](int buf) {
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         const int ln = tid & 63, nn = ln & 15, kq = ln >> 4;
-        const float* base = lds + buf * S::BUF;
+        const float* base = lds + buf * BUF;
         const float* sA = base + AOFF;
         const float* sB = base + BOFF;
         const float* sW = base + WOFF;
@@ -352,20 +385,23 @@ __device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, cons
                 }
             }
         } else {
+            // MFMA (g, s) contracts over tokens 16 g + 4 kq + s (kq = 0..3):
+            // a lane's operands for s = 0..3 are four consecutive tokens of
+            // one feature row, one 16-byte read each.
 #pragma unroll
             for (int g = 0; g < C / 16; ++g) {
+                const int i0 = 16 * g + 4 * kq;
+                const f32x4 wv = *reinterpret_cast<const f32x4*>(&sW[i0]);
+                f32x4 a[NR];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int i = 16 * g + 4 * kq + s;
-                    float a[NR];
+                for (int ri = 0; ri < NR; ++ri)
+                    a[ri] = *reinterpret_cast<const f32x4*>(&sA[(a_off(ri == 0 ? r0 : r1) + nn) * TA::PITCH + i0]) * wv;
 #pragma unroll
-                    for (int ri = 0; ri < NR; ++ri)
-                        a[ri] = sA[i * TA::PITCH + a_off(ri == 0 ? r0 : r1) + nn] * sW[i];
+                for (int t = 0; t < TW; ++t) {
+                    const bool f = NR == 1 || tile_first(t);
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(&sB[(b_off(t) + nn) * TB::PITCH + i0]);
 #pragma unroll
-                    for (int t = 0; t < TW; ++t) {
-                        const bool f = NR == 1 || tile_first(t);
-                        U[t] = mfma4(f ? a[0] : a[NR - 1], sB[i * TB::PITCH + b_off(t) + nn], U[t]);
-                    }
+                    for (int s = 0; s < 4; ++s) U[t] = mfma4(f ? a[0][s] : a[NR - 1][s], b[s], U[t]);
                 }
             }
         }
@@ -374,21 +410,24 @@ __device__ __forceinline__ void chunk_states_walk(const In* __restrict__ k, cons
         for (int t = 0; t < TW; ++t) acc[t] = G * acc[t] + U[t];
     };
 
-    // Pipeline: chunk c + 1 is staged (buffer (c+1) & 1) and chunk c + 3
-    // loaded (register slot (c+1) & 1) while chunk c is multiplied from
-    // buffer c & 1; one barrier per chunk.
+    // Pipeline, one barrier per chunk: chunk c is multiplied from buffer
+    // c & 1, then chunk c + 1 (loaded two steps earlier into register slot
+    // (c+1) & 1) is staged into the other buffer -- its vector work and LDS
+    // writes can run under the tail of the MFMA chain -- and chunk c + 3's
+    // loads go into the freed slot.  At the last chunk the staging repeats
+    // chunk n - 1 into a buffer no wave reads any more.
     load(0, 0);
     load(1, 1);
     stage(0, 0, 0);
     load(2, 0);
     __syncthreads();
     auto step = [&](int c, int sl, int buf) {
-        if (c + 1 < n_chunks) stage(c + 1, sl, buf ^ 1);
-        load(c + 3, sl);
         if (active) {
             if constexpr (WRITE) store_states(c);
             multiply(buf);
         }
+        stage(c + 1, sl, buf ^ 1);
+        load(c + 3, sl);
         __syncthreads();
     };
     for (int c = 0; c < n_chunks; c += 2) {
@@ -437,18 +476,63 @@ __global__ __launch_bounds__(64 * NW) void chunk_states_kernel(
     constexpr int HPACK = D * (D + 16) / 2;
     float* SHh = WRITE ? SH + (size_t)bh * n_chunks * HPACK : nullptr;
     float* SGh = WRITE ? SG + (size_t)bh * n_chunks * D * D : nullptr;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (part < S::HPARTS) {
+        // wave w: row-block pair (w, NT-1-w)
         if (part == 0)
-            chunk_states_walk<D, C, NW, CS, In, 0, S::HT0, 0, WRITE>(k, v, gamma, T, n_chunks, SHh, final_H, 0,
-                                                                     bh, 0, 0, lds);
+            chunk_states_walk<D, C, NW, CS, In, 0, S::HT0, 0, WRITE, 0>(k, v, gamma, T, n_chunks, SHh, final_H, 0,
+                                                                        bh, w, 0, 0, 0, 0, lds);
         else if constexpr (S::HT1 > 0)
-            chunk_states_walk<D, C, NW, CS, In, 0, S::HT1, S::HT0, WRITE>(k, v, gamma, T, n_chunks, SHh, final_H,
-                                                                          0, bh, 0, 0, lds);
+            chunk_states_walk<D, C, NW, CS, In, 0, S::HT1, S::HT0, WRITE, 0>(k, v, gamma, T, n_chunks, SHh,
+                                                                             final_H, 0, bh, w, 0, 0, 0, 0, lds);
     } else {
-        const int g = part - S::HPARTS;
-        chunk_states_walk<D, C, NW, CS, In, 1, S::NTW, 0, WRITE>(k, v, gamma, T, n_chunks, SGh, final_G,
-                                                                 g_transposed, bh, g / CS, g % CS, lds);
+        // row block rb * NW + w, column tiles cs * NTW ..
+        const int g = part - S::HPARTS, rb = g / CS, cs = g % CS;
+        chunk_states_walk<D, C, NW, CS, In, 1, S::NTW, 0, WRITE, 0>(
+            k, v, gamma, T, n_chunks, SGh, final_G, g_transposed, bh, 0, rb * NW + w, cs * S::NTW, rb * 16 * NW,
+            cs * (D / CS), lds);
     }
+}
+
+// d = 128 with fp32 keys and values: four workgroups of eight waves per
+// head, each staging the whole key and value tiles (the fp32 products run
+// at the fp32 MFMA rate, so the work is spread evenly over the SIMDs: one
+// workgroup per CU, two waves per SIMD).  Workgroup q takes row-block pair
+// (q, 7-q) of H, its nine tiles split 3/2/2/2 over waves 0-3, and row blocks
+// 2q, 2q+1 of G^T in halves of four column tiles on waves 4-7, so that the
+// two waves of a SIMD (w and w+4) hold six or seven tiles.
+template <int C, typename In, bool WRITE>
+__global__ __launch_bounds__(512) void chunk_states_full_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma, int T, int n_chunks,
+    float* __restrict__ SH, float* __restrict__ SG, float* __restrict__ final_H, float* __restrict__ final_G,
+    long BH, int* __restrict__ work_counter, int g_transposed) {
+    constexpr int D = 128;
+    using S = K1Shape<D, C, 8, 1, sizeof(In) == 2>;
+    __shared__ alignas(16) float lds[2 * (2 * S::KT::WORDS + C + 4)];
+    if (work_counter && blockIdx.x == 0 && threadIdx.x == 0) *work_counter = 0;
+    // the 4 workgroups of head bh on one XCD
+    const long xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const long bh = (slot / 4) * 8 + xcd;
+    const int q = (int)(slot % 4);
+    if (bh >= BH) return;
+    constexpr int HPACK = D * (D + 16) / 2;
+    float* SHh = WRITE ? SH + (size_t)bh * n_chunks * HPACK : nullptr;
+    float* SGh = WRITE ? SG + (size_t)bh * n_chunks * D * D : nullptr;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#define K1_H(TW, T0)                                                                                            \
+    chunk_states_walk<D, C, 8, 1, In, 0, TW, T0, WRITE, 1>(k, v, gamma, T, n_chunks, SHh, final_H, 0, bh, q, 0, 0, \
+                                                            0, 0, lds)
+    switch (w) {
+        case 0: K1_H(3, 0); break;
+        case 1: K1_H(2, 3); break;
+        case 2: K1_H(2, 5); break;
+        case 3: K1_H(2, 7); break;
+        default:
+            chunk_states_walk<D, C, 8, 1, In, 1, 4, 0, WRITE, 1>(k, v, gamma, T, n_chunks, SGh, final_G,
+                                                                 g_transposed, bh, 0, 2 * q + ((w - 4) >> 1),
+                                                                 ((w - 4) & 1) * 4, 0, 0, lds);
+    }
+#undef K1_H
 }
 
 template <int D, int C, int NW, int CS, typename In>
@@ -474,11 +558,22 @@ hipError_t launch_chunk_states_t(const ChunkStatesArgs& a, hipStream_t s) {
     // would need 103 KB of LDS, one workgroup per CU) and when whole column
     // sets would leave fewer than two workgroups per CU.
     constexpr int NW = D >= 64 ? 4 : D / 16;
-    if constexpr (D == 128) {
-        if (sizeof(In) == 4 || a.BH * K1Shape<D, C, NW, 1, sizeof(In) == 2>::PARTS < 512)
-            return launch_chunk_states_nw<D, C, NW, 2, In>(a, s);
+    if constexpr (D == 128 && sizeof(In) == 4) {
+        const long grid = ((a.BH + 7) / 8) * 8 * 4;
+        if (a.write_chunks)
+            hipLaunchKernelGGL((chunk_states_full_kernel<C, In, true>), dim3((unsigned)grid), dim3(512), 0, s,
+                               (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG, a.final_H,
+                               a.final_G, a.BH, a.work_counter, a.g_transposed);
+        else
+            hipLaunchKernelGGL((chunk_states_full_kernel<C, In, false>), dim3((unsigned)grid), dim3(512), 0, s,
+                               (const In*)a.k, (const In*)a.v, a.gamma, a.T, a.n_chunks, a.SH, a.SG, a.final_H,
+                               a.final_G, a.BH, a.work_counter, a.g_transposed);
+        return hipGetLastError();
+    } else {
+        if constexpr (D == 128)
+            if (a.BH * K1Shape<D, C, NW, 1, true>::PARTS < 512) return launch_chunk_states_nw<D, C, NW, 2, In>(a, s);
+        return launch_chunk_states_nw<D, C, NW, 1, In>(a, s);
     }
-    return launch_chunk_states_nw<D, C, NW, 1, In>(a, s);
 }
 
 template <int D, typename In>
