@@ -510,6 +510,11 @@ __global__ __launch_bounds__(512) void chunk_states_full_kernel(
     using S = K1Shape<D, C, 8, 1, sizeof(In) == 2>;
     __shared__ alignas(16) float lds[2 * (2 * S::KT::WORDS + C + 4)];
     if (work_counter && blockIdx.x == 0 && threadIdx.x == 0) *work_counter = 0;
+    // An (empty) accumulator-register clobber: it makes the compiler keep the
+    // MFMA accumulators in AGPRs.  Without it this 512-thread kernel gets the
+    // all-VGPR MFMA form, where accumulator inputs are rewritten a few wait
+    // states after issue (the pattern codegen_check rejects).
+    asm volatile("" ::: "a0");
     // the 4 workgroups of head bh on one XCD
     const long xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
     const long bh = (slot / 4) * 8 + xcd;
