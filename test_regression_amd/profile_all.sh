@@ -25,9 +25,9 @@ $PS --kernel "$K2" --first 4 --command "$CMD; first 4 dispatches = the headline 
     > profiles/cg_h2_layer_bf16_d128_T4096_traffic.json
 $PS --kernel "$K2F" --first 4 --command "$CMD; first 4 dispatches = the dynamic-stopping forward" \
     > profiles/cg_h2_dynamic_f32_d128_T8192_traffic.json
-$PS --kernel "chunk_states_kernel<128, 64, 4, mesa::bf16_t>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
+$PS --kernel "chunk_states_kernel<128, 64, 4, 2, mesa::bf16_t, true>" --first 4 --command "$CMD; first 4 dispatches = the headline forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_traffic.json
-$PS --kernel "chunk_states_kernel<128, 64, 4, float>" --first 4 --command "$CMD; first 4 dispatches = the dynamic-stopping forward" \
+$PS --kernel "chunk_states_full_kernel<64, float, true>" --first 4 --command "$CMD; first 4 dispatches = the dynamic-stopping forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_dynamic_f32_d128_T8192_traffic.json
 $PS --kernel "decode_kernel<128, false, float>" --command "$CMD" --sources $C/decode.hip $C/mesa_device.h \
     > profiles/decode_f32_d128_N256_traffic.json
@@ -58,9 +58,9 @@ $PM --kernel "$K2F" --first 4 --alg-flops 329013330944 \
 $PM --kernel "bwd_adjoint_split_kernel<128, 64>" --alg-flops 851074613248 --command "$MCMD" \
     --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_split.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_adjoint_layer_bf16_d128_T4096_mfma.json
-$PM --kernel "chunk_states_kernel<128, 64, 4, mesa::bf16_t>" --first 4 --command "$MCMD; first 4 dispatches = the headline forward" \
+$PM --kernel "chunk_states_kernel<128, 64, 4, 2, mesa::bf16_t, true>" --first 4 --command "$MCMD; first 4 dispatches = the headline forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_mfma.json
-$PM --kernel "chunk_states_kernel<128, 64, 4, float>" --first 4 --command "$MCMD; first 4 dispatches = the dynamic-stopping forward" \
+$PM --kernel "chunk_states_full_kernel<64, float, true>" --first 4 --command "$MCMD; first 4 dispatches = the dynamic-stopping forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_dynamic_f32_d128_T8192_mfma.json
 $PM --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$MCMD" --sources $C/bwd_kv.hip $C/mesa_device.h \
     > profiles/bwd_kv_layer_bf16_d128_T4096_mfma.json
