@@ -15,8 +15,9 @@
 // Work split: one workgroup per (head, chunk); wave w owns keys 16w..16w+15
 // and holds their k_i, v_i in registers as the MFMA B operand (lane (n, kk):
 // features 16j + 4kk + r of key n).  The state terms come first: the
-// reverse-state kernel stores each state's blocks in both MFMA orders, so
-// P rows and P columns are A operands read straight from memory, while the
+// reverse-state kernel stores P^gx's blocks in both MFMA orders and the
+// symmetric M = P^zx + (P^zx)^T once, so P rows, P columns and M rows are A
+// operands read straight from memory, while the
 // chunk's x, z, g rows travel from memory into LDS by direct loads.  Then
 // the within-chunk sums: scores come out of the MFMA in exactly the layout
 // the next contraction (over tokens) takes as its B operand, so the token
@@ -101,9 +102,11 @@ __device__ __forceinline__ void state_terms(const float* __restrict__ Pg, const 
 #pragma unroll
             for (int j = 0; j < NT; ++j) A2[j] = mfma4(bg[g & 1][j][s], Vb[g][s], A2[j]);
     }
+    // rows of M = P^zx + (P^zx)^T: M's operand-order block (j, g) is its
+    // stored accumulator-order block (g, j), M being symmetric
     auto load_z = [&](int g, int buf) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) bg[buf][j] = ld(pz + DD + (j * NT + g) * 256) + ld(pz + (g * NT + j) * 256);
+        for (int j = 0; j < NT; ++j) bg[buf][j] = ld(pz + (g * NT + j) * 256);
     };
     load_z(0, 0);
 #pragma unroll
@@ -246,7 +249,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
     const int t0 = c * C;
     const int valid = min(C, T - t0);
     const size_t tok0 = (size_t)bh * T + t0;
-    const size_t soff = ((size_t)bh * n_chunks + c) * 2 * D * D;   // both block orders per chunk
+    const size_t soff = ((size_t)bh * n_chunks + c) * 2 * D * D;   // P^gx: both block orders per chunk
+    const size_t moff = ((size_t)bh * n_chunks + c) * D * D;       // M: accumulator order
 
     // ---- x, z, g rows of the chunk straight into LDS (rows past the end zeroed); l ----
     // One row per wave instruction: lanes 0..D/4-1 each move 16 bytes.
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
     }
 
     const float* pg = Pgx + soff;
-    const float* pz = Pzx + soff;
+    const float* pz = Pzx + moff;
     if (w == 0) {
         kv_wave<D, C, 0, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
     } else if constexpr (NW > 1) {

@@ -11,18 +11,23 @@
 // (e_c the chunk's last token, L the prefix sum of ln gamma), which obey,
 // walking the chunks backwards with l the within-chunk prefix sums,
 //   P_{c-1} = e^{l_end} P_c + sum_{t in c} e^{l_t} a_t x_t^T     (a = g or z).
-// This kernel produces P^gx_c and P^zx_c for every chunk (P of the last chunk
-// is zero).  Work split as the forward's chunk-state kernel: one workgroup per
-// (head, {gx, zx}, row block), each wave a 16 x D slab of the running state in
-// MFMA accumulators, the rank-C update a fresh v_mfma_f32_16x16x4_f32 chain.
+// The key gradient needs P^zx only through its symmetric part, so this kernel
+// produces P^gx_c and M_c = P^zx_c + (P^zx_c)^T for every chunk (both zero
+// after the last chunk); M obeys the same recurrence with the rank-2C update
+// sum_t e^{l_t} (z_t x_t^T + x_t z_t^T).  Work split as the forward's
+// chunk-state kernel: one workgroup per (head, {gx, zx}, row block), each wave
+// a 16 x D slab of the running state in MFMA accumulators, the update a fresh
+// v_mfma_f32_16x16x4_f32 chain (two products per tile for M).
 //
-// Each state is stored twice per chunk, as 16 x 16 blocks of 16 bytes per
-// lane: first all blocks in MFMA accumulator order (lane 16q + m holds rows
-// 4q..4q+3 of column m), then all blocks in operand order (lane 16q + m
-// holds columns 4q..4q+3 of row m).  The key/value kernel takes P rows from
-// the second and P columns (rows of P^T) from the first, as MFMA A operands
-// straight from memory.  The operand-order copy of a block is the
-// accumulator block passed through a 1 KiB per-wave LDS scratch.
+// States are stored as 16 x 16 blocks of 16 bytes per lane.  P^gx is stored
+// twice per chunk: first all blocks in MFMA accumulator order (lane 16q + m
+// holds rows 4q..4q+3 of column m), then all blocks in operand order (lane
+// 16q + m holds columns 4q..4q+3 of row m); the key/value kernel takes P rows
+// from the second and P columns (rows of P^T) from the first, as MFMA A
+// operands straight from memory.  The operand-order copy of a block is the
+// accumulator block passed through a 1 KiB per-wave LDS scratch.  M, being
+// symmetric, is stored once in accumulator order: its block (g, j) there is
+// its block (j, g) in operand order.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -59,12 +64,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     const int part = (int)(slot % PARTS);
     if (bh >= BH) return;   // whole workgroup
     const int rb = part % RB;
-    const int which = part / RB;   // 0: gx, 1: zx
+    // 0: gx, 1: zx.  The kinds swap for every other group of eight heads on
+    // an XCD, so that the two workgroups a CU takes in turn (ids 32 slots
+    // apart on one XCD) are mostly one gx and one zx part: the zx parts do
+    // twice the MFMA work.
+    const int which = (part / RB) ^ (int)((slot / PARTS / 8) & 1);
     const int m0 = rb * 16 * NW + 16 * w;
     const float* ah = (which == 0 ? g : z) + (size_t)bh * T * D;
     const float* xh = x + (size_t)bh * T * D;
     const float* gh = gamma + (size_t)bh * T;
-    float* Pout = (which == 0 ? Pgx : Pzx) + (size_t)bh * n_chunks * 2 * D * D;
+    const bool sym = which == 1;   // M = P^zx + (P^zx)^T, stored once
+    const size_t pstride = sym ? (size_t)D * D : (size_t)2 * D * D;   // floats per chunk
+    float* Pout = (which == 0 ? Pgx : Pzx) + (size_t)bh * n_chunks * pstride;
     const int a0 = m0 / 16;        // the wave's row block
 
     f32x4 acc[NT];
@@ -119,9 +130,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
         __syncthreads();
         if (c > 0) prefetch(c - 1);
 
-        // ---- the state of the tokens after this chunk: block (a0, j) in both orders ----
-        {
-            float* dst = Pout + (size_t)c * 2 * D * D + 4 * lane;
+        // ---- the state of the tokens after this chunk: block (a0, j) in both orders (M: once) ----
+        if (sym) {
+            float* dst = Pout + (size_t)c * pstride + 4 * lane;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) store_nt(dst + (a0 * NT + j) * 256, acc[j]);
+        } else {
+            float* dst = Pout + (size_t)c * pstride + 4 * lane;
             float* sc = sT[w];
             const int m = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -138,7 +153,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
             }
         }
 
-        // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain) ----
+        // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain);
+        //      M also gains sum_t e^{l_t} x_t z_t^T ----
         f32x4 U[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -150,6 +166,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
                 const float a = sA[i * PD + m0 + n] * sW[i];
 #pragma unroll
                 for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sX[i * PD + 16 * j + n], U[j]);
+            }
+        }
+        if (sym) {
+#pragma unroll
+            for (int gg = 0; gg < C / 16; ++gg) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int i = 16 * gg + 4 * kk + s;
+                    const float a = sX[i * PD + m0 + n] * sW[i];
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sA[i * PD + 16 * j + n], U[j]);
+                }
             }
         }
         const float G = sGam;
