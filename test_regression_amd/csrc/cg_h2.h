@@ -39,6 +39,7 @@
 namespace mesa {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_f16x32(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -102,8 +103,8 @@ struct alignas(16) H2Lds {
     static constexpr int SW = D / 2 + 8;                    // words per state / key row
     static constexpr int KW = (C >= 32 ? C : 32) / 2 + 8;   // words per K^T row (at least one 32-key step)
     uint32_t S[2][D * SW];     // S^H_c 2^ES: fp16 planes hi, lo; row r = feature r, columns perm32
-    uint32_t KR[NKP][C * SW];  // K_c rows 2^EK (fp16 parts, columns perm32)
-    uint32_t KT[NKP][D * KW];  // K_c^T 2^EK, later V_c^T 2^EV (fp16 parts, tokens perm32)
+    uint32_t KR[NKP][C * SW];  // K_c rows 2^EK, after the CG V_c rows 2^EV (fp16 parts, columns perm32)
+    uint32_t KT[NKP][D * KW];  // K_c^T 2^EK (fp16 parts, tokens perm32)
     float L[C];                // l_i
     float Lam[D];
     float red[3][4];           // per-wave maxima: chunk state, keys, values
@@ -133,8 +134,20 @@ struct H2Wave {
     }
 };
 
-// The A operand of K^T (or V^T) row block j, 32-key step s, plane pl; the
-// second 16 keys are zero when the chunk has no such block (C = 16).
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, result lane i gets, as element e, half i % 4 of the 8 bytes that
+// lane 4 e + i / 4 addresses (the lane layout was checked with a probe).  So
+// when lane L of a group addresses row r0 + L / 4 of a row tile, at the
+// 4-half piece of columns c0 + 4 (L % 4) .. + 3, lane n receives column
+// c0 + n of rows r0 .. r0 + 3.
+__device__ __forceinline__ f16x4 lds_tr_f16x4(const uint32_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+
+// The A operand of K^T row block j, 32-key step s, plane pl; the second 16
+// keys are zero when the chunk has no such block (C = 16).
 template <int D, int C, int NKP>
 __device__ __forceinline__ f16x8 h2_kt_operand(const H2Lds<D, C, NKP>& L, int pl, int j, int s, int m, int kk) {
     constexpr int KW = H2Lds<D, C, NKP>::KW;
@@ -145,6 +158,21 @@ __device__ __forceinline__ f16x8 h2_kt_operand(const H2Lds<D, C, NKP>& L, int pl
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         return __builtin_bit_cast(f16x8, u32x4{v.x, v.y, 0u, 0u});
     }
+}
+
+// The A operand of V^T row block j (features 16 j + m), 32-token step s,
+// plane pl, read transposed from the value rows staged where the key rows
+// were: k-slots 8 kk .. 8 kk + 3 are tokens 32 s + 4 kk + e, k-slots 8 kk + 4
+// .. 8 kk + 7 tokens 32 s + 16 + 4 kk + e (the order of the B operand's
+// decayed scores, and of the tokens in K^T's rows); the second 16 tokens are
+// zero when the chunk has no such block (C = 16).
+template <int D, int C, int NKP>
+__device__ __forceinline__ f16x8 h2_vt_operand(const H2Lds<D, C, NKP>& L, int pl, int j, int s, int m, int kk) {
+    constexpr int SW = H2Lds<D, C, NKP>::SW;
+    const uint32_t* R = L.KR[pl] + perm32(16 * j + 4 * (m & 3)) / 2;
+    const f16x4 a = lds_tr_f16x4(R + (32 * s + 4 * kk + (m >> 2)) * SW);
+    const f16x4 b = C >= 32 ? lds_tr_f16x4(R + (32 * s + 16 + 4 * kk + (m >> 2)) * SW) : f16x4{0, 0, 0, 0};
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // Accumulators per key block for the scores: one when several key blocks
@@ -185,7 +213,7 @@ __device__ __forceinline__ float h2_score(const f32x4 (&Sc)[NB][h2_score_parts<N
     else return (Sc[ib][0][r] + Sc[ib][2][r]) + Sc[ib][1][r];
 }
 
-// Y[j] += K^T / V^T row block j times the decayed scores W over NS 32-key
+// Y[j] += V^T row block j (from the value rows) times the decayed scores W over NS 32-key
 // steps; W is split here with the per-token exponent EW (W 2^EW):
 // Y = T W 2^(ET + EW).
 template <int D, int C, int NKP, int NS>
@@ -198,9 +226,9 @@ __device__ __forceinline__ void h2_apply(const H2Lds<D, C, NKP>& L, const f32x4 
         h2_split(W[2 * s], W[2 * s + 1], sW, Wh, Wl);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const f16x8 A0 = h2_kt_operand<D, C, NKP>(L, 0, j, s, m, kk);
+            const f16x8 A0 = h2_vt_operand<D, C, NKP>(L, 0, j, s, m, kk);
             Y[j] = mfma_f16x32(A0, Wl, Y[j]);
-            if constexpr (NKP == 2) Y[j] = mfma_f16x32(h2_kt_operand<D, C, NKP>(L, 1, j, s, m, kk), Wh, Y[j]);
+            if constexpr (NKP == 2) Y[j] = mfma_f16x32(h2_vt_operand<D, C, NKP>(L, 1, j, s, m, kk), Wh, Y[j]);
             Y[j] = mfma_f16x32(A0, Wh, Y[j]);
         }
     }
@@ -444,7 +472,6 @@ __device__ __forceinline__ void stage_h2_state(uint32_t (&S)[2][D * (D / 2 + 8)]
         }
         // the mirror S[16b + c][16a + q4 + r]: four consecutive permuted columns
         if (a != b) {
-            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
             const int w0 = (16 * b + c) * SW + perm32(16 * a + q4) / 2;
             *reinterpret_cast<f16x4*>(&S[0][w0]) = f16x4{h[0], h[1], h[2], h[3]};
             *reinterpret_cast<f16x4*>(&S[1][w0]) = f16x4{lo[0], lo[1], lo[2], lo[3]};
@@ -457,7 +484,6 @@ template <int D, int C, int NTHR, int NKP, typename In>
 __device__ __forceinline__ void stage_h2_rows(uint32_t (&KR)[NKP][C * (D / 2 + 8)],
                                               const ChunkRowsRegs<D, C, NTHR, In>& rg, int tid, float s) {
     constexpr int SW = D / 2 + 8;
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int u = 0; u < ChunkRowsRegs<D, C, NTHR, In>::EL4; ++u) {
         int i, f;

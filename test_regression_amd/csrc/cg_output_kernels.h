@@ -290,7 +290,9 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
 // causal keys from the chunk start.  Four workgroup barriers per chunk, as in
 // cg_wave; the exponents of the next chunk's state and keys come from
 // per-wave maxima gathered before barrier (C), and the values' exponent from
-// maxima gathered before barrier (A).
+// maxima gathered before barrier (A).  The output's V^T operands are read
+// transposed from the value rows (staged where the key rows were, after
+// barrier (A)), so the values need no transposed tile.
 template <int D, int C, int W, typename In>
 __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, int tid, ChunkPos& p, int& ES,
                                            int& EK, int n_chunks, int H, int T, long total,
@@ -388,7 +390,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
         const float vm = wave_max(rows_absmax<D, C, NTHR, In>(vrows));
         if (lane == 0) L.red[2][W] = vm;
     }
-    __syncthreads();   // (A) every wave is done with the state planes, K_c rows, K_c^T, l and lambda
+    __syncthreads();   // (A) every wave is done with the state planes, K_c rows and K_c^T, l and lambda
     float vmax = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) vmax = fmaxf(vmax, L.red[2][w2]);
@@ -407,7 +409,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
         }
     }
     load_queries<D, In>(qr, q, pn.tok0, more ? pn.valid : 0, tr, kk);
-    stage_h2_transposed<D, C, NTHR, NKP, In>(L.KT, vrows, tid, pow2(EV));
+    stage_h2_rows<D, C, NTHR, NKP, In>(L.KR, vrows, tid, pow2(EV));   // V_c rows, where K_c's were
     __syncthreads();   // (B)
     {
         const int EWo = h2_exp(kslot_max(absmax<2 * Wv::NS>(Wo)));
@@ -443,7 +445,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
         const int e = tid + u * NTHR;
         if (e < D) L.Lam[e] = nlam[u];
     }
-    __syncthreads();   // (C) every wave is done with V_c^T; the next chunk's maxima are in
+    __syncthreads();   // (C) every wave is done with V_c; the next chunk's maxima are in
     float smax = 0.f, kmax = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) {
