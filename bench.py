@@ -325,7 +325,8 @@ def dynamic(torch, mesa, inputs, dev):
     x = inputs.forward_inputs(w)
     t = {n: to_dev(torch, x[n], "f32", dev) for n in x}
     del x
-    el, k1, k2, _, iters = timed_forward(torch, mesa, t, w, 3, 1)
+    steps = 5
+    el, k1, k2, _, iters = timed_forward(torch, mesa, t, w, steps, 2)
     n_tok = w.B * w.H * w.T
     it = iters.to(torch.float64)
     mean_it = float(it.mean())
@@ -333,7 +334,7 @@ def dynamic(torch, mesa, inputs, dev):
     per_it = 2 * w.d * w.d + 2 * (w.chunk + 1) * w.d + 11 * w.d
     useful = n_tok * (fs + fo) + float(it.sum()) * per_it
     k2_useful = n_tok * fo + float(it.sum()) * per_it
-    ms = 1e3 * el / 3
+    ms = 1e3 * el / steps
     k2_ms = k2[0] / max(k2[1], 1)
     k1_ms = k1[0] / max(k1[1], 1)
     wave_iters = iters.view(-1, w.chunk // 16, 16).amax(dim=-1).cpu().numpy()

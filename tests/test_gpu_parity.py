@@ -484,6 +484,23 @@ def test_bf16_states_at_float_accuracy(d, chunk):
     assert eh <= 5e-7 and eg <= 5e-7
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunk_states_many_heads(dtype):
+    """d = 128 with many heads: bf16 takes the chunk-state kernel's unsplit
+    column sets (one G workgroup per row half, B*H >= 171), fp32 the
+    eight-wave kernel; outputs, iteration counts and both final states
+    against the oracle, with a ragged last chunk."""
+    B, H, T, d = 12, 16, 130, 128
+    say("case many heads", dtype, (B, H, T, d))
+    x = small_inputs(47, B, H, T, d, dtype)
+    g = gpu_forward(x, dtype, 3, 0.0, 64, return_final=True)
+    r = oracle_forward(x, dtype, 3, 0.0, final_state=True)
+    eo, eh, eg = rel_l2(g["out"], r["out"]), rel_l2(g["final_H"], r["final_H"]), rel_l2(g["final_G"], r["final_G"])
+    say(f"out={eo:.2e} final_H={eh:.2e} final_G={eg:.2e}")
+    assert eo <= 1e-5 and eh <= 5e-7 and eg <= 5e-7
+    assert (g["iters"] == 3).all()
+
+
 def test_final_states_and_decode_continue_forward():
     import torch
     from test_regression_amd import mesa
