@@ -83,7 +83,7 @@ typedef enum {
     MESA_KERNEL_BWD_STATES = 5,      /* backward: reverse chunk states                   */
     MESA_KERNEL_BWD_KV = 6,          /* backward: key and value gradients                */
     MESA_KERNEL_BWD_GATE = 7,        /* backward: gate and regulariser gradients         */
-    MESA_KERNEL_HAWK = 8,            /* Hawk layer recurrence (both passes)              */
+    MESA_KERNEL_HAWK = 8,            /* Hawk layer recurrence (all its kernels)          */
     MESA_KERNEL_COUNT = 9
 } mesa_kernel_id;
 
@@ -310,7 +310,10 @@ mesa_status mesa_qk_preprocess(const void *x, int in_dtype, const float *conv_w,
  *   y         [B, T, D]       float32, written
  *   h_final   [B, D]          float32 state after the last token, or NULL
  *   workspace, workspace_bytes  at least mesa_hawk_workspace_bytes(B, T, D)
- * T >= 0; y must not alias the inputs.
+ * T >= 0; y must not alias the inputs.  Wide shapes (B * ceil(D / 64) >= 128)
+ * run as one pass that reads each input once and leaves the workspace
+ * untouched; narrower ones run a two-pass chunked scan that keeps per-chunk
+ * summaries in the workspace.
  */
 size_t mesa_hawk_workspace_bytes(int B, int T, int D);
 mesa_status mesa_hawk_scan(const void *x, const void *ga, const void *gx, int in_dtype, const float *lam,

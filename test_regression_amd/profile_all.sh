@@ -40,10 +40,8 @@ $PS --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$CMD" --sources $
     > profiles/bwd_kv_layer_bf16_d128_T4096_traffic.json
 $PS --kernel "bwd_states_kernel<128, 64, 4>" --command "$CMD" --sources $C/bwd_states.hip $C/mesa_device.h \
     > profiles/bwd_states_layer_bf16_d128_T4096_traffic.json
-$PS --kernel "hawk_summary_kernel<mesa::bf16_t, 4>" --command "$CMD" --sources $C/hawk.hip $C/mesa_device.h \
-    > profiles/hawk_summary_bf16_B8_T4096_D2048_traffic.json
-$PS --kernel "hawk_scan_kernel<mesa::bf16_t, 4>" --command "$CMD" --sources $C/hawk.hip $C/mesa_device.h \
-    > profiles/hawk_scan_bf16_B8_T4096_D2048_traffic.json
+$PS --kernel "hawk_stream_kernel<mesa::bf16_t, 8, 8>" --command "$CMD" --sources $C/hawk.hip $C/mesa_device.h \
+    > profiles/hawk_stream_bf16_B8_T4096_D2048_traffic.json
 M=$OUT/prof_mfma/m_counter_collection.csv
 MA=$OUT/prof_mfma/m_agent_info.csv
 MCMD="cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE -f csv -- python3 \$R/bench.py $SHORT"

@@ -54,6 +54,34 @@ def test_hawk_shapes(D, T, dtype):
         assert np.abs(y - ry).max() <= 1e-4 * max(1.0, np.abs(ry).max())
 
 
+# Shapes with at least 128 blocks of 64 channels take the one-pass schedule
+# (a workgroup per block, rounds of 16 x 8 tokens); the ones above take the
+# two-pass chunked scan.  Ragged D leaves lanes of the last block idle, and
+# ragged T ends inside a round and inside a wave's segment.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D", [(2, 1, 4096), (2, 127, 4039), (2, 300, 4096), (2, 1000, 4039), (128, 257, 64),
+                                   (130, 129, 70)])
+def test_hawk_one_pass_shapes(B, T, D, dtype):
+    seed = 6300 + B + T + D
+    say("case hawk one pass", dict(B=B, D=D, T=T, dtype=dtype, seed=seed))
+    for with_h0 in (False, True):
+        xin = inputs.hawk_inputs(B, T, D, dtype, seed, with_h0=with_h0)
+        y, hf, ry, rh = run(xin, dtype)
+        e, eh = rel_l2(y, ry), rel_l2(hf, rh)
+        say(f"  h0={with_h0} rel_l2 y={e:.2e} h_final={eh:.2e}")
+        assert e <= RTOL[dtype] and eh <= RTOL[dtype]
+        assert np.abs(y - ry).max() <= 1e-4 * max(1.0, np.abs(ry).max())
+
+
+def test_hawk_one_pass_closed_gates_keep_the_state():
+    say("case hawk one pass closed gates")
+    xin = inputs.hawk_inputs(2, 300, 4096, "f32", 6400, with_h0=True)
+    xin["ga"][:] = -60.0
+    y, hf, ry, rh = run(xin, "f32")
+    np.testing.assert_allclose(y, np.broadcast_to(xin["h0"][:, None, :], y.shape), rtol=1e-6)
+    np.testing.assert_allclose(hf, xin["h0"], rtol=1e-6)
+
+
 def test_hawk_closed_gates_keep_the_state_and_empty_sequence():
     import torch
     from test_regression_amd import mesa
