@@ -15,9 +15,11 @@
 // Work split: one workgroup per (head, chunk); wave w owns keys 16w..16w+15
 // and holds their k_i, v_i in registers as the MFMA B operand (lane (n, kk):
 // features 16j + 4kk + r of key n).  The state terms come first: the
-// reverse-state kernel stores P^gx's blocks in both MFMA orders and the
-// symmetric M = P^zx + (P^zx)^T once, so P rows, P columns and M rows are A
-// operands read straight from memory, while the
+// reverse-state kernel stores P^gx and the symmetric M = P^zx + (P^zx)^T
+// once each, in accumulator block order, which is the operand order of the
+// transpose; so P columns (rows of P^T) and M rows are A operands read
+// straight from memory, and P rows come from the same blocks passed through
+// a per-wave LDS transpose.  Meanwhile the
 // chunk's x, z, g rows travel from memory into LDS by direct loads.  Then
 // the within-chunk sums: scores come out of the MFMA in exactly the layout
 // the next contraction (over tokens) takes as its B operand, so the token
@@ -29,11 +31,18 @@
 
 namespace mesa {
 
+// Per-wave scratch of the P block transposes: one diagonal of NT blocks,
+// element (row, col) of block a at a * kTrBlock + (row / 4) * kTrPitch + 4 col + row % 4
+// (pitch 68: the transposed reads of a block hit 64 distinct banks).
+constexpr int kTrPitch = 68;
+constexpr int kTrBlock = 4 * kTrPitch;
+
 template <int D, int C>
 struct alignas(16) KvLds {
     static constexpr int PD = lds_pitch(D);
     float R[3 * C * PD];   // x, z, g rows of the chunk
     float L[C];
+    float Tr[C / 16][(D / 16) * kTrBlock];   // per-wave transpose scratch
 };
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
@@ -57,50 +66,64 @@ __device__ __forceinline__ f32x4 token_scores(const float* rows, const f32x4 (&Z
     return acc;
 }
 
-// The later chunks' terms for the wave's keys, straight from the stored
-// states (block (a, b) of a state at 256 (a NT + b) floats, accumulator
-// order; operand order D^2 floats further on):
+// The later chunks' terms for the wave's keys, from the stored states (block
+// (a, b) of a state at 256 (a NT + b) floats, accumulator order):
 //   A1 = P^gx k_i,   A2 = (P^gx)^T v_i - (P^zx + (P^zx)^T) k_i.
+// P^gx's block (a, b) is (P^gx)^T's operand block (b, a), so it feeds A2[b]
+// with v_i's features of block a as it comes; its transpose is P^gx's operand
+// block (a, b), which feeds A1[a] with k_i's features of block b.  The blocks
+// go by diagonals (b = a + dg mod NT), so consecutive blocks update different
+// accumulators of both sums; a diagonal's blocks are transposed through the
+// wave's LDS scratch while the A2 products of the diagonal run.
 template <int D>
 __device__ __forceinline__ void state_terms(const float* __restrict__ Pg, const float* __restrict__ Pz, int lane,
                                             const f32x4 (&Kb)[D / 16], const f32x4 (&Vb)[D / 16],
-                                            f32x4 (&A1)[D / 16], f32x4 (&A2)[D / 16]) {
+                                            f32x4 (&A1)[D / 16], f32x4 (&A2)[D / 16], float* tr) {
     constexpr int NT = D / 16;
-    constexpr int DD = D * D;
     const float* pg = Pg + 4 * lane;
     const float* pz = Pz + 4 * lane;
+    const int m = lane & 15, q = lane >> 4;
     f32x4 A3[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) A1[j] = A2[j] = A3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // output block j, contraction group g: rows of P are operand block (j, g),
-    // rows of P^T are accumulator block (g, j)
     auto ld = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
     f32x4 bg[2][NT];
-    auto load_g = [&](int g, int buf) {
+    // diagonal dg: block (a, (a + dg) % NT) for a = 0..NT-1
+    auto load_d = [&](int dg, int buf) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) bg[buf][j] = ld(pg + DD + (j * NT + g) * 256);
+        for (int a = 0; a < NT; ++a) bg[buf][a] = ld(pg + (a * NT + (a + dg) % NT) * 256);
     };
-    load_g(0, 0);
+    load_d(0, 0);
 #pragma unroll
-    for (int g = 0; g < NT; ++g) {
-        if (g + 1 < NT) load_g(g + 1, (g + 1) & 1);
+    for (int dg = 0; dg < NT; ++dg) {
+        const int cb = dg & 1;
+        // the diagonal's blocks into the scratch, in accumulator layout
+#pragma unroll
+        for (int a = 0; a < NT; ++a) *reinterpret_cast<f32x4*>(tr + a * kTrBlock + q * kTrPitch + 4 * m) = bg[cb][a];
+        if (dg + 1 < NT) load_d(dg + 1, cb ^ 1);
+        // A2[b] += P^T_op(b, a) v(a)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) A1[j] = mfma4(bg[g & 1][j][s], Kb[g][s], A1[j]);
-    }
-    auto load_t = [&](int g, int buf) {
+            for (int a = 0; a < NT; ++a) {
+                const int b = (a + dg) % NT;
+                A2[b] = mfma4(bg[cb][a][s], Vb[a][s], A2[b]);
+            }
+        wave_lds_sync();
+        // A1[a] += P_op(a, b) k(b): element u of lane (q, m) is row m, column 4q + u of the block
+        f32x4 t[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) bg[buf][j] = ld(pg + (g * NT + j) * 256);
-    };
-    load_t(0, 0);
+        for (int a = 0; a < NT; ++a)
 #pragma unroll
-    for (int g = 0; g < NT; ++g) {
-        if (g + 1 < NT) load_t(g + 1, (g + 1) & 1);
+            for (int u = 0; u < 4; ++u) t[a][u] = tr[a * kTrBlock + (m >> 2) * kTrPitch + 4 * (4 * q + u) + (m & 3)];
+        wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) A2[j] = mfma4(bg[g & 1][j][s], Vb[g][s], A2[j]);
+            for (int a = 0; a < NT; ++a) {
+                const int b = (a + dg) % NT;
+                A1[a] = mfma4(t[a][s], Kb[b][s], A1[a]);
+            }
     }
     // rows of M = P^zx + (P^zx)^T: M's operand-order block (j, g) is its
     // stored accumulator-order block (g, j), M being symmetric
@@ -148,7 +171,7 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
 
     // ---- the later chunks, through the reverse states (while the tiles land) ----
     f32x4 DV[NT], DK[NT];
-    state_terms<D>(Pgx, Pzx, lane, Kb, Vb, DV, DK);
+    state_terms<D>(Pgx, Pzx, lane, Kb, Vb, DV, DK, L.Tr[W]);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct tile loads are in LDS
     __syncthreads();                 // and every wave's, and the log decays
     const float li = L.L[il];
@@ -249,8 +272,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
     const int t0 = c * C;
     const int valid = min(C, T - t0);
     const size_t tok0 = (size_t)bh * T + t0;
-    const size_t soff = ((size_t)bh * n_chunks + c) * 2 * D * D;   // P^gx: both block orders per chunk
-    const size_t moff = ((size_t)bh * n_chunks + c) * D * D;       // M: accumulator order
+    const size_t soff = ((size_t)bh * n_chunks + c) * D * D;   // P^gx, M: accumulator order
 
     // ---- x, z, g rows of the chunk straight into LDS (rows past the end zeroed); l ----
     // One row per wave instruction: lanes 0..D/4-1 each move 16 bytes.
@@ -272,7 +294,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
     }
 
     const float* pg = Pgx + soff;
-    const float* pz = Pzx + moff;
+    const float* pz = Pzx + soff;
     if (w == 0) {
         kv_wave<D, C, 0, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
     } else if constexpr (NW > 1) {

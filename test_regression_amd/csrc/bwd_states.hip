@@ -19,15 +19,13 @@
 // a 16 x D slab of the running state in MFMA accumulators, the update a fresh
 // v_mfma_f32_16x16x4_f32 chain (two products per tile for M).
 //
-// States are stored as 16 x 16 blocks of 16 bytes per lane.  P^gx is stored
-// twice per chunk: first all blocks in MFMA accumulator order (lane 16q + m
-// holds rows 4q..4q+3 of column m), then all blocks in operand order (lane
-// 16q + m holds columns 4q..4q+3 of row m); the key/value kernel takes P rows
-// from the second and P columns (rows of P^T) from the first, as MFMA A
-// operands straight from memory.  The operand-order copy of a block is the
-// accumulator block passed through a 1 KiB per-wave LDS scratch.  M, being
-// symmetric, is stored once in accumulator order: its block (g, j) there is
-// its block (j, g) in operand order.
+// States are stored as 16 x 16 blocks of 16 bytes per lane, each once per
+// chunk in MFMA accumulator order (lane 16q + m holds rows 4q..4q+3 of
+// column m).  Block (a, b) in that order is block (b, a) of the transpose in
+// operand order (lane 16q + m holds columns 4q..4q+3 of row m): the key/value
+// kernel reads P^gx's blocks so as rows of (P^gx)^T, and passes them through a
+// per-wave LDS transpose for the rows of P^gx.  M, being symmetric, needs no
+// transpose: its block (g, j) is its block (j, g) in operand order.
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -46,8 +44,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     __shared__ float sX[C * PD];   // x rows of the chunk (the state's columns)
     __shared__ float sW[C];        // e^{l_t}
     __shared__ float sGam;         // e^{l_end}
-    constexpr int SP = 68;         // scratch pitch per k-slot group (16 lanes x 4 floats + 4)
-    __shared__ __attribute__((aligned(16))) float sT[NW][4 * SP];   // per-wave block transpose
 
     const int tid0 = threadIdx.x;
     const int lane = tid0 & 63;
@@ -73,8 +69,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     const float* ah = (which == 0 ? g : z) + (size_t)bh * T * D;
     const float* xh = x + (size_t)bh * T * D;
     const float* gh = gamma + (size_t)bh * T;
-    const bool sym = which == 1;   // M = P^zx + (P^zx)^T, stored once
-    const size_t pstride = sym ? (size_t)D * D : (size_t)2 * D * D;   // floats per chunk
+    const bool sym = which == 1;   // M = P^zx + (P^zx)^T
+    const size_t pstride = (size_t)D * D;   // floats per chunk
     float* Pout = (which == 0 ? Pgx : Pzx) + (size_t)bh * n_chunks * pstride;
     const int a0 = m0 / 16;        // the wave's row block
 
@@ -130,27 +126,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
         __syncthreads();
         if (c > 0) prefetch(c - 1);
 
-        // ---- the state of the tokens after this chunk: block (a0, j) in both orders (M: once) ----
-        if (sym) {
+        // ---- the state of the tokens after this chunk: blocks (a0, j) ----
+        {
             float* dst = Pout + (size_t)c * pstride + 4 * lane;
 #pragma unroll
             for (int j = 0; j < NT; ++j) store_nt(dst + (a0 * NT + j) * 256, acc[j]);
-        } else {
-            float* dst = Pout + (size_t)c * pstride + 4 * lane;
-            float* sc = sT[w];
-            const int m = lane & 15, q = lane >> 4;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                store_nt(dst + (a0 * NT + j) * 256, acc[j]);
-                // element (row, col) of the block sits at sc[(row / 4) * SP + 4 col + row % 4]
-                *reinterpret_cast<f32x4*>(sc + kk * SP + 4 * n) = acc[j];
-                wave_lds_sync();
-                f32x4 o;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) o[u] = sc[(m / 4) * SP + 4 * (4 * q + u) + m % 4];
-                wave_lds_sync();
-                store_nt(dst + D * D + (a0 * NT + j) * 256, o);
-            }
         }
 
         // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain);

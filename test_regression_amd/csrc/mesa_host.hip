@@ -296,8 +296,8 @@ static BwdLayout bwd_layout(long BH, int T, int d, long nc, int chunk) {
     size_t o = 0;
     l.sh = o;   o += r4((size_t)BH * nc * ((size_t)d * (d + 16) / 2));
     l.sg = o;   o += r4((size_t)BH * nc * d * d);
-    l.pgx = o;  o += r4((size_t)BH * nc * 2 * d * d);   // two block orders per chunk
-    l.pzx = o;  o += r4((size_t)BH * nc * d * d);       // P^zx + (P^zx)^T, one block order
+    l.pgx = o;  o += r4((size_t)BH * nc * d * d);   // P^gx, accumulator block order
+    l.pzx = o;  o += r4((size_t)BH * nc * d * d);   // P^zx + (P^zx)^T, accumulator block order
     l.beta = o; o += r4((size_t)BH * T);
     l.akey = o; o += r4((size_t)BH * T);
     l.lam = o;  o += r4((size_t)BH * nc * waves * d);
