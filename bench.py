@@ -36,7 +36,7 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "cg_h2_layer_bf16_d128_T4096_mfma.jso
 KERNEL_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_output_bf16.hip",
                   "test_regression_amd/csrc/cg_output_kernels.h", "test_regression_amd/csrc/cg_h2.h",
                   "test_regression_amd/csrc/cg_core.h", "test_regression_amd/csrc/persistent.h",
-                  "test_regression_amd/csrc/mesa_device.h", "test_regression_amd/csrc/cg_split.h"]
+                  "test_regression_amd/csrc/mesa_device.h"]
 
 
 def log(*a):
@@ -81,22 +81,24 @@ def h2_cg_mfma_flops(d, C, key_planes, wave_iters):
     return f16, fp32
 
 
-def split_adjoint_mfma_flops(d, C, k, n_chunks):
-    """MFMA flops one launch of the bf16 adjoint kernel issues at a fixed
-    iteration count k: k CG matvecs and H x as in the forward's split
-    kernel; the right side G^T g with the (S^G)^T term and the value scores
-    on fp32 MFMAs and the apply through K^T as three bf16 products.
-    Returns (bf16 flops, fp32 flops)."""
+def h2_adjoint_mfma_flops(d, C, key_planes, k, n_chunks):
+    """MFMA flops one launch of the adjoint kernel (d >= 32) issues at a fixed
+    iteration count k: k CG matvecs and H x, each as a matvec of the forward
+    CG kernel (h2_cg_mfma_flops); the right side G^T g with the (S^G)^T term
+    and the value scores on 16x16x4 fp32 MFMAs, and its apply through K^T on
+    (1 + key planes) fp16 products per row block and 32-key step.
+    Returns (fp16 flops, fp32 flops)."""
     NT, NQ, NW = d // 16, d // 32, C // 16
-    per_iter, rhs_bf16, rhs_fp32 = 0, 0, 0
+    np_ = 1 + key_planes
+    per_iter, rhs16, rhs32 = 0, 0, 0
     for w in range(NW):
         nbo, ns = w + 1, (w + 2) // 2
-        per_iter += 9 * NT * NQ + 3 * NQ * nbo + 3 * NT * ns
-        rhs_bf16 += 3 * NT * ns
-        rhs_fp32 += 4 * NT * NT + 4 * NT * nbo
-    bf16 = 2 * 16 * 16 * 32 * ((k + 1) * per_iter + rhs_bf16) * n_chunks
-    fp32 = 2 * 16 * 16 * 4 * rhs_fp32 * n_chunks
-    return bf16, fp32
+        per_iter += 3 * NT * NQ + np_ * NQ * nbo + np_ * NT * ns
+        rhs16 += np_ * NT * ns
+        rhs32 += 4 * NT * NT + 4 * NT * nbo
+    f16 = 2 * 16 * 16 * 32 * ((k + 1) * per_iter + rhs16) * n_chunks
+    fp32 = 2 * 16 * 16 * 4 * rhs32 * n_chunks
+    return f16, fp32
 
 
 def mixed_roofline(bf16_flops, fp32_flops, ms, alg_flops, bf16_peak, fp32_peak):
@@ -297,7 +299,7 @@ def backward(torch, mesa, h, dev, peaks, steps=5, warmup=2):
     adj_flops = n_tok * (k * (2 * d * d + 2 * (C + 1) * d + 11 * d) + 2 * (2 * d * d + 2 * (C + 1) * d))
     adj_ms = kt["bwd_adjoint_kernel"][0] / max(kt["bwd_adjoint_kernel"][1], 1)
     achieved = adj_flops / (adj_ms * 1e-3) / 1e12
-    bf, fp = split_adjoint_mfma_flops(d, C, k, w.B * w.H * (w.T // C))
+    bf, fp = h2_adjoint_mfma_flops(d, C, 1 if w.dtype == "bf16" else 2, k, w.B * w.H * (w.T // C))
     rl = mixed_roofline(bf, fp, adj_ms, adj_flops, PEAK_BF16_MFMA_TFLOPS, PEAK_FP32_MFMA_TFLOPS)
     rlm = mixed_roofline(bf, fp, adj_ms, adj_flops, peaks["mfma_bf16_tflops"], peaks["mfma_f32_tflops"])
     kernels = {n: {"avg_ms": round(v[0] / max(v[1], 1), 4), "launches": v[1]} for n, v in kt.items()}
@@ -308,13 +310,14 @@ def backward(torch, mesa, h, dev, peaks, steps=5, warmup=2):
             "kernels": kernels,
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
-                         "kernel": "bwd_adjoint_split_kernel<128,64>",
-                         "basis": "algorithmic flops per launch / average launch time / the bf16 MFMA peak",
+                         "kernel": "bwd_adjoint_h2_kernel<128,64,bf16> (fp16 MFMA on two-part splits)",
+                         "basis": "algorithmic flops per launch / average launch time / the fp16 (= bf16) MFMA "
+                                  "peak",
                          "algorithmic_flops_per_launch": adj_flops, "avg_launch_ms": round(adj_ms, 4),
                          "algorithmic_over_fp32_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
                          "issued": {"achieved": rl["achieved"], "peak": rl["peak"], "frac": rl["frac"],
-                                    "bf16_flops": bf, "fp32_flops": fp,
-                                    "basis": "issued MFMA work: bf16 split products at 2500 TFLOP/s, the "
+                                    "fp16_flops": bf, "fp32_flops": fp,
+                                    "basis": "issued MFMA work: fp16 split products at 2500 TFLOP/s, the "
                                              "right side's fp32 products at 157.3",
                                     "peak_measured": rlm["peak"], "frac_measured": rlm["frac"]}}}
 

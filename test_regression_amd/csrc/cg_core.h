@@ -162,48 +162,6 @@ __device__ __forceinline__ void contract_intra(const f32x4 (&W)[NB], const float
     }
 }
 
-// ---- split-bf16 operands (used by the bf16-key kernels of cg_split.h) ----
-// A float x is split by truncation into hi = x with its low 16 bits cleared,
-// mid = the same of x - hi, lo = x - hi - mid.  Both subtractions are exact
-// and lo has at most 8 significant bits, so hi + mid + lo = x exactly and
-// each part is a bf16; a product of a bf16 value with each part is exact in
-// float.  A 32-slot MFMA operand here is two 4-element pieces: lane group kk
-// takes slots 4kk..4kk+3 of a first and of a second 16-slot block.
-
-// Whether keys of type In at head dimension D go to the split-bf16 kernels
-// (bf16 keys, whole 32-feature steps) rather than the fp32 ones.
-template <int D, typename In>
-__host__ __device__ constexpr bool split_keys() { return sizeof(In) == 2 && D % 32 == 0; }
-
-// High halves of a (low) and b (high) in one word: one v_perm_b32, whose
-// byte selectors 0-3 pick bytes of its second source and 4-7 of its first.
-__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
-    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-
-// The three split parts of two 4-element float pieces as operands.
-__device__ __forceinline__ void split_operands(const f32x4& a, const f32x4& b, bf16x8& H, bf16x8& M, bf16x8& L) {
-    float h[8], m[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? a[e] : b[e - 4];
-        h[e] = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
-        const float r = x - h[e];
-        m[e] = __uint_as_float(__float_as_uint(r) & 0xffff0000u);
-        l[e] = r - m[e];
-    }
-    uint32_t wh[4], wm[4], wl[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        wh[q] = pack_hi(h[2 * q], h[2 * q + 1]);
-        wm[q] = pack_hi(m[2 * q], m[2 * q + 1]);
-        wl[q] = pack_hi(l[2 * q], l[2 * q + 1]);
-    }
-    H = as_bf16x8(wh);
-    M = as_bf16x8(wm);
-    L = as_bf16x8(wl);
-}
-
 // S_mid (upper block triangle) = e^{l_{h-1}} S0 + sum_{i<h} e^{l_{h-1}-l_i} k_i k_i^T,
 // blocks distributed over the NW waves.  Written to S1.
 template <int D, int C>

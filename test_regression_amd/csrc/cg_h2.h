@@ -28,15 +28,23 @@
 // matvec).  The products' exponents are undone when the fp32 accumulators
 // are combined.
 //
-// LDS layout as in the bf16-split kernel (cg_split.h): rows of the state
-// planes and key tiles store each 32-column block permuted (perm32) so that
-// a lane's 8-slot MFMA operand (the 4-element pieces 4kk..4kk+3 of two
-// 16-column blocks, which is what the CG vectors hold in registers) is one
-// 128-bit read; row pitches are 8 words more than the row.
+// LDS layout: a 32-slot MFMA operand of lane group kk is the 4-element
+// pieces 4kk..4kk+3 of two 16-column blocks (what the CG vectors hold in
+// registers).  Rows of the state planes and key tiles store each 32-column
+// block permuted (perm32) so that those eight columns are contiguous: a
+// lane's operand is one 128-bit read.  Row pitches are 8 words more than the
+// row (an odd multiple of 8 words), so the 16-byte pieces that rows
+// m = 0..7 and lane groups kk = 0, 1 read fall on distinct banks.
 #pragma once
-#include "cg_split.h"
+#include "cg_core.h"
+#include "persistent.h"
 
 namespace mesa {
+
+// Position of column c within its 32-column block after the permutation.
+__host__ __device__ constexpr int perm32(int c) {
+    return 32 * (c / 32) + 8 * ((c % 16) / 4) + 4 * ((c % 32) / 16) + (c % 4);
+}
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -232,6 +240,82 @@ __device__ __forceinline__ void h2_apply(const H2Lds<D, C, NKP>& L, const f32x4 
             Y[j] = mfma_f16x32(A0, Wh, Y[j]);
         }
     }
+}
+
+// Y[j] += K^T row block j times the decayed scores W over NS 32-key steps;
+// W is split here with the per-token exponent EW (W 2^EW): Y = K^T W 2^(EK + EW).
+template <int D, int C, int NKP, int NS>
+__device__ __forceinline__ void h2_apply_kt(const H2Lds<D, C, NKP>& L, const f32x4 (&W)[2 * NS], float sW, int m,
+                                            int kk, f32x4 (&Y)[D / 16]) {
+    constexpr int NT = D / 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        f16x8 Wh, Wl;
+        h2_split(W[2 * s], W[2 * s + 1], sW, Wh, Wl);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const f16x8 A0 = h2_kt_operand<D, C, NKP>(L, 0, j, s, m, kk);
+            Y[j] = mfma_f16x32(A0, Wl, Y[j]);
+            if constexpr (NKP == 2) Y[j] = mfma_f16x32(h2_kt_operand<D, C, NKP>(L, 1, j, s, m, kk), Wh, Y[j]);
+            Y[j] = mfma_f16x32(A0, Wh, Y[j]);
+        }
+    }
+}
+
+// Y = H_t p for the wave's 16 tokens (no Lambda term), the CG loop's matvec
+// as one plain pass: per 32-feature step the split of p (exponent from
+// max |p| per token), its scores with the causal keys and its state
+// products; then the decayed scores, split, through K^T; then the exponents
+// undone in the combination e^{l_t} S p + intra.
+template <int D, int C, int NKP, int W>
+__device__ __forceinline__ void h2_matvec(const H2Lds<D, C, NKP>& L, const H2Wave<D, C, W>& wv, int ES, int EK,
+                                          const f32x4 (&P)[D / 16], f32x4 (&Y)[D / 16]) {
+    using Wv = H2Wave<D, C, W>;
+    constexpr int NT = D / 16;
+    constexpr int NQ = D / 32;
+    constexpr int NB = Wv::NBO;
+    constexpr int NS = Wv::NS;
+    constexpr int NP = h2_score_parts<NB, NKP>();
+    constexpr int SW = H2Lds<D, C, NKP>::SW;
+    const int n = wv.n, kk = wv.kk;
+    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int EP = h2_exp(kslot_max(absmax<NT>(P)));
+    const float sP = pow2(EP);
+    f32x4 Sc[NB][NP], YS[NT], YI[NT];
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+        for (int t = 0; t < NP; ++t) Sc[ib][t] = zero;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) YS[j] = YI[j] = zero;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        f16x8 Zh, Zl;
+        h2_split(P[2 * q], P[2 * q + 1], sP, Zh, Zl);
+        h2_scores_step<D, C, NKP, NB>(L, q, Zh, Zl, n, kk, Sc);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int off = (16 * i + n) * SW + 16 * q + 4 * kk;
+            const f16x8 Ah = lds_f16x8(&L.S[0][off]), Al = lds_f16x8(&L.S[1][off]);
+            // smallest terms first
+            YS[i] = mfma_f16x32(Al, Zh, YS[i]);
+            YS[i] = mfma_f16x32(Ah, Zl, YS[i]);
+            YS[i] = mfma_f16x32(Ah, Zh, YS[i]);
+        }
+    }
+    f32x4 Wt[2 * NS];
+#pragma unroll
+    for (int ib = 0; ib < 2 * NS; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Wt[ib][r] = ib < NB ? h2_score<NB, NKP>(Sc, ib < NB ? ib : 0, r) * wv.dec[ib][r] : 0.f;
+    const int EW = h2_exp(kslot_max(absmax<2 * NS>(Wt)));
+    h2_apply_kt<D, C, NKP, NS>(L, Wt, pow2(EW), n, kk, YI);
+    const float a = __builtin_amdgcn_ldexpf(wv.eLo, -(ES + EP));
+    const float b = pow2(-(2 * EK + EP + EW));
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y[j][r] = a * YS[j][r] + b * YI[j][r];
 }
 
 // The CG of wave W on (H_t + Lambda) x = b for its 16 tokens, from x = 0,
@@ -520,6 +604,61 @@ __device__ __forceinline__ void stage_h2_transposed(uint32_t (&KT)[NKP][D * ((C 
             if constexpr (NKP == 2) reinterpret_cast<_Float16*>(KT[1])[(f + r) * 2 * KW + perm32(i)] = (_Float16)(y - (float)h);
         }
     }
+}
+
+// The staging of a chunk, in two steps around a workgroup barrier: each wave
+// puts the largest magnitudes of its share of the chunk state and keys in
+// L.red; after the barrier every wave takes the chunk's exponents from them
+// and writes its share of the state planes, the key rows and K^T.
+template <int D, int C, int NTHR, int NKP, typename In>
+__device__ __forceinline__ void h2_put_maxima(H2Lds<D, C, NKP>& L, const PackedStateRegs<D, NTHR>& st,
+                                              const ChunkRowsRegs<D, C, NTHR, In>& kr, int tid, int lane, int w) {
+    const float sm = wave_max(packed_absmax<D, NTHR>(st, tid));
+    const float km = wave_max(rows_absmax<D, C, NTHR, In>(kr));
+    if (lane == 0) {
+        L.red[0][w] = sm;
+        L.red[1][w] = km;
+    }
+}
+
+template <int D, int C, int NTHR, int NKP, typename In>
+__device__ __forceinline__ void h2_stage_chunk(H2Lds<D, C, NKP>& L, const PackedStateRegs<D, NTHR>& st,
+                                               const ChunkRowsRegs<D, C, NTHR, In>& kr, int tid, int& ES, int& EK) {
+    constexpr int NW = NTHR / 64;
+    float smax = 0.f, kmax = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+        smax = fmaxf(smax, L.red[0][w2]);
+        kmax = fmaxf(kmax, L.red[1][w2]);
+    }
+    ES = __builtin_amdgcn_readfirstlane(h2_exp(smax));
+    EK = __builtin_amdgcn_readfirstlane(h2_exp(kmax));
+    stage_h2_state<D, NTHR>(L.S, st, tid, pow2(ES));
+    stage_h2_rows<D, C, NTHR, NKP, In>(L.KR, kr, tid, pow2(EK));
+    stage_h2_transposed<D, C, NTHR, NKP, In>(L.KT, kr, tid, pow2(EK));
+}
+
+// The workgroup's first chunk: its state, keys, gates and lambda, staged
+// (ends with a barrier).
+template <int D, int C, int NTHR, int NKP, typename In>
+__device__ __forceinline__ void h2_stage_first(H2Lds<D, C, NKP>& L, const ChunkPos& p, const float* __restrict__ SH,
+                                               const In* __restrict__ k, const float* __restrict__ gamma,
+                                               const float* __restrict__ lambda, int tid, int& ES, int& EK) {
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    PackedStateRegs<D, NTHR> s0;
+    s0.load(SH + p.hoff, tid);
+    ChunkRowsRegs<D, C, NTHR, In> k0;
+    k0.load(k + p.tok0 * D, p.valid, tid);
+    h2_put_maxima<D, C, NTHR, NKP, In>(L, s0, k0, tid, lane, w);
+    for (int e = tid; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)p.h * D + e];
+    if (w == 0) {
+        const float l = chunk_log_decay(gamma + p.tok0, p.valid, lane);
+        if (lane < C) L.L[lane] = l;
+    }
+    __syncthreads();
+    h2_stage_chunk<D, C, NTHR, NKP, In>(L, s0, k0, tid, ES, EK);
+    __syncthreads();
 }
 
 }  // namespace mesa

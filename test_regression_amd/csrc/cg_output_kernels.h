@@ -428,14 +428,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
     if (!more) return false;
 
     // ---- stage the next chunk ----
-    {
-        const float sm = wave_max(packed_absmax<D, NTHR>(nsh, tid));
-        const float km = wave_max(rows_absmax<D, C, NTHR, In>(nk));
-        if (lane == 0) {
-            L.red[0][W] = sm;
-            L.red[1][W] = km;
-        }
-    }
+    h2_put_maxima<D, C, NTHR, NKP, In>(L, nsh, nk, tid, lane, W);
     if (W == 0) {
         const float l = chunk_log_decay_of(ngam, pn.valid, lane);
         if (lane < C) L.L[lane] = l;
@@ -446,17 +439,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
         if (e < D) L.Lam[e] = nlam[u];
     }
     __syncthreads();   // (C) every wave is done with V_c; the next chunk's maxima are in
-    float smax = 0.f, kmax = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) {
-        smax = fmaxf(smax, L.red[0][w2]);
-        kmax = fmaxf(kmax, L.red[1][w2]);
-    }
-    ES = __builtin_amdgcn_readfirstlane(h2_exp(smax));
-    EK = __builtin_amdgcn_readfirstlane(h2_exp(kmax));
-    stage_h2_state<D, NTHR>(L.S, nsh, tid, pow2(ES));
-    stage_h2_rows<D, C, NTHR, NKP, In>(L.KR, nk, tid, pow2(EK));
-    stage_h2_transposed<D, C, NTHR, NKP, In>(L.KT, nk, tid, pow2(EK));
+    h2_stage_chunk<D, C, NTHR, NKP, In>(L, nsh, nk, tid, ES, EK);
     __syncthreads();   // (D)
     p = pn;
     return true;
@@ -482,38 +465,9 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_h2_kernel(
     int ES, EK;
 
     // ---- the first chunk ----
-    {
-        PackedStateRegs<D, NTHR> s0;
-        s0.load(SH + p.hoff, tid0);
-        ChunkRowsRegs<D, C, NTHR, In> k0;
-        k0.load(k + p.tok0 * D, p.valid, tid0);
-        const float sm = wave_max(packed_absmax<D, NTHR>(s0, tid0));
-        const float km = wave_max(rows_absmax<D, C, NTHR, In>(k0));
-        if (lane == 0) {
-            L.red[0][w] = sm;
-            L.red[1][w] = km;
-        }
-        for (int e = tid0; e < D; e += NTHR) L.Lam[e] = lambda[(size_t)p.h * D + e];
-        if (w == 0) {
-            const float l = chunk_log_decay(gamma + p.tok0, p.valid, lane);
-            if (lane < C) L.L[lane] = l;
-        }
-        __syncthreads();
-        float smax = 0.f, kmax = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            smax = fmaxf(smax, L.red[0][w2]);
-            kmax = fmaxf(kmax, L.red[1][w2]);
-        }
-        ES = __builtin_amdgcn_readfirstlane(h2_exp(smax));
-        EK = __builtin_amdgcn_readfirstlane(h2_exp(kmax));
-        stage_h2_state<D, NTHR>(L.S, s0, tid0, pow2(ES));
-        stage_h2_rows<D, C, NTHR, NKP, In>(L.KR, k0, tid0, pow2(EK));
-        stage_h2_transposed<D, C, NTHR, NKP, In>(L.KT, k0, tid0, pow2(EK));
-    }
+    h2_stage_first<D, C, NTHR, NKP, In>(L, p, SH, k, gamma, lambda, tid0, ES, EK);
     Raw4<In> qr[NT];
     load_queries<D, In>(qr, q, p.tok0, p.valid, 16 * w + (lane & 15), lane >> 4);
-    __syncthreads();
 
     for (bool more = true; more;) {
         int tid = tid0;

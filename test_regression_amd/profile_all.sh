@@ -33,8 +33,8 @@ $PS --kernel "decode_kernel<128, false, float>" --command "$CMD" --sources $C/de
     > profiles/decode_f32_d128_N256_traffic.json
 $PS --kernel "qk_preprocess_kernel<128, mesa::bf16_t, mesa::bf16_t>" --command "$CMD" \
     --sources $C/qk_preprocess.hip $C/mesa_device.h > profiles/qk_preprocess_bf16_d128_T4096_W4_traffic.json
-$PS --kernel "bwd_adjoint_split_kernel<128, 64>" --command "$CMD" \
-    --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_split.h $C/persistent.h $C/mesa_device.h \
+$PS --kernel "bwd_adjoint_h2_kernel<128, 64, mesa::bf16_t>" --command "$CMD" \
+    --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_h2.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_adjoint_layer_bf16_d128_T4096_traffic.json
 $PS --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$CMD" --sources $C/bwd_kv.hip $C/mesa_device.h \
     > profiles/bwd_kv_layer_bf16_d128_T4096_traffic.json
@@ -53,8 +53,8 @@ $PM --kernel "$K2" --first 4 --alg-flops 825170591744 \
     --command "$MCMD; first 4 dispatches = the headline forward" > profiles/cg_h2_layer_bf16_d128_T4096_mfma.json
 $PM --kernel "$K2F" --first 4 --alg-flops 329013330944 \
     --command "$MCMD; first 4 dispatches = the dynamic-stopping forward" > profiles/cg_h2_dynamic_f32_d128_T8192_mfma.json
-$PM --kernel "bwd_adjoint_split_kernel<128, 64>" --alg-flops 851074613248 --command "$MCMD" \
-    --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_split.h $C/persistent.h $C/mesa_device.h \
+$PM --kernel "bwd_adjoint_h2_kernel<128, 64, mesa::bf16_t>" --alg-flops 851074613248 --command "$MCMD" \
+    --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_h2.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_adjoint_layer_bf16_d128_T4096_mfma.json
 $PM --kernel "chunk_states_kernel<128, 64, 4, 2, mesa::bf16_t, true>" --first 4 --command "$MCMD; first 4 dispatches = the headline forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_mfma.json

@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CG_SOURCES = ["test_regression_amd/csrc/cg_output.hip", "test_regression_amd/csrc/cg_output_bf16.hip",
               "test_regression_amd/csrc/cg_output_kernels.h", "test_regression_amd/csrc/cg_h2.h",
               "test_regression_amd/csrc/cg_core.h", "test_regression_amd/csrc/persistent.h",
-              "test_regression_amd/csrc/mesa_device.h", "test_regression_amd/csrc/cg_split.h"]
+              "test_regression_amd/csrc/mesa_device.h"]
 
 
 def cg_source_hash(sources=None) -> str:
