@@ -171,9 +171,10 @@ mesa_status mesa_forward_noalloc(const void *q, const void *k, const void *v, in
 /*
  * Bytes of device workspace mesa_backward needs: the forward chunk states
  * (as mesa_forward_workspace_bytes counts them, without its tail), two
- * d x d reverse states per chunk and head (d^2 floats each), two floats per
- * token, d floats per chunk, head and 16 tokens of the chunk, and a 256-byte
- * tail (the adjoint kernel's chunk-claim counter).  0 if invalid.
+ * d x d reverse states per chunk and head (d^2 floats each, with d/16
+ * exponents each), two floats per token, d floats per chunk, head and 16
+ * tokens of the chunk, and a 256-byte tail (the adjoint kernel's chunk-claim
+ * counter).  0 if invalid.
  */
 size_t mesa_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 

@@ -26,23 +26,30 @@
 // tiles are the A operand both ways, read along rows for the scores and
 // down columns for the sums over tokens.  Every MFMA chain starts from zero
 // and is only read afterwards.
+#include "cg_h2.h"
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
 namespace mesa {
 
-// Per-wave scratch of the P block transposes: one diagonal of NT blocks,
-// element (row, col) of block a at a * kTrBlock + (row / 4) * kTrPitch + 4 col + row % 4
-// (pitch 68: the transposed reads of a block hit 64 distinct banks).
+// Per-wave scratch of the P block transposes.  d = 16 (fp32 states): one
+// block, element (row, col) at (row / 4) * kTrPitch + 4 col + row % 4 (pitch
+// 68: the transposed reads hit 64 distinct banks).  d >= 32 (fp16 states):
+// one 2 x 2 super-block as rows of P^T, two planes (hi, lo) of 32 rows x 32
+// halves, rows kTrRow words apart (24: the eight rows a half-wave's
+// transposed read touches fall on distinct 8-bank windows).
 constexpr int kTrPitch = 68;
 constexpr int kTrBlock = 4 * kTrPitch;
+constexpr int kTrRow = 24;
+constexpr int kTrPlane = 32 * kTrRow;
 
 template <int D, int C>
 struct alignas(16) KvLds {
     static constexpr int PD = lds_pitch(D);
+    static constexpr int TRW = D >= 32 ? 2 * kTrPlane : (D / 16) * kTrBlock;   // scratch words per wave
     float R[3 * C * PD];   // x, z, g rows of the chunk
     float L[C];
-    float Tr[C / 16][(D / 16) * kTrBlock];   // per-wave transpose scratch
+    float Tr[C / 16][TRW];   // per-wave transpose scratch
 };
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
@@ -146,10 +153,149 @@ __device__ __forceinline__ void state_terms(const float* __restrict__ Pg, const 
         for (int r = 0; r < 4; ++r) A2[j][r] -= A3[j][r];
 }
 
+// d >= 32: the stored states are two-part fp16 splits (a lane's 16 bytes:
+// hi then lo of its four values) with an exponent per stored 16-row block
+// (EP for P^gx, EM for M).  P^gx's blocks go by 2 x 2 super-blocks (rows 2A,
+// 2A + 1, columns 2B, 2B + 1), diagonal by diagonal: the accumulator-order
+// pair (2A, b), (2A + 1, b) is a 32-slot operand of (P^gx)^T for A2[b] as it
+// comes; written as rows of P^T into the wave's scratch, the super-block
+// comes back through the transposed LDS read as P's operand pairs (a, 2B),
+// (a, 2B + 1) for A1[a].  An exponent that varies along a contraction (EP[a]
+// for A2, EM[g] for A3) is folded into that operand's split of v or k, so
+// every accumulator chain keeps one scale; the scales are undone at the end.
+template <int D>
+__device__ __forceinline__ void state_terms_h2(const float* __restrict__ Pg, const float* __restrict__ Pz,
+                                               const int* __restrict__ Eg, const int* __restrict__ Ez, int lane,
+                                               const f32x4 (&Kb)[D / 16], const f32x4 (&Vb)[D / 16],
+                                               f32x4 (&A1)[D / 16], f32x4 (&A2)[D / 16], float* trf) {
+    constexpr int NT = D / 16;
+    constexpr int NP = NT / 2;
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    uint32_t* tr = reinterpret_cast<uint32_t*>(trf);
+    const int m = lane & 15, q = lane >> 4;
+    int EP[NT], EM[NT];
+    int cP = 1 << 30, cM = 1 << 30;
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+        EP[a] = Eg[a];
+        EM[a] = Ez[a];
+        cP = min(cP, EP[a]);
+        cM = min(cM, EM[a]);
+    }
+    // per-key exponents (the B operand's columns are the wave's keys)
+    const int EK = h2_exp(kslot_max(absmax<NT>(Kb)));
+    const int EV = h2_exp(kslot_max(absmax<NT>(Vb)));
+    f16x8 Kh[NP], Kl[NP], Mh[NP], Ml[NP], Vh[NP], Vl[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+        h2_split(Kb[2 * pp], Kb[2 * pp + 1], pow2(EK), Kh[pp], Kl[pp]);
+        h2_split2(Kb[2 * pp], Kb[2 * pp + 1], pow2(EK + cM - EM[2 * pp]), pow2(EK + cM - EM[2 * pp + 1]), Mh[pp],
+                  Ml[pp]);
+        h2_split2(Vb[2 * pp], Vb[2 * pp + 1], pow2(EV + cP - EP[2 * pp]), pow2(EV + cP - EP[2 * pp + 1]), Vh[pp],
+                  Vl[pp]);
+    }
+    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 A3[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) A1[j] = A2[j] = A3[j] = zero;
+    auto ld = [&](const float* P, int a, int b) {
+        return *reinterpret_cast<const u32x4v*>(P + (a * NT + b) * 256 + 4 * lane);
+    };
+    // operand of two stacked blocks' plane pl (0: hi, 1: lo)
+    auto pair = [](const u32x4v& u, const u32x4v& v, int pl) {
+        typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+        return __builtin_bit_cast(f16x8, pl == 0 ? u32x4s{u[0], u[1], v[0], v[1]} : u32x4s{u[2], u[3], v[2], v[3]});
+    };
+    u32x4v blk[2][2][2];   // [buffer][i][jb]: block (2A + i, 2B + jb)
+    auto load_sb = [&](int s, int buf) {
+        const int A = s % NP, B = (A + s / NP) % NP;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) blk[buf][i][jb] = ld(Pg, 2 * A + i, 2 * B + jb);
+    };
+    load_sb(0, 0);
+#pragma unroll
+    for (int s = 0; s < NP * NP; ++s) {
+        const int A = s % NP, B = (A + s / NP) % NP, cb = s & 1;
+        // the super-block as rows of P^T: row 16 jb + m, words 8 i + 2 q (P rows 16 i + 4 q .. + 3)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+                    *reinterpret_cast<uint2*>(&tr[pl * kTrPlane + (16 * jb + m) * kTrRow + 8 * i + 2 * q]) =
+                        make_uint2(blk[cb][i][jb][2 * pl], blk[cb][i][jb][2 * pl + 1]);
+        if (s + 1 < NP * NP) load_sb(s + 1, cb ^ 1);
+        // A2[b] += P^T_op(b, 2A..2A+1) v(2A..2A+1)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const f16x8 oh = pair(blk[cb][0][jb], blk[cb][1][jb], 0), ol = pair(blk[cb][0][jb], blk[cb][1][jb], 1);
+            f32x4& acc = A2[2 * B + jb];
+            acc = mfma_f16x32(ol, Vh[A], acc);
+            acc = mfma_f16x32(oh, Vl[A], acc);
+            acc = mfma_f16x32(oh, Vh[A], acc);
+        }
+        wave_lds_sync();
+        // A1[a] += P_op(a, 2B..2B+1) k(2B..2B+1): lane (m, q) receives P[16 a + m][16 b + 4 q + e]
+        f16x8 op[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int pl = 0; pl < 2; ++pl) {
+                const uint32_t* base = &tr[pl * kTrPlane + (4 * q + (m >> 2)) * kTrRow + 8 * i + 2 * (m & 3)];
+                const f16x4 t0 = lds_tr_f16x4(base), t1 = lds_tr_f16x4(base + 16 * kTrRow);
+                op[i][pl] = f16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            f32x4& acc = A1[2 * A + i];
+            acc = mfma_f16x32(op[i][1], Kh[B], acc);
+            acc = mfma_f16x32(op[i][0], Kl[B], acc);
+            acc = mfma_f16x32(op[i][0], Kh[B], acc);
+        }
+    }
+    // rows of M = P^zx + (P^zx)^T: M's operand-order block (j, g) is its stored
+    // accumulator-order block (g, j), M being symmetric
+    u32x4v zb[2][2][NT];   // [buffer][g parity][j]
+    auto load_z = [&](int G, int buf) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            zb[buf][0][j] = ld(Pz, 2 * G, j);
+            zb[buf][1][j] = ld(Pz, 2 * G + 1, j);
+        }
+    };
+    load_z(0, 0);
+#pragma unroll
+    for (int G = 0; G < NP; ++G) {
+        if (G + 1 < NP) load_z(G + 1, (G + 1) & 1);
+        const int cb = G & 1;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) A3[j] = mfma_f16x32(pair(zb[cb][0][j], zb[cb][1][j], 1), Mh[G], A3[j]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) A3[j] = mfma_f16x32(pair(zb[cb][0][j], zb[cb][1][j], 0), Ml[G], A3[j]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) A3[j] = mfma_f16x32(pair(zb[cb][0][j], zb[cb][1][j], 0), Mh[G], A3[j]);
+    }
+    const float s2 = pow2(-(EV + cP)), s3 = pow2(-(EK + cM));
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const float s1 = pow2(-(EK + EP[j]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            A1[j][r] *= s1;
+            A2[j][r] = s2 * A2[j][r] - s3 * A3[j][r];
+        }
+    }
+}
+
 template <int D, int C, int W, typename In>
 __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __restrict__ k,
                                         const In* __restrict__ v, size_t tok0, int valid,
                                         const float* __restrict__ Pgx, const float* __restrict__ Pzx,
+                                        const int* __restrict__ Egx, const int* __restrict__ Ezx,
                                         float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ akey) {
     constexpr int NT = D / 16;
     constexpr int NW = C / 16;
@@ -171,7 +317,8 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
 
     // ---- the later chunks, through the reverse states (while the tiles land) ----
     f32x4 DV[NT], DK[NT];
-    state_terms<D>(Pgx, Pzx, lane, Kb, Vb, DV, DK, L.Tr[W]);
+    if constexpr (D >= 32) state_terms_h2<D>(Pgx, Pzx, Egx, Ezx, lane, Kb, Vb, DV, DK, L.Tr[W]);
+    else state_terms<D>(Pgx, Pzx, lane, Kb, Vb, DV, DK, L.Tr[W]);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct tile loads are in LDS
     __syncthreads();                 // and every wave's, and the log decays
     const float li = L.L[il];
@@ -259,7 +406,8 @@ template <int D, int C, typename In>
 __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
     const In* __restrict__ k, const In* __restrict__ v, const float* __restrict__ gamma,
     const float* __restrict__ x, const float* __restrict__ z, const float* __restrict__ gout,
-    const float* __restrict__ Pgx, const float* __restrict__ Pzx, int T, int n_chunks,
+    const float* __restrict__ Pgx, const float* __restrict__ Pzx, const int* __restrict__ Egx,
+    const int* __restrict__ Ezx, int T, int n_chunks,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ akey) {
     constexpr int NW = C / 16;
     constexpr int PD = lds_pitch(D);
@@ -295,14 +443,17 @@ __global__ __launch_bounds__(64 * (C / 16)) void bwd_kv_kernel(
 
     const float* pg = Pgx + soff;
     const float* pz = Pzx + soff;
+    const size_t eoff = ((size_t)bh * n_chunks + c) * (D / 16);   // the states' exponents (d >= 32)
+    const int* eg = Egx + eoff;
+    const int* ez = Ezx + eoff;
     if (w == 0) {
-        kv_wave<D, C, 0, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
+        kv_wave<D, C, 0, In>(L, lane, k, v, tok0, valid, pg, pz, eg, ez, dk, dv, akey);
     } else if constexpr (NW > 1) {
         if (w == 1) {
-            kv_wave<D, C, 1, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
+            kv_wave<D, C, 1, In>(L, lane, k, v, tok0, valid, pg, pz, eg, ez, dk, dv, akey);
         } else if constexpr (NW > 2) {
-            if (w == 2) kv_wave<D, C, 2, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
-            else kv_wave<D, C, 3, In>(L, lane, k, v, tok0, valid, pg, pz, dk, dv, akey);
+            if (w == 2) kv_wave<D, C, 2, In>(L, lane, k, v, tok0, valid, pg, pz, eg, ez, dk, dv, akey);
+            else kv_wave<D, C, 3, In>(L, lane, k, v, tok0, valid, pg, pz, eg, ez, dk, dv, akey);
         }
     }
 }
@@ -311,7 +462,8 @@ template <int D, int C, typename In>
 static hipError_t launch_t(const BwdKvArgs& a, hipStream_t s) {
     const long grid = a.BH * a.n_chunks;
     hipLaunchKernelGGL((bwd_kv_kernel<D, C, In>), dim3((unsigned)grid), dim3(64 * (C / 16)), 0, s, (const In*)a.k,
-                       (const In*)a.v, a.gamma, a.x, a.z, a.gout, a.Pgx, a.Pzx, a.T, a.n_chunks, a.dk, a.dv, a.akey);
+                       (const In*)a.v, a.gamma, a.x, a.z, a.gout, a.Pgx, a.Pzx, a.Egx, a.Ezx, a.T, a.n_chunks, a.dk,
+                       a.dv, a.akey);
     return hipGetLastError();
 }
 

@@ -25,7 +25,12 @@
 // operand order (lane 16q + m holds columns 4q..4q+3 of row m): the key/value
 // kernel reads P^gx's blocks so as rows of (P^gx)^T, and passes them through a
 // per-wave LDS transpose for the rows of P^gx.  M, being symmetric, needs no
-// transpose: its block (g, j) is its block (j, g) in operand order.
+// transpose: its block (g, j) is its block (j, g) in operand order.  For
+// d >= 32 a lane's 16 bytes are the two-part fp16 split (cg_h2.h) of its four
+// values, hi then lo, scaled by 2^E with one exponent E per 16-row block
+// (the wave's slab) and chunk, stored beside the states; for d = 16 the four
+// floats themselves.
+#include "cg_h2.h"
 #include "mesa_device.h"
 #include "mesa_kernels.h"
 
@@ -35,7 +40,7 @@ template <int D, int C, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     const float* __restrict__ g, const float* __restrict__ z, const float* __restrict__ x,
     const float* __restrict__ gamma, int T, int n_chunks, float* __restrict__ Pgx, float* __restrict__ Pzx,
-    long BH) {
+    int* __restrict__ Egx, int* __restrict__ Ezx, long BH) {
     constexpr int RB = D / (16 * NW);   // row blocks per state
     constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
@@ -72,6 +77,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     const bool sym = which == 1;   // M = P^zx + (P^zx)^T
     const size_t pstride = (size_t)D * D;   // floats per chunk
     float* Pout = (which == 0 ? Pgx : Pzx) + (size_t)bh * n_chunks * pstride;
+    int* Eout = (which == 0 ? Egx : Ezx) + (size_t)bh * n_chunks * NT;
     const int a0 = m0 / 16;        // the wave's row block
 
     f32x4 acc[NT];
@@ -126,13 +132,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
         __syncthreads();
         if (c > 0) prefetch(c - 1);
 
-        // ---- the state of the tokens after this chunk: blocks (a0, j) ----
-        {
-            float* dst = Pout + (size_t)c * pstride + 4 * lane;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) store_nt(dst + (a0 * NT + j) * 256, acc[j]);
-        }
-
         // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain);
         //      M also gains sum_t e^{l_t} x_t z_t^T ----
         f32x4 U[NT];
@@ -160,6 +159,35 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
                 }
             }
         }
+        // ---- the state of the tokens after this chunk, blocks (a0, j): stored
+        //      while the update's MFMAs run ----
+        {
+            float* dst = Pout + (size_t)c * pstride + 4 * lane;
+            if constexpr (D >= 32) {
+                const int E = h2_exp(wave_max(absmax<NT>(acc)));
+                const float sc = pow2(E);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    f16x4 h, l;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float y = acc[j][r] * sc;
+                        h[r] = (_Float16)y;
+                        l[r] = (_Float16)(y - (float)h[r]);
+                    }
+                    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+                    const u32x2v hw = __builtin_bit_cast(u32x2v, h), lw = __builtin_bit_cast(u32x2v, l);
+                    store_nt(dst + (a0 * NT + j) * 256,
+                             f32x4{__uint_as_float(hw[0]), __uint_as_float(hw[1]), __uint_as_float(lw[0]),
+                                   __uint_as_float(lw[1])});
+                }
+                if (lane == 0) Eout[(size_t)c * NT + a0] = E;
+            } else {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) store_nt(dst + (a0 * NT + j) * 256, acc[j]);
+            }
+        }
+
         const float G = sGam;
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j] = G * acc[j] + U[j];
@@ -173,7 +201,7 @@ static hipError_t launch_t(const BwdStatesArgs& a, hipStream_t s) {
     constexpr int RB = D / (16 * NW);
     const long grid = ((a.BH + 7) / 8) * 8 * 2 * RB;   // heads rounded up to a multiple of 8
     hipLaunchKernelGGL((bwd_states_kernel<D, C, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a.g, a.z, a.x,
-                       a.gamma, a.T, a.n_chunks, a.Pgx, a.Pzx, a.BH);
+                       a.gamma, a.T, a.n_chunks, a.Pgx, a.Pzx, a.Egx, a.Ezx, a.BH);
     return hipGetLastError();
 }
 

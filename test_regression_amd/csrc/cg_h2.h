@@ -70,11 +70,20 @@ __device__ __forceinline__ float kslot_max(float v) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Largest magnitude over all 64 lanes.
+// Largest value over all 64 lanes, with lane permutes only (no LDS): within
+// each row of 16 lanes over pairs and quads (DPP quad_perm [1,0,3,2] and
+// [2,3,0,1]), halves (row_half_mirror) and the row (row_mirror), then across
+// the four rows as kslot_max.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_f32<0xb1>(v));
+    v = fmaxf(v, dpp_f32<0x4e>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    return kslot_max(v);
 }
 
 template <int N>
@@ -92,6 +101,17 @@ __device__ __forceinline__ void h2_split(const f32x4& a, const f32x4& b, float s
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float y = (e < 4 ? a[e] : b[e - 4]) * s;
+        const _Float16 h = (_Float16)y;
+        H[e] = h;
+        L[e] = (_Float16)(y - (float)h);
+    }
+}
+
+// The same with a scale per 4-element piece (sa for a, sb for b).
+__device__ __forceinline__ void h2_split2(const f32x4& a, const f32x4& b, float sa, float sb, f16x8& H, f16x8& L) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float y = e < 4 ? a[e] * sa : b[e - 4] * sb;
         const _Float16 h = (_Float16)y;
         H[e] = h;
         L[e] = (_Float16)(y - (float)h);

@@ -284,7 +284,7 @@ mesa_status mesa_forward_noalloc(const void* q, const void* k, const void* v, in
 // Backward workspace: forward chunk states, reverse states, per-token totals,
 // per-chunk regulariser sums; every segment a multiple of 4 floats.
 struct BwdLayout {
-    size_t sh, sg, pgx, pzx, beta, akey, lam, counter, total;   // offsets in floats
+    size_t sh, sg, pgx, pzx, egx, ezx, beta, akey, lam, counter, total;   // offsets in floats
 };
 
 // lam: one d-vector per chunk and 16-token wave of the adjoint kernel;
@@ -298,6 +298,8 @@ static BwdLayout bwd_layout(long BH, int T, int d, long nc, int chunk) {
     l.sg = o;   o += r4((size_t)BH * nc * d * d);
     l.pgx = o;  o += r4((size_t)BH * nc * d * d);   // P^gx, accumulator block order
     l.pzx = o;  o += r4((size_t)BH * nc * d * d);   // P^zx + (P^zx)^T, accumulator block order
+    l.egx = o;  o += r4((size_t)BH * nc * (d / 16));   // their exponents per 16-row block (d >= 32)
+    l.ezx = o;  o += r4((size_t)BH * nc * (d / 16));
     l.beta = o; o += r4((size_t)BH * T);
     l.akey = o; o += r4((size_t)BH * T);
     l.lam = o;  o += r4((size_t)BH * nc * waves * d);
@@ -373,12 +375,15 @@ mesa_status mesa_backward(const void* k, const void* v, int qkv_dtype, const flo
     }
     {
         mesa::BwdStatesArgs a{grad_out, grad_q, x, gamma, BH, T, dk, chunk, (int)n_chunks, ws + lay.pgx,
-                              ws + lay.pzx};
+                              ws + lay.pzx, reinterpret_cast<int*>(ws + lay.egx),
+                              reinterpret_cast<int*>(ws + lay.ezx)};
         e = timed_launch(MESA_KERNEL_BWD_STATES, s, [&] { return mesa::launch_bwd_states(a, s); });
         if (e != hipSuccess) return hip_fail(e, "backward state kernel launch");
     }
     {
-        mesa::BwdKvArgs a{k, v, gamma, x, grad_q, grad_out, ws + lay.pgx, ws + lay.pzx, BH, T, dk, chunk,
+        mesa::BwdKvArgs a{k, v, gamma, x, grad_q, grad_out, ws + lay.pgx, ws + lay.pzx,
+                          reinterpret_cast<const int*>(ws + lay.egx), reinterpret_cast<const int*>(ws + lay.ezx),
+                          BH, T, dk, chunk,
                           (int)n_chunks, bf16, grad_k, grad_v, ws + lay.akey};
         e = timed_launch(MESA_KERNEL_BWD_KV, s, [&] { return mesa::launch_bwd_kv(a, s); });
         if (e != hipSuccess) return hip_fail(e, "backward key/value kernel launch");

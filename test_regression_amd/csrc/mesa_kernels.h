@@ -60,10 +60,12 @@ struct BwdStatesArgs {
     const float* g; const float* z; const float* x; const float* gamma;
     long BH; int T; int d; int chunk; int n_chunks;
     float* Pgx; float* Pzx;
+    int* Egx; int* Ezx;   // d >= 32: the states' exponents per (head, chunk, row block)
 };
 struct BwdKvArgs {
     const void* k; const void* v; const float* gamma; const float* x; const float* z; const float* gout;
     const float* Pgx; const float* Pzx;
+    const int* Egx; const int* Ezx;
     long BH; int T; int d; int chunk; int n_chunks; int bf16;
     float* dk; float* dv; float* akey;
 };

@@ -251,7 +251,8 @@ def test_backward_workspace_bytes():
     B, H, T, d, C = 2, 3, 130, 64, 64
     nc = 3
     waves = C // 16   # per-wave partial sums of z (.) x per chunk
-    want = (r4(B * H * nc * d * (d + 16) // 2) + r4(B * H * nc * d * d) + r4(B * H * nc * d * d) + r4(B * H * nc * d * d)
+    want = (r4(B * H * nc * d * (d + 16) // 2) + 3 * r4(B * H * nc * d * d)
+            + 2 * r4(B * H * nc * (d // 16))   # the reverse states' exponents per 16-row block
             + 2 * r4(B * H * T)
             + r4(B * H * nc * waves * d) + 64) * 4   # + the 256-byte chunk-claim counter
     assert f(B, H, T, d, d, C) == want
