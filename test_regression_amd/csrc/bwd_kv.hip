@@ -36,8 +36,10 @@ namespace mesa {
 // block, element (row, col) at (row / 4) * kTrPitch + 4 col + row % 4 (pitch
 // 68: the transposed reads hit 64 distinct banks).  d >= 32 (fp16 states):
 // one 2 x 2 super-block as rows of P^T, two planes (hi, lo) of 32 rows x 32
-// halves, rows kTrRow words apart (24: the eight rows a half-wave's
-// transposed read touches fall on distinct 8-bank windows).
+// halves, rows kTrRow words apart and rows 8..15 of each 16 shifted by 4
+// words (kTrRow = 24: the eight rows a half-wave's transposed read touches
+// fall on distinct 8-bank windows; the shift puts the sixteen rows a
+// half-wave's writes touch on distinct 4-bank windows).
 constexpr int kTrPitch = 68;
 constexpr int kTrBlock = 4 * kTrPitch;
 constexpr int kTrRow = 24;
@@ -225,7 +227,8 @@ __device__ __forceinline__ void state_terms_h2(const float* __restrict__ Pg, con
             for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
                 for (int pl = 0; pl < 2; ++pl)
-                    *reinterpret_cast<uint2*>(&tr[pl * kTrPlane + (16 * jb + m) * kTrRow + 8 * i + 2 * q]) =
+                    *reinterpret_cast<uint2*>(
+                        &tr[pl * kTrPlane + (16 * jb + m) * kTrRow + 4 * (m >> 3) + 8 * i + 2 * q]) =
                         make_uint2(blk[cb][i][jb][2 * pl], blk[cb][i][jb][2 * pl + 1]);
         if (s + 1 < NP * NP) load_sb(s + 1, cb ^ 1);
         // A2[b] += P^T_op(b, 2A..2A+1) v(2A..2A+1)
@@ -244,7 +247,8 @@ __device__ __forceinline__ void state_terms_h2(const float* __restrict__ Pg, con
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int pl = 0; pl < 2; ++pl) {
-                const uint32_t* base = &tr[pl * kTrPlane + (4 * q + (m >> 2)) * kTrRow + 8 * i + 2 * (m & 3)];
+                const int row = 4 * q + (m >> 2);   // of 16 (jb = 0; jb = 1 adds 16 rows)
+                const uint32_t* base = &tr[pl * kTrPlane + row * kTrRow + 4 * (row >> 3) + 8 * i + 2 * (m & 3)];
                 const f16x4 t0 = lds_tr_f16x4(base), t1 = lds_tr_f16x4(base + 16 * kTrRow);
                 op[i][pl] = f16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
             }
