@@ -136,6 +136,7 @@ struct alignas(16) H2Lds {
     float L[C];                // l_i
     float Lam[D];
     float red[3][4];           // per-wave maxima: chunk state, keys, values
+    int gexp[D / 16];          // exponents of G_c's row blocks while its planes take the state's place
     int next;                  // the claimed next chunk
 };
 

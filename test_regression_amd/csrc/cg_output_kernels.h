@@ -336,10 +336,30 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
     }
 
     // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
+    // With at most two row blocks of G_c per wave (GL), the G_c term runs
+    // after barrier (B) on fp16 MFMAs: each wave loads its row blocks of G_c
+    // now, splits them after barrier (A) into two fp16 planes in the freed
+    // state region (one exponent per row block), and after (B) every wave
+    // reads them there.  Otherwise it streams the fp32 blocks onto fp32
+    // MFMAs before (A).
+    constexpr int RBW = (NT + NW - 1) / NW;   // row blocks of G_c a wave splits
+    constexpr bool GL = RBW <= 2;
+    const int g_row0 = W * RBW;
+    f32x4 gr[GL ? RBW : 1][NT];
+    if constexpr (GL) {
+        const float* gl = SG + p.soff + 4 * lane;
+#pragma unroll
+        for (int i = 0; i < RBW; ++i)
+#pragma unroll
+            for (int g = 0; g < NT; ++g)
+                gr[i][g] = g_row0 + i < NT ? *reinterpret_cast<const f32x4*>(gl + ((g_row0 + i) * NT + g) * 256)
+                                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     ChunkRowsRegs<D, C, NTHR, In> vrows;
     vrows.load(v + p.tok0 * D, p.valid, tid);
     f32x4 Wo[2 * Wv::NS];
     const int EX = h2_exp(kslot_max(absmax<NT>(X)));
+    f16x8 Xh[NQ], Xl[NQ];   // the solution's split, 2^EX
     {
         const float sX = pow2(EX);
         constexpr int NP = h2_score_parts<Wv::NBO, NKP>();
@@ -350,9 +370,8 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
             for (int t = 0; t < NP; ++t) Sc[ib][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int qq = 0; qq < NQ; ++qq) {
-            f16x8 Xh, Xl;
-            h2_split(X[2 * qq], X[2 * qq + 1], sX, Xh, Xl);
-            h2_scores_step<D, C, NKP, Wv::NBO>(L, qq, Xh, Xl, n, kk, Sc);
+            h2_split(X[2 * qq], X[2 * qq + 1], sX, Xh[qq], Xl[qq]);
+            h2_scores_step<D, C, NKP, Wv::NBO>(L, qq, Xh[qq], Xl[qq], n, kk, Sc);
         }
 #pragma unroll
         for (int ib = 0; ib < 2 * Wv::NS; ++ib)
@@ -367,7 +386,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
     f32x4 OS[NT], OI[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) OS[j] = OI[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
+    if constexpr (!GL) {
         const float* gl = SG + p.soff + 4 * lane;
         constexpr int NB_G = 3;
         f32x4 ga[NB_G][NT];
@@ -391,6 +410,33 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
         if (lane == 0) L.red[2][W] = vm;
     }
     __syncthreads();   // (A) every wave is done with the state planes, K_c rows and K_c^T, l and lambda
+    if constexpr (GL) {
+        // the wave's row blocks of G_c as two fp16 planes where the state's were:
+        // row 16 j + n, columns 16 g + 4 kk .. + 3 (perm32)
+        constexpr int SW = H2Lds<D, C, NKP>::SW;
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+            const int j = g_row0 + i;
+            if (j < NT) {
+                const int E = h2_exp(wave_max(absmax<NT>(gr[i])));
+                const float sg = pow2(E);
+#pragma unroll
+                for (int g = 0; g < NT; ++g) {
+                    f16x4 h, lo;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float y = gr[i][g][r] * sg;
+                        h[r] = (_Float16)y;
+                        lo[r] = (_Float16)(y - (float)h[r]);
+                    }
+                    const int w0 = (16 * j + n) * SW + perm32(16 * g + 4 * kk) / 2;
+                    *reinterpret_cast<f16x4*>(&L.S[0][w0]) = h;
+                    *reinterpret_cast<f16x4*>(&L.S[1][w0]) = lo;
+                }
+                if (lane == 0) L.gexp[j] = E;
+            }
+        }
+    }
     float vmax = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) vmax = fmaxf(vmax, L.red[2][w2]);
@@ -411,6 +457,26 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
     load_queries<D, In>(qr, q, pn.tok0, more ? pn.valid : 0, tr, kk);
     stage_h2_rows<D, C, NTHR, NKP, In>(L.KR, vrows, tid, pow2(EV));   // V_c rows, where K_c's were
     __syncthreads();   // (B)
+    if constexpr (GL) {
+        // G_c X^T from the planes: three fp16 products per 32-feature step
+        constexpr int SW = H2Lds<D, C, NKP>::SW;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int off = (16 * j + n) * SW + 16 * qq + 4 * kk;
+                const f16x8 Gh = lds_f16x8(&L.S[0][off]), Gl = lds_f16x8(&L.S[1][off]);
+                OS[j] = mfma_f16x32(Gl, Xh[qq], OS[j]);
+                OS[j] = mfma_f16x32(Gh, Xl[qq], OS[j]);
+                OS[j] = mfma_f16x32(Gh, Xh[qq], OS[j]);
+            }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const float sj = pow2(-(L.gexp[j] + EX));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) OS[j][r] *= sj;
+        }
+    }
     {
         const int EWo = h2_exp(kslot_max(absmax<2 * Wv::NS>(Wo)));
         h2_apply<D, C, NKP, Wv::NS>(L, Wo, pow2(EWo), n, kk, OI);
