@@ -197,7 +197,7 @@ __device__ __forceinline__ bool adjoint_wave(CgLds<D, C>& L, int tid, ChunkPos& 
     if (tok_ok) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            store_nt(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk, Z[j]);
+            store_row(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk, Z[j]);
         if (kk == 0) {
             beta[p.tok0 + tr] = b;
             if (z_iters) z_iters[p.tok0 + tr] = it;
@@ -368,7 +368,7 @@ __device__ __forceinline__ bool adjoint_h2_wave(H2Lds<D, C, h2_key_planes<In>()>
     if (tok_ok) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            store_nt(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk, Z[j]);
+            store_row(dq + (p.tok0 + tr) * D + 16 * j + 4 * kk, Z[j]);
         if (kk == 0) {
             beta[p.tok0 + tr] = b;
             if (z_iters) z_iters[p.tok0 + tr] = it;

@@ -398,8 +398,8 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
             kd += Kb[j][r] * DK[j][r];
         }
         if (key_ok) {
-            store_nt(dv + (tok0 + il) * D + 16 * j + 4 * kk, DV[j]);
-            store_nt(dk + (tok0 + il) * D + 16 * j + 4 * kk, DK[j]);
+            store_row(dv + (tok0 + il) * D + 16 * j + 4 * kk, DV[j]);
+            store_row(dk + (tok0 + il) * D + 16 * j + 4 * kk, DK[j]);
         }
     }
     const float a = 0.5f * (kslot_sum(vd) + kslot_sum(kd));

@@ -112,7 +112,7 @@ __device__ __forceinline__ bool cg_wave(CgLds<D, C>& L, int tid, ChunkPos& p, in
     if (iters && kk == 0 && tok_ok) iters[p.tok0 + tr] = it;
     if (x_out && tok_ok) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) store_nt(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk, X[j]);
+        for (int j = 0; j < NT; ++j) store_row(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk, X[j]);
     }
 
     // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
@@ -189,7 +189,7 @@ __device__ __forceinline__ bool cg_wave(CgLds<D, C>& L, int tid, ChunkPos& p, in
             f32x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = cw.eLo * OS[j][r] + OI[j][r];
-            store_nt(out + (p.tok0 + tr) * D + 16 * j + 4 * kk, o);
+            store_row(out + (p.tok0 + tr) * D + 16 * j + 4 * kk, o);
         }
     }
     if (!more) return false;
@@ -332,7 +332,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
     if (iters && kk == 0 && tok_ok) iters[p.tok0 + tr] = it;
     if (x_out && tok_ok) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) store_nt(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk, X[j]);
+        for (int j = 0; j < NT; ++j) store_row(x_out + (p.tok0 + tr) * D + 16 * j + 4 * kk, X[j]);
     }
 
     // ---- output O = diag(e^l) X G_c^T + (M o (X K^T)) V over the whole chunk, transposed ----
@@ -487,7 +487,7 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
                 f32x4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = wv.eLo * OS[j][r] + bo * OI[j][r];
-                store_nt(out + (p.tok0 + tr) * D + 16 * j + 4 * kk, o);
+                store_row(out + (p.tok0 + tr) * D + 16 * j + 4 * kk, o);
             }
         }
     }

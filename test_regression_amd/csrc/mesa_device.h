@@ -79,6 +79,13 @@ __device__ __forceinline__ void store_nt(float* p, f32x4 v) {
 }
 __device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
+// Ordinary (write-back) store of a lane's 16-byte piece of an output row, for
+// row tiles that one store instruction covers only half of each 128-byte
+// line of (lane (n, kk) at row n, floats 16 j + 4 kk .. + 3; the next j
+// writes the other half).  Streaming stores let the L2 write such half-filled
+// lines out more than once: the write counters read up to 1.35x the bytes.
+__device__ __forceinline__ void store_row(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
 // Registers holding 4 prefetched input elements (bf16 stays packed until staged).
 template <typename In> struct Raw4;
 template <> struct Raw4<float> {
