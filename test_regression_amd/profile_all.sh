@@ -36,9 +36,9 @@ $PS --kernel "qk_preprocess_kernel<128, mesa::bf16_t, mesa::bf16_t>" --command "
 $PS --kernel "bwd_adjoint_h2_kernel<128, 64, mesa::bf16_t>" --command "$CMD" \
     --sources $C/bwd_adjoint.hip $C/cg_core.h $C/cg_h2.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_adjoint_layer_bf16_d128_T4096_traffic.json
-$PS --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$CMD" --sources $C/bwd_kv.hip $C/mesa_device.h \
+$PS --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$CMD" --sources $C/bwd_kv.hip $C/cg_h2.h $C/cg_core.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_kv_layer_bf16_d128_T4096_traffic.json
-$PS --kernel "bwd_states_kernel<128, 64, 4>" --command "$CMD" --sources $C/bwd_states.hip $C/mesa_device.h \
+$PS --kernel "bwd_states_kernel<128, 64, 4>" --command "$CMD" --sources $C/bwd_states.hip $C/cg_h2.h $C/cg_core.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_states_layer_bf16_d128_T4096_traffic.json
 $PS --kernel "hawk_stream_kernel<mesa::bf16_t, 8, 8>" --command "$CMD" --sources $C/hawk.hip $C/mesa_device.h \
     > profiles/hawk_stream_bf16_B8_T4096_D2048_traffic.json
@@ -60,7 +60,7 @@ $PM --kernel "chunk_states_kernel<128, 64, 4, 2, mesa::bf16_t, true>" --first 4 
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_layer_bf16_d128_T4096_mfma.json
 $PM --kernel "chunk_states_full_kernel<64, float, true>" --first 4 --command "$MCMD; first 4 dispatches = the dynamic-stopping forward" \
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_dynamic_f32_d128_T8192_mfma.json
-$PM --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$MCMD" --sources $C/bwd_kv.hip $C/mesa_device.h \
+$PM --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$MCMD" --sources $C/bwd_kv.hip $C/cg_h2.h $C/cg_core.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_kv_layer_bf16_d128_T4096_mfma.json
 python -m test_regression_amd.profile_summary stats $OUT/prof_trace/t_kernel_stats.csv \
     --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "$K2" --first 13 \
