@@ -337,7 +337,7 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
 
     // ---- within the chunk: tokens t >= i, one 16-token block at a time ----
     // Each block's sums are fresh MFMA chains, added into DK, DV on the VALU;
-    // dk's pass and dv's pass run one after the other (register pressure).
+    // the value gradient's weights are the negated x_t . k_i weights of dk's.
 #pragma unroll 1
     for (int tb = W; tb < NW; ++tb) {
         const f32x4 s1 = token_scores<D>(X + 16 * tb * PD, Kb, n, kk);    // x_t . k_i
@@ -351,9 +351,9 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
             w23[r] = zeta * (s2[r] - s3[r]);
             wn1[r] = -zeta * s1[r];
         }
-        f32x4 BK[NT];
+        f32x4 BK[NT], BV[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) BK[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NT; ++j) BK[j] = BV[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int t = 16 * tb + 4 * kk + s;
@@ -361,31 +361,14 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
             for (int j = 0; j < NT; ++j) {
                 BK[j] = mfma4(X[t * PD + 16 * j + n], w23[s], BK[j]);
                 BK[j] = mfma4(Zt[t * PD + 16 * j + n], wn1[s], BK[j]);
+                BV[j] = mfma4(Gt[t * PD + 16 * j + n], -wn1[s], BV[j]);
             }
         }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) DK[j] += BK[j];
-    }
-#pragma unroll 1
-    for (int tb = W; tb < NW; ++tb) {
-        const f32x4 s1 = token_scores<D>(X + 16 * tb * PD, Kb, n, kk);    // x_t . k_i
-        f32x4 w1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tb + 4 * kk + r;
-            w1[r] = (t >= il) ? __expf(L.L[t] - li) * s1[r] : 0.f;
+        for (int j = 0; j < NT; ++j) {
+            DK[j] += BK[j];
+            DV[j] += BV[j];
         }
-        f32x4 BV[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) BV[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int t = 16 * tb + 4 * kk + s;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) BV[j] = mfma4(Gt[t * PD + 16 * j + n], w1[s], BV[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) DV[j] += BV[j];
     }
 
     // ---- outputs ----
