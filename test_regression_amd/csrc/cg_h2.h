@@ -118,6 +118,42 @@ __device__ __forceinline__ void h2_split2(const f32x4& a, const f32x4& b, float 
     }
 }
 
+// h2_split's result, bit for bit (up to the sign of a zero hi part), at two
+// instructions per element: v_fma_mixlo/hi_f16 round s x (exact: s is a
+// power of two) to fp16 into the low or high half of the packed hi word, and
+// round s x - hi, formed exactly by the same fused operation with hi read
+// back from its half, into lo's.  The compiler forms hi twice for h2_split
+// (once for the pack, once for the residual), 3.5 instructions per element.
+// Inline asm is opaque to the compiler's hazard bookkeeping, so the block
+// ends with the two wait states an MFMA reading a VALU result needs; its
+// inputs must be VALU results, never an MFMA's (codegen_check.py checks
+// both in the built assembly).
+__device__ __forceinline__ void h2_split_mix(const f32x4& a, const f32x4& b, float s, f16x8& H, f16x8& L) {
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    asm("v_fma_mixlo_f16 %0, %8, %9, 0\n\t"
+        "v_fma_mixhi_f16 %0, %8, %10, 0\n\t"
+        "v_fma_mixlo_f16 %1, %8, %11, 0\n\t"
+        "v_fma_mixhi_f16 %1, %8, %12, 0\n\t"
+        "v_fma_mixlo_f16 %2, %8, %13, 0\n\t"
+        "v_fma_mixhi_f16 %2, %8, %14, 0\n\t"
+        "v_fma_mixlo_f16 %3, %8, %15, 0\n\t"
+        "v_fma_mixhi_f16 %3, %8, %16, 0\n\t"
+        "v_fma_mixlo_f16 %4, %8, %9, -%0 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %4, %8, %10, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixlo_f16 %5, %8, %11, -%1 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %5, %8, %12, -%1 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixlo_f16 %6, %8, %13, -%2 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %6, %8, %14, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixlo_f16 %7, %8, %15, -%3 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %7, %8, %16, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+        "s_nop 1"
+        : "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3), "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3)
+        : "v"(s), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    H = __builtin_bit_cast(f16x8, u32x4{h0, h1, h2, h3});
+    L = __builtin_bit_cast(f16x8, u32x4{l0, l1, l2, l3});
+}
+
 __device__ __forceinline__ f16x8 lds_f16x8(const uint32_t* p) {
     return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(p));
 }
@@ -355,9 +391,15 @@ __device__ __forceinline__ void h2_matvec(const H2Lds<D, C, NKP>& L, const H2Wav
 //    overflows, and while the residuals shrink b' stays within a small
 //    factor of |p|_2, which spends a few of fp16's bits of headroom;
 //  - the state planes of the next four row blocks are read while the current
-//    ones' products run;
+//    ones' products run; with bf16 keys (one key plane) the hi plane of the
+//    state stays in registers for the whole solve instead (128 words per lane
+//    at d = 128, held in accumulator registers, which MFMAs read directly),
+//    and only the lo plane is read per iteration;
 //  - the apply runs row block by row block, and each block's combination
-//    e^{l_t} S p + intra + lambda p and its share of p.Ap follow its MFMAs.
+//    e^{l_t} S p + intra + lambda p and its share of p.Ap follow its MFMAs;
+//    the K^T operands are read two row blocks ahead with bf16 keys, one with
+//    fp32 keys (the first under the last state products), so their LDS
+//    latency does not stall the chain.
 // The intra-chunk terms run over the causal keys from the chunk start.
 template <int D, int C, int NKP, int W>
 __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wave<D, C, W>& wv, int ES, int EK,
@@ -388,19 +430,42 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
     float alpha = 0.f, beta = 0.f;   // of the previous iteration
     float pbound = sqrtf(rr);        // bounds |p|_2, hence max |p|, of the next direction
 
+    // The hi plane held in registers (bf16 keys: the fp32-key kernel needs
+    // those registers for its second key plane, and is slower with it).
+    constexpr bool SREG = NKP == 1;
+    f16x8 SHr[SREG ? NQ : 1][SREG ? NT : 1];
+    if constexpr (SREG) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) SHr[q][i] = lds_f16x8(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]);
+    }
     auto load_group = [&](int f, f16x8 (&A)[JI][2]) {
         const int q = f / NG, g = f % NG;
 #pragma unroll
         for (int h = 0; h < JI; ++h) {
             const int off = (16 * (g * JI + h) + n) * SW + 16 * q + 4 * kk;
-            A[h][0] = lds_f16x8(&L.S[0][off]);
+            if constexpr (!SREG) A[h][0] = lds_f16x8(&L.S[0][off]);
             A[h][1] = lds_f16x8(&L.S[1][off]);
         }
+    };
+    auto load_kt = [&](int j, f16x8 (&A)[Wv::NS][NKP]) {
+#pragma unroll
+        for (int s = 0; s < Wv::NS; ++s)
+#pragma unroll
+            for (int pl = 0; pl < NKP; ++pl) A[s][pl] = h2_kt_operand<D, C, NKP>(L, pl, j, s, n, kk);
     };
 
     for (int itn = 0; itn < max_iters; ++itn) {
         if (!done && (rr < stop_rr || rr == 0.f)) done = true;
         if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        if constexpr (SREG) {
+            // keeps the hi plane in accumulator registers (no instruction)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int i = 0; i < NT; ++i) asm volatile("" : "+a"(SHr[q][i]));
+        }
         const int EP = h2_exp(pbound);
         const float sP = pow2(EP);
         constexpr int NP = h2_score_parts<NB, NKP>();
@@ -412,7 +477,9 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 #pragma unroll
         for (int j = 0; j < NT; ++j) YS[j] = zero;
         // the direction's features 32q .. 32q + 31, after the deferred x
-        // update, and their split
+        // update, and their split (with fp32 keys the plain split: there the
+        // asm block's eight fixed result registers make the compiler move
+        // operands through accumulator registers that MFMAs still read)
         f16x8 Z[NQ][2];
         auto form = [&](int q) {
 #pragma unroll
@@ -422,7 +489,8 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
                     X[jj][r] += alpha * P[jj][r];
                     P[jj][r] = R[jj][r] + beta * P[jj][r];
                 }
-            h2_split(P[2 * q], P[2 * q + 1], sP, Z[q][0], Z[q][1]);
+            if constexpr (NKP == 1) h2_split_mix(P[2 * q], P[2 * q + 1], sP, Z[q][0], Z[q][1]);
+            else h2_split(P[2 * q], P[2 * q + 1], sP, Z[q][0], Z[q][1]);
         };
         // decayed scores W 2^(EK + EP), their per-token exponent and split
         f16x8 Wh[NS], Wl[NS];
@@ -437,9 +505,16 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
             EW = h2_exp(kslot_max(absmax<2 * NS>(Wt)));
             const float sW = pow2(EW);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) h2_split(Wt[2 * s], Wt[2 * s + 1], sW, Wh[s], Wl[s]);
+            for (int s = 0; s < NS; ++s) {
+                if constexpr (NKP == 1) h2_split_mix(Wt[2 * s], Wt[2 * s + 1], sW, Wh[s], Wl[s]);
+                else h2_split(Wt[2 * s], Wt[2 * s + 1], sW, Wh[s], Wl[s]);
+            }
         };
         f16x8 SA[2][JI][2];
+        // K^T operands of row blocks j .. j + KPF (fp32 keys: two planes, one
+        // block ahead, which keeps the ring out of the accumulator registers)
+        constexpr int KPF = NKP == 1 ? 2 : 1;
+        f16x8 KA[KPF + 1][NS][NKP];
         load_group(0, SA[0]);
         form(0);
         // Per step q: the scores, then the state products, with the next
@@ -451,15 +526,24 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int f = q * NG + g;
-                if (f + 1 < NQ * NG) load_group(f + 1, SA[(f + 1) & 1]);
+                if (f + 1 < NQ * NG) {
+                    load_group(f + 1, SA[(f + 1) & 1]);
+                } else {
+                    if constexpr (KPF > 0) load_kt(0, KA[0]);
+                    if constexpr (KPF > 1 && NT > 1) load_kt(1, KA[1]);
+                }
                 const f16x8(&A)[JI][2] = SA[f & 1];
+                auto hi = [&](int h) -> const f16x8& {
+                    if constexpr (SREG) return SHr[q][g * JI + h];
+                    else return A[h][0];
+                };
                 // smallest terms first
 #pragma unroll
                 for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][1], Z[q][0], YS[g * JI + h]);
 #pragma unroll
-                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Z[q][1], YS[g * JI + h]);
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(hi(h), Z[q][1], YS[g * JI + h]);
 #pragma unroll
-                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(A[h][0], Z[q][0], YS[g * JI + h]);
+                for (int h = 0; h < JI; ++h) YS[g * JI + h] = mfma_f16x32(hi(h), Z[q][0], YS[g * JI + h]);
                 if (g == 0) {
                     if (q + 1 < NQ) form(q + 1);
                     else decayed_scores();
@@ -473,13 +557,14 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
         float pp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
+            if (j + KPF < NT) load_kt(j + KPF, KA[(j + KPF) % (KPF + 1)]);
+            const f16x8(&KJ)[NS][NKP] = KA[j % (KPF + 1)];
             f32x4 yi = zero;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const f16x8 A0 = h2_kt_operand<D, C, NKP>(L, 0, j, s, n, kk);
-                yi = mfma_f16x32(A0, Wl[s], yi);
-                if constexpr (NKP == 2) yi = mfma_f16x32(h2_kt_operand<D, C, NKP>(L, 1, j, s, n, kk), Wh[s], yi);
-                yi = mfma_f16x32(A0, Wh[s], yi);
+                yi = mfma_f16x32(KJ[s][0], Wl[s], yi);
+                if constexpr (NKP == 2) yi = mfma_f16x32(KJ[s][1], Wh[s], yi);
+                yi = mfma_f16x32(KJ[s][0], Wh[s], yi);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

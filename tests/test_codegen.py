@@ -1,5 +1,6 @@
 """The gfx950 assembly of every kernel is free of the MFMA accumulator-input
-(SrcC) rewrite hazard described in test_regression_amd/codegen_check.py."""
+(SrcC) rewrite hazard and of the inline-asm wait-state hazards described in
+test_regression_amd/codegen_check.py."""
 import shutil
 
 import pytest
@@ -29,3 +30,32 @@ def test_scanner_flags_the_known_bad_sequence():
     """
     assert len(codegen_check.scan_asm(bad)) == 1
     assert codegen_check.scan_asm(good) == []
+    # a range write by a load is seen too; a later MFMA's destination is not a hazard
+    range_write = bad.replace("v_accvgpr_write_b32 a19, 0", "ds_read_b128 a[16:19], v2")
+    later_mfma = bad.replace("v_accvgpr_write_b32 a19, 0", "v_mfma_f32_16x16x4_f32 a[16:19], v41, v45, 0")
+    assert len(codegen_check.scan_asm(range_write)) == 1
+    assert codegen_check.scan_asm(later_mfma) == []
+
+
+def test_scanner_flags_inline_asm_hazards():
+    mfma_reads_too_soon = """
+    ;;#ASMSTART
+    v_fma_mixlo_f16 v10, v3, v4, 0
+    v_fma_mixhi_f16 v10, v3, v5, 0
+    ;;#ASMEND
+    s_nop 0
+    v_mfma_f32_16x16x32_f16 a[0:3], v[20:23], v[8:11], a[0:3]
+    """
+    waited = mfma_reads_too_soon.replace("s_nop 0", "s_nop 1")
+    reads_mfma_result = """
+    v_mfma_f32_16x16x32_f16 v[4:7], v[20:23], v[24:27], 0
+    v_add_f32_e32 v30, v31, v32
+    ;;#ASMSTART
+    v_fma_mixlo_f16 v10, v3, v5, 0
+    ;;#ASMEND
+    """
+    rewritten_first = reads_mfma_result.replace("v_add_f32_e32 v30, v31, v32", "v_mov_b32_e32 v5, 0")
+    assert len(codegen_check.scan_inline_asm(mfma_reads_too_soon)) == 1
+    assert codegen_check.scan_inline_asm(waited) == []
+    assert len(codegen_check.scan_inline_asm(reads_mfma_result)) == 1
+    assert codegen_check.scan_inline_asm(rewritten_first) == []
