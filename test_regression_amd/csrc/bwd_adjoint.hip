@@ -353,7 +353,8 @@ __device__ __forceinline__ bool adjoint_h2_wave(H2Lds<D, C, h2_key_planes<In>()>
     adjoint_rhs_h2<D, C, NKP, W, In>(L, wv, lane, p, v, SG, gout, o, EK, Bv, go);
 #pragma unroll
     for (int j = 0; j < NT; ++j) lam[j] = lds4(&L.Lam[16 * j + 4 * kk]);
-    const int it = h2_cg_solve<D, C, NKP, W>(L, wv, ES, EK, Bv, Z, lam, max_iters, tol);
+    H2Hi<D, NKP> SHr;   // unused: the solve reads the hi plane itself
+    const int it = h2_cg_solve<D, C, NKP, W, 0, false>(L, wv, ES, EK, Bv, Z, lam, max_iters, tol, L.S[1], SHr);
 
     // ---- H_t x_t, beta, dq ----
     f32x4 Xv[NT], Hx[NT];

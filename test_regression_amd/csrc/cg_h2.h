@@ -176,24 +176,34 @@ struct alignas(16) H2Lds {
     int next;                  // the claimed next chunk
 };
 
-// Per-wave constants of wave W.
-template <int D, int C, int W>
+// Whether the CG kernel's waves 2 and 3 start their state term from the
+// mid-chunk state (d = 128, 64-token chunks, one key plane: the LDS has room
+// for its lo plane beside the chunk state's two).  Their intra-chunk terms
+// then cover two key blocks at most, as wave 1's, instead of four.
+template <int D, int C, int NKP>
+__host__ __device__ constexpr bool h2_mid_state() { return D == 128 && C == 64 && NKP == 1; }
+
+// Per-wave constants of wave W, for intra-chunk terms over the keys from
+// key block KB0 on (an even block: 0, or 2 when the wave's state term starts
+// from the mid-chunk state, the state after token 16 KB0 - 1).
+template <int D, int C, int W, int KB0 = 0>
 struct H2Wave {
-    static constexpr int NBO = W + 1;          // causal key blocks from the chunk start
+    static_assert(KB0 % 2 == 0 && KB0 <= W, "first key block");
+    static constexpr int NBO = W + 1 - KB0;    // causal key blocks from block KB0
     static constexpr int NS = (NBO + 1) / 2;   // 32-key steps of the intra-chunk apply
     int n, kk, tr;
-    float eLo;                 // e^{l_t}
-    float dec[2 * NS][4];      // e^{l_t - l_i}, key i = 16 ib + 4kk + r <= t, else 0
+    float eLo;                 // e^{l_t - l_{16 KB0 - 1}} (e^{l_t} for KB0 = 0)
+    float dec[2 * NS][4];      // e^{l_t - l_i}, key i = 16 (KB0 + ib) + 4kk + r <= t, else 0
     __device__ __forceinline__ H2Wave(const float* Lv, int lane) {
         n = lane & 15;
         kk = lane >> 4;
         tr = 16 * W + n;
-        eLo = __expf(Lv[tr]);
+        eLo = __expf(KB0 ? Lv[tr] - Lv[16 * KB0 - 1] : Lv[tr]);
 #pragma unroll
         for (int ib = 0; ib < 2 * NS; ++ib)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ib + 4 * kk + r;
+                const int i = 16 * (KB0 + ib) + 4 * kk + r;
                 dec[ib][r] = (i <= tr) ? __expf(Lv[tr] - Lv[i < C ? i : C - 1]) : 0.f;
             }
     }
@@ -246,9 +256,9 @@ __device__ __forceinline__ f16x8 h2_vt_operand(const H2Lds<D, C, NKP>& L, int pl
 template <int NB, int NKP>
 __host__ __device__ constexpr int h2_score_parts() { return NB == 1 ? 1 + NKP : 1; }
 
-// Scores of the wave's tokens with key block ib (ib < NB), Sc = K Z^T
+// Scores of the wave's tokens with key block KB0 + ib (ib < NB), Sc = K Z^T
 // 2^(EK + EZ), from the split of Z per 32-feature step.
-template <int D, int C, int NKP, int NB>
+template <int D, int C, int NKP, int NB, int KB0 = 0>
 __device__ __forceinline__ void h2_scores_step(const H2Lds<D, C, NKP>& L, int q, const f16x8& Zh, const f16x8& Zl,
                                                int m, int kk, f32x4 (&Sc)[NB][h2_score_parts<NB, NKP>()]) {
     constexpr int SW = H2Lds<D, C, NKP>::SW;
@@ -257,7 +267,8 @@ __device__ __forceinline__ void h2_scores_step(const H2Lds<D, C, NKP>& L, int q,
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
-        for (int pl = 0; pl < NKP; ++pl) A[ib][pl] = lds_f16x8(&L.KR[pl][(16 * ib + m) * SW + 16 * q + 4 * kk]);
+        for (int pl = 0; pl < NKP; ++pl)
+            A[ib][pl] = lds_f16x8(&L.KR[pl][(16 * (KB0 + ib) + m) * SW + 16 * q + 4 * kk]);
     // smallest terms first
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib) Sc[ib][0] = mfma_f16x32(A[ib][0], Zl, Sc[ib][0]);
@@ -400,12 +411,19 @@ __device__ __forceinline__ void h2_matvec(const H2Lds<D, C, NKP>& L, const H2Wav
 //    the K^T operands are read two row blocks ahead with bf16 keys, one with
 //    fp32 keys (the first under the last state products), so their LDS
 //    latency does not stall the chain.
-// The intra-chunk terms run over the causal keys from the chunk start.
-template <int D, int C, int NKP, int W>
-__device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wave<D, C, W>& wv, int ES, int EK,
+// The state term's planes: the hi plane is L.S[0] (read into registers at
+// the start with bf16 keys), or with HI_GIVEN the registers SHin the caller
+// filled (the mid-chunk state's); the lo plane is Slo (L.S[1], or the
+// mid-chunk state's); both scaled by 2^ES.  The intra-chunk terms run over
+// the causal keys from key block KB0.
+template <int D, int NKP>
+using H2Hi = f16x8[NKP == 1 ? D / 32 : 1][NKP == 1 ? D / 16 : 1];
+
+template <int D, int C, int NKP, int W, int KB0, bool HI_GIVEN>
+__device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wave<D, C, W, KB0>& wv, int ES, int EK,
                                            f32x4 (&R)[D / 16], f32x4 (&X)[D / 16], const f32x4 (&lam)[D / 16],
-                                           int max_iters, float tol) {
-    using Wv = H2Wave<D, C, W>;
+                                           int max_iters, float tol, const uint32_t* Slo, H2Hi<D, NKP>& SHin) {
+    using Wv = H2Wave<D, C, W, KB0>;
     constexpr int NT = D / 16;
     constexpr int NQ = D / 32;
     constexpr int NB = Wv::NBO;
@@ -433,12 +451,16 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
     // The hi plane held in registers (bf16 keys: the fp32-key kernel needs
     // those registers for its second key plane, and is slower with it).
     constexpr bool SREG = NKP == 1;
+    static_assert(SREG || !HI_GIVEN, "given hi planes need one key plane");
+    // a local array (a reference to the caller's makes the compiler hold it
+    // worse), copied from the caller's registers or read from L.S[0]
     f16x8 SHr[SREG ? NQ : 1][SREG ? NT : 1];
     if constexpr (SREG) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int i = 0; i < NT; ++i) SHr[q][i] = lds_f16x8(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]);
+            for (int i = 0; i < NT; ++i)
+                SHr[q][i] = HI_GIVEN ? SHin[q][i] : lds_f16x8(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]);
     }
     auto load_group = [&](int f, f16x8 (&A)[JI][2]) {
         const int q = f / NG, g = f % NG;
@@ -446,14 +468,14 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
         for (int h = 0; h < JI; ++h) {
             const int off = (16 * (g * JI + h) + n) * SW + 16 * q + 4 * kk;
             if constexpr (!SREG) A[h][0] = lds_f16x8(&L.S[0][off]);
-            A[h][1] = lds_f16x8(&L.S[1][off]);
+            A[h][1] = lds_f16x8(&Slo[off]);
         }
     };
     auto load_kt = [&](int j, f16x8 (&A)[Wv::NS][NKP]) {
 #pragma unroll
         for (int s = 0; s < Wv::NS; ++s)
 #pragma unroll
-            for (int pl = 0; pl < NKP; ++pl) A[s][pl] = h2_kt_operand<D, C, NKP>(L, pl, j, s, n, kk);
+            for (int pl = 0; pl < NKP; ++pl) A[s][pl] = h2_kt_operand<D, C, NKP>(L, pl, j, KB0 / 2 + s, n, kk);
     };
 
     for (int itn = 0; itn < max_iters; ++itn) {
@@ -512,8 +534,9 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
         };
         f16x8 SA[2][JI][2];
         // K^T operands of row blocks j .. j + KPF (fp32 keys: two planes, one
-        // block ahead, which keeps the ring out of the accumulator registers)
-        constexpr int KPF = NKP == 1 ? 2 : 1;
+        // block ahead, which keeps the ring out of the accumulator registers;
+        // 16-token chunks, whose operands are half zeros, read in place)
+        constexpr int KPF = C < 32 ? 0 : NKP == 1 ? 2 : 1;
         f16x8 KA[KPF + 1][NS][NKP];
         load_group(0, SA[0]);
         form(0);
@@ -522,7 +545,7 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
         // formed between the first row group's products and the rest.
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            h2_scores_step<D, C, NKP, NB>(L, q, Z[q][0], Z[q][1], n, kk, Sc);
+            h2_scores_step<D, C, NKP, NB, KB0>(L, q, Z[q][0], Z[q][1], n, kk, Sc);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int f = q * NG + g;
@@ -596,6 +619,108 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 #pragma unroll
         for (int r = 0; r < 4; ++r) X[j][r] += alpha * P[j][r];
     return it;
+}
+
+// The mid-chunk state S_m = e^{l_{M-1}} S + sum_{i<M} e^{l_{M-1} - l_i} k_i k_i^T
+// (M = 16 KB0 tokens: the state after the chunk's first M tokens), formed by
+// a wave for its own CG: the hi plane into its operand registers SHr, the lo
+// plane into Slo (laid out as L.S's planes); returns the planes' exponent
+// (they hold S_m 2^E).
+//  - Tile (c, i) of S_m (rows 16c.., columns 16i..) is e^{l_{M-1}} times S's
+//    tile plus the weighted keys' row block c times the keys' row block i,
+//    over the M keys, on fp16 MFMAs: the keys are exact in one fp16 part, the
+//    weighted keys take two (hi, lo).  In the accumulator layout lane (n, kk)
+//    holds rows 16c + 4kk + r of column 16i + n, which by symmetry is row
+//    16i + n at columns 16c + 4kk + r: tiles (2q, i) and (2q + 1, i) together
+//    are the operand piece (q, i) of row block i, and S's part of them is the
+//    piece its planes hold at row 16i + n (added after the MFMAs, which start
+//    from zero: an accumulator input written just before would be rewritten
+//    for the next tile while the MFMA may still read it).
+//  - The accumulators carry 2^EA, EA = min(ES, 2 EK), so S's part stays below
+//    2^15 and the keys' part below 2^35; one exponent for the whole matrix
+//    comes from its largest diagonal entry (a positive semidefinite matrix's
+//    largest magnitude), from the diagonal tiles, formed first.
+// Waves that form the same S_m write the same bits to Slo.
+template <int D, int C, int NKP, int KB0>
+__device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, int EK, int n, int kk, uint32_t* Slo,
+                                           H2Hi<D, NKP>& SHr) {
+    static_assert(NKP == 1 && KB0 == 2 && C >= 16 * KB0, "one key plane, 32 keys before the mid-chunk state");
+    constexpr int NT = D / 16;
+    constexpr int NQ = D / 32;
+    constexpr int SW = H2Lds<D, C, NKP>::SW;
+    constexpr int M = 16 * KB0;
+    const float lm = L.L[M - 1];
+    const int EA = min(ES, 2 * EK);
+    const float fS = __builtin_amdgcn_ldexpf(__expf(lm), EA - ES);
+    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+    // weights of the lane's 8 key slots (32-key step 0: slot e < 4 is key
+    // 4kk + e, slot 4 + e key 16 + 4kk + e), times 2^(EA - 2EK)
+    float wsl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        wsl[e] = __builtin_amdgcn_ldexpf(__expf(lm - L.L[(e < 4 ? 0 : 16) + 4 * kk + (e & 3)]), EA - 2 * EK);
+    // K^T row blocks over the first 32 keys: the B operand of column block i,
+    // and (weighted) the A operand of row block c, of lane (n, kk)
+    f16x8 B[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) B[i] = h2_kt_operand<D, C, NKP>(L, 0, i, 0, n, kk);
+    auto weighted = [&](int c, f16x8& Ah, f16x8& Al) {
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (float)B[c][e] * wsl[e];
+            b[e] = (float)B[c][4 + e] * wsl[4 + e];
+        }
+        h2_split(a, b, 1.0f, Ah, Al);
+    };
+    // a0, a1 plus S's tiles (2q, i) and (2q + 1, i) times e^{l_{M-1}}
+    // 2^(EA - ES), on mixed-precision fmas from the fp16 parts
+    auto add_s = [&](int i, int q, f32x4& a0, f32x4& a1) {
+        const int off = (16 * i + n) * SW + 16 * q + 4 * kk;
+        const f16x8 h = lds_f16x8(&L.S[0][off]), l = lds_f16x8(&L.S[1][off]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            a0[r] = fmaf((float)h[r], fS, fmaf((float)l[r], fS, a0[r]));
+            a1[r] = fmaf((float)h[4 + r], fS, fmaf((float)l[4 + r], fS, a1[r]));
+        }
+    };
+    float dmax = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        f16x8 Ah0, Al0, Ah1, Al1;
+        weighted(2 * q, Ah0, Al0);
+        weighted(2 * q + 1, Ah1, Al1);
+        f32x4 a0 = mfma_f16x32(Al0, B[2 * q], zero);
+        a0 = mfma_f16x32(Ah0, B[2 * q], a0);
+        f32x4 a1 = mfma_f16x32(Al1, B[2 * q + 1], zero);
+        a1 = mfma_f16x32(Ah1, B[2 * q + 1], a1);
+        f32x4 u = zero;
+        add_s(2 * q, q, a0, u);       // tile (2q, 2q): half 0 of row block 2q's piece q
+        add_s(2 * q + 1, q, u, a1);   // tile (2q + 1, 2q + 1): half 1 of row block 2q + 1's
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * kk + r == n) dmax = fmaxf(dmax, fmaxf(fabsf(a0[r]), fabsf(a1[r])));
+    }
+    const int EM = h2_exp(wave_max(dmax));
+    const float sM = pow2(EM);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        f16x8 Ah0, Al0, Ah1, Al1;
+        weighted(2 * q, Ah0, Al0);
+        weighted(2 * q + 1, Ah1, Al1);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            f32x4 a0 = mfma_f16x32(Al0, B[i], zero);
+            a0 = mfma_f16x32(Ah0, B[i], a0);
+            f32x4 a1 = mfma_f16x32(Al1, B[i], zero);
+            a1 = mfma_f16x32(Ah1, B[i], a1);
+            add_s(i, q, a0, a1);   // VALU results: the asm split may take them
+            f16x8 lo;
+            h2_split_mix(a0, a1, sM, SHr[q][i], lo);
+            *reinterpret_cast<uint4*>(&Slo[(16 * i + n) * SW + 16 * q + 4 * kk]) = __builtin_bit_cast(uint4, lo);
+        }
+    }
+    return EA + EM;
 }
 
 // ---- staging ----

@@ -285,16 +285,19 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
 // ---------------------------------------------------------------------------
 // d >= 32: the same persistent chunk loop with every matvec product on fp16
 // MFMAs over two-part splits (cg_h2.h).  The chunk state is held whole (two
-// fp16 planes of the full matrix), so there is no mid-chunk state: every
-// wave's state term starts from S^H_c and its intra-chunk terms run over the
-// causal keys from the chunk start.  Four workgroup barriers per chunk, as in
+// fp16 planes of the full matrix).  Every wave's state term starts from
+// S^H_c and its intra-chunk terms run over the causal keys from the chunk
+// start, except at d = 128 with 64-token chunks and bf16 keys: there waves 2
+// and 3 each form the mid-chunk state (the state after token 31) before
+// their CG and start from it, so that their intra-chunk terms cover two key
+// blocks at most, as wave 1's do.  Four workgroup barriers per chunk, as in
 // cg_wave; the exponents of the next chunk's state and keys come from
 // per-wave maxima gathered before barrier (C), and the values' exponent from
 // maxima gathered before barrier (A).  The output's V^T operands are read
 // transposed from the value rows (staged where the key rows were, after
 // barrier (A)), so the values need no transposed tile.
 template <int D, int C, int W, typename In>
-__device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, int tid, ChunkPos& p, int& ES,
+__device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, uint32_t* Smid, int tid, ChunkPos& p, int& ES,
                                            int& EK, int n_chunks, int H, int T, long total,
                                            int* __restrict__ work_counter, Raw4<In> (&qr)[D / 16],
                                            const In* __restrict__ q, const In* __restrict__ k,
@@ -325,7 +328,17 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
         R[j] = qr[j].get();
         lam[j] = lds4(&L.Lam[16 * j + 4 * kk]);   // held across the CG, off the update's path
     }
-    const int it = h2_cg_solve<D, C, NKP, W>(L, wv, ES, EK, R, X, lam, max_iters, tol);
+    int it;
+    H2Hi<D, NKP> SHr;
+    if constexpr (h2_mid_state<D, C, NKP>() && W >= 2) {
+        // waves 2 and 3: the state term from the mid-chunk state, which each
+        // forms (both write the same lo plane), and keys from block 2 on
+        const H2Wave<D, C, W, 2> wc(L.L, lane);
+        const int EM = h2_form_mid<D, C, NKP, 2>(L, ES, EK, n, kk, Smid, SHr);
+        it = h2_cg_solve<D, C, NKP, W, 2, true>(L, wc, EM, EK, R, X, lam, max_iters, tol, Smid, SHr);
+    } else {
+        it = h2_cg_solve<D, C, NKP, W, 0, false>(L, wv, ES, EK, R, X, lam, max_iters, tol, L.S[1], SHr);
+    }
     asm volatile("" : "+v"(tid));
     if (W == 0 && lane == 0) L.next = ticket;
 
@@ -523,6 +536,10 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_h2_kernel(
     constexpr int NT = D / 16;
     constexpr int NTHR = 64 * NW;
     __shared__ H2Lds<D, C, NKP> L;
+    // the mid-chunk state's lo plane (waves 2 and 3 at d = 128, chunk 64, bf16
+    // keys), on a 256-byte boundary as the chunk state's planes are (at 96
+    // bytes past one, wave 3's iterations took 8% longer)
+    __shared__ alignas(256) uint32_t Smid[h2_mid_state<D, C, NKP>() ? D * H2Lds<D, C, NKP>::SW : 4];
 
     const int tid0 = threadIdx.x;
     const int lane = tid0 & 63;
@@ -539,18 +556,18 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_h2_kernel(
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         if (w == 0) {
-            more = cg_h2_wave<D, C, 0, In>(L, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k, v,
+            more = cg_h2_wave<D, C, 0, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k, v,
                                            gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
         } else if constexpr (NW > 1) {
             if (w == 1) {
-                more = cg_h2_wave<D, C, 1, In>(L, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k,
+                more = cg_h2_wave<D, C, 1, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k,
                                                v, gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
             } else if constexpr (NW > 2) {
                 if (w == 2)
-                    more = cg_h2_wave<D, C, 2, In>(L, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
+                    more = cg_h2_wave<D, C, 2, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
                                                    k, v, gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
                 else
-                    more = cg_h2_wave<D, C, 3, In>(L, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
+                    more = cg_h2_wave<D, C, 3, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
                                                    k, v, gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
             }
         }
