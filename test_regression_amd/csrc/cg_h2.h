@@ -639,7 +639,7 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 //  - The accumulators carry 2^EA, EA = min(ES, 2 EK), so S's part stays below
 //    2^15 and the keys' part below 2^35; one exponent for the whole matrix
 //    comes from its largest diagonal entry (a positive semidefinite matrix's
-//    largest magnitude), from the diagonal tiles, formed first.
+//    largest magnitude), formed first on the VALU.
 // Waves that form the same S_m write the same bits to Slo.
 template <int D, int C, int NKP, int KB0>
 __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, int EK, int n, int kk, uint32_t* Slo,
@@ -664,15 +664,18 @@ __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, in
     f16x8 B[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) B[i] = h2_kt_operand<D, C, NKP>(L, 0, i, 0, n, kk);
-    auto weighted = [&](int c, f16x8& Ah, f16x8& Al) {
+    // the weighted keys' row blocks as A operands, split once
+    f16x8 Ah[NT], Al[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
         f32x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             a[e] = (float)B[c][e] * wsl[e];
             b[e] = (float)B[c][4 + e] * wsl[4 + e];
         }
-        h2_split(a, b, 1.0f, Ah, Al);
-    };
+        h2_split_mix(a, b, 1.0f, Ah[c], Al[c]);
+    }
     // a0, a1 plus S's tiles (2q, i) and (2q + 1, i) times e^{l_{M-1}}
     // 2^(EA - ES), on mixed-precision fmas from the fp16 parts
     auto add_s = [&](int i, int q, f32x4& a0, f32x4& a1) {
@@ -684,36 +687,33 @@ __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, in
             a1[r] = fmaf((float)h[4 + r], fS, fmaf((float)l[4 + r], fS, a1[r]));
         }
     };
+    // the diagonal, entry 16c + n: S's entry times e^{l_{M-1}} 2^(EA - ES)
+    // plus the lane group's weighted squares summed over the four groups (the
+    // tiles' own diagonals may differ from it by rounding: the exponent then
+    // leaves the largest element within an ulp of the range it aims for)
     float dmax = 0.f;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        f16x8 Ah0, Al0, Ah1, Al1;
-        weighted(2 * q, Ah0, Al0);
-        weighted(2 * q + 1, Ah1, Al1);
-        f32x4 a0 = mfma_f16x32(Al0, B[2 * q], zero);
-        a0 = mfma_f16x32(Ah0, B[2 * q], a0);
-        f32x4 a1 = mfma_f16x32(Al1, B[2 * q + 1], zero);
-        a1 = mfma_f16x32(Ah1, B[2 * q + 1], a1);
-        f32x4 u = zero;
-        add_s(2 * q, q, a0, u);       // tile (2q, 2q): half 0 of row block 2q's piece q
-        add_s(2 * q + 1, q, u, a1);   // tile (2q + 1, 2q + 1): half 1 of row block 2q + 1's
+    for (int c = 0; c < NT; ++c) {
+        float sq = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * kk + r == n) dmax = fmaxf(dmax, fmaxf(fabsf(a0[r]), fabsf(a1[r])));
+        for (int e = 0; e < 8; ++e) sq = fmaf((float)B[c][e] * wsl[e], (float)B[c][e], sq);
+        const int a = 16 * c + n;
+        const int pc = perm32(a);
+        const uint32_t wh = L.S[0][a * SW + pc / 2], wl = L.S[1][a * SW + pc / 2];
+        const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(pc & 1 ? wh >> 16 : wh & 0xffff));
+        const _Float16 l = __builtin_bit_cast(_Float16, (uint16_t)(pc & 1 ? wl >> 16 : wl & 0xffff));
+        dmax = fmaxf(dmax, fabsf(fmaf((float)h + (float)l, fS, kslot_sum(sq))));
     }
     const int EM = h2_exp(wave_max(dmax));
     const float sM = pow2(EM);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        f16x8 Ah0, Al0, Ah1, Al1;
-        weighted(2 * q, Ah0, Al0);
-        weighted(2 * q + 1, Ah1, Al1);
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-            f32x4 a0 = mfma_f16x32(Al0, B[i], zero);
-            a0 = mfma_f16x32(Ah0, B[i], a0);
-            f32x4 a1 = mfma_f16x32(Al1, B[i], zero);
-            a1 = mfma_f16x32(Ah1, B[i], a1);
+            f32x4 a0 = mfma_f16x32(Al[2 * q], B[i], zero);
+            a0 = mfma_f16x32(Ah[2 * q], B[i], a0);
+            f32x4 a1 = mfma_f16x32(Al[2 * q + 1], B[i], zero);
+            a1 = mfma_f16x32(Ah[2 * q + 1], B[i], a1);
             add_s(i, q, a0, a1);   // VALU results: the asm split may take them
             f16x8 lo;
             h2_split_mix(a0, a1, sM, SHr[q][i], lo);
