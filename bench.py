@@ -62,22 +62,35 @@ def h2_cg_mfma_flops(d, C, key_planes, wave_iters):
     16-row block for the state term (hi.hi, hi.lo, lo.hi of the two-part
     splits), and (1 + key planes) per causal key block and feature step for
     the scores and per row block and 32-key step for the apply (keys stored
-    as bf16 are one exact fp16 plane, fp32 keys two).  Per chunk the output
-    adds the scores and apply of the solution (fp16) and the G_c term on
-    16x16x4 fp32 MFMAs.  Returns (fp16 flops, fp32 flops)."""
+    as bf16 are one exact fp16 plane, fp32 keys two).  At d = 128, 64-token
+    chunks and bf16 keys, waves 2 and 3 start from the mid-chunk state, so
+    their causal key blocks start at block 2, and each forms that state per
+    chunk (four MFMAs per 32-feature step and row block).  Per chunk the
+    output adds the scores and apply of the solution over the keys from the
+    chunk start, and the G_c term: three fp16 MFMAs per feature step and row
+    block when a wave splits at most two of G_c's row blocks (64-token
+    chunks at d = 128), else 16x16x4 fp32 MFMAs.  Returns (fp16 flops, fp32
+    flops)."""
     import numpy as np
     NT, NQ, NW = d // 16, d // 32, C // 16
     np_ = 1 + key_planes
+    mid = d == 128 and C == 64 and key_planes == 1
+    gl = (NT + NW - 1) // NW <= 2
     per_iter = np.zeros(NW, np.int64)
     out16 = 0
     for w in range(NW):
-        nbo, ns = w + 1, (w + 2) // 2
-        per_iter[w] = 3 * NT * NQ + np_ * NQ * nbo + np_ * NT * ns
-        out16 += np_ * NQ * nbo + np_ * NT * ns
+        kb0 = 2 if mid and w >= 2 else 0
+        nb = w + 1 - kb0
+        per_iter[w] = 3 * NT * NQ + np_ * NQ * nb + np_ * NT * ((nb + 1) // 2)
+        out16 += np_ * NQ * (w + 1) + np_ * NT * ((w + 2) // 2)
+        if kb0:
+            out16 += 4 * NQ * NT
+        if gl:
+            out16 += 3 * NQ * NT
     wave_iters = np.asarray(wave_iters, np.int64)
     n_chunks = wave_iters.shape[0]
     f16 = 2 * 16 * 16 * 32 * (int((wave_iters * per_iter[None, :]).sum()) + n_chunks * out16)
-    fp32 = 2 * 16 * 16 * 4 * (NW * NT * NT * 4) * n_chunks
+    fp32 = 0 if gl else 2 * 16 * 16 * 4 * (NW * NT * NT * 4) * n_chunks
     return f16, fp32
 
 
