@@ -636,8 +636,12 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 //    piece its planes hold at row 16i + n (added after the MFMAs, which start
 //    from zero: an accumulator input written just before would be rewritten
 //    for the next tile while the MFMA may still read it).
-//  - The accumulators carry 2^EA, EA = min(ES, 2 EK), so S's part stays below
-//    2^15 and the keys' part below 2^35; one exponent for the whole matrix
+//  - The accumulators carry 2^EA, EA = 2 EK: the weighted keys then lie in
+//    fp16's normal range as the scores' keys do (a smaller EA, e.g. the zero
+//    state's default exponent, flushed them to zero for keys far below unit
+//    size), and the keys' part stays below 2^35.  EA is capped at ES + 100 so
+//    that S's part stays below 2^115; where the cap binds the keys' part is
+//    far below S's and may underflow.  One exponent for the whole matrix
 //    comes from its largest diagonal entry (a positive semidefinite matrix's
 //    largest magnitude), formed first on the VALU.
 // Waves that form the same S_m write the same bits to Slo.
@@ -650,7 +654,7 @@ __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, in
     constexpr int SW = H2Lds<D, C, NKP>::SW;
     constexpr int M = 16 * KB0;
     const float lm = L.L[M - 1];
-    const int EA = min(ES, 2 * EK);
+    const int EA = min(2 * EK, ES + 100);
     const float fS = __builtin_amdgcn_ldexpf(__expf(lm), EA - ES);
     const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
     // weights of the lane's 8 key slots (32-key step 0: slot e < 4 is key

@@ -385,17 +385,19 @@ def test_one_and_two_iterations(dtype, k):
         assert (g["iters"] == k).all()
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("scale", [(2.0 ** -10, 2.0 ** -20, 2.0 ** 15), (2.0 ** 10, 2.0 ** 8, 2.0 ** -12)])
-def test_inputs_far_from_unit_size(dtype, scale):
+def test_inputs_far_from_unit_size(dtype, scale, d):
     """Keys, queries, values and lambda scaled by powers of two far from 1
     (the fp16 split products rescale every group by its own exponent, so the
     result must keep its accuracy): keys x sk with lambda x sk^2 is the same
     system up to the scale of x, so the outputs are compared with the oracle
-    at the same bar as unit inputs."""
+    at the same bar as unit inputs.  d = 128 with bf16 keys includes the
+    mid-chunk state that the CG kernel forms from the chunk state and keys."""
     sk, sq, sv = scale
-    B, H, T, d = 1, 2, 150, 64
-    say("case scaled inputs", dtype, scale)
+    B, H, T = 1, 2, 150
+    say("case scaled inputs", dtype, scale, d)
     x = small_inputs(61, B, H, T, d, "f32")
     x["k"] = x["k"] * np.float32(sk)
     x["q"] = x["q"] * np.float32(sq)
