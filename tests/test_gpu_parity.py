@@ -414,6 +414,24 @@ def test_inputs_far_from_unit_size(dtype, scale, d):
         compare_counts(g["iters"], r, cap, tol)
 
 
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strong_decay(dtype, d):
+    """gamma ~ U(0.5, 1): within a chunk the decays e^{l_t - l_i} span many
+    orders of magnitude, the chunk states forget most of their history, and
+    (d = 128, bf16) the mid-chunk state's key weights reach far below 1."""
+    B, H, T = 1, 2, 200
+    say("case strong decay", dtype, d)
+    x = small_inputs(67, B, H, T, d, dtype, glo=0.5)
+    for cap, tol in ((2, 0.0), (12, 0.0), (30, 1e-4)):
+        g = gpu_forward(x, dtype, cap, tol, 64)
+        r = oracle_forward(x, dtype, cap, tol)
+        e = rel_l2(g["out"], r["out"])
+        say(f"strong decay {dtype} d {d} cap {cap}: rel_l2={e:.2e}")
+        assert np.isfinite(g["out"]).all() and e <= 1e-5, (cap, tol, e)
+        compare_counts(g["iters"], r, cap, tol)
+
+
 @pytest.mark.parametrize("d", [16, 128])
 def test_iterating_far_past_convergence_stays_finite(d):
     """Lambda = I and a fixed cap far above d: every token's CG converges
