@@ -101,6 +101,31 @@ def test_backward_dims_chunks_dtypes(d, chunk, dtype):
         check(gpu, ref, dtype, max_iters, tol, f"k={max_iters} tol={tol}")
 
 
+@pytest.mark.parametrize("case", ["small_keys", "large_keys", "strong_decay"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_far_from_unit_and_strong_decay(dtype, d, case):
+    """Keys, queries, values and lambda scaled by powers of two far from 1
+    (keys x sk with lambda x sk^2: the fp16 split products and the stored
+    fp16 reverse states rescale each group by its own exponent), and
+    gamma ~ U(0.5, 1), whose decays span many orders of magnitude."""
+    B, H, T = 1, 2, 150
+    say("case backward", case, dtype, d)
+    x = small_inputs(5400 + d, B, H, T, d, "f32", glo=0.5 if case == "strong_decay" else 0.9)
+    if case != "strong_decay":
+        sk, sq, sv = (2.0 ** -10, 2.0 ** -20, 2.0 ** 15) if case == "small_keys" else (2.0 ** 10, 2.0 ** 8, 2.0 ** -12)
+        x["k"] = x["k"] * np.float32(sk)
+        x["q"] = x["q"] * np.float32(sq)
+        x["v"] = x["v"] * np.float32(sv)
+        x["lam"] = (x["lam"] * np.float32(sk * sk)).astype(np.float32)
+    if dtype == "bf16":
+        x = {n: (inputs.bf16_bits(x[n]) if n in ("q", "k", "v") else x[n]) for n in x}
+    for max_iters, tol in ((8, 0.0), (30, 1e-4)):
+        gpu = gpu_backward(x, dtype, max_iters, tol, 64)
+        ref = oracle_backward(x, dtype, max_iters, tol)
+        check(gpu, ref, dtype, max_iters, tol, f"{case} k={max_iters} tol={tol}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_backward_edge_cases(dtype):
     """bf16 runs the split-product adjoint kernel, chunk 16 its masked second
