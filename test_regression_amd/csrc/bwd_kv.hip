@@ -52,7 +52,17 @@ struct alignas(16) KvLds {
     float R[3 * C * PD];   // x, z, g rows of the chunk
     float L[C];
     float Tr[C / 16][TRW];   // per-wave transpose scratch
+    // with four waves: the within-chunk sums of key block 0 over token block
+    // 3, which wave 3 takes from wave 0: the D / 16 16-byte pieces of dk, then
+    // of dv, each piece stored for the 64 lanes in turn (32 D floats)
+    float Pk0[C == 64 ? 32 * D : 4];
 };
+
+// Whether wave 3 takes key block 0's sums over token block 3 from wave 0
+// (four waves: their within-chunk pairs of key and token blocks, 4, 3, 2, 1,
+// become 3, 3, 2, 2).
+template <int C>
+__host__ __device__ constexpr bool kv_rebalance() { return C == 64; }
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
@@ -295,6 +305,41 @@ __device__ __forceinline__ void state_terms_h2(const float* __restrict__ Pg, con
     }
 }
 
+// The within-chunk sums of keys i (lane (n, kk): key il, log decay li, its
+// k and v in Kb, Vb) over token block tb (tokens t >= i): BK, BV as fresh MFMA
+// chains; the value gradient's weights are the negated x_t . k_i weights of
+// the key gradient's.
+template <int D>
+__device__ __forceinline__ void kv_pair(const float* X, const float* Zt, const float* Gt, const float* Lv, int tb,
+                                        const f32x4 (&Kb)[D / 16], const f32x4 (&Vb)[D / 16], int il, float li,
+                                        int n, int kk, f32x4 (&BK)[D / 16], f32x4 (&BV)[D / 16]) {
+    constexpr int NT = D / 16;
+    constexpr int PD = lds_pitch(D);
+    const f32x4 s1 = token_scores<D>(X + 16 * tb * PD, Kb, n, kk);    // x_t . k_i
+    const f32x4 s2 = token_scores<D>(Gt + 16 * tb * PD, Vb, n, kk);   // g_t . v_i
+    const f32x4 s3 = token_scores<D>(Zt + 16 * tb * PD, Kb, n, kk);   // z_t . k_i
+    f32x4 w23, wn1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * kk + r;
+        const float zeta = (t >= il) ? __expf(Lv[t] - li) : 0.f;
+        w23[r] = zeta * (s2[r] - s3[r]);
+        wn1[r] = -zeta * s1[r];
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) BK[j] = BV[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int t = 16 * tb + 4 * kk + s;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            BK[j] = mfma4(X[t * PD + 16 * j + n], w23[s], BK[j]);
+            BK[j] = mfma4(Zt[t * PD + 16 * j + n], wn1[s], BK[j]);
+            BV[j] = mfma4(Gt[t * PD + 16 * j + n], -wn1[s], BV[j]);
+        }
+    }
+}
+
 template <int D, int C, int W, typename In>
 __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __restrict__ k,
                                         const In* __restrict__ v, size_t tok0, int valid,
@@ -336,34 +381,14 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
         }
 
     // ---- within the chunk: tokens t >= i, one 16-token block at a time ----
-    // Each block's sums are fresh MFMA chains, added into DK, DV on the VALU;
-    // the value gradient's weights are the negated x_t . k_i weights of dk's.
+    // Each block's sums are fresh MFMA chains, added into DK, DV on the VALU.
+    // With four waves, wave 0 leaves its last block (token block 3) to wave 3.
+    constexpr bool RB = kv_rebalance<C>();
+    constexpr int TB_END = RB && W == 0 ? NW - 1 : NW;
 #pragma unroll 1
-    for (int tb = W; tb < NW; ++tb) {
-        const f32x4 s1 = token_scores<D>(X + 16 * tb * PD, Kb, n, kk);    // x_t . k_i
-        const f32x4 s2 = token_scores<D>(Gt + 16 * tb * PD, Vb, n, kk);   // g_t . v_i
-        const f32x4 s3 = token_scores<D>(Zt + 16 * tb * PD, Kb, n, kk);   // z_t . k_i
-        f32x4 w23, wn1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tb + 4 * kk + r;
-            const float zeta = (t >= il) ? __expf(L.L[t] - li) : 0.f;
-            w23[r] = zeta * (s2[r] - s3[r]);
-            wn1[r] = -zeta * s1[r];
-        }
+    for (int tb = W; tb < TB_END; ++tb) {
         f32x4 BK[NT], BV[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) BK[j] = BV[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int t = 16 * tb + 4 * kk + s;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                BK[j] = mfma4(X[t * PD + 16 * j + n], w23[s], BK[j]);
-                BK[j] = mfma4(Zt[t * PD + 16 * j + n], wn1[s], BK[j]);
-                BV[j] = mfma4(Gt[t * PD + 16 * j + n], -wn1[s], BV[j]);
-            }
-        }
+        kv_pair<D>(X, Zt, Gt, L.L, tb, Kb, Vb, il, li, n, kk, BK, BV);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             DK[j] += BK[j];
@@ -372,21 +397,59 @@ __device__ __forceinline__ void kv_wave(KvLds<D, C>& L, int lane, const In* __re
     }
 
     // ---- outputs ----
-    float vd = 0.f, kd = 0.f;
+    auto outputs = [&]() {
+        float vd = 0.f, kd = 0.f;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+        for (int j = 0; j < NT; ++j) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            vd += Vb[j][r] * DV[j][r];
-            kd += Kb[j][r] * DK[j][r];
+            for (int r = 0; r < 4; ++r) {
+                vd += Vb[j][r] * DV[j][r];
+                kd += Kb[j][r] * DK[j][r];
+            }
+            if (key_ok) {
+                store_row(dv + (tok0 + il) * D + 16 * j + 4 * kk, DV[j]);
+                store_row(dk + (tok0 + il) * D + 16 * j + 4 * kk, DK[j]);
+            }
         }
-        if (key_ok) {
-            store_row(dv + (tok0 + il) * D + 16 * j + 4 * kk, DV[j]);
-            store_row(dk + (tok0 + il) * D + 16 * j + 4 * kk, DK[j]);
+        const float a = 0.5f * (kslot_sum(vd) + kslot_sum(kd));
+        if (key_ok && kk == 0) akey[tok0 + il] = a;
+    };
+    if constexpr (!RB) {
+        outputs();
+    } else if constexpr (W == 0) {
+        // key block 0's sums over token block 3, from wave 3
+        __syncthreads();
+        const float* pk = L.Pk0 + lane * 4;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            DK[j] += ld4(pk + 64 * 4 * j);
+            DV[j] += ld4(pk + 64 * 4 * (NT + j));
         }
+        outputs();
+    } else if constexpr (W == NW - 1) {
+        outputs();
+        // key block 0 (keys 0..15) over token block 3, for wave 0
+        f32x4 K0[NT], V0[NT];
+        const bool ok0 = n < valid;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const size_t off = (tok0 + n) * D + 16 * j + 4 * kk;
+            K0[j] = ok0 ? load4(k + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            V0[j] = ok0 ? load4(v + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        f32x4 BK[NT], BV[NT];
+        kv_pair<D>(X, Zt, Gt, L.L, NW - 1, K0, V0, n, L.L[n], n, kk, BK, BV);
+        float* pk = L.Pk0 + lane * 4;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            *reinterpret_cast<f32x4*>(pk + 64 * 4 * j) = BK[j];
+            *reinterpret_cast<f32x4*>(pk + 64 * 4 * (NT + j)) = BV[j];
+        }
+        __syncthreads();
+    } else {
+        outputs();
+        __syncthreads();
     }
-    const float a = 0.5f * (kslot_sum(vd) + kslot_sum(kd));
-    if (key_ok && kk == 0) akey[tok0 + il] = a;
 }
 
 template <int D, int C, typename In>
