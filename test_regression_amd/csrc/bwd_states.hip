@@ -16,8 +16,12 @@
 // after the last chunk); M obeys the same recurrence with the rank-2C update
 // sum_t e^{l_t} (z_t x_t^T + x_t z_t^T).  Work split as the forward's
 // chunk-state kernel: one workgroup per (head, {gx, zx}, row block), each wave
-// a 16 x D slab of the running state in MFMA accumulators, the update a fresh
-// v_mfma_f32_16x16x4_f32 chain (two products per tile for M).
+// a 16 x D slab of the running state in MFMA accumulators, the update summed
+// apart from it on MFMAs (two products per tile for M).  For d >= 32 the
+// update runs on v_mfma_f32_16x16x32_f16 over two-part fp16 splits (cg_h2.h)
+// of the chunk's token rows, a e^{l_t} and x each scaled by one power of two
+// per chunk: three products per operand pair, so each product term carries
+// about 22 significant bits; for d = 16 on v_mfma_f32_16x16x4_f32.
 //
 // States are stored as 16 x 16 blocks of 16 bytes per lane, each once per
 // chunk in MFMA accumulator order (lane 16q + m holds rows 4q..4q+3 of
@@ -36,6 +40,21 @@
 
 namespace mesa {
 
+// The 16x16x32 fp16 MFMA operand of features c0 .. c0 + 15 (lane (m, kk):
+// feature c0 + m) over tokens 32 s + 8 kk .. + 7, from an fp16 plane of token
+// rows (pitch PW words), through two transposed 8-byte LDS reads (gfx950's
+// ds_read_b64_tr_b16; lds_tr_f16x4 in cg_h2.h): lane m addresses token row
+// r0 + m / 4 at the 4-feature piece c0 + 4 (m % 4) and receives feature
+// c0 + m of rows r0 .. r0 + 3.  The A and B operands of an update read the
+// same token order, so each k-slot is one token.
+template <int PW>
+__device__ __forceinline__ f16x8 token_plane_operand(const uint32_t* P, int c0, int s, int m, int kk) {
+    const uint32_t* R = P + (c0 + 4 * (m & 3)) / 2;
+    const f16x4 a = lds_tr_f16x4(R + (32 * s + 8 * kk + (m >> 2)) * PW);
+    const f16x4 b = lds_tr_f16x4(R + (32 * s + 8 * kk + 4 + (m >> 2)) * PW);
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 template <int D, int C, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     const float* __restrict__ g, const float* __restrict__ z, const float* __restrict__ x,
@@ -45,8 +64,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
     constexpr int NT = D / 16;
     constexpr int PD = lds_pitch(D);
     constexpr int NTHR = 64 * NW;
-    __shared__ float sA[C * PD];   // g or z rows of the chunk (the state's rows)
-    __shared__ float sX[C * PD];   // x rows of the chunk (the state's columns)
+    // d >= 32: the update on fp16 MFMAs over two-part splits, from token-row
+    // planes of a_t e^{l_t} 2^Ea and x_t 2^Ex (one exponent per chunk and
+    // tensor), padded to a whole 32-token step; d = 16: fp32 MFMAs from fp32
+    // token rows
+    constexpr bool H2 = D >= 32;
+    constexpr int TR = C >= 32 ? C : 32;   // token rows of an fp16 plane
+    constexpr int PW = D / 2 + 8;          // words per fp16 token row
+    __shared__ float sA[H2 ? 4 : C * PD];   // g or z rows of the chunk (the state's rows)
+    __shared__ float sX[H2 ? 4 : C * PD];   // x rows of the chunk (the state's columns)
+    __shared__ alignas(16) uint32_t pA[2][H2 ? TR * PW : 4];   // (g or z) e^{l_t} 2^Ea: hi, lo
+    __shared__ alignas(16) uint32_t pX[2][H2 ? TR * PW : 4];   // x 2^Ex: hi, lo
+    __shared__ float sMax[2][NW];   // per-wave maxima of |a|, |x|
     __shared__ float sW[C];        // e^{l_t}
     __shared__ float sGam;         // e^{l_end}
 
@@ -110,52 +139,152 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
         if (w == 0) greg = lane < valid ? gh[t0 + lane] : 1.0f;
     };
 
+    if constexpr (H2 && TR > C) {
+        // the token rows past a 16-token chunk stay zero (covered by the
+        // first chunk's barriers)
+        for (int e = tid0; e < (TR - C) * PW; e += NTHR) {
+            pA[0][C * PW + e] = pA[1][C * PW + e] = 0u;
+            pX[0][C * PW + e] = pX[1][C * PW + e] = 0u;
+        }
+    }
     if (n_chunks > 0) prefetch(n_chunks - 1);
     for (int c = n_chunks - 1; c >= 0; --c) {
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, n = lane & 15, kk = lane >> 4;
         const int valid = min(C, T - c * C);
-#pragma unroll
-        for (int u = 0; u < EL4; ++u) {
-            const int e = (tid + u * NTHR) * 4;
-            const int i = e / D, f = e % D;
-            *reinterpret_cast<f32x4*>(&sA[i * PD + f]) = areg[u];
-            *reinterpret_cast<f32x4*>(&sX[i * PD + f]) = xreg[u];
-        }
-        if (w == 0) {
-            const float l = chunk_log_decay_of(greg, valid, lane);
-            const float lend = __shfl(l, C - 1, 64);
-            if (lane < C) sW[lane] = __expf(l);
-            if (lane == 0) sGam = __expf(lend);
-        }
-        __syncthreads();
-        if (c > 0) prefetch(c - 1);
-
-        // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain);
-        //      M also gains sum_t e^{l_t} x_t z_t^T ----
         f32x4 U[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float su = 1.0f;   // undoes the planes' exponents
+        if constexpr (H2) {
+            // ---- (1) the chunk's maxima and log decays ----
+            float am = 0.f, xm = 0.f;
 #pragma unroll
-        for (int gg = 0; gg < C / 16; ++gg) {
+            for (int u = 0; u < EL4; ++u)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int i = 16 * gg + 4 * kk + s;
-                const float a = sA[i * PD + m0 + n] * sW[i];
-#pragma unroll
-                for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sX[i * PD + 16 * j + n], U[j]);
+                for (int r = 0; r < 4; ++r) {
+                    am = fmaxf(am, fabsf(areg[u][r]));
+                    xm = fmaxf(xm, fabsf(xreg[u][r]));
+                }
+            am = wave_max(am);
+            xm = wave_max(xm);
+            if (lane == 0) {
+                sMax[0][w] = am;
+                sMax[1][w] = xm;
             }
-        }
-        if (sym) {
+            if (w == 0) {
+                const float l = chunk_log_decay_of(greg, valid, lane);
+                const float lend = __shfl(l, C - 1, 64);
+                if (lane < C) sW[lane] = __expf(l);
+                if (lane == 0) sGam = __expf(lend);
+            }
+            __syncthreads();
+            float amax = 0.f, xmax = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+                amax = fmaxf(amax, sMax[0][w2]);
+                xmax = fmaxf(xmax, sMax[1][w2]);
+            }
+            const int Ea = h2_exp(amax), Ex = h2_exp(xmax);   // e^{l_t} <= 1 keeps |a e^{l_t}| <= max |a|
+            const float sa = pow2(Ea), sx = pow2(Ex);
+            su = pow2(-(Ea + Ex));
+            // ---- (2) the planes: a thread's 4 features of token i, 8 bytes per plane ----
+#pragma unroll
+            for (int u = 0; u < EL4; ++u) {
+                const int e = (tid + u * NTHR) * 4;
+                const int i = e / D, f = e % D;
+                const float wa = sW[i] * sa;
+                f16x4 ah, al, xh, xl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ya = areg[u][r] * wa, yx = xreg[u][r] * sx;
+                    ah[r] = (_Float16)ya;
+                    al[r] = (_Float16)(ya - (float)ah[r]);
+                    xh[r] = (_Float16)yx;
+                    xl[r] = (_Float16)(yx - (float)xh[r]);
+                }
+                *reinterpret_cast<f16x4*>(&pA[0][i * PW + f / 2]) = ah;
+                *reinterpret_cast<f16x4*>(&pA[1][i * PW + f / 2]) = al;
+                *reinterpret_cast<f16x4*>(&pX[0][i * PW + f / 2]) = xh;
+                *reinterpret_cast<f16x4*>(&pX[1][i * PW + f / 2]) = xl;
+            }
+            __syncthreads();
+            if (c > 0) prefetch(c - 1);
+
+            // ---- (3) U = sum_t (a_t e^{l_t}) x_t^T over the wave's 16 rows; M also
+            //      gains sum_t x_t (a_t e^{l_t})^T: three fp16 products per operand pair ----
+            // each 32-token step and column block a fresh three-product chain
+            // (from zero, read only after it), added into U on the VALU: longer
+            // chains got accumulator inputs rewritten a few wait states after issue
+            const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < TR / 32; ++st) {
+                const f16x8 Ah = token_plane_operand<PW>(pA[0], m0, st, n, kk);
+                const f16x8 Al = token_plane_operand<PW>(pA[1], m0, st, n, kk);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const f16x8 Bh = token_plane_operand<PW>(pX[0], 16 * j, st, n, kk);
+                    const f16x8 Bl = token_plane_operand<PW>(pX[1], 16 * j, st, n, kk);
+                    f32x4 t = mfma_f16x32(Al, Bh, zero);
+                    t = mfma_f16x32(Ah, Bl, t);
+                    t = mfma_f16x32(Ah, Bh, t);
+                    U[j] += t;
+                }
+                if (sym) {
+                    // M's transposed products
+                    const f16x8 Xh = token_plane_operand<PW>(pX[0], m0, st, n, kk);
+                    const f16x8 Xl = token_plane_operand<PW>(pX[1], m0, st, n, kk);
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        const f16x8 Ch = token_plane_operand<PW>(pA[0], 16 * j, st, n, kk);
+                        const f16x8 Cl = token_plane_operand<PW>(pA[1], 16 * j, st, n, kk);
+                        f32x4 t = mfma_f16x32(Xl, Ch, zero);
+                        t = mfma_f16x32(Xh, Cl, t);
+                        t = mfma_f16x32(Xh, Ch, t);
+                        U[j] += t;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < EL4; ++u) {
+                const int e = (tid + u * NTHR) * 4;
+                const int i = e / D, f = e % D;
+                *reinterpret_cast<f32x4*>(&sA[i * PD + f]) = areg[u];
+                *reinterpret_cast<f32x4*>(&sX[i * PD + f]) = xreg[u];
+            }
+            if (w == 0) {
+                const float l = chunk_log_decay_of(greg, valid, lane);
+                const float lend = __shfl(l, C - 1, 64);
+                if (lane < C) sW[lane] = __expf(l);
+                if (lane == 0) sGam = __expf(lend);
+            }
+            __syncthreads();
+            if (c > 0) prefetch(c - 1);
+
+            // ---- P <- e^{l_end} P + sum_t e^{l_t} a_t x_t^T  (U a fresh MFMA chain);
+            //      M also gains sum_t e^{l_t} x_t z_t^T ----
 #pragma unroll
             for (int gg = 0; gg < C / 16; ++gg) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int i = 16 * gg + 4 * kk + s;
-                    const float a = sX[i * PD + m0 + n] * sW[i];
+                    const float a = sA[i * PD + m0 + n] * sW[i];
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sA[i * PD + 16 * j + n], U[j]);
+                    for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sX[i * PD + 16 * j + n], U[j]);
+                }
+            }
+            if (sym) {
+#pragma unroll
+                for (int gg = 0; gg < C / 16; ++gg) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int i = 16 * gg + 4 * kk + s;
+                        const float a = sX[i * PD + m0 + n] * sW[i];
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) U[j] = mfma4(a, sA[i * PD + 16 * j + n], U[j]);
+                    }
                 }
             }
         }
@@ -190,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_states_kernel(
 
         const float G = sGam;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j] = G * acc[j] + U[j];
+        for (int j = 0; j < NT; ++j) acc[j] = G * acc[j] + su * U[j];
         __syncthreads();
     }
 }
