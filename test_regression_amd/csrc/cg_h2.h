@@ -162,6 +162,13 @@ __device__ __forceinline__ f16x8 lds_f16x8(const uint32_t* p) {
 template <typename In>
 __host__ __device__ constexpr int h2_key_planes() { return sizeof(In) == 2 ? 1 : 2; }
 
+// Whether the CG kernel's waves 2 and 3 start their state term from the
+// mid-chunk state (d = 128, 64-token chunks, one key plane: the LDS has room
+// for its lo plane beside the chunk state's two).  Their intra-chunk terms
+// then cover two key blocks at most, as wave 1's, instead of four.
+template <int D, int C, int NKP>
+__host__ __device__ constexpr bool h2_mid_state() { return D == 128 && C == 64 && NKP == 1; }
+
 template <int D, int C, int NKP>
 struct alignas(16) H2Lds {
     static constexpr int SW = D / 2 + 8;                    // words per state / key row
@@ -174,14 +181,10 @@ struct alignas(16) H2Lds {
     float red[3][4];           // per-wave maxima: chunk state, keys, values
     int gexp[D / 16];          // exponents of G_c's row blocks while its planes take the state's place
     int next;                  // the claimed next chunk
+    // the counters of the mid-chunk state's hand-off between the waves (in
+    // what would be the struct's tail padding: the layout stays as without)
+    uint32_t hand[h2_mid_state<D, C, NKP>() ? 2 : 1];
 };
-
-// Whether the CG kernel's waves 2 and 3 start their state term from the
-// mid-chunk state (d = 128, 64-token chunks, one key plane: the LDS has room
-// for its lo plane beside the chunk state's two).  Their intra-chunk terms
-// then cover two key blocks at most, as wave 1's, instead of four.
-template <int D, int C, int NKP>
-__host__ __device__ constexpr bool h2_mid_state() { return D == 128 && C == 64 && NKP == 1; }
 
 // Per-wave constants of wave W, for intra-chunk terms over the keys from
 // key block KB0 on (an even block: 0, or 2 when the wave's state term starts
@@ -419,6 +422,23 @@ __device__ __forceinline__ void h2_matvec(const H2Lds<D, C, NKP>& L, const H2Wav
 template <int D, int NKP>
 using H2Hi = f16x8[NKP == 1 ? D / 32 : 1][NKP == 1 ? D / 16 : 1];
 
+// Hand-off between the waves of one workgroup through a counter in LDS,
+// without a workgroup barrier: a wave adds one once its earlier LDS reads
+// have returned and its LDS writes are done (release), and a wave waits until
+// the counter reaches a target (acquire).  The wait gives up after 2^20 polls
+// (tens of milliseconds), so that every wave exits even if a count went
+// missing.
+__device__ __forceinline__ void lds_signal(uint32_t* c, bool leader) {
+    if (leader) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_wait_count(uint32_t* c, uint32_t target) {
+    for (int i = 0; i < (1 << 20); ++i) {
+        const uint32_t v = __hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 template <int D, int C, int NKP, int W, int KB0, bool HI_GIVEN>
 __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wave<D, C, W, KB0>& wv, int ES, int EK,
                                            f32x4 (&R)[D / 16], f32x4 (&X)[D / 16], const f32x4 (&lam)[D / 16],
@@ -623,9 +643,10 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 
 // The mid-chunk state S_m = e^{l_{M-1}} S + sum_{i<M} e^{l_{M-1} - l_i} k_i k_i^T
 // (M = 16 KB0 tokens: the state after the chunk's first M tokens), formed by
-// a wave for its own CG: the hi plane into its operand registers SHr, the lo
-// plane into Slo (laid out as L.S's planes); returns the planes' exponent
-// (they hold S_m 2^E).
+// a wave for its own CG: the operand pieces q in [QB, QE) of every row block,
+// their hi parts into the wave's registers SHr[q][.], their lo parts into Slo
+// (laid out as L.S's planes); returns the planes' exponent (they hold S_m 2^E),
+// which every wave that forms a share of S_m computes alike.
 //  - Tile (c, i) of S_m (rows 16c.., columns 16i..) is e^{l_{M-1}} times S's
 //    tile plus the weighted keys' row block c times the keys' row block i,
 //    over the M keys, on fp16 MFMAs: the keys are exact in one fp16 part, the
@@ -644,13 +665,12 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 //    far below S's and may underflow.  One exponent for the whole matrix
 //    comes from its largest diagonal entry (a positive semidefinite matrix's
 //    largest magnitude), formed first on the VALU.
-// Waves that form the same S_m write the same bits to Slo.
-template <int D, int C, int NKP, int KB0>
+template <int D, int C, int NKP, int KB0, int QB, int QE>
 __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, int EK, int n, int kk, uint32_t* Slo,
                                            H2Hi<D, NKP>& SHr) {
     static_assert(NKP == 1 && KB0 == 2 && C >= 16 * KB0, "one key plane, 32 keys before the mid-chunk state");
+    static_assert(0 <= QB && QB < QE && QE <= D / 32, "operand pieces formed");
     constexpr int NT = D / 16;
-    constexpr int NQ = D / 32;
     constexpr int SW = H2Lds<D, C, NKP>::SW;
     constexpr int M = 16 * KB0;
     const float lm = L.L[M - 1];
@@ -668,10 +688,11 @@ __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, in
     f16x8 B[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) B[i] = h2_kt_operand<D, C, NKP>(L, 0, i, 0, n, kk);
-    // the weighted keys' row blocks as A operands, split once
+    // the weighted keys' row blocks as A operands (those of the pieces
+    // formed), split once
     f16x8 Ah[NT], Al[NT];
 #pragma unroll
-    for (int c = 0; c < NT; ++c) {
+    for (int c = 2 * QB; c < 2 * QE; ++c) {
         f32x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -711,7 +732,7 @@ __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, in
     const int EM = h2_exp(wave_max(dmax));
     const float sM = pow2(EM);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int q = QB; q < QE; ++q) {
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
             f32x4 a0 = mfma_f16x32(Al[2 * q], B[i], zero);

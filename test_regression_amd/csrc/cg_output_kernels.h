@@ -297,7 +297,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
 // transposed from the value rows (staged where the key rows were, after
 // barrier (A)), so the values need no transposed tile.
 template <int D, int C, int W, typename In>
-__device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, uint32_t* Smid, int tid, ChunkPos& p, int& ES,
+__device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, uint32_t* Smid, uint32_t mc, int tid,
+                                           ChunkPos& p, int& ES,
                                            int& EK, int n_chunks, int H, int T, long total,
                                            int* __restrict__ work_counter, Raw4<In> (&qr)[D / 16],
                                            const In* __restrict__ q, const In* __restrict__ k,
@@ -331,11 +332,43 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
     int it;
     H2Hi<D, NKP> SHr;
     if constexpr (h2_mid_state<D, C, NKP>() && W >= 2) {
-        // waves 2 and 3: the state term from the mid-chunk state, which each
-        // forms (both write the same lo plane), and keys from block 2 on
+        // waves 2 and 3: the state term from the mid-chunk state and keys from
+        // block 2 on.  Each forms half of the state's operand pieces (wave 2
+        // q = 0, 1; wave 3 q = 2, 3): the lo parts into Smid, the hi parts,
+        // once all four waves are done with the chunk state's hi plane (count
+        // L.hand[0]), over that plane in L.S[0]; then (count L.hand[1]) both
+        // read the whole hi plane from there.
+        constexpr int SW = H2Lds<D, C, NKP>::SW;
+        constexpr int QB = W == 2 ? 0 : NQ / 2, QE = W == 2 ? NQ / 2 : NQ;
+        uint32_t* sync = L.hand;
         const H2Wave<D, C, W, 2> wc(L.L, lane);
-        const int EM = h2_form_mid<D, C, NKP, 2>(L, ES, EK, n, kk, Smid, SHr);
-        it = h2_cg_solve<D, C, NKP, W, 2, true>(L, wc, EM, EK, R, X, lam, max_iters, tol, Smid, SHr);
+        const int EM = h2_form_mid<D, C, NKP, 2, QB, QE>(L, ES, EK, n, kk, Smid, SHr);
+        lds_signal(&sync[0], lane == 0);
+        lds_wait_count(&sync[0], 4 * (mc + 1));
+#pragma unroll
+        for (int q = QB; q < QE; ++q)
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+                *reinterpret_cast<f16x8*>(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]) = SHr[q][i];
+        lds_signal(&sync[1], lane == 0);
+        lds_wait_count(&sync[1], 2 * (mc + 1));
+        it = h2_cg_solve<D, C, NKP, W, 2, false>(L, wc, EM, EK, R, X, lam, max_iters, tol, Smid, SHr);
+    } else if constexpr (h2_mid_state<D, C, NKP>()) {
+        // waves 0 and 1: the chunk state's hi plane into registers, then
+        // counted done with L.S[0] in L.hand[0]
+        constexpr int SW = H2Lds<D, C, NKP>::SW;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) SHr[q][i] = lds_f16x8(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]);
+        lds_signal(&L.hand[0], lane == 0);
+        // the lo plane addressed through a register: with its constant address
+        // the compiler waited on each of the loop's LDS reads right after
+        // issuing it (wave 1: 28 full waits per iteration, against 6 so, and
+        // 171k against 154k cycles per chunk for the CG)
+        int o0 = 0;
+        asm volatile("" : "+v"(o0));
+        it = h2_cg_solve<D, C, NKP, W, 0, true>(L, wv, ES, EK, R, X, lam, max_iters, tol, L.S[1] + o0, SHr);
     } else {
         it = h2_cg_solve<D, C, NKP, W, 0, false>(L, wv, ES, EK, R, X, lam, max_iters, tol, L.S[1], SHr);
     }
@@ -548,26 +581,31 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_h2_kernel(
     int ES, EK;
 
     // ---- the first chunk ----
+    if constexpr (h2_mid_state<D, C, NKP>()) {
+        // the hand-off counters, zeroed before the staging's barriers
+        if (tid0 < 2) L.hand[tid0] = 0u;
+    }
     h2_stage_first<D, C, NTHR, NKP, In>(L, p, SH, k, gamma, lambda, tid0, ES, EK);
     Raw4<In> qr[NT];
     load_queries<D, In>(qr, q, p.tok0, p.valid, 16 * w + (lane & 15), lane >> 4);
 
-    for (bool more = true; more;) {
+    uint32_t mc = 0;   // chunks this workgroup has taken before the current one
+    for (bool more = true; more; ++mc) {
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         if (w == 0) {
-            more = cg_h2_wave<D, C, 0, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k, v,
+            more = cg_h2_wave<D, C, 0, In>(L, Smid, mc, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k, v,
                                            gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
         } else if constexpr (NW > 1) {
             if (w == 1) {
-                more = cg_h2_wave<D, C, 1, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k,
+                more = cg_h2_wave<D, C, 1, In>(L, Smid, mc, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q, k,
                                                v, gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
             } else if constexpr (NW > 2) {
                 if (w == 2)
-                    more = cg_h2_wave<D, C, 2, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
+                    more = cg_h2_wave<D, C, 2, In>(L, Smid, mc, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
                                                    k, v, gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
                 else
-                    more = cg_h2_wave<D, C, 3, In>(L, Smid, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
+                    more = cg_h2_wave<D, C, 3, In>(L, Smid, mc, tid, p, ES, EK, n_chunks, H, T, total, work_counter, qr, q,
                                                    k, v, gamma, lambda, SH, SG, max_iters, tol, out, iters, x_out);
             }
         }
