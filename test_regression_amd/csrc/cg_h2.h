@@ -643,10 +643,11 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 
 // The mid-chunk state S_m = e^{l_{M-1}} S + sum_{i<M} e^{l_{M-1} - l_i} k_i k_i^T
 // (M = 16 KB0 tokens: the state after the chunk's first M tokens), formed by
-// a wave for its own CG: the operand pieces q in [QB, QE) of every row block,
-// their hi parts into the wave's registers SHr[q][.], their lo parts into Slo
-// (laid out as L.S's planes); returns the planes' exponent (they hold S_m 2^E),
-// which every wave that forms a share of S_m computes alike.
+// a share of the waves: the operand pieces (q, i) (32-feature step q, row
+// block i) numbered q D/16 + i in [PB, PE), their hi parts into the wave's
+// registers SHr[q][i], their lo parts into Slo (laid out as L.S's planes);
+// returns the planes' exponent (they hold S_m 2^E), which every wave that
+// forms a share computes alike.
 //  - Tile (c, i) of S_m (rows 16c.., columns 16i..) is e^{l_{M-1}} times S's
 //    tile plus the weighted keys' row block c times the keys' row block i,
 //    over the M keys, on fp16 MFMAs: the keys are exact in one fp16 part, the
@@ -665,12 +666,13 @@ __device__ __forceinline__ int h2_cg_solve(const H2Lds<D, C, NKP>& L, const H2Wa
 //    far below S's and may underflow.  One exponent for the whole matrix
 //    comes from its largest diagonal entry (a positive semidefinite matrix's
 //    largest magnitude), formed first on the VALU.
-template <int D, int C, int NKP, int KB0, int QB, int QE>
+template <int D, int C, int NKP, int KB0, int PB, int PE>
 __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, int EK, int n, int kk, uint32_t* Slo,
                                            H2Hi<D, NKP>& SHr) {
     static_assert(NKP == 1 && KB0 == 2 && C >= 16 * KB0, "one key plane, 32 keys before the mid-chunk state");
-    static_assert(0 <= QB && QB < QE && QE <= D / 32, "operand pieces formed");
     constexpr int NT = D / 16;
+    static_assert(0 <= PB && PB < PE && PE <= NT * D / 32, "operand pieces formed");
+    constexpr int QB = PB / NT, QE = (PE - 1) / NT + 1;   // their 32-feature steps
     constexpr int SW = H2Lds<D, C, NKP>::SW;
     constexpr int M = 16 * KB0;
     const float lm = L.L[M - 1];
@@ -734,7 +736,7 @@ __device__ __forceinline__ int h2_form_mid(const H2Lds<D, C, NKP>& L, int ES, in
 #pragma unroll
     for (int q = QB; q < QE; ++q) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
+        for (int i = (q * NT < PB ? PB - q * NT : 0); i < (PE - q * NT < NT ? PE - q * NT : NT); ++i) {
             f32x4 a0 = mfma_f16x32(Al[2 * q], B[i], zero);
             a0 = mfma_f16x32(Ah[2 * q], B[i], a0);
             f32x4 a1 = mfma_f16x32(Al[2 * q + 1], B[i], zero);

@@ -331,44 +331,59 @@ __device__ __forceinline__ bool cg_h2_wave(H2Lds<D, C, h2_key_planes<In>()>& L, 
     }
     int it;
     H2Hi<D, NKP> SHr;
-    if constexpr (h2_mid_state<D, C, NKP>() && W >= 2) {
-        // waves 2 and 3: the state term from the mid-chunk state and keys from
-        // block 2 on.  Each forms half of the state's operand pieces (wave 2
-        // q = 0, 1; wave 3 q = 2, 3): the lo parts into Smid, the hi parts,
-        // once all four waves are done with the chunk state's hi plane (count
-        // L.hand[0]), over that plane in L.S[0]; then (count L.hand[1]) both
-        // read the whole hi plane from there.
+    if constexpr (h2_mid_state<D, C, NKP>()) {
+        // The mid-chunk state for waves 2 and 3, formed by waves 0, 2 and 3
+        // (wave 1, with two key blocks from the chunk state, has no time to
+        // spare), each a third of its 32 operand pieces: the lo parts into
+        // Smid, the hi parts, once all four waves are done with the chunk
+        // state's hi plane (count L.hand[0]), over that plane in L.S[0], where
+        // waves 2 and 3 read the whole of it (count L.hand[1]).  Waves 0 and 1
+        // take the chunk state's hi plane into registers first.
         constexpr int SW = H2Lds<D, C, NKP>::SW;
-        constexpr int QB = W == 2 ? 0 : NQ / 2, QE = W == 2 ? NQ / 2 : NQ;
-        uint32_t* sync = L.hand;
-        const H2Wave<D, C, W, 2> wc(L.L, lane);
-        const int EM = h2_form_mid<D, C, NKP, 2, QB, QE>(L, ES, EK, n, kk, Smid, SHr);
-        lds_signal(&sync[0], lane == 0);
-        lds_wait_count(&sync[0], 4 * (mc + 1));
+        constexpr int NP = NT * NQ;                         // operand pieces
+        constexpr int F = W == 0 ? 0 : W == 1 ? -1 : W - 1;   // the wave's share, -1 none
+        if constexpr (W < 2) {
 #pragma unroll
-        for (int q = QB; q < QE; ++q)
+            for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int i = 0; i < NT; ++i)
-                *reinterpret_cast<f16x8*>(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]) = SHr[q][i];
-        lds_signal(&sync[1], lane == 0);
-        lds_wait_count(&sync[1], 2 * (mc + 1));
-        it = h2_cg_solve<D, C, NKP, W, 2, false>(L, wc, EM, EK, R, X, lam, max_iters, tol, Smid, SHr);
-    } else if constexpr (h2_mid_state<D, C, NKP>()) {
-        // waves 0 and 1: the chunk state's hi plane into registers, then
-        // counted done with L.S[0] in L.hand[0]
-        constexpr int SW = H2Lds<D, C, NKP>::SW;
+                for (int i = 0; i < NT; ++i) SHr[q][i] = lds_f16x8(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]);
+        }
+        int EM = 0;
+        if constexpr (F >= 0) {
+            constexpr int PB = (NP * F + 2) / 3, PE = (NP * (F + 1) + 2) / 3;
+            H2Hi<D, NKP> SM;
+            EM = h2_form_mid<D, C, NKP, 2, PB, PE>(L, ES, EK, n, kk, Smid, SM);
+            lds_signal(&L.hand[0], lane == 0);
+            lds_wait_count(&L.hand[0], 4 * (mc + 1));
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-#pragma unroll
-            for (int i = 0; i < NT; ++i) SHr[q][i] = lds_f16x8(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]);
-        lds_signal(&L.hand[0], lane == 0);
-        // the lo plane addressed through a register: with its constant address
-        // the compiler waited on each of the loop's LDS reads right after
-        // issuing it (wave 1: 28 full waits per iteration, against 6 so, and
-        // 171k against 154k cycles per chunk for the CG)
-        int o0 = 0;
-        asm volatile("" : "+v"(o0));
-        it = h2_cg_solve<D, C, NKP, W, 0, true>(L, wv, ES, EK, R, X, lam, max_iters, tol, L.S[1] + o0, SHr);
+            for (int pc = PB; pc < PE; ++pc) {
+                const int q = pc / NT, i = pc % NT;
+                *reinterpret_cast<f16x8*>(&L.S[0][(16 * i + n) * SW + 16 * q + 4 * kk]) = SM[q][i];
+            }
+            lds_signal(&L.hand[1], lane == 0);
+        } else {
+            lds_signal(&L.hand[0], lane == 0);
+        }
+        if constexpr (W >= 2) {
+            // waves 2 and 3: the state term from the mid-chunk state, keys
+            // from block 2 on
+            lds_wait_count(&L.hand[1], 3 * (mc + 1));
+            const H2Wave<D, C, W, 2> wc(L.L, lane);
+            // wave 3's lo plane through a register too (as waves 0-1's
+            // below): the compiler's schedule of its loop then waits on its
+            // LDS reads in pairs rather than one by one
+            int o0 = 0;
+            if constexpr (W == 3) asm volatile("" : "+v"(o0));
+            it = h2_cg_solve<D, C, NKP, W, 2, false>(L, wc, EM, EK, R, X, lam, max_iters, tol, Smid + o0, SHr);
+        } else {
+            // the lo plane addressed through a register: with its constant
+            // address the compiler waited on each of the loop's LDS reads
+            // right after issuing it (wave 1: 28 full waits per iteration,
+            // against 6 so, and 171k against 154k cycles per chunk for the CG)
+            int o0 = 0;
+            asm volatile("" : "+v"(o0));
+            it = h2_cg_solve<D, C, NKP, W, 0, true>(L, wv, ES, EK, R, X, lam, max_iters, tol, L.S[1] + o0, SHr);
+        }
     } else {
         it = h2_cg_solve<D, C, NKP, W, 0, false>(L, wv, ES, EK, R, X, lam, max_iters, tol, L.S[1], SHr);
     }
