@@ -64,8 +64,9 @@ def h2_cg_mfma_flops(d, C, key_planes, wave_iters):
     the scores and per row block and 32-key step for the apply (keys stored
     as bf16 are one exact fp16 plane, fp32 keys two).  At d = 128, 64-token
     chunks and bf16 keys, waves 2 and 3 start from the mid-chunk state, so
-    their causal key blocks start at block 2, and each forms that state per
-    chunk (four MFMAs per 32-feature step and row block).  Per chunk the
+    their causal key blocks start at block 2; that state is formed once per
+    chunk, shared out among three waves (four MFMAs per 32-feature step and
+    row block).  Per chunk the
     output adds the scores and apply of the solution over the keys from the
     chunk start, and the G_c term: three fp16 MFMAs per feature step and row
     block when a wave splits at most two of G_c's row blocks (64-token
@@ -77,14 +78,12 @@ def h2_cg_mfma_flops(d, C, key_planes, wave_iters):
     mid = d == 128 and C == 64 and key_planes == 1
     gl = (NT + NW - 1) // NW <= 2
     per_iter = np.zeros(NW, np.int64)
-    out16 = 0
+    out16 = 4 * NQ * NT if mid else 0
     for w in range(NW):
         kb0 = 2 if mid and w >= 2 else 0
         nb = w + 1 - kb0
         per_iter[w] = 3 * NT * NQ + np_ * NQ * nb + np_ * NT * ((nb + 1) // 2)
         out16 += np_ * NQ * (w + 1) + np_ * NT * ((w + 2) // 2)
-        if kb0:
-            out16 += 4 * NQ * NT
         if gl:
             out16 += 3 * NQ * NT
     wave_iters = np.asarray(wave_iters, np.int64)
