@@ -153,6 +153,47 @@ def scan_inline_asm(text: str):
     return out
 
 
+def loop_lds_waits(text: str, kernel_prefix: str, min_mfma: int = 100, max_mfma: int = 400):
+    """The loops of one kernel that issue between min_mfma and max_mfma MFMAs
+    per pass (in the CG kernels, each wave's iteration; the persistent loop
+    around the chunks issues more): a list of (MFMAs, full LDS waits
+    `s_waitcnt lgkmcnt(0)`) per pass, in code order.  A loop is the code from
+    a label to a later branch back to it.  The compiler has at times scheduled
+    such a loop to wait on each of its LDS reads right after issuing it, which
+    shows as several times the usual count of full waits."""
+    lines = text.splitlines()
+    starts = [i for i, l in enumerate(lines) if l.startswith(kernel_prefix) and ":" in l]
+    if not starts:
+        raise ValueError(f"no kernel {kernel_prefix} in the assembly")
+    st = starts[0]
+    en = next((i for i in range(st + 1, len(lines)) if re.match(r"^_Z\w+:", lines[i])), len(lines))
+    body = lines[st:en]
+    labels = {}
+    for i, l in enumerate(body):
+        m = re.match(r"^(\.LBB\S+):", l)
+        if m:
+            labels[m.group(1)] = i
+    out = []
+    for i, l in enumerate(body):
+        m = re.search(r"\bs_cbranch_\w+\s+(\.LBB\S+)", l)
+        if not m or m.group(1) not in labels or labels[m.group(1)] >= i:
+            continue
+        ins = [x.strip() for x in body[labels[m.group(1)]:i + 1]]
+        nm = sum(x.startswith("v_mfma") for x in ins)
+        if min_mfma <= nm <= max_mfma:
+            out.append((nm, sum(x == "s_waitcnt lgkmcnt(0)" for x in ins)))
+    return out
+
+
+def compile_asm(src: str) -> str:
+    """gfx950 assembly of one kernel source, built with its own flags."""
+    with tempfile.TemporaryDirectory() as td:
+        asm = os.path.join(td, src + ".s")
+        cmd = [B.HIPCC, *B.flags_for(src), "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", asm]
+        subprocess.run(cmd, check=True, capture_output=True)
+        return open(asm).read()
+
+
 def check_all(sources=None):
     """Compile each kernel source to gfx950 assembly; return {source: hazards},
     the SrcC rewrites of scan_asm followed by the inline-asm findings."""

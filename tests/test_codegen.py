@@ -59,3 +59,37 @@ def test_scanner_flags_inline_asm_hazards():
     assert codegen_check.scan_inline_asm(waited) == []
     assert len(codegen_check.scan_inline_asm(reads_mfma_result)) == 1
     assert codegen_check.scan_inline_asm(rewritten_first) == []
+
+
+@pytest.mark.skipif(shutil.which(build.HIPCC) is None and not __import__("os").path.exists(build.HIPCC),
+                    reason="hipcc not available")
+def test_headline_cg_loops_keep_lds_reads_in_flight():
+    # each wave's CG iteration in the d = 128, 64-token, bf16-key kernel waits
+    # for all its LDS reads at most a dozen times (6-7 with reads kept in
+    # flight; 27-29 when the compiler waits on each read as it is issued,
+    # about 11% slower for that wave)
+    text = codegen_check.compile_asm("cg_output_bf16.hip")
+    loops = codegen_check.loop_lds_waits(text, "_ZN4mesa12cg_h2_kernelILi128ELi64ENS_6bf16_tEEEv")
+    assert sorted(m for m, _ in loops) == [120, 120, 128, 128], loops
+    assert all(w <= 12 for _, w in loops), loops
+
+
+def test_loop_wait_counter():
+    text = """_ZN4mesa3fooEv:
+    s_mov_b32 s0, 0
+.LBB0_1:
+    ds_read_b128 v[0:3], v4
+    s_waitcnt lgkmcnt(0)
+    v_mfma_f32_16x16x32_f16 a[0:3], v[0:3], v[0:3], a[0:3]
+    v_mfma_f32_16x16x32_f16 a[4:7], v[0:3], v[0:3], a[4:7]
+    s_waitcnt lgkmcnt(1)
+    s_cbranch_scc1 .LBB0_1
+    s_endpgm
+_ZN4mesa3barEv:
+.LBB1_1:
+    v_mfma_f32_16x16x32_f16 a[0:3], v[0:3], v[0:3], a[0:3]
+    s_cbranch_scc1 .LBB1_1
+"""
+    assert codegen_check.loop_lds_waits(text, "_ZN4mesa3fooEv", min_mfma=1) == [(2, 1)]
+    assert codegen_check.loop_lds_waits(text, "_ZN4mesa3barEv", min_mfma=1) == [(1, 0)]
+    assert codegen_check.loop_lds_waits(text, "_ZN4mesa3fooEv", min_mfma=3) == []
