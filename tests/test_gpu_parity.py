@@ -432,6 +432,25 @@ def test_strong_decay(dtype, d):
         compare_counts(g["iters"], r, cap, tol)
 
 
+@pytest.mark.parametrize("T", [33, 96, 104, 127])
+def test_mid_state_partial_last_chunk(T):
+    """d = 128, bf16 keys, 64-token chunks: the waves that start from the
+    mid-chunk state (tokens 32..63 of a chunk), with the layer ending at
+    token 33, 32, 40 or 63 of its last chunk.  That state is formed by three
+    waves and handed over through LDS counters whatever the chunk's length;
+    192 heads, so that with two chunks per head some workgroups take two."""
+    B, H, d = 8, 24, 128
+    say("case mid-chunk state, ragged last chunk", T)
+    x = small_inputs(90 + T, B, H, T, d, "bf16")
+    for cap, tol in ((30, 0.0), (30, 1e-4)):
+        g = gpu_forward(x, "bf16", cap, tol, 64)
+        r = oracle_forward(x, "bf16", cap, tol)
+        e = rel_l2(g["out"], r["out"])
+        say(f"T {T} tol {tol}: rel_l2={e:.2e}")
+        assert np.isfinite(g["out"]).all() and e <= 1e-5, (T, tol, e)
+        compare_counts(g["iters"], r, cap, tol)
+
+
 @pytest.mark.parametrize("d", [16, 128])
 def test_iterating_far_past_convergence_stays_finite(d):
     """Lambda = I and a fixed cap far above d: every token's CG converges
