@@ -415,10 +415,11 @@ __device__ __forceinline__ void h2_matvec(const H2Lds<D, C, NKP>& L, const H2Wav
 //    fp32 keys (the first under the last state products), so their LDS
 //    latency does not stall the chain.
 // The state term's planes: the hi plane is L.S[0] (read into registers at
-// the start with bf16 keys), or with HI_GIVEN the registers SHin the caller
-// filled (the mid-chunk state's); the lo plane is Slo (L.S[1], or the
-// mid-chunk state's); both scaled by 2^ES.  The intra-chunk terms run over
-// the causal keys from key block KB0.
+// the start with bf16 keys: the chunk state's, or the mid-chunk state's once
+// the waves that form it have written it there), or with HI_GIVEN the
+// registers SHin the caller filled; the lo plane is Slo (L.S[1], or the
+// mid-chunk state's plane); both scaled by 2^ES.  The intra-chunk terms run
+// over the causal keys from key block KB0.
 template <int D, int NKP>
 using H2Hi = f16x8[NKP == 1 ? D / 32 : 1][NKP == 1 ? D / 16 : 1];
 

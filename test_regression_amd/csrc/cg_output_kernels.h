@@ -288,12 +288,13 @@ __global__ __launch_bounds__(64 * (C / 16)) void cg_output_kernel(
 // fp16 planes of the full matrix).  Every wave's state term starts from
 // S^H_c and its intra-chunk terms run over the causal keys from the chunk
 // start, except at d = 128 with 64-token chunks and bf16 keys: there waves 2
-// and 3 each form the mid-chunk state (the state after token 31) before
-// their CG and start from it, so that their intra-chunk terms cover two key
-// blocks at most, as wave 1's do.  Four workgroup barriers per chunk, as in
-// cg_wave; the exponents of the next chunk's state and keys come from
-// per-wave maxima gathered before barrier (C), and the values' exponent from
-// maxima gathered before barrier (A).  The output's V^T operands are read
+// and 3 start their CG from the mid-chunk state (the state after token 31),
+// which waves 0, 2 and 3 form at the chunk's start, so that their
+// intra-chunk terms cover two key blocks at most, as wave 1's do.  Four
+// workgroup barriers per chunk, as in cg_wave; the exponents of the next
+// chunk's state and keys come from per-wave maxima gathered before barrier
+// (C), and the values' exponent from maxima gathered before barrier (A).
+// The output's V^T operands are read
 // transposed from the value rows (staged where the key rows were, after
 // barrier (A)), so the values need no transposed tile.
 template <int D, int C, int W, typename In>
