@@ -1,18 +1,18 @@
 #!/bin/bash
 # Writes the committed profile summaries (profiles/*.json, profiles/*.txt) from
 # the rocprofv3 output of one profiling run of bench.py (R = repository root):
-#   trace:  cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o t -- python3 $R/bench.py
-#   counts: cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/prof_fetch -o f -- python3 $R/bench.py $SHORT
-#           cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/prof_write -o w -- python3 $R/bench.py $SHORT
+#   trace:  cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_trace -o t -- python3 $R/bench.py
+#   counts: cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/prof_fetch -o f -- python3 $R/bench.py $SHORT
+#           cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/prof_write -o w -- python3 $R/bench.py $SHORT
 #   mfma:   cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16
 #             SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE
-#             -f csv -d $R/gpurun_out/prof_mfma -o m -- python3 $R/bench.py $SHORT
+#             -f csv -d $OUT/prof_mfma -o m -- python3 $R/bench.py $SHORT
 # with SHORT="--steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start"
 # (profile_run.sh runs all four).  The headline forward is the first 4 dispatches of the bf16 CG
 # kernel in a SHORT run; the dynamic-stopping forward is the first 4 dispatches of the fp32 one.
 # Usage: bash test_regression_amd/profile_all.sh <rocprof output dir>   (run from the repository root)
 set -euo pipefail
-OUT=${1:-gpurun_out}
+OUT=${1:-prof_out}
 F=$OUT/prof_fetch/f_counter_collection.csv
 W=$OUT/prof_write/w_counter_collection.csv
 SHORT='--steps 3 --warmup 1 --no-cpu-baseline --copy-probe-gib 1 --decode-steps 16 --no-warm-start'
@@ -64,5 +64,5 @@ $PM --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$MCMD" --sources 
     > profiles/bwd_kv_layer_bf16_d128_T4096_mfma.json
 python -m test_regression_amd.profile_summary stats $OUT/prof_trace/t_kernel_stats.csv \
     --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "$K2" --first 13 \
-    --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o t -- python3 $R/bench.py   (R = repository root; default bench: headline forward 3 warmup + 10 timed steps, small workloads, forward-for-training + backward, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, CPU baseline; the first 13 bf16 CG kernel dispatches are the headline forward)' \
+    --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_trace -o t -- python3 $R/bench.py   (R = repository root; default bench: headline forward 3 warmup + 10 timed steps, small workloads, forward-for-training + backward, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, CPU baseline; the first 13 bf16 CG kernel dispatches are the headline forward)' \
     > profiles/kernels_layer_bf16_d128_T4096_bench_stats.txt
