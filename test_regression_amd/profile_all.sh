@@ -63,6 +63,6 @@ $PM --kernel "chunk_states_full_kernel<64, float, true>" --first 4 --command "$M
 $PM --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$MCMD" --sources $C/bwd_kv.hip $C/cg_h2.h $C/cg_core.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_kv_layer_bf16_d128_T4096_mfma.json
 python -m test_regression_amd.profile_summary stats $OUT/prof_trace/t_kernel_stats.csv \
-    --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "$K2" --first 13 \
-    --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_trace -o t -- python3 $R/bench.py   (R = repository root, OUT = the output directory given to profile_run.sh; default bench: headline forward 3 warmup + 10 timed steps, small workloads, forward-for-training + backward, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, CPU baseline; the first 13 bf16 CG kernel dispatches are the headline forward)' \
+    --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "$K2" --first 13 --skip 3 \
+    --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_trace -o t -- python3 $R/bench.py   (R = repository root, OUT = the output directory given to profile_run.sh; default bench: headline forward 3 warmup + 10 timed steps, small workloads, forward-for-training + backward, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, CPU baseline; the first 13 bf16 CG kernel dispatches are the headline forward: 3 warmup, then the 10 timed)' \
     > profiles/kernels_layer_bf16_d128_T4096_bench_stats.txt

@@ -86,6 +86,11 @@ def cmd_stats(a):
         if d:
             out.append(f"first {len(d)} dispatches of {a.first_kernel}: avg {statistics.mean(d):.1f} us, "
                        f"median {statistics.median(d):.1f} us")
+        # without the first `skip` of them (a workload's untimed warmup launches)
+        t = d[a.skip:]
+        if a.skip and t:
+            out.append(f"dispatches {a.skip + 1}..{len(d)} of {a.first_kernel}: avg {statistics.mean(t):.1f} us, "
+                       f"median {statistics.median(t):.1f} us")
     print("\n".join(out))
 
 
@@ -179,6 +184,7 @@ def main(argv=None):
     s.add_argument("--trace", default="", help="kernel_trace.csv of the same run")
     s.add_argument("--first-kernel", default="", help="kernel name substring for --first")
     s.add_argument("--first", type=int, default=0, help="average only its first N dispatches")
+    s.add_argument("--skip", type=int, default=0, help="also average those first N without their first SKIP")
     t = sub.add_parser("traffic")
     t.add_argument("fetch")
     t.add_argument("write")
