@@ -62,6 +62,10 @@ $PM --kernel "chunk_states_full_kernel<64, float, true>" --first 4 --command "$M
     --sources $C/chunk_states.hip $C/mesa_device.h > profiles/chunk_states_dynamic_f32_d128_T8192_mfma.json
 $PM --kernel "bwd_kv_kernel<128, 64, mesa::bf16_t>" --command "$MCMD" --sources $C/bwd_kv.hip $C/cg_h2.h $C/cg_core.h $C/persistent.h $C/mesa_device.h \
     > profiles/bwd_kv_layer_bf16_d128_T4096_mfma.json
+# reverse states: 6 d^2 T flops per head (one rank-1 update for P^gx, two for M, per token)
+$PM --kernel "bwd_states_kernel<128, 64, 4>" --alg-flops 51539607552 --command "$MCMD" \
+    --sources $C/bwd_states.hip $C/cg_h2.h $C/cg_core.h $C/persistent.h $C/mesa_device.h \
+    > profiles/bwd_states_layer_bf16_d128_T4096_mfma.json
 python -m test_regression_amd.profile_summary stats $OUT/prof_trace/t_kernel_stats.csv \
     --trace $OUT/prof_trace/t_kernel_trace.csv --first-kernel "$K2" --first 13 --skip 3 \
     --command 'cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_trace -o t -- python3 $R/bench.py   (R = repository root, OUT = the output directory given to profile_run.sh; default bench: headline forward 3 warmup + 10 timed steps, small workloads, forward-for-training + backward, dynamic-iteration forward, decode with warm-start runs, q/k pre-processing, Hawk scan, CPU baseline; the first 13 bf16 CG kernel dispatches are the headline forward: 3 warmup, then the 10 timed)' \
